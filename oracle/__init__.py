@@ -1,0 +1,8 @@
+"""fp64 CPU oracle of the FreeSolo FS-L attention forward.
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg import this package.  It shares no code with the HIP path.
+"""
+from .pyoracle import Oracle, Problem, build, make_problem, problem_from
+
+__all__ = ["Oracle", "Problem", "build", "make_problem", "problem_from"]

@@ -1,0 +1,94 @@
+/*
+ * fs_oracle.h -- plain fp64 CPU oracle of the FreeSolo FS-L attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  The product path (the
+ * HIP library and its Python binding) never calls it and shares no code,
+ * header, table or helper with it.
+ *
+ * Source: the FreeSolo paper summary (picx.dev page), section "Methodology",
+ * eqs. (2)-(5) and (7)-(9).  Every function says which equation it follows.
+ * Readings of what the page leaves open:
+ *   - candidate cells of query i are the complete cells whose last token is
+ *     before i - w (the definition of C_i, eq. 6, is missing from the page);
+ *   - the window of eq. (4) holds the w + 1 positions max(0, i - w) .. i;
+ *   - eq. (7) is used with lambda_h = 0 (content score only);
+ *   - RoPE rotates interleaved pairs (2k, 2k+1) by angle p * base^(-2k/d);
+ *   - ties in TopP and top-K go to the larger cell index;
+ *   - the NoPE logits of eq. (9) are q.k / sqrt(d); RMSNorm has unit gain and
+ *     the epsilon given in the problem; an empty selection gives o_lr = 0.
+ *
+ * Layout: q is [B, H, n_q, d], k and v are [B, H, N, d], row-major float32
+ * holding the exact stored values (bf16 inputs are widened without rounding).
+ * All arithmetic is in double.
+ */
+#ifndef FS_ORACLE_H
+#define FS_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int batch, heads, head_dim, n_ctx;
+    int n_q, q_pos0;          /* queries are positions q_pos0 .. q_pos0 + n_q - 1 */
+    int cell, window;         /* s and w */
+    int topk;                 /* K */
+    int budget;               /* P; negative means no pruning (A_i = C_i) */
+    int n_recent;             /* W */
+    double rope_base;
+    double rms_eps;
+    long long pos_offset;     /* absolute position of token 0; RoPE angles only */
+} or_problem;
+
+/* RoPE rotation R(pos) of one d-vector (eq. 3). */
+void or_rope(const or_problem* p, const float* x, long long pos, double* out);
+
+/* Number of candidate cells n_i of the query at position i (C_i = {c < n_i}). */
+int or_n_candidates(const or_problem* p, long long i);
+
+/* Cell summaries of one head (eq. 5): kbar [C, d] and amax [C], C = N / s. */
+void or_cell_summaries_head(const or_problem* p, const float* k_head, double* kbar, double* amax);
+
+/* FS-L pruning (eq. 8) of the candidate set {c < n}: writes the retained cells in
+ * ascending order to keep and returns their number.  gap_rel (nullable) receives
+ * the relative gap between the P-th and (P+1)-th priorities, or +inf. */
+int or_prune_row(const or_problem* p, const double* amax, int n, int* keep, double* gap_rel);
+
+/* Content scores r_c = q.kbar_c / sqrt(d) (eq. 7, lambda = 0) over cand, and the
+ * top-min(K, n_cand) cells written ascending to sel; returns their number.
+ * gap_rel (nullable): relative gap between the K-th and (K+1)-th scores, or +inf.
+ * cand_scores (nullable): the score of every candidate, in cand order. */
+int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
+                  const int* cand, int n_cand, int* sel, double* gap_rel, double* cand_scores);
+
+/* Local branch (eqs. 3-4) of the query at position i. */
+void or_window_row(const or_problem* p, const float* q_row, const float* k_head,
+                   const float* v_head, long long i, double* o_sr);
+
+/* Long-range readout (eq. 9) over the tokens of the n_sel cells in sel. */
+void or_sparse_row(const or_problem* p, const float* q_row, const float* k_head,
+                   const float* v_head, const int* sel, int n_sel, double* o_lr);
+
+/* Whole forward of one head for a list of query rows t (0 <= t < n_q), threaded.
+ * kbar/amax: summaries of this head.  keep_ovr/sel_ovr (nullable) replace the
+ * retained / selected sets of a row when the row's count in *_ovr_n is >= 0;
+ * rows are keep_w / topk ints wide.  Outputs per row: o, o_sr, o_lr [d];
+ * sel [topk] (-1 padded) with its count n_sel; the two boundary gaps. */
+int or_forward_rows(const or_problem* p, const float* q_head, const float* k_head,
+                    const float* v_head, const double* kbar, const double* amax,
+                    double alpha, const int* rows, int n_rows,
+                    const int* keep_ovr, const int* keep_ovr_n, int keep_w,
+                    const int* sel_ovr, const int* sel_ovr_n,
+                    double* o, double* o_sr, double* o_lr, int* sel, int* n_sel,
+                    double* sel_gap, double* keep_gap, int nthreads);
+
+/* Whole forward of the whole problem (eq. 2 for every b, h, query), threaded. */
+int or_forward(const or_problem* p, const float* q, const float* k, const float* v,
+               const float* alpha, double* o, double* o_sr, double* o_lr,
+               int* sel, int* n_sel, double* sel_gap, double* keep_gap, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,194 @@
+"""ctypes wrapper of the fp64 CPU oracle (fs_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the CPU
+baseline leg of the benchmark.  The product path never imports it.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "fs_oracle.c")
+
+
+def build(force: bool = True) -> str:
+    """Compile fs_oracle.c with gcc into liboracle.so (plain -O2, no fast-math)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, SRC_PATH, "-lm", "-lpthread"])
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class Problem(C.Structure):
+    _fields_ = [("batch", C.c_int), ("heads", C.c_int), ("head_dim", C.c_int),
+                ("n_ctx", C.c_int), ("n_q", C.c_int), ("q_pos0", C.c_int),
+                ("cell", C.c_int), ("window", C.c_int), ("topk", C.c_int),
+                ("budget", C.c_int), ("n_recent", C.c_int),
+                ("rope_base", C.c_double), ("rms_eps", C.c_double),
+                ("pos_offset", C.c_longlong)]
+
+
+def problem_from(wl, **kw) -> Problem:
+    """Oracle problem for a synth.Workload, with optional field overrides."""
+    f = dict(batch=wl.batch, heads=wl.heads, head_dim=wl.head_dim, n_ctx=wl.n_ctx,
+             n_q=wl.n_q, q_pos0=wl.q_pos0, cell=wl.cell, window=wl.window, topk=wl.topk,
+             budget=wl.budget, n_recent=wl.n_recent, rope_base=wl.rope_base,
+             rms_eps=wl.rms_eps, pos_offset=0)
+    f.update(kw)
+    return Problem(**f)
+
+
+def make_problem(**kw) -> Problem:
+    f = dict(batch=1, heads=1, head_dim=64, n_ctx=0, n_q=0, q_pos0=0, cell=32, window=512,
+             topk=8, budget=-1, n_recent=0, rope_base=10000.0, rms_eps=1e-6, pos_offset=0)
+    f.update(kw)
+    return Problem(**f)
+
+
+_F32P = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_F64P = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _i32(x):
+    return np.ascontiguousarray(x, dtype=np.int32)
+
+
+class Oracle:
+    def __init__(self, path: str | None = None):
+        path = path or LIB_PATH
+        if not os.path.exists(path):
+            build()
+        L = C.CDLL(path)
+        P = C.POINTER(Problem)
+        L.or_rope.argtypes = [P, _F32P, C.c_longlong, _F64P]
+        L.or_n_candidates.argtypes = [P, C.c_longlong]
+        L.or_n_candidates.restype = C.c_int
+        L.or_cell_summaries_head.argtypes = [P, _F32P, _F64P, _F64P]
+        L.or_prune_row.argtypes = [P, _F64P, C.c_int, _I32P, C.POINTER(C.c_double)]
+        L.or_prune_row.restype = C.c_int
+        L.or_select_row.argtypes = [P, _F32P, _F64P, _I32P, C.c_int, _I32P,
+                                    C.POINTER(C.c_double), C.c_void_p]
+        L.or_select_row.restype = C.c_int
+        L.or_window_row.argtypes = [P, _F32P, _F32P, _F32P, C.c_longlong, _F64P]
+        L.or_sparse_row.argtypes = [P, _F32P, _F32P, _F32P, _I32P, C.c_int, _F64P]
+        vp = C.c_void_p
+        L.or_forward_rows.argtypes = [P, _F32P, _F32P, _F32P, _F64P, _F64P, C.c_double,
+                                      _I32P, C.c_int, vp, vp, C.c_int, vp, vp,
+                                      _F64P, _F64P, _F64P, _I32P, _I32P, _F64P, _F64P, C.c_int]
+        L.or_forward.argtypes = [P, _F32P, _F32P, _F32P, _F32P, _F64P, _F64P, _F64P,
+                                 _I32P, _I32P, _F64P, _F64P, C.c_int]
+        self.L = L
+
+    # -- single steps ------------------------------------------------------
+    def rope(self, p: Problem, x, pos: int) -> np.ndarray:
+        out = np.empty(p.head_dim, np.float64)
+        self.L.or_rope(C.byref(p), _f32(x), int(pos), out)
+        return out
+
+    def n_candidates(self, p: Problem, i: int) -> int:
+        return self.L.or_n_candidates(C.byref(p), int(i))
+
+    def cell_summaries_head(self, p: Problem, k_head):
+        C_ = p.n_ctx // p.cell
+        kbar = np.empty((max(C_, 1), p.head_dim), np.float64)
+        amax = np.empty(max(C_, 1), np.float64)
+        self.L.or_cell_summaries_head(C.byref(p), _f32(k_head), kbar, amax)
+        return kbar[:C_], amax[:C_]
+
+    def prune_row(self, p: Problem, amax, n: int):
+        keep = np.empty(max(n, 1), np.int32)
+        gap = C.c_double()
+        cnt = self.L.or_prune_row(C.byref(p), _f64(amax), int(n), keep, C.byref(gap))
+        return keep[:cnt].copy(), gap.value
+
+    def select_row(self, p: Problem, q_row, kbar, cand):
+        cand = _i32(cand)
+        sel = np.empty(max(len(cand), 1), np.int32)
+        scores = np.empty(max(len(cand), 1), np.float64)
+        gap = C.c_double()
+        cnt = self.L.or_select_row(C.byref(p), _f32(q_row), _f64(kbar), cand, len(cand), sel,
+                                   C.byref(gap), scores.ctypes.data)
+        return sel[:cnt].copy(), gap.value, scores[:len(cand)].copy()
+
+    def window_row(self, p: Problem, q_row, k_head, v_head, i: int) -> np.ndarray:
+        out = np.empty(p.head_dim, np.float64)
+        self.L.or_window_row(C.byref(p), _f32(q_row), _f32(k_head), _f32(v_head), int(i), out)
+        return out
+
+    def sparse_row(self, p: Problem, q_row, k_head, v_head, sel) -> np.ndarray:
+        n_sel = len(sel)
+        arr = _i32(sel) if n_sel else np.zeros(1, np.int32)
+        out = np.empty(p.head_dim, np.float64)
+        self.L.or_sparse_row(C.byref(p), _f32(q_row), _f32(k_head), _f32(v_head), arr, n_sel,
+                             out)
+        return out
+
+    # -- composed -------------------------------------------------------------
+    def forward_rows(self, p: Problem, q_head, k_head, v_head, kbar, amax, alpha, rows,
+                     keep_ovr=None, sel_ovr=None, nthreads: int | None = None) -> dict:
+        """Forward of one head for query rows ``rows`` (indices into q_head).
+
+        keep_ovr / sel_ovr: optional lists (one entry per row, None = no
+        override) of the retained / selected cell sets to use instead of the
+        oracle's own."""
+        rows = _i32(rows)
+        n = len(rows)
+        d, K = p.head_dim, p.topk
+        nthreads = nthreads or os.cpu_count() or 1
+        keep_p = keep_n_p = sel_p = sel_n_p = None
+        keep_w = 0
+        hold = []
+        if keep_ovr is not None:
+            keep_w = max([len(x) for x in keep_ovr if x is not None] + [1])
+            ka = np.full((n, keep_w), -1, np.int32)
+            kn = np.full(n, -1, np.int32)
+            for r, x in enumerate(keep_ovr):
+                if x is not None:
+                    ka[r, :len(x)] = x
+                    kn[r] = len(x)
+            hold += [ka, kn]
+            keep_p, keep_n_p = ka.ctypes.data, kn.ctypes.data
+        if sel_ovr is not None:
+            sa = np.full((n, K), -1, np.int32)
+            sn = np.full(n, -1, np.int32)
+            for r, x in enumerate(sel_ovr):
+                if x is not None:
+                    sa[r, :len(x)] = x
+                    sn[r] = len(x)
+            hold += [sa, sn]
+            sel_p, sel_n_p = sa.ctypes.data, sn.ctypes.data
+        o = np.empty((n, d)); o_sr = np.empty((n, d)); o_lr = np.empty((n, d))
+        sel = np.empty((n, K), np.int32); n_sel = np.empty(n, np.int32)
+        sg = np.empty(n); kg = np.empty(n)
+        kbar_c = _f64(kbar) if len(kbar) else np.zeros((1, d))
+        amax_c = _f64(amax) if len(amax) else np.zeros(1)
+        self.L.or_forward_rows(C.byref(p), _f32(q_head), _f32(k_head), _f32(v_head), kbar_c,
+                               amax_c, float(alpha), rows, n, keep_p, keep_n_p, keep_w, sel_p,
+                               sel_n_p, o, o_sr, o_lr, sel, n_sel, sg, kg, int(nthreads))
+        return dict(o=o, o_sr=o_sr, o_lr=o_lr, sel=sel, n_sel=n_sel, sel_gap=sg, keep_gap=kg)
+
+    def forward(self, p: Problem, q, k, v, alpha, nthreads: int | None = None) -> dict:
+        B, H, nq, d, K = p.batch, p.heads, p.n_q, p.head_dim, p.topk
+        nthreads = nthreads or os.cpu_count() or 1
+        o = np.empty((B, H, nq, d)); o_sr = np.empty_like(o); o_lr = np.empty_like(o)
+        sel = np.empty((B, H, nq, K), np.int32); n_sel = np.empty((B, H, nq), np.int32)
+        sg = np.empty((B, H, nq)); kg = np.empty((B, H, nq))
+        self.L.or_forward(C.byref(p), _f32(q), _f32(k), _f32(v), _f32(alpha), o, o_sr, o_lr,
+                          sel, n_sel, sg, kg, int(nthreads))
+        return dict(o=o, o_sr=o_sr, o_lr=o_lr, sel=sel, n_sel=n_sel, sel_gap=sg, keep_gap=kg)

@@ -1,0 +1,420 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+None of these tests retypes the oracle's formulas: each checks the oracle
+against a hand-derived closed form (tests/golden), a library routine in a
+special case that reduces to it (torch scaled_dot_product_attention, rms_norm,
+numpy complex arithmetic), an independent algorithm (rank counting), or an
+invariant the equations imply.  Citations are to the FreeSolo paper summary
+(picx.dev page), section 3 "Methodology".
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_fs_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def _val(x):
+    if isinstance(x, (int, float)):
+        return float(x)
+    env = {"sqrt": math.sqrt, "cos": math.cos, "sin": math.sin, "__builtins__": {}}
+    return float(eval(x, env))  # expressions written in hand_cases.json only
+
+
+@pytest.fixture(scope="module")
+def gold():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- golden cases
+def test_golden_summaries(orc, gold):
+    for case in gold["summaries"]:
+        k = np.array(case["k"], np.float32)
+        p = oracle.make_problem(head_dim=case["head_dim"], n_ctx=len(k), cell=case["cell"])
+        kbar, amax = orc.cell_summaries_head(p, k)
+        np.testing.assert_array_equal(kbar, np.array(case["kbar"], float))
+        np.testing.assert_array_equal(amax, np.array(case["amax"], float))
+
+
+def test_golden_prune(orc, gold):
+    for case in gold["prune"]:
+        p = oracle.make_problem(budget=case["budget"], n_recent=case["n_recent"])
+        keep, _ = orc.prune_row(p, np.array(case["amax"], float), case["n"])
+        assert keep.tolist() == case["keep"], case["why"]
+
+
+def test_golden_select(orc, gold):
+    for case in gold["select"]:
+        for K, want in case["topk"].items():
+            p = oracle.make_problem(head_dim=case["head_dim"], topk=int(K))
+            sel, _, scores = orc.select_row(p, np.array(case["q"], np.float32),
+                                            np.array(case["kbar"], float), case["cand"])
+            np.testing.assert_allclose(scores, case["scores"], rtol=0, atol=1e-15)
+            assert sel.tolist() == want, (K, case["why"])
+
+
+def test_golden_n_candidates(orc, gold):
+    g = gold["n_candidates"]
+    p = oracle.make_problem(window=g["window"], cell=g["cell"], n_ctx=1 << 20)
+    assert [orc.n_candidates(p, i) for i in g["i"]] == g["n"]
+
+
+def test_golden_window_uniform(orc, gold):
+    g = gold["window_uniform"]
+    v = np.array(g["v"], np.float32)
+    k = np.zeros_like(v)
+    p = oracle.make_problem(head_dim=g["head_dim"], n_ctx=len(v), window=g["window"], cell=2)
+    q = np.array([0.3, -1.7], np.float32)
+    for i, want in enumerate(g["o_sr"]):
+        got = orc.window_row(p, q, k, v, i)
+        np.testing.assert_allclose(got, [_val(x) for x in want], rtol=1e-14, atol=1e-14)
+
+
+def test_golden_readout_uniform(orc, gold):
+    g = gold["readout_uniform"]
+    v = np.array(g["v"], np.float32)
+    k = np.zeros_like(v)
+    p = oracle.make_problem(head_dim=g["head_dim"], n_ctx=len(v), cell=g["cell"],
+                            rms_eps=g["rms_eps"])
+    q = np.array([1.0, 2.0], np.float32)
+    for case in g["cases"]:
+        got = orc.sparse_row(p, q, k, v, case["sel"])
+        np.testing.assert_allclose(got, [_val(x) for x in case["o_lr"]], rtol=1e-14, atol=1e-14)
+
+
+def test_golden_rope_unit(orc, gold):
+    g = gold["rope_unit"]
+    p = oracle.make_problem(head_dim=g["head_dim"], rope_base=g["base"])
+    for case in g["cases"]:
+        got = orc.rope(p, np.array(case["x"], np.float32), case["pos"])
+        np.testing.assert_allclose(got, [_val(x) for x in case["out"]], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- RoPE (eq. 3)
+def _rope_complex(x, pos, base):
+    """Su et al.'s complex form: pair (x_2k, x_2k+1) as x_2k + i x_2k+1 times e^{i pos theta_k}."""
+    d = x.shape[-1]
+    z = x[..., 0::2].astype(np.float64) + 1j * x[..., 1::2].astype(np.float64)
+    theta = np.power(float(base), -np.arange(d // 2) * 2.0 / d)
+    z = z * np.exp(1j * np.outer(np.atleast_1d(pos), theta)).reshape(z.shape)
+    out = np.empty(x.shape, np.float64)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+def test_rope_matches_complex_form(orc):
+    rng = np.random.default_rng(11)
+    for d in (8, 64, 128):
+        p = oracle.make_problem(head_dim=d)
+        for pos in (0, 1, 7, 513, 262143):
+            x = rng.standard_normal(d).astype(np.float32)
+            np.testing.assert_allclose(orc.rope(p, x, pos), _rope_complex(x, pos, 10000.0),
+                                       rtol=0, atol=1e-9)
+
+
+def test_rope_relative_property_and_norm(orc):
+    """(R(i)q).(R(j)k) = q.R(j-i)k (eq. 3 right-hand side) and R preserves norms."""
+    rng = np.random.default_rng(12)
+    d = 64
+    p = oracle.make_problem(head_dim=d)
+    for i, j in ((700, 200), (5, 5), (262143, 261700), (3, 0)):
+        q = rng.standard_normal(d).astype(np.float32)
+        k = rng.standard_normal(d).astype(np.float32)
+        lhs = orc.rope(p, q, i) @ orc.rope(p, k, j)
+        rhs = q.astype(np.float64) @ orc.rope(p, k, j - i)
+        assert abs(lhs - rhs) < 1e-8 * (1 + abs(lhs))
+        assert abs(np.linalg.norm(orc.rope(p, q, i)) - np.linalg.norm(q.astype(np.float64))) < 1e-10
+
+
+def test_rope_frequencies_are_geometric(orc):
+    """Pair k turns by theta_k per position; theta_0 = 1 and theta_k / theta_k+1 = base^(2/d)."""
+    d, base = 16, 10000.0
+    p = oracle.make_problem(head_dim=d, rope_base=base)
+    theta = []
+    for k in range(d // 2):
+        e = np.zeros(d, np.float32)
+        e[2 * k] = 1.0
+        r = orc.rope(p, e, 1)
+        theta.append(math.atan2(r[2 * k + 1], r[2 * k]))
+    theta = np.array(theta)
+    assert abs(theta[0] - 1.0) < 1e-15
+    np.testing.assert_allclose(theta[:-1] / theta[1:], base ** (2.0 / d), rtol=1e-12)
+
+
+# ------------------------------------------------------------- window (eq. 3-4)
+def _rotated(x, base, offset=0):
+    pos = np.arange(x.shape[0]) + offset
+    return np.stack([_rope_complex(x[t], pos[t], base) for t in range(x.shape[0])])
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float64))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=m, is_causal=causal)[0, 0].numpy()
+
+
+def test_window_reduces_to_dense_causal(orc):
+    """w >= N-1: every query sees all earlier tokens, so eq. 4 is causal RoPE attention."""
+    rng = np.random.default_rng(13)
+    N, d = 200, 32
+    q, k, v = (rng.standard_normal((N, d)).astype(np.float32) for _ in range(3))
+    p = oracle.make_problem(head_dim=d, n_ctx=N, n_q=N, window=256, cell=32)
+    want = _sdpa(_rotated(q, 1e4), _rotated(k, 1e4), v, causal=True)
+    got = np.stack([orc.window_row(p, q[i], k, v, i) for i in range(N)])
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_window_edge_is_inclusive(orc):
+    """Rows i <= w equal dense causal rows (the window holds i - w .. i)."""
+    rng = np.random.default_rng(14)
+    N, d, w = 96, 16, 32
+    q, k, v = (rng.standard_normal((N, d)).astype(np.float32) for _ in range(3))
+    p = oracle.make_problem(head_dim=d, n_ctx=N, window=w, cell=8)
+    dense = _sdpa(_rotated(q, 1e4), _rotated(k, 1e4), v, causal=True)
+    for i in range(w + 1):
+        np.testing.assert_allclose(orc.window_row(p, q[i], k, v, i), dense[i], rtol=1e-10,
+                                   atol=1e-12)
+    # past the edge the row differs from dense attention and ignores token i - w - 1
+    i = w + 5
+    assert np.abs(orc.window_row(p, q[i], k, v, i) - dense[i]).max() > 1e-3
+    k2, v2 = k.copy(), v.copy()
+    k2[i - w - 1] *= 5
+    v2[i - w - 1] += 3
+    np.testing.assert_array_equal(orc.window_row(p, q[i], k2, v2, i),
+                                  orc.window_row(p, q[i], k, v, i))
+    k2[i - w] *= 5
+    assert np.abs(orc.window_row(p, q[i], k2, v2, i) - orc.window_row(p, q[i], k, v, i)).max() > 1e-6
+
+
+def test_window_banded_library(orc):
+    rng = np.random.default_rng(15)
+    N, d, w = 160, 16, 40
+    q, k, v = (rng.standard_normal((N, d)).astype(np.float32) for _ in range(3))
+    p = oracle.make_problem(head_dim=d, n_ctx=N, window=w, cell=8)
+    ii, jj = np.meshgrid(np.arange(N), np.arange(N), indexing="ij")
+    band = (jj <= ii) & (jj >= ii - w)
+    want = _sdpa(_rotated(q, 1e4), _rotated(k, 1e4), v, mask=band)
+    got = np.stack([orc.window_row(p, q[i], k, v, i) for i in range(N)])
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_window_shift_invariance(orc):
+    """Adding a common offset to every position leaves the local branch unchanged."""
+    rng = np.random.default_rng(16)
+    N, d = 96, 64
+    q, k, v = (rng.standard_normal((N, d)).astype(np.float32) for _ in range(3))
+    p0 = oracle.make_problem(head_dim=d, n_ctx=N, window=32, cell=8)
+    p1 = oracle.make_problem(head_dim=d, n_ctx=N, window=32, cell=8, pos_offset=262144 - 96)
+    for i in (0, 40, 95):
+        np.testing.assert_allclose(orc.window_row(p1, q[i], k, v, i),
+                                   orc.window_row(p0, q[i], k, v, i), rtol=1e-8, atol=1e-10)
+
+
+# ------------------------------------------------------------ summaries (eq. 5)
+def test_summaries_library_and_special_cases(orc):
+    rng = np.random.default_rng(17)
+    N, d, s = 200, 24, 8
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    p = oracle.make_problem(head_dim=d, n_ctx=N, cell=s)
+    kbar, amax = orc.cell_summaries_head(p, k)
+    C = N // s
+    blocks = k[:C * s].astype(np.float64).reshape(C, s, d)
+    np.testing.assert_allclose(kbar, blocks.mean(axis=1), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(amax, np.linalg.norm(blocks, axis=2).max(axis=1), rtol=1e-14)
+    assert kbar.shape == (C, d)                      # partial tail cell is not a summary
+    p1 = oracle.make_problem(head_dim=d, n_ctx=N, cell=1)   # s = 1: kbar = k, a = |k|
+    kb1, a1 = orc.cell_summaries_head(p1, k)
+    np.testing.assert_array_equal(kb1, k.astype(np.float64))
+    np.testing.assert_allclose(a1, np.linalg.norm(k.astype(np.float64), axis=1), rtol=1e-15)
+    kc = np.tile(np.float32([0.25, -3.5] * (d // 2)), (N, 1))  # constant cells
+    kbc, _ = orc.cell_summaries_head(p, kc)
+    np.testing.assert_array_equal(kbc, np.tile(kc[0].astype(np.float64), (C, 1)))
+
+
+# -------------------------------------------------------------- pruning (eq. 8)
+def _prune_by_rank(a, n, P, W):
+    """Independent algorithm: c is in TopP iff fewer than P candidates outrank it."""
+    keep = []
+    for c in range(n):
+        rank = sum(1 for c2 in range(n) if (a[c2], c2) > (a[c], c))
+        if rank < P or c >= n - W:
+            keep.append(c)
+    return keep
+
+
+def test_prune_rank_counting_and_invariants(orc):
+    rng = np.random.default_rng(18)
+    a = rng.uniform(0, 10, 120)
+    a[[5, 17, 60]] = a[3]                       # plant ties
+    a = np.round(a, 1)                          # and many more
+    for P, W in ((1, 0), (7, 0), (16, 0), (8, 3), (200, 0), (0, 4)):
+        p = oracle.make_problem(budget=P, n_recent=W)
+        prev = None
+        for n in range(0, 121):
+            keep, _ = orc.prune_row(p, a, n)
+            assert keep.tolist() == _prune_by_rank(a, n, P, W), (P, W, n)
+            assert len(keep) <= min(n, W + P)
+            if P >= n:
+                assert keep.tolist() == list(range(n))
+            if W == 0 and prev is not None:
+                assert set(keep.tolist()) <= set(prev) | {n - 1}
+            dropped = sorted(set(range(n)) - set(keep.tolist()) - set(range(n - W, n)))
+            top = [c for c in keep if c < n - W] if W else list(keep)
+            if dropped and top:
+                assert min(a[top]) >= max(a[dropped])
+            prev = keep.tolist()
+
+
+def test_prune_disabled_keeps_all(orc):
+    p = oracle.make_problem(budget=-1)
+    keep, _ = orc.prune_row(p, np.arange(50, dtype=float)[::-1], 37)
+    assert keep.tolist() == list(range(37))
+
+
+# ------------------------------------------------------------ selection (eq. 7)
+def test_select_order_statistics(orc):
+    rng = np.random.default_rng(19)
+    d = 32
+    kbar = rng.standard_normal((300, d))
+    for K in (1, 8, 32, 64):
+        p = oracle.make_problem(head_dim=d, topk=K)
+        for _ in range(5):
+            q = rng.standard_normal(d).astype(np.float32)
+            cand = np.sort(rng.choice(300, size=rng.integers(1, 200), replace=False))
+            sel, gap, scores = orc.select_row(p, q, kbar, cand)
+            np.testing.assert_allclose(scores, kbar[cand] @ q.astype(np.float64) / math.sqrt(d),
+                                       rtol=1e-12, atol=1e-12)
+            assert len(sel) == min(K, len(cand))
+            assert list(sel) == sorted(sel) and set(sel) <= set(cand)
+            chosen = np.isin(cand, sel)
+            if (~chosen).any() and chosen.any():
+                assert scores[chosen].min() >= scores[~chosen].max()
+            if K >= len(cand):
+                assert sel.tolist() == cand.tolist()
+
+
+# ------------------------------------------------------------- readout (eq. 9)
+def test_readout_reduces_to_dense_nope(orc):
+    """No pruning and K covering every candidate: S_i = C_i, so eq. 9 is RMSNorm of
+    NoPE attention over all tokens of the complete cells ending before i - w."""
+    rng = np.random.default_rng(20)
+    N, d, s, w = 256, 16, 8, 64
+    q, k, v = (rng.standard_normal((N, d)).astype(np.float32) for _ in range(3))
+    p = oracle.make_problem(head_dim=d, n_ctx=N, n_q=N, cell=s, window=w, topk=1000,
+                            budget=-1, rms_eps=1e-6)
+    kbar, amax = orc.cell_summaries_head(p, k)
+    res = orc.forward_rows(p, q, k, v, kbar, amax, 1.0, np.arange(N), nthreads=4)
+    n_i = np.array([max(0, (i - w) // s) if i >= w else 0 for i in range(N)])
+    mask = np.arange(N)[None, :] < (n_i * s)[:, None]
+    rows = n_i > 0
+    u = _sdpa(q[rows], k, v, mask=mask[rows])
+    want = torch.nn.functional.rms_norm(torch.from_numpy(u), (d,), eps=1e-6).numpy()
+    np.testing.assert_allclose(res["o_lr"][rows], want, rtol=1e-10, atol=1e-12)
+    assert np.all(res["o_lr"][~rows] == 0)
+    # eq. 2 with alpha = 1: o = o_sr + o_lr, o_sr the window branch
+    np.testing.assert_allclose(res["o"], res["o_sr"] + res["o_lr"], rtol=0, atol=1e-14)
+
+
+def test_readout_rms_of_output(orc):
+    rng = np.random.default_rng(21)
+    N, d, s = 128, 32, 8
+    q, k, v = (rng.standard_normal((N, d)).astype(np.float32) for _ in range(3))
+    for eps in (1e-6, 0.5):
+        p = oracle.make_problem(head_dim=d, n_ctx=N, cell=s, rms_eps=eps)
+        sel = [1, 4, 9]
+        o = orc.sparse_row(p, q[100], k, v, sel)
+        p0 = oracle.make_problem(head_dim=d, n_ctx=N, cell=s, rms_eps=0.0)
+        o0 = orc.sparse_row(p0, q[100], k, v, sel)          # unit RMS without epsilon
+        assert abs(np.sqrt(np.mean(o0 ** 2)) - 1.0) < 1e-12
+        m = 1.0 / np.mean(o0 ** 2)                          # scale-free: u = o0 * sqrt(m_u)
+        assert np.isfinite(m)
+        # with eps: o = o0 * sqrt(m_u / (m_u + eps)); recover m_u from u by direct softmax below
+        toks = np.concatenate([np.arange(c * s, (c + 1) * s) for c in sel])
+        lg = k[toks].astype(np.float64) @ q[100].astype(np.float64) / math.sqrt(d)
+        wts = np.exp(lg - lg.max()); wts /= wts.sum()
+        u = wts @ v[toks].astype(np.float64)
+        mu = np.mean(u ** 2)
+        np.testing.assert_allclose(np.sqrt(np.mean(o ** 2)), np.sqrt(mu / (mu + eps)), rtol=1e-12)
+
+
+def test_readout_ignores_nonselected_and_gap_tokens(orc):
+    """Tokens between the last candidate cell and i - w are in neither branch."""
+    rng = np.random.default_rng(22)
+    N, d, s, w = 256, 16, 8, 64
+    q, k, v = (rng.standard_normal((N, d)).astype(np.float32) for _ in range(3))
+    p = oracle.make_problem(head_dim=d, n_ctx=N, n_q=N, cell=s, window=w, topk=1000, budget=-1)
+    i = 203                                   # n_i = (203 - 64) // 8 = 17: cells 0..16, tokens < 136
+    gap = list(range(136, i - w))             # tokens 136..138; the window starts at 139
+    assert gap == [136, 137, 138]
+    kbar, amax = orc.cell_summaries_head(p, k)
+    base = orc.forward_rows(p, q, k, v, kbar, amax, 0.7, [i])["o"]
+    k2, v2 = k.copy(), v.copy()
+    k2[gap] *= 4; v2[gap] -= 2
+    kb2, am2 = orc.cell_summaries_head(p, k2)
+    np.testing.assert_array_equal(orc.forward_rows(p, q, k2, v2, kb2, am2, 0.7, [i])["o"], base)
+    k3 = k.copy(); k3[135] *= 4               # last token of the last candidate cell matters
+    kb3, am3 = orc.cell_summaries_head(p, k3)
+    assert np.abs(orc.forward_rows(p, q, k3, v, kb3, am3, 0.7, [i])["o"] - base).max() > 1e-6
+
+
+# -------------------------------------------------------- combine and composition
+def test_combine_alpha_linearity(orc):
+    wl = synth.get_workload("c1").replace(n_ctx=800, n_q=800, seed=7)
+    x = synth.generate(wl)
+    p = oracle.problem_from(wl)
+    kbar, amax = orc.cell_summaries_head(p, x["k"][0, 0])
+    rows = np.arange(0, 800, 37)
+    args = (p, x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], kbar, amax)
+    r0 = orc.forward_rows(*args, 0.0, rows)
+    r1 = orc.forward_rows(*args, 0.8, rows)
+    np.testing.assert_array_equal(r0["o"], r0["o_sr"])
+    np.testing.assert_allclose(r1["o"] - r0["o"], 0.8 * r1["o_lr"], rtol=0, atol=1e-13)
+
+
+def test_forward_equals_rows_and_overrides(orc):
+    wl = synth.get_workload("c2").replace(batch=1, heads=2, n_ctx=1100, n_q=1100, budget=6,
+                                          topk=3)
+    x = synth.generate(wl)
+    p = oracle.problem_from(wl)
+    full = orc.forward(p, x["q"], x["k"], x["v"], x["alpha"], nthreads=4)
+    for h in range(2):
+        kbar, amax = orc.cell_summaries_head(p, x["k"][0, h])
+        rows = np.arange(0, 1100, 13)
+        r = orc.forward_rows(p, x["q"][0, h], x["k"][0, h], x["v"][0, h], kbar, amax,
+                             x["alpha"][h], rows)
+        np.testing.assert_array_equal(r["o"], full["o"][0, h, rows])
+        # overriding with the oracle's own sets changes nothing
+        sets = [r["sel"][t, :r["n_sel"][t]] for t in range(len(rows))]
+        r2 = orc.forward_rows(p, x["q"][0, h], x["k"][0, h], x["v"][0, h], kbar, amax,
+                              x["alpha"][h], rows, sel_ovr=sets)
+        np.testing.assert_array_equal(r2["o"], r["o"])
+
+
+def test_needle_is_retained_and_selected(orc):
+    """Planted needle (high max-norm cell aligned with the last queries) survives
+    pruning and is selected by every aligned query."""
+    wl = synth.get_workload("c4").replace(n_ctx=4096, n_q=4096, head_dim=64, heads=2,
+                                          budget=32, topk=8, needle_queries=64)
+    x = synth.generate(wl)
+    p = oracle.problem_from(wl)
+    first = x["meta"]["needle_first_query"]
+    for h in range(2):
+        c_star = int(x["meta"]["needle"][0, h])
+        kbar, amax = orc.cell_summaries_head(p, x["k"][0, h])
+        rows = np.arange(first, wl.n_q)
+        r = orc.forward_rows(p, x["q"][0, h], x["k"][0, h], x["v"][0, h], kbar, amax, 1.0, rows)
+        for t in range(len(rows)):
+            n = orc.n_candidates(p, wl.q_pos0 + rows[t])
+            keep, _ = orc.prune_row(p, amax, n)
+            assert c_star in keep
+            assert c_star in r["sel"][t, :r["n_sel"][t]]
