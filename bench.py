@@ -1,0 +1,267 @@
+"""Benchmark of the FS-L forward (six C-ABI calls) on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input, with
+the inputs resident in HBM: cell summaries, prefix pruning, scoring + top-K,
+window attention, sparse readout, combine.  The headline workload is the 64k
+prefill (B1 H8 N65536 d128 bf16, K32, P256); the 16k prefill and the 256k
+decode are reported alongside.  Per-kernel times come from HIP events recorded
+on the launch stream between the calls of the timed steps.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from long_context_fs_amd import synth  # noqa: E402
+
+PEAK = {"hbm_GBs": 8000.0, "mfma_bf16_TFs": 2500.0, "valu_f32_TFs": 78.6, "mfma_f32_TFs": 157.3}
+METRIC = "FreeSolo forward queries/s and TFLOP/s at N=16k/64k/256k; % of MI355X roofline"
+PRIMARY = "prefill_b1h8_n65536_d128_bf16"
+ALSO = ["prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16"]
+PHASES = ["summaries", "prune", "select", "window", "sparse", "combine"]
+# Source file of each phase's kernel (for matching stored HBM traffic counters).
+PHASE_SRC = {"summaries": "summaries.hip", "prune": "prune.hip", "select": "select.hip",
+             "window": "window.hip", "sparse": "sparse.hip", "combine": "combine.hip"}
+# Engine each phase's kernel uses, which fixes the roofline it is priced against.
+PHASE_ENGINE = {"summaries": "hbm", "prune": "int", "select": "valu_f32", "window": "valu_f32",
+                "sparse": "valu_f32", "combine": "hbm"}
+
+
+def n_cand(wl, i):
+    return 0 if i < wl.window else min((i - wl.window) // wl.cell, wl.n_cells)
+
+
+def algorithmic_work(wl, keep_count=None, n_lo=0):
+    """Algorithmic FLOP / bytes per launch of each phase (matmul FLOP = 2 per MAC)."""
+    d, s, e = wl.head_dim, wl.cell, (2 if wl.dtype == "bf16" else 4)
+    BH = wl.batch * wl.heads
+    i = np.arange(wl.q_pos0, wl.q_pos0 + wl.n_q)
+    n_i = np.where(i < wl.window, 0, np.minimum((i - wl.window) // wl.cell, wl.n_cells))
+    if wl.budget < 0:
+        a_i = n_i.astype(np.float64) * BH
+    elif keep_count is not None:
+        kc = keep_count.reshape(BH, -1)
+        a_i = np.zeros(len(i))
+        pos = n_i > 0
+        a_i[pos] = kc[:, n_i[pos] - n_lo].sum(0)
+    else:
+        a_i = np.minimum(n_i, wl.budget + wl.n_recent).astype(np.float64) * BH
+    win_keys = np.minimum(i, wl.window) + 1
+    sel_cells = np.minimum(a_i / BH, wl.topk)
+    return {
+        "summaries": {"bytes": BH * wl.n_cells * (s * d * e + (d + 1) * 4)},
+        "select": {"flop": float(2 * d * a_i.sum())},
+        "window": {"flop": float(4 * d * win_keys.sum() * BH)},
+        "sparse": {"flop": float(4 * d * s * sel_cells.sum() * BH)},
+        "combine": {"bytes": 3 * BH * wl.n_q * d * e},
+    }
+
+
+def stored_traffic(phase):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel
+    source is unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    ent = data.get(phase)
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "long_context_fs_amd", "csrc", PHASE_SRC[phase])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if ent.get("src_sha") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def run_workload(name, steps, warmup, torch, fs):
+    wl = synth.WORKLOADS[name]
+    x = synth.generate(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v"))
+    alpha = torch.from_numpy(x["alpha"]).to(dev)
+    del x
+    fwd = fs.FsForward.for_workload(wl, device=dev)
+    p = fwd.prob
+
+    def step(ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record()
+        mark(0)
+        fs.fs_cell_summaries(p, k, fwd.kbar, fwd.amax)
+        mark(1)
+        if fwd.pruned:
+            fs.fs_prune_prefix(p, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep, fwd.keep_count)
+        mark(2)
+        fs.fs_select_topk(p, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, fwd.topk,
+                          fwd.idx, None)
+        mark(3)
+        fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)
+        mark(4)
+        fs.fs_sparse_attn(p, q, k, v, fwd.idx, fwd.topk, fwd.rms_eps, fwd.o_lr)
+        mark(5)
+        fs.fs_combine(p, fwd.o_sr, fwd.o_lr, alpha, fwd.o)
+        mark(6)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step time, no events between the calls
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / steps
+    # per-phase times: events on the launch stream between the calls
+    phase_ms = {ph: [] for ph in PHASES}
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        step(ev)
+        torch.cuda.synchronize()
+        for j, ph in enumerate(PHASES):
+            phase_ms[ph].append(ev[j].elapsed_time(ev[j + 1]))
+    phase_avg = {ph: float(np.mean(v)) for ph, v in phase_ms.items()}
+    kc = fwd.keep_count.cpu().numpy() if fwd.pruned else None
+    work = algorithmic_work(wl, kc, fwd.n_lo)
+    queries = wl.batch * wl.n_q
+    total_flop = sum(w.get("flop", 0.0) for w in work.values())
+    return dict(wl=wl, ms_step=ms_step, wall=wall, phase_ms=phase_avg, work=work,
+                qps=queries / (ms_step * 1e-3), tflops=total_flop / (ms_step * 1e-3) / 1e12,
+                total_gflop=total_flop / 1e9)
+
+
+def roofline(res):
+    """Roofline entry for the phase that takes the most time."""
+    ph = max((p for p in PHASES if p != "prune"), key=lambda p: res["phase_ms"][p])
+    t = res["phase_ms"][ph] * 1e-3
+    eng = PHASE_ENGINE[ph]
+    w = res["work"][ph]
+    traffic = stored_traffic(ph)
+    if eng == "hbm":
+        ach = w["bytes"] / t / 1e9
+        out = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"], "unit": "GB/s"}
+    elif eng == "mfma_bf16":
+        ach = w["flop"] / t / 1e12
+        out = {"bound": "mfma", "achieved": ach, "peak": PEAK["mfma_bf16_TFs"], "unit": "TFLOP/s"}
+    else:
+        ach = w["flop"] / t / 1e12
+        out = {"bound": "alu", "achieved": ach, "peak": PEAK["valu_f32_TFs"], "unit": "TFLOP/s"}
+    out["frac"] = out["achieved"] / out["peak"]
+    out["traffic"] = traffic
+    out["kernel"] = ph
+    out["ms_per_launch"] = res["phase_ms"][ph]
+    return out
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of query rows of head 0 of the workload."""
+    import oracle
+    wl = synth.WORKLOADS[name]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    x = synth.generate(wl.replace(batch=1, heads=1))
+    orc = oracle.Oracle()
+    p = oracle.problem_from(wl.replace(batch=1, heads=1))
+    t0 = time.perf_counter()
+    kbar, amax = orc.cell_summaries_head(p, x["k"][0, 0])
+    t_sum = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    n_try = min(64, wl.n_q)
+    rows = np.sort(rng.choice(wl.n_q, n_try, replace=False))
+    t0 = time.perf_counter()
+    orc.forward_rows(p, x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], kbar, amax, 1.0, rows,
+                     nthreads=cores)
+    t_try = time.perf_counter() - t0
+    n_rows = int(min(wl.n_q, max(n_try, n_try * budget_s / max(t_try, 1e-3))))
+    rows = np.sort(rng.choice(wl.n_q, n_rows, replace=False))
+    t0 = time.perf_counter()
+    orc.forward_rows(p, x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], kbar, amax, 1.0, rows,
+                     nthreads=cores)
+    t_rows = time.perf_counter() - t0
+    # per-query cost, with the head's summaries spread over all of its queries
+    per_q = t_rows / n_rows + t_sum / wl.n_q
+    return {"value": 1.0 / per_q, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_rows} random query rows of head 0 of {name} "
+                      f"({t_rows:.1f} s on {cores} threads) + that head's cell summaries "
+                      f"({t_sum:.2f} s, amortised over {wl.n_q} queries)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-primary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
+              "Heads and batch shard across GPUs with no communication; that path is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_fs_amd import fs
+    fs.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    main_res = run_workload(PRIMARY, args.steps, args.warmup, torch, fs)
+    also = {}
+    if not args.only_primary:
+        for name in ALSO:
+            r = run_workload(name, args.steps, args.warmup, torch, fs)
+            also[name] = {"queries_per_s": r["qps"], "ms_per_step": r["ms_step"],
+                          "tflops": r["tflops"], "gflop_per_step": r["total_gflop"],
+                          "phase_ms": r["phase_ms"], "roofline": roofline(r)}
+    wl = main_res["wl"]
+    out = {
+        "metric": METRIC,
+        "value": main_res["qps"],
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v with a planted needle cell)",
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads,
+                   "seq_len": wl.n_ctx, "n_q": wl.n_q, "head_dim": wl.head_dim,
+                   "window": wl.window, "cell": wl.cell, "topk": wl.topk, "budget": wl.budget},
+        "tflops": main_res["tflops"],
+        "gflop_per_step": main_res["total_gflop"],
+        "phase_ms": main_res["phase_ms"],
+        "roofline": roofline(main_res),
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(PRIMARY)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * fs.h -- C ABI of the FreeSolo FS-L sparse-attention forward on MI355X (gfx950).
+ *
+ * The operation is the FS-L forward of the FreeSolo paper summary (picx.dev page,
+ * section 3 "Methodology"): per head, a RoPE sliding-window branch (section 3.2,
+ * eqs. 3-4) plus a NoPE long-range branch over 32-token cells (section 3.3,
+ * eqs. 5, 7, 8, 9), combined by eq. 2.  One entry point per step:
+ *
+ *   fs_cell_summaries  eq. 5   mean key and maximum token-key norm per cell
+ *   fs_prune_prefix    eq. 8   FS-L query-independent pruning to W + P cells
+ *   fs_select_topk     eq. 7   content score q.kbar/sqrt(d), top-K cells per query
+ *   fs_window_attn     eqs.3-4 RoPE attention over positions max(0,i-w) .. i
+ *   fs_sparse_attn     eq. 9   NoPE attention over the selected cells' tokens, RMSNorm
+ *   fs_combine         eq. 2   o = o_sr + alpha_h * o_lr
+ *
+ * Readings of what the page leaves open (fixed here, identical in the oracle):
+ *   - candidates of the query at position i are the complete cells whose last
+ *     token precedes i - w: cells c < n_i = floor((i - w) / s) (0 when i < w);
+ *   - the window holds the w + 1 positions max(0, i - w) .. i;
+ *   - eq. 7 is used with lambda_h = 0; top-K and top-P ties go to the larger cell;
+ *   - RoPE turns interleaved pairs (2k, 2k+1) by angle p * base^(-2k/d);
+ *   - NoPE logits are q.k/sqrt(d); RMSNorm has unit gain; no selected cell gives 0.
+ *
+ * Conventions for every call:
+ *   - All pointers except `problem` are DEVICE pointers, 16-byte aligned, owned
+ *     by the caller.  The library allocates nothing and keeps no state between
+ *     calls; calls are reentrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work; results are valid in stream order.
+ *   - q, k, v, o_sr, o_lr and o hold elements of `problem->dtype`, addressed as
+ *     base + b*stride[0] + h*stride[1] + t*stride[2] + e (element units, the d
+ *     elements of a row contiguous).  Row strides must keep rows 16-byte aligned.
+ *   - The other arrays are dense row-major with the shapes given per call.
+ *   - Errors: arguments are validated on the host before anything is enqueued;
+ *     FS_ERR_INVALID / FS_ERR_UNSUPPORTED is returned and nothing runs.  A failed
+ *     launch returns FS_ERR_HIP.  A fault inside a kernel surfaces at the caller's
+ *     next synchronisation.  fs_last_error() describes the last failure of the
+ *     calling thread.  No exception or abort crosses this interface.
+ */
+#ifndef FS_H
+#define FS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FS_OK = 0, FS_ERR_INVALID = 1, FS_ERR_UNSUPPORTED = 2, FS_ERR_HIP = 3 } fs_status;
+typedef enum { FS_F32 = 0, FS_BF16 = 1 } fs_dtype;
+
+typedef struct {
+    int32_t batch, heads;     /* B, H >= 1 */
+    int32_t head_dim;         /* d: 64 or 128 */
+    int32_t n_ctx;            /* N: k and v hold positions 0 .. N-1 */
+    int32_t n_q, q_pos0;      /* queries are positions q_pos0 .. q_pos0+n_q-1 <= N-1 */
+    int32_t cell;             /* s: 32 */
+    int32_t window;           /* w >= 0 */
+    int32_t dtype;            /* fs_dtype of q, k, v, o_sr, o_lr, o */
+    int32_t reserved;         /* 0 */
+    int64_t q_stride[3];      /* (b, h, t) strides of q, in elements */
+    int64_t kv_stride[3];     /* (b, h, t) strides of k and v */
+    int64_t o_stride[3];      /* (b, h, t) strides of o_sr, o_lr and o */
+} fs_problem;
+
+/* Cell summaries, eq. 5.  For every complete cell c < C = floor(N / s):
+ *   kbar[b][h][c][:] = mean of the raw (unrotated) keys of tokens cs .. cs+s-1
+ *   amax[b][h][c]    = max over those tokens of ||k_j||_2
+ * kbar: float32 [B][H][C][d]; amax: float32 [B][H][C].  The partial tail cell is
+ * not summarised. */
+fs_status fs_cell_summaries(const fs_problem* problem, const void* k, float* kbar, float* amax,
+                            void* stream);
+
+/* Host helper: the candidate counts the query block spans.  Query i has n_i
+ * candidate cells; n_i is non-decreasing in i, so the block spans
+ * n_lo = n_{q_pos0} .. n_lo + n_rows - 1 (n_rows = 0 when n_q = 0). */
+fs_status fs_prune_rows(const fs_problem* problem, int32_t* n_lo, int32_t* n_rows);
+
+/* FS-L prefix pruning, eq. 8.  Eq. 8's retained set depends on the query only
+ * through n_i, so one row is written per candidate count n = n_lo + r:
+ *   keep[b][h][r][0 .. cnt-1] = Recent_W({c < n}) U TopP_{c < n}(amax), ascending,
+ *   keep[b][h][r][cnt ..]     = -1,       keep_count[b][h][r] = cnt <= W + P.
+ * TopP orders by (amax, c) descending.  keep: int32 [B][H][n_rows][n_recent+budget];
+ * keep_count: int32 [B][H][n_rows].  n_recent >= 0, budget >= 0,
+ * 1 <= n_recent + budget <= 4096. */
+fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t n_recent,
+                          int32_t budget, int32_t* keep, int32_t* keep_count, void* stream);
+
+/* Scoring and top-K, eq. 7 with lambda_h = 0.  For each query i the score of
+ * cell c is r_ic = q_i . kbar_c / sqrt(d) with the unrotated query.  Candidates
+ * are the keep row of n_i (keep != NULL; rows as written by fs_prune_prefix,
+ * keep_width wide) or every cell c < n_i (keep == NULL: no pruning).  The
+ * selected set is the min(topk, #candidates) candidates with the largest
+ * (r_ic, c); it is written ascending to idx[b][h][t][:], padded with -1.
+ * score (nullable) receives r_ic aligned with idx (0 for padding).
+ * idx: int32 [B][H][n_q][topk]; score: float32 [B][H][n_q][topk]; 1 <= topk <= 64. */
+fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* kbar,
+                         const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
+                         int32_t topk, int32_t* idx, float* score, void* stream);
+
+/* Bytes of device workspace fs_window_attn needs (its RoPE cos/sin table). */
+fs_status fs_workspace_size(const fs_problem* problem, size_t* bytes);
+
+/* Local branch, eqs. 3-4: o_sr_i = softmax_j((R(i)q_i).(R(j)k_j)/sqrt(d)) v_j over
+ * j = max(0, i-w) .. i, with RoPE base `rope_base`.  The kernel uses relative
+ * angles, which eq. 3's right-hand side makes exact, so positions up to 2^31
+ * lose no accuracy.  workspace: at least fs_workspace_size bytes, overwritten. */
+fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
+                         float rope_base, void* workspace, size_t ws_bytes, void* o_sr,
+                         void* stream);
+
+/* Long-range readout, eq. 9: u_i = softmax_j(q_i.k_j/sqrt(d)) v_j over the tokens
+ * of the cells listed in idx[b][h][t][0 .. topk-1] (-1 entries ignored; cells
+ * must be < C and distinct), unrotated; o_lr_i = u_i / sqrt(mean(u_i^2) + rms_eps).
+ * A query with no selected cell gets o_lr = 0. */
+fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
+                         const int32_t* idx, int32_t topk, float rms_eps, void* o_lr,
+                         void* stream);
+
+/* Range combination, eq. 2: o = o_sr + alpha[h] * o_lr.  alpha: float32 [H]. */
+fs_status fs_combine(const fs_problem* problem, const void* o_sr, const void* o_lr,
+                     const float* alpha, void* o, void* stream);
+
+const char* fs_status_string(fs_status status);
+const char* fs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FS_H */

@@ -1,0 +1,241 @@
+// api.hip -- the C ABI of include/fs.h: host-side validation, launch, error mapping.
+//
+// Every entry point validates its arguments on the host and enqueues nothing on
+// failure.  No exception or abort crosses the interface.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fs.h"
+#include "fs_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+fs_status fail(fs_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fs_status from_hip(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) {
+        g_err[0] = 0;
+        return FS_OK;
+    }
+    return fail(FS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validate the problem and build the kernels' view of it.
+fs_status check_problem(const fs_problem* p, fs::Shape* sh)
+{
+    if (!p) return fail(FS_ERR_INVALID, "problem is NULL");
+    if (p->batch < 1 || p->heads < 1) return fail(FS_ERR_INVALID, "batch and heads must be >= 1");
+    if ((long)p->batch * p->heads > 65535)
+        return fail(FS_ERR_UNSUPPORTED, "batch * heads must be <= 65535");
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(FS_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128", p->head_dim);
+    if (p->cell != 32) return fail(FS_ERR_UNSUPPORTED, "cell %d: only 32", p->cell);
+    if (p->dtype != FS_F32 && p->dtype != FS_BF16)
+        return fail(FS_ERR_INVALID, "dtype %d", p->dtype);
+    if (p->n_ctx < 1) return fail(FS_ERR_INVALID, "n_ctx must be >= 1");
+    if (p->window < 0 || p->window > (1 << 20))
+        return fail(FS_ERR_UNSUPPORTED, "window %d outside [0, 2^20]", p->window);
+    if (p->n_q < 0 || p->q_pos0 < 0 || (long)p->q_pos0 + p->n_q > p->n_ctx)
+        return fail(FS_ERR_INVALID, "queries %d..%d outside 0..n_ctx-1 (%d)", p->q_pos0,
+                    p->q_pos0 + p->n_q - 1, p->n_ctx);
+    if (p->reserved != 0) return fail(FS_ERR_INVALID, "reserved field must be 0");
+    const int epv = p->dtype == FS_BF16 ? 8 : 4;   // elements per 16 bytes
+    const int64_t* strides[3] = {p->q_stride, p->kv_stride, p->o_stride};
+    const char* names[3] = {"q_stride", "kv_stride", "o_stride"};
+    for (int a = 0; a < 3; ++a) {
+        for (int t = 0; t < 3; ++t) {
+            if (strides[a][t] < 0 || strides[a][t] % epv != 0)
+                return fail(FS_ERR_INVALID, "%s[%d] = %lld must be >= 0 and keep rows 16-byte aligned",
+                            names[a], t, (long long)strides[a][t]);
+        }
+        if (strides[a][2] < p->head_dim)
+            return fail(FS_ERR_INVALID, "%s[2] must be >= head_dim", names[a]);
+    }
+    sh->B = p->batch; sh->H = p->heads; sh->d = p->head_dim; sh->N = p->n_ctx;
+    sh->nq = p->n_q; sh->q_pos0 = p->q_pos0; sh->s = p->cell; sh->w = p->window;
+    sh->bf16 = p->dtype == FS_BF16;
+    sh->C = p->n_ctx / p->cell;
+    for (int t = 0; t < 3; ++t) {
+        sh->qs[t] = p->q_stride[t];
+        sh->kvs[t] = p->kv_stride[t];
+        sh->os[t] = p->o_stride[t];
+    }
+    return FS_OK;
+}
+
+#define FS_CHECK(call)                    \
+    do {                                  \
+        fs_status st_ = (call);           \
+        if (st_ != FS_OK) return st_;     \
+    } while (0)
+
+#define FS_PTR(ptr)                                                                      \
+    do {                                                                                 \
+        if (!(ptr)) return fail(FS_ERR_INVALID, "%s is NULL", #ptr);                     \
+        if (!aligned16(ptr)) return fail(FS_ERR_INVALID, "%s is not 16-byte aligned", #ptr); \
+    } while (0)
+
+}  // namespace
+
+namespace fs {
+void candidate_rows(const Shape& sh, int* n_lo, int* n_rows)
+{
+    auto ncand = [&](long i) -> int {
+        if (i < sh.w) return 0;
+        long n = (i - sh.w) / sh.s;
+        return (int)(n < sh.C ? n : sh.C);
+    };
+    if (sh.nq == 0) {
+        *n_lo = 0;
+        *n_rows = 0;
+        return;
+    }
+    *n_lo = ncand(sh.q_pos0);
+    *n_rows = ncand((long)sh.q_pos0 + sh.nq - 1) - *n_lo + 1;
+}
+}  // namespace fs
+
+extern "C" {
+
+const char* fs_status_string(fs_status s)
+{
+    switch (s) {
+        case FS_OK: return "FS_OK";
+        case FS_ERR_INVALID: return "FS_ERR_INVALID";
+        case FS_ERR_UNSUPPORTED: return "FS_ERR_UNSUPPORTED";
+        case FS_ERR_HIP: return "FS_ERR_HIP";
+    }
+    return "unknown fs_status";
+}
+
+const char* fs_last_error(void) { return g_err; }
+
+fs_status fs_cell_summaries(const fs_problem* problem, const void* k, float* kbar, float* amax,
+                            void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(k); FS_PTR(kbar);
+    if (!amax) return fail(FS_ERR_INVALID, "amax is NULL");
+    return from_hip(fs::launch_summaries(sh, k, kbar, amax, (hipStream_t)stream),
+                    "fs_cell_summaries");
+}
+
+fs_status fs_prune_rows(const fs_problem* problem, int32_t* n_lo, int32_t* n_rows)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (!n_lo || !n_rows) return fail(FS_ERR_INVALID, "n_lo / n_rows is NULL");
+    int lo, rows;
+    fs::candidate_rows(sh, &lo, &rows);
+    *n_lo = lo;
+    *n_rows = rows;
+    g_err[0] = 0;
+    return FS_OK;
+}
+
+fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t n_recent,
+                          int32_t budget, int32_t* keep, int32_t* keep_count, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (n_recent < 0 || budget < 0 || n_recent + budget < 1 || n_recent + budget > 4096)
+        return fail(FS_ERR_UNSUPPORTED, "n_recent %d + budget %d must be in [1, 4096]", n_recent,
+                    budget);
+    if (!amax || !keep || !keep_count) return fail(FS_ERR_INVALID, "NULL amax/keep/keep_count");
+    int lo, rows;
+    fs::candidate_rows(sh, &lo, &rows);
+    return from_hip(fs::launch_prune(sh, amax, lo, rows, n_recent, budget, keep, keep_count,
+                                     (hipStream_t)stream),
+                    "fs_prune_prefix");
+}
+
+fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* kbar,
+                         const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
+                         int32_t topk, int32_t* idx, float* score, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(q); FS_PTR(kbar);
+    if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
+    if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
+    if (keep && (!keep_count || keep_width < 1 || keep_width > 4096))
+        return fail(FS_ERR_INVALID, "keep needs keep_count and keep_width in [1, 4096]");
+    int lo, rows;
+    fs::candidate_rows(sh, &lo, &rows);
+    if (!keep) {
+        long last = (long)sh.q_pos0 + sh.nq - 1;
+        long n_hi = last >= sh.w ? (last - sh.w) / sh.s : 0;
+        if (n_hi > 16256)
+            return fail(FS_ERR_UNSUPPORTED, "without pruning at most 16256 candidate cells");
+    }
+    return from_hip(fs::launch_select(sh, q, kbar, keep, keep_count, keep_width, lo, rows, topk,
+                                      idx, score, (hipStream_t)stream),
+                    "fs_select_topk");
+}
+
+fs_status fs_workspace_size(const fs_problem* problem, size_t* bytes)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (!bytes) return fail(FS_ERR_INVALID, "bytes is NULL");
+    *bytes = fs::rope_table_bytes(sh);
+    g_err[0] = 0;
+    return FS_OK;
+}
+
+fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
+                         float rope_base, void* workspace, size_t ws_bytes, void* o_sr,
+                         void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(q); FS_PTR(k); FS_PTR(v); FS_PTR(o_sr); FS_PTR(workspace);
+    if (!(rope_base > 1.0f)) return fail(FS_ERR_INVALID, "rope_base must be > 1");
+    if (ws_bytes < fs::rope_table_bytes(sh))
+        return fail(FS_ERR_INVALID, "workspace of %zu bytes, need %zu", ws_bytes,
+                    fs::rope_table_bytes(sh));
+    return from_hip(fs::launch_window(sh, q, k, v, (double)rope_base, workspace, o_sr,
+                                      (hipStream_t)stream),
+                    "fs_window_attn");
+}
+
+fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
+                         const int32_t* idx, int32_t topk, float rms_eps, void* o_lr,
+                         void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(q); FS_PTR(k); FS_PTR(v); FS_PTR(o_lr);
+    if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
+    if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
+    if (!(rms_eps >= 0.0f)) return fail(FS_ERR_INVALID, "rms_eps must be >= 0");
+    return from_hip(fs::launch_sparse(sh, q, k, v, idx, topk, rms_eps, o_lr, (hipStream_t)stream),
+                    "fs_sparse_attn");
+}
+
+fs_status fs_combine(const fs_problem* problem, const void* o_sr, const void* o_lr,
+                     const float* alpha, void* o, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(o_sr); FS_PTR(o_lr); FS_PTR(o);
+    if (!alpha) return fail(FS_ERR_INVALID, "alpha is NULL");
+    return from_hip(fs::launch_combine(sh, o_sr, o_lr, alpha, o, (hipStream_t)stream),
+                    "fs_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// fs_launch.hpp -- host-side launchers of the FS-L kernels (validated shapes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fs {
+
+// Validated problem shape, as the kernels see it.
+struct Shape {
+    int B, H, d, N, nq, q_pos0, s, w;
+    int bf16;          // 1: bf16 storage, 0: f32 storage
+    int C;             // complete cells, N / s
+    int64_t qs[3], kvs[3], os[3];
+};
+
+// Range of candidate counts spanned by the queries (host helper).
+void candidate_rows(const Shape& sh, int* n_lo, int* n_rows);
+
+hipError_t launch_summaries(const Shape& sh, const void* k, float* kbar, float* amax,
+                            hipStream_t st);
+hipError_t launch_prune(const Shape& sh, const float* amax, int n_lo, int n_rows, int n_recent,
+                        int budget, int32_t* keep, int32_t* keep_count, hipStream_t st);
+hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const int32_t* keep,
+                         const int32_t* keep_count, int keep_w, int n_lo, int n_rows, int topk,
+                         int32_t* idx, float* score, hipStream_t st);
+size_t rope_table_bytes(const Shape& sh);
+hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
+                         double rope_base, void* table, void* o_sr, hipStream_t st);
+hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const void* v,
+                         const int32_t* idx, int topk, float rms_eps, void* o_lr, hipStream_t st);
+hipError_t launch_combine(const Shape& sh, const void* o_sr, const void* o_lr, const float* alpha,
+                          void* o, hipStream_t st);
+
+}  // namespace fs

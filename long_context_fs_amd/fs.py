@@ -1,0 +1,215 @@
+"""Thin ctypes binding of libfs.so, the C ABI declared in include/fs.h.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+of libfs.so.  PyTorch supplies device memory (tensor data pointers) and the
+current HIP stream.  There is no fallback: if the library is missing, every
+call raises FsError.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfs.so")
+
+FS_F32, FS_BF16 = 0, 1
+CELL = 32
+
+SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
+           "fs_workspace_size", "fs_window_attn", "fs_sparse_attn", "fs_combine",
+           "fs_status_string", "fs_last_error")
+
+
+class FsError(RuntimeError):
+    """A libfs call returned an error status, or the library is missing."""
+
+    def __init__(self, msg: str, status: int = -1):
+        super().__init__(msg)
+        self.status = status
+
+
+class FsProblem(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
+                ("n_ctx", C.c_int32), ("n_q", C.c_int32), ("q_pos0", C.c_int32),
+                ("cell", C.c_int32), ("window", C.c_int32), ("dtype", C.c_int32),
+                ("reserved", C.c_int32), ("q_stride", C.c_int64 * 3),
+                ("kv_stride", C.c_int64 * 3), ("o_stride", C.c_int64 * 3)]
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libfs.so (once) and declare the signatures of include/fs.h."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FsError(f"{path} is not built; run __graft_entry__.build() first")
+    L = C.CDLL(path)
+    P, vp, i32, f32 = C.POINTER(FsProblem), C.c_void_p, C.c_int32, C.c_float
+    sig = {
+        "fs_cell_summaries": [P, vp, vp, vp, vp],
+        "fs_prune_rows": [P, C.POINTER(i32), C.POINTER(i32)],
+        "fs_prune_prefix": [P, vp, i32, i32, vp, vp, vp],
+        "fs_select_topk": [P, vp, vp, vp, vp, i32, i32, vp, vp, vp],
+        "fs_workspace_size": [P, C.POINTER(C.c_size_t)],
+        "fs_window_attn": [P, vp, vp, vp, f32, vp, C.c_size_t, vp, vp],
+        "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, vp],
+        "fs_combine": [P, vp, vp, vp, vp, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = C.c_int
+    L.fs_status_string.argtypes = [C.c_int]
+    L.fs_status_string.restype = C.c_char_p
+    L.fs_last_error.argtypes = []
+    L.fs_last_error.restype = C.c_char_p
+    if path == LIB_PATH:
+        _lib = L
+    return L
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        L = load()
+        raise FsError(f"{name}: {L.fs_status_string(status).decode()}: "
+                      f"{L.fs_last_error().decode()}", status)
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _strides(t, default):
+    if t is None:
+        return default
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise FsError("tensors must be [B, H, T, d] with d contiguous")
+    return tuple(t.stride()[:3])
+
+
+def problem(batch: int, heads: int, head_dim: int, n_ctx: int, n_q: int, q_pos0: int,
+            window: int, dtype: int, cell: int = CELL, q=None, kv=None, o=None) -> FsProblem:
+    """fs_problem for [B, H, T, d] tensors (contiguous unless tensors are given)."""
+    dq = (heads * n_q * head_dim, n_q * head_dim, head_dim)
+    dkv = (heads * n_ctx * head_dim, n_ctx * head_dim, head_dim)
+    p = FsProblem()
+    p.batch, p.heads, p.head_dim, p.n_ctx = batch, heads, head_dim, n_ctx
+    p.n_q, p.q_pos0, p.cell, p.window, p.dtype, p.reserved = n_q, q_pos0, cell, window, dtype, 0
+    p.q_stride[:] = _strides(q, dq)
+    p.kv_stride[:] = _strides(kv, dkv)
+    p.o_stride[:] = _strides(o, dq)
+    return p
+
+
+# ---- the C ABI, one wrapper per entry point ---------------------------------
+def fs_cell_summaries(prob, k, kbar, amax, stream=None):
+    _check("fs_cell_summaries", load().fs_cell_summaries(C.byref(prob), _p(k), _p(kbar),
+                                                         _p(amax), _s(stream)))
+
+
+def fs_prune_rows(prob):
+    lo, rows = C.c_int32(), C.c_int32()
+    _check("fs_prune_rows", load().fs_prune_rows(C.byref(prob), C.byref(lo), C.byref(rows)))
+    return lo.value, rows.value
+
+
+def fs_prune_prefix(prob, amax, n_recent, budget, keep, keep_count, stream=None):
+    _check("fs_prune_prefix", load().fs_prune_prefix(C.byref(prob), _p(amax), n_recent, budget,
+                                                     _p(keep), _p(keep_count), _s(stream)))
+
+
+def fs_select_topk(prob, q, kbar, keep, keep_count, keep_width, topk, idx, score=None,
+                   stream=None):
+    _check("fs_select_topk", load().fs_select_topk(C.byref(prob), _p(q), _p(kbar), _p(keep),
+                                                   _p(keep_count), keep_width, topk, _p(idx),
+                                                   _p(score), _s(stream)))
+
+
+def fs_workspace_size(prob) -> int:
+    n = C.c_size_t()
+    _check("fs_workspace_size", load().fs_workspace_size(C.byref(prob), C.byref(n)))
+    return n.value
+
+
+def fs_window_attn(prob, q, k, v, rope_base, workspace, o_sr, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("fs_window_attn", load().fs_window_attn(C.byref(prob), _p(q), _p(k), _p(v),
+                                                   float(rope_base), _p(workspace), nbytes,
+                                                   _p(o_sr), _s(stream)))
+
+
+def fs_sparse_attn(prob, q, k, v, idx, topk, rms_eps, o_lr, stream=None):
+    _check("fs_sparse_attn", load().fs_sparse_attn(C.byref(prob), _p(q), _p(k), _p(v), _p(idx),
+                                                   topk, float(rms_eps), _p(o_lr), _s(stream)))
+
+
+def fs_combine(prob, o_sr, o_lr, alpha, o, stream=None):
+    _check("fs_combine", load().fs_combine(C.byref(prob), _p(o_sr), _p(o_lr), _p(alpha), _p(o),
+                                           _s(stream)))
+
+
+# ---- the whole forward: buffers allocated once, six calls per step -----------
+class FsForward:
+    """The FS-L forward of one problem shape: eq. 5, 8, 7, 3-4, 9, then 2.
+
+    All intermediates are allocated at construction; a call enqueues the six
+    library calls on the stream and allocates nothing."""
+
+    def __init__(self, batch, heads, n_ctx, head_dim, n_q, q_pos0, dtype, topk, budget,
+                 n_recent=0, window=512, rope_base=10000.0, rms_eps=1e-6, device="cuda"):
+        self.dtype = FS_BF16 if dtype in ("bf16", torch.bfloat16, FS_BF16) else FS_F32
+        tdt = torch.bfloat16 if self.dtype == FS_BF16 else torch.float32
+        self.prob = problem(batch, heads, head_dim, n_ctx, n_q, q_pos0, window, self.dtype)
+        self.topk, self.budget, self.n_recent = topk, budget, n_recent
+        self.rope_base, self.rms_eps = rope_base, rms_eps
+        n_cells = n_ctx // CELL
+        B, H, d = batch, heads, head_dim
+        self.n_lo, self.n_rows = fs_prune_rows(self.prob)
+        f32, i32 = torch.float32, torch.int32
+        self.kbar = torch.empty((B, H, max(n_cells, 1), d), dtype=f32, device=device)
+        self.amax = torch.empty((B, H, max(n_cells, 1)), dtype=f32, device=device)
+        self.pruned = budget >= 0
+        self.keep_w = n_recent + budget if self.pruned else 0
+        self.keep = self.keep_count = None
+        if self.pruned:
+            self.keep = torch.empty((B, H, max(self.n_rows, 1), self.keep_w), dtype=i32,
+                                    device=device)
+            self.keep_count = torch.empty((B, H, max(self.n_rows, 1)), dtype=i32, device=device)
+        self.idx = torch.empty((B, H, n_q, topk), dtype=i32, device=device)
+        self.score = torch.empty((B, H, n_q, topk), dtype=f32, device=device)
+        self.ws = torch.empty(fs_workspace_size(self.prob), dtype=torch.uint8, device=device)
+        self.o_sr = torch.empty((B, H, n_q, d), dtype=tdt, device=device)
+        self.o_lr = torch.empty_like(self.o_sr)
+        self.o = torch.empty_like(self.o_sr)
+
+    def __call__(self, q, k, v, alpha, stream=None, keep_score=True):
+        p = self.prob
+        fs_cell_summaries(p, k, self.kbar, self.amax, stream)
+        if self.pruned:
+            fs_prune_prefix(p, self.amax, self.n_recent, self.budget, self.keep, self.keep_count,
+                            stream)
+        fs_select_topk(p, q, self.kbar, self.keep, self.keep_count, self.keep_w, self.topk,
+                       self.idx, self.score if keep_score else None, stream)
+        fs_window_attn(p, q, k, v, self.rope_base, self.ws, self.o_sr, stream)
+        fs_sparse_attn(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_lr, stream)
+        fs_combine(p, self.o_sr, self.o_lr, alpha, self.o, stream)
+        return self.o
+
+    @classmethod
+    def for_workload(cls, wl, device="cuda"):
+        return cls(wl.batch, wl.heads, wl.n_ctx, wl.head_dim, wl.n_q, wl.q_pos0, wl.dtype,
+                   wl.topk, wl.budget, wl.n_recent, wl.window, wl.rope_base, wl.rms_eps, device)

@@ -1,0 +1,118 @@
+"""The C ABI on the host: the library loads, exports what include/fs.h declares,
+and rejects bad arguments before enqueuing anything (no GPU is touched)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_fs_amd import fs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fs.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fs_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fs.LIB_PATH):
+        pytest.skip("libfs.so not built")
+    return fs.load()
+
+
+def test_header_declares_the_six_calls():
+    names = _declared()
+    for n in ("fs_cell_summaries", "fs_prune_prefix", "fs_select_topk", "fs_window_attn",
+              "fs_sparse_attn", "fs_combine"):
+        assert n in names
+    assert set(names) == set(fs.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fs.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (fs_[a-z_]+)$", out, flags=re.M))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_header_compiles_as_c():
+    src = '#include "fs.h"\nint main(void){fs_problem p; (void)p; return (int)FS_OK;}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        "-x", "c", "-", "-fsyntax-only"], input=src, text=True,
+                       capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _prob(**kw):
+    f = dict(batch=1, heads=2, head_dim=64, n_ctx=4096, n_q=4096, q_pos0=0, window=512,
+             dtype=fs.FS_BF16)
+    f.update(kw)
+    return fs.problem(**f)
+
+
+FAKE = C.c_void_p(1 << 20)          # aligned, never dereferenced: validation fails first
+
+
+def test_prune_rows_and_workspace_host_only(lib):
+    assert fs.fs_prune_rows(_prob()) == (0, 112)          # n = (4095-512)//32 = 111
+    assert fs.fs_prune_rows(_prob(n_q=256, q_pos0=4096 - 256)) == ((3840 - 512) // 32, 8)
+    assert fs.fs_prune_rows(_prob(n_q=0)) == (0, 0)
+    assert fs.fs_prune_rows(_prob(n_q=100, n_ctx=400)) == (0, 1)
+    ws = fs.fs_workspace_size(_prob())
+    assert ws == (512 + 256) * 32 * 8
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(head_dim=96), 2), (dict(head_dim=0), 2), (dict(cell=16), 2), (dict(batch=0), 1),
+    (dict(n_ctx=0), 1), (dict(n_q=10, q_pos0=4090), 1), (dict(window=-1), 2),
+    (dict(dtype=7), 1),
+])
+def test_invalid_problem_rejected(lib, bad, status):
+    p = _prob(**bad)
+    with pytest.raises(fs.FsError) as e:
+        fs.fs_prune_rows(p)
+    assert e.value.status == status
+
+
+def test_bad_strides_and_pointers_rejected(lib):
+    p = _prob()
+    p.q_stride[2] = 60                                    # rows not 16-byte aligned
+    st = lib.fs_cell_summaries(C.byref(p), FAKE, FAKE, FAKE, None)
+    assert st == 1 and b"q_stride" in lib.fs_last_error()
+    p = _prob()
+    assert lib.fs_cell_summaries(C.byref(p), None, FAKE, FAKE, None) == 1
+    assert b"k is NULL" in lib.fs_last_error()
+    assert lib.fs_cell_summaries(C.byref(p), C.c_void_p((1 << 20) + 4), FAKE, FAKE, None) == 1
+    assert b"aligned" in lib.fs_last_error()
+    assert lib.fs_cell_summaries(None, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_call_specific_limits(lib):
+    p = _prob()
+    assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 0, FAKE, FAKE, None) == 2
+    assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 5000, FAKE, FAKE, None) == 2
+    assert lib.fs_prune_prefix(C.byref(p), FAKE, -1, 4, FAKE, FAKE, None) == 2
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, 0, 0, FAKE, None, None) == 2
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, 0, 65, FAKE, None, None) == 2
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, FAKE, None, 64, 8, FAKE, None, None) == 1
+    assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, None, 8, 1e-6, FAKE, None) == 1
+    assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, -1.0, FAKE, None) == 1
+    assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 10000.0, FAKE, 16, FAKE, None) == 1
+    assert b"workspace" in lib.fs_last_error()
+    assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 0.5, FAKE, 1 << 30, FAKE, None) == 1
+    assert lib.fs_combine(C.byref(p), FAKE, FAKE, None, FAKE, None) == 1
+    big = _prob(n_ctx=1 << 20, n_q=1 << 20)              # 32752 candidate cells, no pruning
+    assert lib.fs_select_topk(C.byref(big), FAKE, FAKE, None, None, 0, 8, FAKE, None, None) == 2
+
+
+def test_status_strings(lib):
+    assert lib.fs_status_string(0) == b"FS_OK"
+    assert lib.fs_status_string(3) == b"FS_ERR_HIP"
