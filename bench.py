@@ -34,8 +34,8 @@ PHASES = ["summaries", "prune", "select", "window", "sparse", "combine"]
 PHASE_SRC = {"summaries": "summaries.hip", "prune": "prune.hip", "select": "select.hip",
              "window": "window.hip", "sparse": "sparse.hip", "combine": "combine.hip"}
 # Engine each phase's kernel uses, which fixes the roofline it is priced against.
-PHASE_ENGINE = {"summaries": "hbm", "prune": "int", "select": "valu_f32", "window": "valu_f32",
-                "sparse": "valu_f32", "combine": "hbm"}
+PHASE_ENGINE = {"summaries": "hbm", "prune": "int", "select": "valu_f32", "window": "mfma_bf16",
+                "sparse": "mfma_bf16", "combine": "hbm"}
 
 
 def n_cand(wl, i):

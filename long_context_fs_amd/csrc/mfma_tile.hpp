@@ -1,0 +1,200 @@
+// mfma_tile.hpp -- bf16 MFMA building blocks of the flash-style attention tiles.
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16, n = l % 16):
+//   A (16 x 32): lane holds row n, k = 8g .. 8g+7        (8 bf16, 16 bytes)
+//   B (32 x 16): lane holds column n, k = 8g .. 8g+7
+//   C (16 x 16): lane holds column n, rows 4g .. 4g+3    (4 floats)
+//
+// The tiles compute S^T = K Q^T (keys as rows, queries as columns), so a lane's
+// C registers are 4 keys of ONE query: the softmax statistics of a query live
+// in the 4 lanes n, n+16, n+32, n+48.  Two 16-key S^T blocks give a lane the
+// keys {4g..4g+3} and {16+4g..16+4g+3} of a 32-key group, exactly the 8 values
+// the B operand of O^T += V^T P^T needs, if k-slot 8g+j stands for key
+//   pi(8g+j) = 4g+j (j < 4),  16+4g+(j-4) (j >= 4).
+// V^T is therefore stored in LDS with its columns in that order: column
+// 8g+4h+r of a 32-key group holds key 16h+4g+r.
+#pragma once
+
+#include "fs_device.hpp"
+
+namespace fs {
+namespace mf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileK = 64;               // keys per tile
+constexpr int kVtPitch = kTileK + 8;     // V^T row pitch (elements), padded against bank conflicts
+
+template <int D>
+struct KPitch {
+    static constexpr int value = D + 8;  // K row pitch (elements), padded
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ f16x8 as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8, u); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even float -> fp16 bits, two values per dword (low first).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    const uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
+    const uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+    return a | (b << 16);
+}
+
+__device__ __forceinline__ uint4 lds_load16(const uint16_t* p)
+{
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void lds_store16(uint16_t* p, uint4 v)
+{
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& u, int i)
+{
+    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// 8 x 8 transpose of bf16 values: in[j] holds row j (elements 0..7, two per
+// dword, low half first); out[e] receives column e (element j = in[j][e]).
+__device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8])
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t a = word_of(in[2 * q], e >> 1);
+            const uint32_t b = word_of(in[2 * q + 1], e >> 1);
+            w[q] = (e & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+        }
+        out[e] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// Transpose 4 keys x 8 dims (in[r] = key r, two dims per dword) and store the
+// 8 dim-rows of 4 keys (8 bytes each) at dst + e * kVtPitch.
+__device__ __forceinline__ void store_vt_4x8(const uint4 in[4], uint16_t* dst)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t a0 = word_of(in[0], e >> 1), a1 = word_of(in[1], e >> 1);
+        const uint32_t a2 = word_of(in[2], e >> 1), a3 = word_of(in[3], e >> 1);
+        uint2 w;
+        if (e & 1) {
+            w.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
+            w.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
+        } else {
+            w.x = (a0 & 0xFFFFu) | (a1 << 16);
+            w.y = (a2 & 0xFFFFu) | (a3 << 16);
+        }
+        *reinterpret_cast<uint2*>(dst + e * kVtPitch) = w;
+    }
+}
+
+// Key (within its 32-key group) stored at V^T column slot c = 8g + 4h + r.
+__device__ __forceinline__ int vt_slot_key(int g, int j)
+{
+    return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+
+// Pack 8 probabilities (keys pi(8g+0..7)) into the B operand of O^T += V^T P^T.
+__device__ __forceinline__ bf16x8 pack_p(const f32x4& lo, const f32x4& hi)
+{
+    uint4 u;
+    u.x = pack_bf16x2(lo[0], lo[1]);
+    u.y = pack_bf16x2(lo[2], lo[3]);
+    u.z = pack_bf16x2(hi[0], hi[1]);
+    u.w = pack_bf16x2(hi[2], hi[3]);
+    return as_bf16x8(u);
+}
+
+// One 64-key tile of flash attention for a wave's 32 queries (two groups of 16).
+//   ks : K tile in LDS, 64 rows of D (pitch KPitch<D>), element type of QFrag
+//   vt : V^T tile in LDS, D rows of 64 key-permuted bf16 (pitch kVtPitch)
+//   qf : the queries as B operands, qf[qg][t] = dims 32t + 8g .. + 7 of query 16 qg + n
+//   keep(kb, qg, r) : whether key 16 kb + 4 g + r is visible to query 16 qg + n
+// Updates the running max / sum (per lane, log2 domain) and O^T accumulators.
+template <int D, class Frag, class Keep>
+__device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt,
+                                          const Frag (&qf)[2][D / 32], f32x4 (&acc)[D / 16][2],
+                                          float (&m_run)[2], float (&l_run)[2], float scale_log2,
+                                          Keep keep)
+{
+    constexpr int KP = KPitch<D>::value;
+    constexpr int KS = D / 32, DB = D / 16;
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const Frag a = __builtin_bit_cast(Frag, lds_load16(ks + (16 * kb + n) * KP + 32 * t + 8 * g));
+            s[kb][0] = mfma(a, qf[0][t], s[kb][0]);
+            s[kb][1] = mfma(a, qf[1][t], s[kb][1]);
+        }
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = keep(kb, qg, r) ? s[kb][qg][r] * scale_log2 : -INFINITY;
+                s[kb][qg][r] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        const float m_new = fmaxf(m_run[qg], tmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float corr = exp2f(m_run[qg] - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pv = exp2f(s[kb][qg][r] - m_use);
+                s[kb][qg][r] = pv;
+                psum += pv;
+            }
+        }
+        l_run[qg] = l_run[qg] * corr + psum;
+        m_run[qg] = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db][qg] *= corr;
+        pf[0][qg] = pack_p(s[0][qg], s[1][qg]);
+        pf[1][qg] = pack_p(s[2][qg], s[3][qg]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+            const bf16x8 a = as_bf16x8(lds_load16(vt + (16 * db + n) * kVtPitch + 32 * a2 + 8 * g));
+            acc[db][0] = mfma(a, pf[a2][0], acc[db][0]);
+            acc[db][1] = mfma(a, pf[a2][1], acc[db][1]);
+        }
+    }
+}
+
+}  // namespace mf
+}  // namespace fs

@@ -3,8 +3,21 @@
 //
 // u_i = softmax over the tokens of the selected cells of q_i . k_j / sqrt(d)
 // (unrotated, NoPE), times v_j; o_lr_i = u_i / sqrt(mean(u_i^2) + eps).
+//
+// bf16 storage: a workgroup owns 128 consecutive queries of one head.  It first
+// builds the union of the cells they selected (an LDS bitmap over the cells,
+// ranks by prefix popcount), and each query's selected cells as ascending
+// union slots.  It then streams the union two cells (64 keys) at a time through
+// LDS, exactly like the window kernel's key tiles, and each wave runs the
+// flash tile for its 32 queries with the mask "query selected this cell"
+// (a per-query pointer walk over its slot list).  q and k are the exact bf16
+// inputs (no rotation), so S^T = K Q^T is exact-product bf16 MFMA.  Epilogue:
+// divide by the softmax sum, RMSNorm over d with a 4-lane reduction, store.
+// f32 storage (or when the union bookkeeping would not fit in 64 KiB of LDS):
+// one wavefront per query.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
+#include "mfma_tile.hpp"
 
 namespace fs {
 
@@ -93,11 +106,311 @@ __global__ __launch_bounds__(256) void sparse_attn_rowwise_kernel(
     for (int r = 0; r < R; ++r) store1<E>(orow + lane + r * kWave, u[r] * inv_rms);
 }
 
+
+namespace {
+
+constexpr int kSpQ = 128;              // queries per workgroup
+constexpr int kSpMaxCells = 32768;     // bitmap capacity (cells), so N <= 1M tokens
+constexpr uint16_t kNoSlot = 0xFFFF;
+
+struct SpLayout {
+    int nwords, u_cap, topk;
+    size_t off_vt, off_bitmap, off_rank, off_ulist, off_slots, bytes;
+};
+
+template <int D>
+__host__ __device__ inline SpLayout sp_layout(int C, int topk)
+{
+    SpLayout L;
+    L.nwords = (C + 31) / 32;
+    L.topk = topk;
+    L.u_cap = C < kSpQ * topk ? C : kSpQ * topk;
+    auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
+    size_t off = (size_t)mf::kTileK * mf::KPitch<D>::value * 2;
+    L.off_vt = off;
+    off = up16(off + (size_t)D * mf::kVtPitch * 2);
+    L.off_bitmap = off;
+    off = up16(off + (size_t)L.nwords * 4);
+    L.off_rank = off;
+    off = up16(off + (size_t)L.nwords * 2);
+    L.off_ulist = off;
+    off = up16(off + (size_t)L.u_cap * 2);
+    L.off_slots = off;
+    off = up16(off + (size_t)kSpQ * topk * 2);
+    L.bytes = off;
+    return L;
+}
+
+// Block-wide exclusive scan of one int per thread (256 threads); *total = sum.
+__device__ __forceinline__ int block_excl_scan(int x, int* red, int* total)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int inc = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) red[wv] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        before += i < wv ? red[i] : 0;
+        all += red[i];
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+template <int D>
+struct SpStage {
+    static constexpr int KC = (mf::kTileK * D / 8) / 256;
+    uint4 k[KC];
+    uint4 v[4];
+};
+
+// Token row of tile key r (0..63) for union tile u, or -1 past the union.
+__device__ __forceinline__ long sp_row(const uint16_t* ulist, int n_union, int u, int r)
+{
+    const int slot = 2 * u + (r >> 5);
+    return slot < n_union ? (long)ulist[slot] * 32 + (r & 31) : -1;
+}
+
+template <int D>
+__device__ __forceinline__ void sp_load(SpStage<D>& st, const uint16_t* __restrict__ kh,
+                                        const uint16_t* __restrict__ vh, int64_t kvs2,
+                                        const uint16_t* ulist, int n_union, int u)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < SpStage<D>::KC; ++it) {
+        const int c = tid + 256 * it;
+        const int kr = c / (D / 8), part = c % (D / 8);
+        const long j = sp_row(ulist, n_union, u, kr);
+        st.k[it] = j >= 0 ? *reinterpret_cast<const uint4*>(kh + j * kvs2 + part * 8)
+                          : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 2 * D) {
+        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const long j = sp_row(ulist, n_union, u, 32 * grp + 16 * hh + 4 * g + r);
+            st.v[r] = j >= 0 ? *reinterpret_cast<const uint4*>(vh + j * kvs2 + dc * 8)
+                             : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void sp_store(const SpStage<D>& st, uint16_t* ks, uint16_t* vt)
+{
+    constexpr int KP = mf::KPitch<D>::value;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < SpStage<D>::KC; ++it) {
+        const int c = tid + 256 * it;
+        const int kr = c / (D / 8), part = c % (D / 8);
+        mf::lds_store16(ks + kr * KP + part * 8, st.k[it]);
+    }
+    if (tid < 2 * D) {
+        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+        mf::store_vt_4x8(st.v, vt + (dc * 8) * mf::kVtPitch + 32 * grp + 8 * g + 4 * hh);
+    }
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
+    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t kvs0, int64_t kvs1,
+    int64_t kvs2, int H, int nq, int C, const int32_t* __restrict__ idx, int topk,
+    float scale_log2, float rms_eps, uint16_t* __restrict__ o, int64_t os0, int64_t os1,
+    int64_t os2)
+{
+    using namespace mf;
+    constexpr int KS = D / 32, DB = D / 16;
+    extern __shared__ uint4 smem_raw[];
+    const SpLayout L = sp_layout<D>(C, topk);
+    char* base = reinterpret_cast<char*>(smem_raw);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(base);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(base + L.off_vt);
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
+    uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
+    uint16_t* slots = reinterpret_cast<uint16_t*>(base + L.off_slots);
+    __shared__ int red[4];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const long bh = blockIdx.y;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long t0 = (long)blockIdx.x * kSpQ;
+    const int n_rows = nq - t0 < kSpQ ? (int)(nq - t0) : kSpQ;
+    const int32_t* idx_blk = idx + (bh * nq + t0) * (long)topk;
+
+    // ---- union of the selected cells --------------------------------------
+    for (int wd = tid; wd < L.nwords; wd += 256) bitmap[wd] = 0u;
+    __syncthreads();
+    for (int e = tid; e < n_rows * topk; e += 256) {
+        const int c = idx_blk[e];
+        if (c >= 0 && c < C) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    int cnt[4], mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int wd = 4 * tid + j;
+        cnt[j] = wd < L.nwords ? __popc(bitmap[wd]) : 0;
+        mine += cnt[j];
+    }
+    int n_union;
+    int run = block_excl_scan(mine, red, &n_union);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int wd = 4 * tid + j;
+        if (wd < L.nwords) rank[wd] = (uint16_t)run;
+        run += cnt[j];
+    }
+    __syncthreads();
+    for (int wd = tid; wd < L.nwords; wd += 256) {
+        uint32_t bits = bitmap[wd];
+        int r = rank[wd];
+        while (bits) {
+            const int bpos = __ffs(bits) - 1;
+            ulist[r++] = (uint16_t)(32 * wd + bpos);
+            bits &= bits - 1;
+        }
+    }
+    for (int e = tid; e < n_rows * topk; e += 256) {
+        const int c = idx_blk[e];
+        uint16_t sl = kNoSlot;
+        if (c >= 0 && c < C)
+            sl = (uint16_t)(rank[c >> 5] + __popc(bitmap[c >> 5] & ((1u << (c & 31)) - 1u)));
+        slots[e] = sl;
+    }
+    __syncthreads();
+    if (tid < n_rows) {      // each query's slots ascending (insertion sort; already sorted if idx is)
+        uint16_t* row = slots + tid * topk;
+        for (int a = 1; a < topk; ++a) {
+            const uint16_t x = row[a];
+            int z = a - 1;
+            while (z >= 0 && row[z] > x) {
+                row[z + 1] = row[z];
+                --z;
+            }
+            row[z + 1] = x;
+        }
+    }
+    __syncthreads();
+
+    // ---- queries of this wave as B operands -------------------------------
+    const uint16_t* kh = k + b * kvs0 + h * kvs1;
+    const uint16_t* vh = v + b * kvs0 + h * kvs1;
+    bf16x8 qf[2][KS];
+    int ptr[2];
+    uint16_t nxt[2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const int r = 32 * wv + 16 * qg + n;
+        const bool ok = r < n_rows;
+        const uint16_t* qrow = q + b * qs0 + h * qs1 + (t0 + (ok ? r : 0)) * qs2;
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+            qf[qg][t] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
+                                     : make_uint4(0, 0, 0, 0));
+        ptr[qg] = 0;
+        nxt[qg] = ok ? slots[r * topk] : kNoSlot;
+    }
+
+    f32x4 acc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    const int n_tiles = (n_union + 1) / 2;
+    SpStage<D> stage;
+    if (n_tiles > 0) {
+        sp_load<D>(stage, kh, vh, kvs2, ulist, n_union, 0);
+        sp_store<D>(stage, ks, vt);
+    }
+    __syncthreads();
+    for (int u = 0; u < n_tiles; ++u) {
+        if (u + 1 < n_tiles) sp_load<D>(stage, kh, vh, kvs2, ulist, n_union, u + 1);
+        bool sel[2][2];
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+            const int r = 32 * wv + 16 * qg + n;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int slot = 2 * u + c2;
+                while (nxt[qg] < slot) nxt[qg] = ++ptr[qg] < topk ? slots[r * topk + ptr[qg]] : kNoSlot;
+                sel[qg][c2] = nxt[qg] == slot;
+            }
+        }
+        const bool any = __ballot(sel[0][0] || sel[0][1] || sel[1][0] || sel[1][1]) != 0;
+        if (any) {
+            attn_tile<D>(ks, vt, qf, acc, m_run, l_run, scale_log2,
+                         [&](int kb, int qg, int) { return sel[qg][kb >> 1]; });
+        }
+        __syncthreads();
+        if (u + 1 < n_tiles) {
+            sp_store<D>(stage, ks, vt);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: normalise, RMSNorm over d, store ------------------------
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const int r = 32 * wv + 16 * qg + n;
+        float l = l_run[qg];
+        l += __shfl_xor(l, 16, kWave);
+        l += __shfl_xor(l, 32, kWave);
+        const float inv_l = l > 0.f ? 1.f / l : 0.f;
+        float ss = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            acc[db][qg] *= inv_l;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss = fmaf(acc[db][qg][e], acc[db][qg][e], ss);
+        }
+        ss += __shfl_xor(ss, 16, kWave);
+        ss += __shfl_xor(ss, 32, kWave);
+        const float inv_rms = 1.f / sqrtf(ss / (float)D + rms_eps);
+        if (r >= n_rows) continue;
+        uint16_t* orow = o + b * os0 + h * os1 + (t0 + r) * os2;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            uint2 w2;
+            w2.x = pack_bf16x2(acc[db][qg][0] * inv_rms, acc[db][qg][1] * inv_rms);
+            w2.y = pack_bf16x2(acc[db][qg][2] * inv_rms, acc[db][qg][3] * inv_rms);
+            *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = w2;
+        }
+    }
+}
+
 hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const void* v,
                          const int32_t* idx, int topk, float rms_eps, void* o_lr, hipStream_t st)
 {
     if (sh.nq == 0) return hipSuccess;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
+    const size_t lds = sh.d == 64 ? sp_layout<64>(sh.C, topk).bytes
+                                  : sp_layout<128>(sh.C, topk).bytes;
+    if (sh.bf16 && sh.C <= kSpMaxCells && lds <= 65536) {
+        dim3 grid((unsigned)((sh.nq + kSpQ - 1) / kSpQ), (unsigned)(sh.B * sh.H)), block(256);
+#define FS_SPARSE_MFMA(D)                                                                         \
+        hipLaunchKernelGGL((sparse_attn_mfma_kernel<D>), grid, block, lds, st,                    \
+                           (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2],                      \
+                           (const uint16_t*)k, (const uint16_t*)v, sh.kvs[0], sh.kvs[1],          \
+                           sh.kvs[2], sh.H, sh.nq, sh.C, idx, topk, scale_log2, rms_eps,          \
+                           (uint16_t*)o_lr, sh.os[0], sh.os[1], sh.os[2])
+        if (sh.d == 64) FS_SPARSE_MFMA(64); else FS_SPARSE_MFMA(128);
+#undef FS_SPARSE_MFMA
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
 #define FS_SPARSE(E, D)                                                                          \
     hipLaunchKernelGGL((sparse_attn_rowwise_kernel<E, D>), grid, block, 0, st,                   \

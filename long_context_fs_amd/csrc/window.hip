@@ -5,8 +5,24 @@
 // table built in fp64 (then rounded to fp32) for offsets -w-128 .. 127.  No
 // absolute angle i * theta is ever formed in fp32, so accuracy does not decay
 // at 256k positions.
+//
+// bf16 storage: flash-style MFMA kernel.  A workgroup owns 128 consecutive
+// queries (4 wavefronts x 32) and walks the key range [i0 - w, i0 + 127] in
+// tiles of 64 keys.  Each tile is staged in LDS once for the four waves: K
+// rotated by R(j - i0) and rounded to fp16, V transposed (key-permuted, see
+// mfma_tile.hpp).  Queries are rotated by R(i - i0) once and kept in registers
+// as MFMA B operands.  The rotated q and k are no longer the exact bf16 inputs,
+// so they are carried in fp16 (11-bit mantissa: 8x less rounding than bf16 at
+// the same MFMA rate); this requires rotated elements below 65504 in magnitude.
+// Per tile a wave computes S^T = K Q^T (16x16x32 fp16 MFMA, fp32 accumulate),
+// masks to max(0, i-w) <= j <= i, runs the online
+// softmax in fp32 (exp2 with log2(e)/sqrt(d) folded into the scale), and
+// accumulates O^T += V^T P^T with P rounded to bf16.  The next tile's global
+// loads are issued before the current tile's MFMAs (register double buffer).
+// f32 storage: one wavefront per query, all in fp32.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
+#include "mfma_tile.hpp"
 
 namespace fs {
 
@@ -108,6 +124,191 @@ __global__ __launch_bounds__(256) void window_attn_rowwise_kernel(
     for (int r = 0; r < R; ++r) store1<E>(orow + lane + r * kWave, acc[r] * inv_l);
 }
 
+
+namespace {
+
+constexpr int kWinWaves = 4;
+constexpr int kWinQ = kWinWaves * 32;   // queries per workgroup
+
+template <int D>
+struct WinStage {
+    static constexpr int KC = kWinQ == 128 ? (mf::kTileK * D / 8) / 256 : 0;  // K chunks / thread
+    uint4 k[KC];          // raw bf16 of K rows
+    uint4 v[4];           // 4 keys x 8 dims of V (threads < 2D)
+};
+
+template <int D>
+__device__ __forceinline__ void win_load(WinStage<D>& st, const uint16_t* __restrict__ kh,
+                                         const uint16_t* __restrict__ vh, int64_t kvs2, long kt,
+                                         long kv_hi, long i0, int w, const float2* __restrict__ table)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < WinStage<D>::KC; ++it) {
+        const int c = tid + 256 * it;
+        const int kr = c / (D / 8), part = c % (D / 8);
+        const long j = kt + kr;
+        st.k[it] = j <= kv_hi ? *reinterpret_cast<const uint4*>(kh + j * kvs2 + part * 8)
+                              : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 2 * D) {
+        // keys 32 grp + 16 hh + 4 g + r (r = 0..3), dims 8 dc .. 8 dc + 7
+        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const long j = kt + 32 * grp + 16 * hh + 4 * g + r;
+            st.v[r] = j <= kv_hi ? *reinterpret_cast<const uint4*>(vh + j * kvs2 + dc * 8)
+                                 : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+// Rotate one bf16 pair (x, y) by the angle with cosine c and sine s; pack as fp16.
+__device__ __forceinline__ uint32_t rotate_pack(uint32_t xy, float c, float s)
+{
+    const float x = __uint_as_float(xy << 16), y = __uint_as_float(xy & 0xFFFF0000u);
+    return mf::pack_f16x2(x * c - y * s, x * s + y * c);
+}
+
+// Rotate the staged keys by R(j - i0) (table read here, L2-resident) and write
+// K and V^T to LDS.
+template <int D>
+__device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, uint16_t* vt,
+                                          long kt, long kv_hi, long i0, int w,
+                                          const float2* __restrict__ table)
+{
+    constexpr int KP = mf::KPitch<D>::value;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < WinStage<D>::KC; ++it) {
+        const int c = tid + 256 * it;
+        const int kr = c / (D / 8), part = c % (D / 8);
+        const long j = kt + kr <= kv_hi ? kt + kr : kv_hi;     // rows past kv_hi hold zeros
+        const float4* rp = reinterpret_cast<const float4*>(
+            table + (j - i0 + w + kTableSlack) * (D / 2) + part * 4);
+        const float4 a = rp[0], b = rp[1];
+        uint4 o;
+        o.x = rotate_pack(st.k[it].x, a.x, a.y);
+        o.y = rotate_pack(st.k[it].y, a.z, a.w);
+        o.z = rotate_pack(st.k[it].z, b.x, b.y);
+        o.w = rotate_pack(st.k[it].w, b.z, b.w);
+        mf::lds_store16(ks + kr * KP + part * 8, o);
+    }
+    if (tid < 2 * D) {
+        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+        // V^T column slot 8 g + 4 hh + r of the 32-key group holds key 16 hh + 4 g + r
+        mf::store_vt_4x8(st.v, vt + (dc * 8) * mf::kVtPitch + 32 * grp + 8 * g + 4 * hh);
+    }
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
+    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t kvs0, int64_t kvs1,
+    int64_t kvs2, int H, int nq, int q_pos0, int w, const float2* __restrict__ table,
+    float scale_log2, uint16_t* __restrict__ o, int64_t os0, int64_t os1, int64_t os2)
+{
+    using namespace mf;
+    constexpr int KP = KPitch<D>::value;
+    constexpr int KS = D / 32;     // k-steps of the QK^T contraction
+    constexpr int DB = D / 16;     // 16-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * kVtPitch];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const long bh = blockIdx.y;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long i0 = (long)q_pos0 + (long)blockIdx.x * kWinQ;
+    const long i_end = (long)q_pos0 + nq - 1;                 // last query position
+    const long kv_lo = i0 - w > 0 ? i0 - w : 0;
+    const long kv_hi = i0 + kWinQ - 1 < i_end ? i0 + kWinQ - 1 : i_end;
+    const int n_tiles = (int)((kv_hi - kv_lo) / kTileK) + 1;
+
+    const uint16_t* kh = k + b * kvs0 + h * kvs1;
+    const uint16_t* vh = v + b * kvs0 + h * kvs1;
+
+    // this wave's queries: qw0 .. qw0+31 (two groups of 16)
+    const long qw0 = i0 + 32 * wv;
+    const long qw_last = qw0 + 31 < i_end ? qw0 + 31 : i_end;
+    const bool wave_active = qw0 <= i_end;
+
+    // rotated queries as B operands, kept for the whole key range
+    f16x8 qf[2][KS];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const long i = qw0 + 16 * qg + n;
+        const bool ok = i <= i_end;
+        const uint16_t* qrow = q + b * qs0 + h * qs1 + (ok ? i - q_pos0 : 0) * qs2;
+        const float2* rot = table + (ok ? i - i0 + w + kTableSlack : w + kTableSlack) * (D / 2);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            uint4 raw = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
+                           : make_uint4(0, 0, 0, 0);
+            const float4* rp = reinterpret_cast<const float4*>(rot + 16 * t + 4 * g);
+            const float4 a = rp[0], c = rp[1];
+            uint4 u;
+            u.x = rotate_pack(raw.x, a.x, a.y);
+            u.y = rotate_pack(raw.y, a.z, a.w);
+            u.z = rotate_pack(raw.z, c.x, c.y);
+            u.w = rotate_pack(raw.w, c.z, c.w);
+            qf[qg][t] = as_f16x8(u);
+        }
+    }
+
+    f32x4 acc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    WinStage<D> stage;
+    win_load<D>(stage, kh, vh, kvs2, kv_lo, kv_hi, i0, w, table);
+    win_store<D>(stage, ks, vt, kv_lo, kv_hi, i0, w, table);
+    __syncthreads();
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        const long kt = kv_lo + (long)tile * kTileK;
+        if (tile + 1 < n_tiles)
+            win_load<D>(stage, kh, vh, kvs2, kt + kTileK, kv_hi, i0, w, table);
+
+        // does any query of this wave see a key of this tile?
+        const bool work = wave_active && kt <= qw_last && kt + kTileK - 1 >= qw0 - w;
+        if (work) {
+            attn_tile<D>(ks, vt, qf, acc, m_run, l_run, scale_log2,
+                         [&](int kb, int qg, int r) {
+                             const long i = qw0 + 16 * qg + n;
+                             const long j = kt + 16 * kb + 4 * g + r;
+                             return j <= i && j >= i - w;
+                         });
+        }
+        __syncthreads();
+        if (tile + 1 < n_tiles) {
+            win_store<D>(stage, ks, vt, kt + kTileK, kv_hi, i0, w, table);
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const long i = qw0 + 16 * qg + n;
+        float l = l_run[qg];
+        l += __shfl_xor(l, 16, kWave);
+        l += __shfl_xor(l, 32, kWave);
+        if (i > i_end) continue;
+        const float inv = 1.f / l;
+        uint16_t* orow = o + b * os0 + h * os1 + (i - q_pos0) * os2;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            uint2 u;
+            u.x = pack_bf16x2(acc[db][qg][0] * inv, acc[db][qg][1] * inv);
+            u.y = pack_bf16x2(acc[db][qg][2] * inv, acc[db][qg][3] * inv);
+            *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = u;
+        }
+    }
+}
+
 hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
                          double rope_base, void* table, void* o_sr, hipStream_t st)
 {
@@ -119,6 +320,18 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
+    if (sh.bf16) {
+        dim3 grid((unsigned)((sh.nq + kWinQ - 1) / kWinQ), (unsigned)(sh.B * sh.H)), block(256);
+#define FS_WINDOW_MFMA(D)                                                                        \
+        hipLaunchKernelGGL((window_attn_mfma_kernel<D>), grid, block, 0, st, (const uint16_t*)q,  \
+                           sh.qs[0], sh.qs[1], sh.qs[2], (const uint16_t*)k, (const uint16_t*)v,  \
+                           sh.kvs[0], sh.kvs[1], sh.kvs[2], sh.H, sh.nq, sh.q_pos0, sh.w,        \
+                           (const float2*)table, scale_log2, (uint16_t*)o_sr, sh.os[0], sh.os[1], \
+                           sh.os[2])
+        if (sh.d == 64) FS_WINDOW_MFMA(64); else FS_WINDOW_MFMA(128);
+#undef FS_WINDOW_MFMA
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
 #define FS_WINDOW(E, D)                                                                          \
     hipLaunchKernelGGL((window_attn_rowwise_kernel<E, D>), grid, block, 0, st,                   \
@@ -127,11 +340,7 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
                        sh.kvs[1], sh.kvs[2], sh.H, sh.nq, sh.q_pos0, sh.w,                       \
                        (const float2*)table, scale_log2, (typename E::storage*)o_sr, sh.os[0],   \
                        sh.os[1], sh.os[2])
-    if (sh.bf16) {
-        if (sh.d == 64) FS_WINDOW(Bf16, 64); else FS_WINDOW(Bf16, 128);
-    } else {
-        if (sh.d == 64) FS_WINDOW(F32, 64); else FS_WINDOW(F32, 128);
-    }
+    if (sh.d == 64) FS_WINDOW(F32, 64); else FS_WINDOW(F32, 128);
 #undef FS_WINDOW
     return hipGetLastError();
 }
