@@ -107,6 +107,17 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Sum / max over the 16 lanes of a DPP row (lanes 16r .. 16r+15), result in
+// every lane of the row: swap neighbours, swap pairs, mirror halves, mirror row.
+__device__ __forceinline__ int row16_sum(int x)
+{
+    x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    x += __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);   // row_mirror
+    return x;
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -118,6 +129,21 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 __device__ __forceinline__ uint32_t float_key(float f) {
     uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Workgroup -> (head, query tile) mapping for 1-D grids of n_tiles * BH blocks.
+// Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8),
+// each with its own L2.  Making the head the fastest-varying index keeps every
+// block of one head on the same XCD, so that head's K/V (or kbar) working set
+// is cached in one L2 instead of all eight; query tiles advance together.
+struct TileOfBlock {
+    long bh;
+    long tile;
+};
+__device__ __forceinline__ TileOfBlock xcd_tile(long BH)
+{
+    const long bid = blockIdx.x;
+    return TileOfBlock{bid % BH, bid / BH};
 }
 
 // Candidate count of the query at absolute position i: complete cells whose

@@ -112,27 +112,65 @@ __device__ __forceinline__ int vt_slot_key(int g, int j)
     return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even, v_cvt_pk_bf16_f32), low first.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
+{
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // Pack 8 probabilities (keys pi(8g+0..7)) into the B operand of O^T += V^T P^T.
 __device__ __forceinline__ bf16x8 pack_p(const f32x4& lo, const f32x4& hi)
 {
     uint4 u;
-    u.x = pack_bf16x2(lo[0], lo[1]);
-    u.y = pack_bf16x2(lo[2], lo[3]);
-    u.z = pack_bf16x2(hi[0], hi[1]);
-    u.w = pack_bf16x2(hi[2], hi[3]);
+    u.x = cvt_pk_bf16(lo[0], lo[1]);
+    u.y = cvt_pk_bf16(lo[2], lo[3]);
+    u.z = cvt_pk_bf16(hi[0], hi[1]);
+    u.w = cvt_pk_bf16(hi[2], hi[3]);
     return as_bf16x8(u);
 }
+
+// Max / sum over the lanes l, l^16, l^32, l^48 (one query's four lane groups),
+// with the gfx950 row-swap permutes (VALU, no LDS round trip).
+__device__ __forceinline__ float xrow_max(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Rescale threshold of the online softmax (log2 units): the running reference
+// max is only raised when a tile's max exceeds it by more than this, so the
+// accumulators are rarely rescaled; probabilities stay <= 2^kLazy.
+constexpr float kLazy = 8.f;
 
 // One 64-key tile of flash attention for a wave's 32 queries (two groups of 16).
 //   ks : K tile in LDS, 64 rows of D (pitch KPitch<D>), element type of QFrag
 //   vt : V^T tile in LDS, D rows of 64 key-permuted bf16 (pitch kVtPitch)
 //   qf : the queries as B operands, qf[qg][t] = dims 32t + 8g .. + 7 of query 16 qg + n
 //   keep(kb, qg, r) : whether key 16 kb + 4 g + r is visible to query 16 qg + n
-// Updates the running max / sum (per lane, log2 domain) and O^T accumulators.
-template <int D, class Frag, class Keep>
+//                     (not evaluated when MASKED is false: every key visible)
+// Updates the reference max m_ref (log2 domain, raised lazily), the per-lane
+// partial sums and the O^T accumulators.
+template <int D, bool MASKED, class Frag, class Keep>
 __device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt,
                                           const Frag (&qf)[2][D / 32], f32x4 (&acc)[D / 16][2],
-                                          float (&m_run)[2], float (&l_run)[2], float scale_log2,
+                                          float (&m_ref)[2], float (&l_run)[2], float scale_log2,
                                           Keep keep)
 {
     constexpr int KP = KPitch<D>::value;
@@ -151,39 +189,49 @@ __device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt
         }
     }
     bf16x8 pf[2][2];
+    float corr[2];
+    bool any_rescale = false;
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
+        // max of the raw scores (scale_log2 > 0 commutes with max)
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float x = keep(kb, qg, r) ? s[kb][qg][r] * scale_log2 : -INFINITY;
-                s[kb][qg][r] = x;
-                tmax = fmaxf(tmax, x);
+                if (MASKED && !keep(kb, qg, r)) s[kb][qg][r] = -INFINITY;
+                tmax = fmaxf(tmax, s[kb][qg][r]);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        const float m_new = fmaxf(m_run[qg], tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float corr = exp2f(m_run[qg] - m_use);
+        tmax = xrow_max(tmax) * scale_log2;
+        // raise the reference only when the tile max exceeds it by > kLazy
+        const bool raise = tmax > m_ref[qg] + kLazy;
+        const float m_new = raise ? tmax : m_ref[qg];
+        corr[qg] = raise ? __builtin_amdgcn_exp2f(m_ref[qg] - m_new) : 1.f;   // 0 at the start
+        any_rescale |= raise;
+        m_ref[qg] = m_new;
+        const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float pv = exp2f(s[kb][qg][r] - m_use);
+                // v_exp_f32: results below 2^-126 flush to 0, harmless for weights
+                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][qg][r], scale_log2, neg_m));
                 s[kb][qg][r] = pv;
                 psum += pv;
             }
         }
-        l_run[qg] = l_run[qg] * corr + psum;
-        m_run[qg] = m_new;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db][qg] *= corr;
+        l_run[qg] = l_run[qg] * corr[qg] + psum;
         pf[0][qg] = pack_p(s[0][qg], s[1][qg]);
         pf[1][qg] = pack_p(s[2][qg], s[3][qg]);
+    }
+    if (__ballot(any_rescale) != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            acc[db][0] *= corr[0];
+            acc[db][1] *= corr[1];
+        }
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

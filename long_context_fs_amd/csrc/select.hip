@@ -8,8 +8,21 @@
 // neighbouring scores); the reported score is dot / sqrt(d).  The K-th largest
 // key is found exactly by a bitwise search with ballot counts, ties at the
 // threshold go to the larger cell, and the chosen cells are written ascending.
+//
+// bf16 storage (candidate lists up to 640 cells): MFMA kernel.  A workgroup
+// owns 64 consecutive queries (4 wavefronts x 16); they span at most three
+// candidate counts, so their candidates are the union of at most three keep
+// rows (or the prefix [0, n) without pruning), built in LDS with a bitmap.
+// kbar rows of the union are staged 64 at a time, each fp32 value split into
+// three bf16 parts hi + mid + lo (24 significant bits); q is exact in bf16, so
+// three exact-product MFMAs with fp32 accumulation give fp32-accurate scores.
+// The scores go to LDS as order-preserving keys; each query's row is then
+// loaded into one 16-lane DPP row (four queries per wave at a time), the K-th
+// largest key is found by the same bitwise search with 16-lane DPP sums, and
+// the chosen cells are written in slot order using ballot masks.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
+#include "mfma_tile.hpp"
 
 namespace fs {
 
@@ -120,6 +133,341 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
     }
 }
 
+
+namespace {
+
+constexpr int kSelChunk = 32;        // union cells staged per chunk (two 16-cell MFMA blocks)
+constexpr int kSelMaxCells = 32768;
+constexpr int kSelLdsMax = 160 * 1024;
+constexpr int kSelMaxKeysPerLane = 40;   // union of at most 640 cells per query block
+
+struct SelLayout {
+    int nwords, u_cap, waves, keep_w;
+    size_t off_keys, off_bitmap, off_rank, off_ulist, off_vmask, off_krows, bytes;
+};
+
+// LDS carve-up: kbar chunk split in 3 bf16 parts | keys [16*waves][u_cap] |
+// bitmap | rank | union list | row-membership masks | copy of the keep rows.
+template <int D>
+__host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int waves, int keep_w)
+{
+    SelLayout L;
+    L.nwords = (n_hi + 31) / 32;
+    L.u_cap = u_cap;
+    L.waves = waves;
+    L.keep_w = keep_w;
+    auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
+    size_t off = (size_t)3 * kSelChunk * mf::KPitch<D>::value * 2;
+    L.off_keys = off;
+    off = up16(off + (size_t)16 * waves * u_cap * 4);
+    L.off_bitmap = off;
+    off = up16(off + (size_t)L.nwords * 4);
+    L.off_rank = off;
+    off = up16(off + (size_t)L.nwords * 2);
+    L.off_ulist = off;
+    off = up16(off + (size_t)u_cap * 2);
+    L.off_vmask = off;
+    off = up16(off + (size_t)u_cap * 4);
+    L.off_krows = off;
+    off = up16(off + (size_t)3 * keep_w * 2);
+    L.bytes = off;
+    return L;
+}
+
+__device__ __forceinline__ int sel_block_excl_scan(int x, int* red, int* total)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int inc = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) red[wv] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int i = 0; i < nw; ++i) {
+        before += i < wv ? red[i] : 0;
+        all += red[i];
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+}  // namespace
+
+template <int D, int KPL>
+__global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads exactly
+    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const float* __restrict__ kbar, int H, int BH, int C, int nq, int q_pos0, int window,
+    int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
+    int keep_w, int n_lo, int n_rows, int topk, int n_hi_all, int u_cap, float inv_sqrt_d,
+    int32_t* __restrict__ idx, float* __restrict__ score)
+{
+    using namespace mf;
+    constexpr int KP = KPitch<D>::value;
+    constexpr int KS = D / 32;
+    const int waves = blockDim.x >> 6, tq = 16 * waves;
+    extern __shared__ uint4 smem_raw[];
+    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, waves, keep ? keep_w : 0);
+    char* base = reinterpret_cast<char*>(smem_raw);
+    uint16_t* kbs = reinterpret_cast<uint16_t*>(base);      // [3][kSelChunk][KP]
+    uint32_t* keys = reinterpret_cast<uint32_t*>(base + L.off_keys);
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
+    uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
+    uint32_t* vmask = reinterpret_cast<uint32_t*>(base + L.off_vmask);
+    uint16_t* krows = reinterpret_cast<uint16_t*>(base + L.off_krows);
+    __shared__ int red[4];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long t0 = tb.tile * tq;
+    const int n_rows_blk = nq - t0 < tq ? (int)(nq - t0) : tq;
+    const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
+    const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
+
+    // ---- union of the candidate sets of the block's queries --------------
+    int n_union;
+    if (keep != nullptr) {
+        const int nw = (n_b + 31) >> 5;
+        // the (at most three) keep rows, copied to LDS with all loads in flight together
+        const int r_first = n_a > 1 ? n_a : 1;            // rows of n = 0 are empty
+        const int n_kr = n_b >= r_first ? n_b - r_first + 1 : 0;
+        int kcnt[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            kcnt[j] = j < n_kr ? keep_count[bh * n_rows + (r_first + j - n_lo)] : 0;
+        for (int e0 = 0; e0 < 3 * keep_w; e0 += 4 * 256) {
+            int vals[4];
+#pragma unroll
+            for (int u4 = 0; u4 < 4; ++u4) {
+                const int e = e0 + u4 * 256 + tid;
+                const int j = e / keep_w, x = e - j * keep_w;
+                const int cnt = j == 0 ? kcnt[0] : j == 1 ? kcnt[1] : kcnt[2];
+                vals[u4] = (j < 3 && x < cnt)
+                               ? keep[(bh * n_rows + (r_first + j - n_lo)) * keep_w + x] : -1;
+            }
+#pragma unroll
+            for (int u4 = 0; u4 < 4; ++u4) {
+                const int e = e0 + u4 * 256 + tid;
+                if (e < 3 * keep_w) krows[e] = (uint16_t)(vals[u4] < 0 ? 0xFFFF : vals[u4]);
+            }
+        }
+        for (int wd = tid; wd < nw; wd += 256) bitmap[wd] = 0u;
+        __syncthreads();
+        for (int e = tid; e < 3 * keep_w; e += 256) {
+            const int c = krows[e];
+            if (c != 0xFFFF) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+        }
+        __syncthreads();
+        const int wpt = (nw + 255) / 256;   // bitmap words per thread
+        int mine = 0;
+        for (int j = 0; j < wpt; ++j) {
+            const int wd = tid * wpt + j;
+            mine += wd < nw ? __popc(bitmap[wd]) : 0;
+        }
+        int run = sel_block_excl_scan(mine, red, &n_union);
+        for (int j = 0; j < wpt; ++j) {
+            const int wd = tid * wpt + j;
+            if (wd < nw) {
+                rank[wd] = (uint16_t)run;
+                run += __popc(bitmap[wd]);
+            }
+        }
+        __syncthreads();
+        for (int wd = tid; wd < nw; wd += 256) {
+            uint32_t bits = bitmap[wd];
+            int r = rank[wd];
+            while (bits) {
+                const int bp = __ffs(bits) - 1;
+                ulist[r] = (uint16_t)(32 * wd + bp);
+                vmask[r] = 0u;
+                ++r;
+                bits &= bits - 1;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < 3 * keep_w; e += 256) {
+            const int c = krows[e];
+            if (c != 0xFFFF) {
+                const int sl = rank[c >> 5] + __popc(bitmap[c >> 5] & ((1u << (c & 31)) - 1u));
+                atomicOr(&vmask[sl], 1u << (r_first + e / keep_w - n_a));
+            }
+        }
+    } else {
+        n_union = n_b;   // candidates are the prefix [0, n_i); slot == cell
+    }
+
+    // ---- the wave's 16 queries as B operands --------------------------------
+    const int qr = 16 * wv + n;                 // this lane's query row in the block
+    const bool q_ok = qr < n_rows_blk;
+    const int n_q = q_ok ? n_candidates((long)q_pos0 + t0 + qr, window, cell, C) : 0;
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qrow = q + b * qs0 + h * qs1 + (t0 + (q_ok ? qr : 0)) * qs2;
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+            qf[t] = as_bf16x8(q_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
+                                   : make_uint4(0, 0, 0, 0));
+    }
+
+    // ---- scores S^T = Kbar Q^T over the union, kSelChunk cells per step -------
+    // The next chunk's kbar rows are loaded into registers while the current
+    // chunk's MFMAs run.
+    constexpr int kIt = kSelChunk * D / 4 / 256;     // float4 per thread per chunk
+    const float* kb_head = kbar + bh * (long)C * D;
+    float4 pre[kIt];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int f = tid + 256 * it;
+            const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
+            const int slot = c0 + cl;
+            pre[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot < n_union) {
+                const int c = keep ? ulist[slot] : slot;
+                pre[it] = *reinterpret_cast<const float4*>(kb_head + (long)c * D + d4);
+            }
+        }
+    };
+    __syncthreads();                         // ulist complete
+    load_chunk(0);
+    for (int c0 = 0; c0 < n_union; c0 += kSelChunk) {
+        __syncthreads();                     // previous chunk's MFMA reads are done
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int f = tid + 256 * it;
+            const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
+            const float r[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
+            uint32_t part[3][2];
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+                float a0 = r[e], a1 = r[e + 1];
+                const uint32_t h0 = f32_to_bf16(a0), h1 = f32_to_bf16(a1);
+                a0 -= bf16_to_f32(h0);
+                a1 -= bf16_to_f32(h1);
+                const uint32_t m0 = f32_to_bf16(a0), m1 = f32_to_bf16(a1);
+                a0 -= bf16_to_f32(m0);
+                a1 -= bf16_to_f32(m1);
+                part[0][e / 2] = h0 | (h1 << 16);
+                part[1][e / 2] = m0 | (m1 << 16);
+                part[2][e / 2] = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
+            }
+#pragma unroll
+            for (int pp = 0; pp < 3; ++pp)
+                *reinterpret_cast<uint2*>(kbs + (pp * kSelChunk + cl) * KP + d4) =
+                    make_uint2(part[pp][0], part[pp][1]);
+        }
+        __syncthreads();
+        if (c0 + kSelChunk < n_union) load_chunk(c0 + kSelChunk);
+#pragma unroll
+        for (int bb = 0; bb < kSelChunk / 16; ++bb) {
+            const int slot0 = c0 + 16 * bb;
+            if (slot0 >= n_union) break;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+#pragma unroll
+                for (int pp = 0; pp < 3; ++pp) {
+                    const bf16x8 a = as_bf16x8(
+                        lds_load16(kbs + (pp * kSelChunk + 16 * bb + n) * KP + 32 * t + 8 * g));
+                    acc = mfma(a, qf[t], acc);
+                }
+            }
+            uint32_t kk[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int slot = slot0 + 4 * g + r;
+                bool ok = slot < n_union && n_q > 0;
+                if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
+                kk[r] = ok ? float_key(acc[r]) : 0u;
+            }
+            uint32_t* krow = keys + (size_t)qr * u_cap + slot0 + 4 * g;
+            if (slot0 + 4 * g + 3 < u_cap) {
+                *reinterpret_cast<uint4*>(krow) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (slot0 + 4 * g + r < u_cap) krow[r] = kk[r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- per query: exact top-K, written in ascending slot (= cell) order ----
+    // Four queries at a time, one per 16-lane DPP row; lane c of a row holds the
+    // keys of slots c, c+16, c+32, ... of its query in registers.
+    const int rq = lane >> 4, c16 = lane & 15;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int row_b = 16 * wv + 4 * pass + rq;
+        const bool row_ok = row_b < n_rows_blk;
+        const uint32_t* row = keys + (size_t)row_b * u_cap;
+        uint32_t kv[KPL];         // keys past the union are 0 and never counted
+        int nv = 0;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            const int j = c16 + 16 * e;
+            kv[e] = j < n_union ? row[j] : 0u;
+            nv += kv[e] != 0u;
+        }
+        nv = row16_sum(nv);
+        const int kq = nv < topk ? nv : topk;
+        // kq-th largest key: largest thr with #{key >= thr} >= kq
+        uint32_t thr = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) cnt += kv[e] >= cand;
+            if (row16_sum(cnt) >= kq) thr = cand;
+        }
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            gt += kv[e] > thr;
+            eq += kv[e] == thr;
+        }
+        const int n_gt = row16_sum(gt), n_eq = row16_sum(eq);
+        const int need_eq = kq - n_gt;           // equal keys kept: those in the largest slots
+        const long orow = bh * nq + t0 + (row_ok ? row_b : 0);
+        int32_t* out_i = idx + orow * topk;
+        float* out_s = score ? score + orow * topk : nullptr;
+        const uint32_t below = (1u << c16) - 1u;
+        int written = 0, eq_seen = 0;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            const uint32_t k = kv[e];
+            const bool is_eq = kq > 0 && k != 0u && k == thr;
+            const uint32_t me = (uint32_t)(__ballot(is_eq) >> (16 * rq)) & 0xFFFFu;
+            const bool kept = kq > 0 && k != 0u &&
+                              (k > thr || (is_eq && eq_seen + __popc(me & below) >= n_eq - need_eq));
+            const uint32_t mk = (uint32_t)(__ballot(kept) >> (16 * rq)) & 0xFFFFu;
+            if (kept && row_ok) {
+                const int pos = written + __popc(mk & below);
+                const int j = c16 + 16 * e;
+                out_i[pos] = keep ? ulist[j] : j;
+                if (out_s) {
+                    const float dot = __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+                    out_s[pos] = dot * inv_sqrt_d;
+                }
+            }
+            written += __popc(mk);
+            eq_seen += __popc(me);
+        }
+        if (row_ok) {
+            for (int t = kq + c16; t < topk; t += 16) {
+                out_i[t] = -1;
+                if (out_s) out_s[t] = 0.f;
+            }
+        }
+    }
+}
+
 hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const int32_t* keep,
                          const int32_t* keep_count, int keep_w, int n_lo, int n_rows, int topk,
                          int32_t* idx, float* score, hipStream_t st)
@@ -131,6 +479,38 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
         long i = (long)sh.q_pos0 + sh.nq - 1;
         if (i >= sh.w) n_hi = (int)((i - sh.w) / sh.s);
         if (n_hi > sh.C) n_hi = sh.C;
+    }
+    // MFMA path: bf16 storage; the block's scores must fit in LDS.
+    {
+        const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
+        const int uc = u_cap > 0 ? u_cap : 1;
+        const int waves = 4;
+        const int kw = keep ? keep_w : 0;
+        const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, waves, kw).bytes
+                                      : sel_layout<128>(n_hi, uc, waves, kw).bytes;
+        if (sh.bf16 && lds <= (size_t)kSelLdsMax && sh.C <= kSelMaxCells &&
+            uc <= 16 * kSelMaxKeysPerLane) {
+            const int tq = 16 * waves;
+            dim3 grid((unsigned)((sh.nq + tq - 1) / tq * sh.B * sh.H));
+            const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
+            const int kpl_need = (uc + 15) / 16;
+#define FS_SELECT_MFMA(D, KPL)                                                                  \
+            hipLaunchKernelGGL((select_topk_mfma_kernel<D, KPL>), grid, dim3(64 * waves), lds,    \
+                               st, (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, sh.H, \
+                               sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,            \
+                               keep_count, keep_w,                                               \
+                               n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, idx, score)
+#define FS_SELECT_KPL(D)                                                                        \
+            if (kpl_need <= 4) FS_SELECT_MFMA(D, 4);                                            \
+            else if (kpl_need <= 8) FS_SELECT_MFMA(D, 8);                                       \
+            else if (kpl_need <= 16) FS_SELECT_MFMA(D, 16);                                     \
+            else if (kpl_need <= 24) FS_SELECT_MFMA(D, 24);                                     \
+            else FS_SELECT_MFMA(D, 40);
+            if (sh.d == 64) { FS_SELECT_KPL(64) } else { FS_SELECT_KPL(128) }
+#undef FS_SELECT_KPL
+#undef FS_SELECT_MFMA
+            return hipGetLastError();
+        }
     }
     const int cap = keep ? keep_w : (n_hi > 0 ? n_hi : 1);
     // As many waves (query rows) per block as fit in 64 KiB of LDS.

@@ -171,35 +171,31 @@ struct SpStage {
     uint4 v[4];
 };
 
-// Token row of tile key r (0..63) for union tile u, or -1 past the union.
-__device__ __forceinline__ long sp_row(const uint16_t* ulist, int n_union, int u, int r)
-{
-    const int slot = 2 * u + (r >> 5);
-    return slot < n_union ? (long)ulist[slot] * 32 + (r & 31) : -1;
-}
-
 template <int D>
 __device__ __forceinline__ void sp_load(SpStage<D>& st, const uint16_t* __restrict__ kh,
                                         const uint16_t* __restrict__ vh, int64_t kvs2,
                                         const uint16_t* ulist, int n_union, int u)
 {
     const int tid = threadIdx.x;
+    // the tile's two cells (the second may lie past the union)
+    const bool ok0 = 2 * u < n_union, ok1 = 2 * u + 1 < n_union;
+    const int64_t row0 = ok0 ? (int64_t)ulist[2 * u] * 32 * kvs2 : 0;
+    const int64_t row1 = ok1 ? (int64_t)ulist[2 * u + 1] * 32 * kvs2 : 0;
 #pragma unroll
     for (int it = 0; it < SpStage<D>::KC; ++it) {
         const int c = tid + 256 * it;
         const int kr = c / (D / 8), part = c % (D / 8);
-        const long j = sp_row(ulist, n_union, u, kr);
-        st.k[it] = j >= 0 ? *reinterpret_cast<const uint4*>(kh + j * kvs2 + part * 8)
-                          : make_uint4(0, 0, 0, 0);
+        const bool ok = (kr >> 5) ? ok1 : ok0;
+        const int64_t off = ((kr >> 5) ? row1 : row0) + (kr & 31) * kvs2 + part * 8;
+        st.k[it] = ok ? *reinterpret_cast<const uint4*>(kh + off) : make_uint4(0, 0, 0, 0);
     }
     if (tid < 2 * D) {
         const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+        const bool ok = grp ? ok1 : ok0;
+        const uint16_t* vb = vh + (grp ? row1 : row0) + (16 * hh + 4 * g) * kvs2 + dc * 8;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const long j = sp_row(ulist, n_union, u, 32 * grp + 16 * hh + 4 * g + r);
-            st.v[r] = j >= 0 ? *reinterpret_cast<const uint4*>(vh + j * kvs2 + dc * 8)
-                             : make_uint4(0, 0, 0, 0);
-        }
+        for (int r = 0; r < 4; ++r)
+            st.v[r] = ok ? *reinterpret_cast<const uint4*>(vb + r * kvs2) : make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -226,7 +222,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t kvs0, int64_t kvs1,
-    int64_t kvs2, int H, int nq, int C, const int32_t* __restrict__ idx, int topk,
+    int64_t kvs2, int H, int BH, int nq, int C, const int32_t* __restrict__ idx, int topk,
     float scale_log2, float rms_eps, uint16_t* __restrict__ o, int64_t os0, int64_t os1,
     int64_t os2)
 {
@@ -245,9 +241,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
-    const long bh = blockIdx.y;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const long t0 = (long)blockIdx.x * kSpQ;
+    const long t0 = tb.tile * kSpQ;
     const int n_rows = nq - t0 < kSpQ ? (int)(nq - t0) : kSpQ;
     const int32_t* idx_blk = idx + (bh * nq + t0) * (long)topk;
 
@@ -292,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
         slots[e] = sl;
     }
     __syncthreads();
-    if (tid < n_rows) {      // each query's slots ascending (insertion sort; already sorted if idx is)
+    if (tid < n_rows) {      // each query's slots ascending and distinct (sorted already if idx is)
         uint16_t* row = slots + tid * topk;
         for (int a = 1; a < topk; ++a) {
             const uint16_t x = row[a];
@@ -303,6 +300,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
             }
             row[z + 1] = x;
         }
+        int wr = 0;
+        for (int a = 0; a < topk; ++a)
+            if (a == 0 || row[a] != row[a - 1] || row[a] == kNoSlot) row[wr++] = row[a];
+        for (; wr < topk; ++wr) row[wr] = kNoSlot;
     }
     __syncthreads();
 
@@ -339,21 +340,22 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     __syncthreads();
     for (int u = 0; u < n_tiles; ++u) {
         if (u + 1 < n_tiles) sp_load<D>(stage, kh, vh, kvs2, ulist, n_union, u + 1);
+        // slot lists are ascending and distinct, so the walk advances at most
+        // once per slot and never skips a listed slot
         bool sel[2][2];
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
             const int r = 32 * wv + 16 * qg + n;
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const int slot = 2 * u + c2;
-                while (nxt[qg] < slot) nxt[qg] = ++ptr[qg] < topk ? slots[r * topk + ptr[qg]] : kNoSlot;
-                sel[qg][c2] = nxt[qg] == slot;
+                sel[qg][c2] = nxt[qg] == 2 * u + c2;
+                if (sel[qg][c2]) nxt[qg] = ++ptr[qg] < topk ? slots[r * topk + ptr[qg]] : kNoSlot;
             }
         }
         const bool any = __ballot(sel[0][0] || sel[0][1] || sel[1][0] || sel[1][1]) != 0;
         if (any) {
-            attn_tile<D>(ks, vt, qf, acc, m_run, l_run, scale_log2,
-                         [&](int kb, int qg, int) { return sel[qg][kb >> 1]; });
+            attn_tile<D, true>(ks, vt, qf, acc, m_run, l_run, scale_log2,
+                               [&](int kb, int qg, int) { return sel[qg][kb >> 1]; });
         }
         __syncthreads();
         if (u + 1 < n_tiles) {
@@ -366,9 +368,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const int r = 32 * wv + 16 * qg + n;
-        float l = l_run[qg];
-        l += __shfl_xor(l, 16, kWave);
-        l += __shfl_xor(l, 32, kWave);
+        const float l = xrow_sum(l_run[qg]);
         const float inv_l = l > 0.f ? 1.f / l : 0.f;
         float ss = 0.f;
 #pragma unroll
@@ -377,16 +377,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) ss = fmaf(acc[db][qg][e], acc[db][qg][e], ss);
         }
-        ss += __shfl_xor(ss, 16, kWave);
-        ss += __shfl_xor(ss, 32, kWave);
+        ss = xrow_sum(ss);
         const float inv_rms = 1.f / sqrtf(ss / (float)D + rms_eps);
         if (r >= n_rows) continue;
         uint16_t* orow = o + b * os0 + h * os1 + (t0 + r) * os2;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             uint2 w2;
-            w2.x = pack_bf16x2(acc[db][qg][0] * inv_rms, acc[db][qg][1] * inv_rms);
-            w2.y = pack_bf16x2(acc[db][qg][2] * inv_rms, acc[db][qg][3] * inv_rms);
+            w2.x = cvt_pk_bf16(acc[db][qg][0] * inv_rms, acc[db][qg][1] * inv_rms);
+            w2.y = cvt_pk_bf16(acc[db][qg][2] * inv_rms, acc[db][qg][3] * inv_rms);
             *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = w2;
         }
     }
@@ -400,12 +399,14 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
     const size_t lds = sh.d == 64 ? sp_layout<64>(sh.C, topk).bytes
                                   : sp_layout<128>(sh.C, topk).bytes;
     if (sh.bf16 && sh.C <= kSpMaxCells && lds <= 65536) {
-        dim3 grid((unsigned)((sh.nq + kSpQ - 1) / kSpQ), (unsigned)(sh.B * sh.H)), block(256);
+        const long n_tiles = (sh.nq + kSpQ - 1) / kSpQ;
+        dim3 grid((unsigned)(n_tiles * sh.B * sh.H)), block(256);
 #define FS_SPARSE_MFMA(D)                                                                         \
         hipLaunchKernelGGL((sparse_attn_mfma_kernel<D>), grid, block, lds, st,                    \
                            (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2],                      \
                            (const uint16_t*)k, (const uint16_t*)v, sh.kvs[0], sh.kvs[1],          \
-                           sh.kvs[2], sh.H, sh.nq, sh.C, idx, topk, scale_log2, rms_eps,          \
+                           sh.kvs[2], sh.H, sh.B * sh.H, sh.nq, sh.C, idx, topk, scale_log2,      \
+                           rms_eps,                                                               \
                            (uint16_t*)o_lr, sh.os[0], sh.os[1], sh.os[2])
         if (sh.d == 64) FS_SPARSE_MFMA(64); else FS_SPARSE_MFMA(128);
 #undef FS_SPARSE_MFMA

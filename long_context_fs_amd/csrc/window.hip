@@ -207,7 +207,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t kvs0, int64_t kvs1,
-    int64_t kvs2, int H, int nq, int q_pos0, int w, const float2* __restrict__ table,
+    int64_t kvs2, int H, int BH, int nq, int q_pos0, int w, const float2* __restrict__ table,
     float scale_log2, uint16_t* __restrict__ o, int64_t os0, int64_t os1, int64_t os2)
 {
     using namespace mf;
@@ -219,9 +219,10 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
-    const long bh = blockIdx.y;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const long i0 = (long)q_pos0 + (long)blockIdx.x * kWinQ;
+    const long i0 = (long)q_pos0 + tb.tile * kWinQ;
     const long i_end = (long)q_pos0 + nq - 1;                 // last query position
     const long kv_lo = i0 - w > 0 ? i0 - w : 0;
     const long kv_hi = i0 + kWinQ - 1 < i_end ? i0 + kWinQ - 1 : i_end;
@@ -276,12 +277,17 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
         // does any query of this wave see a key of this tile?
         const bool work = wave_active && kt <= qw_last && kt + kTileK - 1 >= qw0 - w;
         if (work) {
-            attn_tile<D>(ks, vt, qf, acc, m_run, l_run, scale_log2,
-                         [&](int kb, int qg, int r) {
-                             const long i = qw0 + 16 * qg + n;
-                             const long j = kt + 16 * kb + 4 * g + r;
-                             return j <= i && j >= i - w;
-                         });
+            // every key of the tile inside every query's window: no masking needed
+            const bool full = kt >= qw_last - w && kt + kTileK - 1 <= qw0;
+            auto keep = [&](int kb, int qg, int r) {
+                const long i = qw0 + 16 * qg + n;
+                const long j = kt + 16 * kb + 4 * g + r;
+                return j <= i && j >= i - w;
+            };
+            if (full)
+                attn_tile<D, false>(ks, vt, qf, acc, m_run, l_run, scale_log2, keep);
+            else
+                attn_tile<D, true>(ks, vt, qf, acc, m_run, l_run, scale_log2, keep);
         }
         __syncthreads();
         if (tile + 1 < n_tiles) {
@@ -293,17 +299,15 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const long i = qw0 + 16 * qg + n;
-        float l = l_run[qg];
-        l += __shfl_xor(l, 16, kWave);
-        l += __shfl_xor(l, 32, kWave);
+        const float l = xrow_sum(l_run[qg]);
         if (i > i_end) continue;
         const float inv = 1.f / l;
         uint16_t* orow = o + b * os0 + h * os1 + (i - q_pos0) * os2;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             uint2 u;
-            u.x = pack_bf16x2(acc[db][qg][0] * inv, acc[db][qg][1] * inv);
-            u.y = pack_bf16x2(acc[db][qg][2] * inv, acc[db][qg][3] * inv);
+            u.x = cvt_pk_bf16(acc[db][qg][0] * inv, acc[db][qg][1] * inv);
+            u.y = cvt_pk_bf16(acc[db][qg][2] * inv, acc[db][qg][3] * inv);
             *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = u;
         }
     }
@@ -321,11 +325,13 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
     if (err != hipSuccess) return err;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
     if (sh.bf16) {
-        dim3 grid((unsigned)((sh.nq + kWinQ - 1) / kWinQ), (unsigned)(sh.B * sh.H)), block(256);
+        const long n_tiles = (sh.nq + kWinQ - 1) / kWinQ;
+        dim3 grid((unsigned)(n_tiles * sh.B * sh.H)), block(256);
 #define FS_WINDOW_MFMA(D)                                                                        \
         hipLaunchKernelGGL((window_attn_mfma_kernel<D>), grid, block, 0, st, (const uint16_t*)q,  \
                            sh.qs[0], sh.qs[1], sh.qs[2], (const uint16_t*)k, (const uint16_t*)v,  \
-                           sh.kvs[0], sh.kvs[1], sh.kvs[2], sh.H, sh.nq, sh.q_pos0, sh.w,        \
+                           sh.kvs[0], sh.kvs[1], sh.kvs[2], sh.H, sh.B * sh.H, sh.nq, sh.q_pos0,  \
+                           sh.w,                                                                  \
                            (const float2*)table, scale_log2, (uint16_t*)o_sr, sh.os[0], sh.os[1], \
                            sh.os[2])
         if (sh.d == 64) FS_WINDOW_MFMA(64); else FS_WINDOW_MFMA(128);
