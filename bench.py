@@ -68,6 +68,14 @@ def algorithmic_work(wl, keep_count=None, n_lo=0):
     }
 
 
+def kernel_source_sha(phase):
+    """Hash of a phase's kernel source and the device headers it includes."""
+    h = hashlib.sha256()
+    for name in (PHASE_SRC[phase], "mfma_tile.hpp", "fs_device.hpp"):
+        h.update(open(os.path.join(ROOT, "long_context_fs_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def stored_traffic(phase):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel
     source is unchanged since they were taken."""
@@ -78,9 +86,7 @@ def stored_traffic(phase):
     ent = data.get(phase)
     if not ent:
         return None
-    src = os.path.join(ROOT, "long_context_fs_amd", "csrc", PHASE_SRC[phase])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if ent.get("src_sha") != sha:
+    if ent.get("src_sha") != kernel_source_sha(phase):
         return None
     return ent.get("bytes_per_launch")
 
@@ -153,7 +159,7 @@ def roofline(res):
     t = res["phase_ms"][ph] * 1e-3
     eng = PHASE_ENGINE[ph]
     w = res["work"][ph]
-    traffic = stored_traffic(ph)
+    traffic = stored_traffic(ph) if res["wl"].name == PRIMARY else None
     if eng == "hbm":
         ach = w["bytes"] / t / 1e9
         out = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"], "unit": "GB/s"}
@@ -206,6 +212,92 @@ def cpu_baseline(name, budget_s=12.0):
                       f"({t_sum:.2f} s, amortised over {wl.n_q} queries)"}
 
 
+# ---- profiling helpers (rocprofv3 drives these; the summaries go to profiles/) ----
+def run_phase(name, phase, reps, torch, fs):
+    """One full forward, then `reps` launches of a single phase (counter runs)."""
+    wl = synth.get_workload(name)
+    x = synth.generate(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v"))
+    alpha = torch.from_numpy(x["alpha"]).to(dev)
+    f = fs.FsForward.for_workload(wl, device=dev)
+    f(q, k, v, alpha)
+    p = f.prob
+    calls = {
+        "summaries": lambda: fs.fs_cell_summaries(p, k, f.kbar, f.amax),
+        "prune": lambda: fs.fs_prune_prefix(p, f.amax, f.n_recent, f.budget, f.keep,
+                                            f.keep_count),
+        "select": lambda: fs.fs_select_topk(p, q, f.kbar, f.keep, f.keep_count, f.keep_w,
+                                            f.topk, f.idx, None),
+        "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),
+        "sparse": lambda: fs.fs_sparse_attn(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_lr),
+        "combine": lambda: fs.fs_combine(p, f.o_sr, f.o_lr, alpha, f.o),
+    }
+    for _ in range(reps):
+        calls[phase]()
+    torch.cuda.synchronize()
+    print(f"phase {phase} of {wl.name}: {reps} launches", flush=True)
+
+
+def run_copy(mib, reps, torch):
+    """A plain device copy of a known size: calibrates the HBM byte counters."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copy {mib} MiB x {reps}", flush=True)
+
+
+def _rocpd_rows(db, query):
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        return list(con.execute(query))
+    finally:
+        con.close()
+
+
+def kernel_stats(db):
+    """[(name, calls, average us, total us)] from a --kernel-trace run."""
+    return [(r[0], int(r[1]), float(r[3]), float(r[2])) for r in _rocpd_rows(
+        db, "select name, total_calls, total_duration, average from top_kernels")]
+
+
+def counter_means(db, substr):
+    """{counter: mean over dispatches of the kernel (summed over hardware units)}."""
+    per = {}
+    for disp, kname, cname, val in _rocpd_rows(
+            db, "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+        if substr in kname:
+            per.setdefault(disp, {}).setdefault(cname, 0.0)
+            per[disp][cname] += val
+    if not per:
+        return {}
+    names = set().union(*per.values())
+    return {c: sum(d.get(c, 0.0) for d in per.values()) / len(per) for c in names}
+
+
+def write_traffic(phase, kernel_substr, fetch_db, write_db, copy_fetch_db, copy_write_db,
+                  copy_mib):
+    """Record HBM bytes per launch of one phase's kernel in profiles/traffic.json."""
+    copy_bytes = copy_mib * (1 << 20)
+    f_copy = counter_means(copy_fetch_db, "copy")["FETCH_SIZE"] * 1024 / copy_bytes
+    w_copy = counter_means(copy_write_db, "copy")["WRITE_SIZE"] * 1024 / copy_bytes
+    fetch = counter_means(fetch_db, kernel_substr)["FETCH_SIZE"] * 1024 / f_copy
+    write = counter_means(write_db, kernel_substr)["WRITE_SIZE"] * 1024 / w_copy
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[phase] = {"kernel": kernel_substr, "src_sha": kernel_source_sha(phase),
+        "fetch_bytes_per_launch": fetch,
+        "write_bytes_per_launch": write, "bytes_per_launch": fetch + write,
+        "copy_factor_fetch": f_copy, "copy_factor_write": w_copy, "copy_mib": copy_mib}
+    json.dump(data, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(data[phase]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,7 +305,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true")
+    ap.add_argument("--phase", help="profiling: launch only this phase --reps times")
+    ap.add_argument("--workload", default=PRIMARY, help="workload of --phase")
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--copy-mib", type=int, help="profiling: plain copy of this many MiB")
+    ap.add_argument("--kernel-stats", metavar="DB", help="print kernel stats of a rocpd db")
+    ap.add_argument("--write-traffic", nargs=6, metavar=("PHASE", "KERNEL", "FETCH_DB",
+                    "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"))
     args = ap.parse_args()
+    if args.kernel_stats:
+        for name, calls, avg, tot in kernel_stats(args.kernel_stats):
+            print(f"{avg:12.2f} us avg  {calls:5d} calls  {tot / 1e3:10.3f} ms total  {name[:110]}")
+        return
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, copy_mib=args.copy_mib or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
               "Heads and batch shard across GPUs with no communication; that path is not built.",
@@ -226,6 +332,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_mib and not args.phase:
+        run_copy(args.copy_mib, args.reps, torch)
+        return
+    if args.phase:
+        run_phase(args.workload, args.phase, args.reps, torch, fs)
+        return
 
     main_res = run_workload(PRIMARY, args.steps, args.warmup, torch, fs)
     also = {}
