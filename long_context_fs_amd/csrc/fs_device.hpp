@@ -118,6 +118,33 @@ __device__ __forceinline__ int row16_sum(int x)
     return x;
 }
 
+// Sum over the 4 consecutive lanes of a quad, result in every lane of the quad.
+__device__ __forceinline__ int quad_sum(int x)
+{
+    x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    return x;
+}
+
+// Exclusive prefix sum over the lanes of a quad (lane 4q+j gets the sum of lanes 4q..4q+j-1).
+__device__ __forceinline__ int quad_excl_prefix(int x)
+{
+    const int j = __lane_id() & 3;
+    const int x0 = __builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, false);   // lane 4q
+    const int x1 = __builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, false);   // lane 4q+1
+    const int x2 = __builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, false);   // lane 4q+2
+    return (j > 0 ? x0 : 0) + (j > 1 ? x1 : 0) + (j > 2 ? x2 : 0);
+}
+
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t x)
+{
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
+    return x;
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -17,9 +17,10 @@
 // three bf16 parts hi + mid + lo (24 significant bits); q is exact in bf16, so
 // three exact-product MFMAs with fp32 accumulation give fp32-accurate scores.
 // The scores go to LDS as order-preserving keys; each query's row is then
-// loaded into one 16-lane DPP row (four queries per wave at a time), the K-th
-// largest key is found by the same bitwise search with 16-lane DPP sums, and
-// the chosen cells are written in slot order using ballot masks.
+// loaded into 4 consecutive lanes (a DPP quad; all 16 queries of a wave at
+// once), the K-th largest key is found by the same bitwise search with quad
+// DPP sums, and the chosen cells are written in slot order from one exclusive
+// prefix over the quad.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 #include "mfma_tile.hpp"
@@ -139,7 +140,7 @@ namespace {
 constexpr int kSelChunk = 32;        // union cells staged per chunk (two 16-cell MFMA blocks)
 constexpr int kSelMaxCells = 32768;
 constexpr int kSelLdsMax = 160 * 1024;
-constexpr int kSelMaxKeysPerLane = 40;   // union of at most 640 cells per query block
+constexpr int kSelMaxKeysPerLane = 132;  // quad layout: union of at most 528 cells per block
 
 struct SelLayout {
     int nwords, u_cap, waves, keep_w;
@@ -197,7 +198,7 @@ __device__ __forceinline__ int sel_block_excl_scan(int x, int* red, int* total)
 
 }  // namespace
 
-template <int D, int KPL>
+template <int D, int KPQ>
 __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads exactly
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const float* __restrict__ kbar, int H, int BH, int C, int nq, int q_pos0, int window,
@@ -344,19 +345,21 @@ __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads
             const int f = tid + 256 * it;
             const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
             const float r[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
+            // x = hi + mid + lo exactly: each residual has at most 16 (then 8)
+            // significant bits, so the fp32 subtractions are exact.
             uint32_t part[3][2];
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
                 float a0 = r[e], a1 = r[e + 1];
-                const uint32_t h0 = f32_to_bf16(a0), h1 = f32_to_bf16(a1);
-                a0 -= bf16_to_f32(h0);
-                a1 -= bf16_to_f32(h1);
-                const uint32_t m0 = f32_to_bf16(a0), m1 = f32_to_bf16(a1);
-                a0 -= bf16_to_f32(m0);
-                a1 -= bf16_to_f32(m1);
-                part[0][e / 2] = h0 | (h1 << 16);
-                part[1][e / 2] = m0 | (m1 << 16);
-                part[2][e / 2] = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
+                const uint32_t h = cvt_pk_bf16(a0, a1);
+                a0 -= __uint_as_float(h << 16);
+                a1 -= __uint_as_float(h & 0xFFFF0000u);
+                const uint32_t m = cvt_pk_bf16(a0, a1);
+                a0 -= __uint_as_float(m << 16);
+                a1 -= __uint_as_float(m & 0xFFFF0000u);
+                part[0][e / 2] = h;
+                part[1][e / 2] = m;
+                part[2][e / 2] = cvt_pk_bf16(a0, a1);
             }
 #pragma unroll
             for (int pp = 0; pp < 3; ++pp)
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads
                 kk[r] = ok ? float_key(acc[r]) : 0u;
             }
             uint32_t* krow = keys + (size_t)qr * u_cap + slot0 + 4 * g;
-            if (slot0 + 4 * g + 3 < u_cap) {
+            if (slot0 + 4 * g + 3 < u_cap) {   // u_cap is a multiple of 16
                 *reinterpret_cast<uint4*>(krow) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
             } else {
 #pragma unroll
@@ -400,67 +403,95 @@ __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads
     __syncthreads();
 
     // ---- per query: exact top-K, written in ascending slot (= cell) order ----
-    // Four queries at a time, one per 16-lane DPP row; lane c of a row holds the
-    // keys of slots c, c+16, c+32, ... of its query in registers.
-    const int rq = lane >> 4, c16 = lane & 15;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int row_b = 16 * wv + 4 * pass + rq;
+    // Quad layout: lanes 4j .. 4j+3 of wave w hold query 16w + j; lane 4j+sub
+    // holds the contiguous slots [sub*kpq, (sub+1)*kpq) of that query's keys.
+    {
+        const int qj = lane >> 2, sub = lane & 3;
+        const int row_b = 16 * wv + qj;
         const bool row_ok = row_b < n_rows_blk;
-        const uint32_t* row = keys + (size_t)row_b * u_cap;
-        uint32_t kv[KPL];         // keys past the union are 0 and never counted
+        const uint32_t* krow = keys + (size_t)row_b * u_cap + sub * KPQ;
+        const int slot0 = sub * KPQ;
+        uint32_t kv[KPQ];           // keys past the union are 0 and never counted
+#pragma unroll
+        for (int e = 0; e < KPQ; e += 4) {
+            const uint4 w4 = *reinterpret_cast<const uint4*>(krow + e);
+            kv[e] = slot0 + e < n_union ? w4.x : 0u;
+            kv[e + 1] = slot0 + e + 1 < n_union ? w4.y : 0u;
+            kv[e + 2] = slot0 + e + 2 < n_union ? w4.z : 0u;
+            kv[e + 3] = slot0 + e + 3 < n_union ? w4.w : 0u;
+        }
         int nv = 0;
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-            const int j = c16 + 16 * e;
-            kv[e] = j < n_union ? row[j] : 0u;
-            nv += kv[e] != 0u;
-        }
-        nv = row16_sum(nv);
+        for (int e = 0; e < KPQ; ++e) nv += kv[e] != 0u;
+        nv = quad_sum(nv);
         const int kq = nv < topk ? nv : topk;
-        // kq-th largest key: largest thr with #{key >= thr} >= kq
+        // kq-th largest key: the largest thr with #{key >= thr} >= kq
         uint32_t thr = 0;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = thr | (1u << bit);
-            int cnt = 0;
+            int c0 = 0, c1 = 0;                   // two chains: shorter dependency
 #pragma unroll
-            for (int e = 0; e < KPL; ++e) cnt += kv[e] >= cand;
-            if (row16_sum(cnt) >= kq) thr = cand;
+            for (int e = 0; e < KPQ; e += 2) {
+                c0 += kv[e] >= cand;
+                c1 += kv[e + 1] >= cand;
+            }
+            if (quad_sum(c0 + c1) >= kq) thr = cand;
         }
-        int gt = 0, eq = 0;
+        // thr >= 1 whenever kq > 0, so "key >= thr" and "key > thr" imply a valid key
+        int ge = 0, gt = 0;
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) {
+        for (int e = 0; e < KPQ; ++e) {
+            ge += kv[e] >= thr;
             gt += kv[e] > thr;
-            eq += kv[e] == thr;
         }
-        const int n_gt = row16_sum(gt), n_eq = row16_sum(eq);
-        const int need_eq = kq - n_gt;           // equal keys kept: those in the largest slots
+        const int eq = ge - gt;
+        const int n_gt = quad_sum(gt), n_eq = quad_sum(eq);
+        const int need_eq = kq - n_gt;            // equal keys kept: those in the largest slots
         const long orow = bh * nq + t0 + (row_ok ? row_b : 0);
         int32_t* out_i = idx + orow * topk;
         float* out_s = score ? score + orow * topk : nullptr;
-        const uint32_t below = (1u << c16) - 1u;
-        int written = 0, eq_seen = 0;
+        auto emit = [&](int p, uint32_t k, int j) {
+            out_i[p] = keep ? ulist[j] : j;
+            if (out_s) {
+                const float dot = __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+                out_s[p] = dot * inv_sqrt_d;
+            }
+        };
+        uint32_t thr_o = thr;
+        asm volatile("" : "+v"(thr_o));           // fresh compares below, not kept masks
+        if (n_eq == need_eq) {
+            // no tie across the boundary: exactly the keys >= thr
+            int pos = quad_excl_prefix(ge);
+            if (row_ok && kq > 0) {
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-            const uint32_t k = kv[e];
-            const bool is_eq = kq > 0 && k != 0u && k == thr;
-            const uint32_t me = (uint32_t)(__ballot(is_eq) >> (16 * rq)) & 0xFFFFu;
-            const bool kept = kq > 0 && k != 0u &&
-                              (k > thr || (is_eq && eq_seen + __popc(me & below) >= n_eq - need_eq));
-            const uint32_t mk = (uint32_t)(__ballot(kept) >> (16 * rq)) & 0xFFFFu;
-            if (kept && row_ok) {
-                const int pos = written + __popc(mk & below);
-                const int j = c16 + 16 * e;
-                out_i[pos] = keep ? ulist[j] : j;
-                if (out_s) {
-                    const float dot = __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-                    out_s[pos] = dot * inv_sqrt_d;
+                for (int e = 0; e < KPQ; ++e) {
+                    if (kv[e] >= thr_o) emit(pos++, kv[e], slot0 + e);
                 }
             }
-            written += __popc(mk);
-            eq_seen += __popc(me);
+        } else {
+            // ties at the threshold: keep the need_eq equal keys with the largest slots
+            int eq_rank = quad_excl_prefix(eq);
+            int kept_here = 0;
+#pragma unroll
+            for (int e = 0; e < KPQ; ++e) {
+                const bool is_eq = kv[e] == thr_o;
+                kept_here += kv[e] > thr_o || (is_eq && eq_rank >= n_eq - need_eq);
+                eq_rank += is_eq;
+            }
+            int pos = quad_excl_prefix(kept_here);
+            eq_rank = quad_excl_prefix(eq);
+            if (row_ok && kq > 0) {
+#pragma unroll
+                for (int e = 0; e < KPQ; ++e) {
+                    const bool is_eq = kv[e] == thr_o;
+                    const bool kept = kv[e] > thr_o || (is_eq && eq_rank >= n_eq - need_eq);
+                    eq_rank += is_eq;
+                    if (kept) emit(pos++, kv[e], slot0 + e);
+                }
+            }
         }
         if (row_ok) {
-            for (int t = kq + c16; t < topk; t += 16) {
+            for (int t = kq + sub; t < topk; t += 4) {
                 out_i[t] = -1;
                 if (out_s) out_s[t] = 0.f;
             }
@@ -483,17 +514,17 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
     // MFMA path: bf16 storage; the block's scores must fit in LDS.
     {
         const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
-        const int uc = u_cap > 0 ? u_cap : 1;
+        const int uc = ((u_cap > 0 ? u_cap : 1) + 15) & ~15;     // rows 16-key aligned
         const int waves = 4;
         const int kw = keep ? keep_w : 0;
         const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, waves, kw).bytes
                                       : sel_layout<128>(n_hi, uc, waves, kw).bytes;
         if (sh.bf16 && lds <= (size_t)kSelLdsMax && sh.C <= kSelMaxCells &&
-            uc <= 16 * kSelMaxKeysPerLane) {
+            uc <= 4 * kSelMaxKeysPerLane) {
             const int tq = 16 * waves;
             dim3 grid((unsigned)((sh.nq + tq - 1) / tq * sh.B * sh.H));
             const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
-            const int kpl_need = (uc + 15) / 16;
+            const int kpq_need = uc / 4;          // multiple of 4
 #define FS_SELECT_MFMA(D, KPL)                                                                  \
             hipLaunchKernelGGL((select_topk_mfma_kernel<D, KPL>), grid, dim3(64 * waves), lds,    \
                                st, (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, sh.H, \
@@ -501,11 +532,11 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
                                keep_count, keep_w,                                               \
                                n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, idx, score)
 #define FS_SELECT_KPL(D)                                                                        \
-            if (kpl_need <= 4) FS_SELECT_MFMA(D, 4);                                            \
-            else if (kpl_need <= 8) FS_SELECT_MFMA(D, 8);                                       \
-            else if (kpl_need <= 16) FS_SELECT_MFMA(D, 16);                                     \
-            else if (kpl_need <= 24) FS_SELECT_MFMA(D, 24);                                     \
-            else FS_SELECT_MFMA(D, 40);
+            if (kpq_need <= 8) FS_SELECT_MFMA(D, 8);                                            \
+            else if (kpq_need <= 16) FS_SELECT_MFMA(D, 16);                                     \
+            else if (kpq_need <= 36) FS_SELECT_MFMA(D, 36);                                     \
+            else if (kpq_need <= 68) FS_SELECT_MFMA(D, 68);                                     \
+            else FS_SELECT_MFMA(D, 132);
             if (sh.d == 64) { FS_SELECT_KPL(64) } else { FS_SELECT_KPL(128) }
 #undef FS_SELECT_KPL
 #undef FS_SELECT_MFMA

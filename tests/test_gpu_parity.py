@@ -314,3 +314,37 @@ def test_full_size_sampled(name):
                 c_star = int(x["meta"]["needle"][b, h])
                 sel = g["idx"][b, h, first:]
                 assert (sel == c_star).any(-1).all(), f"needle cell missed in head {h}"
+
+
+def test_exact_ties_go_to_larger_cell():
+    """Cells with identical keys tie exactly in a_c and in every score; the
+    retained and selected sets must then take the larger cell indices, exactly
+    as the oracle does (eq. 8 and the top-K of eq. 7, ties to the larger index)."""
+    # six tied high-norm cells straddle both the top-P (P=4) and top-K (K=3) boundaries
+    wl = W["prefill_b2h16_n4096_d64_bf16"].replace(batch=1, heads=2, n_ctx=2400, n_q=2400,
+                                                    budget=4, topk=3, structure="iid")
+    x = synth.generate(wl)
+    dups = [7, 11, 20, 33, 41]
+    for c in dups:                       # copy cell 3's keys: exact ties in kbar and a_c
+        x["k"][:, :, c * 32:(c + 1) * 32] = x["k"][:, :, 3 * 32:4 * 32]
+    # make the copies high-norm so they compete in the top-P and top-K
+    x["k"][:, :, 3 * 32:4 * 32] *= 3.0
+    for c in dups:
+        x["k"][:, :, c * 32:(c + 1) * 32] = x["k"][:, :, 3 * 32:4 * 32]
+    g = run_gpu(wl, x)
+    p = oracle.problem_from(wl)
+    check_prune(wl, g)
+    n_tie_rows = 0
+    for h in range(wl.heads):
+        kbar = g["kbar"][0, h].astype(np.float64)
+        for t in range(wl.n_q):
+            cand = candidate_list(wl, g, 0, h, wl.q_pos0 + t)
+            want, gap, _ = orc().select_row(p, x["q"][0, h, t], kbar, cand)
+            sel = g["idx"][0, h, t]
+            sel = sel[sel >= 0]
+            cands_dup = [c for c in [3] + dups if c in set(cand.tolist())]
+            if len(cands_dup) >= 2:
+                n_tie_rows += 1
+            if gap == 0.0 or gap >= 1e-5:
+                np.testing.assert_array_equal(np.sort(sel), np.sort(want), err_msg=f"h{h} t{t}")
+    assert n_tie_rows > 1000
