@@ -111,11 +111,14 @@ namespace {
 
 constexpr int kSpQ = 128;              // queries per workgroup
 constexpr int kSpMaxCells = 32768;     // bitmap capacity (cells), so N <= 1M tokens
-constexpr uint16_t kNoSlot = 0xFFFF;
 
+// LDS of the union-masked readout.  Besides the K / V^T tile: the union bitmap
+// over cells, its per-word ranks, the union list (slot -> cell) and, per query,
+// a bitmap over union slots of the cells that query selected (odd pitch, so the
+// 16 queries of a lane row read distinct banks).
 struct SpLayout {
-    int nwords, u_cap, topk;
-    size_t off_vt, off_bitmap, off_rank, off_ulist, off_slots, bytes;
+    int nwords, u_cap, qpitch;
+    size_t off_vt, off_bitmap, off_rank, off_ulist, off_qbits, bytes;
 };
 
 template <int D>
@@ -123,8 +126,8 @@ __host__ __device__ inline SpLayout sp_layout(int C, int topk)
 {
     SpLayout L;
     L.nwords = (C + 31) / 32;
-    L.topk = topk;
     L.u_cap = C < kSpQ * topk ? C : kSpQ * topk;
+    L.qpitch = ((L.u_cap + 31) / 32) | 1;
     auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
     size_t off = (size_t)mf::kTileK * mf::KPitch<D>::value * 2;
     L.off_vt = off;
@@ -135,8 +138,8 @@ __host__ __device__ inline SpLayout sp_layout(int C, int topk)
     off = up16(off + (size_t)L.nwords * 2);
     L.off_ulist = off;
     off = up16(off + (size_t)L.u_cap * 2);
-    L.off_slots = off;
-    off = up16(off + (size_t)kSpQ * topk * 2);
+    L.off_qbits = off;
+    off = up16(off + (size_t)kSpQ * L.qpitch * 4);
     L.bytes = off;
     return L;
 }
@@ -156,7 +159,7 @@ __device__ __forceinline__ int block_excl_scan(int x, int* red, int* total)
     int before = 0, all = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        before += i < wv ? red[i] : 0;
+        if (i < wv) before += red[i];
         all += red[i];
     }
     __syncthreads();
@@ -164,6 +167,10 @@ __device__ __forceinline__ int block_excl_scan(int x, int* red, int* total)
     return before + inc - x;
 }
 
+// Register stage of one 64-key tile (two cells): KC 16-byte chunks of K rows
+// per thread, and for threads t < 2D four keys x 8 dims of V.  Every chunk a
+// wave loads lies in one cell, so a load is a wave-uniform cell base plus a
+// per-lane byte offset fixed for the whole kernel.
 template <int D>
 struct SpStage {
     static constexpr int KC = (mf::kTileK * D / 8) / 256;
@@ -171,31 +178,57 @@ struct SpStage {
     uint4 v[4];
 };
 
+// Per-lane byte offsets of the stage loads within a cell: thread t's K chunk of
+// stage slot `it` sits at kbase + row(it) * row_bytes, where row(it) is uniform;
+// its V rows at vbase + r * row_bytes, in cell vgrp = t / D (uniform per wave).
 template <int D>
-__device__ __forceinline__ void sp_load(SpStage<D>& st, const uint16_t* __restrict__ kh,
-                                        const uint16_t* __restrict__ vh, int64_t kvs2,
+struct SpOffsets {
+    uint32_t kbase, vbase;
+    int vgrp;
+    bool has_v;
+};
+
+template <int D>
+__device__ __forceinline__ SpOffsets<D> sp_offsets(int64_t kvs2)
+{
+    SpOffsets<D> o;
+    const int tid = threadIdx.x;
+    o.kbase = (uint32_t)(((tid / (D / 8)) * kvs2 + (tid % (D / 8)) * 8) * 2);
+    const int within = tid % D, hh = within & 1, g = (within >> 1) & 3, dc = within >> 3;
+    o.vbase = (uint32_t)(((16 * hh + 4 * g) * kvs2 + dc * 8) * 2);
+    o.vgrp = __builtin_amdgcn_readfirstlane(tid / D);          // wave-uniform
+    o.has_v = __builtin_amdgcn_readfirstlane(tid < 2 * D) != 0;
+    return o;
+}
+
+// Stage slot `it` holds key rows (tid / (D/8)) + it * 2048 / D of the 64-key tile:
+// cell (it * 2048 / D) / 32, row (it * 2048 / D) % 32 of that cell plus the lane's own.
+template <int D>
+__host__ __device__ constexpr int sp_kchunk_cell(int it) { return it * (2048 / D) / 32; }
+template <int D>
+__host__ __device__ constexpr int sp_kchunk_row(int it) { return it * (2048 / D) % 32; }
+
+template <int D>
+__device__ __forceinline__ void sp_load(SpStage<D>& st, const SpOffsets<D>& o, const char* kh,
+                                        const char* vh, int64_t kvs2,
                                         const uint16_t* ulist, int n_union, int u)
 {
-    const int tid = threadIdx.x;
-    // the tile's two cells (the second may lie past the union)
-    const bool ok0 = 2 * u < n_union, ok1 = 2 * u + 1 < n_union;
-    const int64_t row0 = ok0 ? (int64_t)ulist[2 * u] * 32 * kvs2 : 0;
-    const int64_t row1 = ok1 ? (int64_t)ulist[2 * u + 1] * 32 * kvs2 : 0;
+    // the tile's two cells; past the end of an odd union the second repeats the
+    // first (its keys are then masked for every query)
+    const int64_t row_bytes = kvs2 * 2, cell_bytes = 32 * row_bytes;
+    const int c0 = __builtin_amdgcn_readfirstlane(ulist[2 * u]);
+    const int c1 = __builtin_amdgcn_readfirstlane(2 * u + 1 < n_union ? ulist[2 * u + 1] : c0);
 #pragma unroll
     for (int it = 0; it < SpStage<D>::KC; ++it) {
-        const int c = tid + 256 * it;
-        const int kr = c / (D / 8), part = c % (D / 8);
-        const bool ok = (kr >> 5) ? ok1 : ok0;
-        const int64_t off = ((kr >> 5) ? row1 : row0) + (kr & 31) * kvs2 + part * 8;
-        st.k[it] = ok ? *reinterpret_cast<const uint4*>(kh + off) : make_uint4(0, 0, 0, 0);
+        const char* cb = kh + (sp_kchunk_cell<D>(it) ? c1 : c0) * cell_bytes +
+                         sp_kchunk_row<D>(it) * row_bytes;
+        st.k[it] = *reinterpret_cast<const uint4*>(cb + o.kbase);
     }
-    if (tid < 2 * D) {
-        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
-        const bool ok = grp ? ok1 : ok0;
-        const uint16_t* vb = vh + (grp ? row1 : row0) + (16 * hh + 4 * g) * kvs2 + dc * 8;
+    if (o.has_v) {
+        const char* vb = vh + (o.vgrp ? c1 : c0) * cell_bytes;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            st.v[r] = ok ? *reinterpret_cast<const uint4*>(vb + r * kvs2) : make_uint4(0, 0, 0, 0);
+            st.v[r] = *reinterpret_cast<const uint4*>(vb + r * row_bytes + o.vbase);
     }
 }
 
@@ -211,8 +244,96 @@ __device__ __forceinline__ void sp_store(const SpStage<D>& st, uint16_t* ks, uin
         mf::lds_store16(ks + kr * KP + part * 8, st.k[it]);
     }
     if (tid < 2 * D) {
-        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+        const int grp = tid / D, within = tid % D;
+        const int hh = within & 1, g = (within >> 1) & 3, dc = within >> 3;
         mf::store_vt_4x8(st.v, vt + (dc * 8) * mf::kVtPitch + 32 * grp + 8 * g + 4 * hh);
+    }
+}
+
+// One 64-key tile (two cells of 32 keys) for a wave's 32 queries.  sel[qg][c]
+// says whether query 16 qg + n selected the tile's cell c.  A cell's scores are
+// masked through the exponent bias (-inf for a cell the query did not select),
+// so no score is touched twice; the softmax denominator is accumulated on the
+// matrix core as P^T times a row of ones, from the same bf16 weights as O.
+template <int D>
+__device__ __forceinline__ void sp_tile(const uint16_t* ks, const uint16_t* vt,
+                                        const mf::bf16x8 (&qf)[2][D / 32],
+                                        mf::f32x4 (&acc)[D / 16][2], mf::f32x4 (&accl)[2],
+                                        float (&m_ref)[2], float scale_log2,
+                                        const bool (&sel)[2][2])
+{
+    using namespace mf;
+    constexpr int KP = KPitch<D>::value;
+    constexpr int KS = D / 32, DB = D / 16;
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 a = as_bf16x8(lds_load16(ks + (16 * kb + n) * KP + 32 * t + 8 * g));
+            s[kb][0] = mfma(a, qf[0][t], s[kb][0]);
+            s[kb][1] = mfma(a, qf[1][t], s[kb][1]);
+        }
+    }
+    bf16x8 pf[2][2];
+    float corr[2];
+    bool any_rescale = false;
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        float cm[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float x = -INFINITY;
+#pragma unroll
+            for (int kb = 2 * c; kb < 2 * c + 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x = fmaxf(x, s[kb][qg][r]);
+            cm[c] = sel[qg][c] ? x : -INFINITY;
+        }
+        // scale_log2 > 0 commutes with max
+        const float tmax = xrow_max(fmaxf(cm[0], cm[1])) * scale_log2;
+        const bool raise = tmax > m_ref[qg] + kLazy;
+        const float m_new = raise ? tmax : m_ref[qg];
+        corr[qg] = raise ? __builtin_amdgcn_exp2f(m_ref[qg] - m_new) : 1.f;   // 0 at the start
+        any_rescale |= raise;
+        m_ref[qg] = m_new;
+        // a selected cell implies a finite m_new; an unselected one gets p = 0
+        float bias[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) bias[c] = sel[qg][c] ? -m_new : -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                s[kb][qg][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qg][r], scale_log2, bias[kb >> 1]));
+        pf[0][qg] = pack_p(s[0][qg], s[1][qg]);
+        pf[1][qg] = pack_p(s[2][qg], s[3][qg]);
+    }
+    if (__ballot(any_rescale) != 0) {
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db][qg] *= corr[qg];
+            accl[qg] *= corr[qg];
+        }
+    }
+    const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2) {
+        accl[0] = mfma(ones, pf[a2][0], accl[0]);
+        accl[1] = mfma(ones, pf[a2][1], accl[1]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+            const bf16x8 a = as_bf16x8(lds_load16(vt + (16 * db + n) * kVtPitch + 32 * a2 + 8 * g));
+            acc[db][0] = mfma(a, pf[a2][0], acc[db][0]);
+            acc[db][1] = mfma(a, pf[a2][1], acc[db][1]);
+        }
     }
 }
 
@@ -236,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
     uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
-    uint16_t* slots = reinterpret_cast<uint16_t*>(base + L.off_slots);
+    uint32_t* qbits = reinterpret_cast<uint32_t*>(base + L.off_qbits);
     __shared__ int red[4];
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -248,8 +369,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     const int n_rows = nq - t0 < kSpQ ? (int)(nq - t0) : kSpQ;
     const int32_t* idx_blk = idx + (bh * nq + t0) * (long)topk;
 
-    // ---- union of the selected cells --------------------------------------
+    // ---- union of the selected cells, and each query's selection over it ----
     for (int wd = tid; wd < L.nwords; wd += 256) bitmap[wd] = 0u;
+    for (int e = tid; e < kSpQ * L.qpitch; e += 256) qbits[e] = 0u;
     __syncthreads();
     for (int e = tid; e < n_rows * topk; e += 256) {
         const int c = idx_blk[e];
@@ -283,36 +405,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     }
     for (int e = tid; e < n_rows * topk; e += 256) {
         const int c = idx_blk[e];
-        uint16_t sl = kNoSlot;
-        if (c >= 0 && c < C)
-            sl = (uint16_t)(rank[c >> 5] + __popc(bitmap[c >> 5] & ((1u << (c & 31)) - 1u)));
-        slots[e] = sl;
-    }
-    __syncthreads();
-    if (tid < n_rows) {      // each query's slots ascending and distinct (sorted already if idx is)
-        uint16_t* row = slots + tid * topk;
-        for (int a = 1; a < topk; ++a) {
-            const uint16_t x = row[a];
-            int z = a - 1;
-            while (z >= 0 && row[z] > x) {
-                row[z + 1] = row[z];
-                --z;
-            }
-            row[z + 1] = x;
+        if (c >= 0 && c < C) {
+            const int sl = rank[c >> 5] + __popc(bitmap[c >> 5] & ((1u << (c & 31)) - 1u));
+            atomicOr(&qbits[(e / topk) * L.qpitch + (sl >> 5)], 1u << (sl & 31));
         }
-        int wr = 0;
-        for (int a = 0; a < topk; ++a)
-            if (a == 0 || row[a] != row[a - 1] || row[a] == kNoSlot) row[wr++] = row[a];
-        for (; wr < topk; ++wr) row[wr] = kNoSlot;
     }
     __syncthreads();
 
     // ---- queries of this wave as B operands -------------------------------
-    const uint16_t* kh = k + b * kvs0 + h * kvs1;
-    const uint16_t* vh = v + b * kvs0 + h * kvs1;
+    const char* kh = reinterpret_cast<const char*>(k + b * kvs0 + h * kvs1);
+    const char* vh = reinterpret_cast<const char*>(v + b * kvs0 + h * kvs1);
     bf16x8 qf[2][KS];
-    int ptr[2];
-    uint16_t nxt[2];
+    const int qbit_row = (32 * wv + n) * L.qpitch;   // query group 1 is 16 rows further
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const int r = 32 * wv + 16 * qg + n;
@@ -322,41 +426,34 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
         for (int t = 0; t < KS; ++t)
             qf[qg][t] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
                                      : make_uint4(0, 0, 0, 0));
-        ptr[qg] = 0;
-        nxt[qg] = ok ? slots[r * topk] : kNoSlot;
     }
 
-    f32x4 acc[DB][2];
+    f32x4 acc[DB][2], accl[2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    accl[0] = accl[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};
 
+    const SpOffsets<D> offs = sp_offsets<D>(kvs2);
     const int n_tiles = (n_union + 1) / 2;
     SpStage<D> stage;
     if (n_tiles > 0) {
-        sp_load<D>(stage, kh, vh, kvs2, ulist, n_union, 0);
+        sp_load<D>(stage, offs, kh, vh, kvs2, ulist, n_union, 0);
         sp_store<D>(stage, ks, vt);
     }
     __syncthreads();
+    uint32_t qw[2] = {0u, 0u};
     for (int u = 0; u < n_tiles; ++u) {
-        if (u + 1 < n_tiles) sp_load<D>(stage, kh, vh, kvs2, ulist, n_union, u + 1);
-        // slot lists are ascending and distinct, so the walk advances at most
-        // once per slot and never skips a listed slot
-        bool sel[2][2];
-#pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
-            const int r = 32 * wv + 16 * qg + n;
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                sel[qg][c2] = nxt[qg] == 2 * u + c2;
-                if (sel[qg][c2]) nxt[qg] = ++ptr[qg] < topk ? slots[r * topk + ptr[qg]] : kNoSlot;
-            }
+        if (u + 1 < n_tiles) sp_load<D>(stage, offs, kh, vh, kvs2, ulist, n_union, u + 1);
+        if ((u & 15) == 0) {
+            qw[0] = qbits[qbit_row + (u >> 4)];                  // rows past n_rows are zero
+            qw[1] = qbits[qbit_row + 16 * L.qpitch + (u >> 4)];
         }
-        const bool any = __ballot(sel[0][0] || sel[0][1] || sel[1][0] || sel[1][1]) != 0;
-        if (any) {
-            attn_tile<D, true>(ks, vt, qf, acc, m_run, l_run, scale_log2,
-                               [&](int kb, int qg, int) { return sel[qg][kb >> 1]; });
-        }
+        const int sh = (2 * u) & 31;
+        const bool sel[2][2] = {{((qw[0] >> sh) & 1u) != 0, ((qw[0] >> (sh + 1)) & 1u) != 0},
+                                {((qw[1] >> sh) & 1u) != 0, ((qw[1] >> (sh + 1)) & 1u) != 0}};
+        if (__ballot(sel[0][0] || sel[0][1] || sel[1][0] || sel[1][1]) != 0)
+            sp_tile<D>(ks, vt, qf, acc, accl, m_run, scale_log2, sel);
         __syncthreads();
         if (u + 1 < n_tiles) {
             sp_store<D>(stage, ks, vt);
@@ -368,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const int r = 32 * wv + 16 * qg + n;
-        const float l = xrow_sum(l_run[qg]);
+        const float l = accl[qg][0];    // every row of the ones product is the full sum
         const float inv_l = l > 0.f ? 1.f / l : 0.f;
         float ss = 0.f;
 #pragma unroll
@@ -398,7 +495,7 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
     const size_t lds = sh.d == 64 ? sp_layout<64>(sh.C, topk).bytes
                                   : sp_layout<128>(sh.C, topk).bytes;
-    if (sh.bf16 && sh.C <= kSpMaxCells && lds <= 65536) {
+    if (sh.bf16 && sh.C <= kSpMaxCells && lds <= 160 * 1024) {
         const long n_tiles = (sh.nq + kSpQ - 1) / kSpQ;
         dim3 grid((unsigned)(n_tiles * sh.B * sh.H)), block(256);
 #define FS_SPARSE_MFMA(D)                                                                         \
