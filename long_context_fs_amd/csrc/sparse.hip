@@ -129,9 +129,9 @@ __host__ __device__ inline SpLayout sp_layout(int C, int topk)
     L.u_cap = C < kSpQ * topk ? C : kSpQ * topk;
     L.qpitch = ((L.u_cap + 31) / 32) | 1;
     auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
-    size_t off = (size_t)mf::kTileK * mf::KPitch<D>::value * 2;
+    size_t off = (size_t)mf::kTileK * D * 2;          // swizzled K tile
     L.off_vt = off;
-    off = up16(off + (size_t)D * mf::kVtPitch * 2);
+    off = up16(off + (size_t)D * mf::kTileK * 2);        // swizzled V^T tile
     L.off_bitmap = off;
     off = up16(off + (size_t)L.nwords * 4);
     L.off_rank = off;
@@ -235,18 +235,17 @@ __device__ __forceinline__ void sp_load(SpStage<D>& st, const SpOffsets<D>& o, c
 template <int D>
 __device__ __forceinline__ void sp_store(const SpStage<D>& st, uint16_t* ks, uint16_t* vt)
 {
-    constexpr int KP = mf::KPitch<D>::value;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < SpStage<D>::KC; ++it) {
         const int c = tid + 256 * it;
         const int kr = c / (D / 8), part = c % (D / 8);
-        mf::lds_store16(ks + kr * KP + part * 8, st.k[it]);
+        mf::lds_store16(ks + mf::ksw_off<D>(kr, part), st.k[it]);
     }
     if (tid < 2 * D) {
         const int grp = tid / D, within = tid % D;
         const int hh = within & 1, g = (within >> 1) & 3, dc = within >> 3;
-        mf::store_vt_4x8(st.v, vt + (dc * 8) * mf::kVtPitch + 32 * grp + 8 * g + 4 * hh);
+        mf::store_vt_4x8_sw(st.v, vt, dc, 32 * grp + 8 * g + 4 * hh);
     }
 }
 
@@ -263,7 +262,6 @@ __device__ __forceinline__ void sp_tile(const uint16_t* ks, const uint16_t* vt,
                                         const bool (&sel)[2][2])
 {
     using namespace mf;
-    constexpr int KP = KPitch<D>::value;
     constexpr int KS = D / 32, DB = D / 16;
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     f32x4 s[4][2];
@@ -273,7 +271,7 @@ __device__ __forceinline__ void sp_tile(const uint16_t* ks, const uint16_t* vt,
     for (int t = 0; t < KS; ++t) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 a = as_bf16x8(lds_load16(ks + (16 * kb + n) * KP + 32 * t + 8 * g));
+            const bf16x8 a = as_bf16x8(lds_load16(ks + ksw_off<D>(16 * kb + n, 4 * t + g)));
             s[kb][0] = mfma(a, qf[0][t], s[kb][0]);
             s[kb][1] = mfma(a, qf[1][t], s[kb][1]);
         }
@@ -312,7 +310,7 @@ __device__ __forceinline__ void sp_tile(const uint16_t* ks, const uint16_t* vt,
         pf[0][qg] = pack_p(s[0][qg], s[1][qg]);
         pf[1][qg] = pack_p(s[2][qg], s[3][qg]);
     }
-    if (__ballot(any_rescale) != 0) {
+    if (__builtin_expect(__ballot(any_rescale) != 0, 0)) {
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
 #pragma unroll
@@ -322,18 +320,18 @@ __device__ __forceinline__ void sp_tile(const uint16_t* ks, const uint16_t* vt,
     }
     const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 #pragma unroll
-    for (int a2 = 0; a2 < 2; ++a2) {
-        accl[0] = mfma(ones, pf[a2][0], accl[0]);
-        accl[1] = mfma(ones, pf[a2][1], accl[1]);
-    }
-#pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2) {
-            const bf16x8 a = as_bf16x8(lds_load16(vt + (16 * db + n) * kVtPitch + 32 * a2 + 8 * g));
+            const bf16x8 a = as_bf16x8(lds_load16(vt + vtsw_off(16 * db + n, 4 * a2 + g)));
             acc[db][0] = mfma(a, pf[a2][0], acc[db][0]);
             acc[db][1] = mfma(a, pf[a2][1], acc[db][1]);
         }
+    }
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2) {
+        accl[0] = mfma(ones, pf[a2][0], accl[0]);
+        accl[1] = mfma(ones, pf[a2][1], accl[1]);
     }
 }
 
