@@ -9,18 +9,19 @@
 // key is found exactly by a bitwise search with ballot counts, ties at the
 // threshold go to the larger cell, and the chosen cells are written ascending.
 //
-// bf16 storage (candidate lists up to 640 cells): MFMA kernel.  A workgroup
+// bf16 storage (candidate lists up to 528 cells): MFMA kernel.  A workgroup
 // owns 64 consecutive queries (4 wavefronts x 16); they span at most three
 // candidate counts, so their candidates are the union of at most three keep
 // rows (or the prefix [0, n) without pruning), built in LDS with a bitmap.
-// kbar rows of the union are staged 64 at a time, each fp32 value split into
+// kbar rows of the union are staged 32 at a time, each fp32 value split into
 // three bf16 parts hi + mid + lo (24 significant bits); q is exact in bf16, so
 // three exact-product MFMAs with fp32 accumulation give fp32-accurate scores.
-// The scores go to LDS as order-preserving keys; each query's row is then
-// loaded into 4 consecutive lanes (a DPP quad; all 16 queries of a wave at
-// once), the K-th largest key is found by the same bitwise search with quad
-// DPP sums, and the chosen cells are written in slot order from one exclusive
-// prefix over the quad.
+// The scores stay in the MFMA output registers as order-preserving keys: the
+// four lanes n, n+16, n+32, n+48 hold query n's union slots 16 bb + 4 g + r.
+// The K-th largest key is found by a bitwise search over those four lanes
+// (gfx950 row swaps for the sums), starting below the bits all valid keys share
+// and stopping once exactly K keys reach the candidate; the chosen cells are
+// written in slot order from packed prefix counts over the four lanes.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 #include "mfma_tile.hpp"
@@ -139,28 +140,24 @@ namespace {
 
 constexpr int kSelChunk = 32;        // union cells staged per chunk (two 16-cell MFMA blocks)
 constexpr int kSelMaxCells = 32768;
-constexpr int kSelLdsMax = 160 * 1024;
-constexpr int kSelMaxKeysPerLane = 132;  // quad layout: union of at most 528 cells per block
+constexpr int kSelMaxBlocks = 33;    // 16-cell score blocks per query: union of at most 528 cells
 
 struct SelLayout {
-    int nwords, u_cap, waves, keep_w;
-    size_t off_keys, off_bitmap, off_rank, off_ulist, off_vmask, off_krows, bytes;
+    int nwords, u_cap, keep_w;
+    size_t off_bitmap, off_rank, off_ulist, off_vmask, off_krows, bytes;
 };
 
-// LDS carve-up: kbar chunk split in 3 bf16 parts | keys [16*waves][u_cap] |
-// bitmap | rank | union list | row-membership masks | copy of the keep rows.
+// LDS carve-up: kbar chunk split in 3 bf16 parts (swizzled rows) | bitmap |
+// rank | union list | row-membership masks | copy of the keep rows.
 template <int D>
-__host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int waves, int keep_w)
+__host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int keep_w)
 {
     SelLayout L;
     L.nwords = (n_hi + 31) / 32;
     L.u_cap = u_cap;
-    L.waves = waves;
     L.keep_w = keep_w;
     auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
-    size_t off = (size_t)3 * kSelChunk * mf::KPitch<D>::value * 2;
-    L.off_keys = off;
-    off = up16(off + (size_t)16 * waves * u_cap * 4);
+    size_t off = (size_t)3 * kSelChunk * D * 2;
     L.off_bitmap = off;
     off = up16(off + (size_t)L.nwords * 4);
     L.off_rank = off;
@@ -196,10 +193,43 @@ __device__ __forceinline__ int sel_block_excl_scan(int x, int* red, int* total)
     return before + inc - x;
 }
 
+// The four lanes n, n+16, n+32, n+48 of the MFMA output layout hold one query's
+// scores.  Reductions over them use the gfx950 row swaps: after a swap with
+// itself, the two results of a lane are its own value and its partner's.
+template <class Op>
+__device__ __forceinline__ uint32_t x4_reduce(uint32_t x, Op op)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = op(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return op(b[0], b[1]);
+}
+
+// Exclusive prefix over g (lane n + 16 g, in g order) and total of packed
+// counters: 5-bit fields, every partial sum below 32, so no field carries.
+__device__ __forceinline__ void x4_scan(uint32_t v, int g, uint32_t& excl, uint32_t& total)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const uint32_t p = a[0] + a[1] - v;                // row g ^ 1
+    const uint32_t pair = v + p;
+    const uint32_t s1 = (g & 1) ? pair : v;            // inclusive within the row pair
+    const auto b = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+    const uint32_t other = b[0] + b[1] - pair;         // the other row pair's total
+    excl = ((g & 2) ? s1 + other : s1) - v;
+    total = pair + other;
+}
+
+constexpr int kFieldsPerWord = 6;   // 5-bit fields
+
+__device__ __forceinline__ int field5(const uint32_t* w, int i)
+{
+    return (int)((w[i / kFieldsPerWord] >> (5 * (i % kFieldsPerWord))) & 31u);
+}
+
 }  // namespace
 
-template <int D, int KPQ>
-__global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads exactly
+template <int D, int NB>
+__global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel(   // 256 threads exactly
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const float* __restrict__ kbar, int H, int BH, int C, int nq, int q_pos0, int window,
     int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
@@ -207,14 +237,14 @@ __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads
     int32_t* __restrict__ idx, float* __restrict__ score)
 {
     using namespace mf;
-    constexpr int KP = KPitch<D>::value;
     constexpr int KS = D / 32;
-    const int waves = blockDim.x >> 6, tq = 16 * waves;
+    constexpr int kTq = 64;                                    // queries per workgroup
+    constexpr int kNW = (NB + kFieldsPerWord - 1) / kFieldsPerWord;
+    constexpr int kKW = (4 * NB + 31) / 32;                    // kept-key mask words
     extern __shared__ uint4 smem_raw[];
-    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, waves, keep ? keep_w : 0);
+    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, keep ? keep_w : 0);
     char* base = reinterpret_cast<char*>(smem_raw);
-    uint16_t* kbs = reinterpret_cast<uint16_t*>(base);      // [3][kSelChunk][KP]
-    uint32_t* keys = reinterpret_cast<uint32_t*>(base + L.off_keys);
+    uint16_t* kbs = reinterpret_cast<uint16_t*>(base);      // [3 * kSelChunk] swizzled rows of D
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
     uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
@@ -227,8 +257,8 @@ __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads
     const TileOfBlock tb = xcd_tile(BH);
     const long bh = tb.bh;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const long t0 = tb.tile * tq;
-    const int n_rows_blk = nq - t0 < tq ? (int)(nq - t0) : tq;
+    const long t0 = tb.tile * kTq;
+    const int n_rows_blk = nq - t0 < kTq ? (int)(nq - t0) : kTq;
     const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
     const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
 
@@ -317,9 +347,10 @@ __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads
                                    : make_uint4(0, 0, 0, 0));
     }
 
-    // ---- scores S^T = Kbar Q^T over the union, kSelChunk cells per step -------
-    // The next chunk's kbar rows are loaded into registers while the current
-    // chunk's MFMAs run.
+    // ---- scores S^T = Kbar Q^T over the union, kept in registers ------------
+    // kv[bb][r] is the key of union slot 16 bb + 4 g + r for query n (0 when that
+    // slot is not one of the query's candidates).  The next chunk's kbar rows are
+    // loaded into registers while the current chunk's MFMAs run.
     constexpr int kIt = kSelChunk * D / 4 / 256;     // float4 per thread per chunk
     const float* kb_head = kbar + bh * (long)C * D;
     float4 pre[kIt];
@@ -336,165 +367,220 @@ __global__ __launch_bounds__(256) void select_topk_mfma_kernel(   // 256 threads
             }
         }
     };
-    __syncthreads();                         // ulist complete
+    uint32_t kv[NB][4];
+    __syncthreads();                         // ulist / vmask complete
     load_chunk(0);
-    for (int c0 = 0; c0 < n_union; c0 += kSelChunk) {
-        __syncthreads();                     // previous chunk's MFMA reads are done
 #pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int f = tid + 256 * it;
-            const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
-            const float r[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
-            // x = hi + mid + lo exactly: each residual has at most 16 (then 8)
-            // significant bits, so the fp32 subtractions are exact.
-            uint32_t part[3][2];
+    for (int ci = 0; ci < (NB + 1) / 2; ++ci) {
+        const int c0 = ci * kSelChunk;
+        if (c0 < n_union) {                  // block-uniform
+            __syncthreads();                 // previous chunk's MFMA reads are done
 #pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-                float a0 = r[e], a1 = r[e + 1];
-                const uint32_t h = cvt_pk_bf16(a0, a1);
-                a0 -= __uint_as_float(h << 16);
-                a1 -= __uint_as_float(h & 0xFFFF0000u);
-                const uint32_t m = cvt_pk_bf16(a0, a1);
-                a0 -= __uint_as_float(m << 16);
-                a1 -= __uint_as_float(m & 0xFFFF0000u);
-                part[0][e / 2] = h;
-                part[1][e / 2] = m;
-                part[2][e / 2] = cvt_pk_bf16(a0, a1);
-            }
+            for (int it = 0; it < kIt; ++it) {
+                const int f = tid + 256 * it;
+                const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
+                const float r[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
+                // x = hi + mid + lo exactly: each residual has at most 16 (then 8)
+                // significant bits, so the fp32 subtractions are exact.
+                uint32_t part[3][2];
 #pragma unroll
-            for (int pp = 0; pp < 3; ++pp)
-                *reinterpret_cast<uint2*>(kbs + (pp * kSelChunk + cl) * KP + d4) =
-                    make_uint2(part[pp][0], part[pp][1]);
-        }
-        __syncthreads();
-        if (c0 + kSelChunk < n_union) load_chunk(c0 + kSelChunk);
-#pragma unroll
-        for (int bb = 0; bb < kSelChunk / 16; ++bb) {
-            const int slot0 = c0 + 16 * bb;
-            if (slot0 >= n_union) break;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < KS; ++t) {
-#pragma unroll
-                for (int pp = 0; pp < 3; ++pp) {
-                    const bf16x8 a = as_bf16x8(
-                        lds_load16(kbs + (pp * kSelChunk + 16 * bb + n) * KP + 32 * t + 8 * g));
-                    acc = mfma(a, qf[t], acc);
+                for (int e = 0; e < 4; e += 2) {
+                    float a0 = r[e], a1 = r[e + 1];
+                    const uint32_t hi = cvt_pk_bf16(a0, a1);
+                    a0 -= __uint_as_float(hi << 16);
+                    a1 -= __uint_as_float(hi & 0xFFFF0000u);
+                    const uint32_t mid = cvt_pk_bf16(a0, a1);
+                    a0 -= __uint_as_float(mid << 16);
+                    a1 -= __uint_as_float(mid & 0xFFFF0000u);
+                    part[0][e / 2] = hi;
+                    part[1][e / 2] = mid;
+                    part[2][e / 2] = cvt_pk_bf16(a0, a1);
                 }
+#pragma unroll
+                for (int pp = 0; pp < 3; ++pp)
+                    *reinterpret_cast<uint2*>(kbs + sw_off<D>(pp * kSelChunk + cl, d4 >> 3) + (d4 & 4)) =
+                        make_uint2(part[pp][0], part[pp][1]);
             }
-            uint32_t kk[4];
+            __syncthreads();
+            if (c0 + kSelChunk < n_union) load_chunk(c0 + kSelChunk);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int slot = slot0 + 4 * g + r;
-                bool ok = slot < n_union && n_q > 0;
-                if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
-                kk[r] = ok ? float_key(acc[r]) : 0u;
-            }
-            uint32_t* krow = keys + (size_t)qr * u_cap + slot0 + 4 * g;
-            if (slot0 + 4 * g + 3 < u_cap) {   // u_cap is a multiple of 16
-                *reinterpret_cast<uint4*>(krow) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
-            } else {
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int bb = 2 * ci + b2;
+                if (bb >= NB) break;
+                const int slot0 = 16 * bb;
+                if (slot0 < n_union) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (slot0 + 4 * g + r < u_cap) krow[r] = kk[r];
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- per query: exact top-K, written in ascending slot (= cell) order ----
-    // Quad layout: lanes 4j .. 4j+3 of wave w hold query 16w + j; lane 4j+sub
-    // holds the contiguous slots [sub*kpq, (sub+1)*kpq) of that query's keys.
-    {
-        const int qj = lane >> 2, sub = lane & 3;
-        const int row_b = 16 * wv + qj;
-        const bool row_ok = row_b < n_rows_blk;
-        const uint32_t* krow = keys + (size_t)row_b * u_cap + sub * KPQ;
-        const int slot0 = sub * KPQ;
-        uint32_t kv[KPQ];           // keys past the union are 0 and never counted
+                    for (int t = 0; t < KS; ++t) {
 #pragma unroll
-        for (int e = 0; e < KPQ; e += 4) {
-            const uint4 w4 = *reinterpret_cast<const uint4*>(krow + e);
-            kv[e] = slot0 + e < n_union ? w4.x : 0u;
-            kv[e + 1] = slot0 + e + 1 < n_union ? w4.y : 0u;
-            kv[e + 2] = slot0 + e + 2 < n_union ? w4.z : 0u;
-            kv[e + 3] = slot0 + e + 3 < n_union ? w4.w : 0u;
-        }
-        int nv = 0;
+                        for (int pp = 0; pp < 3; ++pp) {
+                            const bf16x8 a = as_bf16x8(
+                                lds_load16(kbs + sw_off<D>(pp * kSelChunk + 16 * b2 + n, 4 * t + g)));
+                            acc = mfma(a, qf[t], acc);
+                        }
+                    }
 #pragma unroll
-        for (int e = 0; e < KPQ; ++e) nv += kv[e] != 0u;
-        nv = quad_sum(nv);
-        const int kq = nv < topk ? nv : topk;
-        // kq-th largest key: the largest thr with #{key >= thr} >= kq
-        uint32_t thr = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = thr | (1u << bit);
-            int c0 = 0, c1 = 0;                   // two chains: shorter dependency
+                    for (int r = 0; r < 4; ++r) {
+                        const int slot = slot0 + 4 * g + r;
+                        bool ok = slot < n_union && n_q > 0;
+                        if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
+                        kv[bb][r] = ok ? float_key(acc[r]) : 0u;
+                    }
+                } else {
 #pragma unroll
-            for (int e = 0; e < KPQ; e += 2) {
-                c0 += kv[e] >= cand;
-                c1 += kv[e + 1] >= cand;
-            }
-            if (quad_sum(c0 + c1) >= kq) thr = cand;
-        }
-        // thr >= 1 whenever kq > 0, so "key >= thr" and "key > thr" imply a valid key
-        int ge = 0, gt = 0;
-#pragma unroll
-        for (int e = 0; e < KPQ; ++e) {
-            ge += kv[e] >= thr;
-            gt += kv[e] > thr;
-        }
-        const int eq = ge - gt;
-        const int n_gt = quad_sum(gt), n_eq = quad_sum(eq);
-        const int need_eq = kq - n_gt;            // equal keys kept: those in the largest slots
-        const long orow = bh * nq + t0 + (row_ok ? row_b : 0);
-        int32_t* out_i = idx + orow * topk;
-        float* out_s = score ? score + orow * topk : nullptr;
-        auto emit = [&](int p, uint32_t k, int j) {
-            out_i[p] = keep ? ulist[j] : j;
-            if (out_s) {
-                const float dot = __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-                out_s[p] = dot * inv_sqrt_d;
-            }
-        };
-        uint32_t thr_o = thr;
-        asm volatile("" : "+v"(thr_o));           // fresh compares below, not kept masks
-        if (n_eq == need_eq) {
-            // no tie across the boundary: exactly the keys >= thr
-            int pos = quad_excl_prefix(ge);
-            if (row_ok && kq > 0) {
-#pragma unroll
-                for (int e = 0; e < KPQ; ++e) {
-                    if (kv[e] >= thr_o) emit(pos++, kv[e], slot0 + e);
+                    for (int r = 0; r < 4; ++r) kv[bb][r] = 0u;
                 }
             }
         } else {
-            // ties at the threshold: keep the need_eq equal keys with the largest slots
-            int eq_rank = quad_excl_prefix(eq);
-            int kept_here = 0;
 #pragma unroll
-            for (int e = 0; e < KPQ; ++e) {
-                const bool is_eq = kv[e] == thr_o;
-                kept_here += kv[e] > thr_o || (is_eq && eq_rank >= n_eq - need_eq);
-                eq_rank += is_eq;
-            }
-            int pos = quad_excl_prefix(kept_here);
-            eq_rank = quad_excl_prefix(eq);
-            if (row_ok && kq > 0) {
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int bb = 2 * ci + b2;
+                if (bb < NB) {
 #pragma unroll
-                for (int e = 0; e < KPQ; ++e) {
-                    const bool is_eq = kv[e] == thr_o;
-                    const bool kept = kv[e] > thr_o || (is_eq && eq_rank >= n_eq - need_eq);
-                    eq_rank += is_eq;
-                    if (kept) emit(pos++, kv[e], slot0 + e);
+                    for (int r = 0; r < 4; ++r) kv[bb][r] = 0u;
                 }
             }
         }
-        if (row_ok) {
-            for (int t = kq + sub; t < topk; t += 4) {
-                out_i[t] = -1;
-                if (out_s) out_s[t] = 0.f;
+    }
+
+    // ---- per query: exact top-K over its four lanes -------------------------
+    int nv = 0;
+    uint32_t k_and = 0xFFFFFFFFu, k_or = 0u;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t k = kv[bb][r];
+            nv += k != 0u;
+            k_and &= k != 0u ? k : 0xFFFFFFFFu;
+            k_or |= k;
+        }
+    nv = (int)x4_reduce((uint32_t)nv, [](uint32_t x, uint32_t y) { return x + y; });
+    k_and = x4_reduce(k_and, [](uint32_t x, uint32_t y) { return x & y; });
+    k_or = x4_reduce(k_or, [](uint32_t x, uint32_t y) { return x | y; });
+    const int kq = nv < topk ? nv : topk;
+    // The kq-th largest key thr: the largest value with #{key >= thr} >= kq.
+    // Bits above the highest bit in which two valid keys differ are common to
+    // all of them and fixed from the start; the search stops for a query as soon
+    // as exactly kq keys are >= the candidate (that set is then the top kq).
+    const uint32_t diff = k_and ^ k_or;
+    const int hb = diff != 0u ? 31 - __clz(diff) : -1;
+    uint32_t thr = hb < 0 ? k_or : (k_or & ~(hb >= 31 ? 0xFFFFFFFFu : (2u << hb) - 1u));
+    bool done = kq == 0 || hb < 0;
+    int hb_w = done ? -1 : hb;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) hb_w = max(hb_w, __shfl_xor(hb_w, m, kWave));
+    for (int bit = hb_w; bit >= 0; --bit) {
+        if (__ballot(!done) == 0) break;
+        const uint32_t cand = thr | (1u << bit);
+        int c0 = 0, c1 = 0;                       // two chains: shorter dependency
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            c0 += (kv[bb][0] >= cand) + (kv[bb][1] >= cand);
+            c1 += (kv[bb][2] >= cand) + (kv[bb][3] >= cand);
+        }
+        const int c = (int)x4_reduce((uint32_t)(c0 + c1), [](uint32_t x, uint32_t y) { return x + y; });
+        if (!done && c >= kq) {
+            thr = cand;
+            done = c == kq;
+        }
+    }
+    // thr >= 1 whenever kq > 0, so "key >= thr" and "key > thr" imply a valid key
+    int ge = 0, gt = 0;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ge += kv[bb][r] >= thr;
+            gt += kv[bb][r] > thr;
+        }
+    const int n_gt = (int)x4_reduce((uint32_t)gt, [](uint32_t x, uint32_t y) { return x + y; });
+    const int n_ge = (int)x4_reduce((uint32_t)ge, [](uint32_t x, uint32_t y) { return x + y; });
+    const int n_eq = n_ge - n_gt;
+    const int need_eq = kq - n_gt;            // equal keys kept: those in the largest slots
+
+    // kept keys as a bit mask over (bb, r)
+    uint32_t km[kKW];
+#pragma unroll
+    for (int w = 0; w < kKW; ++w) km[w] = 0u;
+    if (kq > 0) {
+        uint32_t thr_o = thr;
+        asm volatile("" : "+v"(thr_o));           // fresh compares below, not kept masks
+        if (n_eq == need_eq) {
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (kv[bb][r] >= thr_o) km[(4 * bb + r) / 32] |= 1u << ((4 * bb + r) % 32);
+        } else {
+            // ties at the threshold: rank the equal keys by slot, keep the top need_eq
+            uint32_t cw[kNW], ex[kNW], tot[kNW];
+#pragma unroll
+            for (int w = 0; w < kNW; ++w) cw[w] = 0u;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                uint32_t e = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) e += kv[bb][r] == thr_o;
+                cw[bb / kFieldsPerWord] += e << (5 * (bb % kFieldsPerWord));
             }
+#pragma unroll
+            for (int w = 0; w < kNW; ++w) x4_scan(cw[w], g, ex[w], tot[w]);
+            int run = 0;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                int er = run + field5(ex, bb);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool is_eq = kv[bb][r] == thr_o;
+                    const bool kept = kv[bb][r] > thr_o || (is_eq && er >= n_eq - need_eq);
+                    er += is_eq;
+                    if (kept) km[(4 * bb + r) / 32] |= 1u << ((4 * bb + r) % 32);
+                }
+                run += field5(tot, bb);
+            }
+        }
+    }
+
+    // ---- write the kept cells in ascending slot order -------------------------
+    // Slot order is (bb, g, r): a kept key's position is the kept count of the
+    // earlier blocks, of the lanes g' < g in its block, and of its own r' < r.
+    const long orow = bh * nq + t0 + (q_ok ? qr : 0);
+    int32_t* out_i = idx + orow * topk;
+    float* out_s = score ? score + orow * topk : nullptr;
+    {
+        uint32_t cw[kNW], ex[kNW], tot[kNW];
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) cw[w] = 0u;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            const uint32_t bits = (km[(4 * bb) / 32] >> ((4 * bb) % 32)) & 0xFu;
+            cw[bb / kFieldsPerWord] += (uint32_t)__popc(bits) << (5 * (bb % kFieldsPerWord));
+        }
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) x4_scan(cw[w], g, ex[w], tot[w]);
+        if (q_ok && kq > 0) {
+            int run = 0;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                int p = run + field5(ex, bb);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if ((km[(4 * bb + r) / 32] >> ((4 * bb + r) % 32)) & 1u) {
+                        const int slot = 16 * bb + 4 * g + r;
+                        out_i[p] = keep ? ulist[slot] : slot;
+                        if (out_s) out_s[p] = key_to_float(kv[bb][r]) * inv_sqrt_d;
+                        ++p;
+                    }
+                }
+                run += field5(tot, bb);
+            }
+        }
+    }
+    if (q_ok) {
+        for (int t = kq + g; t < topk; t += 4) {
+            out_i[t] = -1;
+            if (out_s) out_s[t] = 0.f;
         }
     }
 }
@@ -511,34 +597,31 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
         if (i >= sh.w) n_hi = (int)((i - sh.w) / sh.s);
         if (n_hi > sh.C) n_hi = sh.C;
     }
-    // MFMA path: bf16 storage; the block's scores must fit in LDS.
+    // MFMA path: bf16 storage; every query's candidates fit the register blocks.
     {
         const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
-        const int uc = ((u_cap > 0 ? u_cap : 1) + 15) & ~15;     // rows 16-key aligned
-        const int waves = 4;
+        const int uc = ((u_cap > 0 ? u_cap : 1) + 15) & ~15;     // 16-cell blocks
         const int kw = keep ? keep_w : 0;
-        const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, waves, kw).bytes
-                                      : sel_layout<128>(n_hi, uc, waves, kw).bytes;
-        if (sh.bf16 && lds <= (size_t)kSelLdsMax && sh.C <= kSelMaxCells &&
-            uc <= 4 * kSelMaxKeysPerLane) {
-            const int tq = 16 * waves;
-            dim3 grid((unsigned)((sh.nq + tq - 1) / tq * sh.B * sh.H));
+        const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, kw).bytes
+                                      : sel_layout<128>(n_hi, uc, kw).bytes;
+        if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks) {
+            dim3 grid((unsigned)((sh.nq + 63) / 64 * sh.B * sh.H));
             const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
-            const int kpq_need = uc / 4;          // multiple of 4
-#define FS_SELECT_MFMA(D, KPL)                                                                  \
-            hipLaunchKernelGGL((select_topk_mfma_kernel<D, KPL>), grid, dim3(64 * waves), lds,    \
-                               st, (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, sh.H, \
+            const int nb_need = uc / 16;
+#define FS_SELECT_MFMA(D, NB)                                                                   \
+            hipLaunchKernelGGL((select_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,        \
+                               (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, sh.H,     \
                                sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,            \
                                keep_count, keep_w,                                               \
                                n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, idx, score)
-#define FS_SELECT_KPL(D)                                                                        \
-            if (kpq_need <= 8) FS_SELECT_MFMA(D, 8);                                            \
-            else if (kpq_need <= 16) FS_SELECT_MFMA(D, 16);                                     \
-            else if (kpq_need <= 36) FS_SELECT_MFMA(D, 36);                                     \
-            else if (kpq_need <= 68) FS_SELECT_MFMA(D, 68);                                     \
-            else FS_SELECT_MFMA(D, 132);
-            if (sh.d == 64) { FS_SELECT_KPL(64) } else { FS_SELECT_KPL(128) }
-#undef FS_SELECT_KPL
+#define FS_SELECT_NB(D)                                                                         \
+            if (nb_need <= 2) FS_SELECT_MFMA(D, 2);                                             \
+            else if (nb_need <= 4) FS_SELECT_MFMA(D, 4);                                        \
+            else if (nb_need <= 9) FS_SELECT_MFMA(D, 9);                                        \
+            else if (nb_need <= 17) FS_SELECT_MFMA(D, 17);                                      \
+            else FS_SELECT_MFMA(D, 33);
+            if (sh.d == 64) { FS_SELECT_NB(64) } else { FS_SELECT_NB(128) }
+#undef FS_SELECT_NB
 #undef FS_SELECT_MFMA
             return hipGetLastError();
         }
