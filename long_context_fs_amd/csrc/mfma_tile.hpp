@@ -25,12 +25,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileK = 64;               // keys per tile
-constexpr int kVtPitch = kTileK + 8;     // V^T row pitch (elements), padded against bank conflicts
-
-template <int D>
-struct KPitch {
-    static constexpr int value = D + 8;  // K row pitch (elements), padded
-};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -67,43 +61,6 @@ __device__ __forceinline__ void lds_store16(uint16_t* p, uint4 v)
 __device__ __forceinline__ uint32_t word_of(const uint4& u, int i)
 {
     return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
-// 8 x 8 transpose of bf16 values: in[j] holds row j (elements 0..7, two per
-// dword, low half first); out[e] receives column e (element j = in[j][e]).
-__device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8])
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t a = word_of(in[2 * q], e >> 1);
-            const uint32_t b = word_of(in[2 * q + 1], e >> 1);
-            w[q] = (e & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-        }
-        out[e] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
-
-// Transpose 4 keys x 8 dims (in[r] = key r, two dims per dword) and store the
-// 8 dim-rows of 4 keys (8 bytes each) at dst + e * kVtPitch.
-__device__ __forceinline__ void store_vt_4x8(const uint4 in[4], uint16_t* dst)
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t a0 = word_of(in[0], e >> 1), a1 = word_of(in[1], e >> 1);
-        const uint32_t a2 = word_of(in[2], e >> 1), a3 = word_of(in[3], e >> 1);
-        uint2 w;
-        if (e & 1) {
-            w.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
-            w.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
-        } else {
-            w.x = (a0 & 0xFFFFu) | (a1 << 16);
-            w.y = (a2 & 0xFFFFu) | (a3 << 16);
-        }
-        *reinterpret_cast<uint2*>(dst + e * kVtPitch) = w;
-    }
 }
 
 // ---- XOR-swizzled tiles (unpadded) ------------------------------------------
@@ -150,11 +107,6 @@ __device__ __forceinline__ void store_vt_4x8_sw(const uint4 in[4], uint16_t* vt,
     }
 }
 
-// Key (within its 32-key group) stored at V^T column slot c = 8g + 4h + r.
-__device__ __forceinline__ int vt_slot_key(int g, int j)
-{
-    return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -204,20 +156,21 @@ __device__ __forceinline__ float xrow_sum(float x)
 constexpr float kLazy = 8.f;
 
 // One 64-key tile of flash attention for a wave's 32 queries (two groups of 16).
-//   ks : K tile in LDS, 64 rows of D (pitch KPitch<D>), element type of QFrag
-//   vt : V^T tile in LDS, D rows of 64 key-permuted bf16 (pitch kVtPitch)
+//   ks : swizzled K tile in LDS, 64 rows of D (ksw_off), element type of Frag
+//   vt : swizzled V^T tile in LDS, D rows of 64 key-permuted bf16 (vtsw_off)
 //   qf : the queries as B operands, qf[qg][t] = dims 32t + 8g .. + 7 of query 16 qg + n
+//   masked          : whether some key of the tile may be hidden from some query
+//                     (wave-uniform; when false, keep is not evaluated)
 //   keep(kb, qg, r) : whether key 16 kb + 4 g + r is visible to query 16 qg + n
-//                     (not evaluated when MASKED is false: every key visible)
-// Updates the reference max m_ref (log2 domain, raised lazily), the per-lane
-// partial sums and the O^T accumulators.
-template <int D, bool MASKED, class Frag, class Keep>
+// Updates the reference max m_ref (log2 domain, raised lazily), the O^T
+// accumulators and accl, the softmax denominator accumulated on the matrix core
+// as P^T times a row of ones (every row of accl[qg] holds the running sum).
+template <int D, class Frag, class Keep>
 __device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt,
                                           const Frag (&qf)[2][D / 32], f32x4 (&acc)[D / 16][2],
-                                          float (&m_ref)[2], float (&l_run)[2], float scale_log2,
-                                          Keep keep)
+                                          f32x4 (&accl)[2], float (&m_ref)[2], float scale_log2,
+                                          bool masked, Keep keep)
 {
-    constexpr int KP = KPitch<D>::value;
     constexpr int KS = D / 32, DB = D / 16;
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     f32x4 s[4][2];
@@ -227,7 +180,7 @@ __device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt
     for (int t = 0; t < KS; ++t) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const Frag a = __builtin_bit_cast(Frag, lds_load16(ks + (16 * kb + n) * KP + 32 * t + 8 * g));
+            const Frag a = __builtin_bit_cast(Frag, lds_load16(ks + ksw_off<D>(16 * kb + n, 4 * t + g)));
             s[kb][0] = mfma(a, qf[0][t], s[kb][0]);
             s[kb][1] = mfma(a, qf[1][t], s[kb][1]);
         }
@@ -237,16 +190,19 @@ __device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt
     bool any_rescale = false;
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
+        if (masked) {   // one code path for both kinds of tile: no register copies at the join
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (!keep(kb, qg, r)) s[kb][qg][r] = -INFINITY;
+        }
         // max of the raw scores (scale_log2 > 0 commutes with max)
         float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (MASKED && !keep(kb, qg, r)) s[kb][qg][r] = -INFINITY;
-                tmax = fmaxf(tmax, s[kb][qg][r]);
-            }
-        }
+            for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qg][r]);
         tmax = xrow_max(tmax) * scale_log2;
         // raise the reference only when the tile max exceeds it by > kLazy
         const bool raise = tmax > m_ref[qg] + kLazy;
@@ -255,36 +211,39 @@ __device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt
         any_rescale |= raise;
         m_ref[qg] = m_new;
         const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
-        float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 4; ++r)
                 // v_exp_f32: results below 2^-126 flush to 0, harmless for weights
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][qg][r], scale_log2, neg_m));
-                s[kb][qg][r] = pv;
-                psum += pv;
-            }
+                s[kb][qg][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qg][r], scale_log2, neg_m));
         }
-        l_run[qg] = l_run[qg] * corr[qg] + psum;
         pf[0][qg] = pack_p(s[0][qg], s[1][qg]);
         pf[1][qg] = pack_p(s[2][qg], s[3][qg]);
     }
-    if (__ballot(any_rescale) != 0) {
+    if (__builtin_expect(__ballot(any_rescale) != 0, 0)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            acc[db][0] *= corr[0];
-            acc[db][1] *= corr[1];
+        for (int qg = 0; qg < 2; ++qg) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db][qg] *= corr[qg];
+            accl[qg] *= corr[qg];
         }
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2) {
-            const bf16x8 a = as_bf16x8(lds_load16(vt + (16 * db + n) * kVtPitch + 32 * a2 + 8 * g));
+            const bf16x8 a = as_bf16x8(lds_load16(vt + vtsw_off(16 * db + n, 4 * a2 + g)));
             acc[db][0] = mfma(a, pf[a2][0], acc[db][0]);
             acc[db][1] = mfma(a, pf[a2][1], acc[db][1]);
         }
+    }
+    // after the PV products, so that the no-rescale path needs no register copies
+    const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2) {
+        accl[0] = mfma(ones, pf[a2][0], accl[0]);
+        accl[1] = mfma(ones, pf[a2][1], accl[1]);
     }
 }
 

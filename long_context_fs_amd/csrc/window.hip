@@ -153,7 +153,8 @@ __device__ __forceinline__ void win_load(WinStage<D>& st, const uint16_t* __rest
     }
     if (tid < 2 * D) {
         // keys 32 grp + 16 hh + 4 g + r (r = 0..3), dims 8 dc .. 8 dc + 7
-        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+        const int grp = tid / D, within = tid % D;
+        const int hh = within & 1, g = (within >> 1) & 3, dc = within >> 3;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const long j = kt + 32 * grp + 16 * hh + 4 * g + r;
@@ -177,7 +178,6 @@ __device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, u
                                           long kt, long kv_hi, long i0, int w,
                                           const float2* __restrict__ table)
 {
-    constexpr int KP = mf::KPitch<D>::value;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < WinStage<D>::KC; ++it) {
@@ -192,12 +192,13 @@ __device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, u
         o.y = rotate_pack(st.k[it].y, a.z, a.w);
         o.z = rotate_pack(st.k[it].z, b.x, b.y);
         o.w = rotate_pack(st.k[it].w, b.z, b.w);
-        mf::lds_store16(ks + kr * KP + part * 8, o);
+        mf::lds_store16(ks + mf::ksw_off<D>(kr, part), o);
     }
     if (tid < 2 * D) {
-        const int hh = tid & 1, g = (tid >> 1) & 3, grp = (tid >> 3) & 1, dc = tid >> 4;
+        const int grp = tid / D, within = tid % D;
+        const int hh = within & 1, g = (within >> 1) & 3, dc = within >> 3;
         // V^T column slot 8 g + 4 hh + r of the 32-key group holds key 16 hh + 4 g + r
-        mf::store_vt_4x8(st.v, vt + (dc * 8) * mf::kVtPitch + 32 * grp + 8 * g + 4 * hh);
+        mf::store_vt_4x8_sw(st.v, vt, dc, 32 * grp + 8 * g + 4 * hh);
     }
 }
 
@@ -211,11 +212,10 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     float scale_log2, uint16_t* __restrict__ o, int64_t os0, int64_t os1, int64_t os2)
 {
     using namespace mf;
-    constexpr int KP = KPitch<D>::value;
     constexpr int KS = D / 32;     // k-steps of the QK^T contraction
     constexpr int DB = D / 16;     // 16-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * kVtPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK * D];    // swizzled rows
+    __shared__ __attribute__((aligned(16))) uint16_t vt[D * kTileK];    // swizzled rows
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
@@ -259,10 +259,11 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
         }
     }
 
-    f32x4 acc[DB][2];
+    f32x4 acc[DB][2], accl[2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    accl[0] = accl[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};
 
     WinStage<D> stage;
     win_load<D>(stage, kh, vh, kvs2, kv_lo, kv_hi, i0, w, table);
@@ -279,15 +280,13 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
         if (work) {
             // every key of the tile inside every query's window: no masking needed
             const bool full = kt >= qw_last - w && kt + kTileK - 1 <= qw0;
+            // i - j for query 16 qg + n and key 16 kb + 4 g + r, in 32 bits (|i - j| < 2^31)
+            const int d0 = (int)(qw0 - kt) + n - 4 * g;
             auto keep = [&](int kb, int qg, int r) {
-                const long i = qw0 + 16 * qg + n;
-                const long j = kt + 16 * kb + 4 * g + r;
-                return j <= i && j >= i - w;
+                const int d = d0 + 16 * (qg - kb) - r;
+                return d >= 0 && d <= w;
             };
-            if (full)
-                attn_tile<D, false>(ks, vt, qf, acc, m_run, l_run, scale_log2, keep);
-            else
-                attn_tile<D, true>(ks, vt, qf, acc, m_run, l_run, scale_log2, keep);
+            attn_tile<D>(ks, vt, qf, acc, accl, m_run, scale_log2, !full, keep);
         }
         __syncthreads();
         if (tile + 1 < n_tiles) {
@@ -299,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const long i = qw0 + 16 * qg + n;
-        const float l = xrow_sum(l_run[qg]);
+        const float l = accl[qg][0];    // every row of the ones product is the full sum
         if (i > i_end) continue;
         const float inv = 1.f / l;
         uint16_t* orow = o + b * os0 + h * os1 + (i - q_pos0) * os2;
