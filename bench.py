@@ -117,7 +117,7 @@ def run_workload(name, steps, warmup, torch, fs):
         mark(3)
         fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)
         mark(4)
-        fs.fs_sparse_attn(p, q, k, v, fwd.idx, fwd.topk, fwd.rms_eps, fwd.o_lr)
+        fs.fs_sparse_attn(p, q, k, v, fwd.idx, fwd.topk, fwd.rms_eps, fwd.o_lr, fwd.ws_sparse)
         mark(5)
         fs.fs_combine(p, fwd.o_sr, fwd.o_lr, alpha, fwd.o)
         mark(6)
@@ -231,7 +231,7 @@ def run_phase(name, phase, reps, torch, fs):
         "select": lambda: fs.fs_select_topk(p, q, f.kbar, f.keep, f.keep_count, f.keep_w,
                                             f.topk, f.idx, None),
         "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),
-        "sparse": lambda: fs.fs_sparse_attn(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_lr),
+        "sparse": lambda: fs.fs_sparse_attn(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_lr, f.ws_sparse),
         "combine": lambda: fs.fs_combine(p, f.o_sr, f.o_lr, alpha, f.o),
     }
     for _ in range(reps):

@@ -110,13 +110,22 @@ fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k
                          float rope_base, void* workspace, size_t ws_bytes, void* o_sr,
                          void* stream);
 
+/* Bytes of device workspace with which fs_sparse_attn splits each query's cells
+ * over several workgroups (0 when the query range already fills the device). */
+fs_status fs_sparse_workspace_size(const fs_problem* problem, size_t* bytes);
+
 /* Long-range readout, eq. 9: u_i = softmax_j(q_i.k_j/sqrt(d)) v_j over the tokens
  * of the cells listed in idx[b][h][t][0 .. topk-1] (-1 entries ignored; cells
  * must be < C and distinct), unrotated; o_lr_i = u_i / sqrt(mean(u_i^2) + rms_eps).
- * A query with no selected cell gets o_lr = 0. */
+ * A query with no selected cell gets o_lr = 0.
+ * workspace (nullable, device, overwritten): with at least
+ * fs_sparse_workspace_size bytes, a short query range (decode) has its cells split
+ * over workgroups whose partial softmax states are then merged; NULL runs
+ * unsplit.  A non-NULL workspace below that size is an error.  Calls sharing a
+ * workspace must not overlap in time. */
 fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
-                         const int32_t* idx, int32_t topk, float rms_eps, void* o_lr,
-                         void* stream);
+                         const int32_t* idx, int32_t topk, float rms_eps, void* workspace,
+                         size_t ws_bytes, void* o_lr, void* stream);
 
 /* Range combination, eq. 2: o = o_sr + alpha[h] * o_lr.  alpha: float32 [H]. */
 fs_status fs_combine(const fs_problem* problem, const void* o_sr, const void* o_lr,

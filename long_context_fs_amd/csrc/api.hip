@@ -213,9 +213,19 @@ fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k
                     "fs_window_attn");
 }
 
+fs_status fs_sparse_workspace_size(const fs_problem* problem, size_t* bytes)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (!bytes) return fail(FS_ERR_INVALID, "bytes is NULL");
+    *bytes = fs::sparse_ws_bytes(sh);
+    g_err[0] = 0;
+    return FS_OK;
+}
+
 fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
-                         const int32_t* idx, int32_t topk, float rms_eps, void* o_lr,
-                         void* stream)
+                         const int32_t* idx, int32_t topk, float rms_eps, void* workspace,
+                         size_t ws_bytes, void* o_lr, void* stream)
 {
     fs::Shape sh;
     FS_CHECK(check_problem(problem, &sh));
@@ -223,7 +233,11 @@ fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k
     if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
     if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
     if (!(rms_eps >= 0.0f)) return fail(FS_ERR_INVALID, "rms_eps must be >= 0");
-    return from_hip(fs::launch_sparse(sh, q, k, v, idx, topk, rms_eps, o_lr, (hipStream_t)stream),
+    if (workspace && ws_bytes < fs::sparse_ws_bytes(sh))
+        return fail(FS_ERR_INVALID, "workspace of %zu bytes, need %zu", ws_bytes,
+                    fs::sparse_ws_bytes(sh));
+    return from_hip(fs::launch_sparse(sh, q, k, v, idx, topk, rms_eps, workspace, o_lr,
+                                      (hipStream_t)stream),
                     "fs_sparse_attn");
 }
 

@@ -28,8 +28,14 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
 size_t rope_table_bytes(const Shape& sh);
 hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
                          double rope_base, void* table, void* o_sr, hipStream_t st);
+// Workgroups over which the readout splits each query's cells (1: unsplit), and
+// the workspace bytes of their partial softmax states.
+int sparse_splits(const Shape& sh);
+size_t sparse_ws_bytes(const Shape& sh);
+
 hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const void* v,
-                         const int32_t* idx, int topk, float rms_eps, void* o_lr, hipStream_t st);
+                         const int32_t* idx, int topk, float rms_eps, void* ws, void* o_lr,
+                         hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const void* o_sr, const void* o_lr, const float* alpha,
                           void* o, hipStream_t st);
 

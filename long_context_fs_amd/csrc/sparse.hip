@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t kvs0, int64_t kvs1,
     int64_t kvs2, int H, int BH, int nq, int C, const int32_t* __restrict__ idx, int topk,
     float scale_log2, float rms_eps, uint16_t* __restrict__ o, int64_t os0, int64_t os1,
-    int64_t os2)
+    int64_t os2, int n_split, float* __restrict__ ws_acc, float2* __restrict__ ws_ml)
 {
     using namespace mf;
     constexpr int KS = D / 32, DB = D / 16;
@@ -360,10 +360,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
+    // workgroup -> (head, split, query tile); the head is the fastest index (XCD locality)
     const TileOfBlock tb = xcd_tile(BH);
     const long bh = tb.bh;
+    const int split = (int)(tb.tile % n_split);
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const long t0 = tb.tile * kSpQ;
+    const long t0 = (tb.tile / n_split) * kSpQ;
     const int n_rows = nq - t0 < kSpQ ? (int)(nq - t0) : kSpQ;
     const int32_t* idx_blk = idx + (bh * nq + t0) * (long)topk;
 
@@ -433,17 +435,20 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     float m_run[2] = {-INFINITY, -INFINITY};
 
     const SpOffsets<D> offs = sp_offsets<D>(kvs2);
-    const int n_tiles = (n_union + 1) / 2;
+    // this workgroup's share of the union's 64-key tiles
+    const int n_all = (n_union + 1) / 2;
+    const int u_begin = (int)((long)n_all * split / n_split);
+    const int u_end = (int)((long)n_all * (split + 1) / n_split);
     SpStage<D> stage;
-    if (n_tiles > 0) {
-        sp_load<D>(stage, offs, kh, vh, kvs2, ulist, n_union, 0);
+    if (u_begin < u_end) {
+        sp_load<D>(stage, offs, kh, vh, kvs2, ulist, n_union, u_begin);
         sp_store<D>(stage, ks, vt);
     }
     __syncthreads();
     uint32_t qw[2] = {0u, 0u};
-    for (int u = 0; u < n_tiles; ++u) {
-        if (u + 1 < n_tiles) sp_load<D>(stage, offs, kh, vh, kvs2, ulist, n_union, u + 1);
-        if ((u & 15) == 0) {
+    for (int u = u_begin; u < u_end; ++u) {
+        if (u + 1 < u_end) sp_load<D>(stage, offs, kh, vh, kvs2, ulist, n_union, u + 1);
+        if ((u & 15) == 0 || u == u_begin) {
             qw[0] = qbits[qbit_row + (u >> 4)];                  // rows past n_rows are zero
             qw[1] = qbits[qbit_row + 16 * L.qpitch + (u >> 4)];
         }
@@ -453,10 +458,26 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
         if (__ballot(sel[0][0] || sel[0][1] || sel[1][0] || sel[1][1]) != 0)
             sp_tile<D>(ks, vt, qf, acc, accl, m_run, scale_log2, sel);
         __syncthreads();
-        if (u + 1 < n_tiles) {
+        if (u + 1 < u_end) {
             sp_store<D>(stage, ks, vt);
             __syncthreads();
         }
+    }
+
+    if (n_split > 1) {
+        // ---- partial softmax state of this split: (m, l) and the unnormalised O
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+            const int r = 32 * wv + 16 * qg + n;
+            if (r >= n_rows) continue;
+            const long slot = (bh * nq + t0 + r) * n_split + split;
+            if (g == 0) ws_ml[slot] = make_float2(m_run[qg], accl[qg][0]);
+            float* a = ws_acc + slot * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<f32x4*>(a + 16 * db + 4 * g) = acc[db][qg];
+        }
+        return;
     }
 
     // ---- epilogue: normalise, RMSNorm over d, store ------------------------
@@ -486,25 +507,104 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     }
 }
 
+// Merge of the split readout: per query, the partial states (m_s, l_s, O_s)
+// (reference maxima in the log2 domain) combine as O = sum_s 2^(m_s - M) O_s over
+// l = sum_s 2^(m_s - M) l_s with M = max_s m_s; then RMSNorm.  One wavefront per
+// query, D / 64 dims per lane.
+template <int D>
+__global__ __launch_bounds__(256) void sparse_merge_kernel(const float* __restrict__ ws_acc,
+                                                           const float2* __restrict__ ws_ml,
+                                                           int H, int nq, long n_rows_all,
+                                                           int n_split, float rms_eps,
+                                                           uint16_t* __restrict__ o, int64_t os0,
+                                                           int64_t os1, int64_t os2)
+{
+    constexpr int R = D / kWave;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);    // = bh * nq + t
+    if (row >= n_rows_all) return;
+    const int lane = threadIdx.x & 63;
+    const float2* ml = ws_ml + row * n_split;
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ml[sp].x);
+    float acc[R] = {};
+    float l = 0.f;
+    if (M != -INFINITY) {
+        for (int sp = 0; sp < n_split; ++sp) {
+            const float2 e = ml[sp];
+            const float w = __builtin_amdgcn_exp2f(e.x - M);    // 0 for an empty split
+            l = fmaf(w, e.y, l);
+            const float* a = ws_acc + (row * n_split + sp) * D;
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(w, a[lane + r * kWave], acc[r]);
+        }
+    }
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        acc[r] *= inv_l;
+        ss = fmaf(acc[r], acc[r], ss);
+    }
+    ss = wave_sum(ss);
+    const float inv_rms = 1.f / sqrtf(ss / (float)D + rms_eps);
+    const long bh = row / nq, t = row - bh * nq;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    uint16_t* orow = o + b * os0 + h * os1 + t * os2;
+#pragma unroll
+    for (int r = 0; r < R; ++r) store1<Bf16>(orow + lane + r * kWave, acc[r] * inv_rms);
+}
+
+// Split count: enough workgroups to give every CU two, at most 32 per query tile.
+int sparse_splits(const Shape& sh)
+{
+    if (!sh.bf16 || sh.C > kSpMaxCells || sh.nq == 0) return 1;
+    const long base = (sh.nq + kSpQ - 1) / kSpQ * (long)sh.B * sh.H;
+    if (base >= 512) return 1;
+    const long want = (512 + base - 1) / base;
+    return (int)(want < 32 ? want : 32);
+}
+
+size_t sparse_ws_bytes(const Shape& sh)
+{
+    const int S = sparse_splits(sh);
+    if (S <= 1) return 0;
+    const size_t rows = (size_t)sh.B * sh.H * sh.nq * S;
+    return rows * ((size_t)sh.d * sizeof(float) + sizeof(float2));
+}
+
 hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const void* v,
-                         const int32_t* idx, int topk, float rms_eps, void* o_lr, hipStream_t st)
+                         const int32_t* idx, int topk, float rms_eps, void* ws, void* o_lr,
+                         hipStream_t st)
 {
     if (sh.nq == 0) return hipSuccess;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
     const size_t lds = sh.d == 64 ? sp_layout<64>(sh.C, topk).bytes
                                   : sp_layout<128>(sh.C, topk).bytes;
     if (sh.bf16 && sh.C <= kSpMaxCells && lds <= 160 * 1024) {
+        const int S = ws ? sparse_splits(sh) : 1;
+        const long rows_all = (long)sh.B * sh.H * sh.nq;
+        float* ws_acc = S > 1 ? static_cast<float*>(ws) : nullptr;
+        float2* ws_ml = S > 1 ? reinterpret_cast<float2*>(ws_acc + rows_all * S * sh.d) : nullptr;
         const long n_tiles = (sh.nq + kSpQ - 1) / kSpQ;
-        dim3 grid((unsigned)(n_tiles * sh.B * sh.H)), block(256);
+        dim3 grid((unsigned)(n_tiles * S * sh.B * sh.H)), block(256);
 #define FS_SPARSE_MFMA(D)                                                                         \
         hipLaunchKernelGGL((sparse_attn_mfma_kernel<D>), grid, block, lds, st,                    \
                            (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2],                      \
                            (const uint16_t*)k, (const uint16_t*)v, sh.kvs[0], sh.kvs[1],          \
                            sh.kvs[2], sh.H, sh.B * sh.H, sh.nq, sh.C, idx, topk, scale_log2,      \
                            rms_eps,                                                               \
-                           (uint16_t*)o_lr, sh.os[0], sh.os[1], sh.os[2])
+                           (uint16_t*)o_lr, sh.os[0], sh.os[1], sh.os[2], S, ws_acc, ws_ml)
         if (sh.d == 64) FS_SPARSE_MFMA(64); else FS_SPARSE_MFMA(128);
 #undef FS_SPARSE_MFMA
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess || S <= 1) return err;
+        dim3 mgrid((unsigned)((rows_all + 3) / 4));
+#define FS_SPARSE_MERGE(D)                                                                        \
+        hipLaunchKernelGGL((sparse_merge_kernel<D>), mgrid, dim3(256), 0, st, ws_acc, ws_ml,      \
+                           sh.H, sh.nq, rows_all, S, rms_eps, (uint16_t*)o_lr, sh.os[0],          \
+                           sh.os[1], sh.os[2])
+        if (sh.d == 64) FS_SPARSE_MERGE(64); else FS_SPARSE_MERGE(128);
+#undef FS_SPARSE_MERGE
         return hipGetLastError();
     }
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);

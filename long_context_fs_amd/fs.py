@@ -18,7 +18,8 @@ FS_F32, FS_BF16 = 0, 1
 CELL = 32
 
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
-           "fs_workspace_size", "fs_window_attn", "fs_sparse_attn", "fs_combine",
+           "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
+           "fs_combine",
            "fs_status_string", "fs_last_error")
 
 
@@ -58,7 +59,8 @@ def load(path: str | None = None):
         "fs_select_topk": [P, vp, vp, vp, vp, i32, i32, vp, vp, vp],
         "fs_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_window_attn": [P, vp, vp, vp, f32, vp, C.c_size_t, vp, vp],
-        "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, vp],
+        "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
+        "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, C.c_size_t, vp, vp],
         "fs_combine": [P, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
@@ -152,9 +154,19 @@ def fs_window_attn(prob, q, k, v, rope_base, workspace, o_sr, stream=None):
                                                    _p(o_sr), _s(stream)))
 
 
-def fs_sparse_attn(prob, q, k, v, idx, topk, rms_eps, o_lr, stream=None):
+def fs_sparse_workspace_size(prob) -> int:
+    n = C.c_size_t()
+    _check("fs_sparse_workspace_size", load().fs_sparse_workspace_size(C.byref(prob), C.byref(n)))
+    return n.value
+
+
+def fs_sparse_attn(prob, q, k, v, idx, topk, rms_eps, o_lr, workspace=None, stream=None):
+    """workspace: None (unsplit) or a device buffer of >= fs_sparse_workspace_size bytes."""
+    ws, nbytes = (None, 0) if workspace is None else \
+        (_p(workspace), workspace.numel() * workspace.element_size())
     _check("fs_sparse_attn", load().fs_sparse_attn(C.byref(prob), _p(q), _p(k), _p(v), _p(idx),
-                                                   topk, float(rms_eps), _p(o_lr), _s(stream)))
+                                                   topk, float(rms_eps), ws, nbytes, _p(o_lr),
+                                                   _s(stream)))
 
 
 def fs_combine(prob, o_sr, o_lr, alpha, o, stream=None):
@@ -192,6 +204,8 @@ class FsForward:
         self.idx = torch.empty((B, H, n_q, topk), dtype=i32, device=device)
         self.score = torch.empty((B, H, n_q, topk), dtype=f32, device=device)
         self.ws = torch.empty(fs_workspace_size(self.prob), dtype=torch.uint8, device=device)
+        nsp = fs_sparse_workspace_size(self.prob)
+        self.ws_sparse = torch.empty(nsp, dtype=torch.uint8, device=device) if nsp else None
         self.o_sr = torch.empty((B, H, n_q, d), dtype=tdt, device=device)
         self.o_lr = torch.empty_like(self.o_sr)
         self.o = torch.empty_like(self.o_sr)
@@ -205,7 +219,8 @@ class FsForward:
         fs_select_topk(p, q, self.kbar, self.keep, self.keep_count, self.keep_w, self.topk,
                        self.idx, self.score if keep_score else None, stream)
         fs_window_attn(p, q, k, v, self.rope_base, self.ws, self.o_sr, stream)
-        fs_sparse_attn(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_lr, stream)
+        fs_sparse_attn(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_lr, self.ws_sparse,
+                       stream)
         fs_combine(p, self.o_sr, self.o_lr, alpha, self.o, stream)
         return self.o
 

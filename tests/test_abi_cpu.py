@@ -103,8 +103,16 @@ def test_call_specific_limits(lib):
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, 0, 0, FAKE, None, None) == 2
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, 0, 65, FAKE, None, None) == 2
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, FAKE, None, 64, 8, FAKE, None, None) == 1
-    assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, None, 8, 1e-6, FAKE, None) == 1
-    assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, -1.0, FAKE, None) == 1
+    assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, None, 8, 1e-6, None, 0, FAKE,
+                              None) == 1
+    assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, -1.0, None, 0, FAKE,
+                              None) == 1
+    need = C.c_size_t()
+    assert lib.fs_sparse_workspace_size(C.byref(p), C.byref(need)) == 0
+    if need.value > 0:    # an undersized workspace is an error, not a silent fallback
+        assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, 1e-6, FAKE, 16, FAKE,
+                                  None) == 1
+        assert b"workspace" in lib.fs_last_error()
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 10000.0, FAKE, 16, FAKE, None) == 1
     assert b"workspace" in lib.fs_last_error()
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 0.5, FAKE, 1 << 30, FAKE, None) == 1

@@ -239,6 +239,37 @@ def test_small_sparse(name):
     assert (got[none] == 0).all()
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_decode", "bf16_d64_hot", "bf16_d64_noprune_bigk"])
+def test_sparse_split_and_unsplit_agree(name):
+    """The split readout (partial softmax states merged) and the unsplit one give
+    the same o_lr, both within tolerance of the oracle's eq. 9 rows."""
+    wl, x, g, ref = small_case(name)
+    from long_context_fs_amd import fs as fsb
+    q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+    fwd = FsForward.for_workload(wl)
+    p = fwd.prob
+    assert fsb.fs_sparse_workspace_size(p) > 0       # a short query range: split
+    idx = torch.from_numpy(g["idx"]).cuda()
+    outs = []
+    for ws in (None, fwd.ws_sparse):
+        o = torch.full_like(fwd.o_lr, float("nan"))
+        fsb.fs_sparse_attn(p, q, k, v, idx, wl.topk, wl.rms_eps, o, ws)
+        torch.cuda.synchronize()
+        outs.append(o.float().cpu().numpy())
+    rows = all_rows(wl)
+    po = oracle.problem_from(wl)
+    want = np.stack([orc().sparse_row(po, x["q"][b, h, t], x["k"][b, h], x["v"][b, h],
+                                      g["idx"][b, h, t][g["idx"][b, h, t] >= 0])
+                     for b, h, t in rows])
+    for got in outs:
+        got = np.stack([got[b, h, t] for b, h, t in rows])
+        assert np.isfinite(got).all()
+        err = row_rel_err(got, want)
+        assert err.max() <= TOL[wl.dtype], err.max()
+    assert row_rel_err(outs[0].reshape(-1, wl.head_dim),
+                       outs[1].reshape(-1, wl.head_dim).astype(np.float64)).max() <= 1e-2
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_combine_and_end_to_end(name):
     wl, x, g, ref = small_case(name)
