@@ -5,9 +5,15 @@
 // workgroup builds the row of one n: Recent_W({c < n}) U TopP_{c < n}(a_c).
 // The P-th largest priority is found exactly by a bitwise search over the
 // 32-bit patterns of a_c (norms are >= 0, so their bit patterns order like the
-// values), 32 block-wide counts of "key >= candidate threshold".  Ties at the
-// threshold go to the larger cell index.  The row is then written in ascending
-// cell order by a chunked block prefix sum (wave ballot + popcount).
+// values): block-wide counts of "key >= candidate threshold".  Ties at the
+// threshold go to the larger cell index.  The row is written in ascending cell
+// order.
+//
+// Rows of up to 8192 candidates keep their keys in registers (cell 256 j + t in
+// slot j of thread t): one pass over HBM, one barrier per search step, the
+// search starts below the bits every key shares, and the output positions come
+// from one round of per-wave ballot counts.  Longer rows use the streaming
+// kernel below it.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 
@@ -101,13 +107,177 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
     if (tid == 0) keep_count[bh * n_rows + r] = written;
 }
 
+// Bitwise search and compaction with the row's keys in registers.
+template <int KPT>
+__global__ __launch_bounds__(kPruneThreads) void prune_reg_kernel(
+    const float* __restrict__ amax, int C, int n_lo, int n_rows, int n_recent, int budget,
+    int keep_w, int32_t* __restrict__ keep, int32_t* __restrict__ keep_count)
+{
+    __shared__ int red[2][kPruneWaves];         // double-buffered: one barrier per block sum
+    __shared__ int cnt[KPT][kPruneWaves];       // per chunk and wave: kept (then equal) counts
+    __shared__ int cnt_eq[KPT][kPruneWaves];
+    const int r = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int n = n_lo + r;
+    const uint32_t* key = reinterpret_cast<const uint32_t*>(amax + bh * C);
+    int32_t* out = keep + (bh * n_rows + r) * (long)keep_w;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+    uint32_t kv[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int c = 256 * j + tid;
+        kv[j] = c < n ? key[c] : 0u;
+    }
+    int flip = 0;
+    auto bsum = [&](int x) {
+        x = wave_sum_int(x);
+        if (lane == 0) red[flip][wv] = x;
+        __syncthreads();
+        int t = 0;
+#pragma unroll
+        for (int i = 0; i < kPruneWaves; ++i) t += red[flip][i];
+        flip ^= 1;
+        return t;
+    };
+
+    const bool take_all = n <= budget;
+    uint32_t thr = 0;
+    int n_eq = 0, need_eq = 0;
+    if (!take_all) {
+        // bits above the highest one in which two valid keys differ are common
+        uint32_t k_and = 0xFFFFFFFFu, k_or = 0u;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (256 * j + tid < n) {
+                k_and &= kv[j];
+                k_or |= kv[j];
+            }
+        }
+        // block AND / OR via the two sums of per-bit flags would cost 32 sums;
+        // instead reduce the pair through the red buffers directly
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            k_and &= (uint32_t)__shfl_xor((int)k_and, m, kWave);
+            k_or |= (uint32_t)__shfl_xor((int)k_or, m, kWave);
+        }
+        if (lane == 0) {
+            red[flip][wv] = (int)k_and;
+            red[flip ^ 1][wv] = (int)k_or;
+        }
+        __syncthreads();
+        uint32_t a_all = 0xFFFFFFFFu, o_all = 0u;
+#pragma unroll
+        for (int i = 0; i < kPruneWaves; ++i) {
+            a_all &= (uint32_t)red[flip][i];
+            o_all |= (uint32_t)red[flip ^ 1][i];
+        }
+        __syncthreads();
+        const uint32_t diff = a_all ^ o_all;
+        int top = 31;
+        if (diff == 0u) {
+            thr = o_all;                 // every key equal: the ties decide
+            top = -1;
+        } else {
+            top = 31 - __clz(diff);
+            thr = top >= 31 ? 0u : (o_all & ~((2u << top) - 1u));
+        }
+        // largest thr with #{c < n : key_c >= thr} >= budget, i.e. the budget-th largest key
+        for (int bit = top; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) c += kv[j] >= cand;    // kv = 0 past n, cand >= 1
+            if (bsum(c) >= budget) thr = cand;
+        }
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool valid = 256 * j + tid < n;
+            gt += valid && kv[j] > thr;
+            eq += valid && kv[j] == thr;
+        }
+        const int n_gt = bsum(gt);
+        n_eq = bsum(eq);
+        need_eq = budget - n_gt;     // equal keys to keep, those with the largest indices
+    }
+
+    // ---- kept flags, then positions in ascending cell order ------------------
+    const bool ties = !take_all && n_eq != need_eq;
+    if (ties) {
+        // rank of each equal key among the equal keys, in cell order
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool is_eq = 256 * j + tid < n && kv[j] == thr;
+            const uint64_t m = __ballot(is_eq);
+            if (lane == 0) cnt_eq[j][wv] = __popcll(m);
+        }
+        __syncthreads();
+    }
+    uint32_t kept_bits = 0u;
+    {
+        int eq_before = 0;          // equal keys in earlier chunks (ties only)
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int c = 256 * j + tid;
+            const bool valid = c < n;
+            bool kept = valid && (take_all || kv[j] > thr || c >= n - n_recent);
+            if (!take_all && valid && kv[j] == thr) {
+                if (!ties) {
+                    kept = true;
+                } else {
+                    const uint64_t m = __ballot(kv[j] == thr && valid);
+                    int rank = eq_before + lanes_below(m);
+#pragma unroll
+                    for (int i = 0; i < kPruneWaves; ++i) rank += i < wv ? cnt_eq[j][i] : 0;
+                    kept = kept || rank >= n_eq - need_eq;
+                }
+            }
+            if (ties) {
+#pragma unroll
+                for (int i = 0; i < kPruneWaves; ++i) eq_before += cnt_eq[j][i];
+            }
+            kept_bits |= (uint32_t)kept << j;
+            const uint64_t km = __ballot(kept);
+            if (lane == 0) cnt[j][wv] = __popcll(km);
+        }
+    }
+    __syncthreads();
+    int written = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const bool kept = (kept_bits >> j) & 1u;
+        const uint64_t km = __ballot(kept);
+        int pos = written + lanes_below(km);
+#pragma unroll
+        for (int i = 0; i < kPruneWaves; ++i) {
+            pos += i < wv ? cnt[j][i] : 0;
+            written += cnt[j][i];
+        }
+        if (kept) out[pos] = 256 * j + tid;
+    }
+    for (int t = written + tid; t < keep_w; t += kPruneThreads) out[t] = -1;
+    if (tid == 0) keep_count[bh * n_rows + r] = written;
+}
+
 hipError_t launch_prune(const Shape& sh, const float* amax, int n_lo, int n_rows, int n_recent,
                         int budget, int32_t* keep, int32_t* keep_count, hipStream_t st)
 {
     if (n_rows == 0) return hipSuccess;
     dim3 grid((unsigned)n_rows, (unsigned)(sh.B * sh.H)), block(kPruneThreads);
-    hipLaunchKernelGGL(prune_kernel, grid, block, 0, st, amax, sh.C, n_lo, n_rows, n_recent,
-                       budget, n_recent + budget, keep, keep_count);
+    const int n_max = n_lo + n_rows - 1;
+    const int kpt = (n_max + kPruneThreads - 1) / kPruneThreads;
+#define FS_PRUNE_REG(K)                                                                         \
+    hipLaunchKernelGGL((prune_reg_kernel<K>), grid, block, 0, st, amax, sh.C, n_lo, n_rows,     \
+                       n_recent, budget, n_recent + budget, keep, keep_count)
+    if (kpt <= 4) FS_PRUNE_REG(4);
+    else if (kpt <= 8) FS_PRUNE_REG(8);
+    else if (kpt <= 16) FS_PRUNE_REG(16);
+    else if (kpt <= 32) FS_PRUNE_REG(32);
+    else
+        hipLaunchKernelGGL(prune_kernel, grid, block, 0, st, amax, sh.C, n_lo, n_rows, n_recent,
+                           budget, n_recent + budget, keep, keep_count);
+#undef FS_PRUNE_REG
     return hipGetLastError();
 }
 
