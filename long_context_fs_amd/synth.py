@@ -55,10 +55,21 @@ class Workload:
     needle_queries: int = 0         # last queries aligned with the needle
     alpha: float | None = None      # fixed alpha for every head; None = U[0,1] per head
     seed: int = 0
+    prior_lambda: float = 0.0       # eq. 7 prior: head h uses lambda * (h + 1) / H ...
+    prior_sigma: float = 0.0        # ... and sigma * 2^(h mod 4); lambda 0 = no prior
 
     @property
     def n_cells(self) -> int:
         return self.n_ctx // self.cell
+
+    def prior_arrays(self):
+        """Per-head (lambda_h, sigma_h) as float32 arrays, or (None, None)."""
+        if self.prior_lambda <= 0:
+            return None, None
+        h = np.arange(self.heads)
+        lam = np.float32(self.prior_lambda) * (h + 1).astype(np.float32) / np.float32(self.heads)
+        sig = np.float32(self.prior_sigma) * np.float32(2.0) ** (h % 4).astype(np.float32)
+        return lam.astype(np.float32), sig.astype(np.float32)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -84,6 +95,12 @@ WORKLOADS = {
         name="decode_b1h8_n262144_q256_d128_bf16", batch=1, heads=8, n_ctx=262144,
         head_dim=128, dtype="bf16", n_q=256, q_pos0=262144 - 256, topk=32, budget=512,
         structure="needle", needle_queries=256, seed=5),
+    # the 64k prefill with eq. 7's position prior switched on (lambda_h up to 0.1,
+    # sigma_h from 2048 to 16384 tokens)
+    "prefill_b1h8_n65536_d128_bf16_prior": Workload(
+        name="prefill_b1h8_n65536_d128_bf16_prior", batch=1, heads=8, n_ctx=65536,
+        head_dim=128, dtype="bf16", n_q=65536, q_pos0=0, topk=32, budget=256,
+        structure="needle", needle_queries=64, seed=4, prior_lambda=0.1, prior_sigma=2048.0),
 }
 
 # Short aliases in the order the workloads are listed above.

@@ -3,6 +3,6 @@
 TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
 CPU-baseline leg import this package.  It shares no code with the HIP path.
 """
-from .pyoracle import Oracle, Problem, build, make_problem, problem_from
+from .pyoracle import Oracle, Problem, build, make_problem, problem_from, with_prior
 
-__all__ = ["Oracle", "Problem", "build", "make_problem", "problem_from"]
+__all__ = ["Oracle", "Problem", "build", "make_problem", "problem_from", "with_prior"]

@@ -117,8 +117,18 @@ int or_prune_row(const or_problem* p, const double* amax, int n, int* keep, doub
 }
 
 /* ---- query-dependent scoring and top-K (eq. 7 with lambda_h = 0) ------- */
-int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
-                  const int* cand, int n_cand, int* sel, double* gap_rel, double* cand_scores)
+/* ---- eq. 7's position prior ------------------------------------------ */
+double or_prior(const or_problem* p, int head, long long i, int c, double a_c)
+{
+    if (!p->prior_lambda || !p->prior_sigma || head < 0) return 0.0;
+    const double lam = p->prior_lambda[head], sig = p->prior_sigma[head];
+    const double p_c = ((double)c + 0.5) * (double)p->cell;       /* eq. 5 */
+    return lam * a_c * erf(((double)i - p_c) / (2.0 * sig));
+}
+
+int or_select_row_at(const or_problem* p, int head, long long i, const float* q_row,
+                     const double* kbar, const double* amax, const int* cand, int n_cand,
+                     int* sel, double* gap_rel, double* cand_scores)
 {
     const int d = p->head_dim;
     if (gap_rel) *gap_rel = INFINITY;
@@ -128,7 +138,8 @@ int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
         const double* kb = kbar + (size_t)cand[t] * d;
         double dot = 0.0;
         for (int e = 0; e < d; ++e) dot += (double)q_row[e] * kb[e];
-        order[t].key = dot / sqrt((double)d);
+        order[t].key = dot / sqrt((double)d) +
+                       (amax ? or_prior(p, head, i, cand[t], amax[cand[t]]) : 0.0);
         order[t].cell = cand[t];
         if (cand_scores) cand_scores[t] = order[t].key;
     }
@@ -140,6 +151,13 @@ int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
     qsort(sel, (size_t)cnt, sizeof(int), or_cmp_int);
     free(order);
     return cnt;
+}
+
+int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
+                  const int* cand, int n_cand, int* sel, double* gap_rel, double* cand_scores)
+{
+    return or_select_row_at(p, -1, 0, q_row, kbar, NULL, cand, n_cand, sel, gap_rel,
+                            cand_scores);
 }
 
 /* ---- softmax-weighted sum of value rows over a list of token positions -- */
@@ -217,9 +235,9 @@ void or_sparse_row(const or_problem* p, const float* q_row, const float* k_head,
 }
 
 /* ---- one query row of the whole forward (eq. 2) ------------------------ */
-static void or_forward_one(const or_problem* p, const float* q_row, const float* k_head,
-                           const float* v_head, const double* kbar, const double* amax,
-                           double alpha, long long i,
+static void or_forward_one(const or_problem* p, int head, const float* q_row,
+                           const float* k_head, const float* v_head, const double* kbar,
+                           const double* amax, double alpha, long long i,
                            const int* keep_ovr, int keep_ovr_n,
                            const int* sel_ovr, int sel_ovr_n,
                            double* o, double* o_sr, double* o_lr,
@@ -246,7 +264,8 @@ static void or_forward_one(const or_problem* p, const float* q_row, const float*
         n_chosen = sel_ovr_n;
         memcpy(chosen, sel_ovr, sizeof(int) * (size_t)n_chosen);
     } else {
-        n_chosen = or_select_row(p, q_row, kbar, keep, n_keep, chosen, &sg, NULL);
+        n_chosen = or_select_row_at(p, head, i, q_row, kbar, amax, keep, n_keep, chosen, &sg,
+                                    NULL);
     }
     or_sparse_row(p, q_row, k_head, v_head, chosen, n_chosen, o_lr);
     for (int e = 0; e < d; ++e) o[e] = o_sr[e] + alpha * o_lr[e];
@@ -274,6 +293,7 @@ typedef struct {
     double *o, *o_sr, *o_lr;
     int *sel, *n_sel;
     double *sel_gap, *keep_gap;
+    int head;
     int next;                      /* shared work counter */
     pthread_mutex_t lock;
 } or_rows_job;
@@ -289,8 +309,8 @@ static void* or_rows_worker(void* arg)
         if (r >= J->n_rows) break;
         const int t = J->rows[r];
         const long long i = (long long)J->p->q_pos0 + t;
-        or_forward_one(J->p, J->q_head + (size_t)t * d, J->k_head, J->v_head, J->kbar, J->amax,
-                       J->alpha, i,
+        or_forward_one(J->p, J->head, J->q_head + (size_t)t * d, J->k_head, J->v_head, J->kbar,
+                       J->amax, J->alpha, i,
                        J->keep_ovr ? J->keep_ovr + (size_t)r * J->keep_w : NULL,
                        J->keep_ovr_n ? J->keep_ovr_n[r] : -1,
                        J->sel_ovr ? J->sel_ovr + (size_t)r * J->p->topk : NULL,
@@ -310,7 +330,7 @@ int or_forward_rows(const or_problem* p, const float* q_head, const float* k_hea
                     const int* keep_ovr, const int* keep_ovr_n, int keep_w,
                     const int* sel_ovr, const int* sel_ovr_n,
                     double* o, double* o_sr, double* o_lr, int* sel, int* n_sel,
-                    double* sel_gap, double* keep_gap, int nthreads)
+                    double* sel_gap, double* keep_gap, int nthreads, int head)
 {
     or_rows_job J;
     memset(&J, 0, sizeof(J));
@@ -319,7 +339,7 @@ int or_forward_rows(const or_problem* p, const float* q_head, const float* k_hea
     J.keep_ovr = keep_ovr; J.keep_ovr_n = keep_ovr_n; J.keep_w = keep_w;
     J.sel_ovr = sel_ovr; J.sel_ovr_n = sel_ovr_n;
     J.o = o; J.o_sr = o_sr; J.o_lr = o_lr; J.sel = sel; J.n_sel = n_sel;
-    J.sel_gap = sel_gap; J.keep_gap = keep_gap;
+    J.sel_gap = sel_gap; J.keep_gap = keep_gap; J.head = head;
     pthread_mutex_init(&J.lock, NULL);
     if (nthreads < 1) nthreads = 1;
     pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
@@ -356,7 +376,7 @@ int or_forward(const or_problem* p, const float* q, const float* k, const float*
                             sel ? sel + bh * (size_t)nq * p->topk : NULL,
                             n_sel ? n_sel + bh * (size_t)nq : NULL,
                             sel_gap ? sel_gap + bh * (size_t)nq : NULL,
-                            keep_gap ? keep_gap + bh * (size_t)nq : NULL, nthreads);
+                            keep_gap ? keep_gap + bh * (size_t)nq : NULL, nthreads, h);
         }
     }
     free(kbar); free(amax); free(rows);

@@ -12,7 +12,8 @@
  *   - candidate cells of query i are the complete cells whose last token is
  *     before i - w (the definition of C_i, eq. 6, is missing from the page);
  *   - the window of eq. (4) holds the w + 1 positions max(0, i - w) .. i;
- *   - eq. (7) is used with lambda_h = 0 (content score only);
+ *   - eq. (7)'s position prior lambda_h a_c erf((i - p_c) / (2 sigma_h)) is on
+ *     when the problem carries per-head lambda and sigma arrays, else 0;
  *   - RoPE rotates interleaved pairs (2k, 2k+1) by angle p * base^(-2k/d);
  *   - ties in TopP and top-K go to the larger cell index;
  *   - the NoPE logits of eq. (9) are q.k / sqrt(d); RMSNorm has unit gain and
@@ -39,7 +40,15 @@ typedef struct {
     double rope_base;
     double rms_eps;
     long long pos_offset;     /* absolute position of token 0; RoPE angles only */
+    /* eq. (7) prior, per head: lambda_h >= 0, sigma_h > 0 (both NULL: no prior) */
+    const double* prior_lambda;
+    const double* prior_sigma;
 } or_problem;
+
+/* Position prior of eq. (7) for the query at position i and cell c of head h:
+ * lambda_h a_c erf((i - p_c) / (2 sigma_h)) with p_c = (c + 1/2) s (eq. 5);
+ * 0 without prior arrays.  Positions are token indices; only i - p_c enters. */
+double or_prior(const or_problem* p, int head, long long i, int c, double a_c);
 
 /* RoPE rotation R(pos) of one d-vector (eq. 3). */
 void or_rope(const or_problem* p, const float* x, long long pos, double* out);
@@ -55,10 +64,16 @@ void or_cell_summaries_head(const or_problem* p, const float* k_head, double* kb
  * the relative gap between the P-th and (P+1)-th priorities, or +inf. */
 int or_prune_row(const or_problem* p, const double* amax, int n, int* keep, double* gap_rel);
 
-/* Content scores r_c = q.kbar_c / sqrt(d) (eq. 7, lambda = 0) over cand, and the
- * top-min(K, n_cand) cells written ascending to sel; returns their number.
+/* Cell scores r_c = q.kbar_c / sqrt(d) + or_prior(p, head, i, c, amax[c]) (eq. 7)
+ * over cand, and the top-min(K, n_cand) cells written ascending to sel; returns
+ * their number.  amax may be NULL when the problem has no prior.
  * gap_rel (nullable): relative gap between the K-th and (K+1)-th scores, or +inf.
  * cand_scores (nullable): the score of every candidate, in cand order. */
+int or_select_row_at(const or_problem* p, int head, long long i, const float* q_row,
+                     const double* kbar, const double* amax, const int* cand, int n_cand,
+                     int* sel, double* gap_rel, double* cand_scores);
+
+/* or_select_row_at without the prior (content score only). */
 int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
                   const int* cand, int n_cand, int* sel, double* gap_rel, double* cand_scores);
 
@@ -70,7 +85,7 @@ void or_window_row(const or_problem* p, const float* q_row, const float* k_head,
 void or_sparse_row(const or_problem* p, const float* q_row, const float* k_head,
                    const float* v_head, const int* sel, int n_sel, double* o_lr);
 
-/* Whole forward of one head for a list of query rows t (0 <= t < n_q), threaded.
+/* Whole forward of head `head` for a list of query rows t (0 <= t < n_q), threaded.
  * kbar/amax: summaries of this head.  keep_ovr/sel_ovr (nullable) replace the
  * retained / selected sets of a row when the row's count in *_ovr_n is >= 0;
  * rows are keep_w / topk ints wide.  Outputs per row: o, o_sr, o_lr [d];
@@ -81,7 +96,7 @@ int or_forward_rows(const or_problem* p, const float* q_head, const float* k_hea
                     const int* keep_ovr, const int* keep_ovr_n, int keep_w,
                     const int* sel_ovr, const int* sel_ovr_n,
                     double* o, double* o_sr, double* o_lr, int* sel, int* n_sel,
-                    double* sel_gap, double* keep_gap, int nthreads);
+                    double* sel_gap, double* keep_gap, int nthreads, int head);
 
 /* Whole forward of the whole problem (eq. 2 for every b, h, query), threaded. */
 int or_forward(const or_problem* p, const float* q, const float* k, const float* v,

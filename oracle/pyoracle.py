@@ -32,7 +32,18 @@ class Problem(C.Structure):
                 ("cell", C.c_int), ("window", C.c_int), ("topk", C.c_int),
                 ("budget", C.c_int), ("n_recent", C.c_int),
                 ("rope_base", C.c_double), ("rms_eps", C.c_double),
-                ("pos_offset", C.c_longlong)]
+                ("pos_offset", C.c_longlong),
+                ("prior_lambda", C.c_void_p), ("prior_sigma", C.c_void_p)]
+
+
+def with_prior(p: Problem, lam, sigma) -> Problem:
+    """Attach per-head eq. 7 prior arrays (kept alive on the Problem object)."""
+    p._lam = np.ascontiguousarray(lam, dtype=np.float64)
+    p._sig = np.ascontiguousarray(sigma, dtype=np.float64)
+    assert p._lam.shape == (p.heads,) and p._sig.shape == (p.heads,)
+    p.prior_lambda = p._lam.ctypes.data
+    p.prior_sigma = p._sig.ctypes.data
+    return p
 
 
 def problem_from(wl, **kw) -> Problem:
@@ -42,7 +53,11 @@ def problem_from(wl, **kw) -> Problem:
              budget=wl.budget, n_recent=wl.n_recent, rope_base=wl.rope_base,
              rms_eps=wl.rms_eps, pos_offset=0)
     f.update(kw)
-    return Problem(**f)
+    p = Problem(**f)
+    lam, sig = getattr(wl, "prior_arrays", lambda: (None, None))()
+    if lam is not None:
+        with_prior(p, lam, sig)
+    return p
 
 
 def make_problem(**kw) -> Problem:
@@ -85,12 +100,18 @@ class Oracle:
         L.or_select_row.argtypes = [P, _F32P, _F64P, _I32P, C.c_int, _I32P,
                                     C.POINTER(C.c_double), C.c_void_p]
         L.or_select_row.restype = C.c_int
+        L.or_select_row_at.argtypes = [P, C.c_int, C.c_longlong, _F32P, _F64P, C.c_void_p,
+                                       _I32P, C.c_int, _I32P, C.POINTER(C.c_double), C.c_void_p]
+        L.or_select_row_at.restype = C.c_int
+        L.or_prior.argtypes = [P, C.c_int, C.c_longlong, C.c_int, C.c_double]
+        L.or_prior.restype = C.c_double
         L.or_window_row.argtypes = [P, _F32P, _F32P, _F32P, C.c_longlong, _F64P]
         L.or_sparse_row.argtypes = [P, _F32P, _F32P, _F32P, _I32P, C.c_int, _F64P]
         vp = C.c_void_p
         L.or_forward_rows.argtypes = [P, _F32P, _F32P, _F32P, _F64P, _F64P, C.c_double,
                                       _I32P, C.c_int, vp, vp, C.c_int, vp, vp,
-                                      _F64P, _F64P, _F64P, _I32P, _I32P, _F64P, _F64P, C.c_int]
+                                      _F64P, _F64P, _F64P, _I32P, _I32P, _F64P, _F64P, C.c_int,
+                                      C.c_int]
         L.or_forward.argtypes = [P, _F32P, _F32P, _F32P, _F32P, _F64P, _F64P, _F64P,
                                  _I32P, _I32P, _F64P, _F64P, C.c_int]
         self.L = L
@@ -126,6 +147,22 @@ class Oracle:
                                    C.byref(gap), scores.ctypes.data)
         return sel[:cnt].copy(), gap.value, scores[:len(cand)].copy()
 
+    def select_row_at(self, p: Problem, head: int, i: int, q_row, kbar, amax, cand):
+        """Eq. 7 scores with the problem's position prior (if any) for the query at
+        position i of head `head`."""
+        cand = _i32(cand)
+        sel = np.empty(max(len(cand), 1), np.int32)
+        scores = np.empty(max(len(cand), 1), np.float64)
+        gap = C.c_double()
+        am = None if amax is None else _f64(amax)
+        cnt = self.L.or_select_row_at(C.byref(p), int(head), int(i), _f32(q_row), _f64(kbar),
+                                      None if am is None else am.ctypes.data, cand, len(cand),
+                                      sel, C.byref(gap), scores.ctypes.data)
+        return sel[:cnt].copy(), gap.value, scores[:len(cand)].copy()
+
+    def prior(self, p: Problem, head: int, i: int, c: int, a_c: float) -> float:
+        return self.L.or_prior(C.byref(p), int(head), int(i), int(c), float(a_c))
+
     def window_row(self, p: Problem, q_row, k_head, v_head, i: int) -> np.ndarray:
         out = np.empty(p.head_dim, np.float64)
         self.L.or_window_row(C.byref(p), _f32(q_row), _f32(k_head), _f32(v_head), int(i), out)
@@ -141,7 +178,8 @@ class Oracle:
 
     # -- composed -------------------------------------------------------------
     def forward_rows(self, p: Problem, q_head, k_head, v_head, kbar, amax, alpha, rows,
-                     keep_ovr=None, sel_ovr=None, nthreads: int | None = None) -> dict:
+                     keep_ovr=None, sel_ovr=None, nthreads: int | None = None,
+                     head: int = 0) -> dict:
         """Forward of one head for query rows ``rows`` (indices into q_head).
 
         keep_ovr / sel_ovr: optional lists (one entry per row, None = no
@@ -180,7 +218,8 @@ class Oracle:
         amax_c = _f64(amax) if len(amax) else np.zeros(1)
         self.L.or_forward_rows(C.byref(p), _f32(q_head), _f32(k_head), _f32(v_head), kbar_c,
                                amax_c, float(alpha), rows, n, keep_p, keep_n_p, keep_w, sel_p,
-                               sel_n_p, o, o_sr, o_lr, sel, n_sel, sg, kg, int(nthreads))
+                               sel_n_p, o, o_sr, o_lr, sel, n_sel, sg, kg, int(nthreads),
+                               int(head))
         return dict(o=o, o_sr=o_sr, o_lr=o_lr, sel=sel, n_sel=n_sel, sel_gap=sg, keep_gap=kg)
 
     def forward(self, p: Problem, q, k, v, alpha, nthreads: int | None = None) -> dict:

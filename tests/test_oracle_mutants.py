@@ -25,7 +25,14 @@ MUTANTS = [
     ("amax_last_not_max", "if (norm > best) best = norm;", "best = norm;", 0),
     ("ties_to_smaller_index", "if (x->cell > y->cell) return -1;", "if (x->cell < y->cell) return -1;", 0),
     ("recent_cells_dropped", "for (int c = n - p->n_recent; c < n; ++c)", "for (int c = n; c < n; ++c)", 0),
-    ("score_unscaled", "order[t].key = dot / sqrt((double)d);", "order[t].key = dot;", 0),
+    ("score_unscaled", "order[t].key = dot / sqrt((double)d) +", "order[t].key = dot +", 0),
+    ("prior_center_at_cell_start", "const double p_c = ((double)c + 0.5) * (double)p->cell;",
+     "const double p_c = (double)c * (double)p->cell;", 0),
+    ("prior_erf_scale_missing_2", "erf(((double)i - p_c) / (2.0 * sig))",
+     "erf(((double)i - p_c) / sig)", 0),
+    ("prior_offset_sign", "erf(((double)i - p_c) / (2.0 * sig))",
+     "erf((p_c - (double)i) / (2.0 * sig))", 0),
+    ("prior_drops_norm", "return lam * a_c * erf(", "return lam * erf(", 0),
     ("readout_logits_unscaled", "logits[t] = dot / sqrt((double)d);", "logits[t] = dot;", 1),
     ("window_logits_unscaled", "logits[t] = dot / sqrt((double)d);", "logits[t] = dot;", 0),
     ("rmsnorm_drops_eps", "sqrt(ms + p->rms_eps)", "sqrt(ms)", 0),

@@ -304,6 +304,83 @@ def test_select_order_statistics(orc):
 
 
 # ------------------------------------------------------------- readout (eq. 9)
+# ------------------------------------------------ eq. 7's position prior
+# erf(1), Abramowitz & Stegun, Handbook of Mathematical Functions, Table 7.1.
+ERF_1 = 0.8427007929497149
+
+
+def _prior_problem(lam=(0.5, 2.0), sig=(8.0, 40.0)):
+    p = oracle.make_problem(heads=2, head_dim=16, topk=4)
+    return oracle.with_prior(p, lam, sig)
+
+
+def test_prior_textbook_value_and_oddness(orc):
+    """i - p_c = 2 sigma gives lambda a_c erf(1); the cell centre is (c + 1/2) s."""
+    p = _prior_problem()
+    for h, (lam, sig) in enumerate([(0.5, 8.0), (2.0, 40.0)]):
+        c = 7
+        centre = c * 32 + 16
+        i = centre + int(2 * sig)
+        assert orc.prior(p, h, i, c, 3.0) == pytest.approx(lam * 3.0 * ERF_1, rel=1e-15)
+        i_neg = centre - int(2 * sig)
+        assert orc.prior(p, h, i_neg, c, 3.0) == pytest.approx(-lam * 3.0 * ERF_1, rel=1e-15)
+        assert orc.prior(p, h, centre, c, 3.0) == 0.0          # erf(0) = 0 at the centre
+    # without prior arrays the term is absent
+    assert orc.prior(oracle.make_problem(), 0, 1000, 3, 5.0) == 0.0
+
+
+def test_prior_limits_and_shift_invariance(orc):
+    rng = np.random.default_rng(23)
+    d, n_cells = 16, 60
+    kbar = rng.standard_normal((n_cells, d))
+    amax = rng.uniform(0.5, 4.0, n_cells)
+    cand = np.arange(n_cells)
+    q = rng.standard_normal(d).astype(np.float32)
+    i = n_cells * 32 + 512 + 40              # every candidate lies before i - w
+    base = oracle.make_problem(head_dim=d, topk=6)
+    _, _, content = orc.select_row(base, q, kbar, cand)
+    # sigma -> infinity: erf -> 0, the content scores alone
+    wide = oracle.with_prior(oracle.make_problem(head_dim=d, topk=6), [0.7], [1e30])
+    _, _, s_wide = orc.select_row_at(wide, 0, i, q, kbar, amax, cand)
+    np.testing.assert_allclose(s_wide, content, rtol=0, atol=1e-12)
+    # sigma -> 0: erf -> 1 for every candidate (all lie in the past), + lambda a_c
+    narrow = oracle.with_prior(oracle.make_problem(head_dim=d, topk=6), [0.7], [1e-9])
+    _, _, s_narrow = orc.select_row_at(narrow, 0, i, q, kbar, amax, cand)
+    np.testing.assert_allclose(s_narrow, content + 0.7 * amax, rtol=1e-13, atol=1e-13)
+    # the prior depends on i - p_c only: shifting the query by m cells and every
+    # cell by m leaves it unchanged (the page's position-independence property)
+    p = _prior_problem()
+    for m in (1, 5, 1000):
+        for c in (0, 3, 17):
+            assert orc.prior(p, 1, i + 32 * m, c + m, 2.5) == orc.prior(p, 1, i, c, 2.5)
+    # older cells (larger i - p_c) get the larger bonus: erf is increasing
+    broad = oracle.with_prior(oracle.make_problem(), [1.0], [5000.0])
+    vals = [orc.prior(broad, 0, i, c, 1.0) for c in range(n_cells)]
+    assert all(a > b for a, b in zip(vals, vals[1:]))
+
+
+def test_prior_changes_selection_like_a_library_erf(orc):
+    """Top-K under the prior equals the top-K of numpy content scores plus a prior
+    evaluated with scipy's erf."""
+    from scipy.special import erf
+    rng = np.random.default_rng(29)
+    d, n_cells, K = 16, 80, 8
+    kbar = rng.standard_normal((n_cells, d))
+    amax = rng.uniform(0.5, 4.0, n_cells)
+    q = rng.standard_normal(d).astype(np.float32)
+    i = n_cells * 32 + 600
+    p = oracle.with_prior(oracle.make_problem(head_dim=d, topk=K), [0.6], [300.0])
+    cand = np.arange(n_cells)
+    sel, _, sc = orc.select_row_at(p, 0, i, q, kbar, amax, cand)
+    ref = kbar @ q.astype(np.float64) / math.sqrt(d) + \
+        0.6 * amax * erf((i - (cand + 0.5) * 32) / (2 * 300.0))
+    np.testing.assert_allclose(sc, ref, rtol=1e-13, atol=1e-13)
+    order = sorted(cand, key=lambda c: (ref[c], c), reverse=True)[:K]
+    assert sel.tolist() == sorted(order)
+    _, _, content = orc.select_row(oracle.make_problem(head_dim=d, topk=K), q, kbar, cand)
+    assert set(sel) != set(sorted(cand, key=lambda c: (content[c], c), reverse=True)[:K])
+
+
 def test_readout_reduces_to_dense_nope(orc):
     """No pruning and K covering every candidate: S_i = C_i, so eq. 9 is RMSNorm of
     NoPE attention over all tokens of the complete cells ending before i - w."""
