@@ -28,7 +28,8 @@ from long_context_fs_amd import synth  # noqa: E402
 PEAK = {"hbm_GBs": 8000.0, "mfma_bf16_TFs": 2500.0, "valu_f32_TFs": 78.6, "mfma_f32_TFs": 157.3}
 METRIC = "FreeSolo forward queries/s and TFLOP/s at N=16k/64k/256k; % of MI355X roofline"
 PRIMARY = "prefill_b1h8_n65536_d128_bf16"
-ALSO = ["prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16"]
+ALSO = ["prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16",
+        "prefill_b1h8_n65536_d128_bf16_prior"]
 PHASES = ["summaries", "prune", "select", "window", "sparse", "combine"]
 # Source file of each phase's kernel (for matching stored HBM traffic counters).
 PHASE_SRC = {"summaries": "summaries.hip", "prune": "prune.hip", "select": "select.hip",
@@ -113,7 +114,7 @@ def run_workload(name, steps, warmup, torch, fs):
             fs.fs_prune_prefix(p, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep, fwd.keep_count)
         mark(2)
         fs.fs_select_topk(p, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, fwd.topk,
-                          fwd.idx, None)
+                          fwd.idx, None, None, fwd.prior)
         mark(3)
         fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)
         mark(4)
@@ -229,7 +230,7 @@ def run_phase(name, phase, reps, torch, fs):
         "prune": lambda: fs.fs_prune_prefix(p, f.amax, f.n_recent, f.budget, f.keep,
                                             f.keep_count),
         "select": lambda: fs.fs_select_topk(p, q, f.kbar, f.keep, f.keep_count, f.keep_w,
-                                            f.topk, f.idx, None),
+                                            f.topk, f.idx, None, None, f.prior),
         "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),
         "sparse": lambda: fs.fs_sparse_attn(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_lr, f.ws_sparse),
         "combine": lambda: fs.fs_combine(p, f.o_sr, f.o_lr, alpha, f.o),

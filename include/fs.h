@@ -8,7 +8,7 @@
  *
  *   fs_cell_summaries  eq. 5   mean key and maximum token-key norm per cell
  *   fs_prune_prefix    eq. 8   FS-L query-independent pruning to W + P cells
- *   fs_select_topk     eq. 7   content score q.kbar/sqrt(d), top-K cells per query
+ *   fs_select_topk     eq. 7   score q.kbar/sqrt(d) (+ optional erf prior), top-K cells
  *   fs_window_attn     eqs.3-4 RoPE attention over positions max(0,i-w) .. i
  *   fs_sparse_attn     eq. 9   NoPE attention over the selected cells' tokens, RMSNorm
  *   fs_combine         eq. 2   o = o_sr + alpha_h * o_lr
@@ -17,7 +17,8 @@
  *   - candidates of the query at position i are the complete cells whose last
  *     token precedes i - w: cells c < n_i = floor((i - w) / s) (0 when i < w);
  *   - the window holds the w + 1 positions max(0, i - w) .. i;
- *   - eq. 7 is used with lambda_h = 0; top-K and top-P ties go to the larger cell;
+ *   - eq. 7's position prior is optional (absent = lambda_h 0); top-K and top-P
+ *     ties go to the larger cell;
  *   - RoPE turns interleaved pairs (2k, 2k+1) by angle p * base^(-2k/d);
  *   - NoPE logits are q.k/sqrt(d); RMSNorm has unit gain; no selected cell gives 0.
  *
@@ -87,8 +88,12 @@ fs_status fs_prune_rows(const fs_problem* problem, int32_t* n_lo, int32_t* n_row
 fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t n_recent,
                           int32_t budget, int32_t* keep, int32_t* keep_count, void* stream);
 
-/* Scoring and top-K, eq. 7 with lambda_h = 0.  For each query i the score of
- * cell c is r_ic = q_i . kbar_c / sqrt(d) with the unrotated query.  Candidates
+/* Scoring and top-K, eq. 7.  For each query i the score of cell c is
+ * r_ic = q_i . kbar_c / sqrt(d) + lambda_h a_c erf((i - p_c) / (2 sigma_h)) with
+ * the unrotated query and p_c = (c + 1/2) s (eq. 5).  The prior term is present
+ * when prior_lambda is non-NULL; then amax ([B][H][C] as written by
+ * fs_cell_summaries), prior_lambda and prior_sigma (float32 [H], lambda_h >= 0,
+ * sigma_h > 0, device memory, not checked) are all required.  Candidates
  * are the keep row of n_i (keep != NULL; rows as written by fs_prune_prefix,
  * keep_width wide) or every cell c < n_i (keep == NULL: no pruning).  The
  * selected set is the min(topk, #candidates) candidates with the largest
@@ -96,6 +101,7 @@ fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t 
  * score (nullable) receives r_ic aligned with idx (0 for padding).
  * idx: int32 [B][H][n_q][topk]; score: float32 [B][H][n_q][topk]; 1 <= topk <= 64. */
 fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* kbar,
+                         const float* amax, const float* prior_lambda, const float* prior_sigma,
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
                          int32_t topk, int32_t* idx, float* score, void* stream);
 

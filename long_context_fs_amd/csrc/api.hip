@@ -164,12 +164,15 @@ fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t 
 }
 
 fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* kbar,
+                         const float* amax, const float* prior_lambda, const float* prior_sigma,
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
                          int32_t topk, int32_t* idx, float* score, void* stream)
 {
     fs::Shape sh;
     FS_CHECK(check_problem(problem, &sh));
     FS_PTR(q); FS_PTR(kbar);
+    if (prior_lambda && (!prior_sigma || !amax))
+        return fail(FS_ERR_INVALID, "the position prior needs amax, prior_lambda and prior_sigma");
     if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
     if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
     if (keep && (!keep_count || keep_width < 1 || keep_width > 4096))
@@ -182,8 +185,9 @@ fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* 
         if (n_hi > 16256)
             return fail(FS_ERR_UNSUPPORTED, "without pruning at most 16256 candidate cells");
     }
-    return from_hip(fs::launch_select(sh, q, kbar, keep, keep_count, keep_width, lo, rows, topk,
-                                      idx, score, (hipStream_t)stream),
+    const fs::Prior pr{amax, prior_lambda, prior_sigma};
+    return from_hip(fs::launch_select(sh, q, kbar, pr, keep, keep_count, keep_width, lo, rows,
+                                      topk, idx, score, (hipStream_t)stream),
                     "fs_select_topk");
 }
 

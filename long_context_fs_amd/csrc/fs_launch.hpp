@@ -22,9 +22,17 @@ hipError_t launch_summaries(const Shape& sh, const void* k, float* kbar, float* 
                             hipStream_t st);
 hipError_t launch_prune(const Shape& sh, const float* amax, int n_lo, int n_rows, int n_recent,
                         int budget, int32_t* keep, int32_t* keep_count, hipStream_t st);
-hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const int32_t* keep,
-                         const int32_t* keep_count, int keep_w, int n_lo, int n_rows, int topk,
-                         int32_t* idx, float* score, hipStream_t st);
+// Position prior of eq. 7, lambda_h a_c erf((i - p_c) / (2 sigma_h)): device
+// arrays amax [B][H][C], lambda [H], sigma [H]; lambda == nullptr switches it off.
+struct Prior {
+    const float* amax;
+    const float* lambda;
+    const float* sigma;
+};
+
+hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
+                         const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
+                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st);
 size_t rope_table_bytes(const Shape& sh);
 hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
                          double rope_base, void* table, void* o_sr, hipStream_t st);

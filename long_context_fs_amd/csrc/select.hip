@@ -35,11 +35,22 @@ __device__ __forceinline__ float key_to_float(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// eq. 7's prior for the query at position i and cell c of head h (row bh of amax):
+// lambda_h a_c erf((i - p_c) / (2 sigma_h)), p_c = (c + 1/2) s.  i - c s is exact in
+// fp32 below 2^24 tokens; beyond, erf has long saturated for any sigma that small.
+__device__ __forceinline__ float prior_term(const Prior& pr, long bh, int h, int C, long i, int c,
+                                            int cell)
+{
+    const float a = pr.amax[bh * C + c];
+    const float delta = (float)(i - (long)c * cell) - 0.5f * (float)cell;
+    return pr.lambda[h] * a * erff(delta / (2.f * pr.sigma[h]));
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
     const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
-    const float* __restrict__ kbar, int H, int C, int nq, int q_pos0, int window, int cell,
-    const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count, int keep_w,
+    const float* __restrict__ kbar, Prior pr, int H, int C, int nq, int q_pos0, int window,
+    int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count, int keep_w,
     int n_lo, int n_rows, int topk, int cap, float inv_sqrt_d, int32_t* __restrict__ idx,
     float* __restrict__ score)
 {
@@ -85,7 +96,9 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
             dot = fmaf(s_q[e + 2], kv.z, dot);
             dot = fmaf(s_q[e + 3], kv.w, dot);
         }
-        s_key[j] = float_key(dot);
+        // ranked by the unscaled dot without the prior (1/sqrt(d) > 0 keeps the order)
+        s_key[j] = float_key(pr.lambda ? fmaf(dot, inv_sqrt_d, prior_term(pr, bh, h, C, i, c, cell))
+                                       : dot);
     }
     __syncthreads();
     if (!active) return;
@@ -124,7 +137,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
         if (kept) {
             const int pos = written + lanes_below(mk);
             out_i[pos] = cand ? cand[j] : j;
-            if (out_s) out_s[pos] = key_to_float(kj) * inv_sqrt_d;
+            if (out_s) out_s[pos] = key_to_float(kj) * (pr.lambda ? 1.f : inv_sqrt_d);
         }
         written += __popcll(mk);
         eq_seen += __popcll(me);
@@ -231,8 +244,8 @@ __device__ __forceinline__ int field5(const uint32_t* w, int i)
 template <int D, int NB>
 __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel(   // 256 threads exactly
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
-    const float* __restrict__ kbar, int H, int BH, int C, int nq, int q_pos0, int window,
-    int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
+    const float* __restrict__ kbar, Prior pr, int H, int BH, int C, int nq, int q_pos0,
+    int window, int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
     int keep_w, int n_lo, int n_rows, int topk, int n_hi_all, int u_cap, float inv_sqrt_d,
     int32_t* __restrict__ idx, float* __restrict__ score)
 {
@@ -424,7 +437,12 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
                         const int slot = slot0 + 4 * g + r;
                         bool ok = slot < n_union && n_q > 0;
                         if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
-                        kv[bb][r] = ok ? float_key(acc[r]) : 0u;
+                        float rr = acc[r];   // the unscaled dot ranks alike without the prior
+                        if (pr.lambda && ok)
+                            rr = fmaf(rr, inv_sqrt_d,
+                                      prior_term(pr, bh, h, C, (long)q_pos0 + t0 + qr,
+                                                 keep ? ulist[slot] : slot, cell));
+                        kv[bb][r] = ok ? float_key(rr) : 0u;
                     }
                 } else {
 #pragma unroll
@@ -569,7 +587,7 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
                     if ((km[(4 * bb + r) / 32] >> ((4 * bb + r) % 32)) & 1u) {
                         const int slot = 16 * bb + 4 * g + r;
                         out_i[p] = keep ? ulist[slot] : slot;
-                        if (out_s) out_s[p] = key_to_float(kv[bb][r]) * inv_sqrt_d;
+                        if (out_s) out_s[p] = key_to_float(kv[bb][r]) * (pr.lambda ? 1.f : inv_sqrt_d);
                         ++p;
                     }
                 }
@@ -585,9 +603,9 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
     }
 }
 
-hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const int32_t* keep,
-                         const int32_t* keep_count, int keep_w, int n_lo, int n_rows, int topk,
-                         int32_t* idx, float* score, hipStream_t st)
+hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
+                         const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
+                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st)
 {
     if (sh.nq == 0) return hipSuccess;
     // Largest candidate list: the keep width, or every cell below the last query's n.
@@ -610,7 +628,7 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
             const int nb_need = uc / 16;
 #define FS_SELECT_MFMA(D, NB)                                                                   \
             hipLaunchKernelGGL((select_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,        \
-                               (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, sh.H,     \
+                               (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr, sh.H, \
                                sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,            \
                                keep_count, keep_w,                                               \
                                n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, idx, score)
@@ -637,7 +655,8 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
     const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
 #define FS_SELECT(E, D)                                                                        \
     hipLaunchKernelGGL((select_topk_kernel<E, D>), grid, block, lds, st,                       \
-                       (const typename E::storage*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, sh.H, \
+                       (const typename E::storage*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,   \
+                       sh.H,                                                                     \
                        sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep, keep_count, keep_w, n_lo,      \
                        n_rows, topk, cap, inv_sqrt_d, idx, score)
     if (sh.bf16) {

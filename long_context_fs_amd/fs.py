@@ -56,7 +56,7 @@ def load(path: str | None = None):
         "fs_cell_summaries": [P, vp, vp, vp, vp],
         "fs_prune_rows": [P, C.POINTER(i32), C.POINTER(i32)],
         "fs_prune_prefix": [P, vp, i32, i32, vp, vp, vp],
-        "fs_select_topk": [P, vp, vp, vp, vp, i32, i32, vp, vp, vp],
+        "fs_select_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp],
         "fs_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_window_attn": [P, vp, vp, vp, f32, vp, C.c_size_t, vp, vp],
         "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
@@ -135,10 +135,13 @@ def fs_prune_prefix(prob, amax, n_recent, budget, keep, keep_count, stream=None)
 
 
 def fs_select_topk(prob, q, kbar, keep, keep_count, keep_width, topk, idx, score=None,
-                   stream=None):
-    _check("fs_select_topk", load().fs_select_topk(C.byref(prob), _p(q), _p(kbar), _p(keep),
-                                                   _p(keep_count), keep_width, topk, _p(idx),
-                                                   _p(score), _s(stream)))
+                   stream=None, prior=None):
+    """prior: None, or (amax, lambda, sigma) device tensors for eq. 7's position prior."""
+    amax, lam, sig = prior if prior is not None else (None, None, None)
+    _check("fs_select_topk", load().fs_select_topk(C.byref(prob), _p(q), _p(kbar), _p(amax),
+                                                   _p(lam), _p(sig), _p(keep), _p(keep_count),
+                                                   keep_width, topk, _p(idx), _p(score),
+                                                   _s(stream)))
 
 
 def fs_workspace_size(prob) -> int:
@@ -182,7 +185,8 @@ class FsForward:
     library calls on the stream and allocates nothing."""
 
     def __init__(self, batch, heads, n_ctx, head_dim, n_q, q_pos0, dtype, topk, budget,
-                 n_recent=0, window=512, rope_base=10000.0, rms_eps=1e-6, device="cuda"):
+                 n_recent=0, window=512, rope_base=10000.0, rms_eps=1e-6, device="cuda",
+                 prior_lambda=None, prior_sigma=None):
         self.dtype = FS_BF16 if dtype in ("bf16", torch.bfloat16, FS_BF16) else FS_F32
         tdt = torch.bfloat16 if self.dtype == FS_BF16 else torch.float32
         self.prob = problem(batch, heads, head_dim, n_ctx, n_q, q_pos0, window, self.dtype)
@@ -209,6 +213,13 @@ class FsForward:
         self.o_sr = torch.empty((B, H, n_q, d), dtype=tdt, device=device)
         self.o_lr = torch.empty_like(self.o_sr)
         self.o = torch.empty_like(self.o_sr)
+        # eq. 7's position prior: per-head lambda / sigma (float32), or none
+        self.prior = None
+        if prior_lambda is not None:
+            lam = torch.as_tensor(prior_lambda, dtype=f32).to(device)
+            sig = torch.as_tensor(prior_sigma, dtype=f32).to(device)
+            assert lam.shape == (H,) and sig.shape == (H,)
+            self.prior = (self.amax, lam, sig)
 
     def __call__(self, q, k, v, alpha, stream=None, keep_score=True):
         p = self.prob
@@ -217,7 +228,7 @@ class FsForward:
             fs_prune_prefix(p, self.amax, self.n_recent, self.budget, self.keep, self.keep_count,
                             stream)
         fs_select_topk(p, q, self.kbar, self.keep, self.keep_count, self.keep_w, self.topk,
-                       self.idx, self.score if keep_score else None, stream)
+                       self.idx, self.score if keep_score else None, stream, self.prior)
         fs_window_attn(p, q, k, v, self.rope_base, self.ws, self.o_sr, stream)
         fs_sparse_attn(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_lr, self.ws_sparse,
                        stream)
@@ -226,5 +237,7 @@ class FsForward:
 
     @classmethod
     def for_workload(cls, wl, device="cuda"):
+        lam, sig = wl.prior_arrays() if hasattr(wl, "prior_arrays") else (None, None)
         return cls(wl.batch, wl.heads, wl.n_ctx, wl.head_dim, wl.n_q, wl.q_pos0, wl.dtype,
-                   wl.topk, wl.budget, wl.n_recent, wl.window, wl.rope_base, wl.rms_eps, device)
+                   wl.topk, wl.budget, wl.n_recent, wl.window, wl.rope_base, wl.rms_eps, device,
+                   lam, sig)

@@ -100,9 +100,18 @@ def test_call_specific_limits(lib):
     assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 0, FAKE, FAKE, None) == 2
     assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 5000, FAKE, FAKE, None) == 2
     assert lib.fs_prune_prefix(C.byref(p), FAKE, -1, 4, FAKE, FAKE, None) == 2
-    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, 0, 0, FAKE, None, None) == 2
-    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, 0, 65, FAKE, None, None) == 2
-    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, FAKE, None, 64, 8, FAKE, None, None) == 1
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 0, FAKE,
+                              None, None) == 2
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 65, FAKE,
+                              None, None) == 2
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, FAKE, None, 64, 8, FAKE,
+                              None, None) == 1
+    # the prior needs all three of amax, lambda and sigma
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, None, 0, 8, FAKE,
+                              None, None) == 1
+    assert b"prior" in lib.fs_last_error()
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, 0, 8, FAKE,
+                              None, None) == 1
     assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, None, 8, 1e-6, None, 0, FAKE,
                               None) == 1
     assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, -1.0, None, 0, FAKE,
@@ -118,7 +127,8 @@ def test_call_specific_limits(lib):
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 0.5, FAKE, 1 << 30, FAKE, None) == 1
     assert lib.fs_combine(C.byref(p), FAKE, FAKE, None, FAKE, None) == 1
     big = _prob(n_ctx=1 << 20, n_q=1 << 20)              # 32752 candidate cells, no pruning
-    assert lib.fs_select_topk(C.byref(big), FAKE, FAKE, None, None, 0, 8, FAKE, None, None) == 2
+    assert lib.fs_select_topk(C.byref(big), FAKE, FAKE, None, None, None, None, None, 0, 8, FAKE,
+                              None, None) == 2
 
 
 def test_status_strings(lib):

@@ -47,6 +47,11 @@ SMALL = {
         n_ctx=700, n_q=700, window=704),
     "bf16_d64_window0": W["prefill_b2h16_n4096_d64_bf16"].replace(
         batch=1, heads=1, n_ctx=900, n_q=900, window=0, budget=5, topk=2),
+    # eq. 7's position prior, on the MFMA (bf16, pruned) and row-wise (fp32, unpruned) paths
+    "bf16_d128_prior": W["prefill_b1h8_n65536_d128_bf16_prior"].replace(
+        heads=2, n_ctx=2900, n_q=2900, budget=16, topk=8, prior_lambda=0.3, prior_sigma=300.0),
+    "f32_d64_prior_noprune": W["prefill_b1h1_n2048_d64_f32"].replace(
+        heads=2, n_ctx=1500, n_q=1500, prior_lambda=0.5, prior_sigma=200.0),
 }
 FULL = list(synth.WORKLOADS)
 
@@ -142,7 +147,8 @@ def check_select(wl, x, g, rows):
         i = wl.q_pos0 + t
         cand = candidate_list(wl, g, b, h, i)
         kbar = g["kbar"][b, h].astype(np.float64)
-        want, _, scores = orc().select_row(p, x["q"][b, h, t], kbar, cand)
+        amax = g["amax"][b, h].astype(np.float64)
+        want, _, scores = orc().select_row_at(p, h, i, x["q"][b, h, t], kbar, amax, cand)
         sel = g["idx"][b, h, t]
         chosen = sel[sel >= 0]
         assert (sel[len(chosen):] == -1).all() and (np.diff(chosen) > 0).all()
@@ -151,8 +157,12 @@ def check_select(wl, x, g, rows):
             pos = np.searchsorted(cand, chosen) if wl.budget >= 0 else chosen
             # fp32 dot error is bounded relative to |q| |kbar| / sqrt(d), not to the score
             mag = np.linalg.norm(x["q"][b, h, t]) * np.linalg.norm(kbar[chosen], axis=1).max()
+            mag /= np.sqrt(wl.head_dim)
+            lam, _ = wl.prior_arrays()
+            if lam is not None:        # fp32 prior term: error relative to lambda_h a_c
+                mag += float(lam[h]) * float(amax[chosen].max())
             np.testing.assert_allclose(g["score"][b, h, t, :len(chosen)], scores[pos],
-                                       rtol=0, atol=1e-6 * mag / np.sqrt(wl.head_dim))
+                                       rtol=0, atol=1e-6 * mag)
     return ties
 
 
@@ -178,7 +188,7 @@ def oracle_rows(wl, x, g, rows, use_gpu_sets=False):
         if use_gpu_sets:
             kw["sel_ovr"] = [g["idx"][b, h, t][g["idx"][b, h, t] >= 0] for t in ts]
         res = orc().forward_rows(p, x["q"][b, h], x["k"][b, h], x["v"][b, h], kbar, amax,
-                                 x["alpha"][h], ts, **kw)
+                                 x["alpha"][h], ts, head=h, **kw)
         for j, (r, _) in enumerate(items):
             for k in out:
                 out[k][r] = res[k][j]
