@@ -153,6 +153,48 @@ int or_select_row_at(const or_problem* p, int head, long long i, const float* q_
     return cnt;
 }
 
+/* ---- token-level reranking (section 3.4, eq. 12) ---------------------- */
+static double or_cell_lse(const or_problem* p, const float* q_row, const float* k_head, int c)
+{
+    const int d = p->head_dim, s = p->cell;
+    double* lg = (double*)malloc(sizeof(double) * (size_t)s);
+    double mx = -INFINITY;
+    for (int t = 0; t < s; ++t) {
+        const float* kj = k_head + ((size_t)c * s + t) * d;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e) dot += (double)q_row[e] * (double)kj[e];
+        lg[t] = dot / sqrt((double)d);
+        if (lg[t] > mx) mx = lg[t];
+    }
+    double sum = 0.0;
+    for (int t = 0; t < s; ++t) sum += exp(lg[t] - mx);
+    free(lg);
+    return mx + log(sum);
+}
+
+int or_rerank_row(const or_problem* p, int head, long long i, const float* q_row,
+                  const float* k_head, const double* amax, const int* cand, int n_cand,
+                  int* sel, double* gap_rel, double* cand_scores)
+{
+    if (gap_rel) *gap_rel = INFINITY;
+    if (n_cand <= 0) return 0;
+    or_keyed* order = (or_keyed*)malloc(sizeof(or_keyed) * (size_t)n_cand);
+    for (int t = 0; t < n_cand; ++t) {
+        order[t].key = or_cell_lse(p, q_row, k_head, cand[t]) +
+                       (amax ? or_prior(p, head, i, cand[t], amax[cand[t]]) : 0.0);
+        order[t].cell = cand[t];
+        if (cand_scores) cand_scores[t] = order[t].key;
+    }
+    qsort(order, (size_t)n_cand, sizeof(or_keyed), or_cmp_desc);
+    int cnt = n_cand < p->topk ? n_cand : p->topk;
+    if (gap_rel && n_cand > p->topk && p->topk > 0)
+        *gap_rel = or_rel_gap(order[p->topk - 1].key, order[p->topk].key);
+    for (int t = 0; t < cnt; ++t) sel[t] = order[t].cell;
+    qsort(sel, (size_t)cnt, sizeof(int), or_cmp_int);
+    free(order);
+    return cnt;
+}
+
 int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
                   const int* cand, int n_cand, int* sel, double* gap_rel, double* cand_scores)
 {

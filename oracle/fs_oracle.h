@@ -73,6 +73,13 @@ int or_select_row_at(const or_problem* p, int head, long long i, const float* q_
                      const double* kbar, const double* amax, const int* cand, int n_cand,
                      int* sel, double* gap_rel, double* cand_scores);
 
+/* Token-level reranking (eq. 12): r~_c = log sum_{j in I_c} exp(q.k_j / sqrt(d))
+ * + or_prior(p, head, i, c, amax[c]) over cand, with the unrotated query and the
+ * cell's s raw keys; then the same top-K as or_select_row_at. */
+int or_rerank_row(const or_problem* p, int head, long long i, const float* q_row,
+                  const float* k_head, const double* amax, const int* cand, int n_cand,
+                  int* sel, double* gap_rel, double* cand_scores);
+
 /* or_select_row_at without the prior (content score only). */
 int or_select_row(const or_problem* p, const float* q_row, const double* kbar,
                   const int* cand, int n_cand, int* sel, double* gap_rel, double* cand_scores);

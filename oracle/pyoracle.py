@@ -103,6 +103,9 @@ class Oracle:
         L.or_select_row_at.argtypes = [P, C.c_int, C.c_longlong, _F32P, _F64P, C.c_void_p,
                                        _I32P, C.c_int, _I32P, C.POINTER(C.c_double), C.c_void_p]
         L.or_select_row_at.restype = C.c_int
+        L.or_rerank_row.argtypes = [P, C.c_int, C.c_longlong, _F32P, _F32P, C.c_void_p,
+                                    _I32P, C.c_int, _I32P, C.POINTER(C.c_double), C.c_void_p]
+        L.or_rerank_row.restype = C.c_int
         L.or_prior.argtypes = [P, C.c_int, C.c_longlong, C.c_int, C.c_double]
         L.or_prior.restype = C.c_double
         L.or_window_row.argtypes = [P, _F32P, _F32P, _F32P, C.c_longlong, _F64P]
@@ -158,6 +161,19 @@ class Oracle:
         cnt = self.L.or_select_row_at(C.byref(p), int(head), int(i), _f32(q_row), _f64(kbar),
                                       None if am is None else am.ctypes.data, cand, len(cand),
                                       sel, C.byref(gap), scores.ctypes.data)
+        return sel[:cnt].copy(), gap.value, scores[:len(cand)].copy()
+
+    def rerank_row(self, p: Problem, head: int, i: int, q_row, k_head, amax, cand):
+        """Eq. 12 scores (log-sum-exp of the cell's token logits + the prior, if
+        any) and the top-K of the query at position i of head `head`."""
+        cand = _i32(cand)
+        sel = np.empty(max(len(cand), 1), np.int32)
+        scores = np.empty(max(len(cand), 1), np.float64)
+        gap = C.c_double()
+        am = None if amax is None else _f64(amax)
+        cnt = self.L.or_rerank_row(C.byref(p), int(head), int(i), _f32(q_row), _f32(k_head),
+                                   None if am is None else am.ctypes.data, cand, len(cand), sel,
+                                   C.byref(gap), scores.ctypes.data)
         return sel[:cnt].copy(), gap.value, scores[:len(cand)].copy()
 
     def prior(self, p: Problem, head: int, i: int, c: int, a_c: float) -> float:

@@ -33,6 +33,9 @@ MUTANTS = [
     ("prior_offset_sign", "erf(((double)i - p_c) / (2.0 * sig))",
      "erf((p_c - (double)i) / (2.0 * sig))", 0),
     ("prior_drops_norm", "return lam * a_c * erf(", "return lam * erf(", 0),
+    ("rerank_drops_log", "return mx + log(sum);", "return mx + sum;", 0),
+    ("rerank_max_not_lse", "return mx + log(sum);", "return mx;", 0),
+    ("rerank_unscaled_logits", "lg[t] = dot / sqrt((double)d);", "lg[t] = dot;", 0),
     ("readout_logits_unscaled", "logits[t] = dot / sqrt((double)d);", "logits[t] = dot;", 1),
     ("window_logits_unscaled", "logits[t] = dot / sqrt((double)d);", "logits[t] = dot;", 0),
     ("rmsnorm_drops_eps", "sqrt(ms + p->rms_eps)", "sqrt(ms)", 0),

@@ -381,6 +381,51 @@ def test_prior_changes_selection_like_a_library_erf(orc):
     assert set(sel) != set(sorted(cand, key=lambda c: (content[c], c), reverse=True)[:K])
 
 
+# ------------------------------------------- token-level reranking (eq. 12)
+def test_rerank_closed_forms(orc):
+    """A cell of s identical keys scores logit + ln(s); a cell whose keys are all
+    orthogonal to q scores ln(s); one dominant key makes the score its logit."""
+    d, s = 8, 32
+    p = oracle.make_problem(head_dim=d, topk=2)
+    q = np.zeros(d, np.float32)
+    q[0] = 2.0
+    k = np.zeros((3 * s, d), np.float32)
+    k[0:s, 0] = 1.5                      # cell 0: q.k = 3 for every token
+    k[s:2 * s, 1] = 5.0                  # cell 1: orthogonal to q
+    k[2 * s:3 * s, 0] = -40.0            # cell 2: one dominant key, the rest far below
+    k[2 * s + 7, 0] = 30.0
+    _, _, sc = orc.rerank_row(p, 0, 10_000, q, k, None, np.arange(3))
+    assert sc[0] == pytest.approx(3.0 / math.sqrt(d) + math.log(s), rel=1e-14)
+    assert sc[1] == pytest.approx(math.log(s), rel=1e-14)
+    assert sc[2] == pytest.approx(60.0 / math.sqrt(d), rel=1e-14)
+
+
+def test_rerank_matches_library_logsumexp_and_adds_the_prior(orc):
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(31)
+    d, n_cells, K = 16, 40, 6
+    k = rng.standard_normal((n_cells * 32, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    cand = np.sort(rng.choice(n_cells, 25, replace=False))
+    p = oracle.make_problem(head_dim=d, topk=K)
+    sel, _, sc = orc.rerank_row(p, 0, n_cells * 32 + 600, q, k, None, cand)
+    lg = (k.astype(np.float64) @ q.astype(np.float64) / math.sqrt(d)).reshape(n_cells, 32)
+    np.testing.assert_allclose(sc, logsumexp(lg[cand], axis=1), rtol=1e-13, atol=1e-13)
+    order = sorted(cand, key=lambda c: (logsumexp(lg[c]), c), reverse=True)[:K]
+    assert sel.tolist() == sorted(order)
+    # the prior enters exactly as in eq. 7
+    amax = rng.uniform(1, 3, n_cells)
+    pp = oracle.with_prior(oracle.make_problem(head_dim=d, topk=K), [0.4], [150.0])
+    i = n_cells * 32 + 600
+    _, _, sp = orc.rerank_row(pp, 0, i, q, k, amax, cand)
+    prior = np.array([orc.prior(pp, 0, i, int(c), amax[c]) for c in cand])
+    np.testing.assert_allclose(sp, sc + prior, rtol=1e-13, atol=1e-13)
+    # reranking differs from the mean-key score of eq. 7 (the point of eq. 12)
+    kbar = k.reshape(n_cells, 32, d).mean(1).astype(np.float64)
+    sel7, _, _ = orc.select_row(p, q, kbar, cand)
+    assert set(sel7) != set(sel)
+
+
 def test_readout_reduces_to_dense_nope(orc):
     """No pruning and K covering every candidate: S_i = C_i, so eq. 9 is RMSNorm of
     NoPE attention over all tokens of the complete cells ending before i - w."""
