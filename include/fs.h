@@ -11,6 +11,7 @@
  *   fs_select_topk     eq. 7   score q.kbar/sqrt(d) (+ optional erf prior), top-K cells
  *   fs_window_attn     eqs.3-4 RoPE attention over positions max(0,i-w) .. i
  *   fs_sparse_attn     eq. 9   NoPE attention over the selected cells' tokens, RMSNorm
+ *   fs_rerank_topk     eq. 12  token-level reranking (log-sum-exp of a cell's logits), top-K
  *   fs_combine         eq. 2   o = o_sr + alpha_h * o_lr
  *
  * Readings of what the page leaves open (fixed here, identical in the oracle):
@@ -101,6 +102,17 @@ fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t 
  * score (nullable) receives r_ic aligned with idx (0 for padding).
  * idx: int32 [B][H][n_q][topk]; score: float32 [B][H][n_q][topk]; 1 <= topk <= 64. */
 fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* kbar,
+                         const float* amax, const float* prior_lambda, const float* prior_sigma,
+                         const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
+                         int32_t topk, int32_t* idx, float* score, void* stream);
+
+/* Token-level reranking and top-K, eq. 12 (section 3.4): the same candidates,
+ * prior and selection rule as fs_select_topk, with the score of cell c
+ * r~_ic = log sum_{j in I_c} exp(q_i . k_j / sqrt(d)) + lambda_h a_c erf((i - p_c) / (2 sigma_h))
+ * over the cell's s raw (unrotated) keys instead of the mean key.  k: [B][H][N][d]
+ * with the problem's kv strides.  The prior arrays follow fs_select_topk's rule
+ * (all NULL: no prior).  score (nullable) receives r~_ic aligned with idx. */
+fs_status fs_rerank_topk(const fs_problem* problem, const void* q, const void* k,
                          const float* amax, const float* prior_lambda, const float* prior_sigma,
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
                          int32_t topk, int32_t* idx, float* score, void* stream);

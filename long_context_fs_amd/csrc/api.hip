@@ -191,6 +191,34 @@ fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* 
                     "fs_select_topk");
 }
 
+fs_status fs_rerank_topk(const fs_problem* problem, const void* q, const void* k,
+                         const float* amax, const float* prior_lambda, const float* prior_sigma,
+                         const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
+                         int32_t topk, int32_t* idx, float* score, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(q); FS_PTR(k);
+    if (prior_lambda && (!prior_sigma || !amax))
+        return fail(FS_ERR_INVALID, "the position prior needs amax, prior_lambda and prior_sigma");
+    if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
+    if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
+    if (keep && (!keep_count || keep_width < 1 || keep_width > 4096))
+        return fail(FS_ERR_INVALID, "keep needs keep_count and keep_width in [1, 4096]");
+    int lo, rows;
+    fs::candidate_rows(sh, &lo, &rows);
+    if (!keep) {
+        long last = (long)sh.q_pos0 + sh.nq - 1;
+        long n_hi = last >= sh.w ? (last - sh.w) / sh.s : 0;
+        if (n_hi > 16256)
+            return fail(FS_ERR_UNSUPPORTED, "without pruning at most 16256 candidate cells");
+    }
+    const fs::Prior pr{amax, prior_lambda, prior_sigma};
+    return from_hip(fs::launch_rerank(sh, q, k, pr, keep, keep_count, keep_width, lo, rows, topk,
+                                      idx, score, (hipStream_t)stream),
+                    "fs_rerank_topk");
+}
+
 fs_status fs_workspace_size(const fs_problem* problem, size_t* bytes)
 {
     fs::Shape sh;

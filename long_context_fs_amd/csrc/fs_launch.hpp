@@ -33,6 +33,9 @@ struct Prior {
 hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
                          const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
                          int n_rows, int topk, int32_t* idx, float* score, hipStream_t st);
+hipError_t launch_rerank(const Shape& sh, const void* q, const void* k, const Prior& pr,
+                         const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
+                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st);
 size_t rope_table_bytes(const Shape& sh);
 hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
                          double rope_base, void* table, void* o_sr, hipStream_t st);

@@ -46,10 +46,13 @@ __device__ __forceinline__ float prior_term(const Prior& pr, long bh, int h, int
     return pr.lambda[h] * a * erff(delta / (2.f * pr.sigma[h]));
 }
 
-template <class E, int D>
+// RERANK: score a cell by eq. 12's log-sum-exp of its token logits (k, kvs*)
+// instead of eq. 7's mean-key dot (kbar).
+template <class E, int D, bool RERANK>
 __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
     const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
-    const float* __restrict__ kbar, Prior pr, int H, int C, int nq, int q_pos0, int window,
+    const float* __restrict__ kbar, const typename E::storage* __restrict__ k, int64_t kvs0,
+    int64_t kvs1, int64_t kvs2, Prior pr, int H, int C, int nq, int q_pos0, int window,
     int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count, int keep_w,
     int n_lo, int n_rows, int topk, int cap, float inv_sqrt_d, int32_t* __restrict__ idx,
     float* __restrict__ score)
@@ -83,22 +86,42 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
     }
     __syncthreads();
 
-    const float* kb_head = kbar + bh * (long)C * D;
-    for (int j = lane; j < n_cand; j += kWave) {
-        const int c = cand ? cand[j] : j;
-        const float* kb = kb_head + (long)c * D;
-        float dot = 0.f;
-#pragma unroll 8
-        for (int e = 0; e < D; e += 4) {
-            const float4 kv = *reinterpret_cast<const float4*>(kb + e);
-            dot = fmaf(s_q[e], kv.x, dot);
-            dot = fmaf(s_q[e + 1], kv.y, dot);
-            dot = fmaf(s_q[e + 2], kv.z, dot);
-            dot = fmaf(s_q[e + 3], kv.w, dot);
+    if constexpr (RERANK) {
+        // one candidate cell at a time: lane t < s takes token t of the cell
+        const typename E::storage* kh = k + b * kvs0 + h * kvs1;
+        for (int j = 0; j < n_cand; ++j) {
+            const int c = cand ? cand[j] : j;
+            float lg = -INFINITY;
+            if (lane < cell) {
+                const typename E::storage* kr = kh + ((long)c * cell + lane) * kvs2;
+                float dot = 0.f;
+                for (int e = 0; e < D; ++e) dot = fmaf(s_q[e], load1<E>(kr + e), dot);
+                lg = dot * inv_sqrt_d;
+            }
+            const float m = wave_max(lg);
+            const float z = wave_sum(lane < cell ? expf(lg - m) : 0.f);
+            const float r = m + logf(z) + (pr.lambda ? prior_term(pr, bh, h, C, i, c, cell) : 0.f);
+            if (lane == 0) s_key[j] = float_key(r);
         }
-        // ranked by the unscaled dot without the prior (1/sqrt(d) > 0 keeps the order)
-        s_key[j] = float_key(pr.lambda ? fmaf(dot, inv_sqrt_d, prior_term(pr, bh, h, C, i, c, cell))
-                                       : dot);
+    } else {
+        const float* kb_head = kbar + bh * (long)C * D;
+        for (int j = lane; j < n_cand; j += kWave) {
+            const int c = cand ? cand[j] : j;
+            const float* kb = kb_head + (long)c * D;
+            float dot = 0.f;
+#pragma unroll 8
+            for (int e = 0; e < D; e += 4) {
+                const float4 kv = *reinterpret_cast<const float4*>(kb + e);
+                dot = fmaf(s_q[e], kv.x, dot);
+                dot = fmaf(s_q[e + 1], kv.y, dot);
+                dot = fmaf(s_q[e + 2], kv.z, dot);
+                dot = fmaf(s_q[e + 3], kv.w, dot);
+            }
+            // ranked by the unscaled dot without the prior (1/sqrt(d) > 0 keeps the order)
+            s_key[j] = float_key(pr.lambda ? fmaf(dot, inv_sqrt_d,
+                                                  prior_term(pr, bh, h, C, i, c, cell))
+                                           : dot);
+        }
     }
     __syncthreads();
     if (!active) return;
@@ -137,7 +160,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
         if (kept) {
             const int pos = written + lanes_below(mk);
             out_i[pos] = cand ? cand[j] : j;
-            if (out_s) out_s[pos] = key_to_float(kj) * (pr.lambda ? 1.f : inv_sqrt_d);
+            if (out_s) out_s[pos] = key_to_float(kj) * (RERANK || pr.lambda ? 1.f : inv_sqrt_d);
         }
         written += __popcll(mk);
         eq_seen += __popcll(me);
@@ -241,41 +264,18 @@ __device__ __forceinline__ int field5(const uint32_t* w, int i)
 
 }  // namespace
 
-template <int D, int NB>
-__global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel(   // 256 threads exactly
-    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
-    const float* __restrict__ kbar, Prior pr, int H, int BH, int C, int nq, int q_pos0,
-    int window, int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
-    int keep_w, int n_lo, int n_rows, int topk, int n_hi_all, int u_cap, float inv_sqrt_d,
-    int32_t* __restrict__ idx, float* __restrict__ score)
+// Union of the candidate sets of a workgroup's queries (candidate counts n_a ..
+// n_b): the keep rows copied to LDS, a bitmap over cells, per-word ranks, the
+// union list ulist (slot -> cell) and vmask (bit r: the slot is in keep row
+// n_a + r).  Without pruning the union is the prefix [0, n_b) and slot == cell.
+// Returns the union size; ends with the block synchronised.
+__device__ __forceinline__ int sel_union(const int32_t* __restrict__ keep,
+                                         const int32_t* __restrict__ keep_count, int keep_w,
+                                         long bh, int n_lo, int n_rows, int n_a, int n_b,
+                                         uint16_t* krows, uint32_t* bitmap, uint16_t* rank,
+                                         uint16_t* ulist, uint32_t* vmask, int* red)
 {
-    using namespace mf;
-    constexpr int KS = D / 32;
-    constexpr int kTq = 64;                                    // queries per workgroup
-    constexpr int kNW = (NB + kFieldsPerWord - 1) / kFieldsPerWord;
-    constexpr int kKW = (4 * NB + 31) / 32;                    // kept-key mask words
-    extern __shared__ uint4 smem_raw[];
-    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, keep ? keep_w : 0);
-    char* base = reinterpret_cast<char*>(smem_raw);
-    uint16_t* kbs = reinterpret_cast<uint16_t*>(base);      // [3 * kSelChunk] swizzled rows of D
-    uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
-    uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
-    uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
-    uint32_t* vmask = reinterpret_cast<uint32_t*>(base + L.off_vmask);
-    uint16_t* krows = reinterpret_cast<uint16_t*>(base + L.off_krows);
-    __shared__ int red[4];
-
-    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-    const int n = lane & 15, g = lane >> 4;
-    const TileOfBlock tb = xcd_tile(BH);
-    const long bh = tb.bh;
-    const int h = (int)(bh % H), b = (int)(bh / H);
-    const long t0 = tb.tile * kTq;
-    const int n_rows_blk = nq - t0 < kTq ? (int)(nq - t0) : kTq;
-    const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
-    const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
-
-    // ---- union of the candidate sets of the block's queries --------------
+    const int tid = threadIdx.x;
     int n_union;
     if (keep != nullptr) {
         const int nw = (n_b + 31) >> 5;
@@ -347,121 +347,23 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
         n_union = n_b;   // candidates are the prefix [0, n_i); slot == cell
     }
 
-    // ---- the wave's 16 queries as B operands --------------------------------
-    const int qr = 16 * wv + n;                 // this lane's query row in the block
-    const bool q_ok = qr < n_rows_blk;
-    const int n_q = q_ok ? n_candidates((long)q_pos0 + t0 + qr, window, cell, C) : 0;
-    bf16x8 qf[KS];
-    {
-        const uint16_t* qrow = q + b * qs0 + h * qs1 + (t0 + (q_ok ? qr : 0)) * qs2;
-#pragma unroll
-        for (int t = 0; t < KS; ++t)
-            qf[t] = as_bf16x8(q_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
-                                   : make_uint4(0, 0, 0, 0));
-    }
-
-    // ---- scores S^T = Kbar Q^T over the union, kept in registers ------------
-    // kv[bb][r] is the key of union slot 16 bb + 4 g + r for query n (0 when that
-    // slot is not one of the query's candidates).  The next chunk's kbar rows are
-    // loaded into registers while the current chunk's MFMAs run.
-    constexpr int kIt = kSelChunk * D / 4 / 256;     // float4 per thread per chunk
-    const float* kb_head = kbar + bh * (long)C * D;
-    float4 pre[kIt];
-    auto load_chunk = [&](int c0) {
-#pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int f = tid + 256 * it;
-            const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
-            const int slot = c0 + cl;
-            pre[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (slot < n_union) {
-                const int c = keep ? ulist[slot] : slot;
-                pre[it] = *reinterpret_cast<const float4*>(kb_head + (long)c * D + d4);
-            }
-        }
-    };
-    uint32_t kv[NB][4];
     __syncthreads();                         // ulist / vmask complete
-    load_chunk(0);
-#pragma unroll
-    for (int ci = 0; ci < (NB + 1) / 2; ++ci) {
-        const int c0 = ci * kSelChunk;
-        if (c0 < n_union) {                  // block-uniform
-            __syncthreads();                 // previous chunk's MFMA reads are done
-#pragma unroll
-            for (int it = 0; it < kIt; ++it) {
-                const int f = tid + 256 * it;
-                const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
-                const float r[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
-                // x = hi + mid + lo exactly: each residual has at most 16 (then 8)
-                // significant bits, so the fp32 subtractions are exact.
-                uint32_t part[3][2];
-#pragma unroll
-                for (int e = 0; e < 4; e += 2) {
-                    float a0 = r[e], a1 = r[e + 1];
-                    const uint32_t hi = cvt_pk_bf16(a0, a1);
-                    a0 -= __uint_as_float(hi << 16);
-                    a1 -= __uint_as_float(hi & 0xFFFF0000u);
-                    const uint32_t mid = cvt_pk_bf16(a0, a1);
-                    a0 -= __uint_as_float(mid << 16);
-                    a1 -= __uint_as_float(mid & 0xFFFF0000u);
-                    part[0][e / 2] = hi;
-                    part[1][e / 2] = mid;
-                    part[2][e / 2] = cvt_pk_bf16(a0, a1);
-                }
-#pragma unroll
-                for (int pp = 0; pp < 3; ++pp)
-                    *reinterpret_cast<uint2*>(kbs + sw_off<D>(pp * kSelChunk + cl, d4 >> 3) + (d4 & 4)) =
-                        make_uint2(part[pp][0], part[pp][1]);
-            }
-            __syncthreads();
-            if (c0 + kSelChunk < n_union) load_chunk(c0 + kSelChunk);
-#pragma unroll
-            for (int b2 = 0; b2 < 2; ++b2) {
-                const int bb = 2 * ci + b2;
-                if (bb >= NB) break;
-                const int slot0 = 16 * bb;
-                if (slot0 < n_union) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < KS; ++t) {
-#pragma unroll
-                        for (int pp = 0; pp < 3; ++pp) {
-                            const bf16x8 a = as_bf16x8(
-                                lds_load16(kbs + sw_off<D>(pp * kSelChunk + 16 * b2 + n, 4 * t + g)));
-                            acc = mfma(a, qf[t], acc);
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int slot = slot0 + 4 * g + r;
-                        bool ok = slot < n_union && n_q > 0;
-                        if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
-                        float rr = acc[r];   // the unscaled dot ranks alike without the prior
-                        if (pr.lambda && ok)
-                            rr = fmaf(rr, inv_sqrt_d,
-                                      prior_term(pr, bh, h, C, (long)q_pos0 + t0 + qr,
-                                                 keep ? ulist[slot] : slot, cell));
-                        kv[bb][r] = ok ? float_key(rr) : 0u;
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) kv[bb][r] = 0u;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int b2 = 0; b2 < 2; ++b2) {
-                const int bb = 2 * ci + b2;
-                if (bb < NB) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) kv[bb][r] = 0u;
-                }
-            }
-        }
-    }
+    return n_union;
+}
 
-    // ---- per query: exact top-K over its four lanes -------------------------
+// Exact top-K of each query over its four lanes (n, n+16, n+32, n+48), from the
+// keys kv[bb][r] of union slots 16 bb + 4 g + r (0 = not a candidate), and the
+// chosen cells written ascending to the query's idx row (score: the key's value
+// times emit_scale).
+template <int NB>
+__device__ __forceinline__ void sel_topk_emit(const uint32_t (&kv)[NB][4], int topk, bool q_ok,
+                                              int32_t* __restrict__ out_i, float* __restrict__ out_s,
+                                              const int32_t* __restrict__ keep,
+                                              const uint16_t* ulist, float emit_scale)
+{
+    constexpr int kNW = (NB + kFieldsPerWord - 1) / kFieldsPerWord;
+    constexpr int kKW = (4 * NB + 31) / 32;                    // kept-key mask words
+    const int g = (threadIdx.x & 63) >> 4;
     int nv = 0;
     uint32_t k_and = 0xFFFFFFFFu, k_or = 0u;
 #pragma unroll
@@ -563,9 +465,6 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
     // ---- write the kept cells in ascending slot order -------------------------
     // Slot order is (bb, g, r): a kept key's position is the kept count of the
     // earlier blocks, of the lanes g' < g in its block, and of its own r' < r.
-    const long orow = bh * nq + t0 + (q_ok ? qr : 0);
-    int32_t* out_i = idx + orow * topk;
-    float* out_s = score ? score + orow * topk : nullptr;
     {
         uint32_t cw[kNW], ex[kNW], tot[kNW];
 #pragma unroll
@@ -587,7 +486,7 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
                     if ((km[(4 * bb + r) / 32] >> ((4 * bb + r) % 32)) & 1u) {
                         const int slot = 16 * bb + 4 * g + r;
                         out_i[p] = keep ? ulist[slot] : slot;
-                        if (out_s) out_s[p] = key_to_float(kv[bb][r]) * (pr.lambda ? 1.f : inv_sqrt_d);
+                        if (out_s) out_s[p] = key_to_float(kv[bb][r]) * emit_scale;
                         ++p;
                     }
                 }
@@ -603,9 +502,317 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
     }
 }
 
-hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
-                         const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
-                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st)
+template <int D, int NB>
+__global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel(   // 256 threads exactly
+    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const float* __restrict__ kbar, Prior pr, int H, int BH, int C, int nq, int q_pos0,
+    int window, int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
+    int keep_w, int n_lo, int n_rows, int topk, int n_hi_all, int u_cap, float inv_sqrt_d,
+    int32_t* __restrict__ idx, float* __restrict__ score)
+{
+    using namespace mf;
+    constexpr int KS = D / 32;
+    constexpr int kTq = 64;                                    // queries per workgroup
+    extern __shared__ uint4 smem_raw[];
+    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, keep ? keep_w : 0);
+    char* base = reinterpret_cast<char*>(smem_raw);
+    uint16_t* kbs = reinterpret_cast<uint16_t*>(base);      // [3 * kSelChunk] swizzled rows of D
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
+    uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
+    uint32_t* vmask = reinterpret_cast<uint32_t*>(base + L.off_vmask);
+    uint16_t* krows = reinterpret_cast<uint16_t*>(base + L.off_krows);
+    __shared__ int red[4];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long t0 = tb.tile * kTq;
+    const int n_rows_blk = nq - t0 < kTq ? (int)(nq - t0) : kTq;
+    const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
+    const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
+
+    const int n_union = sel_union(keep, keep_count, keep_w, bh, n_lo, n_rows, n_a, n_b, krows,
+                                  bitmap, rank, ulist, vmask, red);
+
+    // ---- the wave's 16 queries as B operands --------------------------------
+    const int qr = 16 * wv + n;                 // this lane's query row in the block
+    const bool q_ok = qr < n_rows_blk;
+    const int n_q = q_ok ? n_candidates((long)q_pos0 + t0 + qr, window, cell, C) : 0;
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qrow = q + b * qs0 + h * qs1 + (t0 + (q_ok ? qr : 0)) * qs2;
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+            qf[t] = as_bf16x8(q_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
+                                   : make_uint4(0, 0, 0, 0));
+    }
+
+    // ---- scores S^T = Kbar Q^T over the union, kept in registers ------------
+    // kv[bb][r] is the key of union slot 16 bb + 4 g + r for query n (0 when that
+    // slot is not one of the query's candidates).  The next chunk's kbar rows are
+    // loaded into registers while the current chunk's MFMAs run.
+    constexpr int kIt = kSelChunk * D / 4 / 256;     // float4 per thread per chunk
+    const float* kb_head = kbar + bh * (long)C * D;
+    float4 pre[kIt];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int f = tid + 256 * it;
+            const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
+            const int slot = c0 + cl;
+            pre[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot < n_union) {
+                const int c = keep ? ulist[slot] : slot;
+                pre[it] = *reinterpret_cast<const float4*>(kb_head + (long)c * D + d4);
+            }
+        }
+    };
+    uint32_t kv[NB][4];
+    load_chunk(0);
+#pragma unroll
+    for (int ci = 0; ci < (NB + 1) / 2; ++ci) {
+        const int c0 = ci * kSelChunk;
+        if (c0 < n_union) {                  // block-uniform
+            __syncthreads();                 // previous chunk's MFMA reads are done
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int f = tid + 256 * it;
+                const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
+                const float r[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
+                // x = hi + mid + lo exactly: each residual has at most 16 (then 8)
+                // significant bits, so the fp32 subtractions are exact.
+                uint32_t part[3][2];
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    float a0 = r[e], a1 = r[e + 1];
+                    const uint32_t hi = cvt_pk_bf16(a0, a1);
+                    a0 -= __uint_as_float(hi << 16);
+                    a1 -= __uint_as_float(hi & 0xFFFF0000u);
+                    const uint32_t mid = cvt_pk_bf16(a0, a1);
+                    a0 -= __uint_as_float(mid << 16);
+                    a1 -= __uint_as_float(mid & 0xFFFF0000u);
+                    part[0][e / 2] = hi;
+                    part[1][e / 2] = mid;
+                    part[2][e / 2] = cvt_pk_bf16(a0, a1);
+                }
+#pragma unroll
+                for (int pp = 0; pp < 3; ++pp)
+                    *reinterpret_cast<uint2*>(kbs + sw_off<D>(pp * kSelChunk + cl, d4 >> 3) + (d4 & 4)) =
+                        make_uint2(part[pp][0], part[pp][1]);
+            }
+            __syncthreads();
+            if (c0 + kSelChunk < n_union) load_chunk(c0 + kSelChunk);
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int bb = 2 * ci + b2;
+                if (bb >= NB) break;
+                const int slot0 = 16 * bb;
+                if (slot0 < n_union) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < KS; ++t) {
+#pragma unroll
+                        for (int pp = 0; pp < 3; ++pp) {
+                            const bf16x8 a = as_bf16x8(
+                                lds_load16(kbs + sw_off<D>(pp * kSelChunk + 16 * b2 + n, 4 * t + g)));
+                            acc = mfma(a, qf[t], acc);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int slot = slot0 + 4 * g + r;
+                        bool ok = slot < n_union && n_q > 0;
+                        if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
+                        float rr = acc[r];   // the unscaled dot ranks alike without the prior
+                        if (pr.lambda && ok)
+                            rr = fmaf(rr, inv_sqrt_d,
+                                      prior_term(pr, bh, h, C, (long)q_pos0 + t0 + qr,
+                                                 keep ? ulist[slot] : slot, cell));
+                        kv[bb][r] = ok ? float_key(rr) : 0u;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) kv[bb][r] = 0u;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int bb = 2 * ci + b2;
+                if (bb < NB) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) kv[bb][r] = 0u;
+                }
+            }
+        }
+    }
+
+    // ---- per query: exact top-K over its four lanes -------------------------
+    const long orow = bh * nq + t0 + (q_ok ? qr : 0);
+    sel_topk_emit<NB>(kv, topk, q_ok, idx + orow * topk, score ? score + orow * topk : nullptr,
+                      keep, ulist, pr.lambda ? 1.f : inv_sqrt_d);
+}
+
+// Token-level reranking (section 3.4, eq. 12) and top-K.  The same workgroup
+// shape, candidate union and selection as the kernel above; the score of union
+// slot u for query n is the log-sum-exp of the s = 32 logits q.k_j / sqrt(d) of
+// its cell's tokens (+ the eq. 7 prior).  Tiles of two cells (64 keys) are staged
+// in LDS (swizzled, bf16 as stored) and multiplied by the wave's 16 queries on
+// the matrix core; a cell's 32 logits of a query sit in the query's four lanes
+// (8 each), so its log-sum-exp is a max and a sum over those lanes.  The next
+// tile is loaded into registers while the current one is scored.
+template <int D, int NB>
+__global__ __launch_bounds__(256, NB >= 33 ? 1 : 2) void rerank_topk_mfma_kernel(
+    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const uint16_t* __restrict__ k, int64_t kvs0, int64_t kvs1, int64_t kvs2, Prior pr, int H,
+    int BH, int C, int nq, int q_pos0, int window, int cell, const int32_t* __restrict__ keep,
+    const int32_t* __restrict__ keep_count, int keep_w, int n_lo, int n_rows, int topk,
+    int n_hi_all, int u_cap, float inv_sqrt_d, int32_t* __restrict__ idx,
+    float* __restrict__ score)
+{
+    using namespace mf;
+    constexpr int KS = D / 32;
+    constexpr int kTq = 64;
+    constexpr int KC = (kTileK * D / 8) / 256;            // 16-byte K chunks per thread
+    extern __shared__ uint4 smem_raw[];
+    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, keep ? keep_w : 0);
+    char* base = reinterpret_cast<char*>(smem_raw);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(base);       // one swizzled 64-key tile
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
+    uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
+    uint32_t* vmask = reinterpret_cast<uint32_t*>(base + L.off_vmask);
+    uint16_t* krows = reinterpret_cast<uint16_t*>(base + L.off_krows);
+    __shared__ int red[4];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long t0 = tb.tile * kTq;
+    const int n_rows_blk = nq - t0 < kTq ? (int)(nq - t0) : kTq;
+    const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
+    const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
+    const int n_union = sel_union(keep, keep_count, keep_w, bh, n_lo, n_rows, n_a, n_b, krows,
+                                  bitmap, rank, ulist, vmask, red);
+
+    const int qr = 16 * wv + n;
+    const bool q_ok = qr < n_rows_blk;
+    const long qpos = (long)q_pos0 + t0 + qr;
+    const int n_q = q_ok ? n_candidates(qpos, window, cell, C) : 0;
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qrow = q + b * qs0 + h * qs1 + (t0 + (q_ok ? qr : 0)) * qs2;
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+            qf[t] = as_bf16x8(q_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
+                                   : make_uint4(0, 0, 0, 0));
+    }
+
+    // K rows of the tile of union slots 2u, 2u + 1 (a slot past the union repeats
+    // the first cell; its score is masked below)
+    const uint16_t* kh = k + b * kvs0 + h * kvs1;
+    uint4 st[KC];
+    auto load_tile = [&](int u) {
+        const int s0 = 2 * u, s1 = 2 * u + 1 < n_union ? 2 * u + 1 : 2 * u;
+        const int c0 = keep ? ulist[s0] : s0, c1 = keep ? ulist[s1] : s1;
+#pragma unroll
+        for (int it = 0; it < KC; ++it) {
+            const int cidx = tid + 256 * it;
+            const int kr = cidx / (D / 8), part = cidx % (D / 8);
+            const int c = kr < 32 ? c0 : c1;
+            st[it] = *reinterpret_cast<const uint4*>(kh + ((long)c * cell + (kr & 31)) * kvs2 +
+                                                     part * 8);
+        }
+    };
+    const int n_tiles = (n_union + 1) / 2;
+    const float scale_log2 = inv_sqrt_d * 1.4426950408889634f;
+    uint32_t kv[NB][4];
+    if (n_tiles > 0) load_tile(0);
+#pragma clang loop unroll(full)
+    for (int bb = 0; bb < NB; ++bb) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};        // this lane's slots 16 bb + 4 g + r
+        if (16 * bb < n_union) {                   // block-uniform
+            for (int t = 0; t < 8; ++t) {
+                const int u = 8 * bb + t;
+                if (u >= n_tiles) break;           // block-uniform
+                __syncthreads();                   // the previous tile's reads are done
+#pragma unroll
+                for (int it = 0; it < KC; ++it) {
+                    const int cidx = tid + 256 * it;
+                    lds_store16(ks + ksw_off<D>(cidx / (D / 8), cidx % (D / 8)), st[it]);
+                }
+                __syncthreads();
+                if (u + 1 < n_tiles) load_tile(u + 1);
+                f32x4 s4[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) s4[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int tt = 0; tt < KS; ++tt)
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        s4[kb] = mfma(as_bf16x8(lds_load16(ks + ksw_off<D>(16 * kb + n, 4 * tt + g))),
+                                      qf[tt], s4[kb]);
+                float lse[2];
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    float m = -INFINITY;
+#pragma unroll
+                    for (int kb = 2 * c2; kb < 2 * c2 + 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) m = fmaxf(m, s4[kb][r]);
+                    m = xrow_max(m);
+                    float z = 0.f;
+#pragma unroll
+                    for (int kb = 2 * c2; kb < 2 * c2 + 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            z += __builtin_amdgcn_exp2f((s4[kb][r] - m) * scale_log2);
+                    z = xrow_sum(z);                   // >= 1: the max term is exp2(0)
+                    lse[c2] = m * inv_sqrt_d + __log2f(z) * 0.6931471805599453f;
+                }
+                // slots 16 bb + 2t + c2 belong to lane row g = t / 2, r = 2 (t % 2) + c2
+                if (g == (t >> 1)) {
+                    if (t & 1) {
+                        v[2] = lse[0];
+                        v[3] = lse[1];
+                    } else {
+                        v[0] = lse[0];
+                        v[1] = lse[1];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int slot = 16 * bb + 4 * g + r;
+            bool ok = slot < n_union && n_q > 0;
+            if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
+            float rr = v[r];
+            if (pr.lambda && ok)
+                rr += prior_term(pr, bh, h, C, qpos, keep ? ulist[slot] : slot, cell);
+            kv[bb][r] = ok ? float_key(rr) : 0u;
+        }
+    }
+
+    const long orow = bh * nq + t0 + (q_ok ? qr : 0);
+    sel_topk_emit<NB>(kv, topk, q_ok, idx + orow * topk, score ? score + orow * topk : nullptr,
+                      keep, ulist, 1.f);
+}
+
+namespace {
+
+// Top-K over the candidates of every query: eq. 7 scores from kbar, or (rerank)
+// eq. 12 scores from the keys k.  MFMA kernels for bf16 storage when every
+// query's candidates fit the register blocks; row-wise kernels otherwise.
+hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const void* k,
+                       const Prior& pr, const int32_t* keep, const int32_t* keep_count,
+                       int keep_w, int n_lo, int n_rows, int topk, int32_t* idx, float* score,
+                       bool rerank, hipStream_t st)
 {
     if (sh.nq == 0) return hipSuccess;
     // Largest candidate list: the keep width, or every cell below the last query's n.
@@ -615,7 +822,7 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
         if (i >= sh.w) n_hi = (int)((i - sh.w) / sh.s);
         if (n_hi > sh.C) n_hi = sh.C;
     }
-    // MFMA path: bf16 storage; every query's candidates fit the register blocks.
+    const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
     {
         const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
         const int uc = ((u_cap > 0 ? u_cap : 1) + 15) & ~15;     // 16-cell blocks
@@ -624,20 +831,27 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
                                       : sel_layout<128>(n_hi, uc, kw).bytes;
         if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks) {
             dim3 grid((unsigned)((sh.nq + 63) / 64 * sh.B * sh.H));
-            const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
             const int nb_need = uc / 16;
 #define FS_SELECT_MFMA(D, NB)                                                                   \
-            hipLaunchKernelGGL((select_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,        \
-                               (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr, sh.H, \
-                               sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,            \
-                               keep_count, keep_w,                                               \
-                               n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, idx, score)
+            if (rerank)                                                                         \
+                hipLaunchKernelGGL((rerank_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,  \
+                                   (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2],             \
+                                   (const uint16_t*)k, sh.kvs[0], sh.kvs[1], sh.kvs[2], pr,      \
+                                   sh.H, sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,  \
+                                   keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, \
+                                   idx, score);                                                  \
+            else                                                                                \
+                hipLaunchKernelGGL((select_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,  \
+                                   (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,   \
+                                   sh.H, sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,  \
+                                   keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, \
+                                   idx, score)
 #define FS_SELECT_NB(D)                                                                         \
-            if (nb_need <= 2) FS_SELECT_MFMA(D, 2);                                             \
-            else if (nb_need <= 4) FS_SELECT_MFMA(D, 4);                                        \
-            else if (nb_need <= 9) FS_SELECT_MFMA(D, 9);                                        \
-            else if (nb_need <= 17) FS_SELECT_MFMA(D, 17);                                      \
-            else FS_SELECT_MFMA(D, 33);
+            if (nb_need <= 2) { FS_SELECT_MFMA(D, 2); }                                         \
+            else if (nb_need <= 4) { FS_SELECT_MFMA(D, 4); }                                    \
+            else if (nb_need <= 9) { FS_SELECT_MFMA(D, 9); }                                    \
+            else if (nb_need <= 17) { FS_SELECT_MFMA(D, 17); }                                  \
+            else { FS_SELECT_MFMA(D, 33); }
             if (sh.d == 64) { FS_SELECT_NB(64) } else { FS_SELECT_NB(128) }
 #undef FS_SELECT_NB
 #undef FS_SELECT_MFMA
@@ -652,20 +866,40 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
     if (lds > 65536) return hipErrorInvalidValue;
     dim3 grid((unsigned)((sh.nq + waves - 1) / waves), (unsigned)(sh.B * sh.H));
     dim3 block(waves * kWave);
-    const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
-#define FS_SELECT(E, D)                                                                        \
-    hipLaunchKernelGGL((select_topk_kernel<E, D>), grid, block, lds, st,                       \
-                       (const typename E::storage*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,   \
-                       sh.H,                                                                     \
-                       sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep, keep_count, keep_w, n_lo,      \
+#define FS_SELECT(E, D, RR)                                                                    \
+    hipLaunchKernelGGL((select_topk_kernel<E, D, RR>), grid, block, lds, st,                   \
+                       (const typename E::storage*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar,       \
+                       (const typename E::storage*)k, sh.kvs[0], sh.kvs[1], sh.kvs[2], pr,      \
+                       sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep, keep_count, keep_w, n_lo,\
                        n_rows, topk, cap, inv_sqrt_d, idx, score)
+#define FS_SELECT_RR(E, D)                                                                     \
+    if (rerank) { FS_SELECT(E, D, true); } else { FS_SELECT(E, D, false); }
     if (sh.bf16) {
-        if (sh.d == 64) FS_SELECT(Bf16, 64); else FS_SELECT(Bf16, 128);
+        if (sh.d == 64) { FS_SELECT_RR(Bf16, 64) } else { FS_SELECT_RR(Bf16, 128) }
     } else {
-        if (sh.d == 64) FS_SELECT(F32, 64); else FS_SELECT(F32, 128);
+        if (sh.d == 64) { FS_SELECT_RR(F32, 64) } else { FS_SELECT_RR(F32, 128) }
     }
+#undef FS_SELECT_RR
 #undef FS_SELECT
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
+                         const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
+                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st)
+{
+    return launch_topk(sh, q, kbar, nullptr, pr, keep, keep_count, keep_w, n_lo, n_rows, topk,
+                       idx, score, false, st);
+}
+
+hipError_t launch_rerank(const Shape& sh, const void* q, const void* k, const Prior& pr,
+                         const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
+                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st)
+{
+    return launch_topk(sh, q, nullptr, k, pr, keep, keep_count, keep_w, n_lo, n_rows, topk, idx,
+                       score, true, st);
 }
 
 }  // namespace fs

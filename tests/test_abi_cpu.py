@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_six_calls():
     names = _declared()
     for n in ("fs_cell_summaries", "fs_prune_prefix", "fs_select_topk", "fs_window_attn",
-              "fs_sparse_attn", "fs_combine"):
+              "fs_sparse_attn", "fs_combine", "fs_rerank_topk"):
         assert n in names
     assert set(names) == set(fs.SYMBOLS)
 
@@ -122,6 +122,13 @@ def test_call_specific_limits(lib):
         assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, 1e-6, FAKE, 16, FAKE,
                                   None) == 1
         assert b"workspace" in lib.fs_last_error()
+    # reranking validates like selection, and needs the keys
+    assert lib.fs_rerank_topk(C.byref(p), FAKE, None, None, None, None, None, None, 0, 8, FAKE,
+                              None, None) == 1
+    assert lib.fs_rerank_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 65, FAKE,
+                              None, None) == 2
+    assert lib.fs_rerank_topk(C.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, None, 0, 8, FAKE,
+                              None, None) == 1
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 10000.0, FAKE, 16, FAKE, None) == 1
     assert b"workspace" in lib.fs_last_error()
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 0.5, FAKE, 1 << 30, FAKE, None) == 1

@@ -249,6 +249,76 @@ def test_small_sparse(name):
     assert (got[none] == 0).all()
 
 
+def run_rerank(wl, x):
+    """GPU eq. 12 reranking with the forward's own summaries and keep rows."""
+    from long_context_fs_amd import fs as fsb
+    q, k = (to_dev(x[n], wl.dtype) for n in ("q", "k"))
+    fwd = FsForward.for_workload(wl)
+    fwd(q, k, to_dev(x["v"], wl.dtype), torch.from_numpy(x["alpha"]).cuda())
+    idx = torch.full_like(fwd.idx, -7)
+    score = torch.zeros_like(fwd.score)
+    fsb.fs_rerank_topk(fwd.prob, q, k, fwd.keep, fwd.keep_count, fwd.keep_w, wl.topk, idx, score,
+                       None, fwd.prior)
+    torch.cuda.synchronize()
+    g = dict(n_lo=fwd.n_lo, n_rows=fwd.n_rows, idx=idx.cpu().numpy(), score=score.cpu().numpy(),
+             amax=fwd.amax.cpu().numpy())
+    for name in ("keep", "keep_count"):
+        t = getattr(fwd, name)
+        g[name] = None if t is None else t.cpu().numpy()
+    return g
+
+
+def check_rerank(wl, x, g, rows):
+    """Eq. 12 sets exact up to near-ties; scores within fp32 dot / exp / log error."""
+    p = oracle.problem_from(wl)
+    lam, _ = wl.prior_arrays()
+    ties = 0
+    for b, h, t in rows:
+        i = wl.q_pos0 + t
+        cand = candidate_list(wl, g, b, h, i)
+        amax = g["amax"][b, h].astype(np.float64)
+        want, _, scores = orc().rerank_row(p, h, i, x["q"][b, h, t], x["k"][b, h], amax, cand)
+        sel = g["idx"][b, h, t]
+        chosen = sel[sel >= 0]
+        assert (sel[len(chosen):] == -1).all() and (np.diff(chosen) > 0).all()
+        ties += accept_set(chosen, cand, scores, wl.topk, want) == "tie"
+        if len(chosen):
+            pos = np.searchsorted(cand, chosen) if wl.budget >= 0 else chosen
+            kh = x["k"][b, h]
+            kn = max(np.linalg.norm(kh[c * wl.cell:(c + 1) * wl.cell], axis=1).max() for c in chosen)
+            mag = np.linalg.norm(x["q"][b, h, t]) * kn / np.sqrt(wl.head_dim) + 1.0
+            if lam is not None:
+                mag += float(lam[h]) * float(amax[chosen].max())
+            np.testing.assert_allclose(g["score"][b, h, t, :len(chosen)], scores[pos],
+                                       rtol=0, atol=2e-6 * mag)
+    return ties
+
+
+@pytest.mark.parametrize("name", ["bf16_d64_scaled_ragged", "bf16_d128_needle", "bf16_d128_decode",
+                                  "bf16_d64_noprune_bigk", "bf16_d128_prior", "f32_d64_noprune",
+                                  "f32_d64_prior_noprune"])
+def test_small_rerank(name):
+    """Token-level reranking (eq. 12) against the oracle on every query row."""
+    wl = SMALL[name]
+    x = synth.generate(wl)
+    g = run_rerank(wl, x)
+    ties = check_rerank(wl, x, g, all_rows(wl))
+    assert ties <= max(2, len(all_rows(wl)) // 200)
+
+
+@pytest.mark.parametrize("name", ["prefill_b1h8_n65536_d128_bf16", "decode_b1h8_n262144_q256_d128_bf16"])
+def test_full_size_rerank_sampled(name):
+    """Eq. 12 at full size, in the benchmark's launch configuration, on sampled rows."""
+    wl = synth.WORKLOADS[name]
+    x = synth.generate(wl)
+    g = run_rerank(wl, x)
+    rng = np.random.default_rng(3)
+    rows = [(0, int(h), int(t)) for h, t in zip(rng.integers(0, wl.heads, 48),
+                                                rng.integers(0, wl.n_q, 48))]
+    rows += [(0, h, wl.n_q - 1) for h in range(wl.heads)]
+    check_rerank(wl, x, g, rows)
+
+
 @pytest.mark.parametrize("name", ["bf16_d128_decode", "bf16_d64_hot", "bf16_d64_noprune_bigk"])
 def test_sparse_split_and_unsplit_agree(name):
     """The split readout (partial softmax states merged) and the unsplit one give
