@@ -33,10 +33,11 @@ ALSO = ["prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16",
 PHASES = ["summaries", "prune", "select", "window", "sparse", "combine"]
 # Source file of each phase's kernel (for matching stored HBM traffic counters).
 PHASE_SRC = {"summaries": "summaries.hip", "prune": "prune.hip", "select": "select.hip",
-             "window": "window.hip", "sparse": "sparse.hip", "combine": "combine.hip"}
+             "window": "window.hip", "sparse": "sparse.hip", "combine": "combine.hip",
+             "rerank": "select.hip"}
 # Engine each phase's kernel uses, which fixes the roofline it is priced against.
 PHASE_ENGINE = {"summaries": "hbm", "prune": "int", "select": "valu_f32", "window": "mfma_bf16",
-                "sparse": "mfma_bf16", "combine": "hbm"}
+                "sparse": "mfma_bf16", "combine": "hbm", "rerank": "mfma_bf16"}
 
 
 def n_cand(wl, i):
@@ -63,6 +64,8 @@ def algorithmic_work(wl, keep_count=None, n_lo=0):
     return {
         "summaries": {"bytes": BH * wl.n_cells * (s * d * e + (d + 1) * 4)},
         "select": {"flop": float(2 * d * a_i.sum())},
+        # eq. 12 reranking (not part of the step): every token of every candidate cell
+        "rerank": {"flop": float(2 * d * s * a_i.sum())},
         "window": {"flop": float(4 * d * win_keys.sum() * BH)},
         "sparse": {"flop": float(4 * d * s * sel_cells.sum() * BH)},
         "combine": {"bytes": 3 * BH * wl.n_q * d * e},
@@ -92,7 +95,7 @@ def stored_traffic(phase):
     return ent.get("bytes_per_launch")
 
 
-def run_workload(name, steps, warmup, torch, fs):
+def run_workload(name, steps, warmup, torch, fs, rerank=False):
     wl = synth.WORKLOADS[name]
     x = synth.generate(wl)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -145,18 +148,38 @@ def run_workload(name, steps, warmup, torch, fs):
         for j, ph in enumerate(PHASES):
             phase_ms[ph].append(ev[j].elapsed_time(ev[j + 1]))
     phase_avg = {ph: float(np.mean(v)) for ph, v in phase_ms.items()}
+    rerank_ms = None
+    if rerank:
+        # eq. 12 token-level reranking in place of eq. 7's scoring, timed on its own
+        rr_idx = torch.empty_like(fwd.idx)
+
+        def rr():
+            fs.fs_rerank_topk(p, q, k, fwd.keep, fwd.keep_count, fwd.keep_w, fwd.topk, rr_idx,
+                              None, None, fwd.prior)
+        for _ in range(warmup):
+            rr()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(steps):
+            rr()
+        s1.record()
+        torch.cuda.synchronize()
+        rerank_ms = s0.elapsed_time(s1) / steps
     kc = fwd.keep_count.cpu().numpy() if fwd.pruned else None
     work = algorithmic_work(wl, kc, fwd.n_lo)
     queries = wl.batch * wl.n_q
     total_flop = sum(w.get("flop", 0.0) for w in work.values())
+    if rerank_ms is not None:
+        phase_avg = dict(phase_avg, rerank=rerank_ms)
     return dict(wl=wl, ms_step=ms_step, wall=wall, phase_ms=phase_avg, work=work,
                 qps=queries / (ms_step * 1e-3), tflops=total_flop / (ms_step * 1e-3) / 1e12,
                 total_gflop=total_flop / 1e9)
 
 
-def roofline(res):
-    """Roofline entry for the phase that takes the most time."""
-    ph = max((p for p in PHASES if p != "prune"), key=lambda p: res["phase_ms"][p])
+def roofline(res, ph=None):
+    """Roofline entry for phase `ph`, by default the one that takes the most time."""
+    if ph is None:
+        ph = max((p for p in PHASES if p != "prune"), key=lambda p: res["phase_ms"][p])
     t = res["phase_ms"][ph] * 1e-3
     eng = PHASE_ENGINE[ph]
     w = res["work"][ph]
@@ -231,6 +254,8 @@ def run_phase(name, phase, reps, torch, fs):
                                             f.keep_count),
         "select": lambda: fs.fs_select_topk(p, q, f.kbar, f.keep, f.keep_count, f.keep_w,
                                             f.topk, f.idx, None, None, f.prior),
+        "rerank": lambda: fs.fs_rerank_topk(p, q, k, f.keep, f.keep_count, f.keep_w, f.topk,
+                                            f.idx, None, None, f.prior),
         "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),
         "sparse": lambda: fs.fs_sparse_attn(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_lr, f.ws_sparse),
         "combine": lambda: fs.fs_combine(p, f.o_sr, f.o_lr, alpha, f.o),
@@ -340,7 +365,7 @@ def main():
         run_phase(args.workload, args.phase, args.reps, torch, fs)
         return
 
-    main_res = run_workload(PRIMARY, args.steps, args.warmup, torch, fs)
+    main_res = run_workload(PRIMARY, args.steps, args.warmup, torch, fs, rerank=True)
     also = {}
     if not args.only_primary:
         for name in ALSO:
@@ -369,6 +394,7 @@ def main():
         "gflop_per_step": main_res["total_gflop"],
         "phase_ms": main_res["phase_ms"],
         "roofline": roofline(main_res),
+        "rerank": roofline(main_res, "rerank"),
         "also": also,
     }
     if not args.no_cpu_baseline:

@@ -183,17 +183,19 @@ struct SelLayout {
     size_t off_bitmap, off_rank, off_ulist, off_vmask, off_krows, bytes;
 };
 
-// LDS carve-up: kbar chunk split in 3 bf16 parts (swizzled rows) | bitmap |
-// rank | union list | row-membership masks | copy of the keep rows.
+// LDS carve-up: kbar chunk split in 3 bf16 parts (swizzled rows), or two
+// 64-key K tiles when reranking | bitmap | rank | union list | row-membership
+// masks | copy of the keep rows.
 template <int D>
-__host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int keep_w)
+__host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int keep_w, bool two_tiles = false)
 {
     SelLayout L;
     L.nwords = (n_hi + 31) / 32;
     L.u_cap = u_cap;
     L.keep_w = keep_w;
     auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
-    size_t off = (size_t)3 * kSelChunk * D * 2;
+    const size_t chunk = (size_t)3 * kSelChunk * D * 2, tiles = (size_t)2 * mf::kTileK * D * 2;
+    size_t off = two_tiles && tiles > chunk ? tiles : chunk;
     L.off_bitmap = off;
     off = up16(off + (size_t)L.nwords * 4);
     L.off_rank = off;
@@ -656,16 +658,33 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
                       keep, ulist, pr.lambda ? 1.f : inv_sqrt_d);
 }
 
+// Combine two partial log-sum-exps (m: max logit in log2 units, z: sum of
+// exp2(logit - m), z >= 1) into one; one exp2, and symmetric in its operands
+// only through their order, which both lanes of a pair share.
+__device__ __forceinline__ void lse_merge(float ma, float za, float mb, float zb, float& m,
+                                          float& z)
+{
+    const float dlt = mb - ma;
+    const float e = __builtin_amdgcn_exp2f(-fabsf(dlt));
+    m = __builtin_elementwise_maximum(ma, mb);
+    z = dlt <= 0.f ? fmaf(zb, e, za) : fmaf(za, e, zb);
+}
+
 // Token-level reranking (section 3.4, eq. 12) and top-K.  The same workgroup
 // shape, candidate union and selection as the kernel above; the score of union
 // slot u for query n is the log-sum-exp of the s = 32 logits q.k_j / sqrt(d) of
 // its cell's tokens (+ the eq. 7 prior).  Tiles of two cells (64 keys) are staged
-// in LDS (swizzled, bf16 as stored) and multiplied by the wave's 16 queries on
-// the matrix core; a cell's 32 logits of a query sit in the query's four lanes
-// (8 each), so its log-sum-exp is a max and a sum over those lanes.  The next
-// tile is loaded into registers while the current one is scored.
+// in LDS (swizzled, bf16 as stored; two buffers, one barrier per tile) and
+// multiplied by the wave's 16 queries on the matrix core.  A cell's 32 logits of
+// a query sit in the query's four lanes (8 each): each lane reduces its 8 to a
+// partial (max, sum of exp2), one lane-half swap merges the partials of both
+// cells at once (lanes 0-31 then hold the first cell, 32-63 the second) and a
+// row swap finishes them.  Tile t of 16-slot block bb holds slots 16 bb + t and
+// 16 bb + 8 + t, so each result lands in the lane that keeps its slot.  Tile
+// u + 2 is loaded into registers while tile u is scored and tile u + 1 is
+// written to the other buffer.
 template <int D, int NB>
-__global__ __launch_bounds__(256, NB >= 33 ? 1 : 2) void rerank_topk_mfma_kernel(
+__global__ __launch_bounds__(256, NB >= 33 ? 1 : (NB >= 17 ? 3 : 4)) void rerank_topk_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const uint16_t* __restrict__ k, int64_t kvs0, int64_t kvs1, int64_t kvs2, Prior pr, int H,
     int BH, int C, int nq, int q_pos0, int window, int cell, const int32_t* __restrict__ keep,
@@ -678,9 +697,9 @@ __global__ __launch_bounds__(256, NB >= 33 ? 1 : 2) void rerank_topk_mfma_kernel
     constexpr int kTq = 64;
     constexpr int KC = (kTileK * D / 8) / 256;            // 16-byte K chunks per thread
     extern __shared__ uint4 smem_raw[];
-    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, keep ? keep_w : 0);
+    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, keep ? keep_w : 0, true);
     char* base = reinterpret_cast<char*>(smem_raw);
-    uint16_t* ks = reinterpret_cast<uint16_t*>(base);       // one swizzled 64-key tile
+    uint16_t* ks = reinterpret_cast<uint16_t*>(base);       // two swizzled 64-key tiles
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
     uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
@@ -713,91 +732,130 @@ __global__ __launch_bounds__(256, NB >= 33 ? 1 : 2) void rerank_topk_mfma_kernel
                                    : make_uint4(0, 0, 0, 0));
     }
 
-    // K rows of the tile of union slots 2u, 2u + 1 (a slot past the union repeats
-    // the first cell; its score is masked below)
+    // Tile u (block bb = u / 8, t = u % 8) holds union slots 16 bb + t and
+    // 16 bb + 8 + t; a second slot past the union repeats the first cell (its
+    // score is masked below).  The tile count covers every slot below n_union.
     const uint16_t* kh = k + b * kvs0 + h * kvs1;
+    uint32_t koff[KC];                                  // byte offset of this thread's chunks in a cell
+#pragma unroll
+    for (int it = 0; it < KC; ++it) {
+        const int cidx = tid + 256 * it;
+        koff[it] = (uint32_t)((((cidx / (D / 8)) & 31) * kvs2 + (cidx % (D / 8)) * 8) * 2);
+    }
     uint4 st[KC];
     auto load_tile = [&](int u) {
-        const int s0 = 2 * u, s1 = 2 * u + 1 < n_union ? 2 * u + 1 : 2 * u;
-        const int c0 = keep ? ulist[s0] : s0, c1 = keep ? ulist[s1] : s1;
+        const int s0 = 16 * (u >> 3) + (u & 7);
+        const int s1 = s0 + 8 < n_union ? s0 + 8 : s0;
+        const int c0 = __builtin_amdgcn_readfirstlane(keep ? (int)ulist[s0] : s0);
+        const int c1 = __builtin_amdgcn_readfirstlane(keep ? (int)ulist[s1] : s1);
+        const char* p0 = reinterpret_cast<const char*>(kh + (long)c0 * cell * kvs2);
+        const char* p1 = reinterpret_cast<const char*>(kh + (long)c1 * cell * kvs2);
+#pragma unroll
+        for (int it = 0; it < KC; ++it)      // rows 0-31 of the tile: first cell
+            st[it] = *reinterpret_cast<const uint4*>((it < KC / 2 ? p0 : p1) + koff[it]);
+    };
+    auto store_tile = [&](uint16_t* buf) {
 #pragma unroll
         for (int it = 0; it < KC; ++it) {
             const int cidx = tid + 256 * it;
-            const int kr = cidx / (D / 8), part = cidx % (D / 8);
-            const int c = kr < 32 ? c0 : c1;
-            st[it] = *reinterpret_cast<const uint4*>(kh + ((long)c * cell + (kr & 31)) * kvs2 +
-                                                     part * 8);
+            lds_store16(buf + ksw_off<D>(cidx / (D / 8), cidx % (D / 8)), st[it]);
         }
     };
-    const int n_tiles = (n_union + 1) / 2;
+    const int n_full = n_union >> 4, rem = n_union & 15;
+    const int n_tiles = 8 * n_full + (rem < 8 ? rem : 8);
     const float scale_log2 = inv_sqrt_d * 1.4426950408889634f;
+    // kv[bb][r]: the log-sum-exp of union slot 16 bb + 4 g + r (float bits) until
+    // the loop ends, then its selection key
     uint32_t kv[NB][4];
-    if (n_tiles > 0) load_tile(0);
-#pragma clang loop unroll(full)
-    for (int bb = 0; bb < NB; ++bb) {
-        float v[4] = {0.f, 0.f, 0.f, 0.f};        // this lane's slots 16 bb + 4 g + r
-        if (16 * bb < n_union) {                   // block-uniform
-            for (int t = 0; t < 8; ++t) {
-                const int u = 8 * bb + t;
-                if (u >= n_tiles) break;           // block-uniform
-                __syncthreads();                   // the previous tile's reads are done
 #pragma unroll
-                for (int it = 0; it < KC; ++it) {
-                    const int cidx = tid + 256 * it;
-                    lds_store16(ks + ksw_off<D>(cidx / (D / 8), cidx % (D / 8)), st[it]);
-                }
-                __syncthreads();
-                if (u + 1 < n_tiles) load_tile(u + 1);
-                f32x4 s4[4];
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) s4[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int tt = 0; tt < KS; ++tt)
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
-                        s4[kb] = mfma(as_bf16x8(lds_load16(ks + ksw_off<D>(16 * kb + n, 4 * tt + g))),
-                                      qf[tt], s4[kb]);
-                float lse[2];
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    float m = -INFINITY;
-#pragma unroll
-                    for (int kb = 2 * c2; kb < 2 * c2 + 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) m = fmaxf(m, s4[kb][r]);
-                    m = xrow_max(m);
-                    float z = 0.f;
-#pragma unroll
-                    for (int kb = 2 * c2; kb < 2 * c2 + 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            z += __builtin_amdgcn_exp2f((s4[kb][r] - m) * scale_log2);
-                    z = xrow_sum(z);                   // >= 1: the max term is exp2(0)
-                    lse[c2] = m * inv_sqrt_d + __log2f(z) * 0.6931471805599453f;
-                }
-                // slots 16 bb + 2t + c2 belong to lane row g = t / 2, r = 2 (t % 2) + c2
-                if (g == (t >> 1)) {
-                    if (t & 1) {
-                        v[2] = lse[0];
-                        v[3] = lse[1];
-                    } else {
-                        v[0] = lse[0];
-                        v[1] = lse[1];
-                    }
-                }
-            }
+        for (int r = 0; r < 4; ++r) kv[bb][r] = 0u;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};             // the current 16-slot block's values
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(ks);
+        if (n_tiles > 1) load_tile(1);
+    }
+    for (int u = 0; u < n_tiles; ++u) {
+        __syncthreads();        // tile u is in buffer u % 2; reads of tile u - 1 are done
+        if (u + 1 < n_tiles) {
+            store_tile(ks + ((u + 1) & 1) * (kTileK * D));
+            if (u + 2 < n_tiles) load_tile(u + 2);
         }
+        const uint16_t* kt = ks + (u & 1) * (kTileK * D);
+        f32x4 s4[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s4[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < KS; ++tt)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                s4[kb] = mfma(as_bf16x8(lds_load16(kt + ksw_off<D>(16 * kb + n, 4 * tt + g))),
+                              qf[tt], s4[kb]);
+        // this lane's partial (max, sum) of each cell: logits of keys 16 kb + 4 g + r
+        float pm[2], pz[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            const f32x4 &x = s4[2 * c2], &y = s4[2 * c2 + 1];
+            // IEEE maximum: MFMA results need no NaN quieting first (finite here)
+            auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+            const float m = mx(mx(mx(x[0], x[1]), mx(x[2], x[3])), mx(mx(y[0], y[1]), mx(y[2], y[3])));
+            const float mb = m * scale_log2;
+            float z0 = __builtin_amdgcn_exp2f(fmaf(x[0], scale_log2, -mb));
+            float z1 = __builtin_amdgcn_exp2f(fmaf(y[0], scale_log2, -mb));
+#pragma unroll
+            for (int r = 1; r < 4; ++r) {
+                z0 += __builtin_amdgcn_exp2f(fmaf(x[r], scale_log2, -mb));
+                z1 += __builtin_amdgcn_exp2f(fmaf(y[r], scale_log2, -mb));
+            }
+            pm[c2] = mb;
+            pz[c2] = z0 + z1;
+        }
+        // lanes 0-31 pair up halves of the first cell, lanes 32-63 of the second
+        const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[0]),
+                                                         __float_as_uint(pm[1]), false, false);
+        const auto sz = __builtin_amdgcn_permlane32_swap(__float_as_uint(pz[0]),
+                                                         __float_as_uint(pz[1]), false, false);
+        float m1, z1;
+        lse_merge(__uint_as_float(sm[0]), __uint_as_float(sz[0]), __uint_as_float(sm[1]),
+                  __uint_as_float(sz[1]), m1, z1);
+        // then rows l and l ^ 16
+        const auto tm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m1), __float_as_uint(m1),
+                                                         false, false);
+        const auto tz = __builtin_amdgcn_permlane16_swap(__float_as_uint(z1), __float_as_uint(z1),
+                                                         false, false);
+        float m2, z2;
+        lse_merge(__uint_as_float(tm[0]), __uint_as_float(tz[0]), __uint_as_float(tm[1]),
+                  __uint_as_float(tz[1]), m2, z2);
+        const float lse = (m2 + __log2f(z2)) * 0.6931471805599453f;
+        // slot 16 bb + 8 c2 + t is kept by lane row g = 2 c2 + t / 4 at r = t % 4
+        const int t = u & 7;
+        const bool mine = (g & 1) == (t >> 2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = mine && r == (t & 3) ? lse : v[r];
+        if (t == 7 || u + 1 == n_tiles) {          // block-uniform: the 16-slot block is done
+            const int bbu = u >> 3;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+                if (bb == bbu) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) kv[bb][r] = __float_as_uint(v[r]);
+                }
+        }
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int slot = 16 * bb + 4 * g + r;
             bool ok = slot < n_union && n_q > 0;
             if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
-            float rr = v[r];
+            float rr = __uint_as_float(kv[bb][r]);
             if (pr.lambda && ok)
                 rr += prior_term(pr, bh, h, C, qpos, keep ? ulist[slot] : slot, cell);
             kv[bb][r] = ok ? float_key(rr) : 0u;
         }
-    }
 
     const long orow = bh * nq + t0 + (q_ok ? qr : 0);
     sel_topk_emit<NB>(kv, topk, q_ok, idx + orow * topk, score ? score + orow * topk : nullptr,
@@ -827,9 +885,12 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
         const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
         const int uc = ((u_cap > 0 ? u_cap : 1) + 15) & ~15;     // 16-cell blocks
         const int kw = keep ? keep_w : 0;
-        const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, kw).bytes
-                                      : sel_layout<128>(n_hi, uc, kw).bytes;
-        if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks) {
+        const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, kw, rerank).bytes
+                                      : sel_layout<128>(n_hi, uc, kw, rerank).bytes;
+        // reranking addresses a cell's rows with 32-bit byte offsets
+        const bool offs_ok = !rerank || ((int64_t)(sh.s - 1) * sh.kvs[2] + sh.d) * 2 < (1ll << 31);
+        if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks &&
+            offs_ok) {
             dim3 grid((unsigned)((sh.nq + 63) / 64 * sh.B * sh.H));
             const int nb_need = uc / 16;
 #define FS_SELECT_MFMA(D, NB)                                                                   \
