@@ -12,6 +12,8 @@
  *   fs_window_attn     eqs.3-4 RoPE attention over positions max(0,i-w) .. i
  *   fs_sparse_attn     eq. 9   NoPE attention over the selected cells' tokens, RMSNorm
  *   fs_rerank_topk     eq. 12  token-level reranking (log-sum-exp of a cell's logits), top-K
+ *   fs_stream_*        eqs. 2-9 from a bounded per-head state ("Bounded memory",
+ *                      Practical Implications): decode or chunked prefill
  *   fs_combine         eq. 2   o = o_sr + alpha_h * o_lr
  *
  * Readings of what the page leaves open (fixed here, identical in the oracle):
@@ -148,6 +150,47 @@ fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k
 /* Range combination, eq. 2: o = o_sr + alpha[h] * o_lr.  alpha: float32 [H]. */
 fs_status fs_combine(const fs_problem* problem, const void* o_sr, const void* o_lr,
                      const float* alpha, void* o, void* stream);
+
+/* ---- Streaming FS-L: eqs. 2-9 from a fixed-size per-head state ---------------
+ * The page's bounded-memory claim (Practical Implications, "Bounded memory"): FS-L
+ * needs O((P + W) s + w + B + s) d token state per head, independent of the
+ * sequence length, because eq. 8 discards a cell for good once it leaves both
+ * Recent_W and TopP (TopP over a longer prefix only ever takes the new cell).
+ * The state, one opaque device buffer owned by the caller, holds per (b, h): the
+ * last L >= w + s + max_new raw keys/values, the retained cells' raw keys/values
+ * and summaries in W + P + ceil(max_new / s) + 2 slots, and eq. 8's sets.  Its
+ * size depends on the config only, never on how many tokens have been appended. */
+typedef struct {
+    int32_t batch, heads, head_dim;   /* B, H, d (64 or 128) */
+    int32_t cell, window;             /* s (32), w (>= 0) */
+    int32_t n_recent, budget;         /* W, P of eq. 8: W, P >= 0, 1 <= W + P <= 1024 */
+    int32_t topk;                     /* K of eq. 9's selection, 1 .. 64 */
+    int32_t max_new;                  /* most tokens one step appends, 1 .. 4096 */
+    fs_dtype dtype;                   /* storage dtype of q/k/v/o and of the state */
+} fs_stream_config;
+
+/* Bytes of the state buffer for a config. */
+fs_status fs_stream_state_size(const fs_stream_config* cfg, size_t* bytes);
+
+/* Empty the state (no tokens).  state: device, 256-byte aligned, >= the size above. */
+fs_status fs_stream_reset(const fs_stream_config* cfg, void* state, size_t state_bytes,
+                          void* stream);
+
+/* One step: append the tokens at positions pos0 .. pos0 + n_new - 1 (k, v) of every
+ * (b, h) and return, for the queries q at those same positions, the FS-L output of
+ * eq. 2 (o_sr of eqs. 3-4 + alpha_h o_lr of eqs. 5, 7, 8, 9), computed from the state
+ * alone.  Equal to the fs_* calls above on the whole prefix for those queries.
+ * pos0 must be the number of tokens appended since the reset (not checked on the
+ * device), pos0 + n_new < 2^31, 1 <= n_new <= max_new.  q, k, v, o: contiguous
+ * [B][H][n_new][d] in the config's dtype (device, 16-byte aligned).  alpha: float32
+ * [H].  prior_lambda, prior_sigma: both NULL (no prior) or both float32 [H] (eq. 7).
+ * idx (nullable): int32 [B][H][n_new][topk], the selected cells (absolute cell
+ * indices, ascending, -1 padded).  Steps on one state must not overlap in time. */
+fs_status fs_stream_step(const fs_stream_config* cfg, void* state, size_t state_bytes,
+                         int64_t pos0, int32_t n_new, const void* q, const void* k,
+                         const void* v, const float* alpha, const float* prior_lambda,
+                         const float* prior_sigma, float rope_base, float rms_eps, void* o,
+                         int32_t* idx, void* stream);
 
 const char* fs_status_string(fs_status status);
 const char* fs_last_error(void);

@@ -8,6 +8,7 @@
 
 #include "../../include/fs.h"
 #include "fs_launch.hpp"
+#include "fs_stream.hpp"
 
 namespace {
 
@@ -271,6 +272,96 @@ fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k
     return from_hip(fs::launch_sparse(sh, q, k, v, idx, topk, rms_eps, workspace, o_lr,
                                       (hipStream_t)stream),
                     "fs_sparse_attn");
+}
+
+}  // extern "C"
+
+namespace {
+
+fs_status check_stream(const fs_stream_config* c, fs::StreamCfg* sc)
+{
+    if (!c) return fail(FS_ERR_INVALID, "config is NULL");
+    if (c->batch < 1 || c->heads < 1) return fail(FS_ERR_INVALID, "batch and heads must be >= 1");
+    if ((long)c->batch * c->heads > 65535)
+        return fail(FS_ERR_UNSUPPORTED, "batch * heads must be <= 65535");
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(FS_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128", c->head_dim);
+    if (c->cell != 32) return fail(FS_ERR_UNSUPPORTED, "cell %d: only 32", c->cell);
+    if (c->window < 0 || c->window > (1 << 20))
+        return fail(FS_ERR_UNSUPPORTED, "window %d outside [0, 2^20]", c->window);
+    if (c->n_recent < 0 || c->budget < 0 || c->n_recent + c->budget < 1 ||
+        c->n_recent + c->budget > 1024)
+        return fail(FS_ERR_UNSUPPORTED, "n_recent %d + budget %d must be in [1, 1024]",
+                    c->n_recent, c->budget);
+    if (c->topk < 1 || c->topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", c->topk);
+    if (c->max_new < 1 || c->max_new > 4096)
+        return fail(FS_ERR_UNSUPPORTED, "max_new %d outside [1, 4096]", c->max_new);
+    if (c->dtype != FS_F32 && c->dtype != FS_BF16) return fail(FS_ERR_INVALID, "dtype %d", c->dtype);
+    sc->B = c->batch; sc->H = c->heads; sc->d = c->head_dim; sc->s = c->cell; sc->w = c->window;
+    sc->W = c->n_recent; sc->P = c->budget; sc->K = c->topk; sc->max_new = c->max_new;
+    sc->bf16 = c->dtype == FS_BF16;
+    return FS_OK;
+}
+
+fs_status check_state(const fs::StreamLayout& Ly, const void* state, size_t state_bytes)
+{
+    if (!state) return fail(FS_ERR_INVALID, "state is NULL");
+    if (reinterpret_cast<uintptr_t>(state) % 256 != 0)
+        return fail(FS_ERR_INVALID, "state is not 256-byte aligned");
+    if (state_bytes < Ly.bytes)
+        return fail(FS_ERR_INVALID, "state of %zu bytes, need %zu", state_bytes, Ly.bytes);
+    return FS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fs_status fs_stream_state_size(const fs_stream_config* cfg, size_t* bytes)
+{
+    fs::StreamCfg sc;
+    FS_CHECK(check_stream(cfg, &sc));
+    if (!bytes) return fail(FS_ERR_INVALID, "bytes is NULL");
+    *bytes = fs::stream_layout(sc).bytes;
+    g_err[0] = 0;
+    return FS_OK;
+}
+
+fs_status fs_stream_reset(const fs_stream_config* cfg, void* state, size_t state_bytes,
+                          void* stream)
+{
+    fs::StreamCfg sc;
+    FS_CHECK(check_stream(cfg, &sc));
+    const fs::StreamLayout Ly = fs::stream_layout(sc);
+    FS_CHECK(check_state(Ly, state, state_bytes));
+    return from_hip(fs::launch_stream_reset(sc, Ly, state, (hipStream_t)stream), "fs_stream_reset");
+}
+
+fs_status fs_stream_step(const fs_stream_config* cfg, void* state, size_t state_bytes,
+                         int64_t pos0, int32_t n_new, const void* q, const void* k,
+                         const void* v, const float* alpha, const float* prior_lambda,
+                         const float* prior_sigma, float rope_base, float rms_eps, void* o,
+                         int32_t* idx, void* stream)
+{
+    fs::StreamCfg sc;
+    FS_CHECK(check_stream(cfg, &sc));
+    const fs::StreamLayout Ly = fs::stream_layout(sc);
+    FS_CHECK(check_state(Ly, state, state_bytes));
+    if (n_new < 1 || n_new > sc.max_new)
+        return fail(FS_ERR_INVALID, "n_new %d outside [1, max_new = %d]", n_new, sc.max_new);
+    if (pos0 < 0 || pos0 + n_new >= ((int64_t)1 << 31))
+        return fail(FS_ERR_UNSUPPORTED, "positions %lld .. %lld outside [0, 2^31)",
+                    (long long)pos0, (long long)(pos0 + n_new - 1));
+    FS_PTR(q); FS_PTR(k); FS_PTR(v); FS_PTR(o);
+    if (!alpha) return fail(FS_ERR_INVALID, "alpha is NULL");
+    if ((prior_lambda == nullptr) != (prior_sigma == nullptr))
+        return fail(FS_ERR_INVALID, "prior_lambda and prior_sigma go together");
+    if (!(rope_base > 1.0f)) return fail(FS_ERR_INVALID, "rope_base must be > 1");
+    if (!(rms_eps >= 0.0f)) return fail(FS_ERR_INVALID, "rms_eps must be >= 0");
+    return from_hip(fs::launch_stream_step(sc, Ly, state, pos0, n_new, q, k, v, alpha,
+                                           prior_lambda, prior_sigma, (double)rope_base,
+                                           rms_eps, o, idx, (hipStream_t)stream),
+                    "fs_stream_step");
 }
 
 fs_status fs_combine(const fs_problem* problem, const void* o_sr, const void* o_lr,

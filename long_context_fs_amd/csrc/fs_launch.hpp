@@ -36,6 +36,18 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
 hipError_t launch_rerank(const Shape& sh, const void* q, const void* k, const Prior& pr,
                          const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
                          int n_rows, int topk, int32_t* idx, float* score, hipStream_t st);
+// Selection over a streaming state's cell pool: keep rows of pool slots (ascending
+// cell order), row r of a head (rows_per_head apart) for candidate count
+// n_row0 + r; kbar [B*H][M][d], amax and cell_of
+// [B*H][M]; lambda == nullptr switches the prior off.  q is [B][H][nq][d] with
+// strides qs; queries sit at positions q_pos0 + t.
+hipError_t launch_stream_select(int B, int H, int d, bool bf16, const void* q, const int64_t* qs,
+                                const float* kbar, const float* amax, const int32_t* cell_of,
+                                int M, const float* lambda, const float* sigma, int nq,
+                                int64_t q_pos0, int window, int cell, const int32_t* keep,
+                                const int32_t* keep_count, int keep_w, int64_t n_row0,
+                                int rows_per_head, int topk, int32_t* idx_slot, int32_t* idx_cell,
+                                float* score, hipStream_t st);
 size_t rope_table_bytes(const Shape& sh);
 hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
                          double rope_base, void* table, void* o_sr, hipStream_t st);
@@ -49,5 +61,16 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
                          hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const void* o_sr, const void* o_lr, const float* alpha,
                           void* o, hipStream_t st);
+
+// Streaming state (fs_stream.hpp): reset, and one append + attend step.
+struct StreamCfg;
+struct StreamLayout;
+hipError_t launch_stream_reset(const StreamCfg& c, const StreamLayout& Ly, void* state,
+                               hipStream_t st);
+hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* state,
+                              int64_t pos0, int n_new, const void* q, const void* k,
+                              const void* v, const float* alpha, const float* lambda,
+                              const float* sigma, double rope_base, float rms_eps, void* o,
+                              int32_t* idx_cell, hipStream_t st);
 
 }  // namespace fs

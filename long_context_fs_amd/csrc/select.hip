@@ -35,6 +35,61 @@ __device__ __forceinline__ float key_to_float(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Exact top-K of one query (one wavefront) over the order-preserving keys
+// s_key[0..n_cand) in LDS: the K-th largest key by a 32-step bitwise search with
+// wave counts; of the keys equal to it, the last ones in list order are kept (the
+// lists are ascending in cell index, so ties go to the larger cell).  The chosen
+// entries are written in list order: out_i[pos] = id_of(j), out_s[pos] = the
+// key's value times out_scale; positions from min(K, n_cand) on get -1 / 0.
+template <class IdOf>
+__device__ __forceinline__ void row_topk_write(const uint32_t* s_key, int n_cand, int topk,
+                                               int lane, int32_t* __restrict__ out_i,
+                                               float* __restrict__ out_s, float out_scale,
+                                               IdOf id_of)
+{
+    const int kq = n_cand < topk ? n_cand : topk;
+    uint32_t thr = 0;
+    if (kq > 0) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t t = thr | (1u << bit);
+            int cnt = 0;
+            for (int j = lane; j < n_cand; j += kWave) cnt += s_key[j] >= t;
+            if (wave_sum_int(cnt) >= kq) thr = t;
+        }
+    }
+    int n_gt = 0, n_eq = 0;
+    for (int j = lane; j < n_cand; j += kWave) {
+        n_gt += s_key[j] > thr;
+        n_eq += s_key[j] == thr;
+    }
+    n_gt = wave_sum_int(n_gt);
+    n_eq = wave_sum_int(n_eq);
+    const int need_eq = kq - n_gt;
+
+    int written = 0, eq_seen = 0;
+    for (int j0 = 0; j0 < n_cand && kq > 0; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool in = j < n_cand;
+        const uint32_t kj = in ? s_key[j] : 0u;
+        const bool is_eq = in && kj == thr;
+        const uint64_t me = __ballot(is_eq);
+        const int eq_rank = eq_seen + lanes_below(me);
+        const bool kept = in && (kj > thr || (is_eq && eq_rank >= n_eq - need_eq));
+        const uint64_t mk = __ballot(kept);
+        if (kept) {
+            const int pos = written + lanes_below(mk);
+            out_i[pos] = id_of(j);
+            if (out_s) out_s[pos] = key_to_float(kj) * out_scale;
+        }
+        written += __popcll(mk);
+        eq_seen += __popcll(me);
+    }
+    for (int t = kq + lane; t < topk; t += kWave) {
+        out_i[t] = -1;
+        if (out_s) out_s[t] = 0.f;
+    }
+}
+
 // eq. 7's prior for the query at position i and cell c of head h (row bh of amax):
 // lambda_h a_c erf((i - p_c) / (2 sigma_h)), p_c = (c + 1/2) s.  i - c s is exact in
 // fp32 below 2^24 tokens; beyond, erf has long saturated for any sigma that small.
@@ -126,51 +181,110 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
     __syncthreads();
     if (!active) return;
 
-    const int kq = n_cand < topk ? n_cand : topk;
-    uint32_t thr = 0;
-    if (kq > 0) {
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t t = thr | (1u << bit);
-            int cnt = 0;
-            for (int j = lane; j < n_cand; j += kWave) cnt += s_key[j] >= t;
-            if (wave_sum_int(cnt) >= kq) thr = t;
-        }
-    }
-    int n_gt = 0, n_eq = 0;
-    for (int j = lane; j < n_cand; j += kWave) {
-        n_gt += s_key[j] > thr;
-        n_eq += s_key[j] == thr;
-    }
-    n_gt = wave_sum_int(n_gt);
-    n_eq = wave_sum_int(n_eq);
-    const int need_eq = kq - n_gt;
-
     int32_t* out_i = idx + (bh * nq + row) * (long)topk;
     float* out_s = score ? score + (bh * nq + row) * (long)topk : nullptr;
-    int written = 0, eq_seen = 0;
-    for (int j0 = 0; j0 < n_cand && kq > 0; j0 += kWave) {
-        const int j = j0 + lane;
-        const bool in = j < n_cand;
-        const uint32_t kj = in ? s_key[j] : 0u;
-        const bool is_eq = in && kj == thr;
-        const uint64_t me = __ballot(is_eq);
-        const int eq_rank = eq_seen + lanes_below(me);
-        const bool kept = in && (kj > thr || (is_eq && eq_rank >= n_eq - need_eq));
-        const uint64_t mk = __ballot(kept);
-        if (kept) {
-            const int pos = written + lanes_below(mk);
-            out_i[pos] = cand ? cand[j] : j;
-            if (out_s) out_s[pos] = key_to_float(kj) * (RERANK || pr.lambda ? 1.f : inv_sqrt_d);
-        }
-        written += __popcll(mk);
-        eq_seen += __popcll(me);
-    }
-    for (int t = kq + lane; t < topk; t += kWave) {
-        out_i[t] = -1;
-        if (out_s) out_s[t] = 0.f;
-    }
+    row_topk_write(s_key, n_cand, topk, lane, out_i, out_s,
+                   RERANK || pr.lambda ? 1.f : inv_sqrt_d,
+                   [&](int j) { return cand ? cand[j] : j; });
 }
 
+
+// Selection over a streaming state's cell pool (eq. 7 on the cells FS-L still
+// holds).  The keep row of a query lists pool slots in ascending cell order;
+// kbar, a_c and the cell index are stored per slot.  One wavefront per query,
+// scoring and ranking as the row-wise kernel above.  idx_slot receives slots
+// (what the readout gathers), idx_cell (optional) the same choice as cell indices.
+template <class E, int D>
+__global__ __launch_bounds__(kSelWaves * kWave) void stream_select_kernel(
+    const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const float* __restrict__ kbar, const float* __restrict__ amax,
+    const int32_t* __restrict__ cell_of, int M, const float* __restrict__ lambda,
+    const float* __restrict__ sigma, int H, int nq, int64_t q_pos0, int window, int cell,
+    const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count, int keep_w,
+    int64_t n_row0, int rows_per_head, int topk, float inv_sqrt_d, int32_t* __restrict__ idx_slot,
+    int32_t* __restrict__ idx_cell, float* __restrict__ score)
+{
+    extern __shared__ uint32_t smem[];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int waves = blockDim.x >> 6;
+    float* s_q = reinterpret_cast<float*>(smem) + wv * D;
+    uint32_t* s_key = smem + waves * D + wv * keep_w;
+
+    const long row = (long)blockIdx.x * waves + wv;
+    const long bh = blockIdx.y;
+    const bool active = row < nq;       // inactive waves still reach the barrier
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const int64_t i = q_pos0 + (active ? row : 0);
+    const int64_t n = i < window ? 0 : (i - window) / cell;
+    const long kr = bh * rows_per_head + (long)(n - n_row0);
+    const int32_t* cand = keep + kr * keep_w;
+    const int n_cand = active ? keep_count[kr] : 0;
+    if (active) {
+        const typename E::storage* qrow = q + b * qs0 + h * qs1 + row * qs2;
+        for (int e = lane; e < D; e += kWave) s_q[e] = load1<E>(qrow + e);
+    }
+    __syncthreads();
+    const float* kb_head = kbar + bh * (long)M * D;
+    for (int j = lane; j < n_cand; j += kWave) {
+        const int slot = cand[j];
+        const float* kb = kb_head + (long)slot * D;
+        float dot = 0.f;
+#pragma unroll 8
+        for (int e = 0; e < D; e += 4) {
+            const float4 kv = *reinterpret_cast<const float4*>(kb + e);
+            dot = fmaf(s_q[e], kv.x, dot);
+            dot = fmaf(s_q[e + 1], kv.y, dot);
+            dot = fmaf(s_q[e + 2], kv.z, dot);
+            dot = fmaf(s_q[e + 3], kv.w, dot);
+        }
+        float key = dot;                 // ranked by the unscaled dot without the prior
+        if (lambda) {
+            const int64_t c = cell_of[bh * M + slot];
+            const float delta = (float)(i - c * cell) - 0.5f * (float)cell;
+            key = fmaf(dot, inv_sqrt_d,
+                       lambda[h] * amax[bh * M + slot] * erff(delta / (2.f * sigma[h])));
+        }
+        s_key[j] = float_key(key);
+    }
+    __syncthreads();
+    if (!active) return;
+    const long orow = (bh * nq + row) * (long)topk;
+    const float scale = lambda ? 1.f : inv_sqrt_d;
+    row_topk_write(s_key, n_cand, topk, lane, idx_slot + orow, score ? score + orow : nullptr,
+                   scale, [&](int j) { return cand[j]; });
+    if (idx_cell)
+        row_topk_write(s_key, n_cand, topk, lane, idx_cell + orow, nullptr, scale,
+                       [&](int j) { return cell_of[bh * M + cand[j]]; });
+}
+
+hipError_t launch_stream_select(int B, int H, int d, bool bf16, const void* q, const int64_t* qs,
+                                const float* kbar, const float* amax, const int32_t* cell_of,
+                                int M, const float* lambda, const float* sigma, int nq,
+                                int64_t q_pos0, int window, int cell, const int32_t* keep,
+                                const int32_t* keep_count, int keep_w, int64_t n_row0,
+                                int rows_per_head, int topk, int32_t* idx_slot, int32_t* idx_cell,
+                                float* score, hipStream_t st)
+{
+    if (nq == 0) return hipSuccess;
+    int waves = kSelWaves;
+    while (waves > 1 && (size_t)waves * (d + keep_w) * sizeof(uint32_t) > 65536) waves >>= 1;
+    const size_t lds = (size_t)waves * (d + keep_w) * sizeof(uint32_t);
+    if (lds > 65536) return hipErrorInvalidValue;
+    const float inv_sqrt_d = 1.0f / sqrtf((float)d);
+    dim3 grid((unsigned)((nq + waves - 1) / waves), (unsigned)(B * H)), block(waves * kWave);
+#define FS_STREAM_SELECT(E, D)                                                                 \
+    hipLaunchKernelGGL((stream_select_kernel<E, D>), grid, block, lds, st,                     \
+                       (const typename E::storage*)q, qs[0], qs[1], qs[2], kbar, amax, cell_of, \
+                       M, lambda, sigma, H, nq, q_pos0, window, cell, keep, keep_count, keep_w, \
+                       n_row0, rows_per_head, topk, inv_sqrt_d, idx_slot, idx_cell, score)
+    if (bf16) {
+        if (d == 64) FS_STREAM_SELECT(Bf16, 64); else FS_STREAM_SELECT(Bf16, 128);
+    } else {
+        if (d == 64) FS_STREAM_SELECT(F32, 64); else FS_STREAM_SELECT(F32, 128);
+    }
+#undef FS_STREAM_SELECT
+    return hipGetLastError();
+}
 
 namespace {
 

@@ -19,8 +19,8 @@ CELL = 32
 
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
            "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
-           "fs_combine", "fs_rerank_topk",
-           "fs_status_string", "fs_last_error")
+           "fs_combine", "fs_rerank_topk", "fs_stream_state_size", "fs_stream_reset",
+           "fs_stream_step", "fs_status_string", "fs_last_error")
 
 
 class FsError(RuntimeError):
@@ -37,6 +37,13 @@ class FsProblem(C.Structure):
                 ("cell", C.c_int32), ("window", C.c_int32), ("dtype", C.c_int32),
                 ("reserved", C.c_int32), ("q_stride", C.c_int64 * 3),
                 ("kv_stride", C.c_int64 * 3), ("o_stride", C.c_int64 * 3)]
+
+
+class FsStreamConfig(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
+                ("cell", C.c_int32), ("window", C.c_int32), ("n_recent", C.c_int32),
+                ("budget", C.c_int32), ("topk", C.c_int32), ("max_new", C.c_int32),
+                ("dtype", C.c_int32)]
 
 
 _lib = None
@@ -63,6 +70,10 @@ def load(path: str | None = None):
         "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, C.c_size_t, vp, vp],
         "fs_combine": [P, vp, vp, vp, vp, vp],
+        "fs_stream_state_size": [C.POINTER(FsStreamConfig), C.POINTER(C.c_size_t)],
+        "fs_stream_reset": [C.POINTER(FsStreamConfig), vp, C.c_size_t, vp],
+        "fs_stream_step": [C.POINTER(FsStreamConfig), vp, C.c_size_t, C.c_int64, i32, vp, vp,
+                           vp, vp, vp, vp, f32, f32, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -251,3 +262,59 @@ class FsForward:
         return cls(wl.batch, wl.heads, wl.n_ctx, wl.head_dim, wl.n_q, wl.q_pos0, wl.dtype,
                    wl.topk, wl.budget, wl.n_recent, wl.window, wl.rope_base, wl.rms_eps, device,
                    lam, sig)
+
+
+# ---- streaming FS-L: a bounded per-head state --------------------------------------
+def fs_stream_state_size(cfg: FsStreamConfig) -> int:
+    n = C.c_size_t()
+    _check("fs_stream_state_size", load().fs_stream_state_size(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def fs_stream_reset(cfg: FsStreamConfig, state, stream=None):
+    _check("fs_stream_reset", load().fs_stream_reset(C.byref(cfg), _p(state),
+                                                      state.numel() * state.element_size(),
+                                                      _s(stream)))
+
+
+def fs_stream_step(cfg: FsStreamConfig, state, pos0: int, q, k, v, alpha, rope_base: float,
+                   rms_eps: float, o, idx=None, prior=None, stream=None):
+    """Append k, v ([B, H, n_new, d], contiguous) at positions pos0 .. and write the
+    FS-L output of the queries q at those positions into o; prior: None or
+    (lambda, sigma) float32 [H] device tensors; idx: optional selected cells."""
+    lam, sig = prior if prior is not None else (None, None)
+    _check("fs_stream_step", load().fs_stream_step(
+        C.byref(cfg), _p(state), state.numel() * state.element_size(), int(pos0),
+        int(q.shape[2]), _p(q), _p(k), _p(v), _p(alpha), _p(lam), _p(sig), float(rope_base),
+        float(rms_eps), _p(o), _p(idx), _s(stream)))
+
+
+class FsStream:
+    """A streaming FS-L layer state on one device: `step(q, k, v)` appends the
+    tokens and returns their outputs, reading only the fixed-size state."""
+
+    def __init__(self, batch, heads, head_dim, window, n_recent, budget, topk, max_new,
+                 dtype, alpha, rope_base=10000.0, rms_eps=1e-6, prior_lambda=None,
+                 prior_sigma=None, device="cuda"):
+        self.cfg = FsStreamConfig(batch, heads, head_dim, CELL, window, n_recent, budget, topk,
+                                  max_new, dtype)
+        self.bytes = fs_stream_state_size(self.cfg)
+        self.state = torch.empty(self.bytes, dtype=torch.uint8, device=device)
+        self.alpha = alpha
+        self.prior = None if prior_lambda is None else (prior_lambda, prior_sigma)
+        self.rope_base, self.rms_eps = rope_base, rms_eps
+        self.pos = 0
+        fs_stream_reset(self.cfg, self.state)
+
+    def reset(self):
+        fs_stream_reset(self.cfg, self.state)
+        self.pos = 0
+
+    def step(self, q, k, v, o=None, idx=None):
+        if o is None:
+            o = torch.empty_like(q)
+        fs_stream_step(self.cfg, self.state, self.pos, q, k, v, self.alpha, self.rope_base,
+                       self.rms_eps, o, idx, self.prior)
+        self.pos += q.shape[2]
+        return o
+

@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_six_calls():
     names = _declared()
     for n in ("fs_cell_summaries", "fs_prune_prefix", "fs_select_topk", "fs_window_attn",
-              "fs_sparse_attn", "fs_combine", "fs_rerank_topk"):
+              "fs_sparse_attn", "fs_combine", "fs_rerank_topk", "fs_stream_step"):
         assert n in names
     assert set(names) == set(fs.SYMBOLS)
 
@@ -141,3 +141,47 @@ def test_call_specific_limits(lib):
 def test_status_strings(lib):
     assert lib.fs_status_string(0) == b"FS_OK"
     assert lib.fs_status_string(3) == b"FS_ERR_HIP"
+
+
+def _scfg(**kw):
+    f = dict(batch=1, heads=8, head_dim=128, cell=32, window=512, n_recent=0, budget=512,
+             topk=32, max_new=256, dtype=fs.FS_BF16)
+    f.update(kw)
+    return fs.FsStreamConfig(*[f[n] for n, _ in fs.FsStreamConfig._fields_])
+
+
+def test_stream_state_is_bounded(lib):
+    """The streaming state is sized by the config alone (no sequence length enters the
+    call) and, at the 256k decode shape, is a small fraction of the K/V it replaces."""
+    n = fs.fs_stream_state_size(_scfg())
+    kv_256k = 2 * 8 * 262144 * 128 * 2
+    assert n < kv_256k / 8
+    # the token-state terms of the page's bound, (P + W) s + w + B + s rows of K and V
+    rows = (512 + 0 + 256 // 32 + 2) * 32 + 2 * 1024
+    assert n >= 8 * rows * 128 * 2 * 2
+    assert fs.fs_stream_state_size(_scfg(budget=1024)) > n > fs.fs_stream_state_size(_scfg(budget=64))
+
+
+@pytest.mark.parametrize("bad, status", [
+    (dict(head_dim=96), 2), (dict(cell=16), 2), (dict(n_recent=0, budget=0), 2),
+    (dict(n_recent=24, budget=1001), 2), (dict(topk=65), 2), (dict(max_new=0), 2),
+    (dict(max_new=4097), 2), (dict(dtype=7), 1), (dict(batch=0), 1), (dict(window=-1), 2)])
+def test_stream_config_rejected(lib, bad, status):
+    n = C.c_size_t()
+    assert lib.fs_stream_state_size(C.byref(_scfg(**bad)), C.byref(n)) == status
+
+
+def test_stream_step_arguments_rejected(lib):
+    cfg = _scfg(max_new=16)
+    need = fs.fs_stream_state_size(cfg)
+    step = lambda state, size, pos0, n_new, lam=None, sig=None, q=FAKE: lib.fs_stream_step(  # noqa: E731
+        C.byref(cfg), state, size, pos0, n_new, q, FAKE, FAKE, FAKE, lam, sig, 10000.0, 1e-6,
+        FAKE, None, None)
+    assert step(FAKE, need - 1, 0, 4) == 1                       # state too small
+    assert step(C.c_void_p((1 << 20) + 16), need, 0, 4) == 1     # not 256-byte aligned
+    assert step(None, need, 0, 4) == 1
+    assert step(FAKE, need, 0, 0) == 1 and step(FAKE, need, 0, 17) == 1
+    assert step(FAKE, need, -1, 4) == 2 and step(FAKE, need, (1 << 31) - 2, 4) == 2
+    assert step(FAKE, need, 0, 4, lam=FAKE) == 1                 # prior arrays go together
+    assert step(FAKE, need, 0, 4, q=C.c_void_p((1 << 20) + 2)) == 1
+    assert lib.fs_stream_reset(C.byref(cfg), FAKE, need - 1, None) == 1
