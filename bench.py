@@ -176,6 +176,62 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
                 total_gflop=total_flop / 1e9)
 
 
+def run_stream(torch, fs, decode_steps=200, lengths=(16384, 262144)):
+    """Streaming FS-L at the 256k decode shape (B1 H8 d128 bf16, w 512, P 512, K 32):
+    a chunked prefill in 256-token steps through the bounded state, then single-token
+    decode steps at each context length in `lengths`.  Inputs are N(0, 1) drawn on the
+    device with a fixed seed."""
+    wl = synth.WORKLOADS["decode_b1h8_n262144_q256_d128_bf16"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12)
+    B, H, d, chunk = wl.batch, wl.heads, wl.head_dim, 256
+    alpha = torch.rand(H, generator=gen, device=dev)
+    out = {"workload": wl.name, "budget": wl.budget, "topk": wl.topk, "window": wl.window,
+           "chunk": chunk}
+
+    def rnd(n):
+        return torch.randn((B, H, n, d), generator=gen, device=dev).to(torch.bfloat16)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for n_ctx in lengths:
+        st = fs.FsStream(B, H, d, wl.window, wl.n_recent, wl.budget, wl.topk, chunk,
+                         fs.FS_BF16, alpha, rope_base=wl.rope_base, rms_eps=wl.rms_eps,
+                         device=dev)
+        out["state_bytes"] = st.bytes
+        n_ch = n_ctx // chunk
+        # the whole context, chunk-major so that every step's tokens are contiguous
+        qa, ka, va = (torch.randn((n_ch, B, H, chunk, d), generator=gen, device=dev)
+                      .to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(qa[0])
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for j in range(n_ch):
+            st.step(qa[j], ka[j], va[j], o)
+        e1.record()
+        torch.cuda.synchronize()
+        if n_ctx == max(lengths):
+            ms = e0.elapsed_time(e1)
+            out["prefill_tokens_per_s"] = n_ctx * B / (ms * 1e-3)
+            out["prefill_ms_per_chunk"] = ms / (n_ctx // chunk)
+        q1, k1, v1 = rnd(1), rnd(1), rnd(1)
+        o1 = torch.empty_like(q1)
+        for _ in range(10):
+            st.step(q1, k1, v1, o1)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(decode_steps):
+            st.step(q1, k1, v1, o1)
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"decode_ms_per_token_n{n_ctx}"] = e0.elapsed_time(e1) / decode_steps
+        del st, qa, ka, va
+    out["decode_tokens_per_s"] = B / (out[f"decode_ms_per_token_n{max(lengths)}"] * 1e-3)
+    return out
+
+
 def roofline(res, ph=None):
     """Roofline entry for phase `ph`, by default the one that takes the most time."""
     if ph is None:
@@ -361,6 +417,10 @@ def main():
     if args.copy_mib and not args.phase:
         run_copy(args.copy_mib, args.reps, torch)
         return
+    if args.phase == "stream":
+        print(json.dumps(run_stream(torch, fs, decode_steps=args.reps, lengths=(262144,))),
+              flush=True)
+        return
     if args.phase:
         run_phase(args.workload, args.phase, args.reps, torch, fs)
         return
@@ -373,6 +433,7 @@ def main():
             also[name] = {"queries_per_s": r["qps"], "ms_per_step": r["ms_step"],
                           "tflops": r["tflops"], "gflop_per_step": r["total_gflop"],
                           "phase_ms": r["phase_ms"], "roofline": roofline(r)}
+    stream = None if args.only_primary else run_stream(torch, fs)
     wl = main_res["wl"]
     out = {
         "metric": METRIC,
@@ -396,6 +457,7 @@ def main():
         "roofline": roofline(main_res),
         "rerank": roofline(main_res, "rerank"),
         "also": also,
+        "stream": stream,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(PRIMARY)

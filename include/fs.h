@@ -119,13 +119,17 @@ fs_status fs_rerank_topk(const fs_problem* problem, const void* q, const void* k
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
                          int32_t topk, int32_t* idx, float* score, void* stream);
 
-/* Bytes of device workspace fs_window_attn needs (its RoPE cos/sin table). */
+/* Bytes of device workspace for fs_window_attn: its RoPE cos/sin table, then room
+ * for the partial states with which a short query range (decode) splits each
+ * query tile's keys over several workgroups. */
 fs_status fs_workspace_size(const fs_problem* problem, size_t* bytes);
 
 /* Local branch, eqs. 3-4: o_sr_i = softmax_j((R(i)q_i).(R(j)k_j)/sqrt(d)) v_j over
  * j = max(0, i-w) .. i, with RoPE base `rope_base`.  The kernel uses relative
  * angles, which eq. 3's right-hand side makes exact, so positions up to 2^31
- * lose no accuracy.  workspace: at least fs_workspace_size bytes, overwritten. */
+ * lose no accuracy.  workspace (overwritten): at least the table; with
+ * fs_workspace_size bytes a short query range splits its keys over workgroups.
+ * Calls sharing a workspace must not overlap in time. */
 fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
                          float rope_base, void* workspace, size_t ws_bytes, void* o_sr,
                          void* stream);
@@ -167,12 +171,15 @@ typedef struct {
     int32_t topk;                     /* K of eq. 9's selection, 1 .. 64 */
     int32_t max_new;                  /* most tokens one step appends, 1 .. 4096 */
     fs_dtype dtype;                   /* storage dtype of q/k/v/o and of the state */
+    float rope_base;                  /* RoPE base of eq. 3 (> 1) */
+    float rms_eps;                    /* RMSNorm epsilon of eq. 9 (>= 0) */
 } fs_stream_config;
 
 /* Bytes of the state buffer for a config. */
 fs_status fs_stream_state_size(const fs_stream_config* cfg, size_t* bytes);
 
-/* Empty the state (no tokens).  state: device, 256-byte aligned, >= the size above. */
+/* Empty the state (no tokens) and tabulate the window's rotations.  state: device,
+ * 256-byte aligned, >= the size above. */
 fs_status fs_stream_reset(const fs_stream_config* cfg, void* state, size_t state_bytes,
                           void* stream);
 
@@ -189,8 +196,7 @@ fs_status fs_stream_reset(const fs_stream_config* cfg, void* state, size_t state
 fs_status fs_stream_step(const fs_stream_config* cfg, void* state, size_t state_bytes,
                          int64_t pos0, int32_t n_new, const void* q, const void* k,
                          const void* v, const float* alpha, const float* prior_lambda,
-                         const float* prior_sigma, float rope_base, float rms_eps, void* o,
-                         int32_t* idx, void* stream);
+                         const float* prior_sigma, void* o, int32_t* idx, void* stream);
 
 const char* fs_status_string(fs_status status);
 const char* fs_last_error(void);

@@ -225,7 +225,7 @@ fs_status fs_workspace_size(const fs_problem* problem, size_t* bytes)
     fs::Shape sh;
     FS_CHECK(check_problem(problem, &sh));
     if (!bytes) return fail(FS_ERR_INVALID, "bytes is NULL");
-    *bytes = fs::rope_table_bytes(sh);
+    *bytes = fs::window_workspace_bytes(sh);
     g_err[0] = 0;
     return FS_OK;
 }
@@ -242,7 +242,7 @@ fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k
         return fail(FS_ERR_INVALID, "workspace of %zu bytes, need %zu", ws_bytes,
                     fs::rope_table_bytes(sh));
     return from_hip(fs::launch_window(sh, q, k, v, (double)rope_base, workspace, o_sr,
-                                      (hipStream_t)stream),
+                                      (hipStream_t)stream, false, ws_bytes),
                     "fs_window_attn");
 }
 
@@ -297,6 +297,10 @@ fs_status check_stream(const fs_stream_config* c, fs::StreamCfg* sc)
     if (c->max_new < 1 || c->max_new > 4096)
         return fail(FS_ERR_UNSUPPORTED, "max_new %d outside [1, 4096]", c->max_new);
     if (c->dtype != FS_F32 && c->dtype != FS_BF16) return fail(FS_ERR_INVALID, "dtype %d", c->dtype);
+    if (!(c->rope_base > 1.0f)) return fail(FS_ERR_INVALID, "rope_base must be > 1");
+    if (!(c->rms_eps >= 0.0f)) return fail(FS_ERR_INVALID, "rms_eps must be >= 0");
+    sc->rope_base = (double)c->rope_base;
+    sc->rms_eps = c->rms_eps;
     sc->B = c->batch; sc->H = c->heads; sc->d = c->head_dim; sc->s = c->cell; sc->w = c->window;
     sc->W = c->n_recent; sc->P = c->budget; sc->K = c->topk; sc->max_new = c->max_new;
     sc->bf16 = c->dtype == FS_BF16;
@@ -340,8 +344,7 @@ fs_status fs_stream_reset(const fs_stream_config* cfg, void* state, size_t state
 fs_status fs_stream_step(const fs_stream_config* cfg, void* state, size_t state_bytes,
                          int64_t pos0, int32_t n_new, const void* q, const void* k,
                          const void* v, const float* alpha, const float* prior_lambda,
-                         const float* prior_sigma, float rope_base, float rms_eps, void* o,
-                         int32_t* idx, void* stream)
+                         const float* prior_sigma, void* o, int32_t* idx, void* stream)
 {
     fs::StreamCfg sc;
     FS_CHECK(check_stream(cfg, &sc));
@@ -356,11 +359,9 @@ fs_status fs_stream_step(const fs_stream_config* cfg, void* state, size_t state_
     if (!alpha) return fail(FS_ERR_INVALID, "alpha is NULL");
     if ((prior_lambda == nullptr) != (prior_sigma == nullptr))
         return fail(FS_ERR_INVALID, "prior_lambda and prior_sigma go together");
-    if (!(rope_base > 1.0f)) return fail(FS_ERR_INVALID, "rope_base must be > 1");
-    if (!(rms_eps >= 0.0f)) return fail(FS_ERR_INVALID, "rms_eps must be >= 0");
     return from_hip(fs::launch_stream_step(sc, Ly, state, pos0, n_new, q, k, v, alpha,
-                                           prior_lambda, prior_sigma, (double)rope_base,
-                                           rms_eps, o, idx, (hipStream_t)stream),
+                                           prior_lambda, prior_sigma, o, idx,
+                                           (hipStream_t)stream),
                     "fs_stream_step");
 }
 

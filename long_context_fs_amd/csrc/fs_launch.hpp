@@ -49,8 +49,20 @@ hipError_t launch_stream_select(int B, int H, int d, bool bf16, const void* q, c
                                 int rows_per_head, int topk, int32_t* idx_slot, int32_t* idx_cell,
                                 float* score, hipStream_t st);
 size_t rope_table_bytes(const Shape& sh);
+// Window workspace: the rotation table (rope_table_bytes, filled first unless
+// table_ready), then, when ws_bytes >= window_workspace_bytes, the partial states
+// of a key range split over window_splits workgroups (short query ranges).
+int window_splits(const Shape& sh);
+size_t window_ws_bytes(const Shape& sh);
+size_t window_workspace_bytes(const Shape& sh);
 hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
-                         double rope_base, void* table, void* o_sr, hipStream_t st);
+                         double rope_base, void* table, void* o_sr, hipStream_t st,
+                         bool table_ready, size_t ws_bytes);
+// Merge of split attention states (bf16 output with the shape's o strides), with
+// the readout's RMSNorm when rms.
+hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const float2* ws_ml,
+                              bool rms, float rms_eps, void* o, hipStream_t st);
+hipError_t launch_rope_table(const Shape& sh, double rope_base, void* table, hipStream_t st);
 // Workgroups over which the readout splits each query's cells (1: unsplit), and
 // the workspace bytes of their partial softmax states.
 int sparse_splits(const Shape& sh);
@@ -70,7 +82,6 @@ hipError_t launch_stream_reset(const StreamCfg& c, const StreamLayout& Ly, void*
 hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* state,
                               int64_t pos0, int n_new, const void* q, const void* k,
                               const void* v, const float* alpha, const float* lambda,
-                              const float* sigma, double rope_base, float rms_eps, void* o,
-                              int32_t* idx_cell, hipStream_t st);
+                              const float* sigma, void* o, int32_t* idx_cell, hipStream_t st);
 
 }  // namespace fs

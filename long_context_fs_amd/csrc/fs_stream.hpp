@@ -24,6 +24,8 @@ namespace fs {
 struct StreamCfg {
     int B, H, d, s, w, W, P, K, max_new;
     int bf16;
+    double rope_base;
+    float rms_eps;
 };
 
 struct StreamLayout {
@@ -35,7 +37,7 @@ struct StreamLayout {
     // byte offsets of [B*H][...] arrays, then of the step scratch
     size_t hdr, ring_k, ring_v, pool_k, pool_v, kbar, amax, cell, topp_a, topp_c, topp_s, recent,
         free_list, pend, keep, keep_cnt;
-    size_t idx, osr, olr, table, ws, ws_bytes, bytes;
+    size_t idx, osr, olr, table, table_bytes, ws, ws_bytes, bytes;
 };
 
 // Header words per (batch, head).

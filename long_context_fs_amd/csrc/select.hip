@@ -36,11 +36,14 @@ __device__ __forceinline__ float key_to_float(uint32_t k)
 }
 
 // Exact top-K of one query (one wavefront) over the order-preserving keys
-// s_key[0..n_cand) in LDS: the K-th largest key by a 32-step bitwise search with
-// wave counts; of the keys equal to it, the last ones in list order are kept (the
-// lists are ascending in cell index, so ties go to the larger cell).  The chosen
-// entries are written in list order: out_i[pos] = id_of(j), out_s[pos] = the
-// key's value times out_scale; positions from min(K, n_cand) on get -1 / 0.
+// s_key[0..n_cand) in LDS.  The K-th largest key thr is found by a bitwise
+// search whose counts are ballots (wave-uniform, no lane shuffles); bits that all
+// keys share are fixed from the start, and the search stops as soon as exactly K
+// keys reach the candidate (that set is then the top K).  Of the keys equal to
+// thr, the last ones in list order are kept (the lists are ascending in cell
+// index, so ties go to the larger cell).  The chosen entries are written in list
+// order: out_i[pos] = id_of(j), out_s[pos] = the key's value times out_scale;
+// positions from min(K, n_cand) on get -1 / 0.
 template <class IdOf>
 __device__ __forceinline__ void row_topk_write(const uint32_t* s_key, int n_cand, int topk,
                                                int lane, int32_t* __restrict__ out_i,
@@ -48,22 +51,64 @@ __device__ __forceinline__ void row_topk_write(const uint32_t* s_key, int n_cand
                                                IdOf id_of)
 {
     const int kq = n_cand < topk ? n_cand : topk;
+    // up to 1024 keys are held in registers (0 pads: every finite score's key is
+    // >= 2^23, and every candidate threshold is >= 1), beyond that they are read
+    // from LDS at each step
+    constexpr int kRegKeys = 16;
+    const bool in_regs = n_cand <= kRegKeys * kWave;
+    uint32_t kr[kRegKeys];
+#pragma unroll
+    for (int r = 0; r < kRegKeys; ++r) {
+        const int j = lane + r * kWave;
+        kr[r] = in_regs && j < n_cand ? s_key[j] : 0u;
+    }
+    auto count_ge = [&](uint32_t t) {        // #{j : s_key[j] >= t}, wave-uniform
+        int c = 0;
+        if (in_regs) {
+#pragma unroll
+            for (int r = 0; r < kRegKeys; ++r) c += __popcll(__ballot(kr[r] >= t));
+        } else {
+            for (int j0 = 0; j0 < n_cand; j0 += kWave) {
+                const int j = j0 + lane;
+                c += __popcll(__ballot(j < n_cand && s_key[j] >= t));
+            }
+        }
+        return c;
+    };
     uint32_t thr = 0;
     if (kq > 0) {
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t t = thr | (1u << bit);
-            int cnt = 0;
-            for (int j = lane; j < n_cand; j += kWave) cnt += s_key[j] >= t;
-            if (wave_sum_int(cnt) >= kq) thr = t;
+        uint32_t k_and = 0xFFFFFFFFu, k_or = 0u;
+        for (int j = lane; j < n_cand; j += kWave) {
+            k_and &= s_key[j];
+            k_or |= s_key[j];
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            k_and &= (uint32_t)__shfl_xor((int)k_and, m, kWave);
+            k_or |= (uint32_t)__shfl_xor((int)k_or, m, kWave);
+        }
+        const uint32_t diff = k_and ^ k_or;
+        if (diff == 0u) {
+            thr = k_or;                      // every key equal
+        } else {
+            const int hb = 31 - __clz(diff);
+            thr = k_or & ~(hb >= 31 ? 0xFFFFFFFFu : (2u << hb) - 1u);
+            for (int bit = hb; bit >= 0; --bit) {
+                const uint32_t t = thr | (1u << bit);
+                const int c = count_ge(t);
+                if (c >= kq) {
+                    thr = t;
+                    if (c == kq) break;      // exactly the top kq reach t
+                }
+            }
         }
     }
     int n_gt = 0, n_eq = 0;
-    for (int j = lane; j < n_cand; j += kWave) {
-        n_gt += s_key[j] > thr;
-        n_eq += s_key[j] == thr;
+    for (int j0 = 0; j0 < n_cand; j0 += kWave) {
+        const int j = j0 + lane;
+        n_gt += __popcll(__ballot(j < n_cand && s_key[j] > thr));
+        n_eq += __popcll(__ballot(j < n_cand && s_key[j] == thr));
     }
-    n_gt = wave_sum_int(n_gt);
-    n_eq = wave_sum_int(n_eq);
     const int need_eq = kq - n_gt;
 
     int written = 0, eq_seen = 0;
@@ -191,11 +236,15 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
 
 // Selection over a streaming state's cell pool (eq. 7 on the cells FS-L still
 // holds).  The keep row of a query lists pool slots in ascending cell order;
-// kbar, a_c and the cell index are stored per slot.  One wavefront per query,
-// scoring and ranking as the row-wise kernel above.  idx_slot receives slots
-// (what the readout gathers), idx_cell (optional) the same choice as cell indices.
-template <class E, int D>
-__global__ __launch_bounds__(kSelWaves * kWave) void stream_select_kernel(
+// kbar, a_c and the cell index are stored per slot.  QPB queries per workgroup
+// (1 for a decode step, 4 otherwise): the query's threads take one candidate per
+// group of D / 8 lanes (8 dims a lane, q in registers), so a candidate's kbar row
+// is one coalesced read and many rows are in flight; the dot is finished by a
+// butterfly over the group.  One wavefront per query then ranks the keys as the
+// row-wise kernel does.  idx_slot receives slots (what the readout gathers),
+// idx_cell (optional) the same choice as cell indices.
+template <class E, int D, int QPB>
+__global__ __launch_bounds__(256) void stream_select_kernel(
     const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const float* __restrict__ kbar, const float* __restrict__ amax,
     const int32_t* __restrict__ cell_of, int M, const float* __restrict__ lambda,
@@ -204,57 +253,83 @@ __global__ __launch_bounds__(kSelWaves * kWave) void stream_select_kernel(
     int64_t n_row0, int rows_per_head, int topk, float inv_sqrt_d, int32_t* __restrict__ idx_slot,
     int32_t* __restrict__ idx_cell, float* __restrict__ score)
 {
+    constexpr int TPQ = 256 / QPB;          // threads per query
+    constexpr int LPC = D / 8;              // lanes per candidate
+    constexpr int CPI = TPQ / LPC;          // candidates per iteration
+    constexpr int UNR = QPB == 1 ? 16 : 4;  // candidate rows in flight per lane group
     extern __shared__ uint32_t smem[];
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int waves = blockDim.x >> 6;
-    float* s_q = reinterpret_cast<float*>(smem) + wv * D;
-    uint32_t* s_key = smem + waves * D + wv * keep_w;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int qi = tid / TPQ, tq = tid % TPQ;
+    const int grp = tq / LPC, gl = tq % LPC;
+    uint32_t* s_key = smem + qi * keep_w;
+    int32_t* s_cand = reinterpret_cast<int32_t*>(smem + QPB * keep_w) + qi * keep_w;
 
-    const long row = (long)blockIdx.x * waves + wv;
+    const long row = (long)blockIdx.x * QPB + qi;
     const long bh = blockIdx.y;
-    const bool active = row < nq;       // inactive waves still reach the barrier
+    const bool active = row < nq;           // inactive queries still reach the barrier
     const int h = (int)(bh % H), b = (int)(bh / H);
     const int64_t i = q_pos0 + (active ? row : 0);
     const int64_t n = i < window ? 0 : (i - window) / cell;
     const long kr = bh * rows_per_head + (long)(n - n_row0);
     const int32_t* cand = keep + kr * keep_w;
     const int n_cand = active ? keep_count[kr] : 0;
-    if (active) {
-        const typename E::storage* qrow = q + b * qs0 + h * qs1 + row * qs2;
-        for (int e = lane; e < D; e += kWave) s_q[e] = load1<E>(qrow + e);
+    for (int j = tq; j < n_cand; j += TPQ) s_cand[j] = cand[j];   // the keep row, once
+    float qv[8];
+    {
+        const typename E::storage* qrow = q + b * qs0 + h * qs1 + (active ? row : 0) * qs2 + gl * 8;
+        if constexpr (E::kPer16B == 8) {
+            load16<E>(qrow, qv);
+        } else {
+            load16<E>(qrow, qv);
+            load16<E>(qrow + 4, qv + 4);
+        }
+    }
+    const float* kb_head = kbar + bh * (long)M * D + gl * 8;
+    __syncthreads();
+    for (int j0 = 0; j0 < n_cand; j0 += CPI * UNR) {
+        float dot[UNR];
+        int slot[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {     // UNR candidates' rows in flight
+            const int j = j0 + u * CPI + grp;
+            slot[u] = j < n_cand ? s_cand[j] : 0;
+            const float4 x0 = *reinterpret_cast<const float4*>(kb_head + (long)slot[u] * D);
+            const float4 x1 = *reinterpret_cast<const float4*>(kb_head + (long)slot[u] * D + 4);
+            float d0 = qv[0] * x0.x;
+            d0 = fmaf(qv[1], x0.y, d0);
+            d0 = fmaf(qv[2], x0.z, d0);
+            d0 = fmaf(qv[3], x0.w, d0);
+            d0 = fmaf(qv[4], x1.x, d0);
+            d0 = fmaf(qv[5], x1.y, d0);
+            d0 = fmaf(qv[6], x1.z, d0);
+            dot[u] = fmaf(qv[7], x1.w, d0);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+#pragma unroll
+            for (int m = 1; m < LPC; m <<= 1) dot[u] += __shfl_xor(dot[u], m, kWave);
+            const int j = j0 + u * CPI + grp;
+            if (gl == 0 && j < n_cand) {
+                float key = dot[u];          // ranked by the unscaled dot without the prior
+                if (lambda) {
+                    const int64_t c = cell_of[bh * M + slot[u]];
+                    const float delta = (float)(i - c * cell) - 0.5f * (float)cell;
+                    key = fmaf(dot[u], inv_sqrt_d,
+                               lambda[h] * amax[bh * M + slot[u]] * erff(delta / (2.f * sigma[h])));
+                }
+                s_key[j] = float_key(key);
+            }
+        }
     }
     __syncthreads();
-    const float* kb_head = kbar + bh * (long)M * D;
-    for (int j = lane; j < n_cand; j += kWave) {
-        const int slot = cand[j];
-        const float* kb = kb_head + (long)slot * D;
-        float dot = 0.f;
-#pragma unroll 8
-        for (int e = 0; e < D; e += 4) {
-            const float4 kv = *reinterpret_cast<const float4*>(kb + e);
-            dot = fmaf(s_q[e], kv.x, dot);
-            dot = fmaf(s_q[e + 1], kv.y, dot);
-            dot = fmaf(s_q[e + 2], kv.z, dot);
-            dot = fmaf(s_q[e + 3], kv.w, dot);
-        }
-        float key = dot;                 // ranked by the unscaled dot without the prior
-        if (lambda) {
-            const int64_t c = cell_of[bh * M + slot];
-            const float delta = (float)(i - c * cell) - 0.5f * (float)cell;
-            key = fmaf(dot, inv_sqrt_d,
-                       lambda[h] * amax[bh * M + slot] * erff(delta / (2.f * sigma[h])));
-        }
-        s_key[j] = float_key(key);
-    }
-    __syncthreads();
-    if (!active) return;
+    if (!active || tq >= kWave) return;     // the query's first wavefront ranks
     const long orow = (bh * nq + row) * (long)topk;
     const float scale = lambda ? 1.f : inv_sqrt_d;
     row_topk_write(s_key, n_cand, topk, lane, idx_slot + orow, score ? score + orow : nullptr,
-                   scale, [&](int j) { return cand[j]; });
+                   scale, [&](int j) { return s_cand[j]; });
     if (idx_cell)
         row_topk_write(s_key, n_cand, topk, lane, idx_cell + orow, nullptr, scale,
-                       [&](int j) { return cell_of[bh * M + cand[j]]; });
+                       [&](int j) { return cell_of[bh * M + s_cand[j]]; });
 }
 
 hipError_t launch_stream_select(int B, int H, int d, bool bf16, const void* q, const int64_t* qs,
@@ -266,22 +341,25 @@ hipError_t launch_stream_select(int B, int H, int d, bool bf16, const void* q, c
                                 float* score, hipStream_t st)
 {
     if (nq == 0) return hipSuccess;
-    int waves = kSelWaves;
-    while (waves > 1 && (size_t)waves * (d + keep_w) * sizeof(uint32_t) > 65536) waves >>= 1;
-    const size_t lds = (size_t)waves * (d + keep_w) * sizeof(uint32_t);
+    // few queries (a decode step): the whole workgroup on one query
+    const int qpb = nq * B * H < 1024 ? 1 : 4;
+    const size_t lds = (size_t)2 * qpb * keep_w * sizeof(uint32_t);   // keys and the keep row
     if (lds > 65536) return hipErrorInvalidValue;
     const float inv_sqrt_d = 1.0f / sqrtf((float)d);
-    dim3 grid((unsigned)((nq + waves - 1) / waves), (unsigned)(B * H)), block(waves * kWave);
-#define FS_STREAM_SELECT(E, D)                                                                 \
-    hipLaunchKernelGGL((stream_select_kernel<E, D>), grid, block, lds, st,                     \
+    dim3 grid((unsigned)((nq + qpb - 1) / qpb), (unsigned)(B * H)), block(256);
+#define FS_STREAM_SELECT(E, D, QPB)                                                            \
+    hipLaunchKernelGGL((stream_select_kernel<E, D, QPB>), grid, block, lds, st,                \
                        (const typename E::storage*)q, qs[0], qs[1], qs[2], kbar, amax, cell_of, \
                        M, lambda, sigma, H, nq, q_pos0, window, cell, keep, keep_count, keep_w, \
                        n_row0, rows_per_head, topk, inv_sqrt_d, idx_slot, idx_cell, score)
+#define FS_STREAM_SELECT_Q(E, D) \
+    if (qpb == 1) { FS_STREAM_SELECT(E, D, 1); } else { FS_STREAM_SELECT(E, D, 4); }
     if (bf16) {
-        if (d == 64) FS_STREAM_SELECT(Bf16, 64); else FS_STREAM_SELECT(Bf16, 128);
+        if (d == 64) { FS_STREAM_SELECT_Q(Bf16, 64) } else { FS_STREAM_SELECT_Q(Bf16, 128) }
     } else {
-        if (d == 64) FS_STREAM_SELECT(F32, 64); else FS_STREAM_SELECT(F32, 128);
+        if (d == 64) { FS_STREAM_SELECT_Q(F32, 64) } else { FS_STREAM_SELECT_Q(F32, 128) }
     }
+#undef FS_STREAM_SELECT_Q
 #undef FS_STREAM_SELECT
     return hipGetLastError();
 }

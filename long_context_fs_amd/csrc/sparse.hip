@@ -507,12 +507,13 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     }
 }
 
-// Merge of the split readout: per query, the partial states (m_s, l_s, O_s)
-// (reference maxima in the log2 domain) combine as O = sum_s 2^(m_s - M) O_s over
-// l = sum_s 2^(m_s - M) l_s with M = max_s m_s; then RMSNorm.  One wavefront per
-// query, D / 64 dims per lane.
-template <int D>
-__global__ __launch_bounds__(256) void sparse_merge_kernel(const float* __restrict__ ws_acc,
+// Merge of a split attention (the readout, or the window branch): per query, the
+// partial states (m_s, l_s, O_s) (reference maxima in the log2 domain) combine as
+// O = sum_s 2^(m_s - M) O_s over l = sum_s 2^(m_s - M) l_s with M = max_s m_s;
+// then RMSNorm when RMS (the readout, eq. 9).  One wavefront per query, D / 64
+// dims per lane.
+template <int D, bool RMS>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ ws_acc,
                                                            const float2* __restrict__ ws_ml,
                                                            int H, int nq, long n_rows_all,
                                                            int n_split, float rms_eps,
@@ -523,19 +524,19 @@ __global__ __launch_bounds__(256) void sparse_merge_kernel(const float* __restri
     const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);    // = bh * nq + t
     if (row >= n_rows_all) return;
     const int lane = threadIdx.x & 63;
-    const float2* ml = ws_ml + row * n_split;
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ml[sp].x);
+    // lane sp holds split sp's (m, l) (n_split <= 32): one max and one sum over the wave
+    const float2 e = lane < n_split ? ws_ml[row * n_split + lane] : make_float2(-INFINITY, 0.f);
+    const float M = wave_max(e.x);
+    const float w = (M != -INFINITY && lane < n_split) ? __builtin_amdgcn_exp2f(e.x - M) : 0.f;
+    const float l = wave_sum(w * e.y);                    // an empty split has weight 0
     float acc[R] = {};
-    float l = 0.f;
     if (M != -INFINITY) {
-        for (int sp = 0; sp < n_split; ++sp) {
-            const float2 e = ml[sp];
-            const float w = __builtin_amdgcn_exp2f(e.x - M);    // 0 for an empty split
-            l = fmaf(w, e.y, l);
-            const float* a = ws_acc + (row * n_split + sp) * D;
+        const float* a = ws_acc + row * n_split * (long)D + lane;
+#pragma unroll 8
+        for (int sp = 0; sp < n_split; ++sp) {            // loads independent of the weights
+            const float ws = __shfl(w, sp, kWave);
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(w, a[lane + r * kWave], acc[r]);
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(ws, a[sp * D + r * kWave], acc[r]);
         }
     }
     const float inv_l = l > 0.f ? 1.f / l : 0.f;
@@ -545,13 +546,31 @@ __global__ __launch_bounds__(256) void sparse_merge_kernel(const float* __restri
         acc[r] *= inv_l;
         ss = fmaf(acc[r], acc[r], ss);
     }
-    ss = wave_sum(ss);
-    const float inv_rms = 1.f / sqrtf(ss / (float)D + rms_eps);
+    float inv_rms = 1.f;
+    if constexpr (RMS) inv_rms = 1.f / sqrtf(wave_sum(ss) / (float)D + rms_eps);
     const long bh = row / nq, t = row - bh * nq;
     const int h = (int)(bh % H), b = (int)(bh / H);
     uint16_t* orow = o + b * os0 + h * os1 + t * os2;
 #pragma unroll
     for (int r = 0; r < R; ++r) store1<Bf16>(orow + lane + r * kWave, acc[r] * inv_rms);
+}
+
+hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const float2* ws_ml,
+                              bool rms, float rms_eps, void* o, hipStream_t st)
+{
+    const long rows_all = (long)sh.B * sh.H * sh.nq;
+    dim3 mgrid((unsigned)((rows_all + 3) / 4));
+#define FS_MERGE(D, RMS)                                                                          \
+    hipLaunchKernelGGL((split_merge_kernel<D, RMS>), mgrid, dim3(256), 0, st, ws_acc, ws_ml,      \
+                       sh.H, sh.nq, rows_all, S, rms_eps, (uint16_t*)o, sh.os[0], sh.os[1],      \
+                       sh.os[2])
+    if (sh.d == 64) {
+        if (rms) FS_MERGE(64, true); else FS_MERGE(64, false);
+    } else {
+        if (rms) FS_MERGE(128, true); else FS_MERGE(128, false);
+    }
+#undef FS_MERGE
+    return hipGetLastError();
 }
 
 // Split count: enough workgroups to give every CU two, at most 32 per query tile.
@@ -598,14 +617,7 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
 #undef FS_SPARSE_MFMA
         hipError_t err = hipGetLastError();
         if (err != hipSuccess || S <= 1) return err;
-        dim3 mgrid((unsigned)((rows_all + 3) / 4));
-#define FS_SPARSE_MERGE(D)                                                                        \
-        hipLaunchKernelGGL((sparse_merge_kernel<D>), mgrid, dim3(256), 0, st, ws_acc, ws_ml,      \
-                           sh.H, sh.nq, rows_all, S, rms_eps, (uint16_t*)o_lr, sh.os[0],          \
-                           sh.os[1], sh.os[2])
-        if (sh.d == 64) FS_SPARSE_MERGE(64); else FS_SPARSE_MERGE(128);
-#undef FS_SPARSE_MERGE
-        return hipGetLastError();
+        return launch_split_merge(sh, S, ws_acc, ws_ml, true, rms_eps, o_lr, st);
     }
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
 #define FS_SPARSE(E, D)                                                                          \

@@ -78,13 +78,15 @@ StreamLayout stream_layout(const StreamCfg& c)
     Shape sh{};
     sh.B = c.B; sh.H = c.H; sh.d = c.d; sh.s = c.s; sh.w = c.w; sh.bf16 = c.bf16;
     sh.C = Ly.M; sh.N = Ly.M * c.s;
-    Ly.table = take(rope_table_bytes(sh));
-    size_t ws = 0;                       // the readout's split workspace, largest over n_new
+    size_t ws = 0, wws = 0;              // split workspaces, largest over n_new
     for (int nq = 1; nq <= c.max_new; ++nq) {
         sh.nq = nq;
-        const size_t b = sparse_ws_bytes(sh);
+        const size_t b = sparse_ws_bytes(sh), bw = window_workspace_bytes(sh);
         ws = b > ws ? b : ws;
+        wws = bw > wws ? bw : wws;
     }
+    Ly.table = take(wws);                // the window's table, then its split states
+    Ly.table_bytes = wws;
     Ly.ws_bytes = ws;
     Ly.ws = take(ws);
     Ly.bytes = off;
@@ -380,14 +382,17 @@ hipError_t launch_stream_reset(const StreamCfg& c, const StreamLayout& Ly, void*
 {
     const StreamDev sd = stream_dev(c, Ly, state);
     hipLaunchKernelGGL(stream_reset_kernel, dim3((unsigned)(c.B * c.H)), dim3(256), 0, st, sd);
-    return hipGetLastError();
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    Shape sh{};
+    sh.d = c.d; sh.w = c.w;
+    return launch_rope_table(sh, c.rope_base, static_cast<char*>(state) + Ly.table, st);
 }
 
 hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* state,
                               int64_t pos0, int n_new, const void* q, const void* k,
                               const void* v, const float* alpha, const float* lambda,
-                              const float* sigma, double rope_base, float rms_eps, void* o,
-                              int32_t* idx_cell, hipStream_t st)
+                              const float* sigma, void* o, int32_t* idx_cell, hipStream_t st)
 {
     if (n_new == 0) return hipSuccess;
     const StreamDev sd = stream_dev(c, Ly, state);
@@ -437,7 +442,8 @@ hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* 
     sh.kvs[2] = c.d;
     const char* kwin = sd.ring_k + shift * c.d * Ly.esize;
     const char* vwin = sd.ring_v + shift * c.d * Ly.esize;
-    err = launch_window(sh, q, kwin, vwin, rope_base, base + Ly.table, base + Ly.osr, st);
+    err = launch_window(sh, q, kwin, vwin, c.rope_base, base + Ly.table, base + Ly.osr, st,
+                        true, Ly.table_bytes);               // tabulated at the reset
     if (err != hipSuccess) return err;
     // 4. readout over the pool: slot u's tokens are rows u s .. u s + s - 1
     sh.q_pos0 = 0;
@@ -446,7 +452,7 @@ hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* 
     sh.kvs[0] = (int64_t)c.H * Ly.M * c.s * c.d;
     sh.kvs[1] = (int64_t)Ly.M * c.s * c.d;
     sh.kvs[2] = c.d;
-    err = launch_sparse(sh, q, sd.pool_k, sd.pool_v, idx_slot, c.K, rms_eps,
+    err = launch_sparse(sh, q, sd.pool_k, sd.pool_v, idx_slot, c.K, c.rms_eps,
                         Ly.ws_bytes ? base + Ly.ws : nullptr, base + Ly.olr, st);
     if (err != hipSuccess) return err;
     // 5. eq. 2

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t kvs0, int64_t kvs1,
     int64_t kvs2, int H, int BH, int nq, int q_pos0, int w, const float2* __restrict__ table,
-    float scale_log2, uint16_t* __restrict__ o, int64_t os0, int64_t os1, int64_t os2)
+    float scale_log2, uint16_t* __restrict__ o, int64_t os0, int64_t os1, int64_t os2,
+    int n_split, float* __restrict__ ws_acc, float2* __restrict__ ws_ml)
 {
     using namespace mf;
     constexpr int KS = D / 32;     // k-steps of the QK^T contraction
@@ -222,11 +223,16 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     const TileOfBlock tb = xcd_tile(BH);
     const long bh = tb.bh;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const long i0 = (long)q_pos0 + tb.tile * kWinQ;
+    // split `split` of n_split takes a contiguous share of the query tile's key tiles
+    const int split = (int)(tb.tile % n_split);
+    const long i0 = (long)q_pos0 + (tb.tile / n_split) * kWinQ;
     const long i_end = (long)q_pos0 + nq - 1;                 // last query position
-    const long kv_lo = i0 - w > 0 ? i0 - w : 0;
+    const long kv_first = i0 - w > 0 ? i0 - w : 0;
     const long kv_hi = i0 + kWinQ - 1 < i_end ? i0 + kWinQ - 1 : i_end;
-    const int n_tiles = (int)((kv_hi - kv_lo) / kTileK) + 1;
+    const int n_all = (int)((kv_hi - kv_first) / kTileK) + 1;
+    const int t_begin = (int)((long)n_all * split / n_split);
+    const int n_tiles = (int)((long)n_all * (split + 1) / n_split) - t_begin;
+    const long kv_lo = kv_first + (long)t_begin * kTileK;     // first key of this split
 
     const uint16_t* kh = k + b * kvs0 + h * kvs1;
     const uint16_t* vh = v + b * kvs0 + h * kvs1;
@@ -266,8 +272,10 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     float m_run[2] = {-INFINITY, -INFINITY};
 
     WinStage<D> stage;
-    win_load<D>(stage, kh, vh, kvs2, kv_lo, kv_hi, i0, w, table);
-    win_store<D>(stage, ks, vt, kv_lo, kv_hi, i0, w, table);
+    if (n_tiles > 0) {                                        // block-uniform
+        win_load<D>(stage, kh, vh, kvs2, kv_lo, kv_hi, i0, w, table);
+        win_store<D>(stage, ks, vt, kv_lo, kv_hi, i0, w, table);
+    }
     __syncthreads();
 
     for (int tile = 0; tile < n_tiles; ++tile) {
@@ -295,6 +303,21 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
         }
     }
 
+    if (n_split > 1) {                  // partial state (m, l, unnormalised O) of this split
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+            const long i = qw0 + 16 * qg + n;
+            if (i > i_end) continue;
+            const long slot = (bh * nq + (i - q_pos0)) * n_split + split;
+            if (g == 0) ws_ml[slot] = make_float2(m_run[qg], accl[qg][0]);
+            float* dst = ws_acc + slot * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) =
+                    make_float4(acc[db][qg][0], acc[db][qg][1], acc[db][qg][2], acc[db][qg][3]);
+        }
+        return;
+    }
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const long i = qw0 + 16 * qg + n;
@@ -312,30 +335,72 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     }
 }
 
-hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
-                         double rope_base, void* table, void* o_sr, hipStream_t st)
+hipError_t launch_rope_table(const Shape& sh, double rope_base, void* table, hipStream_t st)
 {
-    if (sh.nq == 0) return hipSuccess;
     const int rows = sh.w + 2 * kTableSlack, half = sh.d / 2;
     const long n_tab = (long)rows * half;
     hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0, st,
                        (float2*)table, rows, half, sh.w, log(rope_base));
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    return hipGetLastError();
+}
+
+// Splits of each query tile's key range: enough workgroups to give every CU two,
+// at most one per key tile and 16 in all (bf16 storage only).
+int window_splits(const Shape& sh)
+{
+    if (!sh.bf16 || sh.nq == 0) return 1;
+    const long base = (sh.nq + kWinQ - 1) / kWinQ * (long)sh.B * sh.H;
+    if (base >= 512) return 1;
+    const long tiles = (sh.w + kWinQ - 1) / mf::kTileK + 1;       // key tiles of a query tile, at most
+    long want = (512 + base - 1) / base;
+    want = want < tiles ? want : tiles;
+    return (int)(want < 16 ? want : 16);
+}
+
+size_t window_ws_bytes(const Shape& sh)
+{
+    const int S = window_splits(sh);
+    if (S <= 1) return 0;
+    const size_t rows = (size_t)sh.B * sh.H * sh.nq * S;
+    return rows * ((size_t)sh.d * sizeof(float) + sizeof(float2));
+}
+
+size_t window_workspace_bytes(const Shape& sh)
+{
+    return ((rope_table_bytes(sh) + 255) & ~(size_t)255) + window_ws_bytes(sh);
+}
+
+hipError_t launch_window(const Shape& sh, const void* q, const void* k, const void* v,
+                         double rope_base, void* table, void* o_sr, hipStream_t st,
+                         bool table_ready, size_t ws_bytes)
+{
+    if (sh.nq == 0) return hipSuccess;
+    if (!table_ready) {
+        const hipError_t err = launch_rope_table(sh, rope_base, table, st);
+        if (err != hipSuccess) return err;
+    }
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
     if (sh.bf16) {
+        // split the key range when the workspace holds the partial states
+        const int S = ws_bytes >= window_workspace_bytes(sh) ? window_splits(sh) : 1;
+        char* wsb = static_cast<char*>(table) + ((rope_table_bytes(sh) + 255) & ~(size_t)255);
+        const long rows_all = (long)sh.B * sh.H * sh.nq;
+        float* ws_acc = S > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+        float2* ws_ml = S > 1 ? reinterpret_cast<float2*>(ws_acc + rows_all * S * sh.d) : nullptr;
         const long n_tiles = (sh.nq + kWinQ - 1) / kWinQ;
-        dim3 grid((unsigned)(n_tiles * sh.B * sh.H)), block(256);
+        dim3 grid((unsigned)(n_tiles * S * sh.B * sh.H)), block(256);
 #define FS_WINDOW_MFMA(D)                                                                        \
         hipLaunchKernelGGL((window_attn_mfma_kernel<D>), grid, block, 0, st, (const uint16_t*)q,  \
                            sh.qs[0], sh.qs[1], sh.qs[2], (const uint16_t*)k, (const uint16_t*)v,  \
                            sh.kvs[0], sh.kvs[1], sh.kvs[2], sh.H, sh.B * sh.H, sh.nq, sh.q_pos0,  \
                            sh.w,                                                                  \
                            (const float2*)table, scale_log2, (uint16_t*)o_sr, sh.os[0], sh.os[1], \
-                           sh.os[2])
+                           sh.os[2], S, ws_acc, ws_ml)
         if (sh.d == 64) FS_WINDOW_MFMA(64); else FS_WINDOW_MFMA(128);
 #undef FS_WINDOW_MFMA
-        return hipGetLastError();
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess || S <= 1) return err;
+        return launch_split_merge(sh, S, ws_acc, ws_ml, false, 0.f, o_sr, st);
     }
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
 #define FS_WINDOW(E, D)                                                                          \

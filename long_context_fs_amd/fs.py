@@ -43,7 +43,7 @@ class FsStreamConfig(C.Structure):
     _fields_ = [("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
                 ("cell", C.c_int32), ("window", C.c_int32), ("n_recent", C.c_int32),
                 ("budget", C.c_int32), ("topk", C.c_int32), ("max_new", C.c_int32),
-                ("dtype", C.c_int32)]
+                ("dtype", C.c_int32), ("rope_base", C.c_float), ("rms_eps", C.c_float)]
 
 
 _lib = None
@@ -73,7 +73,7 @@ def load(path: str | None = None):
         "fs_stream_state_size": [C.POINTER(FsStreamConfig), C.POINTER(C.c_size_t)],
         "fs_stream_reset": [C.POINTER(FsStreamConfig), vp, C.c_size_t, vp],
         "fs_stream_step": [C.POINTER(FsStreamConfig), vp, C.c_size_t, C.c_int64, i32, vp, vp,
-                           vp, vp, vp, vp, f32, f32, vp, vp, vp],
+                           vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -277,16 +277,16 @@ def fs_stream_reset(cfg: FsStreamConfig, state, stream=None):
                                                       _s(stream)))
 
 
-def fs_stream_step(cfg: FsStreamConfig, state, pos0: int, q, k, v, alpha, rope_base: float,
-                   rms_eps: float, o, idx=None, prior=None, stream=None):
+def fs_stream_step(cfg: FsStreamConfig, state, pos0: int, q, k, v, alpha, o, idx=None,
+                   prior=None, stream=None):
     """Append k, v ([B, H, n_new, d], contiguous) at positions pos0 .. and write the
     FS-L output of the queries q at those positions into o; prior: None or
     (lambda, sigma) float32 [H] device tensors; idx: optional selected cells."""
     lam, sig = prior if prior is not None else (None, None)
     _check("fs_stream_step", load().fs_stream_step(
         C.byref(cfg), _p(state), state.numel() * state.element_size(), int(pos0),
-        int(q.shape[2]), _p(q), _p(k), _p(v), _p(alpha), _p(lam), _p(sig), float(rope_base),
-        float(rms_eps), _p(o), _p(idx), _s(stream)))
+        int(q.shape[2]), _p(q), _p(k), _p(v), _p(alpha), _p(lam), _p(sig), _p(o), _p(idx),
+        _s(stream)))
 
 
 class FsStream:
@@ -297,12 +297,11 @@ class FsStream:
                  dtype, alpha, rope_base=10000.0, rms_eps=1e-6, prior_lambda=None,
                  prior_sigma=None, device="cuda"):
         self.cfg = FsStreamConfig(batch, heads, head_dim, CELL, window, n_recent, budget, topk,
-                                  max_new, dtype)
+                                  max_new, dtype, rope_base, rms_eps)
         self.bytes = fs_stream_state_size(self.cfg)
         self.state = torch.empty(self.bytes, dtype=torch.uint8, device=device)
         self.alpha = alpha
         self.prior = None if prior_lambda is None else (prior_lambda, prior_sigma)
-        self.rope_base, self.rms_eps = rope_base, rms_eps
         self.pos = 0
         fs_stream_reset(self.cfg, self.state)
 
@@ -313,8 +312,7 @@ class FsStream:
     def step(self, q, k, v, o=None, idx=None):
         if o is None:
             o = torch.empty_like(q)
-        fs_stream_step(self.cfg, self.state, self.pos, q, k, v, self.alpha, self.rope_base,
-                       self.rms_eps, o, idx, self.prior)
+        fs_stream_step(self.cfg, self.state, self.pos, q, k, v, self.alpha, o, idx, self.prior)
         self.pos += q.shape[2]
         return o
 

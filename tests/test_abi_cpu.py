@@ -145,7 +145,7 @@ def test_status_strings(lib):
 
 def _scfg(**kw):
     f = dict(batch=1, heads=8, head_dim=128, cell=32, window=512, n_recent=0, budget=512,
-             topk=32, max_new=256, dtype=fs.FS_BF16)
+             topk=32, max_new=256, dtype=fs.FS_BF16, rope_base=10000.0, rms_eps=1e-6)
     f.update(kw)
     return fs.FsStreamConfig(*[f[n] for n, _ in fs.FsStreamConfig._fields_])
 
@@ -165,7 +165,8 @@ def test_stream_state_is_bounded(lib):
 @pytest.mark.parametrize("bad, status", [
     (dict(head_dim=96), 2), (dict(cell=16), 2), (dict(n_recent=0, budget=0), 2),
     (dict(n_recent=24, budget=1001), 2), (dict(topk=65), 2), (dict(max_new=0), 2),
-    (dict(max_new=4097), 2), (dict(dtype=7), 1), (dict(batch=0), 1), (dict(window=-1), 2)])
+    (dict(max_new=4097), 2), (dict(dtype=7), 1), (dict(batch=0), 1), (dict(window=-1), 2),
+    (dict(rope_base=1.0), 1), (dict(rms_eps=-1.0), 1)])
 def test_stream_config_rejected(lib, bad, status):
     n = C.c_size_t()
     assert lib.fs_stream_state_size(C.byref(_scfg(**bad)), C.byref(n)) == status
@@ -175,8 +176,7 @@ def test_stream_step_arguments_rejected(lib):
     cfg = _scfg(max_new=16)
     need = fs.fs_stream_state_size(cfg)
     step = lambda state, size, pos0, n_new, lam=None, sig=None, q=FAKE: lib.fs_stream_step(  # noqa: E731
-        C.byref(cfg), state, size, pos0, n_new, q, FAKE, FAKE, FAKE, lam, sig, 10000.0, 1e-6,
-        FAKE, None, None)
+        C.byref(cfg), state, size, pos0, n_new, q, FAKE, FAKE, FAKE, lam, sig, FAKE, None, None)
     assert step(FAKE, need - 1, 0, 4) == 1                       # state too small
     assert step(C.c_void_p((1 << 20) + 16), need, 0, 4) == 1     # not 256-byte aligned
     assert step(None, need, 0, 4) == 1
