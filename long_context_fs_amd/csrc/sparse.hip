@@ -531,12 +531,20 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
     const float l = wave_sum(w * e.y);                    // an empty split has weight 0
     float acc[R] = {};
     if (M != -INFINITY) {
+        // all splits' loads issued at once: a split past n_split re-reads the last
+        // one and has weight 0, so the loop has no branch
         const float* a = ws_acc + row * n_split * (long)D + lane;
-#pragma unroll 8
-        for (int sp = 0; sp < n_split; ++sp) {            // loads independent of the weights
-            const float ws = __shfl(w, sp, kWave);
+        float x[32][R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(ws, a[sp * D + r * kWave], acc[r]);
+        for (int sp = 0; sp < 32; ++sp)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                x[sp][r] = a[(sp < n_split ? sp : n_split - 1) * D + r * kWave];
+#pragma unroll
+        for (int sp = 0; sp < 32; ++sp) {
+            const float ws = __shfl(w, sp, kWave);          // 0 for sp >= n_split
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = fmaf(ws, x[sp][r], acc[r]);
         }
     }
     const float inv_l = l > 0.f ? 1.f / l : 0.f;
