@@ -202,7 +202,8 @@ __device__ __forceinline__ void attn_tile(const uint16_t* ks, const uint16_t* vt
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qg][r]);
+            for (int r = 0; r < 4; ++r)   // IEEE maximum: no NaN quieting of MFMA results
+                tmax = __builtin_elementwise_maximum(tmax, s[kb][qg][r]);
         tmax = xrow_max(tmax) * scale_log2;
         // raise the reference only when the tile max exceeds it by > kLazy
         const bool raise = tmax > m_ref[qg] + kLazy;

@@ -288,7 +288,8 @@ __device__ __forceinline__ void sp_tile(const uint16_t* ks, const uint16_t* vt,
 #pragma unroll
             for (int kb = 2 * c; kb < 2 * c + 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) x = fmaxf(x, s[kb][qg][r]);
+                for (int r = 0; r < 4; ++r)   // IEEE maximum: no NaN quieting of MFMA results
+                    x = __builtin_elementwise_maximum(x, s[kb][qg][r]);
             cm[c] = sel[qg][c] ? x : -INFINITY;
         }
         // scale_log2 > 0 commutes with max
