@@ -360,6 +360,44 @@ def test_small_combine_and_end_to_end(name):
     print(f"[parity] {name}: o max row rel err {err:.3g}, near-tie rows {n_near}")
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_needle", "f32_d128_recent", "bf16_d128_decode"])
+def test_token_major_strided_views_equal_contiguous(name):
+    """q, k, v and every output as [B, T, H, d] tensors seen as [B, H, T, d] views:
+    the calls take the strides from the views and must reproduce the contiguous
+    run bit for bit (only the addressing differs)."""
+    from long_context_fs_amd import fs as fsb
+    wl, x, g, ref = small_case(name)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def tmajor(a):                       # [B, H, T, d] array -> [B, H, T, d] view of [B, T, H, d]
+        t = torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).cuda().to(tdt)
+        return t.permute(0, 2, 1, 3)
+
+    q, k, v = tmajor(x["q"]), tmajor(x["k"]), tmajor(x["v"])
+    B, H, d = wl.batch, wl.heads, wl.head_dim
+    out = lambda: torch.empty((B, wl.n_q, H, d), dtype=tdt, device="cuda").permute(0, 2, 1, 3)  # noqa: E731
+    o_sr, o_lr, o = out(), out(), out()
+    dt = fsb.FS_BF16 if wl.dtype == "bf16" else fsb.FS_F32
+    p = fsb.problem(B, H, d, wl.n_ctx, wl.n_q, wl.q_pos0, wl.window, dt, q=q, kv=k, o=o)
+    assert tuple(p.kv_stride) == (wl.n_ctx * H * d, d, H * d)
+    fwd = FsForward.for_workload(wl)     # buffers of the right shapes
+    fsb.fs_cell_summaries(p, k, fwd.kbar, fwd.amax)
+    if fwd.pruned:
+        fsb.fs_prune_prefix(p, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep, fwd.keep_count)
+    fsb.fs_select_topk(p, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, wl.topk, fwd.idx,
+                       fwd.score, None, fwd.prior)
+    ws = torch.empty(fsb.fs_workspace_size(p), dtype=torch.uint8, device="cuda")
+    fsb.fs_window_attn(p, q, k, v, wl.rope_base, ws, o_sr)
+    nsp = fsb.fs_sparse_workspace_size(p)
+    wsp = torch.empty(nsp, dtype=torch.uint8, device="cuda") if nsp else None
+    fsb.fs_sparse_attn(p, q, k, v, fwd.idx, wl.topk, wl.rms_eps, o_lr, wsp)
+    fsb.fs_combine(p, o_sr, o_lr, torch.from_numpy(x["alpha"]).cuda(), o)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fwd.idx.cpu().numpy(), g["idx"])
+    for name_, t in (("o_sr", o_sr), ("o_lr", o_lr), ("o", o)):
+        np.testing.assert_array_equal(t.float().cpu().numpy(), g[name_], err_msg=name_)
+
+
 def test_window_dense_equals_causal():
     """w >= N-1: the local branch is dense causal RoPE attention (oracle pinned to SDPA)."""
     wl, x, g, ref = small_case("f32_d64_dense_window")
