@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kPruneThreads) void prune_reg_kernel(
         kv[j] = c < n ? key[c] : 0u;
     }
     int flip = 0;
+    // block sum of a wave-uniform count (ballot popcounts: no lane shuffles)
     auto bsum = [&](int x) {
-        x = wave_sum_int(x);
         if (lane == 0) red[flip][wv] = x;
         __syncthreads();
         int t = 0;
@@ -187,15 +187,15 @@ __global__ __launch_bounds__(kPruneThreads) void prune_reg_kernel(
             const uint32_t cand = thr | (1u << bit);
             int c = 0;
 #pragma unroll
-            for (int j = 0; j < KPT; ++j) c += kv[j] >= cand;    // kv = 0 past n, cand >= 1
+            for (int j = 0; j < KPT; ++j) c += __popcll(__ballot(kv[j] >= cand));   // kv = 0 past n, cand >= 1
             if (bsum(c) >= budget) thr = cand;
         }
         int gt = 0, eq = 0;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const bool valid = 256 * j + tid < n;
-            gt += valid && kv[j] > thr;
-            eq += valid && kv[j] == thr;
+            gt += __popcll(__ballot(valid && kv[j] > thr));
+            eq += __popcll(__ballot(valid && kv[j] == thr));
         }
         const int n_gt = bsum(gt);
         n_eq = bsum(eq);
