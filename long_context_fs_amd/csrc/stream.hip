@@ -152,6 +152,9 @@ __global__ __launch_bounds__(256) void stream_reset_kernel(StreamDev sd)
     }
 }
 
+constexpr int kNCB = 16;          // new cells summarised together (one wave each)
+constexpr int kAppendWaves = 4;   // waves of the append workgroup
+
 __device__ __forceinline__ int block_sum_int(int x, int* red)
 {
     x = wave_sum_int(x);
@@ -191,20 +194,21 @@ __global__ __launch_bounds__(256) void stream_append_kernel(
     extern __shared__ uint4 smem_raw[];
     const int P = sd.P, M = sd.M, W = sd.W, L = sd.L, s = sd.s;
     const int P1 = P > 0 ? P : 1, W1 = W > 0 ? W : 1;
-    float* l_kbar = reinterpret_cast<float*>(smem_raw);                 // [D], 16-byte aligned
-    float* l_ta = l_kbar + D;                                           // TopP a_c [P]
+    float* l_kbar = reinterpret_cast<float*>(smem_raw);                 // [kNCB][D], 16-byte aligned
+    float* l_ta = l_kbar + kNCB * D;                                    // TopP a_c [P]
     int32_t* l_tc = reinterpret_cast<int32_t*>(l_ta + P1);              // TopP cell [P]
     int32_t* l_ts = l_tc + P1;                                          // TopP slot [P]
     int32_t* l_free = l_ts + P1;                                        // [M]
     int32_t* l_pend = l_free + M;                                       // [M]
     int32_t* l_intopp = l_pend + M;                                     // [M] slot in TopP
     int32_t* l_recent = l_intopp + M;                                   // [W]
-    __shared__ float l_amax;
+    __shared__ float l_ab[kNCB];              // a_c of the batch's cells
+    __shared__ int l_slot[kNCB];              // their slots (-1: not kept)
     __shared__ int red_i[4];
     __shared__ uint64_t red_u[4];
     __shared__ int s_pos;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wv = tid >> 6;
     const long bh = blockIdx.x;
     int32_t* hdr = sd.hdr + bh * kHdrWords;
     int tcount = hdr[kHdrTopP], fcount = hdr[kHdrFree];
@@ -248,9 +252,12 @@ __global__ __launch_bounds__(256) void stream_append_kernel(
         const int rr = (int)(n - n_row0);
         int32_t* row = sd.keep + (bh * sd.R + rr) * (long)sd.keep_w;
         const int64_t lim = n - W;
-        int below = 0;
-        for (int j = tid; j < tcount; j += 256) below += l_tc[j] < lim;
-        const int npre = block_sum_int(below, red_i);
+        int npre = tcount;                    // W = 0: every TopP cell precedes n
+        if (W > 0) {
+            int below = 0;
+            for (int j = tid; j < tcount; j += 256) below += l_tc[j] < lim;
+            npre = block_sum_int(below, red_i);
+        }
         const int nrec = (int)(n < W ? n : W);
         for (int j = tid; j < npre; j += 256) row[j] = l_ts[j];
         for (int j = tid; j < nrec; j += 256) row[npre + j] = l_recent[(int)((n - nrec + j) % W)];
@@ -258,102 +265,130 @@ __global__ __launch_bounds__(256) void stream_append_kernel(
     };
     if (n_row0 == n_start) emit_row(n_start);
 
-    for (int64_t c = n_start; c < n_end; ++c) {
-        // (a) summaries of cell c from its 32 ring rows (contiguous thanks to the mirror)
-        const int rbase = (int)((c * s) & (L - 1));
-        if (tid < kWave) wave_cell_summary<E, D>(rk + (long)rbase * D, D, l_kbar, &l_amax);
+    bool stop = false;                        // block-uniform
+    // TopP's smallest (a_c, c) and its position, valid until TopP changes
+    bool min_ok = false;
+    uint64_t kmin = 0;
+    int kpos = 0;
+    for (int64_t cb = n_start; cb < n_end && !stop; cb += kNCB) {
+        const int nb = (int)(n_end - cb < kNCB ? n_end - cb : kNCB);
+        // (a) summaries of the batch's cells, one wave per cell, from their 32 ring
+        //     rows (contiguous thanks to the mirror)
+        for (int j = wv; j < nb; j += kAppendWaves) {
+            const int rbase = (int)(((cb + j) * s) & (L - 1));
+            wave_cell_summary<E, D>(rk + (long)rbase * D, D, l_kbar + j * D, &l_ab[j]);
+        }
+        if (tid < kNCB) l_slot[tid] = -1;     // cells not reached keep no slot
         __syncthreads();
-        const float a = l_amax;
-        // (b) eq. 8: does (a, c) beat TopP's smallest (a_c, c)?
-        bool enter = tcount < P;
-        int ev = -1;
-        if (!enter && P > 0) {
-            uint64_t mine = ~0ull;
-            for (int j = tid; j < tcount; j += 256) {
-                const uint64_t kk = ((uint64_t)__float_as_uint(l_ta[j]) << 32) | (uint32_t)l_tc[j];
-                mine = kk < mine ? kk : mine;
+        for (int jc = 0; jc < nb && !stop; ++jc) {
+            const int64_t c = cb + jc;
+            const float a = l_ab[jc];
+            // (b) eq. 8: does (a, c) beat TopP's smallest (a_c, c)?
+            bool enter = tcount < P;
+            int ev = -1;
+            if (!enter && P > 0) {
+                if (!min_ok) {                // block-uniform
+                    uint64_t mine = ~0ull;
+                    for (int j = tid; j < tcount; j += 256) {
+                        const uint64_t kk =
+                            ((uint64_t)__float_as_uint(l_ta[j]) << 32) | (uint32_t)l_tc[j];
+                        mine = kk < mine ? kk : mine;
+                    }
+                    kmin = block_min_u64(mine, red_u);
+                    const int cmin = (int)(uint32_t)kmin;
+                    for (int j = tid; j < tcount; j += 256)
+                        if (l_tc[j] == cmin) s_pos = j;
+                    __syncthreads();
+                    kpos = s_pos;
+                    min_ok = true;
+                }
+                // a_c >= 0, so its bit pattern orders like its value; c is newer than
+                // every stored cell and wins a tie on a_c
+                enter = __float_as_uint(a) >= (uint32_t)(kmin >> 32);
+                ev = enter ? kpos : -1;
             }
-            const uint64_t kmin = block_min_u64(mine, red_u);
-            const int cmin = (int)(uint32_t)kmin;
-            for (int j = tid; j < tcount; j += 256)
-                if (l_tc[j] == cmin) s_pos = j;
-            __syncthreads();
-            // a_c >= 0, so its bit pattern orders like its value; c is newer than
-            // every stored cell and wins a tie on a_c
-            enter = __float_as_uint(a) >= (uint32_t)(kmin >> 32);
-            ev = enter ? s_pos : -1;
-        }
-        const int ce = ev >= 0 ? l_tc[ev] : -1, se = ev >= 0 ? l_ts[ev] : -1;
-        const int64_t cr = (W > 0 && c - W >= 0) ? c - W : -1;   // leaves Recent_W
-        const int sr = cr >= 0 ? l_recent[(int)(cr % W)] : -1;
-        const bool retained = enter || W > 0;
-        if (retained && fcount == 0) {       // cannot happen with M slots; flagged, not faulted
-            err = 1;
-            break;
-        }
-        const int slot = retained ? l_free[fcount - 1] : -1;
-        if (retained) --fcount;
-        // set aside: the evicted cell unless Recent_W (cells c-W+1 .. c) keeps it, and
-        // the cell leaving Recent_W unless TopP keeps it (counted once if both)
-        const bool drop_e = ev >= 0 && ce <= c - W;
-        const bool drop_r = cr >= 0 && cr != ce && !l_intopp[sr];
-        __syncthreads();                     // every thread has read the entries it needs
+            if (enter) min_ok = false;        // TopP changes below
+            const int ce = ev >= 0 ? l_tc[ev] : -1, se = ev >= 0 ? l_ts[ev] : -1;
+            const int64_t cr = (W > 0 && c - W >= 0) ? c - W : -1;   // leaves Recent_W
+            const int sr = cr >= 0 ? l_recent[(int)(cr % W)] : -1;
+            const bool retained = enter || W > 0;
+            if (retained && fcount == 0) {       // cannot happen with M slots; flagged, not faulted
+                err = 1;
+                stop = true;
+                break;
+            }
+            const int slot = retained ? l_free[fcount - 1] : -1;
+            if (retained) --fcount;
+            // set aside: the evicted cell unless Recent_W (cells c-W+1 .. c) keeps it, and
+            // the cell leaving Recent_W unless TopP keeps it (counted once if both)
+            const bool drop_e = ev >= 0 && ce <= c - W;
+            const bool drop_r = cr >= 0 && cr != ce && !l_intopp[sr];
+            __syncthreads();                     // every thread has read the entries it needs
 
-        // (c) TopP update, in ascending cell order: drop entry ev, append c
-        if (enter) {
-            if (ev >= 0) {
-                float va[4];
-                int32_t vc[4], vs[4];
+            // (c) TopP update, in ascending cell order: drop entry ev, append c
+            if (enter) {
+                if (ev >= 0) {
+                    float va[4];
+                    int32_t vc[4], vs[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int j = tid + 256 * u;
-                    if (j > ev && j < tcount) { va[u] = l_ta[j]; vc[u] = l_tc[j]; vs[u] = l_ts[j]; }
-                }
-                __syncthreads();
+                    for (int u = 0; u < 4; ++u) {
+                        const int j = tid + 256 * u;
+                        if (j > ev && j < tcount) { va[u] = l_ta[j]; vc[u] = l_tc[j]; vs[u] = l_ts[j]; }
+                    }
+                    __syncthreads();
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int j = tid + 256 * u;
-                    if (j > ev && j < tcount) { l_ta[j - 1] = va[u]; l_tc[j - 1] = vc[u]; l_ts[j - 1] = vs[u]; }
+                    for (int u = 0; u < 4; ++u) {
+                        const int j = tid + 256 * u;
+                        if (j > ev && j < tcount) { l_ta[j - 1] = va[u]; l_tc[j - 1] = vc[u]; l_ts[j - 1] = vs[u]; }
+                    }
+                    --tcount;
                 }
-                --tcount;
+                if (tid == 0) {                  // index tcount is not among the shifted ones
+                    l_ta[tcount] = a;
+                    l_tc[tcount] = (int32_t)c;
+                    l_ts[tcount] = slot;
+                }
+                ++tcount;
             }
-            if (tid == 0) {                  // index tcount is not among the shifted ones
-                l_ta[tcount] = a;
-                l_tc[tcount] = (int32_t)c;
-                l_ts[tcount] = slot;
+            // (d) set-aside list, TopP membership, Recent_W
+            if (tid == 0) {
+                if (ev >= 0) l_intopp[se] = 0;
+                if (enter) l_intopp[slot] = 1;
+                if (drop_e) l_pend[pcount] = se;
+                if (drop_r) l_pend[pcount + drop_e] = sr;
+                if (W > 0) l_recent[(int)(c % W)] = slot;
             }
-            ++tcount;
+            pcount += (int)drop_e + (int)drop_r;
+            if (tid == 0) l_slot[jc] = retained ? slot : -1;
+            __syncthreads();
+            if (c + 1 >= n_row0) emit_row(c + 1);
+            __syncthreads();
         }
-        // (d) set-aside list, TopP membership, Recent_W
-        if (tid == 0) {
-            if (ev >= 0) l_intopp[se] = 0;
-            if (enter) l_intopp[slot] = 1;
-            if (drop_e) l_pend[pcount] = se;
-            if (drop_r) l_pend[pcount + drop_e] = sr;
-            if (W > 0) l_recent[(int)(c % W)] = slot;
-        }
-        pcount += (int)drop_e + (int)drop_r;
-        // (e) a kept cell is copied into its slot with its summaries
-        if (retained) {
+        // (e) the batch's kept cells are copied into their slots with their summaries
+        for (int e = tid; e < nb * s * CPR; e += 256) {
+            const int j = e / (s * CPR), t = (e / CPR) % s, ch = e % CPR;
+            const int slot = l_slot[j];
+            if (slot < 0) continue;
+            const int rbase = (int)(((cb + j) * s) & (L - 1));
             T* pk = reinterpret_cast<T*>(sd.pool_k) + (bh * M + slot) * (long)s * D;
             T* pv = reinterpret_cast<T*>(sd.pool_v) + (bh * M + slot) * (long)s * D;
-            for (int e = tid; e < s * CPR; e += 256) {
-                const int t = e / CPR, ch = e % CPR;
-                const long src = (long)(rbase + t) * D + ch * EPV;
-                *reinterpret_cast<uint4*>(pk + (long)t * D + ch * EPV) =
-                    *reinterpret_cast<const uint4*>(rk + src);
-                *reinterpret_cast<uint4*>(pv + (long)t * D + ch * EPV) =
-                    *reinterpret_cast<const uint4*>(rv + src);
-            }
-            for (int e = tid; e < D; e += 256) sd.kbar[(bh * M + slot) * (long)D + e] = l_kbar[e];
-            if (tid == 0) {
-                sd.amax[bh * M + slot] = a;
-                sd.cell[bh * M + slot] = (int32_t)c;
+            const long src = (long)(rbase + t) * D + ch * EPV;
+            *reinterpret_cast<uint4*>(pk + (long)t * D + ch * EPV) =
+                *reinterpret_cast<const uint4*>(rk + src);
+            *reinterpret_cast<uint4*>(pv + (long)t * D + ch * EPV) =
+                *reinterpret_cast<const uint4*>(rv + src);
+        }
+        for (int e = tid; e < nb * D; e += 256) {
+            const int slot = l_slot[e / D];
+            if (slot >= 0) sd.kbar[(bh * M + slot) * (long)D + e % D] = l_kbar[e];
+        }
+        for (int j = tid; j < nb; j += 256) {
+            if (l_slot[j] >= 0) {
+                sd.amax[bh * M + l_slot[j]] = l_ab[j];
+                sd.cell[bh * M + l_slot[j]] = (int32_t)(cb + j);
             }
         }
-        __syncthreads();
-        if (c + 1 >= n_row0) emit_row(c + 1);
-        __syncthreads();
+        __syncthreads();                      // l_kbar, l_ab and l_slot are reused
     }
 
     // ---- write the set structures back
@@ -403,7 +438,8 @@ hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* 
 
     // 1. state update
     const int P1 = c.P > 0 ? c.P : 1, W1 = c.W > 0 ? c.W : 1;
-    const size_t lds = (size_t)c.d * 4 + (size_t)3 * P1 * 4 + (size_t)3 * Ly.M * 4 + (size_t)W1 * 4;
+    const size_t lds = (size_t)kNCB * c.d * 4 + (size_t)3 * P1 * 4 + (size_t)3 * Ly.M * 4 +
+                       (size_t)W1 * 4;
 #define FS_APPEND(E, D)                                                                          \
     hipLaunchKernelGGL((stream_append_kernel<E, D>), dim3((unsigned)(c.B * c.H)), dim3(256), lds, \
                        st, sd, (const typename E::storage*)k, (const typename E::storage*)v,      \
