@@ -67,7 +67,12 @@ def test_prune_rows_and_workspace_host_only(lib):
     assert fs.fs_prune_rows(_prob(n_q=0)) == (0, 0)
     assert fs.fs_prune_rows(_prob(n_q=100, n_ctx=400)) == (0, 1)
     ws = fs.fs_workspace_size(_prob())
-    assert ws == (512 + 256) * 32 * 8
+    table = (512 + 256) * 32 * 8                           # (w + 256) x d/2 float2
+    # 2 x 32 query tiles fill 64 < 512 workgroups: each tile's keys split 8 ways,
+    # one partial (O row of d floats, then (m, l)) per query and split
+    assert ws == table + 2 * 4096 * 8 * (64 * 4 + 8)
+    # enough queries to fill the device: the table alone
+    assert fs.fs_workspace_size(_prob(batch=8, heads=16, n_q=4096)) == table
 
 
 @pytest.mark.parametrize("bad,status", [
