@@ -152,10 +152,12 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
     if rerank:
         # eq. 12 token-level reranking in place of eq. 7's scoring, timed on its own
         rr_idx = torch.empty_like(fwd.idx)
+        rr_ws = torch.empty(fs.fs_rerank_workspace_size(p, fwd.keep_w if fwd.pruned else 0),
+                            dtype=torch.uint8, device=q.device)
 
         def rr():
             fs.fs_rerank_topk(p, q, k, fwd.keep, fwd.keep_count, fwd.keep_w, fwd.topk, rr_idx,
-                              None, None, fwd.prior)
+                              None, None, fwd.prior, rr_ws)
         for _ in range(warmup):
             rr()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -304,6 +306,8 @@ def run_phase(name, phase, reps, torch, fs):
     f = fs.FsForward.for_workload(wl, device=dev)
     f(q, k, v, alpha)
     p = f.prob
+    rr_ws = torch.empty(fs.fs_rerank_workspace_size(p, f.keep_w if f.pruned else 0),
+                        dtype=torch.uint8, device=dev)
     calls = {
         "summaries": lambda: fs.fs_cell_summaries(p, k, f.kbar, f.amax),
         "prune": lambda: fs.fs_prune_prefix(p, f.amax, f.n_recent, f.budget, f.keep,
@@ -311,7 +315,7 @@ def run_phase(name, phase, reps, torch, fs):
         "select": lambda: fs.fs_select_topk(p, q, f.kbar, f.keep, f.keep_count, f.keep_w,
                                             f.topk, f.idx, None, None, f.prior),
         "rerank": lambda: fs.fs_rerank_topk(p, q, k, f.keep, f.keep_count, f.keep_w, f.topk,
-                                            f.idx, None, None, f.prior),
+                                            f.idx, None, None, f.prior, rr_ws),
         "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),
         "sparse": lambda: fs.fs_sparse_attn(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_lr, f.ws_sparse),
         "combine": lambda: fs.fs_combine(p, f.o_sr, f.o_lr, alpha, f.o),

@@ -113,11 +113,25 @@ fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* 
  * r~_ic = log sum_{j in I_c} exp(q_i . k_j / sqrt(d)) + lambda_h a_c erf((i - p_c) / (2 sigma_h))
  * over the cell's s raw (unrotated) keys instead of the mean key.  k: [B][H][N][d]
  * with the problem's kv strides.  The prior arrays follow fs_select_topk's rule
- * (all NULL: no prior).  score (nullable) receives r~_ic aligned with idx. */
+ * (all NULL: no prior).  score (nullable) receives r~_ic aligned with idx.
+ * workspace (nullable, device memory, 256-byte aligned, owned by the caller, not
+ * kept after the call's work is done) of workspace_bytes >=
+ * fs_rerank_workspace_size(problem, keep ? keep_width : 0) lets bf16 problems
+ * score 128 queries per workgroup with the scores held there; a smaller or NULL
+ * workspace uses a 64-query kernel that needs none.  The result does not depend
+ * on it.  Calls sharing one workspace on different streams race. */
 fs_status fs_rerank_topk(const fs_problem* problem, const void* q, const void* k,
                          const float* amax, const float* prior_lambda, const float* prior_sigma,
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
-                         int32_t topk, int32_t* idx, float* score, void* stream);
+                         int32_t topk, int32_t* idx, float* score, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Bytes of the workspace fs_rerank_topk uses (keep_width 0: no pruning):
+ * ceil(n_q / 128) B H round16(u) 128 float32 scores, u the most union cells of
+ * the five candidate counts 128 queries span (keep_width + 5, or every candidate
+ * cell without pruning). */
+fs_status fs_rerank_workspace_size(const fs_problem* problem, int32_t keep_width,
+                                   size_t* bytes);
 
 /* Bytes of device workspace for fs_window_attn: its RoPE cos/sin table, then room
  * for the partial states with which a short query range (decode) splits each

@@ -33,9 +33,13 @@ struct Prior {
 hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
                          const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
                          int n_rows, int topk, int32_t* idx, float* score, hipStream_t st);
+// Reranking keeps each block's (cell, query) scores in a workspace when ws_bytes
+// >= rerank_ws_bytes (pruned: keep != nullptr); otherwise it needs none.
+size_t rerank_ws_bytes(const Shape& sh, bool pruned, int keep_w);
 hipError_t launch_rerank(const Shape& sh, const void* q, const void* k, const Prior& pr,
                          const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
-                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st);
+                         int n_rows, int topk, int32_t* idx, float* score, void* ws,
+                         size_t ws_bytes, hipStream_t st);
 // Selection over a streaming state's cell pool: keep rows of pool slots (ascending
 // cell order), row r of a head (rows_per_head apart) for candidate count
 // n_row0 + r; kbar [B*H][M][d], amax and cell_of

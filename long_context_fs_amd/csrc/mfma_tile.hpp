@@ -35,6 +35,14 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 32x32x16 bf16 product: lane l holds A row l % 32 and B column l % 32 with
+// k = 8 (l / 32) .. + 7; C register e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4
+// of column l % 32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

@@ -379,7 +379,8 @@ struct SelLayout {
 // 64-key K tiles when reranking | bitmap | rank | union list | row-membership
 // masks | copy of the keep rows.
 template <int D>
-__host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int keep_w, bool two_tiles = false)
+__host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int keep_w, bool two_tiles = false,
+                                                int rows = 3)
 {
     SelLayout L;
     L.nwords = (n_hi + 31) / 32;
@@ -397,7 +398,7 @@ __host__ __device__ inline SelLayout sel_layout(int n_hi, int u_cap, int keep_w,
     L.off_vmask = off;
     off = up16(off + (size_t)u_cap * 4);
     L.off_krows = off;
-    off = up16(off + (size_t)3 * keep_w * 2);
+    off = up16(off + (size_t)rows * keep_w * 2);
     L.bytes = off;
     return L;
 }
@@ -463,6 +464,7 @@ __device__ __forceinline__ int field5(const uint32_t* w, int i)
 // union list ulist (slot -> cell) and vmask (bit r: the slot is in keep row
 // n_a + r).  Without pruning the union is the prefix [0, n_b) and slot == cell.
 // Returns the union size; ends with the block synchronised.
+template <int ROWS>
 __device__ __forceinline__ int sel_union(const int32_t* __restrict__ keep,
                                          const int32_t* __restrict__ keep_count, int keep_w,
                                          long bh, int n_lo, int n_rows, int n_a, int n_b,
@@ -473,32 +475,34 @@ __device__ __forceinline__ int sel_union(const int32_t* __restrict__ keep,
     int n_union;
     if (keep != nullptr) {
         const int nw = (n_b + 31) >> 5;
-        // the (at most three) keep rows, copied to LDS with all loads in flight together
+        // the (at most ROWS) keep rows, copied to LDS with all loads in flight together
         const int r_first = n_a > 1 ? n_a : 1;            // rows of n = 0 are empty
         const int n_kr = n_b >= r_first ? n_b - r_first + 1 : 0;
-        int kcnt[3];
+        int kcnt[ROWS];
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < ROWS; ++j)
             kcnt[j] = j < n_kr ? keep_count[bh * n_rows + (r_first + j - n_lo)] : 0;
-        for (int e0 = 0; e0 < 3 * keep_w; e0 += 4 * 256) {
+        for (int e0 = 0; e0 < ROWS * keep_w; e0 += 4 * 256) {
             int vals[4];
 #pragma unroll
             for (int u4 = 0; u4 < 4; ++u4) {
                 const int e = e0 + u4 * 256 + tid;
                 const int j = e / keep_w, x = e - j * keep_w;
-                const int cnt = j == 0 ? kcnt[0] : j == 1 ? kcnt[1] : kcnt[2];
-                vals[u4] = (j < 3 && x < cnt)
+                int cnt = 0;
+#pragma unroll
+                for (int jj = 0; jj < ROWS; ++jj) cnt = j == jj ? kcnt[jj] : cnt;
+                vals[u4] = (j < ROWS && x < cnt)
                                ? keep[(bh * n_rows + (r_first + j - n_lo)) * keep_w + x] : -1;
             }
 #pragma unroll
             for (int u4 = 0; u4 < 4; ++u4) {
                 const int e = e0 + u4 * 256 + tid;
-                if (e < 3 * keep_w) krows[e] = (uint16_t)(vals[u4] < 0 ? 0xFFFF : vals[u4]);
+                if (e < ROWS * keep_w) krows[e] = (uint16_t)(vals[u4] < 0 ? 0xFFFF : vals[u4]);
             }
         }
         for (int wd = tid; wd < nw; wd += 256) bitmap[wd] = 0u;
         __syncthreads();
-        for (int e = tid; e < 3 * keep_w; e += 256) {
+        for (int e = tid; e < ROWS * keep_w; e += 256) {
             const int c = krows[e];
             if (c != 0xFFFF) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
         }
@@ -530,7 +534,7 @@ __device__ __forceinline__ int sel_union(const int32_t* __restrict__ keep,
             }
         }
         __syncthreads();
-        for (int e = tid; e < 3 * keep_w; e += 256) {
+        for (int e = tid; e < ROWS * keep_w; e += 256) {
             const int c = krows[e];
             if (c != 0xFFFF) {
                 const int sl = rank[c >> 5] + __popc(bitmap[c >> 5] & ((1u << (c & 31)) - 1u));
@@ -728,7 +732,7 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
     const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
     const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
 
-    const int n_union = sel_union(keep, keep_count, keep_w, bh, n_lo, n_rows, n_a, n_b, krows,
+    const int n_union = sel_union<3>(keep, keep_count, keep_w, bh, n_lo, n_rows, n_a, n_b, krows,
                                   bitmap, rank, ulist, vmask, red);
 
     // ---- the wave's 16 queries as B operands --------------------------------
@@ -908,7 +912,7 @@ __global__ __launch_bounds__(256, NB >= 33 ? 1 : (NB >= 17 ? 3 : 4)) void rerank
     const int n_rows_blk = nq - t0 < kTq ? (int)(nq - t0) : kTq;
     const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
     const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
-    const int n_union = sel_union(keep, keep_count, keep_w, bh, n_lo, n_rows, n_a, n_b, krows,
+    const int n_union = sel_union<3>(keep, keep_count, keep_w, bh, n_lo, n_rows, n_a, n_b, krows,
                                   bitmap, rank, ulist, vmask, red);
 
     const int qr = 16 * wv + n;
@@ -1054,33 +1058,242 @@ __global__ __launch_bounds__(256, NB >= 33 ? 1 : (NB >= 17 ? 3 : 4)) void rerank
                       keep, ulist, 1.f);
 }
 
+// Reranking (eq. 12) for 128 queries per workgroup on the 32x32x16 matrix core,
+// when the caller gives a workspace.  A wave scores its 32 queries against each
+// 32-key cell in one 32x32 block, so every K fragment read from LDS serves 32
+// queries (twice the 16x16 kernel above), and a query's 32 logits of a cell sit
+// in lanes l and l + 32 (16 each): a local (max, sum of exp2) per lane, then one
+// lane-half swap merges both cells of the tile at once.  The per-slot scores go
+// to the workspace, [workgroup][union slot][query], and are read back in two
+// rounds of 16 queries for the same exact top-K search as the kernels above.
+// The union spans at most five keep rows (128 consecutive queries).
+template <int D, int NB>
+__global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void rerank32_kernel(
+    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const uint16_t* __restrict__ k, int64_t kvs0, int64_t kvs1, int64_t kvs2, Prior pr, int H,
+    int BH, int C, int nq, int q_pos0, int window, int cell, const int32_t* __restrict__ keep,
+    const int32_t* __restrict__ keep_count, int keep_w, int n_lo, int n_rows, int topk,
+    int n_hi_all, int u_cap, float inv_sqrt_d, float* __restrict__ ws,
+    int32_t* __restrict__ idx, float* __restrict__ score)
+{
+    using namespace mf;
+    constexpr int KS = D / 16;                              // k-steps of 32x32x16
+    constexpr int kTq = 128;
+    constexpr int KC = (kTileK * D / 8) / 256;              // 16-byte K chunks per thread
+    extern __shared__ uint4 smem_raw[];
+    const SelLayout L = sel_layout<D>(n_hi_all, u_cap, keep ? keep_w : 0, true, 5);
+    char* base = reinterpret_cast<char*>(smem_raw);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(base);       // two swizzled 64-key tiles
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
+    uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
+    uint32_t* vmask = reinterpret_cast<uint32_t*>(base + L.off_vmask);
+    uint16_t* krows = reinterpret_cast<uint16_t*>(base + L.off_krows);
+    __shared__ int red[4];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long t0 = tb.tile * kTq;
+    const int n_rows_blk = nq - t0 < kTq ? (int)(nq - t0) : kTq;
+    const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
+    const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
+    const int n_union = sel_union<5>(keep, keep_count, keep_w, bh, n_lo, n_rows, n_a, n_b,
+                                     krows, bitmap, rank, ulist, vmask, red);
+
+    // the wave's 32 queries as B operands: lane l holds query 32 wv + l % 32,
+    // dims 16 ks + 8 (l / 32) .. + 7
+    const int qc = 32 * wv + (lane & 31);
+    const bool qc_ok = qc < n_rows_blk;
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qrow = q + b * qs0 + h * qs1 + (t0 + (qc_ok ? qc : 0)) * qs2;
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+            qf[t] = as_bf16x8(qc_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * t + 8 * (lane >> 5))
+                                    : make_uint4(0, 0, 0, 0));
+    }
+
+    // tile u holds union slots 2u (rows 0-31) and 2u + 1 (rows 32-63; past the
+    // union it repeats the first cell)
+    const uint16_t* kh = k + b * kvs0 + h * kvs1;
+    uint32_t koff[KC];
+#pragma unroll
+    for (int it = 0; it < KC; ++it) {
+        const int cidx = tid + 256 * it;
+        koff[it] = (uint32_t)((((cidx / (D / 8)) & 31) * kvs2 + (cidx % (D / 8)) * 8) * 2);
+    }
+    uint4 st[KC];
+    auto load_tile = [&](int u) {
+        const int s0 = 2 * u, s1 = 2 * u + 1 < n_union ? 2 * u + 1 : 2 * u;
+        const int c0 = __builtin_amdgcn_readfirstlane(keep ? (int)ulist[s0] : s0);
+        const int c1 = __builtin_amdgcn_readfirstlane(keep ? (int)ulist[s1] : s1);
+        const char* p0 = reinterpret_cast<const char*>(kh + (long)c0 * cell * kvs2);
+        const char* p1 = reinterpret_cast<const char*>(kh + (long)c1 * cell * kvs2);
+#pragma unroll
+        for (int it = 0; it < KC; ++it)
+            st[it] = *reinterpret_cast<const uint4*>((it < KC / 2 ? p0 : p1) + koff[it]);
+    };
+    auto store_tile = [&](uint16_t* buf) {
+#pragma unroll
+        for (int it = 0; it < KC; ++it) {
+            const int cidx = tid + 256 * it;
+            lds_store16(buf + ksw_off<D>(cidx / (D / 8), cidx % (D / 8)), st[it]);
+        }
+    };
+    const int n_tiles = (n_union + 1) / 2;
+    const float scale_log2 = inv_sqrt_d * 1.4426950408889634f;
+    float* wsb = ws + (long)blockIdx.x * ((u_cap + 15) & ~15) * kTq;   // [slot][query]
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(ks);
+        if (n_tiles > 1) load_tile(1);
+    }
+    for (int u = 0; u < n_tiles; ++u) {
+        __syncthreads();        // tile u is in buffer u % 2; reads of tile u - 1 are done
+        if (u + 1 < n_tiles) {
+            store_tile(ks + ((u + 1) & 1) * (kTileK * D));
+            if (u + 2 < n_tiles) load_tile(u + 2);
+        }
+        const uint16_t* kt = ks + (u & 1) * (kTileK * D);
+        f32x16 sc[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sc[c2][e] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+                sc[c2] = mfma32(as_bf16x8(lds_load16(kt + ksw_off<D>(32 * c2 + (lane & 31),
+                                                                     2 * t + (lane >> 5)))),
+                                qf[t], sc[c2]);
+        // this lane's partial (max, sum) of each cell: 16 of the query's 32 logits
+        float pm[2], pz[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            auto mx = [](float a, float bb) { return __builtin_elementwise_maximum(a, bb); };
+            float m = sc[c2][0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) m = mx(m, sc[c2][e]);
+            const float mb = m * scale_log2;
+            float z0 = __builtin_amdgcn_exp2f(fmaf(sc[c2][0], scale_log2, -mb));
+            float z1 = __builtin_amdgcn_exp2f(fmaf(sc[c2][1], scale_log2, -mb));
+#pragma unroll
+            for (int e = 2; e < 16; e += 2) {
+                z0 += __builtin_amdgcn_exp2f(fmaf(sc[c2][e], scale_log2, -mb));
+                z1 += __builtin_amdgcn_exp2f(fmaf(sc[c2][e + 1], scale_log2, -mb));
+            }
+            pm[c2] = mb;
+            pz[c2] = z0 + z1;
+        }
+        // lanes 0-31 pair up the halves of the first cell, lanes 32-63 of the second
+        const auto sm = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[0]),
+                                                         __float_as_uint(pm[1]), false, false);
+        const auto sz = __builtin_amdgcn_permlane32_swap(__float_as_uint(pz[0]),
+                                                         __float_as_uint(pz[1]), false, false);
+        float m1, z1;
+        lse_merge(__uint_as_float(sm[0]), __uint_as_float(sz[0]), __uint_as_float(sm[1]),
+                  __uint_as_float(sz[1]), m1, z1);
+        const int slot = 2 * u + (lane >> 5);
+        if (slot < n_union) wsb[slot * kTq + qc] = (m1 + __log2f(z1)) * 0.6931471805599453f;
+    }
+    __syncthreads();            // the scores are visible to the whole workgroup
+
+    // ---- per query: exact top-K over its four lanes, 16 queries per round ----
+    const int n = lane & 15, g = lane >> 4;
+    for (int ro = 0; ro < 2; ++ro) {
+        const int qr = 32 * wv + 16 * ro + n;
+        const bool q_ok = qr < n_rows_blk;
+        const long qpos = (long)q_pos0 + t0 + qr;
+        const int n_q = q_ok ? n_candidates(qpos, window, cell, C) : 0;
+        uint32_t kv[NB][4];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int slot = 16 * bb + 4 * g + r;
+                bool ok = slot < n_union && n_q > 0;
+                if (ok) ok = keep ? ((vmask[slot] >> (n_q - n_a)) & 1u) != 0u : slot < n_q;
+                float rr = ok ? wsb[slot * kTq + qr] : 0.f;
+                if (pr.lambda && ok)
+                    rr += prior_term(pr, bh, h, C, qpos, keep ? ulist[slot] : slot, cell);
+                kv[bb][r] = ok ? float_key(rr) : 0u;
+            }
+        const long orow = bh * nq + t0 + (q_ok ? qr : 0);
+        sel_topk_emit<NB>(kv, topk, q_ok, idx + orow * topk,
+                          score ? score + orow * topk : nullptr, keep, ulist, 1.f);
+    }
+}
+
 namespace {
 
 // Top-K over the candidates of every query: eq. 7 scores from kbar, or (rerank)
 // eq. 12 scores from the keys k.  MFMA kernels for bf16 storage when every
 // query's candidates fit the register blocks; row-wise kernels otherwise.
+// Largest candidate list: the keep width, or every cell below the last query's n.
+int largest_candidate_count(const Shape& sh)
+{
+    int n_hi = 0;
+    const long i = (long)sh.q_pos0 + sh.nq - 1;
+    if (i >= sh.w) n_hi = (int)((i - sh.w) / sh.s);
+    return n_hi > sh.C ? sh.C : n_hi;
+}
+
+// Union slots the 128-query reranking kernel provides for (at most five keep rows),
+// in 16-slot blocks.
+int rerank32_slots(const Shape& sh, bool pruned, int keep_w)
+{
+    const int n_hi = largest_candidate_count(sh);
+    const int u_cap = pruned ? (keep_w + 5 < n_hi ? keep_w + 5 : n_hi) : n_hi;
+    return ((u_cap > 0 ? u_cap : 1) + 15) & ~15;
+}
+
 hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const void* k,
                        const Prior& pr, const int32_t* keep, const int32_t* keep_count,
                        int keep_w, int n_lo, int n_rows, int topk, int32_t* idx, float* score,
-                       bool rerank, hipStream_t st)
+                       bool rerank, void* ws, size_t ws_bytes, hipStream_t st)
 {
     if (sh.nq == 0) return hipSuccess;
-    // Largest candidate list: the keep width, or every cell below the last query's n.
-    int n_hi = 0;
-    {
-        long i = (long)sh.q_pos0 + sh.nq - 1;
-        if (i >= sh.w) n_hi = (int)((i - sh.w) / sh.s);
-        if (n_hi > sh.C) n_hi = sh.C;
-    }
+    const int n_hi = largest_candidate_count(sh);
     const float inv_sqrt_d = 1.0f / sqrtf((float)sh.d);
+    // reranking addresses a cell's rows with 32-bit byte offsets
+    const bool offs_ok = !rerank || ((int64_t)(sh.s - 1) * sh.kvs[2] + sh.d) * 2 < (1ll << 31);
+    if (rerank && ws && ws_bytes >= rerank_ws_bytes(sh, keep != nullptr, keep_w)) {
+        const int uc = rerank32_slots(sh, keep != nullptr, keep_w);
+        const int kw = keep ? keep_w : 0;
+        const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, kw, true, 5).bytes
+                                      : sel_layout<128>(n_hi, uc, kw, true, 5).bytes;
+        if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks &&
+            offs_ok) {
+            dim3 grid((unsigned)((sh.nq + 127) / 128 * sh.B * sh.H));
+            const int nb_need = uc / 16;
+#define FS_RERANK32(D, NB)                                                                      \
+            hipLaunchKernelGGL((rerank32_kernel<D, NB>), grid, dim3(256), lds, st,              \
+                               (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2],                 \
+                               (const uint16_t*)k, sh.kvs[0], sh.kvs[1], sh.kvs[2], pr, sh.H,    \
+                               sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,            \
+                               keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d,     \
+                               static_cast<float*>(ws), idx, score)
+#define FS_RERANK32_NB(D)                                                                       \
+            if (nb_need <= 2) { FS_RERANK32(D, 2); }                                            \
+            else if (nb_need <= 4) { FS_RERANK32(D, 4); }                                       \
+            else if (nb_need <= 9) { FS_RERANK32(D, 9); }                                       \
+            else if (nb_need <= 17) { FS_RERANK32(D, 17); }                                     \
+            else { FS_RERANK32(D, 33); }
+            if (sh.d == 64) { FS_RERANK32_NB(64) } else { FS_RERANK32_NB(128) }
+#undef FS_RERANK32_NB
+#undef FS_RERANK32
+            return hipGetLastError();
+        }
+    }
     {
         const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
         const int uc = ((u_cap > 0 ? u_cap : 1) + 15) & ~15;     // 16-cell blocks
         const int kw = keep ? keep_w : 0;
         const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, kw, rerank).bytes
                                       : sel_layout<128>(n_hi, uc, kw, rerank).bytes;
-        // reranking addresses a cell's rows with 32-bit byte offsets
-        const bool offs_ok = !rerank || ((int64_t)(sh.s - 1) * sh.kvs[2] + sh.d) * 2 < (1ll << 31);
         if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks &&
             offs_ok) {
             dim3 grid((unsigned)((sh.nq + 63) / 64 * sh.B * sh.H));
@@ -1144,15 +1357,22 @@ hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, cons
                          int n_rows, int topk, int32_t* idx, float* score, hipStream_t st)
 {
     return launch_topk(sh, q, kbar, nullptr, pr, keep, keep_count, keep_w, n_lo, n_rows, topk,
-                       idx, score, false, st);
+                       idx, score, false, nullptr, 0, st);
+}
+
+size_t rerank_ws_bytes(const Shape& sh, bool pruned, int keep_w)
+{
+    const size_t blocks = (size_t)(sh.nq + 127) / 128 * sh.B * sh.H;
+    return blocks * rerank32_slots(sh, pruned, keep_w) * 128 * sizeof(float);
 }
 
 hipError_t launch_rerank(const Shape& sh, const void* q, const void* k, const Prior& pr,
                          const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
-                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st)
+                         int n_rows, int topk, int32_t* idx, float* score, void* ws,
+                         size_t ws_bytes, hipStream_t st)
 {
     return launch_topk(sh, q, nullptr, k, pr, keep, keep_count, keep_w, n_lo, n_rows, topk, idx,
-                       score, true, st);
+                       score, true, ws, ws_bytes, st);
 }
 
 }  // namespace fs

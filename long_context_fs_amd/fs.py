@@ -19,7 +19,7 @@ CELL = 32
 
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
            "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
-           "fs_combine", "fs_rerank_topk", "fs_stream_state_size", "fs_stream_reset",
+           "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size", "fs_stream_state_size", "fs_stream_reset",
            "fs_stream_step", "fs_status_string", "fs_last_error")
 
 
@@ -64,7 +64,9 @@ def load(path: str | None = None):
         "fs_prune_rows": [P, C.POINTER(i32), C.POINTER(i32)],
         "fs_prune_prefix": [P, vp, i32, i32, vp, vp, vp],
         "fs_select_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp],
-        "fs_rerank_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp],
+        "fs_rerank_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, C.c_size_t,
+                           vp],
+        "fs_rerank_workspace_size": [P, i32, C.POINTER(C.c_size_t)],
         "fs_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_window_attn": [P, vp, vp, vp, f32, vp, C.c_size_t, vp, vp],
         "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
@@ -157,12 +159,24 @@ def fs_select_topk(prob, q, kbar, keep, keep_count, keep_width, topk, idx, score
 
 
 def fs_rerank_topk(prob, q, k, keep, keep_count, keep_width, topk, idx, score=None,
-                   stream=None, prior=None):
-    """Eq. 12 reranking + top-K; prior: None or (amax, lambda, sigma) device tensors."""
+                   stream=None, prior=None, workspace=None):
+    """Eq. 12 reranking + top-K; prior: None or (amax, lambda, sigma) device tensors;
+    workspace: None, or a device buffer of >= fs_rerank_workspace_size bytes."""
     amax, lam, sig = prior if prior is not None else (None, None, None)
+    ws, nbytes = (None, 0) if workspace is None else \
+        (_p(workspace), workspace.numel() * workspace.element_size())
     _check("fs_rerank_topk", load().fs_rerank_topk(C.byref(prob), _p(q), _p(k), _p(amax), _p(lam),
                                                    _p(sig), _p(keep), _p(keep_count), keep_width,
-                                                   topk, _p(idx), _p(score), _s(stream)))
+                                                   topk, _p(idx), _p(score), ws, nbytes,
+                                                   _s(stream)))
+
+
+def fs_rerank_workspace_size(prob, keep_width) -> int:
+    """keep_width: the keep rows' width, 0 without pruning."""
+    n = C.c_size_t()
+    _check("fs_rerank_workspace_size",
+           load().fs_rerank_workspace_size(C.byref(prob), int(keep_width), C.byref(n)))
+    return n.value
 
 
 def fs_workspace_size(prob) -> int:

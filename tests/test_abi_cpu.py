@@ -129,11 +129,17 @@ def test_call_specific_limits(lib):
         assert b"workspace" in lib.fs_last_error()
     # reranking validates like selection, and needs the keys
     assert lib.fs_rerank_topk(C.byref(p), FAKE, None, None, None, None, None, None, 0, 8, FAKE,
-                              None, None) == 1
+                              None, None, 0, None) == 1
     assert lib.fs_rerank_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 65, FAKE,
-                              None, None) == 2
+                              None, None, 0, None) == 2
     assert lib.fs_rerank_topk(C.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, None, 0, 8, FAKE,
-                              None, None) == 1
+                              None, None, 0, None) == 1
+    assert lib.fs_rerank_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 8, FAKE,
+                              None, C.c_void_p(0x1008), 1 << 20, None) == 1
+    assert b"aligned" in lib.fs_last_error()
+    rw = C.c_size_t()
+    assert lib.fs_rerank_workspace_size(C.byref(p), -1, C.byref(rw)) == 1
+    assert lib.fs_rerank_workspace_size(C.byref(p), 0, None) == 1
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 10000.0, FAKE, 16, FAKE, None) == 1
     assert b"workspace" in lib.fs_last_error()
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 0.5, FAKE, 1 << 30, FAKE, None) == 1

@@ -249,16 +249,21 @@ def test_small_sparse(name):
     assert (got[none] == 0).all()
 
 
-def run_rerank(wl, x):
-    """GPU eq. 12 reranking with the forward's own summaries and keep rows."""
+def run_rerank(wl, x, workspace=False):
+    """GPU eq. 12 reranking with the forward's own summaries and keep rows (with a
+    workspace: the 128-query kernel where the problem allows it)."""
     from long_context_fs_amd import fs as fsb
     q, k = (to_dev(x[n], wl.dtype) for n in ("q", "k"))
     fwd = FsForward.for_workload(wl)
     fwd(q, k, to_dev(x["v"], wl.dtype), torch.from_numpy(x["alpha"]).cuda())
     idx = torch.full_like(fwd.idx, -7)
     score = torch.zeros_like(fwd.score)
+    ws = None
+    if workspace:
+        nb = fsb.fs_rerank_workspace_size(fwd.prob, fwd.keep_w if fwd.keep is not None else 0)
+        ws = torch.full((max(nb, 1) // 4 + 1,), float("nan"), device="cuda")
     fsb.fs_rerank_topk(fwd.prob, q, k, fwd.keep, fwd.keep_count, fwd.keep_w, wl.topk, idx, score,
-                       None, fwd.prior)
+                       None, fwd.prior, workspace=ws)
     torch.cuda.synchronize()
     g = dict(n_lo=fwd.n_lo, n_rows=fwd.n_rows, idx=idx.cpu().numpy(), score=score.cpu().numpy(),
              amax=fwd.amax.cpu().numpy())
@@ -297,21 +302,25 @@ def check_rerank(wl, x, g, rows):
 @pytest.mark.parametrize("name", ["bf16_d64_scaled_ragged", "bf16_d128_needle", "bf16_d128_decode",
                                   "bf16_d64_noprune_bigk", "bf16_d128_prior", "f32_d64_noprune",
                                   "f32_d64_prior_noprune"])
-def test_small_rerank(name):
-    """Token-level reranking (eq. 12) against the oracle on every query row."""
+@pytest.mark.parametrize("workspace", [False, True])
+def test_small_rerank(name, workspace):
+    """Token-level reranking (eq. 12) against the oracle on every query row, by the
+    64-query kernel (no workspace) and the 128-query kernel (scores in the workspace)."""
     wl = SMALL[name]
     x = synth.generate(wl)
-    g = run_rerank(wl, x)
+    g = run_rerank(wl, x, workspace)
     ties = check_rerank(wl, x, g, all_rows(wl))
     assert ties <= max(2, len(all_rows(wl)) // 200)
 
 
 @pytest.mark.parametrize("name", ["prefill_b1h8_n65536_d128_bf16", "decode_b1h8_n262144_q256_d128_bf16"])
-def test_full_size_rerank_sampled(name):
-    """Eq. 12 at full size, in the benchmark's launch configuration, on sampled rows."""
+@pytest.mark.parametrize("workspace", [False, True])
+def test_full_size_rerank_sampled(name, workspace):
+    """Eq. 12 at full size, in the benchmark's launch configuration (with the
+    workspace), and without a workspace, on sampled rows."""
     wl = synth.WORKLOADS[name]
     x = synth.generate(wl)
-    g = run_rerank(wl, x)
+    g = run_rerank(wl, x, workspace)
     rng = np.random.default_rng(3)
     rows = [(0, int(h), int(t)) for h, t in zip(rng.integers(0, wl.heads, 48),
                                                 rng.integers(0, wl.n_q, 48))]
