@@ -119,7 +119,9 @@ fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* 
  * fs_rerank_workspace_size(problem, keep ? keep_width : 0) lets bf16 problems
  * score 128 queries per workgroup with the scores held there; a smaller or NULL
  * workspace uses a 64-query kernel that needs none.  The result does not depend
- * on it.  Calls sharing one workspace on different streams race. */
+ * on it.  The 128-query kernel halves the workgroups: pass a workspace when
+ * ceil(n_q / 128) B H is at least the device's compute-unit count, none for
+ * short query ranges.  Calls sharing one workspace on different streams race. */
 fs_status fs_rerank_topk(const fs_problem* problem, const void* q, const void* k,
                          const float* amax, const float* prior_lambda, const float* prior_sigma,
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
