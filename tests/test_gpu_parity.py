@@ -47,6 +47,12 @@ SMALL = {
         n_ctx=700, n_q=700, window=704),
     "bf16_d64_window0": W["prefill_b2h16_n4096_d64_bf16"].replace(
         batch=1, heads=1, n_ctx=900, n_q=900, window=0, budget=5, topk=2),
+    # contexts without a complete cell (C = 0), and with one cell (K > candidates)
+    "f32_d64_no_cells": W["prefill_b1h1_n2048_d64_f32"].replace(n_ctx=20, n_q=20),
+    "bf16_d128_no_cells": W["prefill_b2h16_n4096_d64_bf16"].replace(
+        batch=1, heads=2, n_ctx=20, n_q=20, head_dim=128),
+    "bf16_d64_one_cell": W["prefill_b2h16_n4096_d64_bf16"].replace(
+        batch=1, heads=2, n_ctx=45, n_q=45, window=0, budget=3, topk=2),
     # eq. 7's position prior, on the MFMA (bf16, pruned) and row-wise (fp32, unpruned) paths
     "bf16_d128_prior": W["prefill_b1h8_n65536_d128_bf16_prior"].replace(
         heads=2, n_ctx=2900, n_q=2900, budget=16, topk=8, prior_lambda=0.3, prior_sigma=300.0),
@@ -506,3 +512,38 @@ def test_exact_ties_go_to_larger_cell():
             if gap == 0.0 or gap >= 1e-5:
                 np.testing.assert_array_equal(np.sort(sel), np.sort(want), err_msg=f"h{h} t{t}")
     assert n_tie_rows > 1000
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_query_range_writes_nothing(dtype):
+    """n_q = 0: every call succeeds and leaves its outputs untouched (pointers to
+    one-element sentinels stand in for the empty q, o and index arrays)."""
+    from long_context_fs_amd import fs as fsb
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dt = fsb.FS_BF16 if dtype == "bf16" else fsb.FS_F32
+    B, H, N, d = 1, 2, 4096, 64
+    p = fsb.problem(B, H, d, N, 0, N, 512, dt)
+    assert fsb.fs_prune_rows(p) == (0, 0)
+    gen = torch.Generator().manual_seed(5)
+    k = torch.randn((B, H, N, d), generator=gen).to(tdt).cuda()
+    v = torch.randn((B, H, N, d), generator=gen).to(tdt).cuda()
+    C_ = N // 32
+    kbar = torch.empty((B, H, C_, d), device="cuda")
+    amax = torch.empty((B, H, C_), device="cuda")
+    fsb.fs_cell_summaries(p, k, kbar, amax)            # the summaries do not depend on n_q
+    sent = lambda dt_: torch.full((16,), 7, dtype=dt_, device="cuda")  # noqa: E731
+    q, o_sr, o_lr, o = sent(tdt), sent(tdt), sent(tdt), sent(tdt)
+    keep, keep_count, idx = sent(torch.int32), sent(torch.int32), sent(torch.int32)
+    score = sent(torch.float32)
+    alpha = torch.ones(H, device="cuda")
+    fsb.fs_prune_prefix(p, amax, 0, 8, keep, keep_count)
+    fsb.fs_select_topk(p, q, kbar, keep, keep_count, 8, 4, idx, score)
+    fsb.fs_select_topk(p, q, kbar, None, None, 0, 4, idx, score)
+    fsb.fs_rerank_topk(p, q, k, keep, keep_count, 8, 4, idx, score)
+    ws = torch.empty(max(fsb.fs_workspace_size(p), 1), dtype=torch.uint8, device="cuda")
+    fsb.fs_window_attn(p, q, k, v, 10000.0, ws, o_sr)
+    fsb.fs_sparse_attn(p, q, k, v, idx, 4, 1e-6, o_lr)
+    fsb.fs_combine(p, o_sr, o_lr, alpha, o)
+    torch.cuda.synchronize()
+    for t in (q, o_sr, o_lr, o, keep, keep_count, idx, score):
+        assert (t.float().cpu() == 7).all()
