@@ -53,6 +53,13 @@ SMALL = {
         batch=1, heads=2, n_ctx=20, n_q=20, head_dim=128),
     "bf16_d64_one_cell": W["prefill_b2h16_n4096_d64_bf16"].replace(
         batch=1, heads=2, n_ctx=45, n_q=45, window=0, budget=3, topk=2),
+    # the largest K (64) and keep rows wider than the MFMA kernels' register blocks
+    # (row-wise selection and reranking for bf16)
+    "bf16_d64_wide_keep_k64": W["prefill_b2h16_n4096_d64_bf16"].replace(
+        batch=1, heads=2, n_ctx=24000, n_q=200, q_pos0=23800, budget=700, topk=64),
+    "bf16_d128_wide_keep_k64": W["prefill_b2h16_n4096_d64_bf16"].replace(
+        batch=1, heads=2, n_ctx=24000, n_q=150, q_pos0=23850, head_dim=128, budget=600,
+        n_recent=40, topk=64),
     # eq. 7's position prior, on the MFMA (bf16, pruned) and row-wise (fp32, unpruned) paths
     "bf16_d128_prior": W["prefill_b1h8_n65536_d128_bf16_prior"].replace(
         heads=2, n_ctx=2900, n_q=2900, budget=16, topk=8, prior_lambda=0.3, prior_sigma=300.0),
@@ -307,7 +314,7 @@ def check_rerank(wl, x, g, rows):
 
 @pytest.mark.parametrize("name", ["bf16_d64_scaled_ragged", "bf16_d128_needle", "bf16_d128_decode",
                                   "bf16_d64_noprune_bigk", "bf16_d128_prior", "f32_d64_noprune",
-                                  "f32_d64_prior_noprune"])
+                                  "f32_d64_prior_noprune", "bf16_d64_wide_keep_k64"])
 @pytest.mark.parametrize("workspace", [False, True])
 def test_small_rerank(name, workspace):
     """Token-level reranking (eq. 12) against the oracle on every query row, by the
