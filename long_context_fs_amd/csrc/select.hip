@@ -41,14 +41,12 @@ __device__ __forceinline__ float key_to_float(uint32_t k)
 // keys share are fixed from the start, and the search stops as soon as exactly K
 // keys reach the candidate (that set is then the top K).  Of the keys equal to
 // thr, the last ones in list order are kept (the lists are ascending in cell
-// index, so ties go to the larger cell).  The chosen entries are written in list
-// order: out_i[pos] = id_of(j), out_s[pos] = the key's value times out_scale;
-// positions from min(K, n_cand) on get -1 / 0.
-template <class IdOf>
+// index, so ties go to the larger cell).  The chosen entries are handed over in
+// list order, emit(pos, j, key) for output position pos = 0 .. min(K, n_cand) - 1;
+// pad(t) is called for the positions t from min(K, n_cand) to K - 1.
+template <class Emit, class Pad>
 __device__ __forceinline__ void row_topk_write(const uint32_t* s_key, int n_cand, int topk,
-                                               int lane, int32_t* __restrict__ out_i,
-                                               float* __restrict__ out_s, float out_scale,
-                                               IdOf id_of)
+                                               int lane, Emit emit, Pad pad)
 {
     const int kq = n_cand < topk ? n_cand : topk;
     // up to 1024 keys are held in registers (0 pads: every finite score's key is
@@ -121,18 +119,11 @@ __device__ __forceinline__ void row_topk_write(const uint32_t* s_key, int n_cand
         const int eq_rank = eq_seen + lanes_below(me);
         const bool kept = in && (kj > thr || (is_eq && eq_rank >= n_eq - need_eq));
         const uint64_t mk = __ballot(kept);
-        if (kept) {
-            const int pos = written + lanes_below(mk);
-            out_i[pos] = id_of(j);
-            if (out_s) out_s[pos] = key_to_float(kj) * out_scale;
-        }
+        if (kept) emit(written + lanes_below(mk), j, kj);
         written += __popcll(mk);
         eq_seen += __popcll(me);
     }
-    for (int t = kq + lane; t < topk; t += kWave) {
-        out_i[t] = -1;
-        if (out_s) out_s[t] = 0.f;
-    }
+    for (int t = kq + lane; t < topk; t += kWave) pad(t);
 }
 
 // eq. 7's prior for the query at position i and cell c of head h (row bh of amax):
@@ -228,9 +219,17 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_topk_kernel(
 
     int32_t* out_i = idx + (bh * nq + row) * (long)topk;
     float* out_s = score ? score + (bh * nq + row) * (long)topk : nullptr;
-    row_topk_write(s_key, n_cand, topk, lane, out_i, out_s,
-                   RERANK || pr.lambda ? 1.f : inv_sqrt_d,
-                   [&](int j) { return cand ? cand[j] : j; });
+    const float out_scale = RERANK || pr.lambda ? 1.f : inv_sqrt_d;
+    row_topk_write(
+        s_key, n_cand, topk, lane,
+        [&](int pos, int j, uint32_t kj) {
+            out_i[pos] = cand ? cand[j] : j;
+            if (out_s) out_s[pos] = key_to_float(kj) * out_scale;
+        },
+        [&](int t) {
+            out_i[t] = -1;
+            if (out_s) out_s[t] = 0.f;
+        });
 }
 
 
@@ -325,11 +324,20 @@ __global__ __launch_bounds__(256) void stream_select_kernel(
     if (!active || tq >= kWave) return;     // the query's first wavefront ranks
     const long orow = (bh * nq + row) * (long)topk;
     const float scale = lambda ? 1.f : inv_sqrt_d;
-    row_topk_write(s_key, n_cand, topk, lane, idx_slot + orow, score ? score + orow : nullptr,
-                   scale, [&](int j) { return s_cand[j]; });
-    if (idx_cell)
-        row_topk_write(s_key, n_cand, topk, lane, idx_cell + orow, nullptr, scale,
-                       [&](int j) { return cell_of[bh * M + s_cand[j]]; });
+    // one search writes the slots (for the readout), the cells and the scores
+    row_topk_write(
+        s_key, n_cand, topk, lane,
+        [&](int pos, int j, uint32_t kj) {
+            const int sl = s_cand[j];
+            idx_slot[orow + pos] = sl;
+            if (idx_cell) idx_cell[orow + pos] = cell_of[bh * M + sl];
+            if (score) score[orow + pos] = key_to_float(kj) * scale;
+        },
+        [&](int t) {
+            idx_slot[orow + t] = -1;
+            if (idx_cell) idx_cell[orow + t] = -1;
+            if (score) score[orow + t] = 0.f;
+        });
 }
 
 hipError_t launch_stream_select(int B, int H, int d, bool bf16, const void* q, const int64_t* qs,
