@@ -142,14 +142,15 @@ __device__ __forceinline__ void win_load(WinStage<D>& st, const uint16_t* __rest
                                          const uint16_t* __restrict__ vh, int64_t kvs2, long kt,
                                          long kv_hi, long i0, int w, const float2* __restrict__ table)
 {
+    // Rows past kv_hi repeat row kv_hi: they lie after every query of the tile, so
+    // the tile is masked and their weights are exactly 0.
     const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < WinStage<D>::KC; ++it) {
         const int c = tid + 256 * it;
         const int kr = c / (D / 8), part = c % (D / 8);
-        const long j = kt + kr;
-        st.k[it] = j <= kv_hi ? *reinterpret_cast<const uint4*>(kh + j * kvs2 + part * 8)
-                              : make_uint4(0, 0, 0, 0);
+        const long j = kt + kr <= kv_hi ? kt + kr : kv_hi;
+        st.k[it] = *reinterpret_cast<const uint4*>(kh + j * kvs2 + part * 8);
     }
     if (tid < 2 * D) {
         // keys 32 grp + 16 hh + 4 g + r (r = 0..3), dims 8 dc .. 8 dc + 7
@@ -157,9 +158,9 @@ __device__ __forceinline__ void win_load(WinStage<D>& st, const uint16_t* __rest
         const int hh = within & 1, g = (within >> 1) & 3, dc = within >> 3;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const long j = kt + 32 * grp + 16 * hh + 4 * g + r;
-            st.v[r] = j <= kv_hi ? *reinterpret_cast<const uint4*>(vh + j * kvs2 + dc * 8)
-                                 : make_uint4(0, 0, 0, 0);
+            const long jr = kt + 32 * grp + 16 * hh + 4 * g + r;
+            const long j = jr <= kv_hi ? jr : kv_hi;
+            st.v[r] = *reinterpret_cast<const uint4*>(vh + j * kvs2 + dc * 8);
         }
     }
 }
@@ -183,7 +184,7 @@ __device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, u
     for (int it = 0; it < WinStage<D>::KC; ++it) {
         const int c = tid + 256 * it;
         const int kr = c / (D / 8), part = c % (D / 8);
-        const long j = kt + kr <= kv_hi ? kt + kr : kv_hi;     // rows past kv_hi hold zeros
+        const long j = kt + kr <= kv_hi ? kt + kr : kv_hi;     // rows past kv_hi repeat it
         const float4* rp = reinterpret_cast<const float4*>(
             table + (j - i0 + w + kTableSlack) * (D / 2) + part * 4);
         const float4 a = rp[0], b = rp[1];
