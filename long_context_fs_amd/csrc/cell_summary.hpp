@@ -14,7 +14,8 @@ namespace fs {
 // per token it touched; a token's norm is finished by a butterfly over the lanes
 // that share the token, then a max over tokens.  kbar_out[0..D) (16-byte
 // aligned) is written by the lanes of the first token row, *amax_out by lane 0.
-template <class E, int D>
+// STREAM: the keys are read once (non-temporal loads, bf16 storage).
+template <class E, int D, bool STREAM = false>
 __device__ __forceinline__ void wave_cell_summary(const typename E::storage* __restrict__ row0,
                                                   int64_t kvs2, float* kbar_out, float* amax_out)
 {
@@ -30,7 +31,20 @@ __device__ __forceinline__ void wave_cell_summary(const typename E::storage* __r
 
     float x[LOADS][EPL];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) load16<E>(base + (int64_t)(it * TPL) * kvs2, x[it]);
+    for (int it = 0; it < LOADS; ++it) {
+        const typename E::storage* p = base + (int64_t)(it * TPL) * kvs2;
+        if constexpr (STREAM && EPL == 8) {
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[it][2 * i] = __uint_as_float(w[i] << 16);
+                x[it][2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        } else {
+            load16<E>(p, x[it]);
+        }
+    }
 
     float sum[EPL];
 #pragma unroll

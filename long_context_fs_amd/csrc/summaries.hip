@@ -6,7 +6,8 @@
 // running sum of its d-slice (the mean is a register sum) and one squared norm
 // per token it touched; the token norm is finished by a butterfly over the
 // lanes that share the token, then a max over tokens.  HBM-bound: every key
-// byte is read once, kbar (fp32) and amax are written once.
+// byte is read once (non-temporal loads for bf16 keys), kbar (fp32) and amax
+// are written once.
 #include "cell_summary.hpp"
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
@@ -23,8 +24,8 @@ __global__ __launch_bounds__(256) void cell_summaries_kernel(
     const int c = (int)(cell_id % C);
     const long bh = cell_id / C;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    wave_cell_summary<E, D>(k + b * kvs0 + h * kvs1 + (int64_t)c * 32 * kvs2, kvs2,
-                            kbar + (bh * C + c) * (long)D, amax + bh * C + c);
+    wave_cell_summary<E, D, true>(k + b * kvs0 + h * kvs1 + (int64_t)c * 32 * kvs2, kvs2,
+                                  kbar + (bh * C + c) * (long)D, amax + bh * C + c);
 }
 
 hipError_t launch_summaries(const Shape& sh, const void* k, float* kbar, float* amax,
