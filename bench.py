@@ -117,7 +117,7 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
             fs.fs_prune_prefix(p, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep, fwd.keep_count)
         mark(2)
         fs.fs_select_topk(p, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, fwd.topk,
-                          fwd.idx, None, None, fwd.prior)
+                          fwd.idx, None, None, fwd.prior, fwd.ws_select)
         mark(3)
         fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)
         mark(4)
@@ -329,7 +329,7 @@ def run_phase(name, phase, reps, torch, fs):
         "prune": lambda: fs.fs_prune_prefix(p, f.amax, f.n_recent, f.budget, f.keep,
                                             f.keep_count),
         "select": lambda: fs.fs_select_topk(p, q, f.kbar, f.keep, f.keep_count, f.keep_w,
-                                            f.topk, f.idx, None, None, f.prior),
+                                            f.topk, f.idx, None, None, f.prior, f.ws_select),
         "rerank": lambda: fs.fs_rerank_topk(p, q, k, f.keep, f.keep_count, f.keep_w, f.topk,
                                             f.idx, None, None, f.prior, rr_ws),
         "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),

@@ -106,7 +106,20 @@ fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t 
 fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* kbar,
                          const float* amax, const float* prior_lambda, const float* prior_sigma,
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
-                         int32_t topk, int32_t* idx, float* score, void* stream);
+                         int32_t topk, int32_t* idx, float* score, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Bytes of the optional workspace of fs_select_topk (keep_width 0: no pruning):
+ * 0 unless the query range is short (bf16, fewer than 256 workgroups of 64
+ * queries) and the candidate union wider than 64 cells; then B H n_q S topk
+ * (int32 cell + float32 key), S = ceil(union / 64) splits.  With such a
+ * workspace (device memory, 256-byte aligned, owned by the caller) the union is
+ * split over S workgroups per query tile, each ranking its 64 cells, and a merge
+ * ranks their top-K lists again by the same keys; without one (NULL or smaller)
+ * a single workgroup ranks the whole union.  The result does not depend on it.
+ * Calls sharing one workspace on different streams race. */
+fs_status fs_select_workspace_size(const fs_problem* problem, int32_t keep_width, int32_t topk,
+                                   size_t* bytes);
 
 /* Token-level reranking and top-K, eq. 12 (section 3.4): the same candidates,
  * prior and selection rule as fs_select_topk, with the score of cell c

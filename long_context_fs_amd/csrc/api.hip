@@ -167,11 +167,14 @@ fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t 
 fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* kbar,
                          const float* amax, const float* prior_lambda, const float* prior_sigma,
                          const int32_t* keep, const int32_t* keep_count, int32_t keep_width,
-                         int32_t topk, int32_t* idx, float* score, void* stream)
+                         int32_t topk, int32_t* idx, float* score, void* workspace,
+                         size_t workspace_bytes, void* stream)
 {
     fs::Shape sh;
     FS_CHECK(check_problem(problem, &sh));
     FS_PTR(q); FS_PTR(kbar);
+    if (workspace && ((uintptr_t)workspace & 255))
+        return fail(FS_ERR_INVALID, "workspace must be 256-byte aligned");
     if (prior_lambda && (!prior_sigma || !amax))
         return fail(FS_ERR_INVALID, "the position prior needs amax, prior_lambda and prior_sigma");
     if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
@@ -188,7 +191,8 @@ fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* 
     }
     const fs::Prior pr{amax, prior_lambda, prior_sigma};
     return from_hip(fs::launch_select(sh, q, kbar, pr, keep, keep_count, keep_width, lo, rows,
-                                      topk, idx, score, (hipStream_t)stream),
+                                      topk, idx, score, workspace,
+                                      workspace ? workspace_bytes : 0, (hipStream_t)stream),
                     "fs_select_topk");
 }
 
@@ -222,6 +226,20 @@ fs_status fs_rerank_topk(const fs_problem* problem, const void* q, const void* k
                                       idx, score, workspace, workspace ? workspace_bytes : 0,
                                       (hipStream_t)stream),
                     "fs_rerank_topk");
+}
+
+fs_status fs_select_workspace_size(const fs_problem* problem, int32_t keep_width, int32_t topk,
+                                   size_t* bytes)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (!bytes) return fail(FS_ERR_INVALID, "bytes is NULL");
+    if (keep_width < 0 || keep_width > 4096)
+        return fail(FS_ERR_INVALID, "keep_width %d outside [0, 4096]", keep_width);
+    if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
+    *bytes = fs::select_ws_bytes(sh, keep_width > 0, keep_width, topk);
+    g_err[0] = 0;
+    return FS_OK;
 }
 
 fs_status fs_rerank_workspace_size(const fs_problem* problem, int32_t keep_width, size_t* bytes)

@@ -30,9 +30,14 @@ struct Prior {
     const float* sigma;
 };
 
+// Selection splits a short query range's union over workgroups when ws_bytes >=
+// select_ws_bytes (their partial top-K lists, merged by a second kernel).
+int select_splits(const Shape& sh, bool pruned, int keep_w);
+size_t select_ws_bytes(const Shape& sh, bool pruned, int keep_w, int topk);
 hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
                          const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
-                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st);
+                         int n_rows, int topk, int32_t* idx, float* score, void* ws,
+                         size_t ws_bytes, hipStream_t st);
 // Reranking keeps each block's (cell, query) scores in a workspace when ws_bytes
 // >= rerank_ws_bytes (pruned: keep != nullptr); otherwise it needs none.
 size_t rerank_ws_bytes(const Shape& sh, bool pruned, int keep_w);

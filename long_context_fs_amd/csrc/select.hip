@@ -565,7 +565,8 @@ template <int NB>
 __device__ __forceinline__ void sel_topk_emit(const uint32_t (&kv)[NB][4], int topk, bool q_ok,
                                               int32_t* __restrict__ out_i, float* __restrict__ out_s,
                                               const int32_t* __restrict__ keep,
-                                              const uint16_t* ulist, float emit_scale)
+                                              const uint16_t* ulist, float emit_scale,
+                                              int slot_base = 0)
 {
     constexpr int kNW = (NB + kFieldsPerWord - 1) / kFieldsPerWord;
     constexpr int kKW = (4 * NB + 31) / 32;                    // kept-key mask words
@@ -690,7 +691,7 @@ __device__ __forceinline__ void sel_topk_emit(const uint32_t (&kv)[NB][4], int t
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if ((km[(4 * bb + r) / 32] >> ((4 * bb + r) % 32)) & 1u) {
-                        const int slot = 16 * bb + 4 * g + r;
+                        const int slot = slot_base + 16 * bb + 4 * g + r;
                         out_i[p] = keep ? ulist[slot] : slot;
                         if (out_s) out_s[p] = key_to_float(kv[bb][r]) * emit_scale;
                         ++p;
@@ -714,7 +715,8 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
     const float* __restrict__ kbar, Prior pr, int H, int BH, int C, int nq, int q_pos0,
     int window, int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
     int keep_w, int n_lo, int n_rows, int topk, int n_hi_all, int u_cap, float inv_sqrt_d,
-    int32_t* __restrict__ idx, float* __restrict__ score)
+    int32_t* __restrict__ idx, float* __restrict__ score, int n_split,
+    int32_t* __restrict__ ws_cell, float* __restrict__ ws_val)
 {
     using namespace mf;
     constexpr int KS = D / 32;
@@ -735,7 +737,10 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
     const TileOfBlock tb = xcd_tile(BH);
     const long bh = tb.bh;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    const long t0 = tb.tile * kTq;
+    // split `split` of n_split scores union slots s_base .. s_base + 16 NB - 1
+    const int split = (int)(tb.tile % n_split);
+    const long t0 = (tb.tile / n_split) * kTq;
+    const int s_base = split * 16 * NB;
     const int n_rows_blk = nq - t0 < kTq ? (int)(nq - t0) : kTq;
     const int n_a = n_candidates((long)q_pos0 + t0, window, cell, C);
     const int n_b = n_candidates((long)q_pos0 + t0 + n_rows_blk - 1, window, cell, C);
@@ -777,10 +782,10 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
         }
     };
     uint32_t kv[NB][4];
-    load_chunk(0);
+    load_chunk(s_base);
 #pragma unroll
     for (int ci = 0; ci < (NB + 1) / 2; ++ci) {
-        const int c0 = ci * kSelChunk;
+        const int c0 = s_base + ci * kSelChunk;
         if (c0 < n_union) {                  // block-uniform
             __syncthreads();                 // previous chunk's MFMA reads are done
 #pragma unroll
@@ -815,7 +820,7 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
             for (int b2 = 0; b2 < 2; ++b2) {
                 const int bb = 2 * ci + b2;
                 if (bb >= NB) break;
-                const int slot0 = 16 * bb;
+                const int slot0 = s_base + 16 * bb;
                 if (slot0 < n_union) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -858,8 +863,56 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
 
     // ---- per query: exact top-K over its four lanes -------------------------
     const long orow = bh * nq + t0 + (q_ok ? qr : 0);
+    if (n_split > 1) {         // this split's top K, with the exact key values, for the merge
+        const long wrow = (orow * n_split + split) * (long)topk;
+        sel_topk_emit<NB>(kv, topk, q_ok, ws_cell + wrow, ws_val + wrow, keep, ulist, 1.f,
+                          s_base);
+        return;
+    }
     sel_topk_emit<NB>(kv, topk, q_ok, idx + orow * topk, score ? score + orow * topk : nullptr,
                       keep, ulist, pr.lambda ? 1.f : inv_sqrt_d);
+}
+
+// Merge of a split selection: per query, the n_split partial top-K lists (cells
+// ascending within a split, splits in ascending slot order, so their valid
+// entries concatenate to an ascending list) ranked again by the same keys.  One
+// wavefront per query, four queries per workgroup.
+__global__ __launch_bounds__(256) void select_merge_kernel(
+    const int32_t* __restrict__ ws_cell, const float* __restrict__ ws_val, long rows, int n_split,
+    int topk, float out_scale, int32_t* __restrict__ idx, float* __restrict__ score)
+{
+    extern __shared__ uint32_t smem[];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + wv;
+    const int cap = n_split * topk;
+    uint32_t* s_key = smem + wv * 2 * cap;
+    int32_t* s_cell = reinterpret_cast<int32_t*>(s_key + cap);
+    if (row >= rows) return;                        // no barrier below: whole waves leave
+    const int32_t* wc = ws_cell + row * cap;
+    const float* wk = ws_val + row * cap;
+    // compact the valid entries (a prefix of each split's list, topk <= 64), in
+    // split order; LDS accesses of one wavefront stay in order
+    int n_valid = 0;
+    for (int sp = 0; sp < n_split; ++sp) {
+        const bool ok = lane < topk && wc[sp * topk + lane] >= 0;
+        if (ok) {
+            s_cell[n_valid + lane] = wc[sp * topk + lane];
+            s_key[n_valid + lane] = float_key(wk[sp * topk + lane]);
+        }
+        n_valid += __popcll(__ballot(ok));
+    }
+    int32_t* out_i = idx + row * topk;
+    float* out_s = score ? score + row * topk : nullptr;
+    row_topk_write(
+        s_key, n_valid, topk, lane,
+        [&](int pos, int j, uint32_t kj) {
+            out_i[pos] = s_cell[j];
+            if (out_s) out_s[pos] = key_to_float(kj) * out_scale;
+        },
+        [&](int t) {
+            out_i[t] = -1;
+            if (out_s) out_s[t] = 0.f;
+        });
 }
 
 // Combine two partial log-sum-exps (m: max logit in log2 units, z: sum of
@@ -1258,6 +1311,15 @@ int rerank32_slots(const Shape& sh, bool pruned, int keep_w)
     return ((u_cap > 0 ? u_cap : 1) + 15) & ~15;
 }
 
+// Union slots the 64-query selection kernel provides for (at most three keep
+// rows), in 16-slot blocks.
+int select_slots(const Shape& sh, bool pruned, int keep_w)
+{
+    const int n_hi = largest_candidate_count(sh);
+    const int u_cap = pruned ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
+    return ((u_cap > 0 ? u_cap : 1) + 15) & ~15;
+}
+
 hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const void* k,
                        const Prior& pr, const int32_t* keep, const int32_t* keep_count,
                        int keep_w, int n_lo, int n_rows, int topk, int32_t* idx, float* score,
@@ -1304,6 +1366,31 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
                                       : sel_layout<128>(n_hi, uc, kw, rerank).bytes;
         if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks &&
             offs_ok) {
+            // short query ranges: the union split over workgroups of 64 slots each,
+            // then a merge of their top-K lists (selection with a workspace only)
+            const int S = !rerank && ws && ws_bytes >= select_ws_bytes(sh, keep != nullptr, keep_w,
+                                                                      topk)
+                              ? select_splits(sh, keep != nullptr, keep_w) : 1;
+            if (S > 1) {
+                int32_t* ws_cell = static_cast<int32_t*>(ws);
+                float* ws_val = reinterpret_cast<float*>(ws_cell + (size_t)sh.B * sh.H * sh.nq * S * topk);
+                dim3 grid_s((unsigned)((sh.nq + 63) / 64 * S * sh.B * sh.H));
+#define FS_SELECT_SPLIT(D)                                                                      \
+                hipLaunchKernelGGL((select_topk_mfma_kernel<D, 4>), grid_s, dim3(256), lds, st, \
+                                   (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,   \
+                                   sh.H, sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,  \
+                                   keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, \
+                                   idx, score, S, ws_cell, ws_val)
+                if (sh.d == 64) { FS_SELECT_SPLIT(64); } else { FS_SELECT_SPLIT(128); }
+#undef FS_SELECT_SPLIT
+                hipError_t err = hipGetLastError();
+                if (err != hipSuccess) return err;
+                const long rows = (long)sh.B * sh.H * sh.nq;
+                hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                                   (size_t)4 * 2 * S * topk * sizeof(uint32_t), st, ws_cell, ws_val,
+                                   rows, S, topk, pr.lambda ? 1.f : inv_sqrt_d, idx, score);
+                return hipGetLastError();
+            }
             dim3 grid((unsigned)((sh.nq + 63) / 64 * sh.B * sh.H));
             const int nb_need = uc / 16;
 #define FS_SELECT_MFMA(D, NB)                                                                   \
@@ -1319,7 +1406,7 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
                                    (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,   \
                                    sh.H, sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,  \
                                    keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, \
-                                   idx, score)
+                                   idx, score, 1, nullptr, nullptr)
 #define FS_SELECT_NB(D)                                                                         \
             if (nb_need <= 2) { FS_SELECT_MFMA(D, 2); }                                         \
             else if (nb_need <= 4) { FS_SELECT_MFMA(D, 4); }                                    \
@@ -1360,12 +1447,28 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
 
 }  // namespace
 
+int select_splits(const Shape& sh, bool pruned, int keep_w)
+{
+    const long blocks = (long)(sh.nq + 63) / 64 * sh.B * sh.H;
+    const int uc = select_slots(sh, pruned, keep_w);
+    if (!sh.bf16 || blocks >= 256 || uc <= 64 || uc > 16 * kSelMaxBlocks) return 1;
+    return (uc + 63) / 64;            // 64 slots (four 16-slot blocks) per split
+}
+
+size_t select_ws_bytes(const Shape& sh, bool pruned, int keep_w, int topk)
+{
+    const int S = select_splits(sh, pruned, keep_w);
+    if (S <= 1) return 0;
+    return (size_t)sh.B * sh.H * sh.nq * S * topk * (sizeof(int32_t) + sizeof(float));
+}
+
 hipError_t launch_select(const Shape& sh, const void* q, const float* kbar, const Prior& pr,
                          const int32_t* keep, const int32_t* keep_count, int keep_w, int n_lo,
-                         int n_rows, int topk, int32_t* idx, float* score, hipStream_t st)
+                         int n_rows, int topk, int32_t* idx, float* score, void* ws,
+                         size_t ws_bytes, hipStream_t st)
 {
     return launch_topk(sh, q, kbar, nullptr, pr, keep, keep_count, keep_w, n_lo, n_rows, topk,
-                       idx, score, false, nullptr, 0, st);
+                       idx, score, false, ws, ws_bytes, st);
 }
 
 size_t rerank_ws_bytes(const Shape& sh, bool pruned, int keep_w)

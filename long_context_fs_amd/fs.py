@@ -19,7 +19,7 @@ CELL = 32
 
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
            "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
-           "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size", "fs_stream_state_size", "fs_stream_reset",
+           "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size", "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
            "fs_stream_step", "fs_status_string", "fs_last_error")
 
 
@@ -63,7 +63,9 @@ def load(path: str | None = None):
         "fs_cell_summaries": [P, vp, vp, vp, vp],
         "fs_prune_rows": [P, C.POINTER(i32), C.POINTER(i32)],
         "fs_prune_prefix": [P, vp, i32, i32, vp, vp, vp],
-        "fs_select_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp],
+        "fs_select_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, C.c_size_t,
+                           vp],
+        "fs_select_workspace_size": [P, i32, i32, C.POINTER(C.c_size_t)],
         "fs_rerank_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, C.c_size_t,
                            vp],
         "fs_rerank_workspace_size": [P, i32, C.POINTER(C.c_size_t)],
@@ -149,13 +151,24 @@ def fs_prune_prefix(prob, amax, n_recent, budget, keep, keep_count, stream=None)
 
 
 def fs_select_topk(prob, q, kbar, keep, keep_count, keep_width, topk, idx, score=None,
-                   stream=None, prior=None):
-    """prior: None, or (amax, lambda, sigma) device tensors for eq. 7's position prior."""
+                   stream=None, prior=None, workspace=None):
+    """prior: None, or (amax, lambda, sigma) device tensors for eq. 7's position prior;
+    workspace: None, or a device buffer of >= fs_select_workspace_size bytes."""
     amax, lam, sig = prior if prior is not None else (None, None, None)
+    ws, nbytes = (None, 0) if workspace is None else \
+        (_p(workspace), workspace.numel() * workspace.element_size())
     _check("fs_select_topk", load().fs_select_topk(C.byref(prob), _p(q), _p(kbar), _p(amax),
                                                    _p(lam), _p(sig), _p(keep), _p(keep_count),
-                                                   keep_width, topk, _p(idx), _p(score),
-                                                   _s(stream)))
+                                                   keep_width, topk, _p(idx), _p(score), ws,
+                                                   nbytes, _s(stream)))
+
+
+def fs_select_workspace_size(prob, keep_width, topk) -> int:
+    """keep_width: the keep rows' width, 0 without pruning."""
+    n = C.c_size_t()
+    _check("fs_select_workspace_size",
+           load().fs_select_workspace_size(C.byref(prob), int(keep_width), int(topk), C.byref(n)))
+    return n.value
 
 
 def fs_rerank_topk(prob, q, k, keep, keep_count, keep_width, topk, idx, score=None,
@@ -245,6 +258,8 @@ class FsForward:
         self.ws = torch.empty(fs_workspace_size(self.prob), dtype=torch.uint8, device=device)
         nsp = fs_sparse_workspace_size(self.prob)
         self.ws_sparse = torch.empty(nsp, dtype=torch.uint8, device=device) if nsp else None
+        nsel = fs_select_workspace_size(self.prob, self.keep_w, topk)
+        self.ws_select = torch.empty(nsel, dtype=torch.uint8, device=device) if nsel else None
         self.o_sr = torch.empty((B, H, n_q, d), dtype=tdt, device=device)
         self.o_lr = torch.empty_like(self.o_sr)
         self.o = torch.empty_like(self.o_sr)
@@ -263,7 +278,8 @@ class FsForward:
             fs_prune_prefix(p, self.amax, self.n_recent, self.budget, self.keep, self.keep_count,
                             stream)
         fs_select_topk(p, q, self.kbar, self.keep, self.keep_count, self.keep_w, self.topk,
-                       self.idx, self.score if keep_score else None, stream, self.prior)
+                       self.idx, self.score if keep_score else None, stream, self.prior,
+                       self.ws_select)
         fs_window_attn(p, q, k, v, self.rope_base, self.ws, self.o_sr, stream)
         fs_sparse_attn(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_lr, self.ws_sparse,
                        stream)

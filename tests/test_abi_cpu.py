@@ -73,6 +73,14 @@ def test_prune_rows_and_workspace_host_only(lib):
     assert ws == table + 2 * 4096 * 8 * (64 * 4 + 8)
     # enough queries to fill the device: the table alone
     assert fs.fs_workspace_size(_prob(batch=8, heads=16, n_q=4096)) == table
+    # selection splits a short query range's union over 64-cell workgroups: 256
+    # queries of 2 heads, keep rows of 500 cells -> union up to 503 -> 512 slots, 8 splits
+    dec = _prob(n_ctx=65536, n_q=256, q_pos0=65536 - 256)
+    assert fs.fs_select_workspace_size(dec, 500, 32) == 2 * 256 * 8 * 32 * 8
+    assert fs.fs_select_workspace_size(dec, 40, 32) == 0           # union of 48 slots
+    assert fs.fs_select_workspace_size(_prob(batch=8, heads=16), 500, 32) == 0   # 2048 tiles
+    assert fs.fs_select_workspace_size(_prob(dtype=fs.FS_F32, n_ctx=65536, n_q=256,
+                                             q_pos0=65536 - 256), 500, 32) == 0
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -106,17 +114,23 @@ def test_call_specific_limits(lib):
     assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 5000, FAKE, FAKE, None) == 2
     assert lib.fs_prune_prefix(C.byref(p), FAKE, -1, 4, FAKE, FAKE, None) == 2
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 0, FAKE,
-                              None, None) == 2
+                              None, None, 0, None) == 2
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 65, FAKE,
-                              None, None) == 2
+                              None, None, 0, None) == 2
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, FAKE, None, 64, 8, FAKE,
-                              None, None) == 1
+                              None, None, 0, None) == 1
     # the prior needs all three of amax, lambda and sigma
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, FAKE, FAKE, None, None, 0, 8, FAKE,
-                              None, None) == 1
+                              None, None, 0, None) == 1
     assert b"prior" in lib.fs_last_error()
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, 0, 8, FAKE,
-                              None, None) == 1
+                              None, None, 0, None) == 1
+    assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 8, FAKE,
+                              None, C.c_void_p(0x1010), 1 << 20, None) == 1
+    assert b"aligned" in lib.fs_last_error()
+    sw = C.c_size_t()
+    assert lib.fs_select_workspace_size(C.byref(p), 0, 0, C.byref(sw)) == 2
+    assert lib.fs_select_workspace_size(C.byref(p), -1, 8, C.byref(sw)) == 1
     assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, None, 8, 1e-6, None, 0, FAKE,
                               None) == 1
     assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, -1.0, None, 0, FAKE,
@@ -146,7 +160,7 @@ def test_call_specific_limits(lib):
     assert lib.fs_combine(C.byref(p), FAKE, FAKE, None, FAKE, None) == 1
     big = _prob(n_ctx=1 << 20, n_q=1 << 20)              # 32752 candidate cells, no pruning
     assert lib.fs_select_topk(C.byref(big), FAKE, FAKE, None, None, None, None, None, 0, 8, FAKE,
-                              None, None) == 2
+                              None, None, 0, None) == 2
 
 
 def test_status_strings(lib):

@@ -60,6 +60,14 @@ SMALL = {
     "bf16_d128_wide_keep_k64": W["prefill_b2h16_n4096_d64_bf16"].replace(
         batch=1, heads=2, n_ctx=24000, n_q=150, q_pos0=23850, head_dim=128, budget=600,
         n_recent=40, topk=64),
+    # short query ranges whose candidate unions selection splits over workgroups
+    "bf16_d128_decode_wide": W["decode_b1h8_n262144_q256_d128_bf16"].replace(
+        heads=2, n_ctx=9000, n_q=77, q_pos0=9000 - 77, budget=200, topk=16, needle_queries=77),
+    "bf16_d64_decode_noprune": W["prefill_b2h16_n4096_d64_bf16"].replace(
+        batch=1, heads=2, n_ctx=5000, n_q=60, q_pos0=5000 - 60, budget=-1, topk=12),
+    "bf16_d128_decode_prior": W["decode_b1h8_n262144_q256_d128_bf16"].replace(
+        heads=2, n_ctx=7000, n_q=70, q_pos0=7000 - 70, budget=100, topk=8, needle_queries=70,
+        prior_lambda=0.3, prior_sigma=400.0),
     # eq. 7's position prior, on the MFMA (bf16, pruned) and row-wise (fp32, unpruned) paths
     "bf16_d128_prior": W["prefill_b1h8_n65536_d128_bf16_prior"].replace(
         heads=2, n_ctx=2900, n_q=2900, budget=16, topk=8, prior_lambda=0.3, prior_sigma=300.0),
@@ -554,3 +562,31 @@ def test_empty_query_range_writes_nothing(dtype):
     torch.cuda.synchronize()
     for t in (q, o_sr, o_lr, o, keep, keep_count, idx, score):
         assert (t.float().cpu() == 7).all()
+
+
+@pytest.mark.parametrize("name", ["bf16_d128_decode_wide", "bf16_d64_decode_noprune",
+                                  "bf16_d128_decode_prior"])
+def test_split_selection_equals_unsplit(name):
+    """Selection with its workspace (the union split over workgroups, top-K lists
+    merged) gives the same cells and the same scores, bit for bit, as one
+    workgroup over the whole union: every slot's key is the same arithmetic."""
+    from long_context_fs_amd import fs as fsb
+    wl, x, g, ref = small_case(name)
+    fwd = FsForward.for_workload(wl)
+    assert fwd.ws_select is not None              # the case takes the split path
+    q = to_dev(x["q"], wl.dtype)
+    k = to_dev(x["k"], wl.dtype)
+    fsb.fs_cell_summaries(fwd.prob, k, fwd.kbar, fwd.amax)
+    if fwd.pruned:
+        fsb.fs_prune_prefix(fwd.prob, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep,
+                            fwd.keep_count)
+    out = []
+    for ws in (None, fwd.ws_select):
+        idx = torch.full_like(fwd.idx, -7)
+        score = torch.full_like(fwd.score, float("nan"))
+        fsb.fs_select_topk(fwd.prob, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, wl.topk,
+                           idx, score, None, fwd.prior, ws)
+        torch.cuda.synchronize()
+        out.append((idx.cpu().numpy(), score.cpu().numpy()))
+    np.testing.assert_array_equal(out[0][0], out[1][0])
+    np.testing.assert_array_equal(out[0][1], out[1][1])
