@@ -75,7 +75,11 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
             const uint32_t cand = thr | (1u << bit);
             int cnt = 0;
             for (int c = tid; c < n; c += kPruneThreads) cnt += key[c] >= cand;
-            if (block_sum(cnt, red) >= budget) thr = cand;
+            const int total = block_sum(cnt, red);        // block-uniform
+            if (total >= budget) {
+                thr = cand;
+                if (total == budget) break;               // exactly the top budget reach it
+            }
         }
         int gt = 0, eq = 0;
         for (int c = tid; c < n; c += kPruneThreads) {
@@ -182,13 +186,18 @@ __global__ __launch_bounds__(kPruneThreads) void prune_reg_kernel(
             top = 31 - __clz(diff);
             thr = top >= 31 ? 0u : (o_all & ~((2u << top) - 1u));
         }
-        // largest thr with #{c < n : key_c >= thr} >= budget, i.e. the budget-th largest key
+        // largest thr with #{c < n : key_c >= thr} >= budget, i.e. the budget-th largest
+        // key; once exactly `budget` keys reach a candidate, they are the top budget
         for (int bit = top; bit >= 0; --bit) {
             const uint32_t cand = thr | (1u << bit);
             int c = 0;
 #pragma unroll
             for (int j = 0; j < KPT; ++j) c += __popcll(__ballot(kv[j] >= cand));   // kv = 0 past n, cand >= 1
-            if (bsum(c) >= budget) thr = cand;
+            const int total = bsum(c);                    // block-uniform
+            if (total >= budget) {
+                thr = cand;
+                if (total == budget) break;
+            }
         }
         int gt = 0, eq = 0;
 #pragma unroll
