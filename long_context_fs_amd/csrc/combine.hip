@@ -1,6 +1,6 @@
 // combine.hip -- range separation (FreeSolo summary, section 3.1, eq. 2):
 // o_i = o_sr_i + alpha_h * o_lr_i.  Elementwise and HBM-bound: 16-byte loads
-// and stores, one vector per thread.
+// (non-temporal for bf16) and stores, one vector per thread.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 
@@ -24,8 +24,21 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int64_t off = b * os0 + h * os1 + row * os2 + e0;
     const float a = alpha[h];
     float x[EPL], y[EPL], z[EPL];
-    load16<E>(o_sr + off, x);
-    load16<E>(o_lr + off, y);
+    if constexpr (EPL == 8) {          // bf16: both branch outputs are read once
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 wx = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o_sr + off));
+        const u32x4 wy = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o_lr + off));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(wx[i] << 16);
+            x[2 * i + 1] = __uint_as_float(wx[i] & 0xFFFF0000u);
+            y[2 * i] = __uint_as_float(wy[i] << 16);
+            y[2 * i + 1] = __uint_as_float(wy[i] & 0xFFFF0000u);
+        }
+    } else {
+        load16<E>(o_sr + off, x);
+        load16<E>(o_lr + off, y);
+    }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) z[e] = fmaf(a, y[e], x[e]);
     store16<E>(o + off, z);
