@@ -423,8 +423,8 @@ def main():
         write_traffic(*args.write_traffic, copy_mib=args.copy_mib or 1024)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
-              "Heads and batch shard across GPUs with no communication; that path is not built.",
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported. "
+              "Heads and batch shard across GPUs with no communication; that path is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 
