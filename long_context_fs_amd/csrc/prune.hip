@@ -11,8 +11,9 @@
 //
 // Rows of up to 8192 candidates keep their keys in registers (cell 256 j + t in
 // slot j of thread t): one pass over HBM, one barrier per search step, the
-// search starts below the bits every key shares, and the output positions come
-// from one round of per-wave ballot counts.  Longer rows use the streaming
+// search starts below the bits every key shares and stops once exactly P keys
+// reach the candidate, and the output positions come from one round of per-wave
+// ballot counts.  Longer rows use the streaming
 // kernel below it.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"

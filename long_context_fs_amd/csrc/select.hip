@@ -1,5 +1,7 @@
 // select.hip -- cell scoring and per-query top-K (FreeSolo summary, section 3.3,
-// eq. 7 with lambda_h = 0; the selected set S_i of eq. 9).
+// eq. 7, with its position prior when lambda is given; the selected set S_i of
+// eq. 9), token-level reranking (section 3.4, eq. 12), and the selection over a
+// streaming state's cell pool.
 //
 // One wavefront per query row.  The unrotated query is staged in LDS; each lane
 // scores candidate cells c (from the keep row of the query's candidate count,
@@ -21,7 +23,13 @@
 // The K-th largest key is found by a bitwise search over those four lanes
 // (gfx950 row swaps for the sums), starting below the bits all valid keys share
 // and stopping once exactly K keys reach the candidate; the chosen cells are
-// written in slot order from packed prefix counts over the four lanes.
+// written in slot order from packed prefix counts over the four lanes.  For
+// short query ranges the union can be split over workgroups of 64 slots, whose
+// top-K lists a merge kernel ranks again.
+//
+// Reranking (eq. 12) scores each candidate cell by the log-sum-exp of its 32
+// token logits: 32x32x16 MFMA over two-cell key tiles for 128 queries per
+// workgroup (scores through a caller workspace), or 16x16x32 for 64 queries.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 #include "mfma_tile.hpp"

@@ -10,7 +10,7 @@
 // union slots.  It then streams the union two cells (64 keys) at a time through
 // LDS, exactly like the window kernel's key tiles, and each wave runs the
 // flash tile for its 32 queries with the mask "query selected this cell"
-// (a per-query pointer walk over its slot list).  q and k are the exact bf16
+// (a per-query bitmap over the union slots).  q and k are the exact bf16
 // inputs (no rotation), so S^T = K Q^T is exact-product bf16 MFMA.  Epilogue:
 // divide by the softmax sum, RMSNorm over d with a 4-lane reduction, store.
 // f32 storage (or when the union bookkeeping would not fit in 64 KiB of LDS):

@@ -19,6 +19,9 @@
 // softmax in fp32 (exp2 with log2(e)/sqrt(d) folded into the scale), and
 // accumulates O^T += V^T P^T with P rounded to bf16.  The next tile's global
 // loads are issued before the current tile's MFMAs (register double buffer).
+// When the query tiles alone would leave the chip idle (decode), a tile's key
+// range is split over workgroups whose partial (max, sum, O) states the
+// readout's merge kernel combines.
 // f32 storage: one wavefront per query, all in fp32.
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
