@@ -110,6 +110,47 @@ int or_forward(const or_problem* p, const float* q, const float* k, const float*
                const float* alpha, double* o, double* o_sr, double* o_lr,
                int* sel, int* n_sel, double* sel_gap, double* keep_gap, int nthreads);
 
+
+/* ---- FS-B: causal forests and beam search (section 3.4, eqs. 10-11) ------
+ * Readings and the decision precision are stated in fsb_oracle.c.  A forest
+ * is built over one head's fp32 cell summaries; the caller allocates every
+ * array: cell_of [C], prefix [C + 1], first / amax / rho [2C], mu [2C * d]. */
+typedef struct {
+    int n_cells, head_dim;
+    int m;                 /* admitted cells (leaves) */
+    int n_levels;          /* levels 0 .. n_levels - 1 */
+    int level_start[32];   /* node (l, j) is node level_start[l] + j */
+    int* cell_of;          /* leaf j -> cell, ascending */
+    int* prefix;           /* prefix[n] = admitted cells among cells 0 .. n-1 */
+    int* first;            /* node -> its first cell */
+    float* amax;           /* node -> A_v */
+    float* rho;            /* node -> rho_v */
+    float* mu;             /* node -> mu_v [d] */
+} or_forest;
+
+/* Dot product of two d-vectors (d a multiple of 16) in the fixed fp64 order. */
+double or_dot16(const float* a, const float* b, int d);
+
+/* Builds the forest of the cells with amax >= tau (use_tau), or of every cell;
+ * returns the number of leaves. */
+int or_forest_build(const float* kbar, const float* amax, int n_cells, int d, int use_tau,
+                    double tau, or_forest* f);
+
+/* Roots (level, index) covering the first n_leaves leaves, largest first. */
+int or_forest_roots(const or_forest* f, int n_leaves, int* level, int* index);
+
+/* U_v of node (level, index) for the query at position i of head `head` (eq. 11);
+ * q_norm = sqrt(or_dot16(q, q)). */
+double or_node_score(const or_problem* p, int head, long long i, const float* q_row,
+                     double q_norm, const or_forest* f, int level, int index, double slack);
+
+/* S_i of the query at position i: beam search of width `beam` in f0 and ftau
+ * (either may be NULL), then the best min(K, |found|) by eq. 7's score, in
+ * descending (score, cell) order.  Returns the count. */
+int or_beam_row(const or_problem* p, int head, long long i, const float* q_row,
+                const or_forest* f0, const or_forest* ftau, int beam, double slack,
+                int* sel, double* score);
+
 #ifdef __cplusplus
 }
 #endif

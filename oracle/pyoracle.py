@@ -14,14 +14,16 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "fs_oracle.c")
+FSB_SRC_PATH = os.path.join(_HERE, "fsb_oracle.c")
 
 
 def build(force: bool = True) -> str:
-    """Compile fs_oracle.c with gcc into liboracle.so (plain -O2, no fast-math)."""
+    """Compile fs_oracle.c and fsb_oracle.c with gcc into liboracle.so (plain -O2,
+    no fast-math, no fp contraction)."""
     if force or not os.path.exists(LIB_PATH):
         tmp = LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall",
-                               "-o", tmp, SRC_PATH, "-lm", "-lpthread"])
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-Wall", "-o", tmp, SRC_PATH, FSB_SRC_PATH, "-lm", "-lpthread"])
         os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
@@ -84,6 +86,42 @@ def _i32(x):
     return np.ascontiguousarray(x, dtype=np.int32)
 
 
+class _ForestStruct(C.Structure):
+    _fields_ = [("n_cells", C.c_int), ("head_dim", C.c_int), ("m", C.c_int),
+                ("n_levels", C.c_int), ("level_start", C.c_int * 32),
+                ("cell_of", C.c_void_p), ("prefix", C.c_void_p), ("first", C.c_void_p),
+                ("amax", C.c_void_p), ("rho", C.c_void_p), ("mu", C.c_void_p)]
+
+
+class Forest:
+    """One FS-B causal forest of one head (section 3.4), with numpy views of its
+    node arrays: node (l, j) is row level_start[l] + j."""
+
+    def __init__(self, n_cells: int, d: int):
+        n = max(n_cells, 1)
+        self.cell_of = np.zeros(n, np.int32)
+        self.prefix = np.zeros(n + 1, np.int32)
+        self.first = np.zeros(2 * n, np.int32)
+        self.amax = np.zeros(2 * n, np.float32)
+        self.rho = np.zeros(2 * n, np.float32)
+        self.mu = np.zeros((2 * n, d), np.float32)
+        self.s = _ForestStruct(n_cells, d, 0, 0, (C.c_int * 32)(),
+                               self.cell_of.ctypes.data, self.prefix.ctypes.data,
+                               self.first.ctypes.data, self.amax.ctypes.data,
+                               self.rho.ctypes.data, self.mu.ctypes.data)
+
+    @property
+    def m(self) -> int:
+        return self.s.m
+
+    @property
+    def n_levels(self) -> int:
+        return self.s.n_levels
+
+    def node(self, level: int, index: int) -> int:
+        return self.s.level_start[level] + index
+
+
 class Oracle:
     def __init__(self, path: str | None = None):
         path = path or LIB_PATH
@@ -117,7 +155,62 @@ class Oracle:
                                       C.c_int]
         L.or_forward.argtypes = [P, _F32P, _F32P, _F32P, _F32P, _F64P, _F64P, _F64P,
                                  _I32P, _I32P, _F64P, _F64P, C.c_int]
+        FP = C.POINTER(_ForestStruct)
+        L.or_dot16.argtypes = [_F32P, _F32P, C.c_int]
+        L.or_dot16.restype = C.c_double
+        L.or_forest_build.argtypes = [_F32P, _F32P, C.c_int, C.c_int, C.c_int, C.c_double, FP]
+        L.or_forest_build.restype = C.c_int
+        L.or_forest_roots.argtypes = [FP, C.c_int, _I32P, _I32P]
+        L.or_forest_roots.restype = C.c_int
+        L.or_node_score.argtypes = [P, C.c_int, C.c_longlong, _F32P, C.c_double, FP, C.c_int,
+                                    C.c_int, C.c_double]
+        L.or_node_score.restype = C.c_double
+        L.or_beam_row.argtypes = [P, C.c_int, C.c_longlong, _F32P, C.c_void_p, C.c_void_p,
+                                  C.c_int, C.c_double, _I32P, _F64P]
+        L.or_beam_row.restype = C.c_int
         self.L = L
+
+    # -- FS-B (section 3.4) ---------------------------------------------------
+    def dot16(self, a, b) -> float:
+        a, b = _f32(a), _f32(b)
+        return self.L.or_dot16(a, b, a.shape[0])
+
+    def forest_build(self, kbar, amax, tau: float | None = None) -> Forest:
+        """Forest over one head's fp32 summaries: every cell (tau None, A^0) or the
+        cells with amax >= tau (A^tau, eq. 10)."""
+        kbar, amax = _f32(kbar), _f32(amax)
+        n_cells, d = kbar.shape
+        f = Forest(n_cells, d)
+        self.L.or_forest_build(kbar if n_cells else np.zeros((1, d), np.float32),
+                               amax if n_cells else np.zeros(1, np.float32), n_cells, d,
+                               0 if tau is None else 1, 0.0 if tau is None else float(tau),
+                               C.byref(f.s))
+        return f
+
+    def forest_roots(self, f: Forest, n_leaves: int):
+        lv = np.zeros(32, np.int32)
+        ix = np.zeros(32, np.int32)
+        cnt = self.L.or_forest_roots(C.byref(f.s), int(n_leaves), lv, ix)
+        return list(zip(lv[:cnt].tolist(), ix[:cnt].tolist()))
+
+    def node_score(self, p: Problem, head: int, i: int, q_row, f: Forest, level: int,
+                   index: int, slack: float) -> float:
+        q = _f32(q_row)
+        qn = float(np.sqrt(self.dot16(q, q)))
+        return self.L.or_node_score(C.byref(p), int(head), int(i), q, qn, C.byref(f.s),
+                                    int(level), int(index), float(slack))
+
+    def beam_row(self, p: Problem, head: int, i: int, q_row, f0: Forest | None,
+                 ftau: Forest | None, beam: int, slack: float):
+        """S_i of the query at position i by beam search (eqs. 10-11), with its eq. 7
+        scores, in descending (score, cell) order."""
+        sel = np.zeros(max(p.topk, 1), np.int32)
+        sc = np.zeros(max(p.topk, 1), np.float64)
+        cnt = self.L.or_beam_row(C.byref(p), int(head), int(i), _f32(q_row),
+                                 None if f0 is None else C.addressof(f0.s),
+                                 None if ftau is None else C.addressof(ftau.s),
+                                 int(beam), float(slack), sel, sc)
+        return sel[:cnt].copy(), sc[:cnt].copy()
 
     # -- single steps ------------------------------------------------------
     def rope(self, p: Problem, x, pos: int) -> np.ndarray:

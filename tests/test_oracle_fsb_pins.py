@@ -1,0 +1,192 @@
+"""Pins of the FS-B oracle (FreeSolo paper summary, picx.dev page, section 3.4,
+eqs. 10-11) against facts that do not come from the oracle itself.
+
+- hand-worked searches on a four-cell forest (tests/golden/fsb_hand_cases.json);
+- a beam wide enough to keep every node reduces the search to an exhaustive
+  top-K, which must equal the FS-L oracle's eq. 7 selection over C_i (and,
+  for the admitted forest, a brute-force top-K over {c in C_i : a_c >= tau});
+- node statistics against their definitions computed by numpy;
+- with slack 1, U_v bounds the eq. 7 score of every cell below v (Cauchy-
+  Schwarz and the monotone erf), so the bound must hold for every node;
+- the roots of a prefix are its binary decomposition;
+- the fixed-order dot product against an exact rational sum.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import make_problem, with_prior
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fsb_hand_cases.json")
+
+
+def _summaries(rng, n_cells, d):
+    kbar = (rng.standard_normal((n_cells, d)) * 0.25).astype(np.float32)
+    amax = (8.0 + 2.0 * rng.random(n_cells)).astype(np.float32)
+    return kbar, amax
+
+
+def test_golden_fsb(orc):
+    g = json.load(open(GOLDEN))
+    d = 16
+    kbar = np.zeros((4, d), np.float32)
+    kbar[:, 0] = g["kbar0"]
+    q = np.zeros(d, np.float32)
+    q[0] = 1.0
+    for case in g["cases"]:
+        p = make_problem(head_dim=d, n_ctx=4 * 32, window=512, topk=case["topk"])
+        am = np.array(case["tau_amax"] or [1, 1, 1, 1], np.float32)
+        f0 = None if case.get("tau_only") else orc.forest_build(kbar, am)
+        ft = None if case["tau"] is None else orc.forest_build(kbar, am, case["tau"])
+        sel, sc = orc.beam_row(p, 0, g["query_pos"], q, f0, ft, case["beam"], case["slack"])
+        assert sel.tolist() == case["sel"], case["why"]
+        np.testing.assert_allclose(sc, case["score"], rtol=0, atol=1e-12)
+
+
+def test_golden_forest_stats(orc):
+    g = json.load(open(GOLDEN))
+    kbar = np.zeros((4, 16), np.float32)
+    kbar[:, 0] = g["kbar0"]
+    f = orc.forest_build(kbar, np.ones(4, np.float32))
+    assert (f.m, f.n_levels) == (4, 3)
+    assert f.mu[f.node(1, 0), 0] == 0 and f.rho[f.node(1, 0)] == 5
+    assert f.mu[f.node(1, 1), 0] == 4 and f.rho[f.node(1, 1)] == 0
+    assert f.mu[f.node(2, 0), 0] == 2 and f.rho[f.node(2, 0)] == 7
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 7, 8, 13, 64, 100, 1023])
+def test_roots_are_binary_decomposition(orc, n):
+    kbar, amax = _summaries(np.random.default_rng(1), 1024, 16)
+    f = orc.forest_build(kbar, amax)
+    roots = orc.forest_roots(f, n)
+    sizes = [1 << lv for lv, _ in roots]
+    assert sizes == [1 << b for b in reversed(range(11)) if (n >> b) & 1]
+    start = 0
+    for lv, ix in roots:   # aligned, disjoint, covering [0, n) in order
+        assert ix << lv == start
+        start += 1 << lv
+    assert start == n
+
+
+def test_node_statistics_match_definitions(orc):
+    rng = np.random.default_rng(2)
+    kbar, amax = _summaries(rng, 77, 64)
+    for tau in (None, 9.0):
+        f = orc.forest_build(kbar, amax, tau)
+        cells = np.arange(77) if tau is None else np.nonzero(amax >= tau)[0]
+        assert f.m == len(cells) and f.cell_of[:f.m].tolist() == cells.tolist()
+        assert f.prefix.tolist() == [int(np.sum(cells < n)) for n in range(78)]
+        for lv in range(f.n_levels):
+            for j in range(f.m >> lv):
+                leaves = cells[j << lv:(j + 1) << lv]
+                v = f.node(lv, j)
+                mean = kbar[leaves].astype(np.float64).mean(axis=0)
+                np.testing.assert_allclose(f.mu[v], mean, rtol=1e-6, atol=1e-7)
+                dist = np.linalg.norm(kbar[leaves].astype(np.float64) - f.mu[v].astype(np.float64),
+                                      axis=1).max()
+                assert abs(f.rho[v] - dist) <= 1e-6 * max(dist, 1e-3)
+                assert f.amax[v] == amax[leaves].max()
+                assert f.first[v] == leaves[0]
+
+
+def test_dot16_exact_for_integers(orc):
+    rng = np.random.default_rng(3)
+    for d in (16, 64, 128):
+        a = rng.integers(-1000, 1000, d).astype(np.float32)
+        b = rng.integers(-1000, 1000, d).astype(np.float32)
+        assert orc.dot16(a, b) == float(sum(Fraction(int(x)) * int(y) for x, y in zip(a, b)))
+        x = rng.standard_normal(d).astype(np.float32)
+        y = rng.standard_normal(d).astype(np.float32)
+        exact = sum(Fraction(float(u)) * Fraction(float(w)) for u, w in zip(x, y))
+        assert abs(orc.dot16(x, y) - float(exact)) <= 1e-13 * float(sum(abs(Fraction(float(u)) * Fraction(float(w))) for u, w in zip(x, y)))
+
+
+def _wide_problem(n_cells, d, topk, prior):
+    p = make_problem(head_dim=d, n_ctx=n_cells * 32, window=512, topk=topk, heads=1)
+    if prior:
+        with_prior(p, [0.05], [900.0])
+    return p
+
+
+@pytest.mark.parametrize("prior", [False, True])
+def test_exhaustive_beam_equals_eq7_topk(orc, prior):
+    """A beam that never drops a node finds every leaf, so S_i is eq. 7's top-K
+    over C_i: compared with the FS-L oracle's selection (sets and scores)."""
+    rng = np.random.default_rng(4)
+    n_cells, d, topk = 150, 64, 12
+    kbar, amax = _summaries(rng, n_cells, d)
+    p = _wide_problem(n_cells, d, topk, prior)
+    f0 = orc.forest_build(kbar, amax)
+    for _ in range(25):
+        i = int(rng.integers(512, 512 + 32 * n_cells + 40))
+        q = rng.standard_normal(d).astype(np.float32)
+        n = orc.n_candidates(p, i)
+        sel, sc = orc.beam_row(p, 0, i, q, f0, None, 2 * n_cells, 0.0)
+        ref, _, ref_sc = orc.select_row_at(p, 0, i, q, kbar.astype(np.float64),
+                                           amax.astype(np.float64), np.arange(n, dtype=np.int32))
+        assert sorted(sel.tolist()) == sorted(ref.tolist())
+        np.testing.assert_allclose(sc, np.sort(ref_sc)[::-1][:len(sc)], rtol=1e-12, atol=1e-12)
+        assert np.all(np.diff(sc) <= 0)
+
+
+def test_exhaustive_admitted_forest_brute_force(orc):
+    rng = np.random.default_rng(5)
+    n_cells, d, topk, tau = 120, 64, 10, 9.2
+    kbar, amax = _summaries(rng, n_cells, d)
+    p = _wide_problem(n_cells, d, topk, False)
+    ft = orc.forest_build(kbar, amax, tau)
+    f0 = orc.forest_build(kbar, amax)
+    for _ in range(20):
+        i = int(rng.integers(512, 512 + 32 * n_cells))
+        q = rng.standard_normal(d).astype(np.float32)
+        n = orc.n_candidates(p, i)
+        scores = kbar[:n].astype(np.float64) @ q.astype(np.float64) / 8.0
+        adm = np.nonzero(amax[:n] >= tau)[0]
+        sel, _ = orc.beam_row(p, 0, i, q, None, ft, 2 * n_cells, 0.0)
+        assert sorted(sel.tolist()) == sorted(adm[np.argsort(-scores[adm])][:topk].tolist())
+        # both forests, exhaustive: the admitted cells are a subset, so eq. 7 over C_i
+        sel2, _ = orc.beam_row(p, 0, i, q, f0, ft, 2 * n_cells, 0.0)
+        assert sorted(sel2.tolist()) == sorted(np.argsort(-scores)[:topk].tolist())
+
+
+@pytest.mark.parametrize("prior", [False, True])
+def test_slack_one_bounds_every_leaf(orc, prior):
+    """Eq. 11 with c = 1: q.mu + |q| rho >= q.kbar_c (Cauchy-Schwarz) and
+    A_v g(i - p_min) >= a_c g(i - p_c) (erf increasing, g >= 0 on C_i)."""
+    rng = np.random.default_rng(6)
+    n_cells, d = 64, 64
+    kbar, amax = _summaries(rng, n_cells, d)
+    p = _wide_problem(n_cells, d, 8, prior)
+    f = orc.forest_build(kbar, amax)
+    i = 512 + 32 * n_cells
+    for _ in range(5):
+        q = rng.standard_normal(d).astype(np.float32)
+        leaf = [orc.node_score(p, 0, i, q, f, 0, j, 1.0) for j in range(f.m)]
+        for lv in range(1, f.n_levels):
+            for j in range(f.m >> lv):
+                u = orc.node_score(p, 0, i, q, f, lv, j, 1.0)
+                assert u >= max(leaf[j << lv:(j + 1) << lv]) - 1e-12
+        # a leaf's U is eq. 7's score
+        _, _, ref = orc.select_row_at(p, 0, i, q, kbar.astype(np.float64),
+                                      amax.astype(np.float64), np.arange(n_cells, dtype=np.int32))
+        np.testing.assert_allclose(leaf, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_empty_and_narrow(orc):
+    rng = np.random.default_rng(7)
+    kbar, amax = _summaries(rng, 40, 64)
+    p = _wide_problem(40, 64, 8, False)
+    f0 = orc.forest_build(kbar, amax)
+    q = rng.standard_normal(64).astype(np.float32)
+    sel, _ = orc.beam_row(p, 0, 100, q, f0, None, 8, 1.0)        # i < w: C_i empty
+    assert len(sel) == 0
+    sel, _ = orc.beam_row(p, 0, 512 + 32 * 3, q, f0, None, 8, 1.0)   # n_i = 3 < K
+    assert sorted(sel.tolist()) == [0, 1, 2]
+    ft = orc.forest_build(kbar, amax, 100.0)                     # nothing admitted
+    assert ft.m == 0
+    sel, _ = orc.beam_row(p, 0, 512 + 32 * 40, q, None, ft, 8, 1.0)
+    assert len(sel) == 0

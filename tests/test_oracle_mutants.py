@@ -67,8 +67,9 @@ def test_pins_kill_mutant(tmp_path, name, old, new, occ):
     c_path.write_text(mutated)
     (tmp_path / "fs_oracle.h").write_text(open(os.path.join(ROOT, "oracle", "fs_oracle.h")).read())
     lib = tmp_path / "liboracle_mut.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", str(lib),
-                           str(c_path), "-lm", "-lpthread"])
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fPIC", "-shared", "-o", str(lib),
+                           str(c_path), os.path.join(ROOT, "oracle", "fsb_oracle.c"), "-I",
+                           str(tmp_path), "-lm", "-lpthread"])
     env = dict(os.environ, ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
