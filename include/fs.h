@@ -15,6 +15,8 @@
  *   fs_stream_*        eqs. 2-9 from a bounded per-head state ("Bounded memory",
  *                      Practical Implications): decode or chunked prefill
  *   fs_combine         eq. 2   o = o_sr + alpha_h * o_lr
+ *   fs_forest_*, fs_beam_select  eqs. 10-11  FS-B: causal forests over the cell
+ *                      summaries and beam search for S_i (section 3.4)
  *
  * Readings of what the page leaves open (fixed here, identical in the oracle):
  *   - candidates of the query at position i are the complete cells whose last
@@ -147,6 +149,52 @@ fs_status fs_rerank_topk(const fs_problem* problem, const void* q, const void* k
  * cell without pruning). */
 fs_status fs_rerank_workspace_size(const fs_problem* problem, int32_t keep_width,
                                    size_t* bytes);
+
+/* ---- FS-B, section 3.4 (eqs. 10-11) -------------------------------------------
+ * The page gives the admitted sets (eq. 10) and the node score (eq. 11) only;
+ * the readings fixed here (identical in the oracle):
+ *   - a causal forest over a sequence of cells is the set of complete, aligned
+ *     power-of-two blocks: node (l, j) covers leaves j 2^l .. (j+1) 2^l - 1 and
+ *     has children (l-1, 2j), (l-1, 2j+1); a prefix of n leaves is covered by
+ *     one root per set bit of n.  Forest 0 holds every complete cell (A^0); a
+ *     forest built with tau holds the cells with amax >= tau_h, ascending (A^tau).
+ *     Query i searches the part of each forest that lies in C_i (cells < n_i);
+ *   - mu_v = mean of the node's cell means, rho_v = the largest distance from
+ *     mu_v to one of them, A_v = the largest amax, p_v^min = centre of the first
+ *     cell.  With slack 1 and lambda_h >= 0, U_v bounds eq. 7's score of every
+ *     cell below v;
+ *   - beam search of width `beam` per forest: start from the best `beam` roots;
+ *     each step replaces every inner node by its two children, keeps leaves and
+ *     retains the best `beam` by U; stop when only leaves remain.  S_i is the
+ *     best min(topk, #found) cells of both final beams by eq. 7's score (a
+ *     leaf's U), written ascending like fs_select_topk.  Ties: larger U, then the
+ *     later block (larger cell), then the lower level.
+ * U is computed in fp64 from the fp32 node statistics in one fixed order (dot
+ * products as 16 contiguous partial sums added pairwise at distances 8, 4, 2,
+ * 1), so the search's decisions are reproducible.
+ *
+ * Forest storage: fs_forest_size bytes of device memory (256-byte aligned, owned
+ * by the caller) per forest, covering every (b, h); its layout is private to the
+ * library.  Both calls accept at most 32768 cells. */
+fs_status fs_forest_size(const fs_problem* problem, size_t* bytes);
+
+/* Builds one forest per (b, h) from kbar [B][H][C][d] and amax [B][H][C] (float32,
+ * as written by fs_cell_summaries).  tau: NULL for forest 0 (every cell), or
+ * float32 [H] thresholds for the admitted forest (amax >= tau_h).  Overwrites
+ * `forest`; nothing else is read or written. */
+fs_status fs_forest_build(const fs_problem* problem, const float* kbar, const float* amax,
+                          const float* tau, void* forest, void* stream);
+
+/* S_i by beam search (eq. 11) in forest0 and/or forest_tau (either may be NULL,
+ * not both; each built for this problem's shape).  beam in [1, 64], slack c >= 0
+ * (finite), topk in [1, 64].  prior_lambda, prior_sigma: both NULL (no prior) or
+ * float32 [H] (lambda_h >= 0, sigma_h > 0, not checked).  idx: int32
+ * [B][H][n_q][topk], ascending, -1 padded; score (nullable): float32 eq. 7
+ * score aligned with idx (0 for padding). */
+fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* forest0,
+                         const void* forest_tau, int32_t beam, float slack,
+                         const float* prior_lambda, const float* prior_sigma, int32_t topk,
+                         int32_t* idx, float* score, void* stream);
 
 /* Bytes of device workspace for fs_window_attn: its RoPE cos/sin table, then room
  * for the partial states with which a short query range (decode) splits each

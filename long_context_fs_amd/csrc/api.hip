@@ -254,6 +254,55 @@ fs_status fs_rerank_workspace_size(const fs_problem* problem, int32_t keep_width
     return FS_OK;
 }
 
+fs_status fs_forest_size(const fs_problem* problem, size_t* bytes)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (!bytes) return fail(FS_ERR_INVALID, "bytes is NULL");
+    if (sh.C > 32768) return fail(FS_ERR_UNSUPPORTED, "FS-B forests hold at most 32768 cells");
+    *bytes = fs::forest_bytes(sh);
+    return FS_OK;
+}
+
+fs_status fs_forest_build(const fs_problem* problem, const float* kbar, const float* amax,
+                          const float* tau, void* forest, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (sh.C > 32768) return fail(FS_ERR_UNSUPPORTED, "FS-B forests hold at most 32768 cells");
+    FS_PTR(kbar);
+    if (!amax) return fail(FS_ERR_INVALID, "amax is NULL");
+    if (!forest || ((uintptr_t)forest & 255))
+        return fail(FS_ERR_INVALID, "forest must be non-NULL and 256-byte aligned");
+    return from_hip(fs::launch_forest_build(sh, kbar, amax, tau, forest, (hipStream_t)stream),
+                    "fs_forest_build");
+}
+
+fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* forest0,
+                         const void* forest_tau, int32_t beam, float slack,
+                         const float* prior_lambda, const float* prior_sigma, int32_t topk,
+                         int32_t* idx, float* score, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (sh.C > 32768) return fail(FS_ERR_UNSUPPORTED, "FS-B forests hold at most 32768 cells");
+    FS_PTR(q);
+    if (!forest0 && !forest_tau) return fail(FS_ERR_INVALID, "both forests are NULL");
+    if (((uintptr_t)forest0 & 255) || ((uintptr_t)forest_tau & 255))
+        return fail(FS_ERR_INVALID, "forests must be 256-byte aligned");
+    if (beam < 1 || beam > 64) return fail(FS_ERR_UNSUPPORTED, "beam %d outside [1, 64]", beam);
+    if (!(slack >= 0.f) || slack > 3.0e38f)
+        return fail(FS_ERR_INVALID, "slack must be finite and >= 0");
+    if (prior_lambda && !prior_sigma)
+        return fail(FS_ERR_INVALID, "the position prior needs prior_lambda and prior_sigma");
+    if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
+    if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
+    return from_hip(fs::launch_beam_select(sh, q, forest0, forest_tau, beam, (double)slack,
+                                           prior_lambda, prior_lambda ? prior_sigma : nullptr,
+                                           topk, idx, score, (hipStream_t)stream),
+                    "fs_beam_select");
+}
+
 fs_status fs_workspace_size(const fs_problem* problem, size_t* bytes)
 {
     fs::Shape sh;

@@ -93,4 +93,14 @@ hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* 
                               const void* v, const float* alpha, const float* lambda,
                               const float* sigma, void* o, int32_t* idx_cell, hipStream_t st);
 
+// FS-B (section 3.4): forest storage of all (b, h), its construction, and the
+// beam search writing S_i like launch_select (ascending cells, -1 padded).
+size_t forest_bytes(const Shape& sh);
+hipError_t launch_forest_build(const Shape& sh, const float* kbar, const float* amax,
+                               const float* tau, void* forest, hipStream_t st);
+hipError_t launch_beam_select(const Shape& sh, const void* q, const void* forest0,
+                              const void* forest_tau, int beam, double slack,
+                              const float* prior_lambda, const float* prior_sigma, int topk,
+                              int32_t* idx, float* score, hipStream_t st);
+
 }  // namespace fs

@@ -20,7 +20,8 @@ CELL = 32
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
            "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
            "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size", "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
-           "fs_stream_step", "fs_status_string", "fs_last_error")
+           "fs_stream_step", "fs_forest_size", "fs_forest_build", "fs_beam_select",
+           "fs_status_string", "fs_last_error")
 
 
 class FsError(RuntimeError):
@@ -74,6 +75,9 @@ def load(path: str | None = None):
         "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, C.c_size_t, vp, vp],
         "fs_combine": [P, vp, vp, vp, vp, vp],
+        "fs_forest_size": [P, C.POINTER(C.c_size_t)],
+        "fs_forest_build": [P, vp, vp, vp, vp, vp],
+        "fs_beam_select": [P, vp, vp, vp, i32, f32, vp, vp, i32, vp, vp, vp],
         "fs_stream_state_size": [C.POINTER(FsStreamConfig), C.POINTER(C.c_size_t)],
         "fs_stream_reset": [C.POINTER(FsStreamConfig), vp, C.c_size_t, vp],
         "fs_stream_step": [C.POINTER(FsStreamConfig), vp, C.c_size_t, C.c_int64, i32, vp, vp,
@@ -190,6 +194,30 @@ def fs_rerank_workspace_size(prob, keep_width) -> int:
     _check("fs_rerank_workspace_size",
            load().fs_rerank_workspace_size(C.byref(prob), int(keep_width), C.byref(n)))
     return n.value
+
+
+def fs_forest_size(prob) -> int:
+    """Bytes of one FS-B forest (every (b, h)) for this problem's shape."""
+    n = C.c_size_t()
+    _check("fs_forest_size", load().fs_forest_size(C.byref(prob), C.byref(n)))
+    return n.value
+
+
+def fs_forest_build(prob, kbar, amax, forest, tau=None, stream=None):
+    """FS-B forest (eq. 10) into `forest` (a device buffer of fs_forest_size bytes,
+    256-byte aligned): every cell when tau is None, else the cells with amax >= tau[h]."""
+    _check("fs_forest_build", load().fs_forest_build(C.byref(prob), _p(kbar), _p(amax), _p(tau),
+                                                     _p(forest), _s(stream)))
+
+
+def fs_beam_select(prob, q, forest0, forest_tau, beam, slack, topk, idx, score=None,
+                   prior=None, stream=None):
+    """FS-B beam search (eq. 11) for S_i; prior: None or (lambda, sigma) device tensors."""
+    lam, sig = prior if prior is not None else (None, None)
+    _check("fs_beam_select", load().fs_beam_select(C.byref(prob), _p(q), _p(forest0),
+                                                   _p(forest_tau), int(beam), float(slack),
+                                                   _p(lam), _p(sig), int(topk), _p(idx),
+                                                   _p(score), _s(stream)))
 
 
 def fs_workspace_size(prob) -> int:

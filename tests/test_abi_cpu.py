@@ -210,3 +210,42 @@ def test_stream_step_arguments_rejected(lib):
     assert step(FAKE, need, 0, 4, lam=FAKE) == 1                 # prior arrays go together
     assert step(FAKE, need, 0, 4, q=C.c_void_p((1 << 20) + 2)) == 1
     assert lib.fs_stream_reset(C.byref(cfg), FAKE, need - 1, None) == 1
+
+
+def test_fsb_arguments_rejected(lib):
+    """FS-B calls validate on the host and launch nothing on error."""
+    p = _prob()
+    fs_ = C.c_size_t()
+    assert lib.fs_forest_size(C.byref(p), C.byref(fs_)) == 0 and fs_.value > 0
+    big = _prob(n_ctx=1 << 21, n_q=1)                    # 65536 cells
+    assert lib.fs_forest_size(C.byref(big), C.byref(fs_)) == 2
+    assert lib.fs_forest_size(C.byref(p), None) == 1
+    F = C.c_void_p(1 << 20)                                # 256-byte aligned stand-in
+    assert lib.fs_forest_build(C.byref(p), FAKE, FAKE, None, C.c_void_p((1 << 20) + 16),
+                               None) == 1
+    assert b"256-byte" in lib.fs_last_error()
+    assert lib.fs_forest_build(C.byref(p), FAKE, None, None, F, None) == 1
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, None, 8, 1.0, None, None, 8, FAKE,
+                              None, None) == 1
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 0, 1.0, None, None, 8, FAKE, None,
+                              None) == 2
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 65, 1.0, None, None, 8, FAKE, None,
+                              None) == 2
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, -1.0, None, None, 8, FAKE, None,
+                              None) == 1
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, float("nan"), None, None, 8, FAKE,
+                              None, None) == 1
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, FAKE, None, 8, FAKE, None,
+                              None) == 1
+    assert b"prior" in lib.fs_last_error()
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, None, None, 65, FAKE, None,
+                              None) == 2
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, None, None, 8, None, None,
+                              None) == 1
+    # forest storage grows with the number of cells and holds their node statistics
+    small, large = C.c_size_t(), C.c_size_t()
+    lib.fs_forest_size(C.byref(_prob(n_ctx=4096, n_q=1)), C.byref(small))
+    lib.fs_forest_size(C.byref(_prob(n_ctx=8192, n_q=1)), C.byref(large))
+    n_cells = 8192 // 32                                   # 2 heads, 2 n_cells - 1 nodes, d 64
+    assert large.value > small.value >= 2 * (2 * n_cells // 2 - 1) * 64 * 4
+    assert large.value >= 2 * (2 * n_cells - 1) * 64 * 4

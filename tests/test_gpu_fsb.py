@@ -1,0 +1,237 @@
+"""GPU parity of FS-B (FreeSolo summary, picx.dev page, section 3.4, eqs. 10-11)
+against the CPU oracle (oracle/fsb_oracle.c).
+
+The forest statistics and the beam search's scores are defined in one fixed
+fp64 order on both sides, so the search takes the same decisions: node
+statistics must be bit-identical, the selected cells identical, and the eq. 7
+scores equal as float32 (within one ulp where the prior's erf enters).  Inputs:
+seeded q and keys from synth; the cell summaries are the oracle's eq. 5 values
+rounded to float32 and given to both sides.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from long_context_fs_amd import fs, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def forest_layout(C, d):
+    """Byte layout of one (b, h) forest, as the library lays it out."""
+    lev_off, nodes, lv = [], 0, 0
+    while lv < 16 and (C >> lv) > 0:
+        lev_off.append(nodes)
+        nodes += C >> lv
+        lv += 1
+    up = lambda x: (x + 255) & ~255  # noqa: E731
+    off = 256
+    L = {"lev_off": lev_off, "nodes": nodes, "prefix": off}
+    off = up(off + 4 * (C + 1))
+    L["first"] = off
+    off = up(off + 4 * nodes)
+    L["amax"] = off
+    off = up(off + 4 * nodes)
+    L["rho"] = off
+    off = up(off + 4 * nodes)
+    L["mu"] = off
+    L["stride"] = up(off + 4 * nodes * d)
+    return L
+
+
+def decode_forest(buf: np.ndarray, L, bh, C, d):
+    r = buf[bh * L["stride"]:(bh + 1) * L["stride"]]
+    n = L["nodes"]
+    return {"m": int(r[:4].view(np.int32)[0]),
+            "prefix": r[L["prefix"]:L["prefix"] + 4 * (C + 1)].view(np.int32),
+            "first": r[L["first"]:L["first"] + 4 * n].view(np.int32),
+            "amax": r[L["amax"]:L["amax"] + 4 * n].view(np.float32),
+            "rho": r[L["rho"]:L["rho"] + 4 * n].view(np.float32),
+            "mu": r[L["mu"]:L["mu"] + 4 * n * d].view(np.float32).reshape(n, d)}
+
+
+def make_inputs(wl, tau_q=0.7, seed=None):
+    """q (numpy, storage values), kbar/amax float32 [B, H, C, (d)] from the oracle's
+    eq. 5, and per-head thresholds tau (float32 quantiles of amax)."""
+    inp = synth.generate(wl, seed)
+    orc = oracle.Oracle()
+    p = oracle.problem_from(wl)
+    B, H, C, d = wl.batch, wl.heads, wl.n_cells, wl.head_dim
+    kbar = np.zeros((B, H, max(C, 1), d), np.float32)[:, :, :C]
+    amax = np.zeros((B, H, max(C, 1)), np.float32)[:, :, :C]
+    for b in range(B):
+        for h in range(H):
+            kb, am = orc.cell_summaries_head(p, inp["k"][b, h])
+            kbar[b, h], amax[b, h] = kb.astype(np.float32), am.astype(np.float32)
+    tau = np.array([np.quantile(amax[0, h], tau_q) if C else 0.0 for h in range(H)], np.float32)
+    return inp, np.ascontiguousarray(kbar), np.ascontiguousarray(amax), tau
+
+
+def gpu_fsb(wl, inp, kbar, amax, tau, beam, slack, use0=True, use_tau=True, prior=None):
+    prob = fs.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, wl.n_q, wl.q_pos0, wl.window,
+                      fs.FS_BF16 if wl.dtype == "bf16" else fs.FS_F32)
+    nbytes = fs.fs_forest_size(prob)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(inp["q"]).to("cuda").to(dt)
+    kb = torch.from_numpy(kbar).cuda()
+    am = torch.from_numpy(amax).cuda()
+    f0 = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if use0 else None
+    ft = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if use_tau else None
+    if use0:
+        fs.fs_forest_build(prob, kb, am, f0)
+    if use_tau:
+        fs.fs_forest_build(prob, kb, am, ft, tau=torch.from_numpy(tau).cuda())
+    B, H, K = wl.batch, wl.heads, wl.topk
+    idx = torch.full((B, H, wl.n_q, K), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((B, H, wl.n_q, K), -7.0, dtype=torch.float32, device="cuda")
+    pr = None if prior is None else tuple(torch.from_numpy(a).cuda() for a in prior)
+    fs.fs_beam_select(prob, q, f0, ft, beam, slack, K, idx, sc, prior=pr)
+    torch.cuda.synchronize()
+    out = {"idx": idx.cpu().numpy(), "score": sc.cpu().numpy(), "nbytes": nbytes}
+    if use0:
+        out["f0"] = f0.cpu().numpy()
+    if use_tau:
+        out["ft"] = ft.cpu().numpy()
+    return out
+
+
+def oracle_problem(wl, prior):
+    p = oracle.problem_from(wl)
+    if prior is not None:
+        oracle.with_prior(p, prior[0].astype(np.float64), prior[1].astype(np.float64))
+    return p
+
+
+def check_rows(wl, inp, kbar, amax, tau, got, beam, slack, rows, use0=True, use_tau=True,
+               prior=None, score_ulps=0):
+    orc = oracle.Oracle()
+    p = oracle_problem(wl, prior)
+    n_exact = 0
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            f0 = orc.forest_build(kbar[b, h], amax[b, h]) if use0 else None
+            ft = orc.forest_build(kbar[b, h], amax[b, h], float(tau[h])) if use_tau else None
+            for t in rows:
+                i = wl.q_pos0 + int(t)
+                sel, sc = orc.beam_row(p, h, i, inp["q"][b, h, t], f0, ft, beam, slack)
+                order = np.argsort(sel)
+                want = np.full(wl.topk, -1, np.int32)
+                want[:len(sel)] = sel[order]
+                g = got["idx"][b, h, t]
+                assert np.array_equal(g, want), (b, h, t, g, want)
+                ws = np.zeros(wl.topk, np.float32)
+                ws[:len(sel)] = sc[order].astype(np.float32)
+                gs = got["score"][b, h, t]
+                ulp = np.abs(gs.view(np.int32).astype(np.int64) - ws.view(np.int32).astype(np.int64))
+                assert ulp.max() <= score_ulps, (b, h, t, gs, ws)
+                n_exact += int(ulp.max() == 0)
+    return n_exact
+
+
+def small(name, **kw):
+    base = dict(name=name, batch=1, heads=2, n_ctx=3200 + 17, head_dim=64, dtype="bf16",
+                n_q=3200 + 17, q_pos0=0, topk=8, budget=-1, seed=11)
+    base.update(kw)
+    return synth.Workload(**base)
+
+
+CASES = {
+    # name: (workload, beam, slack, use forest 0, use forest tau, prior)
+    "bf16_d64_two_forests": (small("a"), 8, 1.0, True, True, False),
+    "f32_d128_prior": (small("b", dtype="f32", head_dim=128, n_ctx=2048 + 31, n_q=700,
+                             q_pos0=2048 + 31 - 700, topk=16, prior_lambda=0.1,
+                             prior_sigma=600.0), 16, 0.5, True, True, True),
+    "bf16_d64_beam1_greedy": (small("c", topk=4), 1, 0.0, True, False, False),
+    "bf16_d128_beam64_k64": (small("d", head_dim=128, topk=64, n_ctx=4096, n_q=1024,
+                                   q_pos0=3072), 64, 1.0, True, True, False),
+    "bf16_d64_admitted_only": (small("e", batch=2), 4, 2.0, False, True, False),
+    "bf16_d128_decode": (small("f", head_dim=128, n_ctx=8192, n_q=64, q_pos0=8192 - 64,
+                               topk=32, structure="needle", needle_queries=64), 32, 1.0,
+                         True, True, False),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_forest_statistics_bit_exact(case):
+    wl, beam, slack, use0, use_tau, prior = CASES[case]
+    inp, kbar, amax, tau = make_inputs(wl)
+    got = gpu_fsb(wl, inp, kbar, amax, tau, beam, slack, use0, use_tau)
+    C, d = wl.n_cells, wl.head_dim
+    L = forest_layout(C, d)
+    assert got["nbytes"] == L["stride"] * wl.batch * wl.heads
+    orc = oracle.Oracle()
+    for key, use, t in (("f0", use0, None), ("ft", use_tau, True)):
+        if not use:
+            continue
+        for b in range(wl.batch):
+            for h in range(wl.heads):
+                bh = b * wl.heads + h
+                g = decode_forest(got[key], L, bh, C, d)
+                f = orc.forest_build(kbar[b, h], amax[b, h], None if t is None else float(tau[h]))
+                assert g["m"] == f.m
+                assert np.array_equal(g["prefix"], f.prefix[:C + 1])
+                for lv in range(f.n_levels):
+                    for j in range(f.m >> lv):
+                        gn, on = L["lev_off"][lv] + j, f.node(lv, j)
+                        assert g["first"][gn] == f.first[on]
+                        assert g["amax"][gn] == f.amax[on]
+                        assert g["rho"][gn].view(np.int32) == f.rho[on].view(np.int32), (lv, j)
+                        assert np.array_equal(g["mu"][gn].view(np.int32),
+                                              f.mu[on].view(np.int32)), (lv, j)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_beam_select_matches_oracle(case):
+    wl, beam, slack, use0, use_tau, prior = CASES[case]
+    inp, kbar, amax, tau = make_inputs(wl)
+    pr = wl.prior_arrays() if prior else None
+    got = gpu_fsb(wl, inp, kbar, amax, tau, beam, slack, use0, use_tau, pr)
+    n_exact = check_rows(wl, inp, kbar, amax, tau, got, beam, slack, range(wl.n_q), use0,
+                         use_tau, pr, score_ulps=1 if prior else 0)
+    assert n_exact >= 0.99 * wl.n_q * wl.batch * wl.heads
+    # rows whose query sees no complete cell are all padding
+    first = max(0, wl.window + wl.cell - wl.q_pos0)
+    if first > 0:
+        assert (got["idx"][:, :, :min(first, wl.n_q)] == -1).all()
+
+
+@pytest.mark.parametrize("tau_q", [-1.0, 2.0])
+def test_admitted_forest_all_or_nothing(tau_q):
+    """tau below every a_c admits all cells (the admitted forest equals forest 0);
+    above every a_c admits none (no leaves: only forest 0 contributes)."""
+    wl = small("g", n_ctx=2048, n_q=512, q_pos0=2048 - 512)
+    inp, kbar, amax, _ = make_inputs(wl)
+    tau = np.full(wl.heads, -1.0 if tau_q < 0 else 1e30, np.float32)
+    got = gpu_fsb(wl, inp, kbar, amax, tau, 8, 1.0)
+    ref = gpu_fsb(wl, inp, kbar, amax, tau, 8, 1.0, use_tau=False)
+    L = forest_layout(wl.n_cells, wl.head_dim)
+    for bh in range(wl.batch * wl.heads):
+        a = decode_forest(got["f0"], L, bh, wl.n_cells, wl.head_dim)
+        t = decode_forest(got["ft"], L, bh, wl.n_cells, wl.head_dim)
+        if tau_q < 0:       # same leaves, hence the same nodes (padding is not compared)
+            assert a["m"] == t["m"] == wl.n_cells
+            assert np.array_equal(a["prefix"], t["prefix"])
+            n_used = [L["lev_off"][lv] + j for lv in range(len(L["lev_off"]))
+                      for j in range(a["m"] >> lv)]
+            for key in ("first", "amax", "rho", "mu"):
+                assert np.array_equal(a[key][n_used], t[key][n_used]), key
+        else:
+            assert t["m"] == 0 and not t["prefix"].any()
+    assert np.array_equal(got["idx"], ref["idx"])
+    check_rows(wl, inp, kbar, amax, tau, got, 8, 1.0, range(wl.n_q))
+
+
+def test_full_size_sampled():
+    """The 64k prefill shape (B1 H8 d128 bf16, K 32) with both forests and a beam of
+    32, in the launch configuration the benchmark times; 48 sampled rows per head."""
+    wl = synth.get_workload("prefill_b1h8_n65536_d128_bf16")
+    inp, kbar, amax, tau = make_inputs(wl)
+    got = gpu_fsb(wl, inp, kbar, amax, tau, 32, 1.0)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.integers(0, wl.n_q, 40), np.arange(wl.n_q - 8, wl.n_q)]))
+    check_rows(wl, inp, kbar, amax, tau, got, 32, 1.0, rows)
+    assert (got["idx"][:, :, :wl.window + wl.cell] == -1).all()
