@@ -234,6 +234,102 @@ def run_stream(torch, fs, decode_steps=200, lengths=(16384, 262144)):
     return out
 
 
+FSB_BEAM, FSB_SLACK, FSB_TAU_Q = 32, 1.0, 0.7
+
+
+class FsbSetup:
+    """FS-B (section 3.4) at a workload's shape: both forests' storage, the per-head
+    admission thresholds tau_h (the 70th percentile of the head's a_c) and the
+    selection outputs.  kbar/amax are the caller's eq. 5 summaries on the device."""
+
+    def __init__(self, torch, fs, wl, p, kbar, amax):
+        B, H, C = wl.batch, wl.heads, wl.n_cells
+        self.fs, self.p, self.kbar, self.amax = fs, p, kbar, amax
+        self.tau = torch.quantile(amax[0].reshape(H, C).float(), FSB_TAU_Q, dim=1).contiguous()
+        nb = fs.fs_forest_size(p)
+        self.f0 = torch.empty(nb, dtype=torch.uint8, device=kbar.device)
+        self.ft = torch.empty(nb, dtype=torch.uint8, device=kbar.device)
+        self.idx = torch.empty(B, H, wl.n_q, wl.topk, dtype=torch.int32, device=kbar.device)
+        self.effort = torch.empty(B, H, wl.n_q, dtype=torch.int32, device=kbar.device)
+        self.topk = wl.topk
+
+    def build(self):
+        self.fs.fs_forest_build(self.p, self.kbar, self.amax, self.f0)
+        self.fs.fs_forest_build(self.p, self.kbar, self.amax, self.ft, tau=self.tau)
+
+    def search(self, q, effort=False):
+        self.fs.fs_beam_select(self.p, q, self.f0, self.ft, FSB_BEAM, FSB_SLACK, self.topk,
+                               self.idx, None, effort=self.effort if effort else None)
+
+
+def run_fsb(name, steps, warmup, torch, fs):
+    """FS-B forward at a workload's shape: summaries, both forests, beam search of
+    width FSB_BEAM (slack FSB_SLACK), then the FS-L window, readout and combine."""
+    wl = synth.WORKLOADS[name]
+    x = synth.generate(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v"))
+    alpha = torch.from_numpy(x["alpha"]).to(dev)
+    del x
+    fwd = fs.FsForward.for_workload(wl, device=dev)
+    p = fwd.prob
+    fs.fs_cell_summaries(p, k, fwd.kbar, fwd.amax)
+    fb = FsbSetup(torch, fs, wl, p, fwd.kbar, fwd.amax)
+    calls = [("summaries", lambda: fs.fs_cell_summaries(p, k, fwd.kbar, fwd.amax)),
+             ("forest_build", fb.build),
+             ("beam_select", lambda: fb.search(q)),
+             ("window", lambda: fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)),
+             ("sparse", lambda: fs.fs_sparse_attn(p, q, k, v, fb.idx, wl.topk, fwd.rms_eps,
+                                                  fwd.o_lr, fwd.ws_sparse)),
+             ("combine", lambda: fs.fs_combine(p, fwd.o_sr, fwd.o_lr, alpha, fwd.o))]
+
+    def step(ev=None):
+        for j, (_, fn) in enumerate(calls):
+            if ev is not None:
+                ev[j].record()
+            fn()
+        if ev is not None:
+            ev[-1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    times = {nm: [] for nm, _ in calls}
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        step(ev)
+        torch.cuda.synchronize()
+        for j, (nm, _) in enumerate(calls):
+            times[nm].append(ev[j].elapsed_time(ev[j + 1]))
+    phase_ms = {nm: float(np.mean(t)) for nm, t in times.items()}
+    fb.search(q, effort=True)
+    torch.cuda.synchronize()
+    scored = int(fb.effort.to(torch.int64).sum().item())
+    nq = wl.batch * wl.heads * wl.n_q
+    # algorithmic bytes of one search launch: each scored node's mean row and its
+    # (rho, A, first cell), each query row once, the selected cells written
+    e = 2 if wl.dtype == "bf16" else 4
+    bytes_beam = scored * (4 * wl.head_dim + 12) + nq * (wl.head_dim * e + 4 * wl.topk)
+    t = phase_ms["beam_select"] * 1e-3
+    ach = bytes_beam / t / 1e9
+    return {"workload": wl.name, "beam": FSB_BEAM, "slack": FSB_SLACK,
+            "tau": f"per head, the {FSB_TAU_Q:.0%} quantile of its a_c",
+            "ms_per_step": ms_step, "queries_per_s": wl.batch * wl.n_q / (ms_step * 1e-3),
+            "phase_ms": phase_ms, "nodes_scored_per_query_head": scored / nq,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"],
+                         "unit": "GB/s", "frac": ach / PEAK["hbm_GBs"], "traffic": None,
+                         "kernel": "beam_select", "bytes_per_launch": bytes_beam,
+                         "ms_per_launch": phase_ms["beam_select"]}}
+
+
 def roofline(res, ph=None):
     """Roofline entry for phase `ph`, by default the one that takes the most time."""
     if ph is None:
@@ -324,7 +420,12 @@ def run_phase(name, phase, reps, torch, fs):
     p = f.prob
     rr_ws = torch.empty(fs.fs_rerank_workspace_size(p, f.keep_w if f.pruned else 0),
                         dtype=torch.uint8, device=dev)
+    fb = FsbSetup(torch, fs, wl, p, f.kbar, f.amax) if phase.startswith("fsb_") else None
+    if fb is not None:
+        fb.build()
     calls = {
+        "fsb_forest": lambda: fb.build(),
+        "fsb_beam": lambda: fb.search(q),
         "summaries": lambda: fs.fs_cell_summaries(p, k, f.kbar, f.amax),
         "prune": lambda: fs.fs_prune_prefix(p, f.amax, f.n_recent, f.budget, f.keep,
                                             f.keep_count),
@@ -454,6 +555,7 @@ def main():
                           "tflops": r["tflops"], "gflop_per_step": r["total_gflop"],
                           "phase_ms": r["phase_ms"], "roofline": roofline(r)}
     stream = None if args.only_primary else run_stream(torch, fs)
+    fsb = None if args.only_primary else run_fsb(PRIMARY, max(2, args.steps // 4), 2, torch, fs)
     wl = main_res["wl"]
     out = {
         "metric": METRIC,
@@ -478,6 +580,7 @@ def main():
         "rerank": roofline(main_res, "rerank"),
         "also": also,
         "stream": stream,
+        "fsb": fsb,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(PRIMARY)

@@ -190,11 +190,13 @@ fs_status fs_forest_build(const fs_problem* problem, const float* kbar, const fl
  * (finite), topk in [1, 64].  prior_lambda, prior_sigma: both NULL (no prior) or
  * float32 [H] (lambda_h >= 0, sigma_h > 0, not checked).  idx: int32
  * [B][H][n_q][topk], ascending, -1 padded; score (nullable): float32 eq. 7
- * score aligned with idx (0 for padding). */
+ * score aligned with idx (0 for padding); effort (nullable): int32 [B][H][n_q],
+ * the number of node scores U_v the query's searches computed (its search
+ * effort: the node rows it read). */
 fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* forest0,
                          const void* forest_tau, int32_t beam, float slack,
                          const float* prior_lambda, const float* prior_sigma, int32_t topk,
-                         int32_t* idx, float* score, void* stream);
+                         int32_t* idx, float* score, int32_t* effort, void* stream);
 
 /* Bytes of device workspace for fs_window_attn: its RoPE cos/sin table, then room
  * for the partial states with which a short query range (decode) splits each

@@ -281,7 +281,7 @@ fs_status fs_forest_build(const fs_problem* problem, const float* kbar, const fl
 fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* forest0,
                          const void* forest_tau, int32_t beam, float slack,
                          const float* prior_lambda, const float* prior_sigma, int32_t topk,
-                         int32_t* idx, float* score, void* stream)
+                         int32_t* idx, float* score, int32_t* effort, void* stream)
 {
     fs::Shape sh;
     FS_CHECK(check_problem(problem, &sh));
@@ -299,7 +299,7 @@ fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* f
     if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
     return from_hip(fs::launch_beam_select(sh, q, forest0, forest_tau, beam, (double)slack,
                                            prior_lambda, prior_lambda ? prior_sigma : nullptr,
-                                           topk, idx, score, (hipStream_t)stream),
+                                           topk, idx, score, effort, (hipStream_t)stream),
                     "fs_beam_select");
 }
 

@@ -101,6 +101,6 @@ hipError_t launch_forest_build(const Shape& sh, const float* kbar, const float* 
 hipError_t launch_beam_select(const Shape& sh, const void* q, const void* forest0,
                               const void* forest_tau, int beam, double slack,
                               const float* prior_lambda, const float* prior_sigma, int topk,
-                              int32_t* idx, float* score, hipStream_t st);
+                              int32_t* idx, float* score, int32_t* effort, hipStream_t st);
 
 }  // namespace fs

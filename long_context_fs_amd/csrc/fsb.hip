@@ -153,7 +153,33 @@ __global__ __launch_bounds__(256) void forest_mean_kernel(const float* __restric
     const float* a = amax + bh * (long)L.C;
     double s = 0.0;
     float a_best = -INFINITY;
-    for (int t = 0; t < width; ++t) {
+    int t = 0;
+    // 16 leaves per round: their loads are independent and issued together, the
+    // sum still runs in ascending leaf order (leaf0 is a multiple of 16 here)
+    for (; t + 16 <= width; t += 16) {
+        const int4* c4 = reinterpret_cast<const int4*>(f.first + leaf0 + t);
+        int c[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int4 v = c4[u];
+            c[4 * u] = v.x;
+            c[4 * u + 1] = v.y;
+            c[4 * u + 2] = v.z;
+            c[4 * u + 3] = v.w;
+        }
+        float x[16], av[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            x[u] = kb[(long)c[u] * L.d + e];
+            av[u] = a[c[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            s += (double)x[u];
+            if (av[u] > a_best) a_best = av[u];
+        }
+    }
+    for (; t < width; ++t) {
         const int c = f.first[leaf0 + t];
         s += (double)kb[(long)c * L.d + e];
         if (a[c] > a_best) a_best = a[c];
@@ -319,7 +345,7 @@ __device__ __forceinline__ int beam_keep(BeamLds& S, int n_cand, int beam)
 // beam's cells and scores to the found list at *n_found.
 template <int D>
 __device__ __forceinline__ void beam_forest(BeamLds& S, const FsbView& f, const FsbLayout& L, int n_leaves,
-                            int beam, const QueryCtx<D>& Q, int* n_found)
+                            int beam, const QueryCtx<D>& Q, int* n_found, int* n_scored)
 {
     const int lane = threadIdx.x & 63;
     if (n_leaves <= 0) return;
@@ -337,6 +363,7 @@ __device__ __forceinline__ void beam_forest(BeamLds& S, const FsbView& f, const 
     }
     __syncthreads();
     beam_score<D>(S, n_cand, f, L, Q);
+    *n_scored += n_cand;
     int n_cur = beam_keep(S, n_cand, beam);
     for (;;) {
         const bool inner = lane < n_cur && S.blv[lane] > 0;
@@ -364,6 +391,7 @@ __device__ __forceinline__ void beam_forest(BeamLds& S, const FsbView& f, const 
         n_cand = n_cur + __popcll(im);
         __syncthreads();
         beam_score<D>(S, 2 * __popcll(im), f, L, Q);
+        *n_scored += 2 * __popcll(im);
         n_cur = beam_keep(S, n_cand, beam);
     }
     if (lane < n_cur) {
@@ -380,7 +408,7 @@ __global__ __launch_bounds__(64, 4) void beam_select_kernel(
     int nq, int q_pos0, int w, int s, FsbLayout L, char* forest0, char* forest_tau, int beam,
     double slack, double inv_sqrt_d, const float* __restrict__ prior_lambda,
     const float* __restrict__ prior_sigma, int topk, int32_t* __restrict__ idx,
-    float* __restrict__ score)
+    float* __restrict__ score, int32_t* __restrict__ effort)
 {
     __shared__ BeamLds S;
     const int lane = threadIdx.x;
@@ -407,15 +435,15 @@ __global__ __launch_bounds__(64, 4) void beam_select_kernel(
 
     long n = i < w ? 0 : (i - w) / s;
     if (n > L.C) n = L.C;
-    int n_found = 0, n_first = 0;
+    int n_found = 0, n_first = 0, n_scored = 0;
     if (forest0) {
         const FsbView f = fsb_view(forest0, L, bh);
-        beam_forest<D>(S, f, L, f.prefix[n], beam, Q, &n_found);
+        beam_forest<D>(S, f, L, f.prefix[n], beam, Q, &n_found, &n_scored);
     }
     n_first = n_found;
     if (forest_tau) {
         const FsbView f = fsb_view(forest_tau, L, bh);
-        beam_forest<D>(S, f, L, f.prefix[n], beam, Q, &n_found);
+        beam_forest<D>(S, f, L, f.prefix[n], beam, Q, &n_found, &n_scored);
     }
 
     // union of the two beams (a cell found twice has the same score), best min(K, .)
@@ -463,6 +491,7 @@ __global__ __launch_bounds__(64, 4) void beam_select_kernel(
         orow[lane] = -1;
         if (srow) srow[lane] = 0.f;
     }
+    if (effort && lane == 0) effort[bh * nq + row] = n_scored;
 }
 
 }  // namespace
@@ -491,7 +520,7 @@ hipError_t launch_forest_build(const Shape& sh, const float* kbar, const float* 
 hipError_t launch_beam_select(const Shape& sh, const void* q, const void* forest0,
                               const void* forest_tau, int beam, double slack,
                               const float* prior_lambda, const float* prior_sigma, int topk,
-                              int32_t* idx, float* score, hipStream_t st)
+                              int32_t* idx, float* score, int32_t* effort, hipStream_t st)
 {
     if (sh.nq == 0) return hipSuccess;
     const FsbLayout L = fsb_layout(sh.C, sh.d);
@@ -502,7 +531,8 @@ hipError_t launch_beam_select(const Shape& sh, const void* q, const void* forest
 #define FS_BEAM_LAUNCH(E, DD, T)                                                          \
     beam_select_kernel<E, DD><<<grid, 64, 0, st>>>(                                         \
         static_cast<const T*>(q), sh.qs[0], sh.qs[1], sh.qs[2], sh.H, sh.nq, sh.q_pos0, sh.w, \
-        sh.s, L, f0, ft, beam, slack, inv_sqrt_d, prior_lambda, prior_sigma, topk, idx, score)
+        sh.s, L, f0, ft, beam, slack, inv_sqrt_d, prior_lambda, prior_sigma, topk, idx, score, \
+        effort)
     if (sh.bf16 && sh.d == 128) FS_BEAM_LAUNCH(Bf16, 128, uint16_t);
     else if (sh.bf16) FS_BEAM_LAUNCH(Bf16, 64, uint16_t);
     else if (sh.d == 128) FS_BEAM_LAUNCH(F32, 128, float);

@@ -77,7 +77,7 @@ def load(path: str | None = None):
         "fs_combine": [P, vp, vp, vp, vp, vp],
         "fs_forest_size": [P, C.POINTER(C.c_size_t)],
         "fs_forest_build": [P, vp, vp, vp, vp, vp],
-        "fs_beam_select": [P, vp, vp, vp, i32, f32, vp, vp, i32, vp, vp, vp],
+        "fs_beam_select": [P, vp, vp, vp, i32, f32, vp, vp, i32, vp, vp, vp, vp],
         "fs_stream_state_size": [C.POINTER(FsStreamConfig), C.POINTER(C.c_size_t)],
         "fs_stream_reset": [C.POINTER(FsStreamConfig), vp, C.c_size_t, vp],
         "fs_stream_step": [C.POINTER(FsStreamConfig), vp, C.c_size_t, C.c_int64, i32, vp, vp,
@@ -211,13 +211,14 @@ def fs_forest_build(prob, kbar, amax, forest, tau=None, stream=None):
 
 
 def fs_beam_select(prob, q, forest0, forest_tau, beam, slack, topk, idx, score=None,
-                   prior=None, stream=None):
-    """FS-B beam search (eq. 11) for S_i; prior: None or (lambda, sigma) device tensors."""
+                   prior=None, effort=None, stream=None):
+    """FS-B beam search (eq. 11) for S_i; prior: None or (lambda, sigma) device tensors;
+    effort: None or an int32 [B, H, n_q] tensor for the node scores per query."""
     lam, sig = prior if prior is not None else (None, None)
     _check("fs_beam_select", load().fs_beam_select(C.byref(prob), _p(q), _p(forest0),
                                                    _p(forest_tau), int(beam), float(slack),
                                                    _p(lam), _p(sig), int(topk), _p(idx),
-                                                   _p(score), _s(stream)))
+                                                   _p(score), _p(effort), _s(stream)))
 
 
 def fs_workspace_size(prob) -> int:

@@ -146,10 +146,11 @@ double or_node_score(const or_problem* p, int head, long long i, const float* q_
 
 /* S_i of the query at position i: beam search of width `beam` in f0 and ftau
  * (either may be NULL), then the best min(K, |found|) by eq. 7's score, in
- * descending (score, cell) order.  Returns the count. */
+ * descending (score, cell) order.  Returns the count; *n_scored (nullable)
+ * receives the number of node scores U_v the two searches computed. */
 int or_beam_row(const or_problem* p, int head, long long i, const float* q_row,
                 const or_forest* f0, const or_forest* ftau, int beam, double slack,
-                int* sel, double* score);
+                int* sel, double* score, int* n_scored);
 
 #ifdef __cplusplus
 }

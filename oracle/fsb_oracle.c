@@ -169,7 +169,7 @@ static int or_cmp_beam(const void* a, const void* b)
  * beam's cells and scores; returns their count. */
 static int or_beam_forest(const or_problem* p, int head, long long i, const float* q_row,
                           double q_norm, const or_forest* f, int n_leaves, int beam,
-                          double slack, int* cells, double* scores)
+                          double slack, int* cells, double* scores, int* n_scored)
 {
     if (!f || n_leaves <= 0 || beam <= 0) return 0;
     or_beam_ent* cur = (or_beam_ent*)malloc(sizeof(or_beam_ent) * (size_t)(2 * beam + 32));
@@ -183,6 +183,7 @@ static int or_beam_forest(const or_problem* p, int head, long long i, const floa
         cur[n_cur].first = f->first[f->level_start[lv[r]] + ix[r]];
         cur[n_cur].u = or_node_score(p, head, i, q_row, q_norm, f, lv[r], ix[r], slack);
         ++n_cur;
+        ++*n_scored;
     }
     qsort(cur, (size_t)n_cur, sizeof(or_beam_ent), or_cmp_beam);
     if (n_cur > beam) n_cur = beam;
@@ -203,6 +204,7 @@ static int or_beam_forest(const or_problem* p, int head, long long i, const floa
                 e.first = f->first[f->level_start[e.level] + e.index];
                 e.u = or_node_score(p, head, i, q_row, q_norm, f, e.level, e.index, slack);
                 cand[n_cand++] = e;
+                ++*n_scored;
             }
         }
         qsort(cand, (size_t)n_cand, sizeof(or_beam_ent), or_cmp_beam);
@@ -221,8 +223,9 @@ static int or_beam_forest(const or_problem* p, int head, long long i, const floa
 /* ---- S_i of one query (eqs. 10-11, then eq. 7 over the found leaves) ----- */
 int or_beam_row(const or_problem* p, int head, long long i, const float* q_row,
                 const or_forest* f0, const or_forest* ftau, int beam, double slack,
-                int* sel, double* score)
+                int* sel, double* score, int* n_scored)
 {
+    int scored = 0;
     const int d = p->head_dim;
     const int n = or_n_candidates(p, i);
     const double q_norm = sqrt(or_dot16(q_row, q_row, d));
@@ -231,11 +234,11 @@ int or_beam_row(const or_problem* p, int head, long long i, const float* q_row,
     int cnt = 0;
     if (f0) cnt += or_beam_forest(p, head, i, q_row, q_norm, f0,
                                   f0->prefix[n < f0->n_cells ? n : f0->n_cells], beam, slack,
-                                  cells, sc);
+                                  cells, sc, &scored);
     if (ftau) {
         const int nt = ftau->prefix[n < ftau->n_cells ? n : ftau->n_cells];
         cnt += or_beam_forest(p, head, i, q_row, q_norm, ftau, nt, beam, slack, cells + cnt,
-                              sc + cnt);
+                              sc + cnt, &scored);
     }
     /* union of the two beams (a cell found twice has the same score) */
     or_beam_ent* u = (or_beam_ent*)malloc(sizeof(or_beam_ent) * (size_t)(cnt > 0 ? cnt : 1));
@@ -259,5 +262,6 @@ int or_beam_row(const or_problem* p, int head, long long i, const float* q_row,
     free(u);
     free(cells);
     free(sc);
+    if (n_scored) *n_scored = scored;
     return k;
 }

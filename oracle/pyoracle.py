@@ -166,7 +166,7 @@ class Oracle:
                                     C.c_int, C.c_double]
         L.or_node_score.restype = C.c_double
         L.or_beam_row.argtypes = [P, C.c_int, C.c_longlong, _F32P, C.c_void_p, C.c_void_p,
-                                  C.c_int, C.c_double, _I32P, _F64P]
+                                  C.c_int, C.c_double, _I32P, _F64P, C.POINTER(C.c_int)]
         L.or_beam_row.restype = C.c_int
         self.L = L
 
@@ -201,15 +201,19 @@ class Oracle:
                                     int(level), int(index), float(slack))
 
     def beam_row(self, p: Problem, head: int, i: int, q_row, f0: Forest | None,
-                 ftau: Forest | None, beam: int, slack: float):
+                 ftau: Forest | None, beam: int, slack: float, effort: bool = False):
         """S_i of the query at position i by beam search (eqs. 10-11), with its eq. 7
-        scores, in descending (score, cell) order."""
+        scores, in descending (score, cell) order.  With effort=True also returns
+        the number of node scores the searches computed."""
         sel = np.zeros(max(p.topk, 1), np.int32)
         sc = np.zeros(max(p.topk, 1), np.float64)
+        n_scored = C.c_int()
         cnt = self.L.or_beam_row(C.byref(p), int(head), int(i), _f32(q_row),
                                  None if f0 is None else C.addressof(f0.s),
                                  None if ftau is None else C.addressof(ftau.s),
-                                 int(beam), float(slack), sel, sc)
+                                 int(beam), float(slack), sel, sc, C.byref(n_scored))
+        if effort:
+            return sel[:cnt].copy(), sc[:cnt].copy(), n_scored.value
         return sel[:cnt].copy(), sc[:cnt].copy()
 
     # -- single steps ------------------------------------------------------

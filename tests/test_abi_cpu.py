@@ -226,22 +226,22 @@ def test_fsb_arguments_rejected(lib):
     assert b"256-byte" in lib.fs_last_error()
     assert lib.fs_forest_build(C.byref(p), FAKE, None, None, F, None) == 1
     assert lib.fs_beam_select(C.byref(p), FAKE, None, None, 8, 1.0, None, None, 8, FAKE,
-                              None, None) == 1
+                              None, None, None) == 1
     assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 0, 1.0, None, None, 8, FAKE, None,
-                              None) == 2
+                              None, None) == 2
     assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 65, 1.0, None, None, 8, FAKE, None,
-                              None) == 2
+                              None, None) == 2
     assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, -1.0, None, None, 8, FAKE, None,
-                              None) == 1
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, float("nan"), None, None, 8, FAKE,
                               None, None) == 1
+    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, float("nan"), None, None, 8, FAKE,
+                              None, None, None) == 1
     assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, FAKE, None, 8, FAKE, None,
-                              None) == 1
+                              None, None) == 1
     assert b"prior" in lib.fs_last_error()
     assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, None, None, 65, FAKE, None,
-                              None) == 2
+                              None, None) == 2
     assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, None, None, 8, None, None,
-                              None) == 1
+                              None, None) == 1
     # forest storage grows with the number of cells and holds their node statistics
     small, large = C.c_size_t(), C.c_size_t()
     lib.fs_forest_size(C.byref(_prob(n_ctx=4096, n_q=1)), C.byref(small))

@@ -88,10 +88,12 @@ def gpu_fsb(wl, inp, kbar, amax, tau, beam, slack, use0=True, use_tau=True, prio
     B, H, K = wl.batch, wl.heads, wl.topk
     idx = torch.full((B, H, wl.n_q, K), -7, dtype=torch.int32, device="cuda")
     sc = torch.full((B, H, wl.n_q, K), -7.0, dtype=torch.float32, device="cuda")
+    eff = torch.full((B, H, wl.n_q), -7, dtype=torch.int32, device="cuda")
     pr = None if prior is None else tuple(torch.from_numpy(a).cuda() for a in prior)
-    fs.fs_beam_select(prob, q, f0, ft, beam, slack, K, idx, sc, prior=pr)
+    fs.fs_beam_select(prob, q, f0, ft, beam, slack, K, idx, sc, prior=pr, effort=eff)
     torch.cuda.synchronize()
-    out = {"idx": idx.cpu().numpy(), "score": sc.cpu().numpy(), "nbytes": nbytes}
+    out = {"idx": idx.cpu().numpy(), "score": sc.cpu().numpy(), "effort": eff.cpu().numpy(),
+           "nbytes": nbytes}
     if use0:
         out["f0"] = f0.cpu().numpy()
     if use_tau:
@@ -117,7 +119,9 @@ def check_rows(wl, inp, kbar, amax, tau, got, beam, slack, rows, use0=True, use_
             ft = orc.forest_build(kbar[b, h], amax[b, h], float(tau[h])) if use_tau else None
             for t in rows:
                 i = wl.q_pos0 + int(t)
-                sel, sc = orc.beam_row(p, h, i, inp["q"][b, h, t], f0, ft, beam, slack)
+                sel, sc, eff = orc.beam_row(p, h, i, inp["q"][b, h, t], f0, ft, beam, slack,
+                                            effort=True)
+                assert got["effort"][b, h, t] == eff, (b, h, t)
                 order = np.argsort(sel)
                 want = np.full(wl.topk, -1, np.int32)
                 want[:len(sel)] = sel[order]

@@ -190,3 +190,25 @@ def test_empty_and_narrow(orc):
     assert ft.m == 0
     sel, _ = orc.beam_row(p, 0, 512 + 32 * 40, q, None, ft, 8, 1.0)
     assert len(sel) == 0
+
+
+def test_search_effort_closed_form(orc):
+    """Nodes scored by one forest's search: the roots, plus two per inner node of
+    each step's beam.  With a beam that never drops a node (width >= leaves), every
+    node of the covering trees is scored exactly once: 2 * 2^l - 1 per root of
+    level l."""
+    rng = np.random.default_rng(8)
+    n_cells, d = 90, 64
+    kbar, amax = _summaries(rng, n_cells, d)
+    p = _wide_problem(n_cells, d, 8, False)
+    f0 = orc.forest_build(kbar, amax)
+    for n in (1, 5, 16, 37, 90):
+        i = 512 + 32 * n
+        q = rng.standard_normal(d).astype(np.float32)
+        *_, e = orc.beam_row(p, 0, i, q, f0, None, 2 * n_cells, 0.0, effort=True)
+        assert e == sum(2 * (1 << lv) - 1 for lv, _ in orc.forest_roots(f0, n))
+        # a beam of width 1 scores the roots, then two children per level below the
+        # best root: at most roots + 2 * (its level)
+        *_, e1 = orc.beam_row(p, 0, i, q, f0, None, 1, 0.0, effort=True)
+        roots = orc.forest_roots(f0, n)
+        assert len(roots) <= e1 <= len(roots) + 2 * max(lv for lv, _ in roots)
