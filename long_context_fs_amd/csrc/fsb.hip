@@ -225,20 +225,24 @@ __global__ __launch_bounds__(256) void forest_radius_kernel(const float* __restr
 
 // ---- search -------------------------------------------------------------------
 
+// Per-wave search state in LDS, kept small (cells and node indices < 32768 fit
+// int16) so that many waves fit a compute unit.
 struct BeamLds {
     alignas(16) float q[128];     // the query row
     double cu[2 * kMaxBeam];      // candidates: U, level, index, first cell
-    int clv[2 * kMaxBeam], cix[2 * kMaxBeam], cfirst[2 * kMaxBeam];
-    int todo[2 * kMaxBeam];       // candidate slots whose U is still to be computed
     double bu[kMaxBeam];          // the beam
-    int blv[kMaxBeam], bix[kMaxBeam], bfirst[kMaxBeam];
-    double fu[2 * kMaxBeam];      // leaves found by both forests
-    int fcell[2 * kMaxBeam], fdup[2 * kMaxBeam];
+    double fu[2 * kMaxBeam];      // leaves found by both forests: score, cell
+    int16_t cix[2 * kMaxBeam], cfirst[2 * kMaxBeam];
+    int16_t bix[kMaxBeam], bfirst[kMaxBeam];
+    int16_t fcell[2 * kMaxBeam];
+    uint8_t clv[2 * kMaxBeam], blv[kMaxBeam];
+    uint8_t todo[2 * kMaxBeam];   // candidate slots whose U is still to be computed
+    uint8_t fdup[2 * kMaxBeam];   // found twice (second forest)
+    uint8_t frank[2 * kMaxBeam];  // rank among the found cells
 };
 
-template <int D>
 struct QueryCtx {
-    float4 q[4][D / 64];          // chunks r, r+4, r+8, r+12 of q (r = lane mod 4)
+    const float4* q;              // the query row in LDS
     double q_norm;
     double i_pos;                 // the query's position
     double lam, sig;              // eq. 7 prior of the head (lam 0: none)
@@ -250,16 +254,21 @@ struct QueryCtx {
 // ascending order), combined as (p_r + p_{r+8}) + (p_{r+4} + p_{r+12}).  Two
 // shuffles at distances 2 and 1 then finish the pairwise sum.
 template <int D>
-__device__ __forceinline__ double dot_share(const float4 (&q)[4][D / 64], const float4* x4, int r)
+__device__ __forceinline__ double dot_share(const float4* q, const float4* x4, int r)
 {
     constexpr int C4 = D / 64;
+    float4 xv4[4][C4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < C4; ++g) xv4[j][g] = x4[(r + 4 * j) * C4 + g];
     double p[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         double acc = 0.0;
 #pragma unroll
         for (int g = 0; g < C4; ++g) {
-            const float4 xv = x4[(r + 4 * j) * C4 + g], qv = q[j][g];
+            const float4 xv = xv4[j][g], qv = q[(r + 4 * j) * C4 + g];
             acc = __builtin_fma((double)qv.x, (double)xv.x, acc);
             acc = __builtin_fma((double)qv.y, (double)xv.y, acc);
             acc = __builtin_fma((double)qv.z, (double)xv.z, acc);
@@ -281,33 +290,47 @@ __device__ __forceinline__ bool beam_better(double ub, int fb, int lb, double ua
     return ub > ua || (ub == ua && (fb > fa || (fb == fa && lb < la)));
 }
 
+// lambda_h A_v erf((i - p) / (2 sigma_h)), kept out of line so that erf's
+// registers do not weigh on the search without a prior.
+__device__ __attribute__((noinline)) double fsb_prior(double lam, double a_v, double i_pos,
+                                                       double p_c, double sig)
+{
+    return lam * a_v * erf((i_pos - p_c) / (2.0 * sig));
+}
+
 // U of the candidates listed in todo[0 .. n_todo): four lanes per node.
 template <int D>
 __device__ __forceinline__ void beam_score(BeamLds& S, int n_todo, const FsbView& f,
-                                           const FsbLayout& L, const QueryCtx<D>& Q)
+                                           const FsbLayout& L, const QueryCtx& Q)
 {
     const int lane = threadIdx.x & 63, r = lane & 3;
     for (int k0 = 0; k0 < n_todo; k0 += 16) {
         const int k = k0 + (lane >> 2);
         const bool valid = k < n_todo;
-        int slot = 0, node = 0;
+        int slot = 0, node = 0, c = 0;
+        float rho = 0.f, a_v = 0.f;
         double part = 0.0;
         if (valid) {
             slot = S.todo[k];
             node = L.lev_off[S.clv[slot]] + S.cix[slot];
+            // the node's statistics load alongside its mean row
+            if (r == 0) {
+                rho = f.rho[node];
+                c = f.first[node];
+                a_v = f.amax[node];
+            }
             part = dot_share<D>(Q.q, reinterpret_cast<const float4*>(f.mu + (long)node * D), r);
         }
         const double dot = dot_finish(part);
         if (valid && r == 0) {
             double t = Q.slack * Q.q_norm;
-            t = t * (double)f.rho[node];
+            t = t * (double)rho;
             double u = dot + t;
             u = u * Q.inv_sqrt_d;
-            const int c = f.first[node];
             double prior = 0.0;
             if (Q.lam != 0.0 || Q.sig != 0.0) {
                 const double p_c = ((double)c + 0.5) * (double)Q.s;
-                prior = Q.lam * (double)f.amax[node] * erf((Q.i_pos - p_c) / (2.0 * Q.sig));
+                prior = fsb_prior(Q.lam, (double)a_v, Q.i_pos, p_c, Q.sig);
             }
             S.cu[slot] = u + prior;
             S.cfirst[slot] = c;
@@ -345,7 +368,7 @@ __device__ __forceinline__ int beam_keep(BeamLds& S, int n_cand, int beam)
 // beam's cells and scores to the found list at *n_found.
 template <int D>
 __device__ __forceinline__ void beam_forest(BeamLds& S, const FsbView& f, const FsbLayout& L, int n_leaves,
-                            int beam, const QueryCtx<D>& Q, int* n_found, int* n_scored)
+                            int beam, const QueryCtx& Q, int* n_found, int* n_scored)
 {
     const int lane = threadIdx.x & 63;
     if (n_leaves <= 0) return;
@@ -403,7 +426,7 @@ __device__ __forceinline__ void beam_forest(BeamLds& S, const FsbView& f, const 
 }
 
 template <class E, int D>
-__global__ __launch_bounds__(64, 4) void beam_select_kernel(
+__global__ __launch_bounds__(64, 6) void beam_select_kernel(
     const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2, int H,
     int nq, int q_pos0, int w, int s, FsbLayout L, char* forest0, char* forest_tau, int beam,
     double slack, double inv_sqrt_d, const float* __restrict__ prior_lambda,
@@ -418,12 +441,9 @@ __global__ __launch_bounds__(64, 4) void beam_select_kernel(
     const typename E::storage* qr = q + b * qs0 + h * qs1 + row * qs2;
     for (int e = lane; e < D; e += kWave) S.q[e] = load1<E>(qr + e);
     __syncthreads();
-    QueryCtx<D> Q;
+    QueryCtx Q;
     const float4* q4 = reinterpret_cast<const float4*>(S.q);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < D / 64; ++g) Q.q[j][g] = q4[((lane & 3) + 4 * j) * (D / 64) + g];
+    Q.q = q4;
     Q.s = s;
     Q.slack = slack;
     Q.inv_sqrt_d = inv_sqrt_d;
@@ -473,16 +493,16 @@ __global__ __launch_bounds__(64, 4) void beam_select_kernel(
             for (int c = 0; c < n_found; ++c)
                 if (!S.fdup[c]) rank += beam_better(S.fu[c], S.fcell[c], 0, S.fu[a], S.fcell[a], 0);
         }
-        S.todo[a] = rank;
+        S.frank[a] = (uint8_t)rank;
     }
     __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int a = lane + 64 * hh;
-        if (a < n_found && S.todo[a] < k) {
+        if (a < n_found && S.frank[a] < k) {
             int pos = 0;
             for (int c = 0; c < n_found; ++c)
-                pos += (S.todo[c] < k && S.fcell[c] < S.fcell[a]) ? 1 : 0;
+                pos += (S.frank[c] < k && S.fcell[c] < S.fcell[a]) ? 1 : 0;
             orow[pos] = S.fcell[a];
             if (srow) srow[pos] = (float)S.fu[a];
         }
