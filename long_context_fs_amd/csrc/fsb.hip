@@ -239,6 +239,7 @@ struct BeamLds {
     uint8_t todo[2 * kMaxBeam];   // candidate slots whose U is still to be computed
     uint8_t fdup[2 * kMaxBeam];   // found twice (second forest)
     uint8_t frank[2 * kMaxBeam];  // rank among the found cells
+    int ctie[2 * kMaxBeam];       // candidates' tie order
 };
 
 struct QueryCtx {
@@ -340,23 +341,42 @@ __device__ __forceinline__ void beam_score(BeamLds& S, int n_todo, const FsbView
 }
 
 // Keeps the best min(n_cand, beam) candidates as the beam; returns its size.
+// The tie order (later first cell, then lower level) is one int per candidate,
+// first * 16 + 15 - level, so a comparison reads two LDS words.
 __device__ __forceinline__ int beam_keep(BeamLds& S, int n_cand, int beam)
 {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int a = lane + 64 * h;
+        if (a < 2 * kMaxBeam) S.ctie[a] = a < n_cand ? S.cfirst[a] * 16 + 15 - S.clv[a] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int a = lane + 64 * h;
         if (a < n_cand) {
             const double ua = S.cu[a];
-            const int fa = S.cfirst[a], la = S.clv[a];
-            int rank = 0;
-            for (int b = 0; b < n_cand; ++b)
-                rank += beam_better(S.cu[b], S.cfirst[b], S.clv[b], ua, fa, la) ? 1 : 0;
+            const int la = S.clv[a], ta = S.ctie[a];
+            int rank = 0, b = 0;
+            for (; b + 4 <= n_cand; b += 4) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const double ub = S.cu[b + u];
+                    const int tb = S.ctie[b + u];
+                    rank += (ub > ua || (ub == ua && tb > ta)) ? 1 : 0;
+                }
+            }
+            for (; b < n_cand; ++b) {
+                const double ub = S.cu[b];
+                const int tb = S.ctie[b];
+                rank += (ub > ua || (ub == ua && tb > ta)) ? 1 : 0;
+            }
             if (rank < beam) {
                 S.bu[rank] = ua;
                 S.blv[rank] = la;
                 S.bix[rank] = S.cix[a];
-                S.bfirst[rank] = fa;
+                S.bfirst[rank] = S.cfirst[a];
             }
         }
     }
