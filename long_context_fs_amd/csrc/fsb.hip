@@ -10,7 +10,7 @@
 // 2^-l, rounded to fp32), rho_v the largest distance from mu_v to one of them
 // (fp64, rounded to fp32), A_v the largest a_c, p_v^min the centre of its first
 // cell.  Built by three kernels: admission (a block scan per head), means (a
-// thread per (node, dim)), radii (a wave per node).
+// thread per (node, dim)), radii (a thread per (level, leaf)).
 //
 // Search.  One wave per query and forest: the beam starts from the best B
 // roots, each step replaces inner nodes by their children, keeps leaves and
@@ -187,40 +187,53 @@ __global__ __launch_bounds__(256) void forest_mean_kernel(const float* __restric
     f.mu[(long)node * L.d + e] = (float)(s * __builtin_ldexp(1.0, -l));
     if (e == 0) {
         f.amax[node] = a_best;
+        f.rho[node] = 0.f;
         if (l > 0) f.first[node] = f.first[leaf0];
     }
 }
 
-// rho_v: a wave per node, lanes over its leaves, each distance summed over d in order.
+// rho_v: a thread per (level, leaf) computes the leaf's squared distance to its
+// node's mean (summed over d in order, fp64), a segmented wave maximum combines
+// the node's leaves, and nodes wider than a wave combine their waves with an
+// integer maximum on the fp32 bits of sqrt(max) (rho >= 0, and rounding and sqrt
+// are monotone, so this equals rounding the square root of the overall maximum).
+// forest_mean_kernel zeroes rho first.
+template <int D>
 __global__ __launch_bounds__(256) void forest_radius_kernel(const float* __restrict__ kbar,
                                                             FsbLayout L, char* __restrict__ forest)
 {
-    const long bh = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int node = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (node >= L.lev_off[L.n_levels]) return;
+    const long bh = blockIdx.z;
+    const int l = blockIdx.y, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 256 + threadIdx.x;
     const FsbView f = fsb_view(forest, L, bh);
-    const int l = fsb_level_of(L, node), j = node - L.lev_off[l];
-    if (j >= (*f.m >> l)) return;
-    const int leaf0 = j << l, width = 1 << l;
-    const float* kb = kbar + bh * (long)L.C * L.d;
-    const float* mu = f.mu + (long)node * L.d;
+    const int n_nodes = *f.m >> l, j = t >> l;
+    const bool on = j < n_nodes;
     double r2 = 0.0;
-    for (int t = lane; t < width; t += kWave) {
-        const float* kr = kb + (long)f.first[leaf0 + t] * L.d;
-        double acc = 0.0;
-        for (int e = 0; e < L.d; ++e) {
-            const double diff = (double)kr[e] - (double)mu[e];
-            acc = __builtin_fma(diff, diff, acc);
+    if (on) {
+        const float4* kr = reinterpret_cast<const float4*>(kbar + (bh * (long)L.C + f.first[t]) * D);
+        const float4* mu = reinterpret_cast<const float4*>(f.mu + (long)(L.lev_off[l] + j) * D);
+#pragma unroll 8
+        for (int g = 0; g < D / 4; ++g) {
+            const float4 a = kr[g], m = mu[g];
+            double diff = (double)a.x - (double)m.x;
+            r2 = __builtin_fma(diff, diff, r2);
+            diff = (double)a.y - (double)m.y;
+            r2 = __builtin_fma(diff, diff, r2);
+            diff = (double)a.z - (double)m.z;
+            r2 = __builtin_fma(diff, diff, r2);
+            diff = (double)a.w - (double)m.w;
+            r2 = __builtin_fma(diff, diff, r2);
         }
-        if (acc > r2) r2 = acc;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    const int seg = l < 6 ? 1 << l : kWave;       // lanes holding one node's leaves
+    for (int off = seg >> 1; off >= 1; off >>= 1) {
         const double o = __shfl_xor(r2, off);
         if (o > r2) r2 = o;
     }
-    if (lane == 0) f.rho[node] = (float)__builtin_sqrt(r2);
+    if (on && (lane & (seg - 1)) == 0) {
+        const float rho = (float)__builtin_sqrt(r2);
+        atomicMax(reinterpret_cast<int*>(f.rho + L.lev_off[l] + j), __float_as_int(rho));
+    }
 }
 
 // ---- search -------------------------------------------------------------------
@@ -552,7 +565,9 @@ hipError_t launch_forest_build(const Shape& sh, const float* kbar, const float* 
     if (nodes > 0) {
         const int per = 256 / sh.d;
         forest_mean_kernel<<<dim3((nodes + per - 1) / per, BH), 256, 0, st>>>(kbar, amax, L, F);
-        forest_radius_kernel<<<dim3((nodes + 3) / 4, BH), 256, 0, st>>>(kbar, L, F);
+        const dim3 g((sh.C + 255) / 256, L.n_levels, BH);
+        if (sh.d == 128) forest_radius_kernel<128><<<g, 256, 0, st>>>(kbar, L, F);
+        else forest_radius_kernel<64><<<g, 256, 0, st>>>(kbar, L, F);
     }
     return hipGetLastError();
 }
