@@ -25,7 +25,8 @@ sys.path.insert(0, ROOT)
 
 from long_context_fs_amd import synth  # noqa: E402
 
-PEAK = {"hbm_GBs": 8000.0, "mfma_bf16_TFs": 2500.0, "valu_f32_TFs": 78.6, "mfma_f32_TFs": 157.3}
+PEAK = {"hbm_GBs": 8000.0, "mfma_bf16_TFs": 2500.0, "valu_f32_TFs": 78.6, "mfma_f32_TFs": 157.3,
+        "valu_f64_TFs": 78.6}
 METRIC = "FreeSolo forward queries/s and TFLOP/s at N=16k/64k/256k; % of MI355X roofline"
 PRIMARY = "prefill_b1h8_n65536_d128_bf16"
 ALSO = ["prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16",
@@ -34,7 +35,7 @@ PHASES = ["summaries", "prune", "select", "window", "sparse", "combine"]
 # Source file of each phase's kernel (for matching stored HBM traffic counters).
 PHASE_SRC = {"summaries": "summaries.hip", "prune": "prune.hip", "select": "select.hip",
              "window": "window.hip", "sparse": "sparse.hip", "combine": "combine.hip",
-             "rerank": "select.hip"}
+             "rerank": "select.hip", "fsb_beam": "fsb.hip"}
 # Engine each phase's kernel uses, which fixes the roofline it is priced against.
 PHASE_ENGINE = {"summaries": "hbm", "prune": "int", "select": "valu_f32", "window": "mfma_bf16",
                 "sparse": "mfma_bf16", "combine": "hbm", "rerank": "mfma_bf16"}
@@ -314,19 +315,24 @@ def run_fsb(name, steps, warmup, torch, fs):
     torch.cuda.synchronize()
     scored = int(fb.effort.to(torch.int64).sum().item())
     nq = wl.batch * wl.heads * wl.n_q
-    # algorithmic bytes of one search launch: each scored node's mean row and its
-    # (rho, A, first cell), each query row once, the selected cells written
+    # algorithmic work of one search launch: a d-long fp64 dot product (2d flops)
+    # per scored node; the node rows it reads (mean row + rho, A, first cell) come
+    # from a forest of a few tens of MB held in the caches, so HBM does not bound it
     e = 2 if wl.dtype == "bf16" else 4
+    flop_beam = scored * 2.0 * wl.head_dim
     bytes_beam = scored * (4 * wl.head_dim + 12) + nq * (wl.head_dim * e + 4 * wl.topk)
     t = phase_ms["beam_select"] * 1e-3
-    ach = bytes_beam / t / 1e9
+    ach = flop_beam / t / 1e12
     return {"workload": wl.name, "beam": FSB_BEAM, "slack": FSB_SLACK,
             "tau": f"per head, the {FSB_TAU_Q:.0%} quantile of its a_c",
             "ms_per_step": ms_step, "queries_per_s": wl.batch * wl.n_q / (ms_step * 1e-3),
             "phase_ms": phase_ms, "nodes_scored_per_query_head": scored / nq,
-            "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"],
-                         "unit": "GB/s", "frac": ach / PEAK["hbm_GBs"], "traffic": None,
-                         "kernel": "beam_select", "bytes_per_launch": bytes_beam,
+            "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK["valu_f64_TFs"],
+                         "unit": "TFLOP/s", "frac": ach / PEAK["valu_f64_TFs"],
+                         "traffic": stored_traffic("fsb_beam") if name == PRIMARY else None,
+                         "kernel": "beam_select", "flop_per_launch": flop_beam,
+                         "node_bytes_per_launch": bytes_beam,
+                         "node_bytes_GBs": bytes_beam / t / 1e9,
                          "ms_per_launch": phase_ms["beam_select"]}}
 
 
@@ -426,6 +432,7 @@ def run_phase(name, phase, reps, torch, fs):
     calls = {
         "fsb_forest": lambda: fb.build(),
         "fsb_beam": lambda: fb.search(q),
+        "fsb_all": lambda: (fb.build(), fb.search(q)),
         "summaries": lambda: fs.fs_cell_summaries(p, k, f.kbar, f.amax),
         "prune": lambda: fs.fs_prune_prefix(p, f.amax, f.n_recent, f.budget, f.keep,
                                             f.keep_count),
@@ -486,11 +493,32 @@ def counter_means(db, substr):
 def write_traffic(phase, kernel_substr, fetch_db, write_db, copy_fetch_db, copy_write_db,
                   copy_mib):
     """Record HBM bytes per launch of one phase's kernel in profiles/traffic.json."""
+    write_traffic_kib(phase, kernel_substr,
+                      counter_means(fetch_db, kernel_substr)["FETCH_SIZE"],
+                      counter_means(write_db, kernel_substr)["WRITE_SIZE"],
+                      counter_means(copy_fetch_db, "copy")["FETCH_SIZE"],
+                      counter_means(copy_write_db, "copy")["WRITE_SIZE"], copy_mib)
+
+
+def write_traffic_jsonl(phase, kernel_substr, path_jsonl, copy_mib):
+    """Same, from per-dispatch counter means already reduced to JSON lines
+    ({"tag": counter, "kernel": substring, "counters": {...}})."""
+    kib = {}
+    for line in open(path_jsonl):
+        r = json.loads(line)
+        kib[(r["kernel"], r["tag"])] = r["counters"][r["tag"]]
+    write_traffic_kib(phase, kernel_substr, kib[(kernel_substr, "FETCH_SIZE")],
+                      kib[(kernel_substr, "WRITE_SIZE")], kib[("copy", "FETCH_SIZE")],
+                      kib[("copy", "WRITE_SIZE")], copy_mib)
+
+
+def write_traffic_kib(phase, kernel_substr, fetch_kib, write_kib, copy_fetch_kib,
+                      copy_write_kib, copy_mib):
     copy_bytes = copy_mib * (1 << 20)
-    f_copy = counter_means(copy_fetch_db, "copy")["FETCH_SIZE"] * 1024 / copy_bytes
-    w_copy = counter_means(copy_write_db, "copy")["WRITE_SIZE"] * 1024 / copy_bytes
-    fetch = counter_means(fetch_db, kernel_substr)["FETCH_SIZE"] * 1024 / f_copy
-    write = counter_means(write_db, kernel_substr)["WRITE_SIZE"] * 1024 / w_copy
+    f_copy = copy_fetch_kib * 1024 / copy_bytes
+    w_copy = copy_write_kib * 1024 / copy_bytes
+    fetch = fetch_kib * 1024 / f_copy
+    write = write_kib * 1024 / w_copy
     path = os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     data[phase] = {"kernel": kernel_substr, "src_sha": kernel_source_sha(phase),
@@ -515,6 +543,7 @@ def main():
     ap.add_argument("--kernel-stats", metavar="DB", help="print kernel stats of a rocpd db")
     ap.add_argument("--write-traffic", nargs=6, metavar=("PHASE", "KERNEL", "FETCH_DB",
                     "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"))
+    ap.add_argument("--write-traffic-jsonl", nargs=3, metavar=("PHASE", "KERNEL", "JSONL"))
     args = ap.parse_args()
     if args.kernel_stats:
         for name, calls, avg, tot in kernel_stats(args.kernel_stats):
@@ -522,6 +551,9 @@ def main():
         return
     if args.write_traffic:
         write_traffic(*args.write_traffic, copy_mib=args.copy_mib or 1024)
+        return
+    if args.write_traffic_jsonl:
+        write_traffic_jsonl(*args.write_traffic_jsonl, copy_mib=args.copy_mib or 1024)
         return
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported. "
