@@ -239,3 +239,33 @@ def test_full_size_sampled():
     rows = np.unique(np.concatenate([rng.integers(0, wl.n_q, 40), np.arange(wl.n_q - 8, wl.n_q)]))
     check_rows(wl, inp, kbar, amax, tau, got, 32, 1.0, rows)
     assert (got["idx"][:, :, :wl.window + wl.cell] == -1).all()
+
+
+def test_f32_d64_strided_queries_and_empty_range():
+    """fp32 storage at d = 64 with q given as a [B, n_q, H, d] buffer viewed as
+    [B, H, n_q, d] (the problem's q strides), and a call with no queries."""
+    wl = small("h", dtype="f32", n_ctx=2048 + 64, n_q=600, q_pos0=2048 + 64 - 600, topk=12)
+    inp, kbar, amax, tau = make_inputs(wl)
+    B, H, K = wl.batch, wl.heads, wl.topk
+    qt = torch.from_numpy(np.ascontiguousarray(inp["q"].transpose(0, 2, 1, 3))).cuda()
+    q = qt.permute(0, 2, 1, 3)
+    prob = fs.problem(B, H, wl.head_dim, wl.n_ctx, wl.n_q, wl.q_pos0, wl.window, fs.FS_F32, q=q)
+    nbytes = fs.fs_forest_size(prob)
+    f0 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ft = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    kb, am = torch.from_numpy(kbar).cuda(), torch.from_numpy(amax).cuda()
+    fs.fs_forest_build(prob, kb, am, f0)
+    fs.fs_forest_build(prob, kb, am, ft, tau=torch.from_numpy(tau).cuda())
+    idx = torch.full((B, H, wl.n_q, K), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, H, wl.n_q, K), dtype=torch.float32, device="cuda")
+    eff = torch.zeros((B, H, wl.n_q), dtype=torch.int32, device="cuda")
+    fs.fs_beam_select(prob, q, f0, ft, 6, 1.0, K, idx, sc, effort=eff)
+    torch.cuda.synchronize()
+    got = {"idx": idx.cpu().numpy(), "score": sc.cpu().numpy(), "effort": eff.cpu().numpy()}
+    check_rows(wl, inp, kbar, amax, tau, got, 6, 1.0, range(wl.n_q))
+    # no queries: nothing is written
+    empty = fs.problem(B, H, wl.head_dim, wl.n_ctx, 0, 0, wl.window, fs.FS_F32)
+    before = idx.clone()
+    fs.fs_beam_select(empty, q, f0, ft, 6, 1.0, K, idx, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, before)
