@@ -12,7 +12,8 @@
 // cell.  Built by three kernels: admission (a block scan per head), means (a
 // thread per (node, dim)), radii (a thread per (level, leaf)).
 //
-// Search.  One wave per query and forest: the beam starts from the best B
+// Search.  One wave per (query, head) searches both forests in turn; in each the
+// beam starts from the best B
 // roots, each step replaces inner nodes by their children, keeps leaves and
 // retains the best B by U_v = (q.mu_v + c |q| rho_v) / sqrt(d) + lambda_h A_v
 // erf((i - p_v^min) / (2 sigma_h)) (eq. 11), until only leaves remain.  S_i is
