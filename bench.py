@@ -149,6 +149,23 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
         for j, ph in enumerate(PHASES):
             phase_ms[ph].append(ev[j].elapsed_time(ev[j + 1]))
     phase_avg = {ph: float(np.mean(v)) for ph, v in phase_ms.items()}
+    phase_pct = {ph: [float(np.percentile(v, q)) for q in (10, 50, 90)]
+                 for ph, v in phase_ms.items()}
+    cold_ms = None
+    if wl.q_pos0 > 0:
+        # decode: every step after a 512 MiB write that evicts L2 and the Infinity Cache
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(steps):
+            flush.fill_(1)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step()
+            c1.record()
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        cold_ms = [float(np.percentile(cold, q)) for q in (10, 50, 90)]
+        del flush
     rerank_ms = None
     if rerank:
         # eq. 12 token-level reranking in place of eq. 7's scoring, timed on its own
@@ -176,7 +193,24 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
         phase_avg = dict(phase_avg, rerank=rerank_ms)
     return dict(wl=wl, ms_step=ms_step, wall=wall, phase_ms=phase_avg, work=work,
                 qps=queries / (ms_step * 1e-3), tflops=total_flop / (ms_step * 1e-3) / 1e12,
-                total_gflop=total_flop / 1e9)
+                total_gflop=total_flop / 1e9, phase_pct=phase_pct, cold_ms=cold_ms,
+                qhps=queries * wl.heads / (ms_step * 1e-3))
+
+
+def phase_fracs(res):
+    """Each timed phase's algorithmic work over its roofline time, divided by the
+    measured time (pruning is integer work: time only)."""
+    out = {}
+    for ph, ms in res["phase_ms"].items():
+        eng, w = PHASE_ENGINE.get(ph), res["work"].get(ph, {})
+        if eng == "hbm":
+            t_roof = w["bytes"] / (PEAK["hbm_GBs"] * 1e9)
+        elif eng in ("mfma_bf16", "valu_f32") and "flop" in w:
+            t_roof = w["flop"] / (PEAK["mfma_bf16_TFs"] * 1e12)
+        else:
+            continue
+        out[ph] = t_roof / (ms * 1e-3)
+    return out
 
 
 def run_stream(torch, fs, decode_steps=200, lengths=(16384, 262144)):
@@ -583,9 +617,13 @@ def main():
     if not args.only_primary:
         for name in ALSO:
             r = run_workload(name, args.steps, args.warmup, torch, fs)
-            also[name] = {"queries_per_s": r["qps"], "ms_per_step": r["ms_step"],
+            also[name] = {"queries_per_s": r["qps"], "query_heads_per_s": r["qhps"],
+                          "ms_per_step": r["ms_step"],
                           "tflops": r["tflops"], "gflop_per_step": r["total_gflop"],
-                          "phase_ms": r["phase_ms"], "roofline": roofline(r)}
+                          "phase_ms": r["phase_ms"], "phase_ms_p10_p50_p90": r["phase_pct"],
+                          "phase_roofline_frac": phase_fracs(r), "roofline": roofline(r)}
+            if r["cold_ms"] is not None:
+                also[name]["cold_ms_per_step_p10_p50_p90"] = r["cold_ms"]
     stream = None if args.only_primary else run_stream(torch, fs)
     fsb = None if args.only_primary else run_fsb(PRIMARY, max(2, args.steps // 4), 2, torch, fs)
     wl = main_res["wl"]
@@ -608,6 +646,9 @@ def main():
         "tflops": main_res["tflops"],
         "gflop_per_step": main_res["total_gflop"],
         "phase_ms": main_res["phase_ms"],
+        "phase_ms_p10_p50_p90": main_res["phase_pct"],
+        "phase_roofline_frac": phase_fracs(main_res),
+        "query_heads_per_s": main_res["qhps"],
         "roofline": roofline(main_res),
         "rerank": roofline(main_res, "rerank"),
         "also": also,
