@@ -440,7 +440,16 @@ def cpu_baseline(name, budget_s=15.0):
         n_rows += take
     # per-query cost, with each head's summaries spread over all of its queries
     per_q = t_rows / n_rows + t_sums / n_heads / wl.n_q
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": 1.0 / per_q, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu,
             "sample": f"{n_rows} random query rows of {n_heads} head(s) of {name} "
                       f"({t_rows:.1f} s on {cores} threads) + those heads' cell summaries "
                       f"({t_sums:.2f} s, amortised over {wl.n_q} queries per head)"}
