@@ -143,9 +143,10 @@ __global__ __launch_bounds__(256) void forest_mean_kernel(const float* __restric
 {
     const long bh = blockIdx.y;
     const int per = 256 / L.d;
-    const int node = blockIdx.x * per + threadIdx.x / L.d, e = threadIdx.x % L.d;
     const int nodes = L.lev_off[L.n_levels];
-    if (node >= nodes) return;
+    // top levels first: their long serial sums start with the first blocks
+    const int node = nodes - 1 - (blockIdx.x * per + threadIdx.x / L.d), e = threadIdx.x % L.d;
+    if (node < 0) return;
     const FsbView f = fsb_view(forest, L, bh);
     const int l = fsb_level_of(L, node), j = node - L.lev_off[l];
     if (j >= (*f.m >> l)) return;
@@ -155,29 +156,34 @@ __global__ __launch_bounds__(256) void forest_mean_kernel(const float* __restric
     double s = 0.0;
     float a_best = -INFINITY;
     int t = 0;
-    // 16 leaves per round: their loads are independent and issued together, the
-    // sum still runs in ascending leaf order (leaf0 is a multiple of 16 here)
-    for (; t + 16 <= width; t += 16) {
-        const int4* c4 = reinterpret_cast<const int4*>(f.first + leaf0 + t);
-        int c[16];
+    // 32 leaves per round, the next round's cell indices loaded with this round's
+    // values; the sum still runs in ascending leaf order (leaf0 is a multiple of
+    // 32 here)
+    if (width >= 32) {
+        const int4* c4 = reinterpret_cast<const int4*>(f.first + leaf0);
+        int4 cur[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int4 v = c4[u];
-            c[4 * u] = v.x;
-            c[4 * u + 1] = v.y;
-            c[4 * u + 2] = v.z;
-            c[4 * u + 3] = v.w;
-        }
-        float x[16], av[16];
+        for (int u = 0; u < 8; ++u) cur[u] = c4[u];
+        for (; t + 32 <= width; t += 32) {
+            float x[32], av[32];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            x[u] = kb[(long)c[u] * L.d + e];
-            av[u] = a[c[u]];
-        }
+            for (int u = 0; u < 8; ++u) {
+                const int cc[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            s += (double)x[u];
-            if (av[u] > a_best) a_best = av[u];
+                for (int w = 0; w < 4; ++w) {
+                    x[4 * u + w] = kb[(long)cc[w] * L.d + e];
+                    av[4 * u + w] = a[cc[w]];
+                }
+            }
+            if (t + 64 <= width) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) cur[u] = c4[(t + 32) / 4 + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                s += (double)x[u];
+                if (av[u] > a_best) a_best = av[u];
+            }
         }
     }
     for (; t < width; ++t) {
