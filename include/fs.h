@@ -175,18 +175,20 @@ fs_status fs_rerank_workspace_size(const fs_problem* problem, int32_t keep_width
  *
  * Forest storage: fs_forest_size bytes of device memory (256-byte aligned, owned
  * by the caller) per forest, covering every (b, h); its layout is private to the
- * library.  Both calls accept at most 32768 cells. */
+ * library.  A forest depends on batch, heads, head_dim and n_ctx only, so one
+ * build serves any query range over the same cells.  The three calls accept at
+ * most 32768 cells. */
 fs_status fs_forest_size(const fs_problem* problem, size_t* bytes);
 
 /* Builds one forest per (b, h) from kbar [B][H][C][d] and amax [B][H][C] (float32,
  * as written by fs_cell_summaries).  tau: NULL for forest 0 (every cell), or
- * float32 [H] thresholds for the admitted forest (amax >= tau_h).  Overwrites
- * `forest`; nothing else is read or written. */
+ * float32 [H] thresholds for the admitted forest (amax >= tau_h).  Writes
+ * `forest` only. */
 fs_status fs_forest_build(const fs_problem* problem, const float* kbar, const float* amax,
                           const float* tau, void* forest, void* stream);
 
 /* S_i by beam search (eq. 11) in forest0 and/or forest_tau (either may be NULL,
- * not both; each built for this problem's shape).  beam in [1, 64], slack c >= 0
+ * not both; each built with this problem's batch, heads, head_dim and n_ctx).  beam in [1, 64], slack c >= 0
  * (finite), topk in [1, 64].  prior_lambda, prior_sigma: both NULL (no prior) or
  * float32 [H] (lambda_h >= 0, sigma_h > 0, not checked).  idx: int32
  * [B][H][n_q][topk], ascending, -1 padded; score (nullable): float32 eq. 7
