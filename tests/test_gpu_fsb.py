@@ -269,3 +269,21 @@ def test_f32_d64_strided_queries_and_empty_range():
     fs.fs_beam_select(empty, q, f0, ft, 6, 1.0, K, idx, sc)
     torch.cuda.synchronize()
     assert torch.equal(idx, before)
+
+
+def test_forest_serves_any_query_range():
+    """A forest depends on the cells only: built once, it gives a sub-range of
+    queries (another q_pos0 and n_q) the same rows as the full-range search."""
+    wl = small("i", n_ctx=3072, n_q=3072, topk=8)
+    inp, kbar, amax, tau = make_inputs(wl)
+    full = gpu_fsb(wl, inp, kbar, amax, tau, 8, 1.0)
+    B, H, K = wl.batch, wl.heads, wl.topk
+    lo, n = 1500, 700
+    q = torch.from_numpy(np.ascontiguousarray(inp["q"][:, :, lo:lo + n])).cuda().to(torch.bfloat16)
+    sub = fs.problem(B, H, wl.head_dim, wl.n_ctx, n, lo, wl.window, fs.FS_BF16)
+    f0 = torch.from_numpy(full["f0"]).cuda()
+    ft = torch.from_numpy(full["ft"]).cuda()
+    idx = torch.full((B, H, n, K), -7, dtype=torch.int32, device="cuda")
+    fs.fs_beam_select(sub, q, f0, ft, 8, 1.0, K, idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), full["idx"][:, :, lo:lo + n])
