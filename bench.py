@@ -273,28 +273,22 @@ FSB_BEAM, FSB_SLACK, FSB_TAU_Q = 32, 1.0, 0.7
 
 
 class FsbSetup:
-    """FS-B (section 3.4) at a workload's shape: both forests' storage, the per-head
-    admission thresholds tau_h (the 70th percentile of the head's a_c) and the
-    selection outputs.  kbar/amax are the caller's eq. 5 summaries on the device."""
+    """FS-B (section 3.4) at a workload's shape through fs.FsbSelect, with the
+    per-head admission thresholds tau_h (the 70% quantile of the head's a_c).
+    kbar/amax are the caller's eq. 5 summaries on the device."""
 
     def __init__(self, torch, fs, wl, p, kbar, amax):
-        B, H, C = wl.batch, wl.heads, wl.n_cells
-        self.fs, self.p, self.kbar, self.amax = fs, p, kbar, amax
+        H, C = wl.heads, wl.n_cells
+        self.kbar, self.amax = kbar, amax
         self.tau = torch.quantile(amax[0].reshape(H, C).float(), FSB_TAU_Q, dim=1).contiguous()
-        nb = fs.fs_forest_size(p)
-        self.f0 = torch.empty(nb, dtype=torch.uint8, device=kbar.device)
-        self.ft = torch.empty(nb, dtype=torch.uint8, device=kbar.device)
-        self.idx = torch.empty(B, H, wl.n_q, wl.topk, dtype=torch.int32, device=kbar.device)
-        self.effort = torch.empty(B, H, wl.n_q, dtype=torch.int32, device=kbar.device)
-        self.topk = wl.topk
+        self.sel = fs.FsbSelect(p, wl.topk, FSB_BEAM, FSB_SLACK, device=kbar.device)
+        self.idx, self.effort = self.sel.idx, self.sel.effort
 
     def build(self):
-        self.fs.fs_forest_build(self.p, self.kbar, self.amax, self.f0)
-        self.fs.fs_forest_build(self.p, self.kbar, self.amax, self.ft, tau=self.tau)
+        self.sel.build(self.kbar, self.amax, self.tau)
 
     def search(self, q, effort=False):
-        self.fs.fs_beam_select(self.p, q, self.f0, self.ft, FSB_BEAM, FSB_SLACK, self.topk,
-                               self.idx, None, effort=self.effort if effort else None)
+        self.sel.select(q, effort=effort)
 
 
 def run_fsb(name, steps, warmup, torch, fs):

@@ -324,6 +324,45 @@ class FsForward:
 
 
 # ---- streaming FS-L: a bounded per-head state --------------------------------------
+class FsbSelect:
+    """FS-B selection (section 3.4) for one problem shape: both forests' storage
+    and the outputs are allocated at construction; build() enqueues the two
+    forest builds (eq. 10) from the cell summaries, select() the beam search
+    (eq. 11).  The forests depend on the cells only, so one build serves any
+    query range over the same keys (pass that range's problem to select)."""
+
+    def __init__(self, prob, topk, beam=32, slack=1.0, admitted=True, device="cuda"):
+        self.prob, self.topk, self.beam, self.slack = prob, topk, beam, slack
+        nb = fs_forest_size(prob)
+        self.forest0 = torch.empty(nb, dtype=torch.uint8, device=device)
+        self.forest_tau = torch.empty(nb, dtype=torch.uint8, device=device) if admitted else None
+        B, H, nq = prob.batch, prob.heads, prob.n_q
+        self.idx = torch.empty((B, H, nq, topk), dtype=torch.int32, device=device)
+        self.score = torch.empty((B, H, nq, topk), dtype=torch.float32, device=device)
+        self.effort = torch.empty((B, H, nq), dtype=torch.int32, device=device)
+
+    def build(self, kbar, amax, tau=None, stream=None):
+        """kbar, amax: eq. 5 summaries (as fs_cell_summaries writes them); tau: the
+        admitted forest's float32 [H] thresholds (required when it was allocated)."""
+        fs_forest_build(self.prob, kbar, amax, self.forest0, stream=stream)
+        if self.forest_tau is not None:
+            if tau is None:
+                raise FsError("FsbSelect.build: the admitted forest needs tau")
+            fs_forest_build(self.prob, kbar, amax, self.forest_tau, tau=tau, stream=stream)
+
+    def select(self, q, prob=None, idx=None, score=False, effort=False, prior=None,
+               stream=None):
+        """S_i into self.idx (or `idx`, for another query range's problem `prob`).
+        score / effort: False (not written), True (into self.score / self.effort)
+        or a tensor; prior: None or (lambda, sigma) device tensors.  Returns idx."""
+        out = self.idx if idx is None else idx
+        sc = self.score if score is True else (score if score is not False else None)
+        ef = self.effort if effort is True else (effort if effort is not False else None)
+        fs_beam_select(prob or self.prob, q, self.forest0, self.forest_tau, self.beam,
+                       self.slack, self.topk, out, sc, prior=prior, effort=ef, stream=stream)
+        return out
+
+
 def fs_stream_state_size(cfg: FsStreamConfig) -> int:
     n = C.c_size_t()
     _check("fs_stream_state_size", load().fs_stream_state_size(C.byref(cfg), C.byref(n)))

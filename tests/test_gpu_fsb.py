@@ -287,3 +287,21 @@ def test_forest_serves_any_query_range():
     fs.fs_beam_select(sub, q, f0, ft, 8, 1.0, K, idx)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), full["idx"][:, :, lo:lo + n])
+
+
+def test_fsb_select_wrapper_matches_entry_points():
+    """fs.FsbSelect (allocation + the same calls) gives the entry points' rows."""
+    wl = small("j", n_ctx=2048, n_q=800, q_pos0=2048 - 800)
+    inp, kbar, amax, tau = make_inputs(wl)
+    ref = gpu_fsb(wl, inp, kbar, amax, tau, 8, 1.0)
+    prob = fs.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, wl.n_q, wl.q_pos0,
+                      wl.window, fs.FS_BF16)
+    sel = fs.FsbSelect(prob, wl.topk, beam=8, slack=1.0)
+    sel.build(torch.from_numpy(kbar).cuda(), torch.from_numpy(amax).cuda(),
+              torch.from_numpy(tau).cuda())
+    q = torch.from_numpy(inp["q"]).cuda().to(torch.bfloat16)
+    idx = sel.select(q, score=True, effort=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    assert np.array_equal(sel.score.cpu().numpy(), ref["score"])
+    assert np.array_equal(sel.effort.cpu().numpy(), ref["effort"])
