@@ -305,3 +305,21 @@ def test_fsb_select_wrapper_matches_entry_points():
     assert np.array_equal(idx.cpu().numpy(), ref["idx"])
     assert np.array_equal(sel.score.cpu().numpy(), ref["score"])
     assert np.array_equal(sel.effort.cpu().numpy(), ref["effort"])
+
+
+def test_maximum_forest_size():
+    """32768 cells (the most the calls accept: cell and node indices fill int16,
+    15 levels), from seeded summaries given to both sides, with query rows at the
+    end of a 2^20-token context."""
+    rng = np.random.default_rng(21)
+    H, d, C, n_q, K = 2, 64, 32768, 24, 16
+    n_ctx = C * 32
+    kbar = (rng.standard_normal((1, H, C, d)) * 0.18).astype(np.float32)
+    amax = (8.0 + rng.random((1, H, C)) * 2.0).astype(np.float32)
+    tau = np.array([np.quantile(amax[0, h], 0.8) for h in range(H)], np.float32)
+    q = rng.standard_normal((1, H, n_q, d)).astype(np.float32)
+    wl = synth.Workload(name="max", batch=1, heads=H, n_ctx=n_ctx, head_dim=d, dtype="f32",
+                        n_q=n_q, q_pos0=n_ctx - n_q, topk=K, budget=-1)
+    got = gpu_fsb(wl, {"q": q}, kbar, amax, tau, 16, 1.0)
+    check_rows(wl, {"q": q}, kbar, amax, tau, got, 16, 1.0, range(n_q))
+    assert (got["idx"] >= 0).all() and got["idx"].max() < C
