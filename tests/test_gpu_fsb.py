@@ -323,3 +323,34 @@ def test_maximum_forest_size():
     got = gpu_fsb(wl, {"q": q}, kbar, amax, tau, 16, 1.0)
     check_rows(wl, {"q": q}, kbar, amax, tau, got, 16, 1.0, range(n_q))
     assert (got["idx"] >= 0).all() and got["idx"].max() < C
+
+
+def test_fsb_selection_feeds_the_readout():
+    """FS-B's S_i drives eq. 9's readout like FS-L's: the GPU readout over the
+    search's cells against the oracle's readout over the oracle's FS-B cells
+    (bf16 storage, row-wise relative error <= 2e-2)."""
+    wl = small("k", head_dim=128, n_ctx=2560, n_q=640, q_pos0=2560 - 640, topk=12)
+    inp, kbar, amax, tau = make_inputs(wl)
+    got = gpu_fsb(wl, inp, kbar, amax, tau, 12, 1.0)
+    prob = fs.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, wl.n_q, wl.q_pos0, wl.window,
+                      fs.FS_BF16)
+    q, k, v = (torch.from_numpy(inp[n]).cuda().to(torch.bfloat16) for n in ("q", "k", "v"))
+    idx = torch.from_numpy(got["idx"]).cuda()
+    o_lr = torch.empty_like(q)
+    ws = torch.empty(max(fs.fs_sparse_workspace_size(prob), 1), dtype=torch.uint8, device="cuda")
+    fs.fs_sparse_attn(prob, q, k, v, idx, wl.topk, wl.rms_eps, o_lr, ws)
+    torch.cuda.synchronize()
+    o = o_lr.float().cpu().numpy()
+    orc = oracle.Oracle()
+    p = oracle.problem_from(wl)
+    worst = 0.0
+    for h in range(wl.heads):
+        f0 = orc.forest_build(kbar[0, h], amax[0, h])
+        ft = orc.forest_build(kbar[0, h], amax[0, h], float(tau[h]))
+        for t in range(0, wl.n_q, 5):
+            sel, _ = orc.beam_row(p, h, wl.q_pos0 + t, inp["q"][0, h, t], f0, ft, 12, 1.0)
+            ref = orc.sparse_row(p, inp["q"][0, h, t], inp["k"][0, h], inp["v"][0, h], sel)
+            den = np.abs(ref).max()
+            err = np.abs(o[0, h, t] - ref).max() / (den if den > 0 else 1.0)
+            worst = max(worst, err)
+    assert worst <= 2e-2, worst
