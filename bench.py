@@ -25,20 +25,32 @@ sys.path.insert(0, ROOT)
 
 from long_context_fs_amd import synth  # noqa: E402
 
-PEAK = {"hbm_GBs": 8000.0, "mfma_bf16_TFs": 2500.0, "valu_f32_TFs": 78.6, "mfma_f32_TFs": 157.3,
+# MI355X published peaks: HBM3E, dense bf16 MFMA, fp32 (vector and MFMA), fp64 vector.
+PEAK = {"hbm_GBs": 8000.0, "mfma_bf16_TFs": 2500.0, "valu_f32_TFs": 157.3, "mfma_f32_TFs": 157.3,
         "valu_f64_TFs": 78.6}
+# Threads of the oracle's CPU baseline: the host cores a one-GPU job is allotted
+# (16 per GPU), even where the machine shows more.
+CPU_SHARE = 16
 METRIC = "FreeSolo forward queries/s and TFLOP/s at N=16k/64k/256k; % of MI355X roofline"
 PRIMARY = "prefill_b1h8_n65536_d128_bf16"
-ALSO = ["prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16",
+ALSO = ["prefill_b1h1_n2048_d64_f32", "prefill_b2h16_n4096_d64_bf16",
+        "prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16",
         "prefill_b1h8_n65536_d128_bf16_prior"]
 PHASES = ["summaries", "prune", "select", "window", "sparse", "combine"]
 # Source file of each phase's kernel (for matching stored HBM traffic counters).
 PHASE_SRC = {"summaries": "summaries.hip", "prune": "prune.hip", "select": "select.hip",
              "window": "window.hip", "sparse": "sparse.hip", "combine": "combine.hip",
              "rerank": "select.hip", "fsb_beam": "fsb.hip"}
-# Engine each phase's kernel uses, which fixes the roofline it is priced against.
-PHASE_ENGINE = {"summaries": "hbm", "prune": "int", "select": "valu_f32", "window": "mfma_bf16",
-                "sparse": "mfma_bf16", "combine": "hbm", "rerank": "mfma_bf16"}
+# Engine each phase's kernel uses, which fixes the roofline it is priced against
+# (selection issues three bf16 products per algorithmic MAC, priced on the
+# algorithmic count; fp32 storage prices the matrix phases at the fp32 peak).
+PHASE_ENGINE = {"summaries": "hbm", "prune": "int", "select": "mfma", "window": "mfma",
+                "sparse": "mfma", "combine": "hbm", "rerank": "mfma"}
+
+
+def mfma_peak(wl):
+    """Peak (TFLOP/s) the matrix phases of a workload are priced against."""
+    return PEAK["mfma_bf16_TFs"] if wl.dtype == "bf16" else PEAK["mfma_f32_TFs"]
 
 
 def n_cand(wl, i):
@@ -71,6 +83,12 @@ def algorithmic_work(wl, keep_count=None, n_lo=0):
         "sparse": {"flop": float(4 * d * s * sel_cells.sum() * BH)},
         "combine": {"bytes": 3 * BH * wl.n_q * d * e},
     }
+
+
+def step_flop(work):
+    """Algorithmic FLOP of one timed step: the matrix phases the step runs (eq. 12
+    reranking is timed on its own and is not part of it)."""
+    return sum(work[ph].get("flop", 0.0) for ph in PHASES if ph in work)
 
 
 def kernel_source_sha(phase):
@@ -188,7 +206,7 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
     kc = fwd.keep_count.cpu().numpy() if fwd.pruned else None
     work = algorithmic_work(wl, kc, fwd.n_lo)
     queries = wl.batch * wl.n_q
-    total_flop = sum(w.get("flop", 0.0) for w in work.values())
+    total_flop = step_flop(work)
     if rerank_ms is not None:
         phase_avg = dict(phase_avg, rerank=rerank_ms)
     return dict(wl=wl, ms_step=ms_step, wall=wall, phase_ms=phase_avg, work=work,
@@ -205,8 +223,8 @@ def phase_fracs(res):
         eng, w = PHASE_ENGINE.get(ph), res["work"].get(ph, {})
         if eng == "hbm":
             t_roof = w["bytes"] / (PEAK["hbm_GBs"] * 1e9)
-        elif eng in ("mfma_bf16", "valu_f32") and "flop" in w:
-            t_roof = w["flop"] / (PEAK["mfma_bf16_TFs"] * 1e12)
+        elif eng == "mfma" and "flop" in w:
+            t_roof = w["flop"] / (mfma_peak(res["wl"]) * 1e12)
         else:
             continue
         out[ph] = t_roof / (ms * 1e-3)
@@ -375,12 +393,9 @@ def roofline(res, ph=None):
     if eng == "hbm":
         ach = w["bytes"] / t / 1e9
         out = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"], "unit": "GB/s"}
-    elif eng == "mfma_bf16":
-        ach = w["flop"] / t / 1e12
-        out = {"bound": "mfma", "achieved": ach, "peak": PEAK["mfma_bf16_TFs"], "unit": "TFLOP/s"}
     else:
         ach = w["flop"] / t / 1e12
-        out = {"bound": "alu", "achieved": ach, "peak": PEAK["valu_f32_TFs"], "unit": "TFLOP/s"}
+        out = {"bound": "mfma", "achieved": ach, "peak": mfma_peak(res["wl"]), "unit": "TFLOP/s"}
     out["frac"] = out["achieved"] / out["peak"]
     out["traffic"] = traffic
     out["kernel"] = ph
@@ -398,7 +413,7 @@ def cpu_baseline(name, budget_s=15.0):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores = max(1, min(cores, CPU_SHARE))
     p = oracle.problem_from(wl.replace(batch=1, heads=1))
     orc = oracle.Oracle()
     rng = np.random.default_rng(0)
@@ -443,7 +458,8 @@ def cpu_baseline(name, budget_s=15.0):
     except OSError:
         pass
     return {"value": 1.0 / per_q, "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "cpu": cpu,
+            "cpu": cpu, "cores_note": f"threads = the job's affinity cores, at most the "
+                                      f"{CPU_SHARE} host cores allotted per GPU",
             "sample": f"{n_rows} random query rows of {n_heads} head(s) of {name} "
                       f"({t_rows:.1f} s on {cores} threads) + those heads' cell summaries "
                       f"({t_sums:.2f} s, amortised over {wl.n_q} queries per head)"}

@@ -355,11 +355,28 @@ class FsbSelect:
         """S_i into self.idx (or `idx`, for another query range's problem `prob`).
         score / effort: False (not written), True (into self.score / self.effort)
         or a tensor; prior: None or (lambda, sigma) device tensors.  Returns idx."""
+        p = prob or self.prob
+        mine = self.prob
+        if prob is not None:
+            same = all(getattr(prob, f) == getattr(mine, f)
+                       for f in ("batch", "heads", "head_dim", "n_ctx", "cell", "dtype"))
+            if not same:
+                raise FsError("FsbSelect.select: prob must match the forests' batch, heads, "
+                              "head_dim, n_ctx, cell and dtype")
+        B, H, nq = p.batch, p.heads, p.n_q
+        if nq != mine.n_q and (idx is None or score is True or effort is True):
+            raise FsError("FsbSelect.select: a query range of another length needs its own "
+                          "idx (and score / effort tensors)")
         out = self.idx if idx is None else idx
         sc = self.score if score is True else (score if score is not False else None)
         ef = self.effort if effort is True else (effort if effort is not False else None)
-        fs_beam_select(prob or self.prob, q, self.forest0, self.forest_tau, self.beam,
-                       self.slack, self.topk, out, sc, prior=prior, effort=ef, stream=stream)
+        for name, t, shape in (("idx", out, (B, H, nq, self.topk)),
+                               ("score", sc, (B, H, nq, self.topk)), ("effort", ef, (B, H, nq))):
+            if t is not None and tuple(t.shape) != shape:
+                raise FsError(f"FsbSelect.select: {name} has shape {tuple(t.shape)}, "
+                              f"expected {shape}")
+        fs_beam_select(p, q, self.forest0, self.forest_tau, self.beam, self.slack, self.topk,
+                       out, sc, prior=prior, effort=ef, stream=stream)
         return out
 
 

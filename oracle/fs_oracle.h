@@ -152,6 +152,46 @@ int or_beam_row(const or_problem* p, int head, long long i, const float* q_row,
                 const or_forest* f0, const or_forest* ftau, int beam, double slack,
                 int* sel, double* score, int* n_scored);
 
+/* ---- FS-B in plain fp64 (fsb_plain.c) -------------------------------------
+ * The same readings, with fp64 node statistics from fp64 cell summaries and
+ * dot products in index order.  The caller allocates cell_of [C], prefix
+ * [C + 1], first [2C], amax / rho [2C], mu [2C * d]. */
+typedef struct {
+    int n_cells, head_dim;
+    int m;
+    int n_levels;
+    int level_start[32];
+    int* cell_of;
+    int* prefix;
+    int* first;
+    double* amax;
+    double* rho;
+    double* mu;
+} or_forest64;
+
+int or_forest64_build(const double* kbar, const double* amax, int n_cells, int d, int use_tau,
+                      double tau, or_forest64* f);
+
+/* Roots (level, index) covering the first n leaves, largest first. */
+int or_forest64_roots(const or_forest64* f, int n, int* level, int* index);
+
+double or_node64_score(const or_problem* p, int head, long long i, const float* q_row,
+                       const or_forest64* f, int level, int index, double slack);
+
+/* S_i of one query (as or_beam_row); *gap (nullable) receives the smallest
+ * relative gap of the search's cuts and of the final top-K (+inf: none). */
+int or_beam64_row(const or_problem* p, int head, long long i, const float* q_row,
+                  const or_forest64* f0, const or_forest64* ftau, int beam, double slack,
+                  int* sel, double* score, int* n_scored, double* gap);
+
+/* or_beam64_row for the query rows t in `rows` (positions q_pos0 + t) of head
+ * `head`, threaded.  Per row: sel / score [topk] in descending (score, cell)
+ * order, -1 / 0 padded; n_sel; n_scored; gap. */
+int or_beam64_rows(const or_problem* p, int head, const float* q_head, const int* rows,
+                   int n_rows, const or_forest64* f0, const or_forest64* ftau, int beam,
+                   double slack, int* sel, double* score, int* n_sel, int* n_scored,
+                   double* gap, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

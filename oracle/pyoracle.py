@@ -15,15 +15,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "fs_oracle.c")
 FSB_SRC_PATH = os.path.join(_HERE, "fsb_oracle.c")
+FSB_PLAIN_SRC_PATH = os.path.join(_HERE, "fsb_plain.c")
 
 
 def build(force: bool = True) -> str:
-    """Compile fs_oracle.c and fsb_oracle.c with gcc into liboracle.so (plain -O2,
-    no fast-math, no fp contraction)."""
+    """Compile fs_oracle.c, fsb_oracle.c and fsb_plain.c with gcc into liboracle.so
+    (plain -O2, no fast-math, no fp contraction)."""
     if force or not os.path.exists(LIB_PATH):
         tmp = LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fPIC", "-shared",
-                               "-Wall", "-o", tmp, SRC_PATH, FSB_SRC_PATH, "-lm", "-lpthread"])
+                               "-Wall", "-o", tmp, SRC_PATH, FSB_SRC_PATH, FSB_PLAIN_SRC_PATH,
+                               "-lm", "-lpthread"])
         os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
@@ -122,6 +124,96 @@ class Forest:
         return self.s.level_start[level] + index
 
 
+class _Forest64Struct(C.Structure):
+    _fields_ = [("n_cells", C.c_int), ("head_dim", C.c_int), ("m", C.c_int),
+                ("n_levels", C.c_int), ("level_start", C.c_int * 32),
+                ("cell_of", C.c_void_p), ("prefix", C.c_void_p), ("first", C.c_void_p),
+                ("amax", C.c_void_p), ("rho", C.c_void_p), ("mu", C.c_void_p)]
+
+
+class Forest64(Forest):
+    """A forest of the plain fp64 FS-B oracle (fsb_plain.c): node statistics in
+    float64, from float64 cell summaries."""
+
+    def __init__(self, n_cells: int, d: int):
+        n = max(n_cells, 1)
+        self.cell_of = np.zeros(n, np.int32)
+        self.prefix = np.zeros(n + 1, np.int32)
+        self.first = np.zeros(2 * n, np.int32)
+        self.amax = np.zeros(2 * n, np.float64)
+        self.rho = np.zeros(2 * n, np.float64)
+        self.mu = np.zeros((2 * n, d), np.float64)
+        self.s = _Forest64Struct(n_cells, d, 0, 0, (C.c_int * 32)(),
+                                 self.cell_of.ctypes.data, self.prefix.ctypes.data,
+                                 self.first.ctypes.data, self.amax.ctypes.data,
+                                 self.rho.ctypes.data, self.mu.ctypes.data)
+
+
+class PlainFsb:
+    """The plain fp64 FS-B oracle (fsb_plain.c) behind the interface of the
+    fixed-order one: forest_build, forest_roots, node_score, beam_row, plus
+    beam_rows for many rows with each row's decision gap."""
+
+    def __init__(self, orc: "Oracle"):
+        self.orc, self.L = orc, orc.L
+
+    def forest_build(self, kbar, amax, tau: float | None = None) -> Forest64:
+        kbar, amax = _f64(kbar), _f64(amax)
+        n_cells, d = kbar.shape
+        f = Forest64(n_cells, d)
+        self.L.or_forest64_build(kbar if n_cells else np.zeros((1, d)),
+                                 amax if n_cells else np.zeros(1), n_cells, d,
+                                 0 if tau is None else 1, 0.0 if tau is None else float(tau),
+                                 C.byref(f.s))
+        return f
+
+    def forest_roots(self, f: Forest64, n_leaves: int):
+        lv = np.zeros(32, np.int32)
+        ix = np.zeros(32, np.int32)
+        cnt = self.L.or_forest64_roots(C.byref(f.s), int(n_leaves), lv, ix)
+        return list(zip(lv[:cnt].tolist(), ix[:cnt].tolist()))
+
+    def node_score(self, p: Problem, head: int, i: int, q_row, f: Forest64, level: int,
+                   index: int, slack: float) -> float:
+        return self.L.or_node64_score(C.byref(p), int(head), int(i), _f32(q_row), C.byref(f.s),
+                                      int(level), int(index), float(slack))
+
+    def beam_row(self, p: Problem, head: int, i: int, q_row, f0, ftau, beam: int, slack: float,
+                 effort: bool = False, gap: bool = False):
+        sel = np.zeros(max(p.topk, 1), np.int32)
+        sc = np.zeros(max(p.topk, 1), np.float64)
+        n_scored, g = C.c_int(), C.c_double()
+        cnt = self.L.or_beam64_row(C.byref(p), int(head), int(i), _f32(q_row),
+                                   None if f0 is None else C.addressof(f0.s),
+                                   None if ftau is None else C.addressof(ftau.s),
+                                   int(beam), float(slack), sel, sc, C.byref(n_scored),
+                                   C.byref(g))
+        out = (sel[:cnt].copy(), sc[:cnt].copy())
+        if effort:
+            out += (n_scored.value,)
+        if gap:
+            out += (g.value,)
+        return out
+
+    def beam_rows(self, p: Problem, head: int, q_head, rows, f0, ftau, beam: int, slack: float,
+                  nthreads: int | None = None) -> dict:
+        """S_i of query rows `rows` (indices into q_head, positions q_pos0 + t):
+        sel / score [n, K] descending, -1 / 0 padded; n_sel, effort, gap [n]."""
+        rows = _i32(rows)
+        n, K = len(rows), p.topk
+        sel = np.empty((max(n, 1), K), np.int32)
+        sc = np.empty((max(n, 1), K), np.float64)
+        n_sel = np.empty(max(n, 1), np.int32)
+        eff = np.empty(max(n, 1), np.int32)
+        gap = np.empty(max(n, 1), np.float64)
+        self.L.or_beam64_rows(C.byref(p), int(head), _f32(q_head), rows, n,
+                              None if f0 is None else C.addressof(f0.s),
+                              None if ftau is None else C.addressof(ftau.s), int(beam),
+                              float(slack), sel, sc, n_sel, eff, gap,
+                              int(nthreads or os.cpu_count() or 1))
+        return dict(sel=sel[:n], score=sc[:n], n_sel=n_sel[:n], effort=eff[:n], gap=gap[:n])
+
+
 class Oracle:
     def __init__(self, path: str | None = None):
         path = path or LIB_PATH
@@ -168,7 +260,24 @@ class Oracle:
         L.or_beam_row.argtypes = [P, C.c_int, C.c_longlong, _F32P, C.c_void_p, C.c_void_p,
                                   C.c_int, C.c_double, _I32P, _F64P, C.POINTER(C.c_int)]
         L.or_beam_row.restype = C.c_int
+        F64 = C.POINTER(_Forest64Struct)
+        L.or_forest64_build.argtypes = [_F64P, _F64P, C.c_int, C.c_int, C.c_int, C.c_double, F64]
+        L.or_forest64_build.restype = C.c_int
+        L.or_forest64_roots.argtypes = [F64, C.c_int, _I32P, _I32P]
+        L.or_forest64_roots.restype = C.c_int
+        L.or_node64_score.argtypes = [P, C.c_int, C.c_longlong, _F32P, F64, C.c_int, C.c_int,
+                                      C.c_double]
+        L.or_node64_score.restype = C.c_double
+        L.or_beam64_row.argtypes = [P, C.c_int, C.c_longlong, _F32P, C.c_void_p, C.c_void_p,
+                                    C.c_int, C.c_double, _I32P, _F64P, C.POINTER(C.c_int),
+                                    C.POINTER(C.c_double)]
+        L.or_beam64_row.restype = C.c_int
+        L.or_beam64_rows.argtypes = [P, C.c_int, _F32P, _I32P, C.c_int, C.c_void_p, C.c_void_p,
+                                     C.c_int, C.c_double, _I32P, _F64P, _I32P, _I32P, _F64P,
+                                     C.c_int]
+        L.or_beam64_rows.restype = C.c_int
         self.L = L
+        self.plain = PlainFsb(self)
 
     # -- FS-B (section 3.4) ---------------------------------------------------
     def dot16(self, a, b) -> float:

@@ -56,3 +56,19 @@ def test_algorithmic_work_counts_pairs():
     assert w["combine"]["bytes"] == 3 * wl.n_q * d * 4
     assert w["summaries"]["bytes"] == wl.n_cells * (s * d * 4 + (d + 1) * 4)
     assert np.isclose(w["rerank"]["flop"], 2 * d * s * cand)
+
+
+def test_step_flop_is_the_timed_phases_only():
+    """The step's FLOP total is selection + window + readout; eq. 12 reranking is
+    timed on its own and stays out of it."""
+    wl = synth.get_workload("c4")
+    w = bench.algorithmic_work(wl)
+    assert bench.step_flop(w) == w["select"]["flop"] + w["window"]["flop"] + w["sparse"]["flop"]
+    assert "rerank" not in bench.PHASES
+
+
+def test_matrix_phases_are_priced_at_their_dtype_peak():
+    assert bench.mfma_peak(synth.get_workload("c1")) == 157.3      # fp32 storage
+    assert bench.mfma_peak(synth.get_workload("c4")) == 2500.0     # bf16
+    assert bench.PEAK["valu_f32_TFs"] == 157.3 and bench.PEAK["valu_f64_TFs"] == 78.6
+    assert set(bench.ALSO) >= {"prefill_b1h1_n2048_d64_f32", "prefill_b2h16_n4096_d64_bf16"}

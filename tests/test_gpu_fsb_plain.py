@@ -1,0 +1,196 @@
+"""FS-B on the GPU against the plain fp64 FS-B oracle (oracle/fsb_plain.c),
+through the whole chain the benchmark runs: fs_cell_summaries on the raw keys,
+fs_forest_build (every cell, and the cells admitted by a_c >= tau_h),
+fs_beam_select, then fs_sparse_attn over the cells found.  The oracle starts
+from the same raw keys: fp64 eq. 5 summaries, fp64 node statistics, dot
+products in index order (FreeSolo summary, picx.dev page, section 3.4,
+eqs. 10-11, and section 3.3, eqs. 5, 7, 9).
+
+The two sides round differently, so a search decision may go either way where
+the oracle's own decision is close: each oracle row records the smallest
+relative gap of its cuts (the B-th and (B+1)-th U of a beam step, the K-th and
+(K+1)-th score of the final top-K).  Rows whose gap is at least 1e-5 must give
+the same cells and the same search effort; rows below it must give a valid
+selection (distinct candidate cells, each with its eq. 7 score).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_fs_amd import fs, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+GAP = 1e-5
+THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+def admit_threshold(amax64, q=0.7):
+    """tau between two consecutive a_c near the q-quantile, far from both."""
+    a = np.sort(amax64)
+    j = max(1, min(len(a) - 1, int(q * len(a))))
+    while j < len(a) - 1 and a[j] - a[j - 1] <= 1e-4 * a[j]:
+        j += 1
+    tau = np.float32(0.5 * (a[j - 1] + a[j]))
+    assert np.abs(amax64 - float(tau)).min() > 1e-5 * float(tau)
+    return tau
+
+
+def gpu_chain(wl, inp, tau, beam, slack, prior=None, use_tau=True):
+    """Summaries, forests, search and readout on the device from raw q, k, v."""
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    prob = fs.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, wl.n_q, wl.q_pos0, wl.window,
+                      fs.FS_BF16 if wl.dtype == "bf16" else fs.FS_F32)
+    q, k, v = (torch.from_numpy(inp[n]).cuda().to(dt) for n in ("q", "k", "v"))
+    B, H, C, d, K = wl.batch, wl.heads, wl.n_cells, wl.head_dim, wl.topk
+    kbar = torch.empty((B, H, max(C, 1), d), dtype=torch.float32, device="cuda")
+    amax = torch.empty((B, H, max(C, 1)), dtype=torch.float32, device="cuda")
+    fs.fs_cell_summaries(prob, k, kbar, amax)
+    nb = fs.fs_forest_size(prob)
+    f0 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ft = torch.empty(nb, dtype=torch.uint8, device="cuda") if use_tau else None
+    fs.fs_forest_build(prob, kbar, amax, f0)
+    if use_tau:
+        fs.fs_forest_build(prob, kbar, amax, ft, tau=torch.from_numpy(tau).cuda())
+    idx = torch.full((B, H, wl.n_q, K), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, H, wl.n_q, K), dtype=torch.float32, device="cuda")
+    eff = torch.zeros((B, H, wl.n_q), dtype=torch.int32, device="cuda")
+    pr = None if prior is None else tuple(torch.from_numpy(a).cuda() for a in prior)
+    fs.fs_beam_select(prob, q, f0, ft, beam, slack, K, idx, sc, prior=pr, effort=eff)
+    o_lr = torch.empty_like(q)
+    ws_n = fs.fs_sparse_workspace_size(prob)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
+    fs.fs_sparse_attn(prob, q, k, v, idx, K, wl.rms_eps, o_lr, ws)
+    torch.cuda.synchronize()
+    return {"idx": idx.cpu().numpy(), "score": sc.cpu().numpy(), "effort": eff.cpu().numpy(),
+            "o_lr": o_lr.float().cpu().numpy()}
+
+
+def oracle_problem(wl, prior):
+    p = oracle.problem_from(wl)
+    if prior is not None:
+        oracle.with_prior(p, prior[0].astype(np.float64), prior[1].astype(np.float64))
+    return p
+
+
+def check_head(wl, inp, got, b, h, tau, beam, slack, rows, prior=None, use_tau=True,
+               readout_rows=()):
+    """Plain-oracle chain for head (b, h) over `rows`; returns (decided, near-tie)."""
+    orc = oracle.Oracle()
+    p = oracle_problem(wl, prior)
+    kbar, amax = orc.cell_summaries_head(p, inp["k"][b, h])
+    f0 = orc.plain.forest_build(kbar, amax)
+    ft = orc.plain.forest_build(kbar, amax, float(tau[h])) if use_tau else None
+    ref = orc.plain.beam_rows(p, h, inp["q"][b, h], rows, f0, ft, beam, slack, THREADS)
+    K = wl.topk
+    n_dec = n_tie = 0
+    for r, t in enumerate(rows):
+        i = wl.q_pos0 + int(t)
+        n_i = orc.n_candidates(p, i)
+        g_idx, g_sc = got["idx"][b, h, t], got["score"][b, h, t]
+        n_g = int((g_idx >= 0).sum())
+        assert (g_idx[n_g:] == -1).all() and (np.diff(g_idx[:n_g]) > 0).all(), (b, h, t)
+        assert n_g == 0 or (g_idx[0] >= 0 and g_idx[n_g - 1] < n_i), (b, h, t, g_idx, n_i)
+        # eq. 7 scores of the GPU's cells, from the oracle's fp64 summaries
+        cells = g_idx[:n_g]
+        if n_g:
+            _, _, want = orc.select_row_at(p, h, i, inp["q"][b, h, t], kbar, amax, cells)
+            np.testing.assert_allclose(g_sc[:n_g], want, rtol=GAP, atol=1e-6,
+                                       err_msg=f"scores of row {(b, h, t)}")
+        cnt = int(ref["n_sel"][r])
+        if ref["gap"][r] >= GAP:
+            want_cells = np.sort(ref["sel"][r, :cnt])
+            assert np.array_equal(cells, want_cells), (b, h, t, cells, want_cells)
+            assert got["effort"][b, h, t] == ref["effort"][r], (b, h, t)
+            n_dec += 1
+        else:
+            n_tie += 1
+    orc_rows = [t for t in readout_rows]
+    if orc_rows:
+        worst = 0.0
+        for t in orc_rows:
+            cells = got["idx"][b, h, t]
+            cells = cells[cells >= 0]
+            o = orc.sparse_row(p, inp["q"][b, h, t], inp["k"][b, h], inp["v"][b, h], cells)
+            den = np.abs(o).max()
+            err = np.abs(got["o_lr"][b, h, t] - o).max() / (den if den > 0 else 1.0)
+            worst = max(worst, err)
+        tol = 2e-2 if wl.dtype == "bf16" else 1e-4
+        assert worst <= tol, (b, h, worst)
+    return n_dec, n_tie
+
+
+def small(name, **kw):
+    base = dict(name=name, batch=1, heads=2, n_ctx=3200 + 17, head_dim=64, dtype="bf16",
+                n_q=3200 + 17, q_pos0=0, topk=8, budget=-1, seed=31)
+    base.update(kw)
+    return synth.Workload(**base)
+
+
+CASES = {
+    # name: (workload, beam, slack, prior, use the admitted forest)
+    "bf16_d64_two_forests": (small("pa"), 8, 1.0, False, True),
+    "f32_d128_prior": (small("pb", dtype="f32", head_dim=128, n_ctx=2048 + 31, n_q=700,
+                             q_pos0=2048 + 31 - 700, topk=16, prior_lambda=0.1,
+                             prior_sigma=600.0), 16, 0.5, True, True),
+    "bf16_d64_beam1_greedy": (small("pc", topk=4), 1, 0.0, False, False),
+    "bf16_d128_needle_decode": (small("pd", head_dim=128, n_ctx=8192, n_q=64,
+                                      q_pos0=8192 - 64, topk=32, structure="needle",
+                                      needle_queries=64), 32, 1.0, False, True),
+    "bf16_d64_keyscale_b2": (small("pe", batch=2, structure="key_scale", n_ctx=4096,
+                                   n_q=1024, q_pos0=3072, topk=16), 16, 1.0, False, True),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_chain_from_raw_keys(case):
+    wl, beam, slack, prior, use_tau = CASES[case]
+    inp = synth.generate(wl)
+    orc = oracle.Oracle()
+    p = oracle.problem_from(wl)
+    tau = np.array([admit_threshold(np.concatenate(
+        [orc.cell_summaries_head(p, inp["k"][b, h])[1] for b in range(wl.batch)]))
+        for h in range(wl.heads)], np.float32)
+    pr = wl.prior_arrays() if prior else None
+    got = gpu_chain(wl, inp, tau, beam, slack, pr, use_tau)
+    n_dec = n_tie = 0
+    rows = np.arange(wl.n_q)
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            d_, t_ = check_head(wl, inp, got, b, h, tau, beam, slack, rows, pr, use_tau,
+                                readout_rows=rows[::7])
+            n_dec += d_
+            n_tie += t_
+    assert n_tie <= 0.02 * (n_dec + n_tie), (n_dec, n_tie)
+
+
+def test_chain_full_head_at_benchmark_shape():
+    """The 64k prefill (B1 H8 d128 bf16, K 32, beam 32, slack 1, tau_h near the
+    70% quantile of a_c) in the launch configuration the benchmark times: every
+    one of head 0's 65536 rows and 2048 rows of head 5 against the plain oracle,
+    and the readout over the found cells on two whole 128-query tiles plus
+    sampled rows."""
+    wl = synth.get_workload("prefill_b1h8_n65536_d128_bf16")
+    inp = synth.generate(wl)
+    orc = oracle.Oracle()
+    p = oracle.problem_from(wl)
+    tau = np.array([admit_threshold(orc.cell_summaries_head(p, inp["k"][0, h])[1])
+                    for h in range(wl.heads)], np.float32)
+    got = gpu_chain(wl, inp, tau, 32, 1.0)
+    rng = np.random.default_rng(5)
+    read = np.concatenate([np.arange(30720, 30720 + 128), np.arange(wl.n_q - 128, wl.n_q),
+                           rng.integers(0, wl.n_q, 64)])
+    n_dec, n_tie = check_head(wl, inp, got, 0, 0, tau, 32, 1.0, np.arange(wl.n_q),
+                              readout_rows=read)
+    print(f"head 0: {n_dec} rows decided alike, {n_tie} near-tie rows")
+    assert n_tie <= 0.05 * wl.n_q
+    rows5 = np.sort(rng.choice(wl.n_q, 2048, replace=False))
+    d5, t5 = check_head(wl, inp, got, 0, 5, tau, 32, 1.0, rows5, readout_rows=rows5[:64])
+    assert t5 <= 0.05 * len(rows5)
+    assert (got["idx"][:, :, :wl.window + wl.cell] == -1).all()

@@ -10,6 +10,9 @@ eqs. 10-11) against facts that do not come from the oracle itself.
   Schwarz and the monotone erf), so the bound must hold for every node;
 - the roots of a prefix are its binary decomposition;
 - the fixed-order dot product against an exact rational sum.
+
+Every pin except the last runs on both FS-B oracles: the fixed-order one
+(fsb_oracle.c, float32 node statistics) and the plain fp64 one (fsb_plain.c).
 """
 import json
 import math
@@ -24,13 +27,30 @@ from oracle import make_problem, with_prior
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fsb_hand_cases.json")
 
 
+class _Plain:
+    """The plain fp64 FS-B oracle with the FS-L oracle's other calls."""
+
+    def __init__(self, orc):
+        self.orc, self.plain = orc, orc.plain
+
+    def __getattr__(self, name):
+        if name in ("forest_build", "forest_roots", "node_score", "beam_row"):
+            return getattr(self.plain, name)
+        return getattr(self.orc, name)
+
+
+@pytest.fixture(params=["fixed_order", "plain_fp64"])
+def fsb(request, orc):
+    return orc if request.param == "fixed_order" else _Plain(orc)
+
+
 def _summaries(rng, n_cells, d):
     kbar = (rng.standard_normal((n_cells, d)) * 0.25).astype(np.float32)
     amax = (8.0 + 2.0 * rng.random(n_cells)).astype(np.float32)
     return kbar, amax
 
 
-def test_golden_fsb(orc):
+def test_golden_fsb(fsb):
     g = json.load(open(GOLDEN))
     d = 16
     kbar = np.zeros((4, d), np.float32)
@@ -40,18 +60,18 @@ def test_golden_fsb(orc):
     for case in g["cases"]:
         p = make_problem(head_dim=d, n_ctx=4 * 32, window=512, topk=case["topk"])
         am = np.array(case["tau_amax"] or [1, 1, 1, 1], np.float32)
-        f0 = None if case.get("tau_only") else orc.forest_build(kbar, am)
-        ft = None if case["tau"] is None else orc.forest_build(kbar, am, case["tau"])
-        sel, sc = orc.beam_row(p, 0, g["query_pos"], q, f0, ft, case["beam"], case["slack"])
+        f0 = None if case.get("tau_only") else fsb.forest_build(kbar, am)
+        ft = None if case["tau"] is None else fsb.forest_build(kbar, am, case["tau"])
+        sel, sc = fsb.beam_row(p, 0, g["query_pos"], q, f0, ft, case["beam"], case["slack"])
         assert sel.tolist() == case["sel"], case["why"]
         np.testing.assert_allclose(sc, case["score"], rtol=0, atol=1e-12)
 
 
-def test_golden_forest_stats(orc):
+def test_golden_forest_stats(fsb):
     g = json.load(open(GOLDEN))
     kbar = np.zeros((4, 16), np.float32)
     kbar[:, 0] = g["kbar0"]
-    f = orc.forest_build(kbar, np.ones(4, np.float32))
+    f = fsb.forest_build(kbar, np.ones(4, np.float32))
     assert (f.m, f.n_levels) == (4, 3)
     assert f.mu[f.node(1, 0), 0] == 0 and f.rho[f.node(1, 0)] == 5
     assert f.mu[f.node(1, 1), 0] == 4 and f.rho[f.node(1, 1)] == 0
@@ -59,10 +79,10 @@ def test_golden_forest_stats(orc):
 
 
 @pytest.mark.parametrize("n", [0, 1, 2, 3, 7, 8, 13, 64, 100, 1023])
-def test_roots_are_binary_decomposition(orc, n):
+def test_roots_are_binary_decomposition(fsb, n):
     kbar, amax = _summaries(np.random.default_rng(1), 1024, 16)
-    f = orc.forest_build(kbar, amax)
-    roots = orc.forest_roots(f, n)
+    f = fsb.forest_build(kbar, amax)
+    roots = fsb.forest_roots(f, n)
     sizes = [1 << lv for lv, _ in roots]
     assert sizes == [1 << b for b in reversed(range(11)) if (n >> b) & 1]
     start = 0
@@ -72,11 +92,11 @@ def test_roots_are_binary_decomposition(orc, n):
     assert start == n
 
 
-def test_node_statistics_match_definitions(orc):
+def test_node_statistics_match_definitions(fsb):
     rng = np.random.default_rng(2)
     kbar, amax = _summaries(rng, 77, 64)
     for tau in (None, 9.0):
-        f = orc.forest_build(kbar, amax, tau)
+        f = fsb.forest_build(kbar, amax, tau)
         cells = np.arange(77) if tau is None else np.nonzero(amax >= tau)[0]
         assert f.m == len(cells) and f.cell_of[:f.m].tolist() == cells.tolist()
         assert f.prefix.tolist() == [int(np.sum(cells < n)) for n in range(78)]
@@ -113,86 +133,86 @@ def _wide_problem(n_cells, d, topk, prior):
 
 
 @pytest.mark.parametrize("prior", [False, True])
-def test_exhaustive_beam_equals_eq7_topk(orc, prior):
+def test_exhaustive_beam_equals_eq7_topk(fsb, prior):
     """A beam that never drops a node finds every leaf, so S_i is eq. 7's top-K
     over C_i: compared with the FS-L oracle's selection (sets and scores)."""
     rng = np.random.default_rng(4)
     n_cells, d, topk = 150, 64, 12
     kbar, amax = _summaries(rng, n_cells, d)
     p = _wide_problem(n_cells, d, topk, prior)
-    f0 = orc.forest_build(kbar, amax)
+    f0 = fsb.forest_build(kbar, amax)
     for _ in range(25):
         i = int(rng.integers(512, 512 + 32 * n_cells + 40))
         q = rng.standard_normal(d).astype(np.float32)
-        n = orc.n_candidates(p, i)
-        sel, sc = orc.beam_row(p, 0, i, q, f0, None, 2 * n_cells, 0.0)
-        ref, _, ref_sc = orc.select_row_at(p, 0, i, q, kbar.astype(np.float64),
+        n = fsb.n_candidates(p, i)
+        sel, sc = fsb.beam_row(p, 0, i, q, f0, None, 2 * n_cells, 0.0)
+        ref, _, ref_sc = fsb.select_row_at(p, 0, i, q, kbar.astype(np.float64),
                                            amax.astype(np.float64), np.arange(n, dtype=np.int32))
         assert sorted(sel.tolist()) == sorted(ref.tolist())
         np.testing.assert_allclose(sc, np.sort(ref_sc)[::-1][:len(sc)], rtol=1e-12, atol=1e-12)
         assert np.all(np.diff(sc) <= 0)
 
 
-def test_exhaustive_admitted_forest_brute_force(orc):
+def test_exhaustive_admitted_forest_brute_force(fsb):
     rng = np.random.default_rng(5)
     n_cells, d, topk, tau = 120, 64, 10, 9.2
     kbar, amax = _summaries(rng, n_cells, d)
     p = _wide_problem(n_cells, d, topk, False)
-    ft = orc.forest_build(kbar, amax, tau)
-    f0 = orc.forest_build(kbar, amax)
+    ft = fsb.forest_build(kbar, amax, tau)
+    f0 = fsb.forest_build(kbar, amax)
     for _ in range(20):
         i = int(rng.integers(512, 512 + 32 * n_cells))
         q = rng.standard_normal(d).astype(np.float32)
-        n = orc.n_candidates(p, i)
+        n = fsb.n_candidates(p, i)
         scores = kbar[:n].astype(np.float64) @ q.astype(np.float64) / 8.0
         adm = np.nonzero(amax[:n] >= tau)[0]
-        sel, _ = orc.beam_row(p, 0, i, q, None, ft, 2 * n_cells, 0.0)
+        sel, _ = fsb.beam_row(p, 0, i, q, None, ft, 2 * n_cells, 0.0)
         assert sorted(sel.tolist()) == sorted(adm[np.argsort(-scores[adm])][:topk].tolist())
         # both forests, exhaustive: the admitted cells are a subset, so eq. 7 over C_i
-        sel2, _ = orc.beam_row(p, 0, i, q, f0, ft, 2 * n_cells, 0.0)
+        sel2, _ = fsb.beam_row(p, 0, i, q, f0, ft, 2 * n_cells, 0.0)
         assert sorted(sel2.tolist()) == sorted(np.argsort(-scores)[:topk].tolist())
 
 
 @pytest.mark.parametrize("prior", [False, True])
-def test_slack_one_bounds_every_leaf(orc, prior):
+def test_slack_one_bounds_every_leaf(fsb, prior):
     """Eq. 11 with c = 1: q.mu + |q| rho >= q.kbar_c (Cauchy-Schwarz) and
     A_v g(i - p_min) >= a_c g(i - p_c) (erf increasing, g >= 0 on C_i)."""
     rng = np.random.default_rng(6)
     n_cells, d = 64, 64
     kbar, amax = _summaries(rng, n_cells, d)
     p = _wide_problem(n_cells, d, 8, prior)
-    f = orc.forest_build(kbar, amax)
+    f = fsb.forest_build(kbar, amax)
     i = 512 + 32 * n_cells
     for _ in range(5):
         q = rng.standard_normal(d).astype(np.float32)
-        leaf = [orc.node_score(p, 0, i, q, f, 0, j, 1.0) for j in range(f.m)]
+        leaf = [fsb.node_score(p, 0, i, q, f, 0, j, 1.0) for j in range(f.m)]
         for lv in range(1, f.n_levels):
             for j in range(f.m >> lv):
-                u = orc.node_score(p, 0, i, q, f, lv, j, 1.0)
+                u = fsb.node_score(p, 0, i, q, f, lv, j, 1.0)
                 assert u >= max(leaf[j << lv:(j + 1) << lv]) - 1e-12
         # a leaf's U is eq. 7's score
-        _, _, ref = orc.select_row_at(p, 0, i, q, kbar.astype(np.float64),
+        _, _, ref = fsb.select_row_at(p, 0, i, q, kbar.astype(np.float64),
                                       amax.astype(np.float64), np.arange(n_cells, dtype=np.int32))
         np.testing.assert_allclose(leaf, ref, rtol=1e-12, atol=1e-12)
 
 
-def test_empty_and_narrow(orc):
+def test_empty_and_narrow(fsb):
     rng = np.random.default_rng(7)
     kbar, amax = _summaries(rng, 40, 64)
     p = _wide_problem(40, 64, 8, False)
-    f0 = orc.forest_build(kbar, amax)
+    f0 = fsb.forest_build(kbar, amax)
     q = rng.standard_normal(64).astype(np.float32)
-    sel, _ = orc.beam_row(p, 0, 100, q, f0, None, 8, 1.0)        # i < w: C_i empty
+    sel, _ = fsb.beam_row(p, 0, 100, q, f0, None, 8, 1.0)        # i < w: C_i empty
     assert len(sel) == 0
-    sel, _ = orc.beam_row(p, 0, 512 + 32 * 3, q, f0, None, 8, 1.0)   # n_i = 3 < K
+    sel, _ = fsb.beam_row(p, 0, 512 + 32 * 3, q, f0, None, 8, 1.0)   # n_i = 3 < K
     assert sorted(sel.tolist()) == [0, 1, 2]
-    ft = orc.forest_build(kbar, amax, 100.0)                     # nothing admitted
+    ft = fsb.forest_build(kbar, amax, 100.0)                     # nothing admitted
     assert ft.m == 0
-    sel, _ = orc.beam_row(p, 0, 512 + 32 * 40, q, None, ft, 8, 1.0)
+    sel, _ = fsb.beam_row(p, 0, 512 + 32 * 40, q, None, ft, 8, 1.0)
     assert len(sel) == 0
 
 
-def test_search_effort_closed_form(orc):
+def test_search_effort_closed_form(fsb):
     """Nodes scored by one forest's search: the roots, plus two per inner node of
     each step's beam.  With a beam that never drops a node (width >= leaves), every
     node of the covering trees is scored exactly once: 2 * 2^l - 1 per root of
@@ -201,14 +221,43 @@ def test_search_effort_closed_form(orc):
     n_cells, d = 90, 64
     kbar, amax = _summaries(rng, n_cells, d)
     p = _wide_problem(n_cells, d, 8, False)
-    f0 = orc.forest_build(kbar, amax)
+    f0 = fsb.forest_build(kbar, amax)
     for n in (1, 5, 16, 37, 90):
         i = 512 + 32 * n
         q = rng.standard_normal(d).astype(np.float32)
-        *_, e = orc.beam_row(p, 0, i, q, f0, None, 2 * n_cells, 0.0, effort=True)
-        assert e == sum(2 * (1 << lv) - 1 for lv, _ in orc.forest_roots(f0, n))
+        *_, e = fsb.beam_row(p, 0, i, q, f0, None, 2 * n_cells, 0.0, effort=True)
+        assert e == sum(2 * (1 << lv) - 1 for lv, _ in fsb.forest_roots(f0, n))
         # a beam of width 1 scores the roots, then two children per level below the
         # best root: at most roots + 2 * (its level)
-        *_, e1 = orc.beam_row(p, 0, i, q, f0, None, 1, 0.0, effort=True)
-        roots = orc.forest_roots(f0, n)
+        *_, e1 = fsb.beam_row(p, 0, i, q, f0, None, 1, 0.0, effort=True)
+        roots = fsb.forest_roots(f0, n)
         assert len(roots) <= e1 <= len(roots) + 2 * max(lv for lv, _ in roots)
+
+
+@pytest.mark.parametrize("prior", [False, True])
+def test_plain_and_fixed_order_agree_where_decided(orc, prior):
+    """The two FS-B oracles round differently (fp64 from fp64 summaries against a
+    fixed order on float32 statistics), so they may part only at a near-tie
+    decision: every row whose plain-oracle gap is at least 1e-5 selects the same
+    cells with the same search effort."""
+    rng = np.random.default_rng(9)
+    n_cells, d, topk = 300, 64, 8
+    kb64 = rng.standard_normal((n_cells, d)) * 0.2
+    am64 = 8.0 + 2.0 * rng.random(n_cells)
+    p = _wide_problem(n_cells, d, topk, prior)
+    tau = float(np.float32(np.quantile(am64, 0.6)))
+    pf0, pft = orc.plain.forest_build(kb64, am64), orc.plain.forest_build(kb64, am64, tau)
+    kb32, am32 = kb64.astype(np.float32), am64.astype(np.float32)
+    f0, ft = orc.forest_build(kb32, am32), orc.forest_build(kb32, am32, tau)
+    qs = rng.standard_normal((400, d)).astype(np.float32)
+    p.q_pos0 = 512 + 32 * n_cells - 400
+    ref = orc.plain.beam_rows(p, 0, qs, np.arange(400), pf0, pft, 6, 1.0, 4)
+    decided = 0
+    for t in range(400):
+        sel, _, eff = orc.beam_row(p, 0, p.q_pos0 + t, qs[t], f0, ft, 6, 1.0, effort=True)
+        if ref["gap"][t] < 1e-5:
+            continue
+        decided += 1
+        assert sorted(sel.tolist()) == sorted(ref["sel"][t, :ref["n_sel"][t]].tolist()), t
+        assert eff == ref["effort"][t], t
+    assert decided >= 390
