@@ -735,3 +735,33 @@ def test_decode_rows_equal_prefill_rows(n_ctx):
         want = pre[n][:, :, n_ctx - nq:].view(np.uint16).astype(np.uint32) << 16
         err = row_rel_err(got.view(np.float32), want.view(np.float32))
         assert err.max() <= 1e-2, (n, err.max())
+
+
+@pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n].dtype == "bf16"])
+def test_small_sparse_unsplit(name):
+    """The readout without a split workspace (one workgroup per 128-query tile,
+    ragged last tile) on every row against the oracle's eq. 9 rows over the
+    GPU's cells, and bit for bit on a repeat."""
+    from long_context_fs_amd import fs as fsb
+    wl, x, g, ref = small_case(name)
+    q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+    fwd = FsForward.for_workload(wl)
+    idx = torch.from_numpy(g["idx"]).cuda()
+    outs = []
+    for _ in range(2):
+        o = torch.full_like(fwd.o_lr, float("nan"))
+        fsb.fs_sparse_attn(fwd.prob, q, k, v, idx, wl.topk, wl.rms_eps, o, None)
+        torch.cuda.synchronize()
+        outs.append(o.float().cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+    rows = all_rows(wl)
+    p = oracle.problem_from(wl)
+    want = np.stack([orc().sparse_row(p, x["q"][b, h, t], x["k"][b, h], x["v"][b, h],
+                                      g["idx"][b, h, t][g["idx"][b, h, t] >= 0])
+                     for b, h, t in rows])
+    got = np.stack([outs[0][b, h, t] for b, h, t in rows])
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, want)
+    assert err.max() <= TOL[wl.dtype], err.max()
+    none = np.array([(g["idx"][b, h, t] < 0).all() for b, h, t in rows])
+    assert (got[none] == 0).all()
