@@ -30,7 +30,8 @@
  * Conventions for every call:
  *   - All pointers except `problem` are DEVICE pointers, 16-byte aligned, owned
  *     by the caller.  The library allocates nothing and keeps no state between
- *     calls; calls are reentrant.
+ *     calls; calls are reentrant.  (The one exception is fs_sparse_attn_noalloc,
+ *     whose scratch is a fixed device array of the library, one per GPU.)
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *     work; results are valid in stream order.
  *   - q, k, v, o_sr, o_lr and o hold elements of `problem->dtype`, addressed as
@@ -231,6 +232,21 @@ fs_status fs_sparse_workspace_size(const fs_problem* problem, size_t* bytes);
 fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
                          const int32_t* idx, int32_t topk, float rms_eps, void* workspace,
                          size_t ws_bytes, void* o_lr, void* stream);
+
+/* fs_sparse_attn for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * readout as fs_sparse_attn with a workspace of fs_sparse_workspace_size bytes,
+ * with the split states held in a device array the library owns (48 MiB per GPU,
+ * kept until the process ends) instead of a caller workspace.  It calls no
+ * allocating routine.  A shape whose split states exceed 48 MiB returns
+ * FS_ERR_UNSUPPORTED and runs nothing (the 256k decode shape, 8 heads x 256
+ * queries x 32 splits x 520 bytes, needs 34 MiB).  Every call on one GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must not be issued; the array keeps the last call's
+ * states, which the next call overwrites before reading. */
+fs_status fs_sparse_attn_noalloc(const fs_problem* problem, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, int32_t topk, float rms_eps,
+                                 void* o_lr, void* stream);
 
 /* Range combination, eq. 2: o = o_sr + alpha[h] * o_lr.  alpha: float32 [H]. */
 fs_status fs_combine(const fs_problem* problem, const void* o_sr, const void* o_lr,

@@ -357,6 +357,32 @@ fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k
                     "fs_sparse_attn");
 }
 
+fs_status fs_sparse_attn_noalloc(const fs_problem* problem, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, int32_t topk, float rms_eps,
+                                 void* o_lr, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(q); FS_PTR(k); FS_PTR(v); FS_PTR(o_lr);
+    if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
+    if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
+    if (!(rms_eps >= 0.0f)) return fail(FS_ERR_INVALID, "rms_eps must be >= 0");
+    const size_t need = fs::sparse_ws_bytes(sh);
+    if (need > fs::kSparseNoAllocBytes)
+        return fail(FS_ERR_UNSUPPORTED,
+                    "the split readout needs %zu bytes of scratch, more than the %zu the "
+                    "allocation-free call holds", need, fs::kSparseNoAllocBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        hipError_t e;
+        ws = fs::sparse_noalloc_scratch(&e);
+        if (!ws) return from_hip(e, "fs_sparse_attn_noalloc: scratch address");
+    }
+    return from_hip(fs::launch_sparse(sh, q, k, v, idx, topk, rms_eps, ws, o_lr,
+                                      (hipStream_t)stream),
+                    "fs_sparse_attn_noalloc");
+}
+
 }  // extern "C"
 
 namespace {

@@ -76,6 +76,10 @@ hipError_t launch_rope_table(const Shape& sh, double rope_base, void* table, hip
 // the workspace bytes of their partial softmax states.
 int sparse_splits(const Shape& sh);
 size_t sparse_ws_bytes(const Shape& sh);
+// The allocation-free readout's scratch: its size, and this device's address of
+// it (looked up once per device; nullptr and *err set on failure).
+constexpr size_t kSparseNoAllocBytes = (size_t)48 << 20;
+void* sparse_noalloc_scratch(hipError_t* err);
 
 hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const void* v,
                          const int32_t* idx, int topk, float rms_eps, void* ws, void* o_lr,

@@ -15,11 +15,45 @@
 // divide by the softmax sum, RMSNorm over d with a 4-lane reduction, store.
 // f32 storage (or when the union bookkeeping would not fit in 64 KiB of LDS):
 // one wavefront per query.
+#include <mutex>
+
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 #include "mfma_tile.hpp"
 
+// Scratch of the allocation-free readout (fs_sparse_attn_noalloc): the partial
+// softmax states of a split readout, in device memory each GPU holds for the
+// life of the process.  Host code never uses this name as an address; it uses
+// the per-device pointer hipGetSymbolAddress returns (sparse_noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[fs::kSparseNoAllocBytes];
+
 namespace fs {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+void* sparse_noalloc_scratch(hipError_t* err)
+{
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *err = hipSuccess;
+    return g_scratch_ptr[dev];
+}
 
 // One wavefront per query row; lanes take two selected cells (64 tokens) at a time.
 template <class E, int D>

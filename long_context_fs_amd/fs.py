@@ -19,7 +19,8 @@ CELL = 32
 
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
            "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
-           "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size", "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
+           "fs_sparse_attn_noalloc", "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size",
+           "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
            "fs_stream_step", "fs_forest_size", "fs_forest_build", "fs_beam_select",
            "fs_status_string", "fs_last_error")
 
@@ -74,6 +75,7 @@ def load(path: str | None = None):
         "fs_window_attn": [P, vp, vp, vp, f32, vp, C.c_size_t, vp, vp],
         "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, C.c_size_t, vp, vp],
+        "fs_sparse_attn_noalloc": [P, vp, vp, vp, vp, i32, f32, vp, vp],
         "fs_combine": [P, vp, vp, vp, vp, vp],
         "fs_forest_size": [P, C.POINTER(C.c_size_t)],
         "fs_forest_build": [P, vp, vp, vp, vp, vp],
@@ -247,6 +249,14 @@ def fs_sparse_attn(prob, q, k, v, idx, topk, rms_eps, o_lr, workspace=None, stre
     _check("fs_sparse_attn", load().fs_sparse_attn(C.byref(prob), _p(q), _p(k), _p(v), _p(idx),
                                                    topk, float(rms_eps), ws, nbytes, _p(o_lr),
                                                    _s(stream)))
+
+
+def fs_sparse_attn_noalloc(prob, q, k, v, idx, topk, rms_eps, o_lr, stream=None):
+    """fs_sparse_attn with the split states in the library's own device array (no
+    workspace, no allocation)."""
+    _check("fs_sparse_attn_noalloc",
+           load().fs_sparse_attn_noalloc(C.byref(prob), _p(q), _p(k), _p(v), _p(idx), topk,
+                                         float(rms_eps), _p(o_lr), _s(stream)))
 
 
 def fs_combine(prob, o_sr, o_lr, alpha, o, stream=None):

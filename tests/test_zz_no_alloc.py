@@ -1,0 +1,61 @@
+"""The allocation-free readout (fs_sparse_attn_noalloc, include/fs.h) against
+fs_sparse_attn with a caller workspace: two calls in a row on the split
+(decode) path, the second on a smaller problem, must give the same o_lr bit for
+bit (the same kernels, splits and states, the states held in the library's
+device array instead of the workspace), and the workspace path must match the
+oracle's eq. 9 rows (FreeSolo summary, picx.dev page, section 3.3)."""
+import numpy as np
+import pytest
+
+import oracle
+from long_context_fs_amd import fs, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _run(wl, seed):
+    x = synth.generate(wl, seed)
+    q, k, v = (torch.from_numpy(x[n]).cuda().to(torch.bfloat16) for n in ("q", "k", "v"))
+    fwd = fs.FsForward.for_workload(wl)
+    fwd(q, k, v, torch.from_numpy(x["alpha"]).cuda())
+    assert fwd.ws_sparse is not None                   # the decode shape splits
+    ref = torch.full_like(fwd.o_lr, float("nan"))
+    fs.fs_sparse_attn(fwd.prob, q, k, v, fwd.idx, wl.topk, wl.rms_eps, ref, fwd.ws_sparse)
+    got = torch.full_like(fwd.o_lr, float("nan"))
+    fs.fs_sparse_attn_noalloc(fwd.prob, q, k, v, fwd.idx, wl.topk, wl.rms_eps, got)
+    torch.cuda.synchronize()
+    return x, fwd.idx.cpu().numpy(), ref.float().cpu().numpy(), got.float().cpu().numpy()
+
+
+def test_noalloc_equals_workspace_twice():
+    big = synth.WORKLOADS["decode_b1h8_n262144_q256_d128_bf16"].replace(
+        n_ctx=65536, q_pos0=65536 - 256)
+    small = big.replace(heads=2, n_ctx=20000, n_q=77, q_pos0=20000 - 77, needle_queries=77,
+                        budget=96)
+    for wl, seed in ((big, 5), (small, 6)):
+        x, idx, ref, got = _run(wl, seed)
+        assert np.isfinite(got).all()
+        np.testing.assert_array_equal(got, ref)
+        p = oracle.problem_from(wl)
+        orc = oracle.Oracle()
+        for h in range(wl.heads):
+            for t in range(0, wl.n_q, 17):
+                cells = idx[0, h, t][idx[0, h, t] >= 0]
+                want = orc.sparse_row(p, x["q"][0, h, t], x["k"][0, h], x["v"][0, h], cells)
+                err = np.abs(got[0, h, t] - want).max() / max(np.abs(want).max(), 1e-30)
+                assert err <= 2e-2, (wl.n_ctx, h, t, err)
+
+
+def test_noalloc_rejects_oversized_states():
+    """A split readout whose states exceed the 48 MiB array is refused."""
+    # 170 heads x 3 query tiles: 510 workgroups, so two splits of 384 rows each
+    prob = fs.problem(1, 170, 128, 4096, 384, 4096 - 384, 512, fs.FS_BF16)
+    need = fs.fs_sparse_workspace_size(prob)
+    assert need > 48 << 20
+    dummy = torch.zeros(16, dtype=torch.int32, device="cuda")
+    with pytest.raises(fs.FsError, match="48|scratch"):
+        fs.fs_sparse_attn_noalloc(prob, dummy, dummy, dummy, dummy, 8, 1e-6, dummy)
