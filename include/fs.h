@@ -298,6 +298,13 @@ fs_status fs_stream_step(const fs_stream_config* cfg, void* state, size_t state_
 const char* fs_status_string(fs_status status);
 const char* fs_last_error(void);
 
+/* The kernel path the calling thread's last readout, window, selection or
+ * reranking call chose: the MFMA kernels (and their split count), or a row-wise
+ * fallback and its reason (fp32 storage, a union wider than the MFMA kernels'
+ * register blocks, too little LDS, too many cells).  Empty before any such
+ * call; valid until the thread's next call. */
+const char* fs_last_path(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,7 @@
 namespace {
 
 thread_local char g_err[512];
+thread_local char g_path[256];
 
 fs_status fail(fs_status st, const char* fmt, ...)
 {
@@ -92,6 +93,16 @@ fs_status check_problem(const fs_problem* p, fs::Shape* sh)
 }  // namespace
 
 namespace fs {
+void note_path(const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_path, sizeof(g_path), fmt, ap);
+    va_end(ap);
+}
+}  // namespace fs
+
+namespace fs {
 void candidate_rows(const Shape& sh, int* n_lo, int* n_rows)
 {
     auto ncand = [&](long i) -> int {
@@ -123,6 +134,8 @@ const char* fs_status_string(fs_status s)
 }
 
 const char* fs_last_error(void) { return g_err; }
+
+const char* fs_last_path(void) { return g_path; }
 
 fs_status fs_cell_summaries(const fs_problem* problem, const void* k, float* kbar, float* amax,
                             void* stream)

@@ -7,6 +7,10 @@
 
 namespace fs {
 
+// Records, for fs_last_path(), which kernel path the calling thread's current
+// call takes (printf-style).
+void note_path(const char* fmt, ...);
+
 // Validated problem shape, as the kernels see it.
 struct Shape {
     int B, H, d, N, nq, q_pos0, s, w;

@@ -1347,6 +1347,7 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
             offs_ok) {
             dim3 grid((unsigned)((sh.nq + 127) / 128 * sh.B * sh.H));
             const int nb_need = uc / 16;
+            note_path("rerank: MFMA, 128 queries per workgroup, scores in the workspace");
 #define FS_RERANK32(D, NB)                                                                      \
             hipLaunchKernelGGL((rerank32_kernel<D, NB>), grid, dim3(256), lds, st,              \
                                (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2],                 \
@@ -1380,6 +1381,7 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
                                                                       topk)
                               ? select_splits(sh, keep != nullptr, keep_w) : 1;
             if (S > 1) {
+                note_path("select: MFMA, union split over %d workgroups, then a merge", S);
                 int32_t* ws_cell = static_cast<int32_t*>(ws);
                 float* ws_val = reinterpret_cast<float*>(ws_cell + (size_t)sh.B * sh.H * sh.nq * S * topk);
                 dim3 grid_s((unsigned)((sh.nq + 63) / 64 * S * sh.B * sh.H));
@@ -1401,6 +1403,7 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
             }
             dim3 grid((unsigned)((sh.nq + 63) / 64 * sh.B * sh.H));
             const int nb_need = uc / 16;
+            note_path("%s: MFMA, 64 queries per workgroup", rerank ? "rerank" : "select");
 #define FS_SELECT_MFMA(D, NB)                                                                   \
             if (rerank)                                                                         \
                 hipLaunchKernelGGL((rerank_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,  \
@@ -1426,6 +1429,14 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
 #undef FS_SELECT_MFMA
             return hipGetLastError();
         }
+    }
+    {
+        const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
+        note_path("%s: row-wise, one wavefront per query (%s)", rerank ? "rerank" : "select",
+                  !sh.bf16 ? "fp32 storage"
+                  : sh.C > kSelMaxCells ? "more than 32768 cells"
+                  : u_cap > 16 * kSelMaxBlocks ? "candidate union wider than 528 cells"
+                  : "bookkeeping exceeds 64 KiB of LDS");
     }
     const int cap = keep ? keep_w : (n_hi > 0 ? n_hi : 1);
     // As many waves (query rows) per block as fit in 64 KiB of LDS.

@@ -648,6 +648,7 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
         float* ws_acc = S > 1 ? static_cast<float*>(ws) : nullptr;
         float2* ws_ml = S > 1 ? reinterpret_cast<float2*>(ws_acc + rows_all * S * sh.d) : nullptr;
         const long n_tiles = (sh.nq + kSpQ - 1) / kSpQ;
+        note_path("readout: MFMA tiles of 128 queries over their union, %d split(s)", S);
         dim3 grid((unsigned)(n_tiles * S * sh.B * sh.H)), block(256);
 #define FS_SPARSE_MFMA(D)                                                                         \
         hipLaunchKernelGGL((sparse_attn_mfma_kernel<D>), grid, block, lds, st,                    \
@@ -662,6 +663,10 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
         if (err != hipSuccess || S <= 1) return err;
         return launch_split_merge(sh, S, ws_acc, ws_ml, true, rms_eps, o_lr, st);
     }
+    note_path("readout: row-wise, one wavefront per query (%s)",
+              !sh.bf16 ? "fp32 storage"
+              : sh.C > kSpMaxCells ? "more than 32768 cells"
+              : "the union bookkeeping exceeds 160 KiB of LDS");
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
 #define FS_SPARSE(E, D)                                                                          \
     hipLaunchKernelGGL((sparse_attn_rowwise_kernel<E, D>), grid, block, 0, st,                   \

@@ -13,7 +13,12 @@
 // mfma_tile.hpp).  Queries are rotated by R(i - i0) once and kept in registers
 // as MFMA B operands.  The rotated q and k are no longer the exact bf16 inputs,
 // so they are carried in fp16 (11-bit mantissa: 8x less rounding than bf16 at
-// the same MFMA rate); this requires rotated elements below 65504 in magnitude.
+// the same MFMA rate).  fp16 stops at 65504, so each wave's queries and each key
+// tile are scaled by a power of two 2^-e before packing, e the smallest shift
+// that keeps every rotated element below 2^15 (taken from the bf16 exponents;
+// blocks of tiny values are scaled up instead; 0 for ordinary inputs), and the
+// logits by 2^(e_q + e_k) after the product: exact, and any finite bf16 input
+// gives a finite output.
 // Per tile a wave computes S^T = K Q^T (16x16x32 fp16 MFMA, fp32 accumulate),
 // masks to max(0, i-w) <= j <= i, runs the online
 // softmax in fp32 (exp2 with log2(e)/sqrt(d) folded into the scale), and
@@ -175,14 +180,45 @@ __device__ __forceinline__ uint32_t rotate_pack(uint32_t xy, float c, float s)
     return mf::pack_f16x2(x * c - y * s, x * s + y * c);
 }
 
+// Largest biased exponent field of the 8 bf16 values in u.
+__device__ __forceinline__ uint32_t max_bf16_exp(const uint4& u)
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = mf::word_of(u, i);
+        m = max(m, max((w >> 7) & 0xFFu, (w >> 23) & 0xFFu));
+    }
+    return m;
+}
+
+// Shift e of a block whose largest bf16 exponent field is E: a rotated pair has
+// norm <= sqrt(2) * 2^(E - 126) < 2^(E - 125), and 2^(E - 125 - e) <= 2^15 keeps
+// it inside fp16.  A block of tiny values (largest below 2^-15, where fp16 is
+// subnormal) is scaled up to a largest value near 1.  In between, e = 0.
+__device__ __forceinline__ int fp16_shift(uint32_t E)
+{
+    if (E > 140u) return (int)E - 140;
+    if (E < 112u) return E > 27u ? (int)E - 127 : -100;   // (all zero: any shift)
+    return 0;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m, kWave));
+    return x;
+}
+
 // Rotate the staged keys by R(j - i0) (table read here, L2-resident) and write
 // K and V^T to LDS.
 template <int D>
 __device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, uint16_t* vt,
                                           long kt, long kv_hi, long i0, int w,
-                                          const float2* __restrict__ table)
+                                          const float2* __restrict__ table, int e_k)
 {
     const int tid = threadIdx.x;
+    const float sc = ldexpf(1.f, -e_k);                         // exact power of two
 #pragma unroll
     for (int it = 0; it < WinStage<D>::KC; ++it) {
         const int c = tid + 256 * it;
@@ -190,7 +226,11 @@ __device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, u
         const long j = kt + kr <= kv_hi ? kt + kr : kv_hi;     // rows past kv_hi repeat it
         const float4* rp = reinterpret_cast<const float4*>(
             table + (j - i0 + w + kTableSlack) * (D / 2) + part * 4);
-        const float4 a = rp[0], b = rp[1];
+        float4 a = rp[0], b = rp[1];
+        if (e_k != 0) {                                         // block-uniform
+            a.x *= sc; a.y *= sc; a.z *= sc; a.w *= sc;
+            b.x *= sc; b.y *= sc; b.z *= sc; b.w *= sc;
+        }
         uint4 o;
         o.x = rotate_pack(st.k[it].x, a.x, a.y);
         o.y = rotate_pack(st.k[it].y, a.z, a.w);
@@ -204,6 +244,22 @@ __device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, u
         // V^T column slot 8 g + 4 hh + r of the 32-key group holds key 16 hh + 4 g + r
         mf::store_vt_4x8_sw(st.v, vt, dc, 32 * grp + 8 * g + 4 * hh);
     }
+}
+
+// Each wave's largest exponent of the staged raw keys, into red[wave].
+template <int D>
+__device__ __forceinline__ void win_key_exp(const WinStage<D>& st, uint32_t* red)
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int it = 0; it < WinStage<D>::KC; ++it) m = max(m, max_bf16_exp(st.k[it]));
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+}
+
+__device__ __forceinline__ int win_block_shift(const uint32_t* red)
+{
+    return fp16_shift(max(max(red[0], red[1]), max(red[2], red[3])));
 }
 
 }  // namespace
@@ -221,6 +277,7 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     constexpr int DB = D / 16;     // 16-row blocks of O^T
     __shared__ __attribute__((aligned(16))) uint16_t ks[kTileK * D];    // swizzled rows
     __shared__ __attribute__((aligned(16))) uint16_t vt[D * kTileK];    // swizzled rows
+    __shared__ uint32_t kexp[kWinWaves];                                 // per-wave key exponents
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
@@ -246,20 +303,39 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     const long qw_last = qw0 + 31 < i_end ? qw0 + 31 : i_end;
     const bool wave_active = qw0 <= i_end;
 
-    // rotated queries as B operands, kept for the whole key range
+    // rotated queries as B operands, kept for the whole key range, scaled by the
+    // wave's 2^-e_q
     f16x8 qf[2][KS];
+    uint4 qraw[2][KS];
+    uint32_t qe = 0;
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const long i = qw0 + 16 * qg + n;
         const bool ok = i <= i_end;
         const uint16_t* qrow = q + b * qs0 + h * qs1 + (ok ? i - q_pos0 : 0) * qs2;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            qraw[qg][t] = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
+                             : make_uint4(0, 0, 0, 0);
+            qe = max(qe, max_bf16_exp(qraw[qg][t]));
+        }
+    }
+    const int e_q = fp16_shift(wave_max_u32(qe));
+    const float q_sc = ldexpf(1.f, -e_q);
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const long i = qw0 + 16 * qg + n;
+        const bool ok = i <= i_end;
         const float2* rot = table + (ok ? i - i0 + w + kTableSlack : w + kTableSlack) * (D / 2);
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-            uint4 raw = ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
-                           : make_uint4(0, 0, 0, 0);
+            const uint4 raw = qraw[qg][t];
             const float4* rp = reinterpret_cast<const float4*>(rot + 16 * t + 4 * g);
-            const float4 a = rp[0], c = rp[1];
+            float4 a = rp[0], c = rp[1];
+            if (e_q != 0) {                                     // wave-uniform
+                a.x *= q_sc; a.y *= q_sc; a.z *= q_sc; a.w *= q_sc;
+                c.x *= q_sc; c.y *= q_sc; c.z *= q_sc; c.w *= q_sc;
+            }
             uint4 u;
             u.x = rotate_pack(raw.x, a.x, a.y);
             u.y = rotate_pack(raw.y, a.z, a.w);
@@ -276,9 +352,13 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     float m_run[2] = {-INFINITY, -INFINITY};
 
     WinStage<D> stage;
+    int e_k = 0;                                              // the staged tile's key shift
     if (n_tiles > 0) {                                        // block-uniform
         win_load<D>(stage, kh, vh, kvs2, kv_lo, kv_hi, i0, w, table);
-        win_store<D>(stage, ks, vt, kv_lo, kv_hi, i0, w, table);
+        win_key_exp<D>(stage, kexp);
+        __syncthreads();
+        e_k = win_block_shift(kexp);
+        win_store<D>(stage, ks, vt, kv_lo, kv_hi, i0, w, table, e_k);
     }
     __syncthreads();
 
@@ -286,6 +366,8 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
         const long kt = kv_lo + (long)tile * kTileK;
         if (tile + 1 < n_tiles)
             win_load<D>(stage, kh, vh, kvs2, kt + kTileK, kv_hi, i0, w, table);
+        // logits of this tile: the scaled product times 2^(e_q + e_k)
+        const float scale_t = (e_q + e_k) == 0 ? scale_log2 : ldexpf(scale_log2, e_q + e_k);
 
         // does any query of this wave see a key of this tile?
         const bool work = wave_active && kt <= qw_last && kt + kTileK - 1 >= qw0 - w;
@@ -298,11 +380,13 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
                 const int d = d0 + 16 * (qg - kb) - r;
                 return d >= 0 && d <= w;
             };
-            attn_tile<D>(ks, vt, qf, acc, accl, m_run, scale_log2, !full, keep);
+            attn_tile<D>(ks, vt, qf, acc, accl, m_run, scale_t, !full, keep);
         }
+        if (tile + 1 < n_tiles) win_key_exp<D>(stage, kexp);     // the next tile's keys
         __syncthreads();
         if (tile + 1 < n_tiles) {
-            win_store<D>(stage, ks, vt, kt + kTileK, kv_hi, i0, w, table);
+            e_k = win_block_shift(kexp);
+            win_store<D>(stage, ks, vt, kt + kTileK, kv_hi, i0, w, table, e_k);
             __syncthreads();
         }
     }
@@ -392,6 +476,7 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
         float* ws_acc = S > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
         float2* ws_ml = S > 1 ? reinterpret_cast<float2*>(ws_acc + rows_all * S * sh.d) : nullptr;
         const long n_tiles = (sh.nq + kWinQ - 1) / kWinQ;
+        note_path("window: MFMA tiles of 128 queries, %d split(s)", S);
         dim3 grid((unsigned)(n_tiles * S * sh.B * sh.H)), block(256);
 #define FS_WINDOW_MFMA(D)                                                                        \
         hipLaunchKernelGGL((window_attn_mfma_kernel<D>), grid, block, 0, st, (const uint16_t*)q,  \
@@ -406,6 +491,7 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
         if (err != hipSuccess || S <= 1) return err;
         return launch_split_merge(sh, S, ws_acc, ws_ml, false, 0.f, o_sr, st);
     }
+    note_path("window: row-wise, one wavefront per query (fp32 storage)");
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
 #define FS_WINDOW(E, D)                                                                          \
     hipLaunchKernelGGL((window_attn_rowwise_kernel<E, D>), grid, block, 0, st,                   \

@@ -22,7 +22,7 @@ SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_t
            "fs_sparse_attn_noalloc", "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size",
            "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
            "fs_stream_step", "fs_forest_size", "fs_forest_build", "fs_beam_select",
-           "fs_status_string", "fs_last_error")
+           "fs_status_string", "fs_last_error", "fs_last_path")
 
 
 class FsError(RuntimeError):
@@ -93,6 +93,8 @@ def load(path: str | None = None):
     L.fs_status_string.restype = C.c_char_p
     L.fs_last_error.argtypes = []
     L.fs_last_error.restype = C.c_char_p
+    L.fs_last_path.argtypes = []
+    L.fs_last_path.restype = C.c_char_p
     if path == LIB_PATH:
         _lib = L
     return L
@@ -249,6 +251,11 @@ def fs_sparse_attn(prob, q, k, v, idx, topk, rms_eps, o_lr, workspace=None, stre
     _check("fs_sparse_attn", load().fs_sparse_attn(C.byref(prob), _p(q), _p(k), _p(v), _p(idx),
                                                    topk, float(rms_eps), ws, nbytes, _p(o_lr),
                                                    _s(stream)))
+
+
+def last_path() -> str:
+    """The kernel path of the calling thread's last readout / window / selection call."""
+    return load().fs_last_path().decode()
 
 
 def fs_sparse_attn_noalloc(prob, q, k, v, idx, topk, rms_eps, o_lr, stream=None):

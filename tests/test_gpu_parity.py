@@ -765,3 +765,62 @@ def test_small_sparse_unsplit(name):
     assert err.max() <= TOL[wl.dtype], err.max()
     none = np.array([(g["idx"][b, h, t] < 0).all() for b, h, t in rows])
     assert (got[none] == 0).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale_k,scale_q", [(1.5e4, 1.0 / 1.5e4), (1e-6, 1e6), (3e4, 1.0 / 3e4)])
+def test_window_extreme_magnitudes(d, scale_k, scale_q):
+    """Rotated q and k are carried in fp16: keys scaled so that rotated elements
+    exceed 65504, or queries / keys below fp16's normal range, must still give
+    the oracle's eq. 3-4 rows (the logits q.k/sqrt(d) stay ordinary).  Finite
+    output on every row, row error within the bf16 tolerance."""
+    from long_context_fs_amd import fs as fsb
+    wl = W["prefill_b2h16_n4096_d64_bf16"].replace(batch=1, heads=2, n_ctx=1100, n_q=1100,
+                                                    head_dim=d, budget=8, topk=4,
+                                                    structure="iid")
+    x = synth.generate(wl)
+    x["k"] = synth.round_bf16(x["k"] * np.float32(scale_k))
+    x["q"] = synth.round_bf16(x["q"] * np.float32(scale_q))
+    q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+    fwd = FsForward.for_workload(wl)
+    fsb.fs_window_attn(fwd.prob, q, k, v, wl.rope_base, fwd.ws, fwd.o_sr)
+    torch.cuda.synchronize()
+    got = fwd.o_sr.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    p = oracle.problem_from(wl)
+    want = np.stack([[orc().window_row(p, x["q"][0, h, t], x["k"][0, h], x["v"][0, h], t)
+                      for t in range(wl.n_q)] for h in range(wl.heads)])
+    err = row_rel_err(got[0], want)
+    assert err.max() <= TOL[wl.dtype], err.max()
+
+
+def test_last_path_reports_fallbacks():
+    """fs_last_path names the kernel each call took: MFMA for bf16 shapes, and
+    the row-wise fallback with its reason for fp32 storage or a candidate union
+    wider than the MFMA selection's 528 slots."""
+    from long_context_fs_amd import fs as fsb
+    cases = [("f32_d64_noprune", "fp32 storage", "fp32 storage"),
+             ("bf16_d64_wide_keep_k64", "wider than 528", None),
+             ("bf16_d128_needle", None, None)]
+    for name, sel_reason, read_reason in cases:
+        wl, x, g, _ = small_case(name)
+        q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+        fwd = FsForward.for_workload(wl)
+        fsb.fs_cell_summaries(fwd.prob, k, fwd.kbar, fwd.amax)
+        if fwd.pruned:
+            fsb.fs_prune_prefix(fwd.prob, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep,
+                                fwd.keep_count)
+        fsb.fs_select_topk(fwd.prob, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, wl.topk,
+                           fwd.idx, None, None, fwd.prior, fwd.ws_select)
+        path = fsb.last_path()
+        assert path.startswith("select: ")
+        assert ("row-wise" in path) == (sel_reason is not None), path
+        if sel_reason:
+            assert sel_reason in path, path
+        fsb.fs_sparse_attn(fwd.prob, q, k, v, fwd.idx, wl.topk, wl.rms_eps, fwd.o_lr,
+                           fwd.ws_sparse)
+        path = fsb.last_path()
+        assert path.startswith("readout: ") and (("row-wise" in path) == (read_reason is not None))
+        if read_reason:
+            assert read_reason in path, path
+    torch.cuda.synchronize()
