@@ -180,16 +180,26 @@ __device__ __forceinline__ uint32_t rotate_pack(uint32_t xy, float c, float s)
     return mf::pack_f16x2(x * c - y * s, x * s + y * c);
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running maximum of the bf16 magnitudes (sign cleared; they order like the
+// values) of the 8 bf16 values in u, two lanes of 16 bits.
+__device__ __forceinline__ u16x2 max_bf16_mag(u16x2 m, const uint4& u)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        m = __builtin_elementwise_max(
+            m, __builtin_bit_cast(u16x2, mf::word_of(u, i) & 0x7FFF7FFFu));
+    return m;
+}
+
+// Biased exponent field of the larger of the two magnitudes.
+__device__ __forceinline__ uint32_t mag_exp(u16x2 m) { return (uint32_t)max(m.x, m.y) >> 7; }
+
 // Largest biased exponent field of the 8 bf16 values in u.
 __device__ __forceinline__ uint32_t max_bf16_exp(const uint4& u)
 {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w = mf::word_of(u, i);
-        m = max(m, max((w >> 7) & 0xFFu, (w >> 23) & 0xFFu));
-    }
-    return m;
+    return mag_exp(max_bf16_mag(u16x2{0, 0}, u));
 }
 
 // Shift e of a block whose largest bf16 exponent field is E: a rotated pair has
@@ -246,14 +256,18 @@ __device__ __forceinline__ void win_store(const WinStage<D>& st, uint16_t* ks, u
     }
 }
 
-// Each wave's largest exponent of the staged raw keys, into red[wave].
+// Each wave's largest exponent of the staged raw keys, into red[wave]; the
+// exact maximum is only formed when some value is outside the shift-free range
+// (a ballot), otherwise a value inside it stands for the wave.
 template <int D>
 __device__ __forceinline__ void win_key_exp(const WinStage<D>& st, uint32_t* red)
 {
-    uint32_t m = 0;
+    u16x2 mm = {0, 0};
 #pragma unroll
-    for (int it = 0; it < WinStage<D>::KC; ++it) m = max(m, max_bf16_exp(st.k[it]));
-    m = wave_max_u32(m);
+    for (int it = 0; it < WinStage<D>::KC; ++it) mm = max_bf16_mag(mm, st.k[it]);
+    uint32_t m = mag_exp(mm);
+    const bool big = __ballot(m > 140u) != 0, tiny = __ballot(m >= 112u) == 0;
+    m = (big || tiny) ? wave_max_u32(m) : 127u;
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
 }
 
