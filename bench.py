@@ -305,8 +305,8 @@ class FsbSetup:
     def build(self):
         self.sel.build(self.kbar, self.amax, self.tau)
 
-    def search(self, q, effort=False):
-        self.sel.select(q, effort=effort)
+    def search(self, q, effort=False, k=None):
+        self.sel.select(q, effort=effort, k=k)
 
 
 def run_fsb(name, steps, warmup, torch, fs):
@@ -357,6 +357,15 @@ def run_fsb(name, steps, warmup, torch, fs):
         for j, (nm, _) in enumerate(calls):
             times[nm].append(ev[j].elapsed_time(ev[j + 1]))
     phase_ms = {nm: float(np.mean(t)) for nm, t in times.items()}
+    # the same search with eq. 12's token-level reranking of the found cells
+    rr = []
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        fb.search(q, k=k)
+        ev[1].record()
+        torch.cuda.synchronize()
+        rr.append(ev[0].elapsed_time(ev[1]))
     fb.search(q, effort=True)
     torch.cuda.synchronize()
     scored = int(fb.effort.to(torch.int64).sum().item())
@@ -372,7 +381,8 @@ def run_fsb(name, steps, warmup, torch, fs):
     return {"workload": wl.name, "beam": FSB_BEAM, "slack": FSB_SLACK,
             "tau": f"per head, the {FSB_TAU_Q:.0%} quantile of its a_c",
             "ms_per_step": ms_step, "queries_per_s": wl.batch * wl.n_q / (ms_step * 1e-3),
-            "phase_ms": phase_ms, "nodes_scored_per_query_head": scored / nq,
+            "phase_ms": phase_ms, "beam_select_rerank_ms": float(np.mean(rr)),
+            "nodes_scored_per_query_head": scored / nq,
             "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK["valu_f64_TFs"],
                          "unit": "TFLOP/s", "frac": ach / PEAK["valu_f64_TFs"],
                          "traffic": stored_traffic("fsb_beam") if name == PRIMARY else None,

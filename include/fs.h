@@ -169,7 +169,11 @@ fs_status fs_rerank_workspace_size(const fs_problem* problem, int32_t keep_width
  *     retains the best `beam` by U; stop when only leaves remain.  S_i is the
  *     best min(topk, #found) cells of both final beams by eq. 7's score (a
  *     leaf's U), written ascending like fs_select_topk.  Ties: larger U, then the
- *     later block (larger cell), then the lower level.
+ *     later block (larger cell), then the lower level;
+ *   - with token-level reranking (eq. 12, which the page places in FS-B), the
+ *     found cells are ranked instead by r~ = log sum_j exp(q.k_j / sqrt(d)) over
+ *     the cell's raw keys plus the same prior, ties to the larger cell; r~ is
+ *     an fp32 dot product per key and an fp32 log-sum-exp.
  * U is computed in fp64 from the fp32 node statistics in one fixed order (dot
  * products as 16 contiguous partial sums added pairwise at distances 8, 4, 2,
  * 1), so the search's decisions are reproducible.
@@ -189,15 +193,18 @@ fs_status fs_forest_build(const fs_problem* problem, const float* kbar, const fl
                           const float* tau, void* forest, void* stream);
 
 /* S_i by beam search (eq. 11) in forest0 and/or forest_tau (either may be NULL,
- * not both; each built with this problem's batch, heads, head_dim and n_ctx).  beam in [1, 64], slack c >= 0
- * (finite), topk in [1, 64].  prior_lambda, prior_sigma: both NULL (no prior) or
- * float32 [H] (lambda_h >= 0, sigma_h > 0, not checked).  idx: int32
- * [B][H][n_q][topk], ascending, -1 padded; score (nullable): float32 eq. 7
- * score aligned with idx (0 for padding); effort (nullable): int32 [B][H][n_q],
- * the number of node scores U_v the query's searches computed (its search
- * effort: the node rows it read). */
-fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* forest0,
-                         const void* forest_tau, int32_t beam, float slack,
+ * not both; each built with this problem's batch, heads, head_dim and n_ctx).
+ * k: NULL to rank the found cells by eq. 7's score, or the raw keys [B][H][n_ctx][d]
+ * (kv_stride, 16-byte aligned) to rank them by eq. 12's token-level score.
+ * beam in [1, 64], slack c >= 0 (finite), topk in [1, 64].  prior_lambda,
+ * prior_sigma: both NULL (no prior) or float32 [H] (lambda_h >= 0, sigma_h > 0,
+ * not checked).  idx: int32 [B][H][n_q][topk], ascending, -1 padded; score
+ * (nullable): float32, the ranking's score (eq. 7's, or eq. 12's with k) aligned
+ * with idx (0 for padding); effort (nullable): int32 [B][H][n_q], the number of
+ * node scores U_v the query's searches computed (its search effort: the node rows
+ * it read). */
+fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* k,
+                         const void* forest0, const void* forest_tau, int32_t beam, float slack,
                          const float* prior_lambda, const float* prior_sigma, int32_t topk,
                          int32_t* idx, float* score, int32_t* effort, void* stream);
 

@@ -291,8 +291,8 @@ fs_status fs_forest_build(const fs_problem* problem, const float* kbar, const fl
                     "fs_forest_build");
 }
 
-fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* forest0,
-                         const void* forest_tau, int32_t beam, float slack,
+fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* k,
+                         const void* forest0, const void* forest_tau, int32_t beam, float slack,
                          const float* prior_lambda, const float* prior_sigma, int32_t topk,
                          int32_t* idx, float* score, int32_t* effort, void* stream)
 {
@@ -300,6 +300,7 @@ fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* f
     FS_CHECK(check_problem(problem, &sh));
     if (sh.C > 32768) return fail(FS_ERR_UNSUPPORTED, "FS-B forests hold at most 32768 cells");
     FS_PTR(q);
+    if (k && !aligned16(k)) return fail(FS_ERR_INVALID, "k is not 16-byte aligned");
     if (!forest0 && !forest_tau) return fail(FS_ERR_INVALID, "both forests are NULL");
     if (((uintptr_t)forest0 & 255) || ((uintptr_t)forest_tau & 255))
         return fail(FS_ERR_INVALID, "forests must be 256-byte aligned");
@@ -310,7 +311,7 @@ fs_status fs_beam_select(const fs_problem* problem, const void* q, const void* f
         return fail(FS_ERR_INVALID, "the position prior needs prior_lambda and prior_sigma");
     if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
     if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
-    return from_hip(fs::launch_beam_select(sh, q, forest0, forest_tau, beam, (double)slack,
+    return from_hip(fs::launch_beam_select(sh, q, k, forest0, forest_tau, beam, (double)slack,
                                            prior_lambda, prior_lambda ? prior_sigma : nullptr,
                                            topk, idx, score, effort, (hipStream_t)stream),
                     "fs_beam_select");

@@ -106,8 +106,8 @@ hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* 
 size_t forest_bytes(const Shape& sh);
 hipError_t launch_forest_build(const Shape& sh, const float* kbar, const float* amax,
                                const float* tau, void* forest, hipStream_t st);
-hipError_t launch_beam_select(const Shape& sh, const void* q, const void* forest0,
-                              const void* forest_tau, int beam, double slack,
+hipError_t launch_beam_select(const Shape& sh, const void* q, const void* k,
+                              const void* forest0, const void* forest_tau, int beam, double slack,
                               const float* prior_lambda, const float* prior_sigma, int topk,
                               int32_t* idx, float* score, int32_t* effort, hipStream_t st);
 

@@ -26,6 +26,12 @@
 // levels in registers, the last two by shuffles.  Ties: the
 // larger U, then the later block, then the lower level.  Floating-point
 // contraction is off in this file so every product and sum rounds on its own.
+//
+// Reranking (eq. 12, section 3.4).  Given the raw keys, the found cells are
+// ranked instead by r~ = log sum_j exp(q.k_j / sqrt(d)) over the cell's s = 32
+// keys plus the prior at the cell: a half-wave per cell, one key per lane (an
+// fp32 dot product in ascending element order), the half-wave's maximum and
+// sum of exp2 by shuffles.
 #include <cmath>
 
 #include "fs_device.hpp"
@@ -255,6 +261,7 @@ struct BeamLds {
     int16_t cix[2 * kMaxBeam], cfirst[2 * kMaxBeam];
     int16_t bix[kMaxBeam], bfirst[kMaxBeam];
     int16_t fcell[2 * kMaxBeam];
+    int16_t fleaf[2 * kMaxBeam];  // the found cell's leaf index in its forest
     uint8_t clv[2 * kMaxBeam], blv[kMaxBeam];
     uint8_t todo[2 * kMaxBeam];   // candidate slots whose U is still to be computed
     uint8_t fdup[2 * kMaxBeam];   // found twice (second forest)
@@ -460,16 +467,65 @@ __device__ __forceinline__ void beam_forest(BeamLds& S, const FsbView& f, const 
     if (lane < n_cur) {
         S.fu[*n_found + lane] = S.bu[lane];
         S.fcell[*n_found + lane] = S.bfirst[lane];
+        S.fleaf[*n_found + lane] = S.bix[lane];
     }
     *n_found += n_cur;
     __syncthreads();
 }
 
+// Eq. 12's score of every found cell that is not a repeat, into fu.  kh: the
+// head's keys (row stride ks); a0 / at: the leaves' A_v in the forest each
+// entry came from (entries below n_first from forest 0).
 template <class E, int D>
+__device__ __forceinline__ void rerank_found(BeamLds& S, int n_found, int n_first,
+                                             const typename E::storage* __restrict__ kh,
+                                             int64_t ks, const float* a0, const float* at,
+                                             const QueryCtx& Q, float scale_log2)
+{
+    const int lane = threadIdx.x & 63, j = lane & 31;
+    for (int a2 = 0; a2 < n_found; a2 += 2) {
+        const int a = a2 + (lane >> 5);
+        const bool on = a < n_found && !S.fdup[a];
+        float x = -INFINITY;
+        if (on) {
+            const typename E::storage* kr = kh + ((int64_t)S.fcell[a] * Q.s + j) * ks;
+            float acc = 0.f;
+#pragma unroll 4
+            for (int e0 = 0; e0 < D; e0 += E::kPer16B) {
+                float kv[E::kPer16B];
+                load16<E>(kr + e0, kv);
+#pragma unroll
+                for (int t = 0; t < E::kPer16B; ++t) acc = __builtin_fmaf(S.q[e0 + t], kv[t], acc);
+            }
+            x = acc * scale_log2;
+        }
+        // xor distances below 32 keep the two half-waves apart
+        float m = x;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        float e = on ? exp2f(x - m) : 0.f;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) e += __shfl_xor(e, o);
+        if (on && j == 0) {
+            double r = (double)((m + log2f(e)) * 0.69314718055994531f);
+            if (Q.lam != 0.0 || Q.sig != 0.0) {
+                const int c = S.fcell[a];
+                const float a_v = (a < n_first ? a0 : at)[S.fleaf[a]];
+                r = r + fsb_prior(Q.lam, (double)a_v, Q.i_pos, ((double)c + 0.5) * (double)Q.s,
+                                  Q.sig);
+            }
+            S.fu[a] = r;
+        }
+    }
+    __syncthreads();
+}
+
+template <class E, int D, bool RR>
 __global__ __launch_bounds__(64, 6) void beam_select_kernel(
-    const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2, int H,
+    const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const typename E::storage* __restrict__ k, int64_t ks0, int64_t ks1, int64_t ks2, int H,
     int nq, int q_pos0, int w, int s, FsbLayout L, char* forest0, char* forest_tau, int beam,
-    double slack, double inv_sqrt_d, const float* __restrict__ prior_lambda,
+    double slack, double inv_sqrt_d, float scale_log2, const float* __restrict__ prior_lambda,
     const float* __restrict__ prior_sigma, int topk, int32_t* __restrict__ idx,
     float* __restrict__ score, int32_t* __restrict__ effort)
 {
@@ -518,12 +574,16 @@ __global__ __launch_bounds__(64, 6) void beam_select_kernel(
         }
     }
     __syncthreads();
+    if (RR)
+        rerank_found<E, D>(S, n_found, n_first, k + b * ks0 + h * ks1, ks2,
+                           forest0 ? fsb_view(forest0, L, bh).amax : nullptr,
+                           forest_tau ? fsb_view(forest_tau, L, bh).amax : nullptr, Q, scale_log2);
     int n_unique = 0;
     for (int a = 0; a < n_found; ++a) n_unique += S.fdup[a] ? 0 : 1;
-    const int k = n_unique < topk ? n_unique : topk;
+    const int n_sel = n_unique < topk ? n_unique : topk;
     int32_t* orow = idx + (bh * nq + row) * (long)topk;
     float* srow = score ? score + (bh * nq + row) * (long)topk : nullptr;
-    // rank by (U, cell) descending, then write the selected cells ascending
+    // rank by (score, cell) descending, then write the selected cells ascending
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int a = lane + 64 * hh;
@@ -539,15 +599,15 @@ __global__ __launch_bounds__(64, 6) void beam_select_kernel(
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int a = lane + 64 * hh;
-        if (a < n_found && S.frank[a] < k) {
+        if (a < n_found && S.frank[a] < n_sel) {
             int pos = 0;
             for (int c = 0; c < n_found; ++c)
-                pos += (S.frank[c] < k && S.fcell[c] < S.fcell[a]) ? 1 : 0;
+                pos += (S.frank[c] < n_sel && S.fcell[c] < S.fcell[a]) ? 1 : 0;
             orow[pos] = S.fcell[a];
             if (srow) srow[pos] = (float)S.fu[a];
         }
     }
-    if (lane >= k && lane < topk) {
+    if (lane >= n_sel && lane < topk) {
         orow[lane] = -1;
         if (srow) srow[lane] = 0.f;
     }
@@ -579,8 +639,8 @@ hipError_t launch_forest_build(const Shape& sh, const float* kbar, const float* 
     return hipGetLastError();
 }
 
-hipError_t launch_beam_select(const Shape& sh, const void* q, const void* forest0,
-                              const void* forest_tau, int beam, double slack,
+hipError_t launch_beam_select(const Shape& sh, const void* q, const void* k,
+                              const void* forest0, const void* forest_tau, int beam, double slack,
                               const float* prior_lambda, const float* prior_sigma, int topk,
                               int32_t* idx, float* score, int32_t* effort, hipStream_t st)
 {
@@ -588,17 +648,25 @@ hipError_t launch_beam_select(const Shape& sh, const void* q, const void* forest
     const FsbLayout L = fsb_layout(sh.C, sh.d);
     const dim3 grid(sh.nq, sh.B * sh.H);
     const double inv_sqrt_d = 1.0 / std::sqrt((double)sh.d);
+    const float scale_log2 = (float)(1.4426950408889634 * inv_sqrt_d);
     char* f0 = static_cast<char*>(const_cast<void*>(forest0));
     char* ft = static_cast<char*>(const_cast<void*>(forest_tau));
-#define FS_BEAM_LAUNCH(E, DD, T)                                                          \
-    beam_select_kernel<E, DD><<<grid, 64, 0, st>>>(                                         \
-        static_cast<const T*>(q), sh.qs[0], sh.qs[1], sh.qs[2], sh.H, sh.nq, sh.q_pos0, sh.w, \
-        sh.s, L, f0, ft, beam, slack, inv_sqrt_d, prior_lambda, prior_sigma, topk, idx, score, \
-        effort)
-    if (sh.bf16 && sh.d == 128) FS_BEAM_LAUNCH(Bf16, 128, uint16_t);
-    else if (sh.bf16) FS_BEAM_LAUNCH(Bf16, 64, uint16_t);
-    else if (sh.d == 128) FS_BEAM_LAUNCH(F32, 128, float);
-    else FS_BEAM_LAUNCH(F32, 64, float);
+#define FS_BEAM_LAUNCH(E, DD, T, RR)                                                      \
+    beam_select_kernel<E, DD, RR><<<grid, 64, 0, st>>>(                                     \
+        static_cast<const T*>(q), sh.qs[0], sh.qs[1], sh.qs[2], static_cast<const T*>(k),   \
+        sh.kvs[0], sh.kvs[1], sh.kvs[2], sh.H, sh.nq, sh.q_pos0, sh.w, sh.s, L, f0, ft, beam, \
+        slack, inv_sqrt_d, scale_log2, prior_lambda, prior_sigma, topk, idx, score, effort)
+#define FS_BEAM_DISPATCH(RR)                                                              \
+    if (sh.bf16 && sh.d == 128) FS_BEAM_LAUNCH(Bf16, 128, uint16_t, RR);                   \
+    else if (sh.bf16) FS_BEAM_LAUNCH(Bf16, 64, uint16_t, RR);                              \
+    else if (sh.d == 128) FS_BEAM_LAUNCH(F32, 128, float, RR);                             \
+    else FS_BEAM_LAUNCH(F32, 64, float, RR)
+    if (k) {
+        FS_BEAM_DISPATCH(true);
+    } else {
+        FS_BEAM_DISPATCH(false);
+    }
+#undef FS_BEAM_DISPATCH
 #undef FS_BEAM_LAUNCH
     return hipGetLastError();
 }

@@ -79,7 +79,7 @@ def load(path: str | None = None):
         "fs_combine": [P, vp, vp, vp, vp, vp],
         "fs_forest_size": [P, C.POINTER(C.c_size_t)],
         "fs_forest_build": [P, vp, vp, vp, vp, vp],
-        "fs_beam_select": [P, vp, vp, vp, i32, f32, vp, vp, i32, vp, vp, vp, vp],
+        "fs_beam_select": [P, vp, vp, vp, vp, i32, f32, vp, vp, i32, vp, vp, vp, vp],
         "fs_stream_state_size": [C.POINTER(FsStreamConfig), C.POINTER(C.c_size_t)],
         "fs_stream_reset": [C.POINTER(FsStreamConfig), vp, C.c_size_t, vp],
         "fs_stream_step": [C.POINTER(FsStreamConfig), vp, C.c_size_t, C.c_int64, i32, vp, vp,
@@ -215,11 +215,12 @@ def fs_forest_build(prob, kbar, amax, forest, tau=None, stream=None):
 
 
 def fs_beam_select(prob, q, forest0, forest_tau, beam, slack, topk, idx, score=None,
-                   prior=None, effort=None, stream=None):
+                   prior=None, effort=None, stream=None, k=None):
     """FS-B beam search (eq. 11) for S_i; prior: None or (lambda, sigma) device tensors;
-    effort: None or an int32 [B, H, n_q] tensor for the node scores per query."""
+    effort: None or an int32 [B, H, n_q] tensor for the node scores per query;
+    k: None (rank the found cells by eq. 7) or the raw keys (rank them by eq. 12)."""
     lam, sig = prior if prior is not None else (None, None)
-    _check("fs_beam_select", load().fs_beam_select(C.byref(prob), _p(q), _p(forest0),
+    _check("fs_beam_select", load().fs_beam_select(C.byref(prob), _p(q), _p(k), _p(forest0),
                                                    _p(forest_tau), int(beam), float(slack),
                                                    _p(lam), _p(sig), int(topk), _p(idx),
                                                    _p(score), _p(effort), _s(stream)))
@@ -368,10 +369,11 @@ class FsbSelect:
             fs_forest_build(self.prob, kbar, amax, self.forest_tau, tau=tau, stream=stream)
 
     def select(self, q, prob=None, idx=None, score=False, effort=False, prior=None,
-               stream=None):
+               stream=None, k=None):
         """S_i into self.idx (or `idx`, for another query range's problem `prob`).
         score / effort: False (not written), True (into self.score / self.effort)
-        or a tensor; prior: None or (lambda, sigma) device tensors.  Returns idx."""
+        or a tensor; prior: None or (lambda, sigma) device tensors; k: None, or the
+        raw keys to rank the found cells by eq. 12 instead of eq. 7.  Returns idx."""
         p = prob or self.prob
         mine = self.prob
         if prob is not None:
@@ -393,7 +395,7 @@ class FsbSelect:
                 raise FsError(f"FsbSelect.select: {name} has shape {tuple(t.shape)}, "
                               f"expected {shape}")
         fs_beam_select(p, q, self.forest0, self.forest_tau, self.beam, self.slack, self.topk,
-                       out, sc, prior=prior, effort=ef, stream=stream)
+                       out, sc, prior=prior, effort=ef, stream=stream, k=k)
         return out
 
 

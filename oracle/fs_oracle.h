@@ -184,6 +184,14 @@ int or_beam64_row(const or_problem* p, int head, long long i, const float* q_row
                   const or_forest64* f0, const or_forest64* ftau, int beam, double slack,
                   int* sel, double* score, int* n_scored, double* gap);
 
+/* The cells both searches of or_beam64_row end with, without repeats (at most
+ * 2 beam), in search order; *gap receives the smallest relative gap of the
+ * searches' cuts.  Eq. 12's reranking over them is or_rerank_row with these
+ * cells as candidates. */
+int or_beam64_found(const or_problem* p, int head, long long i, const float* q_row,
+                    const or_forest64* f0, const or_forest64* ftau, int beam, double slack,
+                    int* cells, int* n_scored, double* gap);
+
 /* or_beam64_row for the query rows t in `rows` (positions q_pos0 + t) of head
  * `head`, threaded.  Per row: sel / score [topk] in descending (score, cell)
  * order, -1 / 0 padded; n_sel; n_scored; gap. */

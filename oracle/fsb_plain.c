@@ -193,36 +193,60 @@ static int pl_beam_forest(const or_problem* p, int head, long long i, const floa
     return n_cur;
 }
 
-int or_beam64_row(const or_problem* p, int head, long long i, const float* q_row,
-                  const or_forest64* f0, const or_forest64* ftau, int beam, double slack,
-                  int* sel, double* score, int* n_scored, double* gap)
+/* The leaves both searches end with, without repeats (a cell found by both
+ * forests has one score), in search order; *gap receives the smallest relative
+ * gap of the searches' cuts. */
+static int pl_found(const or_problem* p, int head, long long i, const float* q_row,
+                    const or_forest64* f0, const or_forest64* ftau, int beam, double slack,
+                    pl_ent* found, int* n_scored, double* gap)
 {
     int scored = 0;
-    double g = INFINITY;
     const int n = or_n_candidates(p, i);
-    pl_ent* found = (pl_ent*)malloc(sizeof(pl_ent) * (size_t)(2 * beam + 2));
     int cnt = 0;
     if (f0)
         cnt += pl_beam_forest(p, head, i, q_row, f0, f0->prefix[n < f0->n_cells ? n : f0->n_cells],
-                              beam, slack, found, &scored, &g);
+                              beam, slack, found, &scored, gap);
     if (ftau)
         cnt += pl_beam_forest(p, head, i, q_row, ftau,
                               ftau->prefix[n < ftau->n_cells ? n : ftau->n_cells], beam, slack,
-                              found + cnt, &scored, &g);
-    /* union of the two final beams (a cell found in both has one score) */
+                              found + cnt, &scored, gap);
     int n_u = 0;
     for (int t = 0; t < cnt; ++t) {
         int dup = 0;
         for (int r = 0; r < n_u; ++r) dup |= found[r].first == found[t].first;
         if (!dup) found[n_u++] = found[t];
     }
+    if (n_scored) *n_scored = scored;
+    return n_u;
+}
+
+int or_beam64_found(const or_problem* p, int head, long long i, const float* q_row,
+                    const or_forest64* f0, const or_forest64* ftau, int beam, double slack,
+                    int* cells, int* n_scored, double* gap)
+{
+    double g = INFINITY;
+    pl_ent* found = (pl_ent*)malloc(sizeof(pl_ent) * (size_t)(2 * beam + 2));
+    const int n_u = pl_found(p, head, i, q_row, f0, ftau, beam, slack, found, n_scored, &g);
+    for (int t = 0; t < n_u; ++t) cells[t] = found[t].first;
+    free(found);
+    if (gap) *gap = g;
+    return n_u;
+}
+
+int or_beam64_row(const or_problem* p, int head, long long i, const float* q_row,
+                  const or_forest64* f0, const or_forest64* ftau, int beam, double slack,
+                  int* sel, double* score, int* n_scored, double* gap)
+{
+    double g = INFINITY;
+    pl_ent* found = (pl_ent*)malloc(sizeof(pl_ent) * (size_t)(2 * beam + 2));
+    const int n_u = pl_found(p, head, i, q_row, f0, ftau, beam, slack, found, n_scored, &g);
+    /* eq. 7's score of a leaf is its U: the best K of the found cells */
     const int k = pl_cut(found, n_u, p->topk, &g);
     for (int t = 0; t < k; ++t) {
         sel[t] = found[t].first;
         if (score) score[t] = found[t].u;
     }
     free(found);
-    if (n_scored) *n_scored = scored;
     if (gap) *gap = g;
     return k;
 }

@@ -195,6 +195,17 @@ class PlainFsb:
             out += (g.value,)
         return out
 
+    def beam_found(self, p: Problem, head: int, i: int, q_row, f0, ftau, beam: int,
+                   slack: float):
+        """The cells the two searches end with (no repeats) and the searches' gap."""
+        cells = np.zeros(2 * beam + 2, np.int32)
+        n_scored, g = C.c_int(), C.c_double()
+        cnt = self.L.or_beam64_found(C.byref(p), int(head), int(i), _f32(q_row),
+                                     None if f0 is None else C.addressof(f0.s),
+                                     None if ftau is None else C.addressof(ftau.s), int(beam),
+                                     float(slack), cells, C.byref(n_scored), C.byref(g))
+        return cells[:cnt].copy(), g.value
+
     def beam_rows(self, p: Problem, head: int, q_head, rows, f0, ftau, beam: int, slack: float,
                   nthreads: int | None = None) -> dict:
         """S_i of query rows `rows` (indices into q_head, positions q_pos0 + t):
@@ -272,6 +283,10 @@ class Oracle:
                                     C.c_int, C.c_double, _I32P, _F64P, C.POINTER(C.c_int),
                                     C.POINTER(C.c_double)]
         L.or_beam64_row.restype = C.c_int
+        L.or_beam64_found.argtypes = [P, C.c_int, C.c_longlong, _F32P, C.c_void_p, C.c_void_p,
+                                      C.c_int, C.c_double, _I32P, C.POINTER(C.c_int),
+                                      C.POINTER(C.c_double)]
+        L.or_beam64_found.restype = C.c_int
         L.or_beam64_rows.argtypes = [P, C.c_int, _F32P, _I32P, C.c_int, C.c_void_p, C.c_void_p,
                                      C.c_int, C.c_double, _I32P, _F64P, _I32P, _I32P, _F64P,
                                      C.c_int]

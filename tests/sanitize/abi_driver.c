@@ -92,10 +92,14 @@ int main(void)
            "noalloc NULL idx");
     expect(fs_window_attn(&good, x, x, NULL, 1e4f, x, 1 << 16, x, NULL), FS_ERR_INVALID, "NULL v");
     expect(fs_forest_build(&good, fx, fx, NULL, NULL, NULL), FS_ERR_INVALID, "NULL forest");
-    expect(fs_beam_select(&good, x, NULL, NULL, 8, 1.f, NULL, NULL, 8, ix, NULL, NULL, NULL),
+    expect(fs_beam_select(&good, x, NULL, NULL, NULL, 8, 1.f, NULL, NULL, 8, ix, NULL, NULL,
+                          NULL),
            FS_ERR_INVALID, "no forest");
-    expect(fs_beam_select(&good, x, x, NULL, 65, 1.f, NULL, NULL, 8, ix, NULL, NULL, NULL),
+    expect(fs_beam_select(&good, x, NULL, x, NULL, 65, 1.f, NULL, NULL, 8, ix, NULL, NULL, NULL),
            FS_ERR_UNSUPPORTED, "beam 65");
+    expect(fs_beam_select(&good, x, (const char*)x + 2, x, NULL, 8, 1.f, NULL, NULL, 8, ix, NULL,
+                          NULL, NULL),
+           FS_ERR_INVALID, "misaligned keys");
     sc.max_new = 0;
     expect(fs_stream_state_size(&sc, &n), FS_ERR_UNSUPPORTED, "stream max_new 0");
     expect(fs_stream_step(&sc, x, 1 << 16, 0, 1, x, x, x, fx, NULL, NULL, x, NULL, NULL),

@@ -225,23 +225,27 @@ def test_fsb_arguments_rejected(lib):
                                None) == 1
     assert b"256-byte" in lib.fs_last_error()
     assert lib.fs_forest_build(C.byref(p), FAKE, None, None, F, None) == 1
-    assert lib.fs_beam_select(C.byref(p), FAKE, None, None, 8, 1.0, None, None, 8, FAKE,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, None, None, 8, 1.0, None, None, 8, FAKE,
                               None, None, None) == 1
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 0, 1.0, None, None, 8, FAKE, None,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, F, None, 0, 1.0, None, None, 8, FAKE, None,
                               None, None) == 2
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 65, 1.0, None, None, 8, FAKE, None,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, F, None, 65, 1.0, None, None, 8, FAKE, None,
                               None, None) == 2
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, -1.0, None, None, 8, FAKE, None,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, F, None, 8, -1.0, None, None, 8, FAKE, None,
                               None, None) == 1
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, float("nan"), None, None, 8, FAKE,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, F, None, 8, float("nan"), None, None, 8, FAKE,
                               None, None, None) == 1
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, FAKE, None, 8, FAKE, None,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, F, None, 8, 1.0, FAKE, None, 8, FAKE, None,
                               None, None) == 1
     assert b"prior" in lib.fs_last_error()
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, None, None, 65, FAKE, None,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, F, None, 8, 1.0, None, None, 65, FAKE, None,
                               None, None) == 2
-    assert lib.fs_beam_select(C.byref(p), FAKE, F, None, 8, 1.0, None, None, 8, None, None,
+    assert lib.fs_beam_select(C.byref(p), FAKE, None, F, None, 8, 1.0, None, None, 8, None, None,
                               None, None) == 1
+    # keys for eq. 12's reranking must keep 16-byte rows
+    assert lib.fs_beam_select(C.byref(p), FAKE, C.c_void_p(FAKE.value + 2), F, None, 8, 1.0,
+                              None, None, 8, FAKE, None, None, None) == 1
+    assert b"k is not 16-byte aligned" in lib.fs_last_error()
     # forest storage grows with the number of cells and holds their node statistics
     small, large = C.c_size_t(), C.c_size_t()
     lib.fs_forest_size(C.byref(_prob(n_ctx=4096, n_q=1)), C.byref(small))

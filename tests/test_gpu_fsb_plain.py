@@ -19,6 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
+from fs_testutil import accept_set
 from long_context_fs_amd import fs, synth
 
 pytestmark = pytest.mark.gpu
@@ -42,8 +43,9 @@ def admit_threshold(amax64, q=0.7):
     return tau
 
 
-def gpu_chain(wl, inp, tau, beam, slack, prior=None, use_tau=True):
-    """Summaries, forests, search and readout on the device from raw q, k, v."""
+def gpu_chain(wl, inp, tau, beam, slack, prior=None, use_tau=True, rerank=False):
+    """Summaries, forests, search and readout on the device from raw q, k, v
+    (rerank: the found cells ranked by eq. 12 over the raw keys)."""
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     prob = fs.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, wl.n_q, wl.q_pos0, wl.window,
                       fs.FS_BF16 if wl.dtype == "bf16" else fs.FS_F32)
@@ -62,7 +64,8 @@ def gpu_chain(wl, inp, tau, beam, slack, prior=None, use_tau=True):
     sc = torch.zeros((B, H, wl.n_q, K), dtype=torch.float32, device="cuda")
     eff = torch.zeros((B, H, wl.n_q), dtype=torch.int32, device="cuda")
     pr = None if prior is None else tuple(torch.from_numpy(a).cuda() for a in prior)
-    fs.fs_beam_select(prob, q, f0, ft, beam, slack, K, idx, sc, prior=pr, effort=eff)
+    fs.fs_beam_select(prob, q, f0, ft, beam, slack, K, idx, sc, prior=pr, effort=eff,
+                      k=k if rerank else None)
     o_lr = torch.empty_like(q)
     ws_n = fs.fs_sparse_workspace_size(prob)
     ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
@@ -193,4 +196,88 @@ def test_chain_full_head_at_benchmark_shape():
     rows5 = np.sort(rng.choice(wl.n_q, 2048, replace=False))
     d5, t5 = check_head(wl, inp, got, 0, 5, tau, 32, 1.0, rows5, readout_rows=rows5[:64])
     assert t5 <= 0.05 * len(rows5)
+    assert (got["idx"][:, :, :wl.window + wl.cell] == -1).all()
+
+
+def check_rerank_head(wl, inp, got, b, h, tau, beam, slack, rows, prior=None, use_tau=True):
+    """Eq. 12 over the cells the search found: rows whose search is decided (gap
+    >= 1e-5) must pick eq. 12's top-K of the oracle's found cells, up to a
+    near-tie of eq. 12's scores, with each score within fp32 dot / exp / log
+    error; returns (exact, tie, undecided) counts."""
+    orc = oracle.Oracle()
+    p = oracle_problem(wl, prior)
+    kbar, amax = orc.cell_summaries_head(p, inp["k"][b, h])
+    f0 = orc.plain.forest_build(kbar, amax)
+    ft = orc.plain.forest_build(kbar, amax, float(tau[h])) if use_tau else None
+    lam = None if prior is None else float(prior[0][h])
+    counts = {"exact": 0, "tie": 0, "undecided": 0}
+    kh = inp["k"][b, h]
+    for t in rows:
+        i = wl.q_pos0 + int(t)
+        q = inp["q"][b, h, t]
+        g_idx = got["idx"][b, h, t]
+        chosen = g_idx[g_idx >= 0]
+        assert (g_idx[len(chosen):] == -1).all() and (np.diff(chosen) > 0).all(), (b, h, t)
+        found, gap = orc.plain.beam_found(p, h, i, q, f0, ft, beam, slack)
+        if gap < GAP:
+            counts["undecided"] += 1
+            continue
+        cand = np.sort(found)
+        want, _, scores = orc.rerank_row(p, h, i, q, kh, amax, cand)
+        counts[accept_set(chosen, cand, scores, wl.topk, want)] += 1
+        if len(chosen):
+            kn = max(np.linalg.norm(kh[c * wl.cell:(c + 1) * wl.cell], axis=1).max()
+                     for c in chosen)
+            mag = np.linalg.norm(q) * kn / np.sqrt(wl.head_dim) + 1.0
+            if lam is not None:
+                mag += lam * float(amax[chosen].max())
+            np.testing.assert_allclose(got["score"][b, h, t, :len(chosen)],
+                                       scores[np.searchsorted(cand, chosen)], rtol=0,
+                                       atol=2e-6 * mag, err_msg=f"row {(b, h, t)}")
+    return counts
+
+
+@pytest.mark.parametrize("case", ["bf16_d64_two_forests", "f32_d128_prior",
+                                  "bf16_d128_needle_decode", "bf16_d64_keyscale_b2"])
+def test_rerank_over_found_cells(case):
+    """FS-B with eq. 12's token-level reranking of the found cells."""
+    wl, beam, slack, prior, use_tau = CASES[case]
+    inp = synth.generate(wl)
+    orc = oracle.Oracle()
+    p = oracle.problem_from(wl)
+    tau = np.array([admit_threshold(np.concatenate(
+        [orc.cell_summaries_head(p, inp["k"][b, h])[1] for b in range(wl.batch)]))
+        for h in range(wl.heads)], np.float32)
+    pr = wl.prior_arrays() if prior else None
+    got = gpu_chain(wl, inp, tau, beam, slack, pr, use_tau, rerank=True)
+    base = gpu_chain(wl, inp, tau, beam, slack, pr, use_tau)
+    assert np.array_equal(got["effort"], base["effort"])   # the search itself is unchanged
+    total = {"exact": 0, "tie": 0, "undecided": 0}
+    rows = np.arange(wl.n_q)
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            c = check_rerank_head(wl, inp, got, b, h, tau, beam, slack, rows, pr, use_tau)
+            for key in total:
+                total[key] += c[key]
+    print(case, total)
+    n = sum(total.values())
+    assert total["tie"] + total["undecided"] <= 0.03 * n, total
+
+
+def test_rerank_at_benchmark_shape_sampled():
+    """Eq. 12 reranking after the 64k prefill's search (beam 32, slack 1, both
+    forests), on 1024 sampled rows of heads 0 and 6."""
+    wl = synth.get_workload("prefill_b1h8_n65536_d128_bf16")
+    inp = synth.generate(wl)
+    orc = oracle.Oracle()
+    p = oracle.problem_from(wl)
+    tau = np.array([admit_threshold(orc.cell_summaries_head(p, inp["k"][0, h])[1])
+                    for h in range(wl.heads)], np.float32)
+    got = gpu_chain(wl, inp, tau, 32, 1.0, rerank=True)
+    rng = np.random.default_rng(12)
+    rows = np.sort(rng.choice(np.arange(wl.window + wl.cell, wl.n_q), 1024, replace=False))
+    for h in (0, 6):
+        c = check_rerank_head(wl, inp, got, 0, h, tau, 32, 1.0, rows)
+        print(h, c)
+        assert c["tie"] + c["undecided"] <= 0.05 * len(rows), c
     assert (got["idx"][:, :, :wl.window + wl.cell] == -1).all()

@@ -55,6 +55,7 @@ PLAIN_MUTANTS = [
     ("plain_prior_at_next_cell", "or_prior(p, head, i, f->first[node], f->amax[node])",
      "or_prior(p, head, i, f->first[node] + 1, f->amax[node])"),
     ("plain_topk_off_by_one", "pl_cut(found, n_u, p->topk, &g)", "pl_cut(found, n_u, p->topk - 1, &g)"),
+    ("plain_found_repeats", "dup |= found[r].first == found[t].first;", "dup |= 0;"),
 ]
 
 CASES = [("fsb_oracle.c",) + m for m in MUTANTS] + [("fsb_plain.c",) + m for m in PLAIN_MUTANTS]

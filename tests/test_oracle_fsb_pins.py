@@ -261,3 +261,49 @@ def test_plain_and_fixed_order_agree_where_decided(orc, prior):
         assert sorted(sel.tolist()) == sorted(ref["sel"][t, :ref["n_sel"][t]].tolist()), t
         assert eff == ref["effort"][t], t
     assert decided >= 390
+
+
+def test_found_cells_of_an_exhaustive_search(orc):
+    """A beam as wide as the leaves keeps every node, so the plain oracle's found
+    cells are all of C_i (forest 0), the admitted cells of C_i (forest tau), and
+    with both forests C_i again: the admitted cells come twice and are kept once."""
+    rng = np.random.default_rng(10)
+    n_cells, d, tau = 60, 64, 9.0
+    kbar, amax = _summaries(rng, n_cells, d)
+    p = _wide_problem(n_cells, d, 8, True)
+    f0 = orc.plain.forest_build(kbar, amax)
+    ft = orc.plain.forest_build(kbar, amax, tau)
+    for _ in range(12):
+        i = int(rng.integers(512, 512 + 32 * n_cells + 40))
+        q = rng.standard_normal(d).astype(np.float32)
+        n = orc.n_candidates(p, i)
+        cells, _ = orc.plain.beam_found(p, 0, i, q, f0, None, 64, 0.0)
+        assert sorted(cells.tolist()) == list(range(n))
+        cells, _ = orc.plain.beam_found(p, 0, i, q, None, ft, 64, 0.0)
+        assert sorted(cells.tolist()) == np.nonzero(amax[:n] >= tau)[0].tolist()
+        cells, _ = orc.plain.beam_found(p, 0, i, q, f0, ft, 64, 0.0)
+        assert sorted(cells.tolist()) == list(range(n))
+
+
+@pytest.mark.parametrize("prior", [False, True])
+def test_rerank_of_found_cells_with_constant_keys(orc, prior):
+    """When a cell's s keys all equal its mean key, eq. 12's score is eq. 7's plus
+    ln s (a log-sum-exp of s equal logits), so reranking the cells a search
+    found picks the same cells as the search's own eq. 7 top-K."""
+    rng = np.random.default_rng(11)
+    n_cells, d, topk, s = 200, 64, 8, 32
+    kbar, amax = _summaries(rng, n_cells, d)
+    k_head = np.repeat(kbar, s, axis=0)
+    p = _wide_problem(n_cells, d, topk, prior)
+    f0 = orc.plain.forest_build(kbar, amax)
+    ft = orc.plain.forest_build(kbar, amax, 9.3)
+    am64 = amax.astype(np.float64)
+    for _ in range(20):
+        i = int(rng.integers(512 + 32 * 20, 512 + 32 * n_cells))
+        q = rng.standard_normal(d).astype(np.float32)
+        cells, gap = orc.plain.beam_found(p, 0, i, q, f0, ft, 6, 1.0)
+        sel, sc = orc.plain.beam_row(p, 0, i, q, f0, ft, 6, 1.0)
+        rr, _, rr_sc = orc.rerank_row(p, 0, i, q, k_head, am64, cells)
+        assert sorted(rr.tolist()) == sorted(sel.tolist())
+        _, _, u = orc.select_row_at(p, 0, i, q, kbar.astype(np.float64), am64, cells)
+        np.testing.assert_allclose(rr_sc, u + math.log(s), rtol=1e-12, atol=1e-12)
