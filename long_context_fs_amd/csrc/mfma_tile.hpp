@@ -103,14 +103,12 @@ __device__ __forceinline__ void store_vt_4x8_sw(const uint4 in[4], uint16_t* vt,
     for (int e = 0; e < 8; ++e) {
         const uint32_t a0 = word_of(in[0], e >> 1), a1 = word_of(in[1], e >> 1);
         const uint32_t a2 = word_of(in[2], e >> 1), a3 = word_of(in[3], e >> 1);
+        // one byte permute per dword: the low (even e) or high (odd e) halves of
+        // two rows, first row low (v_perm_b32 selectors 0-3 pick src1's bytes)
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         uint2 w;
-        if (e & 1) {
-            w.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
-            w.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
-        } else {
-            w.x = (a0 & 0xFFFFu) | (a1 << 16);
-            w.y = (a2 & 0xFFFFu) | (a3 << 16);
-        }
+        w.x = __builtin_amdgcn_perm(a1, a0, sel);
+        w.y = __builtin_amdgcn_perm(a3, a2, sel);
         *reinterpret_cast<uint2*>(vt + vtsw_off(dc * 8 + e, col >> 3) + (col & 4)) = w;
     }
 }
@@ -139,14 +137,15 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x4& lo, const f32x4& hi)
 
 // Max / sum over the lanes l, l^16, l^32, l^48 (one query's four lane groups),
 // with the gfx950 row-swap permutes (VALU, no LDS round trip).
+// (IEEE maximum, which needs no canonicalising of the permuted operands)
 __device__ __forceinline__ float xrow_max(float x)
 {
     const uint32_t u = __float_as_uint(x);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const uint32_t v = __float_as_uint(x);
     const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float xrow_sum(float x)
 {

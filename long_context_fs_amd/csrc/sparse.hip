@@ -327,7 +327,7 @@ __device__ __forceinline__ void sp_tile(const uint16_t* ks, const uint16_t* vt,
             cm[c] = sel[qg][c] ? x : -INFINITY;
         }
         // scale_log2 > 0 commutes with max
-        const float tmax = xrow_max(fmaxf(cm[0], cm[1])) * scale_log2;
+        const float tmax = xrow_max(__builtin_elementwise_maximum(cm[0], cm[1])) * scale_log2;
         const bool raise = tmax > m_ref[qg] + kLazy;
         const float m_new = raise ? tmax : m_ref[qg];
         corr[qg] = raise ? __builtin_amdgcn_exp2f(m_ref[qg] - m_new) : 1.f;   // 0 at the start
