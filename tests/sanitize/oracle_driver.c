@@ -125,6 +125,11 @@ static int run(int n_ctx, int d, int window, int topk, int budget, int n_recent,
             or_beam_row(&p, 0, i, q + (size_t)i * d, &f32s[0], &f32s[1], 4, 1.0, sel, scores, &ns);
             or_beam64_row(&p, 0, i, q + (size_t)i * d, &f64s[0], &f64s[1], 4, 1.0, sel, scores,
                           &ns, &gap);
+            /* eq. 12 over the found cells (at most 2 beam + 2 of them) */
+            int found[10];
+            const int nf = or_beam64_found(&p, 0, i, q + (size_t)i * d, &f64s[0], &f64s[1], 4,
+                                           1.0, found, &ns, &gap);
+            or_rerank_row(&p, 0, i, q + (size_t)i * d, k, amax, found, nf, sel, &gap, scores);
         }
         int* bsel = (int*)malloc(sizeof(int) * nr * topk);
         double* bsc = (double*)malloc(sizeof(double) * nr * topk);
