@@ -1,8 +1,9 @@
-"""Benchmark of the FS-L forward (six C-ABI calls) on one MI355X.
+"""Benchmark of the FS-L forward (five C-ABI calls) on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input, with
 the inputs resident in HBM: cell summaries, prefix pruning, scoring + top-K,
-window attention, sparse readout, combine.  The headline workload is the 64k
+window attention, and the sparse readout with the combine (eq. 2) in its
+epilogue.  The headline workload is the 64k
 prefill (B1 H8 N65536 d128 bf16, K32, P256); the 16k prefill and the 256k
 decode are reported alongside.  Per-kernel times come from HIP events recorded
 on the launch stream between the calls of the timed steps.
@@ -36,7 +37,9 @@ PRIMARY = "prefill_b1h8_n65536_d128_bf16"
 ALSO = ["prefill_b1h1_n2048_d64_f32", "prefill_b2h16_n4096_d64_bf16",
         "prefill_b1h16_n16384_d64_bf16", "decode_b1h8_n262144_q256_d128_bf16",
         "prefill_b1h8_n65536_d128_bf16_prior"]
-PHASES = ["summaries", "prune", "select", "window", "sparse", "combine"]
+# Timed phases of a step; "sparse" is the readout with eq. 2 in its epilogue
+# (fs_sparse_attn_combine), so the step has no separate combine pass.
+PHASES = ["summaries", "prune", "select", "window", "sparse"]
 # Source file of each phase's kernel (for matching stored HBM traffic counters).
 PHASE_SRC = {"summaries": "summaries.hip", "prune": "prune.hip", "select": "select.hip",
              "window": "window.hip", "sparse": "sparse.hip", "combine": "combine.hip",
@@ -140,10 +143,9 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
         mark(3)
         fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)
         mark(4)
-        fs.fs_sparse_attn(p, q, k, v, fwd.idx, fwd.topk, fwd.rms_eps, fwd.o_lr, fwd.ws_sparse)
+        fs.fs_sparse_attn_combine(p, q, k, v, fwd.idx, fwd.topk, fwd.rms_eps, fwd.o_sr, alpha,
+                                  fwd.o, fwd.ws_sparse)
         mark(5)
-        fs.fs_combine(p, fwd.o_sr, fwd.o_lr, alpha, fwd.o)
-        mark(6)
 
     for _ in range(warmup):
         step()
@@ -161,7 +163,7 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
     # per-phase times: events on the launch stream between the calls
     phase_ms = {ph: [] for ph in PHASES}
     for _ in range(steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(PHASES) + 1)]
         step(ev)
         torch.cuda.synchronize()
         for j, ph in enumerate(PHASES):
@@ -311,7 +313,8 @@ class FsbSetup:
 
 def run_fsb(name, steps, warmup, torch, fs):
     """FS-B forward at a workload's shape: summaries, both forests, beam search of
-    width FSB_BEAM (slack FSB_SLACK), then the FS-L window, readout and combine."""
+    width FSB_BEAM (slack FSB_SLACK), then the FS-L window and the readout with eq. 2 in
+    its epilogue."""
     wl = synth.WORKLOADS[name]
     x = synth.generate(wl)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -327,9 +330,9 @@ def run_fsb(name, steps, warmup, torch, fs):
              ("forest_build", fb.build),
              ("beam_select", lambda: fb.search(q)),
              ("window", lambda: fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)),
-             ("sparse", lambda: fs.fs_sparse_attn(p, q, k, v, fb.idx, wl.topk, fwd.rms_eps,
-                                                  fwd.o_lr, fwd.ws_sparse)),
-             ("combine", lambda: fs.fs_combine(p, fwd.o_sr, fwd.o_lr, alpha, fwd.o))]
+             ("sparse", lambda: fs.fs_sparse_attn_combine(p, q, k, v, fb.idx, wl.topk,
+                                                          fwd.rms_eps, fwd.o_sr, alpha, fwd.o,
+                                                          fwd.ws_sparse))]
 
     def step(ev=None):
         for j, (_, fn) in enumerate(calls):
@@ -504,7 +507,8 @@ def run_phase(name, phase, reps, torch, fs):
         "rerank": lambda: fs.fs_rerank_topk(p, q, k, f.keep, f.keep_count, f.keep_w, f.topk,
                                             f.idx, None, None, f.prior, rr_ws),
         "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),
-        "sparse": lambda: fs.fs_sparse_attn(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_lr, f.ws_sparse),
+        "sparse": lambda: fs.fs_sparse_attn_combine(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_sr,
+                                                    alpha, f.o, f.ws_sparse),
         "combine": lambda: fs.fs_combine(p, f.o_sr, f.o_lr, alpha, f.o),
     }
     for _ in range(reps):

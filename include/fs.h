@@ -15,6 +15,7 @@
  *   fs_stream_*        eqs. 2-9 from a bounded per-head state ("Bounded memory",
  *                      Practical Implications): decode or chunked prefill
  *   fs_combine         eq. 2   o = o_sr + alpha_h * o_lr
+ *   fs_sparse_attn_combine  eqs. 9 + 2  the readout with eq. 2 in its epilogue
  *   fs_forest_*, fs_beam_select  eqs. 10-11  FS-B: causal forests over the cell
  *                      summaries and beam search for S_i (section 3.4)
  *
@@ -254,6 +255,19 @@ fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k
 fs_status fs_sparse_attn_noalloc(const fs_problem* problem, const void* q, const void* k,
                                  const void* v, const int32_t* idx, int32_t topk, float rms_eps,
                                  void* o_lr, void* stream);
+
+/* The long-range readout (eq. 9, as fs_sparse_attn) with the range combination
+ * (eq. 2) in its epilogue: o = o_sr + alpha[h] * o_lr, o_lr kept in fp32 until
+ * the sum (fs_sparse_attn followed by fs_combine rounds it to the storage type
+ * first, so bf16 results may differ by one rounding of alpha_h o_lr).  o_sr and
+ * o: [B][H][n_q][d] with the problem's o_stride; o may be o_sr itself (each
+ * element is read before it is written, by the same thread).  alpha: float32
+ * [H].  workspace / ws_bytes as for fs_sparse_attn.  One fewer pass over the
+ * branch outputs than the two calls. */
+fs_status fs_sparse_attn_combine(const fs_problem* problem, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, int32_t topk, float rms_eps,
+                                 const void* o_sr, const float* alpha, void* workspace,
+                                 size_t ws_bytes, void* o, void* stream);
 
 /* Range combination, eq. 2: o = o_sr + alpha[h] * o_lr.  alpha: float32 [H]. */
 fs_status fs_combine(const fs_problem* problem, const void* o_sr, const void* o_lr,

@@ -371,6 +371,26 @@ fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k
                     "fs_sparse_attn");
 }
 
+fs_status fs_sparse_attn_combine(const fs_problem* problem, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, int32_t topk, float rms_eps,
+                                 const void* o_sr, const float* alpha, void* workspace,
+                                 size_t ws_bytes, void* o, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(q); FS_PTR(k); FS_PTR(v); FS_PTR(o_sr); FS_PTR(o);
+    if (!idx) return fail(FS_ERR_INVALID, "idx is NULL");
+    if (!alpha) return fail(FS_ERR_INVALID, "alpha is NULL");
+    if (topk < 1 || topk > 64) return fail(FS_ERR_UNSUPPORTED, "topk %d outside [1, 64]", topk);
+    if (!(rms_eps >= 0.0f)) return fail(FS_ERR_INVALID, "rms_eps must be >= 0");
+    if (workspace && ws_bytes < fs::sparse_ws_bytes(sh))
+        return fail(FS_ERR_INVALID, "workspace of %zu bytes, need %zu", ws_bytes,
+                    fs::sparse_ws_bytes(sh));
+    return from_hip(fs::launch_sparse(sh, q, k, v, idx, topk, rms_eps, workspace, o,
+                                      (hipStream_t)stream, o_sr, alpha),
+                    "fs_sparse_attn_combine");
+}
+
 fs_status fs_sparse_attn_noalloc(const fs_problem* problem, const void* q, const void* k,
                                  const void* v, const int32_t* idx, int32_t topk, float rms_eps,
                                  void* o_lr, void* stream)

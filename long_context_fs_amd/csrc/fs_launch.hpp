@@ -73,8 +73,10 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
                          bool table_ready, size_t ws_bytes);
 // Merge of split attention states (bf16 output with the shape's o strides), with
 // the readout's RMSNorm when rms.
+// o_sr (nullable): then o = o_sr + alpha[h] * (the merged, RMS-normalised row), eq. 2.
 hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const float2* ws_ml,
-                              bool rms, float rms_eps, void* o, hipStream_t st);
+                              bool rms, float rms_eps, void* o, hipStream_t st,
+                              const void* o_sr = nullptr, const float* alpha = nullptr);
 hipError_t launch_rope_table(const Shape& sh, double rope_base, void* table, hipStream_t st);
 // Workgroups over which the readout splits each query's cells (1: unsplit), and
 // the workspace bytes of their partial softmax states.
@@ -85,9 +87,12 @@ size_t sparse_ws_bytes(const Shape& sh);
 constexpr size_t kSparseNoAllocBytes = (size_t)48 << 20;
 void* sparse_noalloc_scratch(hipError_t* err);
 
+// o_sr (nullable): eq. 2 in the readout's epilogue, o_lr then receives
+// o = o_sr + alpha[h] * o_lr (o_lr kept in fp32 until the sum; o may alias o_sr).
 hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const void* v,
                          const int32_t* idx, int topk, float rms_eps, void* ws, void* o_lr,
-                         hipStream_t st);
+                         hipStream_t st, const void* o_sr = nullptr,
+                         const float* alpha = nullptr);
 hipError_t launch_combine(const Shape& sh, const void* o_sr, const void* o_lr, const float* alpha,
                           void* o, hipStream_t st);
 

@@ -61,8 +61,9 @@ __global__ __launch_bounds__(256) void sparse_attn_rowwise_kernel(
     const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const typename E::storage* __restrict__ k, const typename E::storage* __restrict__ v,
     int64_t kvs0, int64_t kvs1, int64_t kvs2, int H, int nq, const int32_t* __restrict__ idx,
-    int topk, float scale_log2, float rms_eps, typename E::storage* __restrict__ o,
-    int64_t os0, int64_t os1, int64_t os2)
+    int topk, float scale_log2, float rms_eps, typename E::storage* o,
+    int64_t os0, int64_t os1, int64_t os2, const typename E::storage* o_sr,
+    const float* __restrict__ alpha)
 {
     constexpr int EPL = E::kPer16B;
     constexpr int R = D / kWave;
@@ -136,6 +137,16 @@ __global__ __launch_bounds__(256) void sparse_attn_rowwise_kernel(
     ss = wave_sum(ss);
     const float inv_rms = 1.f / sqrtf(ss / (float)D + rms_eps);
     typename E::storage* orow = o + b * os0 + h * os1 + row * os2;
+    if (o_sr) {                        // eq. 2 in the epilogue: o = o_sr + alpha_h o_lr
+        const typename E::storage* srow = o_sr + b * os0 + h * os1 + row * os2;
+        const float a = alpha[h];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float x = load1<E>(srow + lane + r * kWave);
+            store1<E>(orow + lane + r * kWave, fmaf(a, u[r] * inv_rms, x));
+        }
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) store1<E>(orow + lane + r * kWave, u[r] * inv_rms);
 }
@@ -377,8 +388,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t kvs0, int64_t kvs1,
     int64_t kvs2, int H, int BH, int nq, int C, const int32_t* __restrict__ idx, int topk,
-    float scale_log2, float rms_eps, uint16_t* __restrict__ o, int64_t os0, int64_t os1,
-    int64_t os2, int n_split, float* __restrict__ ws_acc, float2* __restrict__ ws_ml)
+    float scale_log2, float rms_eps, uint16_t* o, int64_t os0, int64_t os1,
+    int64_t os2, int n_split, float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
+    const uint16_t* o_sr, const float* __restrict__ alpha)
 {
     using namespace mf;
     constexpr int KS = D / 32, DB = D / 16;
@@ -532,6 +544,23 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
         const float inv_rms = 1.f / sqrtf(ss / (float)D + rms_eps);
         if (r >= n_rows) continue;
         uint16_t* orow = o + b * os0 + h * os1 + (t0 + r) * os2;
+        if (o_sr) {                    // eq. 2 in the epilogue: o = o_sr + alpha_h o_lr
+            const uint16_t* srow = o_sr + b * os0 + h * os1 + (t0 + r) * os2;
+            const float a = alpha[h];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const uint2 x2 = *reinterpret_cast<const uint2*>(srow + 16 * db + 4 * g);
+                uint2 w2;
+                w2.x = cvt_pk_bf16(fmaf(a, acc[db][qg][0] * inv_rms, __uint_as_float(x2.x << 16)),
+                                   fmaf(a, acc[db][qg][1] * inv_rms,
+                                        __uint_as_float(x2.x & 0xFFFF0000u)));
+                w2.y = cvt_pk_bf16(fmaf(a, acc[db][qg][2] * inv_rms, __uint_as_float(x2.y << 16)),
+                                   fmaf(a, acc[db][qg][3] * inv_rms,
+                                        __uint_as_float(x2.y & 0xFFFF0000u)));
+                *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = w2;
+            }
+            continue;
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             uint2 w2;
@@ -552,8 +581,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
                                                            const float2* __restrict__ ws_ml,
                                                            int H, int nq, long n_rows_all,
                                                            int n_split, float rms_eps,
-                                                           uint16_t* __restrict__ o, int64_t os0,
-                                                           int64_t os1, int64_t os2)
+                                                           uint16_t* o, int64_t os0,
+                                                           int64_t os1, int64_t os2,
+                                                           const uint16_t* o_sr,
+                                                           const float* __restrict__ alpha)
 {
     constexpr int R = D / kWave;
     const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);    // = bh * nq + t
@@ -594,19 +625,30 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
     const long bh = row / nq, t = row - bh * nq;
     const int h = (int)(bh % H), b = (int)(bh / H);
     uint16_t* orow = o + b * os0 + h * os1 + t * os2;
+    if (o_sr) {                        // eq. 2 in the epilogue: o = o_sr + alpha_h o_lr
+        const uint16_t* srow = o_sr + b * os0 + h * os1 + t * os2;
+        const float a = alpha[h];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float x = load1<Bf16>(srow + lane + r * kWave);
+            store1<Bf16>(orow + lane + r * kWave, fmaf(a, acc[r] * inv_rms, x));
+        }
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) store1<Bf16>(orow + lane + r * kWave, acc[r] * inv_rms);
 }
 
 hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const float2* ws_ml,
-                              bool rms, float rms_eps, void* o, hipStream_t st)
+                              bool rms, float rms_eps, void* o, hipStream_t st, const void* o_sr,
+                              const float* alpha)
 {
     const long rows_all = (long)sh.B * sh.H * sh.nq;
     dim3 mgrid((unsigned)((rows_all + 3) / 4));
 #define FS_MERGE(D, RMS)                                                                          \
     hipLaunchKernelGGL((split_merge_kernel<D, RMS>), mgrid, dim3(256), 0, st, ws_acc, ws_ml,      \
                        sh.H, sh.nq, rows_all, S, rms_eps, (uint16_t*)o, sh.os[0], sh.os[1],      \
-                       sh.os[2])
+                       sh.os[2], (const uint16_t*)o_sr, alpha)
     if (sh.d == 64) {
         if (rms) FS_MERGE(64, true); else FS_MERGE(64, false);
     } else {
@@ -636,7 +678,7 @@ size_t sparse_ws_bytes(const Shape& sh)
 
 hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const void* v,
                          const int32_t* idx, int topk, float rms_eps, void* ws, void* o_lr,
-                         hipStream_t st)
+                         hipStream_t st, const void* o_sr, const float* alpha)
 {
     if (sh.nq == 0) return hipSuccess;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
@@ -656,12 +698,13 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
                            (const uint16_t*)k, (const uint16_t*)v, sh.kvs[0], sh.kvs[1],          \
                            sh.kvs[2], sh.H, sh.B * sh.H, sh.nq, sh.C, idx, topk, scale_log2,      \
                            rms_eps,                                                               \
-                           (uint16_t*)o_lr, sh.os[0], sh.os[1], sh.os[2], S, ws_acc, ws_ml)
+                           (uint16_t*)o_lr, sh.os[0], sh.os[1], sh.os[2], S, ws_acc, ws_ml,      \
+                           (const uint16_t*)o_sr, alpha)
         if (sh.d == 64) FS_SPARSE_MFMA(64); else FS_SPARSE_MFMA(128);
 #undef FS_SPARSE_MFMA
         hipError_t err = hipGetLastError();
         if (err != hipSuccess || S <= 1) return err;
-        return launch_split_merge(sh, S, ws_acc, ws_ml, true, rms_eps, o_lr, st);
+        return launch_split_merge(sh, S, ws_acc, ws_ml, true, rms_eps, o_lr, st, o_sr, alpha);
     }
     note_path("readout: row-wise, one wavefront per query (%s)",
               !sh.bf16 ? "fp32 storage"
@@ -673,7 +716,8 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
                        (const typename E::storage*)q, sh.qs[0], sh.qs[1], sh.qs[2],              \
                        (const typename E::storage*)k, (const typename E::storage*)v, sh.kvs[0],  \
                        sh.kvs[1], sh.kvs[2], sh.H, sh.nq, idx, topk, scale_log2, rms_eps,        \
-                       (typename E::storage*)o_lr, sh.os[0], sh.os[1], sh.os[2])
+                       (typename E::storage*)o_lr, sh.os[0], sh.os[1], sh.os[2],                 \
+                       (const typename E::storage*)o_sr, alpha)
     if (sh.bf16) {
         if (sh.d == 64) FS_SPARSE(Bf16, 64); else FS_SPARSE(Bf16, 128);
     } else {

@@ -488,11 +488,9 @@ hipError_t launch_stream_step(const StreamCfg& c, const StreamLayout& Ly, void* 
     sh.kvs[0] = (int64_t)c.H * Ly.M * c.s * c.d;
     sh.kvs[1] = (int64_t)Ly.M * c.s * c.d;
     sh.kvs[2] = c.d;
-    err = launch_sparse(sh, q, sd.pool_k, sd.pool_v, idx_slot, c.K, c.rms_eps,
-                        Ly.ws_bytes ? base + Ly.ws : nullptr, base + Ly.olr, st);
-    if (err != hipSuccess) return err;
-    // 5. eq. 2
-    return launch_combine(sh, base + Ly.osr, base + Ly.olr, alpha, o, st);
+    // 5. eq. 2 in the readout's epilogue: o = o_sr + alpha_h o_lr
+    return launch_sparse(sh, q, sd.pool_k, sd.pool_v, idx_slot, c.K, c.rms_eps,
+                         Ly.ws_bytes ? base + Ly.ws : nullptr, o, st, base + Ly.osr, alpha);
 }
 
 }  // namespace fs

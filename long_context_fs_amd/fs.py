@@ -19,7 +19,7 @@ CELL = 32
 
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
            "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
-           "fs_sparse_attn_noalloc", "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size",
+           "fs_sparse_attn_noalloc", "fs_sparse_attn_combine", "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size",
            "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
            "fs_stream_step", "fs_forest_size", "fs_forest_build", "fs_beam_select",
            "fs_status_string", "fs_last_error", "fs_last_path")
@@ -76,6 +76,7 @@ def load(path: str | None = None):
         "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, C.c_size_t, vp, vp],
         "fs_sparse_attn_noalloc": [P, vp, vp, vp, vp, i32, f32, vp, vp],
+        "fs_sparse_attn_combine": [P, vp, vp, vp, vp, i32, f32, vp, vp, vp, C.c_size_t, vp, vp],
         "fs_combine": [P, vp, vp, vp, vp, vp],
         "fs_forest_size": [P, C.POINTER(C.c_size_t)],
         "fs_forest_build": [P, vp, vp, vp, vp, vp],
@@ -259,6 +260,17 @@ def last_path() -> str:
     return load().fs_last_path().decode()
 
 
+def fs_sparse_attn_combine(prob, q, k, v, idx, topk, rms_eps, o_sr, alpha, o, workspace=None,
+                           stream=None):
+    """Eq. 9's readout with eq. 2 in its epilogue: o = o_sr + alpha_h * o_lr (o may be o_sr)."""
+    ws, nbytes = (None, 0) if workspace is None else \
+        (_p(workspace), workspace.numel() * workspace.element_size())
+    _check("fs_sparse_attn_combine",
+           load().fs_sparse_attn_combine(C.byref(prob), _p(q), _p(k), _p(v), _p(idx), topk,
+                                         float(rms_eps), _p(o_sr), _p(alpha), ws, nbytes, _p(o),
+                                         _s(stream)))
+
+
 def fs_sparse_attn_noalloc(prob, q, k, v, idx, topk, rms_eps, o_lr, stream=None):
     """fs_sparse_attn with the split states in the library's own device array (no
     workspace, no allocation)."""
@@ -318,7 +330,9 @@ class FsForward:
             assert lam.shape == (H,) and sig.shape == (H,)
             self.prior = (self.amax, lam, sig)
 
-    def __call__(self, q, k, v, alpha, stream=None, keep_score=True):
+    def __call__(self, q, k, v, alpha, stream=None, keep_score=True, fused=False):
+        """The forward; fused: eq. 2 in the readout's epilogue (fs_sparse_attn_combine),
+        so o_lr is not written."""
         p = self.prob
         fs_cell_summaries(p, k, self.kbar, self.amax, stream)
         if self.pruned:
@@ -328,6 +342,10 @@ class FsForward:
                        self.idx, self.score if keep_score else None, stream, self.prior,
                        self.ws_select)
         fs_window_attn(p, q, k, v, self.rope_base, self.ws, self.o_sr, stream)
+        if fused:
+            fs_sparse_attn_combine(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_sr,
+                                   alpha, self.o, self.ws_sparse, stream)
+            return self.o
         fs_sparse_attn(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_lr, self.ws_sparse,
                        stream)
         fs_combine(p, self.o_sr, self.o_lr, alpha, self.o, stream)

@@ -141,6 +141,14 @@ def test_call_specific_limits(lib):
         assert lib.fs_sparse_attn(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, 1e-6, FAKE, 16, FAKE,
                                   None) == 1
         assert b"workspace" in lib.fs_last_error()
+    # the readout with eq. 2 in its epilogue needs o_sr, alpha and o
+    assert lib.fs_sparse_attn_combine(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, 1e-6, None, FAKE,
+                                      None, 0, FAKE, None) == 1
+    assert lib.fs_sparse_attn_combine(C.byref(p), FAKE, FAKE, FAKE, FAKE, 8, 1e-6, FAKE, None,
+                                      None, 0, FAKE, None) == 1
+    assert b"alpha" in lib.fs_last_error()
+    assert lib.fs_sparse_attn_combine(C.byref(p), FAKE, FAKE, FAKE, FAKE, 65, 1e-6, FAKE, FAKE,
+                                      None, 0, FAKE, None) == 2
     # reranking validates like selection, and needs the keys
     assert lib.fs_rerank_topk(C.byref(p), FAKE, None, None, None, None, None, None, 0, 8, FAKE,
                               None, None, 0, None) == 1

@@ -767,6 +767,57 @@ def test_small_sparse_unsplit(name):
     assert (got[none] == 0).all()
 
 
+@pytest.mark.parametrize("name", ["f32_d64_noprune", "f32_d128_recent", "bf16_d64_scaled_ragged",
+                                  "bf16_d128_needle", "bf16_d128_decode", "bf16_d128_decode_wide",
+                                  "bf16_d128_wide_keep_k64", "bf16_d128_no_cells"])
+@pytest.mark.parametrize("split", [False, True])
+def test_readout_with_combine_epilogue(name, split):
+    """fs_sparse_attn_combine (eq. 9 with eq. 2 in its epilogue) against the two
+    calls fs_sparse_attn + fs_combine on the same cells and o_sr: bit for bit for
+    fp32 storage (the same fp32 operations); for bf16 within one rounding of
+    alpha_h o_lr, which the two calls round to bf16 before the sum.  In place
+    (o = o_sr) it equals the out-of-place call bit for bit, and every row is
+    within tolerance of the oracle's eq. 2 row over the GPU's cells."""
+    from long_context_fs_amd import fs as fsb
+    wl, x, g, ref = small_case(name)
+    q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+    fwd = FsForward.for_workload(wl)
+    p = fwd.prob
+    idx = torch.from_numpy(g["idx"]).cuda()
+    o_sr = to_dev(g["o_sr"], wl.dtype)                 # the GPU's own branch output, exact
+    alpha = torch.from_numpy(x["alpha"]).cuda()
+    ws = fwd.ws_sparse if split else None
+    nan = lambda: torch.full_like(o_sr, float("nan"))
+    o_lr, o_two = nan(), nan()
+    fsb.fs_sparse_attn(p, q, k, v, idx, wl.topk, wl.rms_eps, o_lr, ws)
+    fsb.fs_combine(p, o_sr, o_lr, alpha, o_two)
+    o_one = nan()
+    fsb.fs_sparse_attn_combine(p, q, k, v, idx, wl.topk, wl.rms_eps, o_sr, alpha, o_one, ws)
+    o_in = o_sr.clone()
+    fsb.fs_sparse_attn_combine(p, q, k, v, idx, wl.topk, wl.rms_eps, o_in, alpha, o_in, ws)
+    torch.cuda.synchronize()
+    two, one, inp = (t.float().cpu().numpy() for t in (o_two, o_one, o_in))
+    lr = o_lr.float().cpu().numpy()
+    assert np.isfinite(one).all()
+    np.testing.assert_array_equal(one, inp)
+    if wl.dtype == "f32":
+        np.testing.assert_array_equal(one, two)
+    else:
+        a = x["alpha"][None, :, None, None]
+        # the unfused o_lr's rounding (half an ulp, <= 2^-8 relative) and one bf16
+        # ulp (<= 2^-7 relative) where the two sums round to neighbours
+        bound = a * 2.0 ** -8 * np.abs(lr) + 2.0 ** -7 * np.maximum(np.abs(one), np.abs(two))
+        assert (np.abs(one - two) <= bound).all(), np.abs(one - two).max()
+    rows = all_rows(wl)
+    pr = oracle.problem_from(wl)
+    want = np.stack([g["o_sr"][b, h, t].astype(np.float64) + x["alpha"][h] *
+                     orc().sparse_row(pr, x["q"][b, h, t], x["k"][b, h], x["v"][b, h],
+                                      g["idx"][b, h, t][g["idx"][b, h, t] >= 0])
+                     for b, h, t in rows])
+    got = np.stack([one[b, h, t] for b, h, t in rows])
+    assert row_rel_err(got, want).max() <= TOL[wl.dtype]
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale_k,scale_q", [(1.5e4, 1.0 / 1.5e4), (1e-6, 1e6), (3e4, 1.0 / 3e4)])
 def test_window_extreme_magnitudes(d, scale_k, scale_q):
