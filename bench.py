@@ -171,6 +171,26 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
     phase_avg = {ph: float(np.mean(v)) for ph, v in phase_ms.items()}
     phase_pct = {ph: [float(np.percentile(v, q)) for q in (10, 50, 90)]
                  for ph, v in phase_ms.items()}
+    # the same step captured once in a HIP graph and replayed (no launch gaps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / steps
+    del graph
     cold_ms = None
     if wl.q_pos0 > 0:
         # decode: every step after a 512 MiB write that evicts L2 and the Infinity Cache
@@ -214,6 +234,7 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
     return dict(wl=wl, ms_step=ms_step, wall=wall, phase_ms=phase_avg, work=work,
                 qps=queries / (ms_step * 1e-3), tflops=total_flop / (ms_step * 1e-3) / 1e12,
                 total_gflop=total_flop / 1e9, phase_pct=phase_pct, cold_ms=cold_ms,
+                graph_ms=graph_ms,
                 qhps=queries * wl.heads / (ms_step * 1e-3))
 
 
@@ -651,7 +672,7 @@ def main():
         for name in ALSO:
             r = run_workload(name, args.steps, args.warmup, torch, fs)
             also[name] = {"queries_per_s": r["qps"], "query_heads_per_s": r["qhps"],
-                          "ms_per_step": r["ms_step"],
+                          "ms_per_step": r["ms_step"], "graph_ms_per_step": r["graph_ms"],
                           "tflops": r["tflops"], "gflop_per_step": r["total_gflop"],
                           "phase_ms": r["phase_ms"], "phase_ms_p10_p50_p90": r["phase_pct"],
                           "phase_roofline_frac": phase_fracs(r), "roofline": roofline(r)}
@@ -668,6 +689,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": main_res["ms_step"],
+        "graph_ms_per_step": main_res["graph_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
