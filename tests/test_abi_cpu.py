@@ -261,3 +261,20 @@ def test_fsb_arguments_rejected(lib):
     n_cells = 8192 // 32                                   # 2 heads, 2 n_cells - 1 nodes, d 64
     assert large.value > small.value >= 2 * (2 * n_cells // 2 - 1) * 64 * 4
     assert large.value >= 2 * (2 * n_cells - 1) * 64 * 4
+
+
+def test_fsb_select_wrapper_checks_shapes(lib):
+    """FsbSelect refuses a query range over other forests' cells, a range of another
+    length without its own outputs, and outputs of the wrong shape, before any call
+    (host tensors: nothing reaches the device)."""
+    torch = pytest.importorskip("torch")
+    p = _prob(n_ctx=2048, n_q=256, q_pos0=2048 - 256)
+    sel = fs.FsbSelect(p, 8, beam=4, slack=1.0, device="cpu")
+    q = torch.zeros((1, 2, 256, 64), dtype=torch.bfloat16)
+    with pytest.raises(fs.FsError, match="must match"):
+        sel.select(q, prob=_prob(n_ctx=4096, n_q=256, q_pos0=4096 - 256))
+    with pytest.raises(fs.FsError, match="another length"):
+        sel.select(q[:, :, :100], prob=_prob(n_ctx=2048, n_q=100, q_pos0=1000))
+    bad = torch.zeros((1, 2, 100, 7), dtype=torch.int32)
+    with pytest.raises(fs.FsError, match="idx has shape"):
+        sel.select(q[:, :, :100], prob=_prob(n_ctx=2048, n_q=100, q_pos0=1000), idx=bad)

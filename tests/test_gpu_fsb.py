@@ -354,3 +354,31 @@ def test_fsb_selection_feeds_the_readout():
             err = np.abs(o[0, h, t] - ref).max() / (den if den > 0 else 1.0)
             worst = max(worst, err)
     assert worst <= 2e-2, worst
+
+
+def test_fsb_select_wrapper_sub_range():
+    """FsbSelect.select(prob=...) for a query sub-range over the same forests
+    (its own idx, score and effort tensors) gives the same rows as the full
+    range."""
+    wl = small("m", n_ctx=2048, n_q=800, q_pos0=2048 - 800)
+    inp, kbar, amax, tau = make_inputs(wl)
+    prob = fs.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, wl.n_q, wl.q_pos0,
+                      wl.window, fs.FS_BF16)
+    sel = fs.FsbSelect(prob, wl.topk, beam=8, slack=1.0)
+    sel.build(torch.from_numpy(kbar).cuda(), torch.from_numpy(amax).cuda(),
+              torch.from_numpy(tau).cuda())
+    q = torch.from_numpy(inp["q"]).cuda().to(torch.bfloat16)
+    full = sel.select(q, score=True, effort=True).clone()
+    full_sc, full_ef = sel.score.clone(), sel.effort.clone()
+    lo, n = 300, 137
+    sub = fs.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, n, wl.q_pos0 + lo, wl.window,
+                     fs.FS_BF16)
+    B, H, K = wl.batch, wl.heads, wl.topk
+    idx = torch.full((B, H, n, K), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, H, n, K), dtype=torch.float32, device="cuda")
+    ef = torch.zeros((B, H, n), dtype=torch.int32, device="cuda")
+    sel.select(q[:, :, lo:lo + n].contiguous(), prob=sub, idx=idx, score=sc, effort=ef)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, full[:, :, lo:lo + n])
+    assert torch.equal(sc, full_sc[:, :, lo:lo + n])
+    assert torch.equal(ef, full_ef[:, :, lo:lo + n])
