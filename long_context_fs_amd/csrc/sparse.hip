@@ -576,14 +576,14 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
 // O = sum_s 2^(m_s - M) O_s over l = sum_s 2^(m_s - M) l_s with M = max_s m_s;
 // then RMSNorm when RMS (the readout, eq. 9).  One wavefront per query, D / 64
 // dims per lane.
-template <int D, bool RMS>
+template <class E, int D, bool RMS>
 __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ ws_acc,
                                                            const float2* __restrict__ ws_ml,
                                                            int H, int nq, long n_rows_all,
                                                            int n_split, float rms_eps,
-                                                           uint16_t* o, int64_t os0,
+                                                           typename E::storage* o, int64_t os0,
                                                            int64_t os1, int64_t os2,
-                                                           const uint16_t* o_sr,
+                                                           const typename E::storage* o_sr,
                                                            const float* __restrict__ alpha)
 {
     constexpr int R = D / kWave;
@@ -624,19 +624,19 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
     if constexpr (RMS) inv_rms = 1.f / sqrtf(wave_sum(ss) / (float)D + rms_eps);
     const long bh = row / nq, t = row - bh * nq;
     const int h = (int)(bh % H), b = (int)(bh / H);
-    uint16_t* orow = o + b * os0 + h * os1 + t * os2;
+    typename E::storage* orow = o + b * os0 + h * os1 + t * os2;
     if (o_sr) {                        // eq. 2 in the epilogue: o = o_sr + alpha_h o_lr
-        const uint16_t* srow = o_sr + b * os0 + h * os1 + t * os2;
+        const typename E::storage* srow = o_sr + b * os0 + h * os1 + t * os2;
         const float a = alpha[h];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float x = load1<Bf16>(srow + lane + r * kWave);
-            store1<Bf16>(orow + lane + r * kWave, fmaf(a, acc[r] * inv_rms, x));
+            const float x = load1<E>(srow + lane + r * kWave);
+            store1<E>(orow + lane + r * kWave, fmaf(a, acc[r] * inv_rms, x));
         }
         return;
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) store1<Bf16>(orow + lane + r * kWave, acc[r] * inv_rms);
+    for (int r = 0; r < R; ++r) store1<E>(orow + lane + r * kWave, acc[r] * inv_rms);
 }
 
 hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const float2* ws_ml,
@@ -645,14 +645,18 @@ hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const
 {
     const long rows_all = (long)sh.B * sh.H * sh.nq;
     dim3 mgrid((unsigned)((rows_all + 3) / 4));
-#define FS_MERGE(D, RMS)                                                                          \
-    hipLaunchKernelGGL((split_merge_kernel<D, RMS>), mgrid, dim3(256), 0, st, ws_acc, ws_ml,      \
-                       sh.H, sh.nq, rows_all, S, rms_eps, (uint16_t*)o, sh.os[0], sh.os[1],      \
-                       sh.os[2], (const uint16_t*)o_sr, alpha)
-    if (sh.d == 64) {
-        if (rms) FS_MERGE(64, true); else FS_MERGE(64, false);
-    } else {
-        if (rms) FS_MERGE(128, true); else FS_MERGE(128, false);
+#define FS_MERGE(E, D, RMS)                                                                       \
+    hipLaunchKernelGGL((split_merge_kernel<E, D, RMS>), mgrid, dim3(256), 0, st, ws_acc, ws_ml,   \
+                       sh.H, sh.nq, rows_all, S, rms_eps, (typename E::storage*)o, sh.os[0],     \
+                       sh.os[1], sh.os[2], (const typename E::storage*)o_sr, alpha)
+    if (sh.bf16) {
+        if (sh.d == 64) {
+            if (rms) FS_MERGE(Bf16, 64, true); else FS_MERGE(Bf16, 64, false);
+        } else {
+            if (rms) FS_MERGE(Bf16, 128, true); else FS_MERGE(Bf16, 128, false);
+        }
+    } else {   // fp32 storage: only the window splits (the readout runs row-wise)
+        if (sh.d == 64) FS_MERGE(F32, 64, false); else FS_MERGE(F32, 128, false);
     }
 #undef FS_MERGE
     return hipGetLastError();

@@ -27,7 +27,7 @@
 // When the query tiles alone would leave the chip idle (decode), a tile's key
 // range is split over workgroups whose partial (max, sum, O) states the
 // readout's merge kernel combines.
-// f32 storage: one wavefront per query, all in fp32.
+// f32 storage: the same tiles on the fp32 matrix product (below).
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 #include "mfma_tile.hpp"
@@ -54,84 +54,6 @@ __global__ void rope_table_kernel(float2* __restrict__ table, int rows, int half
     sincos(ang, &s, &c);
     table[t] = make_float2((float)c, (float)s);
 }
-
-// One wavefront per query row; lanes take 64 keys at a time.
-template <class E, int D>
-__global__ __launch_bounds__(256) void window_attn_rowwise_kernel(
-    const typename E::storage* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
-    const typename E::storage* __restrict__ k, const typename E::storage* __restrict__ v,
-    int64_t kvs0, int64_t kvs1, int64_t kvs2, int H, int nq, int q_pos0, int w,
-    const float2* __restrict__ table, float scale_log2, typename E::storage* __restrict__ o,
-    int64_t os0, int64_t os1, int64_t os2)
-{
-    constexpr int EPL = E::kPer16B;
-    constexpr int R = D / kWave;       // output elements per lane
-    __shared__ float s_q[4][D];
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long row = (long)blockIdx.x * 4 + wv;
-    const long bh = blockIdx.y;
-    const int h = (int)(bh % H), b = (int)(bh / H);
-    const bool active = row < nq;
-    if (active) {
-        const typename E::storage* qrow = q + b * qs0 + h * qs1 + row * qs2;
-        for (int e = lane; e < D; e += kWave) s_q[wv][e] = load1<E>(qrow + e);
-    }
-    __syncthreads();
-    if (!active) return;
-
-    const long i = (long)q_pos0 + row;
-    const long lo = i - w > 0 ? i - w : 0;
-    const typename E::storage* kh = k + b * kvs0 + h * kvs1;
-    const typename E::storage* vh = v + b * kvs0 + h * kvs1;
-    const float* qv = s_q[wv];
-
-    float m = -INFINITY, l = 0.f, acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-
-    for (long j0 = lo; j0 <= i; j0 += kWave) {
-        const long j = j0 + lane;
-        const bool valid = j <= i;
-        float s = -INFINITY;
-        if (valid) {
-            const float2* rot = table + (long)(j - i + w + kTableSlack) * (D / 2);
-            const typename E::storage* kr = kh + j * kvs2;
-            float dot = 0.f;
-            for (int e0 = 0; e0 < D; e0 += EPL) {
-                float x[EPL];
-                load16<E>(kr + e0, x);
-#pragma unroll
-                for (int p = 0; p < EPL / 2; ++p) {
-                    const float2 cs = rot[e0 / 2 + p];
-                    const float kx = x[2 * p] * cs.x - x[2 * p + 1] * cs.y;
-                    const float ky = x[2 * p] * cs.y + x[2 * p + 1] * cs.x;
-                    dot = fmaf(qv[e0 + 2 * p], kx, dot);
-                    dot = fmaf(qv[e0 + 2 * p + 1], ky, dot);
-                }
-            }
-            s = dot * scale_log2;
-        }
-        const float m_new = fmaxf(m, wave_max(s));
-        const float corr = exp2f(m - m_new);
-        const float p = valid ? exp2f(s - m_new) : 0.f;
-        l = l * corr + wave_sum(p);
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] *= corr;
-        const int cnt = (int)((i - j0 + 1) < kWave ? (i - j0 + 1) : kWave);
-        for (int jj = 0; jj < cnt; ++jj) {
-            const float pj = __shfl(p, jj, kWave);
-            const typename E::storage* vr = vh + (j0 + jj) * kvs2;
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = fmaf(pj, load1<E>(vr + lane + r * kWave), acc[r]);
-        }
-        m = m_new;
-    }
-    const float inv_l = 1.f / l;
-    typename E::storage* orow = o + b * os0 + h * os1 + row * os2;
-#pragma unroll
-    for (int r = 0; r < R; ++r) store1<E>(orow + lane + r * kWave, acc[r] * inv_l);
-}
-
 
 namespace {
 
@@ -437,6 +359,271 @@ __global__ __launch_bounds__(256, 2) void window_attn_mfma_kernel(
     }
 }
 
+// ---- fp32 storage on the matrix core ------------------------------------------
+//
+// The same workgroup shape and key tiles as the bf16 kernel, on the fp32
+// product v_mfma_f32_16x16x4f32 (exact fp32 products, fp32 sums), so fp32
+// inputs keep fp32 accuracy and need no operand range care.  The QK^T
+// contraction over d runs as D/4 steps in which lane group g supplies dimension
+// g*D/4 + t: a lane reads its key row's D/4 consecutive floats (16-byte LDS
+// reads) and holds its query's D/4 consecutive rotated floats.  For PV, step j
+// of a 16-key block contracts keys 4g + j, which is register j of the lane's S^T
+// fragment, so P needs no movement; V is read from a row-major LDS tile.  Rows
+// are padded by 16 bytes against LDS bank conflicts.  The softmax sum is kept
+// per lane and reduced over the four lanes of a query at the end.
+
+namespace {
+
+constexpr int kF32Pad = 4;                 // floats of row padding
+
+template <int D>
+struct WinStageF32 {
+    static constexpr int KC = (mf::kTileK * D / 4) / 256;   // 16-byte chunks of K per thread
+    float4 k[KC];
+    float4 v[KC];
+};
+
+template <int D>
+__device__ __forceinline__ void winf_load(WinStageF32<D>& st, const float* __restrict__ kh,
+                                          const float* __restrict__ vh, int64_t kvs2, long kt,
+                                          long kv_hi)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < WinStageF32<D>::KC; ++it) {
+        const int c = tid + 256 * it;
+        const int kr = c / (D / 4), part = c % (D / 4);
+        const long j = kt + kr <= kv_hi ? kt + kr : kv_hi;   // rows past kv_hi repeat it
+        st.k[it] = *reinterpret_cast<const float4*>(kh + j * kvs2 + part * 4);
+        st.v[it] = *reinterpret_cast<const float4*>(vh + j * kvs2 + part * 4);
+    }
+}
+
+// K rotated by R(j - i0) and V, row-major with padded rows, into LDS.
+template <int D>
+__device__ __forceinline__ void winf_store(const WinStageF32<D>& st, float* ks, float* vs, long kt,
+                                           long kv_hi, long i0, int w,
+                                           const float2* __restrict__ table)
+{
+    constexpr int P = D + kF32Pad;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < WinStageF32<D>::KC; ++it) {
+        const int c = tid + 256 * it;
+        const int kr = c / (D / 4), part = c % (D / 4);
+        const long j = kt + kr <= kv_hi ? kt + kr : kv_hi;
+        const float4 cs = *reinterpret_cast<const float4*>(
+            table + (j - i0 + w + kTableSlack) * (D / 2) + part * 2);
+        const float4 x = st.k[it];
+        float4 r;
+        r.x = x.x * cs.x - x.y * cs.y;
+        r.y = x.x * cs.y + x.y * cs.x;
+        r.z = x.z * cs.z - x.w * cs.w;
+        r.w = x.z * cs.w + x.w * cs.z;
+        *reinterpret_cast<float4*>(ks + kr * P + part * 4) = r;
+        *reinterpret_cast<float4*>(vs + kr * P + part * 4) = st.v[it];
+    }
+}
+
+__device__ __forceinline__ mf::f32x4 mfma_f32(float a, float b, mf::f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace
+
+// d128 holds 2 x 32 rotated query floats, 2 x 32 accumulators and a 16 KiB-per-tile
+// register stage per lane, which only fit at one wave per SIMD.
+template <int D>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void window_attn_f32_kernel(
+    const float* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const float* __restrict__ k, const float* __restrict__ v, int64_t kvs0, int64_t kvs1,
+    int64_t kvs2, int H, int BH, int nq, int q_pos0, int w, const float2* __restrict__ table,
+    float scale_log2, float* __restrict__ o, int64_t os0, int64_t os1, int64_t os2,
+    int n_split, float* __restrict__ ws_acc, float2* __restrict__ ws_ml)
+{
+    using namespace mf;
+    constexpr int T = D / 4;       // contraction steps over d; floats per lane and row
+    constexpr int DB = D / 16;     // 16-row blocks of O^T
+    constexpr int P = D + kF32Pad;
+    __shared__ __attribute__((aligned(16))) float ks[kTileK * P];
+    __shared__ __attribute__((aligned(16))) float vs[kTileK * P];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const int split = (int)(tb.tile % n_split);
+    const long i0 = (long)q_pos0 + (tb.tile / n_split) * kWinQ;
+    const long i_end = (long)q_pos0 + nq - 1;
+    const long kv_first = i0 - w > 0 ? i0 - w : 0;
+    const long kv_hi = i0 + kWinQ - 1 < i_end ? i0 + kWinQ - 1 : i_end;
+    const int n_all = (int)((kv_hi - kv_first) / kTileK) + 1;
+    const int t_begin = (int)((long)n_all * split / n_split);
+    const int n_tiles = (int)((long)n_all * (split + 1) / n_split) - t_begin;
+    const long kv_lo = kv_first + (long)t_begin * kTileK;
+
+    const float* kh = k + b * kvs0 + h * kvs1;
+    const float* vh = v + b * kvs0 + h * kvs1;
+    const long qw0 = i0 + 32 * wv;
+    const long qw_last = qw0 + 31 < i_end ? qw0 + 31 : i_end;
+    const bool wave_active = qw0 <= i_end;
+
+    // lane (n, g): dims g*T .. g*T+T-1 of query 16 qg + n, rotated by R(i - i0)
+    float qf[2][T];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const long i = qw0 + 16 * qg + n;
+        const bool ok = i <= i_end;
+        const float* qrow = q + b * qs0 + h * qs1 + (ok ? i - q_pos0 : 0) * qs2 + g * T;
+        const float2* rot = table + (ok ? i - i0 + w + kTableSlack : w + kTableSlack) * (D / 2) +
+                            g * (T / 2);
+#pragma unroll
+        for (int c = 0; c < T / 4; ++c) {
+            const float4 x = ok ? *reinterpret_cast<const float4*>(qrow + 4 * c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 cs = *reinterpret_cast<const float4*>(rot + 2 * c);
+            qf[qg][4 * c + 0] = x.x * cs.x - x.y * cs.y;
+            qf[qg][4 * c + 1] = x.x * cs.y + x.y * cs.x;
+            qf[qg][4 * c + 2] = x.z * cs.z - x.w * cs.w;
+            qf[qg][4 * c + 3] = x.z * cs.w + x.w * cs.z;
+        }
+    }
+
+    f32x4 acc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float l_part[2] = {0.f, 0.f};              // this lane's share of the softmax sums
+    float m_run[2] = {-INFINITY, -INFINITY};
+
+    WinStageF32<D> stage;
+    if (n_tiles > 0) {
+        winf_load<D>(stage, kh, vh, kvs2, kv_lo, kv_hi);
+        winf_store<D>(stage, ks, vs, kv_lo, kv_hi, i0, w, table);
+    }
+    __syncthreads();
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        const long kt = kv_lo + (long)tile * kTileK;
+        if (tile + 1 < n_tiles) winf_load<D>(stage, kh, vh, kvs2, kt + kTileK, kv_hi);
+        const bool work = wave_active && kt <= qw_last && kt + kTileK - 1 >= qw0 - w;
+        if (work) {
+            const bool full = kt >= qw_last - w && kt + kTileK - 1 <= qw0;
+            const int d0 = (int)(qw0 - kt) + n - 4 * g;   // i - j for key 16 kb + 4 g + r
+            f32x4 s[4][2];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const float* krow = ks + (16 * kb + n) * P + g * T;
+#pragma unroll
+                for (int c = 0; c < T / 4; ++c) {
+                    const float4 a = *reinterpret_cast<const float4*>(krow + 4 * c);
+                    s[kb][0] = mfma_f32(a.x, qf[0][4 * c + 0], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.x, qf[1][4 * c + 0], s[kb][1]);
+                    s[kb][0] = mfma_f32(a.y, qf[0][4 * c + 1], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.y, qf[1][4 * c + 1], s[kb][1]);
+                    s[kb][0] = mfma_f32(a.z, qf[0][4 * c + 2], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.z, qf[1][4 * c + 2], s[kb][1]);
+                    s[kb][0] = mfma_f32(a.w, qf[0][4 * c + 3], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.w, qf[1][4 * c + 3], s[kb][1]);
+                }
+            }
+            float corr[2];
+            bool any_rescale = false;
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) {
+                if (!full) {
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int dd = d0 + 16 * (qg - kb) - r;
+                            if (!(dd >= 0 && dd <= w)) s[kb][qg][r] = -INFINITY;
+                        }
+                }
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        tmax = __builtin_elementwise_maximum(tmax, s[kb][qg][r]);
+                tmax = xrow_max(tmax) * scale_log2;
+                const bool raise = tmax > m_run[qg] + kLazy;
+                const float m_new = raise ? tmax : m_run[qg];
+                corr[qg] = raise ? __builtin_amdgcn_exp2f(m_run[qg] - m_new) : 1.f;
+                any_rescale |= raise;
+                m_run[qg] = m_new;
+                const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+                float ls = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s[kb][qg][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qg][r], scale_log2, neg_m));
+                        ls += s[kb][qg][r];
+                    }
+                l_part[qg] = fmaf(l_part[qg], corr[qg], ls);
+            }
+            if (__builtin_expect(__ballot(any_rescale) != 0, 0)) {
+#pragma unroll
+                for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) acc[db][qg] *= corr[qg];
+            }
+            // O^T += V^T P^T: step (kb, j) contracts keys 16 kb + 4 g + j
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float a = vs[(16 * kb + 4 * g + j) * P + 16 * db + n];
+                        acc[db][0] = mfma_f32(a, s[kb][0][j], acc[db][0]);
+                        acc[db][1] = mfma_f32(a, s[kb][1][j], acc[db][1]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (tile + 1 < n_tiles) {
+            winf_store<D>(stage, ks, vs, kt + kTileK, kv_hi, i0, w, table);
+            __syncthreads();
+        }
+    }
+
+    float l[2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) l[qg] = xrow_sum(l_part[qg]);
+    if (n_split > 1) {
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+            const long i = qw0 + 16 * qg + n;
+            if (i > i_end) continue;
+            const long slot = (bh * nq + (i - q_pos0)) * n_split + split;
+            if (g == 0) ws_ml[slot] = make_float2(m_run[qg], l[qg]);
+            float* dst = ws_acc + slot * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) =
+                    make_float4(acc[db][qg][0], acc[db][qg][1], acc[db][qg][2], acc[db][qg][3]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const long i = qw0 + 16 * qg + n;
+        if (i > i_end) continue;
+        const float inv = 1.f / l[qg];
+        float* orow = o + b * os0 + h * os1 + (i - q_pos0) * os2;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float4*>(orow + 16 * db + 4 * g) =
+                make_float4(acc[db][qg][0] * inv, acc[db][qg][1] * inv, acc[db][qg][2] * inv,
+                            acc[db][qg][3] * inv);
+    }
+}
+
 hipError_t launch_rope_table(const Shape& sh, double rope_base, void* table, hipStream_t st)
 {
     const int rows = sh.w + 2 * kTableSlack, half = sh.d / 2;
@@ -447,10 +634,10 @@ hipError_t launch_rope_table(const Shape& sh, double rope_base, void* table, hip
 }
 
 // Splits of each query tile's key range: enough workgroups to give every CU two,
-// at most one per key tile and 16 in all (bf16 storage only).
+// at most one per key tile and 16 in all.
 int window_splits(const Shape& sh)
 {
-    if (!sh.bf16 || sh.nq == 0) return 1;
+    if (sh.nq == 0) return 1;
     const long base = (sh.nq + kWinQ - 1) / kWinQ * (long)sh.B * sh.H;
     if (base >= 512) return 1;
     const long tiles = (sh.w + kWinQ - 1) / mf::kTileK + 1;       // key tiles of a query tile, at most
@@ -482,16 +669,30 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
         if (err != hipSuccess) return err;
     }
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
-    if (sh.bf16) {
-        // split the key range when the workspace holds the partial states
-        const int S = ws_bytes >= window_workspace_bytes(sh) ? window_splits(sh) : 1;
-        char* wsb = static_cast<char*>(table) + ((rope_table_bytes(sh) + 255) & ~(size_t)255);
-        const long rows_all = (long)sh.B * sh.H * sh.nq;
-        float* ws_acc = S > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
-        float2* ws_ml = S > 1 ? reinterpret_cast<float2*>(ws_acc + rows_all * S * sh.d) : nullptr;
-        const long n_tiles = (sh.nq + kWinQ - 1) / kWinQ;
+    // split the key range when the workspace holds the partial states
+    const int S = ws_bytes >= window_workspace_bytes(sh) ? window_splits(sh) : 1;
+    char* wsb = static_cast<char*>(table) + ((rope_table_bytes(sh) + 255) & ~(size_t)255);
+    const long rows_all = (long)sh.B * sh.H * sh.nq;
+    float* ws_acc = S > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+    float2* ws_ml = S > 1 ? reinterpret_cast<float2*>(ws_acc + rows_all * S * sh.d) : nullptr;
+    const long n_tiles = (sh.nq + kWinQ - 1) / kWinQ;
+    dim3 grid((unsigned)(n_tiles * S * sh.B * sh.H)), block(256);
+    if (!sh.bf16) {
+        note_path("window: fp32 MFMA tiles of 128 queries, %d split(s)", S);
+#define FS_WINDOW_F32(D)                                                                         \
+        hipLaunchKernelGGL((window_attn_f32_kernel<D>), grid, block, 0, st, (const float*)q,      \
+                           sh.qs[0], sh.qs[1], sh.qs[2], (const float*)k, (const float*)v,        \
+                           sh.kvs[0], sh.kvs[1], sh.kvs[2], sh.H, sh.B * sh.H, sh.nq, sh.q_pos0,  \
+                           sh.w, (const float2*)table, scale_log2, (float*)o_sr, sh.os[0],        \
+                           sh.os[1], sh.os[2], S, ws_acc, ws_ml)
+        if (sh.d == 64) FS_WINDOW_F32(64); else FS_WINDOW_F32(128);
+#undef FS_WINDOW_F32
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess || S <= 1) return err;
+        return launch_split_merge(sh, S, ws_acc, ws_ml, false, 0.f, o_sr, st);
+    }
+    {
         note_path("window: MFMA tiles of 128 queries, %d split(s)", S);
-        dim3 grid((unsigned)(n_tiles * S * sh.B * sh.H)), block(256);
 #define FS_WINDOW_MFMA(D)                                                                        \
         hipLaunchKernelGGL((window_attn_mfma_kernel<D>), grid, block, 0, st, (const uint16_t*)q,  \
                            sh.qs[0], sh.qs[1], sh.qs[2], (const uint16_t*)k, (const uint16_t*)v,  \
@@ -505,18 +706,6 @@ hipError_t launch_window(const Shape& sh, const void* q, const void* k, const vo
         if (err != hipSuccess || S <= 1) return err;
         return launch_split_merge(sh, S, ws_acc, ws_ml, false, 0.f, o_sr, st);
     }
-    note_path("window: row-wise, one wavefront per query (fp32 storage)");
-    dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
-#define FS_WINDOW(E, D)                                                                          \
-    hipLaunchKernelGGL((window_attn_rowwise_kernel<E, D>), grid, block, 0, st,                   \
-                       (const typename E::storage*)q, sh.qs[0], sh.qs[1], sh.qs[2],              \
-                       (const typename E::storage*)k, (const typename E::storage*)v, sh.kvs[0],  \
-                       sh.kvs[1], sh.kvs[2], sh.H, sh.nq, sh.q_pos0, sh.w,                       \
-                       (const float2*)table, scale_log2, (typename E::storage*)o_sr, sh.os[0],   \
-                       sh.os[1], sh.os[2])
-    if (sh.d == 64) FS_WINDOW(F32, 64); else FS_WINDOW(F32, 128);
-#undef FS_WINDOW
-    return hipGetLastError();
 }
 
 }  // namespace fs

@@ -846,9 +846,10 @@ def test_window_extreme_magnitudes(d, scale_k, scale_q):
 
 
 def test_last_path_reports_fallbacks():
-    """fs_last_path names the kernel each call took: MFMA for bf16 shapes, and
-    the row-wise fallback with its reason for fp32 storage or a candidate union
-    wider than the MFMA selection's 528 slots."""
+    """fs_last_path names the kernel each call took: MFMA for bf16 shapes, the
+    fp32 matrix-core window for fp32 storage, and the row-wise fallback with its
+    reason for fp32 storage (selection, readout) or a candidate union wider than
+    the MFMA selection's 528 slots."""
     from long_context_fs_amd import fs as fsb
     cases = [("f32_d64_noprune", "fp32 storage", "fp32 storage"),
              ("bf16_d64_wide_keep_k64", "wider than 528", None),
@@ -868,6 +869,10 @@ def test_last_path_reports_fallbacks():
         assert ("row-wise" in path) == (sel_reason is not None), path
         if sel_reason:
             assert sel_reason in path, path
+        fsb.fs_window_attn(fwd.prob, q, k, v, wl.rope_base, fwd.ws, fwd.o_sr)
+        path = fsb.last_path()            # both storage types run the window on the matrix core
+        assert path.startswith("window: ") and "MFMA" in path, path
+        assert ("fp32" in path) == (wl.dtype == "f32"), path
         fsb.fs_sparse_attn(fwd.prob, q, k, v, fwd.idx, wl.topk, wl.rms_eps, fwd.o_lr,
                            fwd.ws_sparse)
         path = fsb.last_path()
