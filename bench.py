@@ -136,7 +136,8 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
         fs.fs_cell_summaries(p, k, fwd.kbar, fwd.amax)
         mark(1)
         if fwd.pruned:
-            fs.fs_prune_prefix(p, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep, fwd.keep_count)
+            fs.fs_prune_prefix(p, fwd.amax, fwd.n_recent, fwd.budget, fwd.keep, fwd.keep_count,
+                               workspace=fwd.ws_prune)
         mark(2)
         fs.fs_select_topk(p, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, fwd.topk,
                           fwd.idx, None, None, fwd.prior, fwd.ws_select)
@@ -522,7 +523,7 @@ def run_phase(name, phase, reps, torch, fs):
         "fsb_all": lambda: (fb.build(), fb.search(q)),
         "summaries": lambda: fs.fs_cell_summaries(p, k, f.kbar, f.amax),
         "prune": lambda: fs.fs_prune_prefix(p, f.amax, f.n_recent, f.budget, f.keep,
-                                            f.keep_count),
+                                            f.keep_count, workspace=f.ws_prune),
         "select": lambda: fs.fs_select_topk(p, q, f.kbar, f.keep, f.keep_count, f.keep_w,
                                             f.topk, f.idx, None, None, f.prior, f.ws_select),
         "rerank": lambda: fs.fs_rerank_topk(p, q, k, f.keep, f.keep_count, f.keep_w, f.topk,

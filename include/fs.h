@@ -8,6 +8,7 @@
  *
  *   fs_cell_summaries  eq. 5   mean key and maximum token-key norm per cell
  *   fs_prune_prefix    eq. 8   FS-L query-independent pruning to W + P cells
+ *                               (+ fs_prune_workspace_size)
  *   fs_select_topk     eq. 7   score q.kbar/sqrt(d) (+ optional erf prior), top-K cells
  *   fs_window_attn     eqs.3-4 RoPE attention over positions max(0,i-w) .. i
  *   fs_sparse_attn     eq. 9   NoPE attention over the selected cells' tokens, RMSNorm
@@ -91,9 +92,18 @@ fs_status fs_prune_rows(const fs_problem* problem, int32_t* n_lo, int32_t* n_row
  *   keep[b][h][r][cnt ..]     = -1,       keep_count[b][h][r] = cnt <= W + P.
  * TopP orders by (amax, c) descending.  keep: int32 [B][H][n_rows][n_recent+budget];
  * keep_count: int32 [B][H][n_rows].  n_recent >= 0, budget >= 0,
- * 1 <= n_recent + budget <= 4096. */
+ * 1 <= n_recent + budget <= 4096.  workspace (nullable, device, overwritten):
+ * with at least fs_prune_workspace_size bytes, a call with many rows (a prefill)
+ * finds each cell's eviction point once (the row count n from which P cells of
+ * the prefix beat it) instead of searching every row; the rows are identical.
+ * Calls sharing a workspace must not overlap in time. */
 fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t n_recent,
-                          int32_t budget, int32_t* keep, int32_t* keep_count, void* stream);
+                          int32_t budget, int32_t* keep, int32_t* keep_count, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* Bytes of the workspace fs_prune_prefix can use: one int32 per (b, h) and cell
+ * below the largest candidate count the query block spans. */
+fs_status fs_prune_workspace_size(const fs_problem* problem, size_t* bytes);
 
 /* Scoring and top-K, eq. 7.  For each query i the score of cell c is
  * r_ic = q_i . kbar_c / sqrt(d) + lambda_h a_c erf((i - p_c) / (2 sigma_h)) with

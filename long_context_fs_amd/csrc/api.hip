@@ -161,8 +161,19 @@ fs_status fs_prune_rows(const fs_problem* problem, int32_t* n_lo, int32_t* n_row
     return FS_OK;
 }
 
+fs_status fs_prune_workspace_size(const fs_problem* problem, size_t* bytes)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    if (!bytes) return fail(FS_ERR_INVALID, "bytes is NULL");
+    *bytes = fs::prune_ws_bytes(sh);
+    g_err[0] = 0;
+    return FS_OK;
+}
+
 fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t n_recent,
-                          int32_t budget, int32_t* keep, int32_t* keep_count, void* stream)
+                          int32_t budget, int32_t* keep, int32_t* keep_count, void* workspace,
+                          size_t ws_bytes, void* stream)
 {
     fs::Shape sh;
     FS_CHECK(check_problem(problem, &sh));
@@ -170,10 +181,15 @@ fs_status fs_prune_prefix(const fs_problem* problem, const float* amax, int32_t 
         return fail(FS_ERR_UNSUPPORTED, "n_recent %d + budget %d must be in [1, 4096]", n_recent,
                     budget);
     if (!amax || !keep || !keep_count) return fail(FS_ERR_INVALID, "NULL amax/keep/keep_count");
+    if (workspace && ws_bytes < fs::prune_ws_bytes(sh))
+        return fail(FS_ERR_INVALID, "workspace of %zu bytes, need %zu", ws_bytes,
+                    fs::prune_ws_bytes(sh));
+    if (workspace && ((uintptr_t)workspace & 15))
+        return fail(FS_ERR_INVALID, "workspace is not 16-byte aligned");
     int lo, rows;
     fs::candidate_rows(sh, &lo, &rows);
     return from_hip(fs::launch_prune(sh, amax, lo, rows, n_recent, budget, keep, keep_count,
-                                     (hipStream_t)stream),
+                                     (hipStream_t)stream, workspace, ws_bytes),
                     "fs_prune_prefix");
 }
 

@@ -24,8 +24,12 @@ void candidate_rows(const Shape& sh, int* n_lo, int* n_rows);
 
 hipError_t launch_summaries(const Shape& sh, const void* k, float* kbar, float* amax,
                             hipStream_t st);
+// ws (nullable, prune_ws_bytes): lets a call with many rows take each cell's
+// eviction point once instead of a search per row.
+size_t prune_ws_bytes(const Shape& sh);
 hipError_t launch_prune(const Shape& sh, const float* amax, int n_lo, int n_rows, int n_recent,
-                        int budget, int32_t* keep, int32_t* keep_count, hipStream_t st);
+                        int budget, int32_t* keep, int32_t* keep_count, hipStream_t st,
+                        void* ws = nullptr, size_t ws_bytes = 0);
 // Position prior of eq. 7, lambda_h a_c erf((i - p_c) / (2 sigma_h)): device
 // arrays amax [B][H][C], lambda [H], sigma [H]; lambda == nullptr switches it off.
 struct Prior {

@@ -15,6 +15,16 @@
 // reach the candidate, and the output positions come from one round of per-wave
 // ballot counts.  Longer rows use the streaming
 // kernel below it.
+//
+// Many rows (a prefill), given a workspace: row membership has a closed form.
+// Cell c is beaten by c' when (a_c', c') > (a_c, c); with E(c) the index of
+// the P-th cell beating c (cells in index order; none: never), c is in
+// TopP({c' < n}) exactly when c < n <= E(c), since the prefix [0, n) then holds
+// fewer than P of its beaters.  One kernel finds E for every cell (a scan of
+// the prefix per cell, in LDS chunks), then one workgroup per row compacts
+// {c < n : n <= E(c)} U Recent_W with ballots: no per-row search.
+#include <climits>
+
 #include "fs_device.hpp"
 #include "fs_launch.hpp"
 
@@ -270,13 +280,132 @@ __global__ __launch_bounds__(kPruneThreads) void prune_reg_kernel(
     if (tid == 0) keep_count[bh * n_rows + r] = written;
 }
 
+// E(c) for the cells c < n_max of each (b, h): the index of the budget-th cell
+// beating c in index order, or INT_MAX.  A workgroup stages the head's keys in
+// LDS and its waves take kEvictCells cells each: a wave walks the prefix 64
+// cells at a time (lane l takes cell r0 + l), counts that round's beaters with a
+// ballot, and in the round where the running count reaches `budget` picks the
+// beater of the remaining rank from the ballot mask.
+constexpr int kEvictCells = 4;                  // cells per wave
+constexpr int kEvictMaxCells = 8192;
+
+__global__ __launch_bounds__(kPruneThreads) void prune_evict_kernel(
+    const float* __restrict__ amax, int C, int n_max, int budget, int32_t* __restrict__ evict)
+{
+    __shared__ uint32_t kbuf[kEvictMaxCells];
+    const long bh = blockIdx.y;
+    const uint32_t* key = reinterpret_cast<const uint32_t*>(amax + bh * C);
+    for (int t = threadIdx.x; t < n_max; t += kPruneThreads) kbuf[t] = key[t];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c0 = (blockIdx.x * kPruneWaves + wv) * kEvictCells;
+    for (int ci = 0; ci < kEvictCells; ++ci) {
+        const int c = c0 + ci;                           // wave-uniform
+        if (c >= n_max) break;
+        const uint32_t kc = kbuf[c];
+        int total = 0, e = INT_MAX;
+        for (int r0 = 0; r0 < n_max; r0 += kWave) {
+            const int cp = r0 + lane;
+            bool beat = false;
+            if (cp < n_max) {
+                const uint32_t kp = kbuf[cp];
+                beat = kp > kc || (kp == kc && cp > c);
+            }
+            uint64_t m = __ballot(beat);
+            const int cnt = __popcll(m);
+            if (total + cnt >= budget) {                 // wave-uniform
+                for (int k = budget - total; k > 1; --k) m &= m - 1;   // drop lower beaters
+                e = r0 + __ffsll((long long)m) - 1;
+                break;
+            }
+            total += cnt;
+        }
+        if (lane == 0) evict[bh * n_max + c] = e;
+    }
+}
+
+// Row n = n_lo + blockIdx.x from E: {c < n : n <= E(c)} U {n - n_recent <= c < n},
+// ascending, by per-wave ballots (cell 256 j + t in slot j of thread t).
+template <int KPT>
+__global__ __launch_bounds__(kPruneThreads) void prune_rows_kernel(
+    const int32_t* __restrict__ evict, int n_max, int n_lo, int n_rows, int n_recent, int keep_w,
+    int32_t* __restrict__ keep, int32_t* __restrict__ keep_count)
+{
+    __shared__ int cnt[KPT][kPruneWaves];
+    const int r = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int n = n_lo + r;
+    const int32_t* E = evict + bh * n_max;
+    int32_t* out = keep + (bh * n_rows + r) * (long)keep_w;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint32_t kept_bits = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int c = 256 * j + tid;
+        const bool kept = c < n && (n <= E[c] || c >= n - n_recent);
+        kept_bits |= (uint32_t)kept << j;
+        const uint64_t km = __ballot(kept);
+        if (lane == 0) cnt[j][wv] = __popcll(km);
+    }
+    __syncthreads();
+    int written = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const bool kept = (kept_bits >> j) & 1u;
+        const uint64_t km = __ballot(kept);
+        int pos = written + lanes_below(km);
+#pragma unroll
+        for (int i = 0; i < kPruneWaves; ++i) {
+            pos += i < wv ? cnt[j][i] : 0;
+            written += cnt[j][i];
+        }
+        if (kept) out[pos] = 256 * j + tid;
+    }
+    for (int t = written + tid; t < keep_w; t += kPruneThreads) out[t] = -1;
+    if (tid == 0) keep_count[bh * n_rows + r] = written;
+}
+
+// Workspace of the many-row path: E per cell below the largest candidate count.
+size_t prune_ws_bytes(const Shape& sh)
+{
+    int n_lo, n_rows;
+    candidate_rows(sh, &n_lo, &n_rows);
+    const long n_max = n_rows > 0 ? n_lo + n_rows - 1 : 0;
+    return (size_t)sh.B * sh.H * n_max * sizeof(int32_t);
+}
+
+// The closed form pays one scan of the prefix per cell; the per-row search pays
+// a bitwise search per row.  With rows at least a sixteenth of the cells the
+// scan is the cheaper.
+static bool prune_by_evict(int n_rows, int n_max)
+{
+    return n_rows >= 64 && 16L * n_rows >= n_max && n_max <= kEvictMaxCells;
+}
+
 hipError_t launch_prune(const Shape& sh, const float* amax, int n_lo, int n_rows, int n_recent,
-                        int budget, int32_t* keep, int32_t* keep_count, hipStream_t st)
+                        int budget, int32_t* keep, int32_t* keep_count, hipStream_t st, void* ws,
+                        size_t ws_bytes)
 {
     if (n_rows == 0) return hipSuccess;
     dim3 grid((unsigned)n_rows, (unsigned)(sh.B * sh.H)), block(kPruneThreads);
     const int n_max = n_lo + n_rows - 1;
     const int kpt = (n_max + kPruneThreads - 1) / kPruneThreads;
+    if (ws && ws_bytes >= prune_ws_bytes(sh) && budget > 0 && prune_by_evict(n_rows, n_max)) {
+        int32_t* evict = static_cast<int32_t*>(ws);
+        constexpr int per_block = kPruneWaves * kEvictCells;
+        dim3 egrid((unsigned)((n_max + per_block - 1) / per_block), (unsigned)(sh.B * sh.H));
+        hipLaunchKernelGGL(prune_evict_kernel, egrid, block, 0, st, amax, sh.C, n_max, budget,
+                           evict);
+#define FS_PRUNE_ROWS(K)                                                                        \
+        hipLaunchKernelGGL((prune_rows_kernel<K>), grid, block, 0, st, evict, n_max, n_lo,      \
+                           n_rows, n_recent, n_recent + budget, keep, keep_count)
+        if (kpt <= 4) FS_PRUNE_ROWS(4);
+        else if (kpt <= 8) FS_PRUNE_ROWS(8);
+        else if (kpt <= 16) FS_PRUNE_ROWS(16);
+        else FS_PRUNE_ROWS(32);
+#undef FS_PRUNE_ROWS
+        return hipGetLastError();
+    }
 #define FS_PRUNE_REG(K)                                                                         \
     hipLaunchKernelGGL((prune_reg_kernel<K>), grid, block, 0, st, amax, sh.C, n_lo, n_rows,     \
                        n_recent, budget, n_recent + budget, keep, keep_count)

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfs.so")
 FS_F32, FS_BF16 = 0, 1
 CELL = 32
 
-SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_select_topk",
+SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_prune_workspace_size",
+           "fs_select_topk",
            "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
            "fs_sparse_attn_noalloc", "fs_sparse_attn_combine", "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size",
            "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
@@ -64,7 +65,8 @@ def load(path: str | None = None):
     sig = {
         "fs_cell_summaries": [P, vp, vp, vp, vp],
         "fs_prune_rows": [P, C.POINTER(i32), C.POINTER(i32)],
-        "fs_prune_prefix": [P, vp, i32, i32, vp, vp, vp],
+        "fs_prune_prefix": [P, vp, i32, i32, vp, vp, vp, C.c_size_t, vp],
+        "fs_prune_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_select_topk": [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, C.c_size_t,
                            vp],
         "fs_select_workspace_size": [P, i32, i32, C.POINTER(C.c_size_t)],
@@ -154,9 +156,19 @@ def fs_prune_rows(prob):
     return lo.value, rows.value
 
 
-def fs_prune_prefix(prob, amax, n_recent, budget, keep, keep_count, stream=None):
+def fs_prune_workspace_size(prob) -> int:
+    n = C.c_size_t()
+    _check("fs_prune_workspace_size", load().fs_prune_workspace_size(C.byref(prob), C.byref(n)))
+    return n.value
+
+
+def fs_prune_prefix(prob, amax, n_recent, budget, keep, keep_count, stream=None, workspace=None):
+    """workspace: None, or a device buffer of >= fs_prune_workspace_size bytes."""
+    ws, nbytes = (None, 0) if workspace is None else \
+        (_p(workspace), workspace.numel() * workspace.element_size())
     _check("fs_prune_prefix", load().fs_prune_prefix(C.byref(prob), _p(amax), n_recent, budget,
-                                                     _p(keep), _p(keep_count), _s(stream)))
+                                                     _p(keep), _p(keep_count), ws, nbytes,
+                                                     _s(stream)))
 
 
 def fs_select_topk(prob, q, kbar, keep, keep_count, keep_width, topk, idx, score=None,
@@ -315,6 +327,8 @@ class FsForward:
         self.idx = torch.empty((B, H, n_q, topk), dtype=i32, device=device)
         self.score = torch.empty((B, H, n_q, topk), dtype=f32, device=device)
         self.ws = torch.empty(fs_workspace_size(self.prob), dtype=torch.uint8, device=device)
+        npr = fs_prune_workspace_size(self.prob) if self.pruned else 0
+        self.ws_prune = torch.empty(npr, dtype=torch.uint8, device=device) if npr else None
         nsp = fs_sparse_workspace_size(self.prob)
         self.ws_sparse = torch.empty(nsp, dtype=torch.uint8, device=device) if nsp else None
         nsel = fs_select_workspace_size(self.prob, self.keep_w, topk)
@@ -337,7 +351,7 @@ class FsForward:
         fs_cell_summaries(p, k, self.kbar, self.amax, stream)
         if self.pruned:
             fs_prune_prefix(p, self.amax, self.n_recent, self.budget, self.keep, self.keep_count,
-                            stream)
+                            stream, self.ws_prune)
         fs_select_topk(p, q, self.kbar, self.keep, self.keep_count, self.keep_w, self.topk,
                        self.idx, self.score if keep_score else None, stream, self.prior,
                        self.ws_select)

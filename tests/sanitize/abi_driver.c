@@ -82,7 +82,10 @@ int main(void)
            FS_ERR_INVALID, "prior without sigma");
     expect(fs_rerank_topk(&good, x, x, NULL, NULL, NULL, ix, NULL, 8, 8, ix, NULL, NULL, 0, NULL),
            FS_ERR_INVALID, "keep without keep_count");
-    expect(fs_prune_prefix(&good, fx, 0, 0, ix, ix, NULL), FS_ERR_UNSUPPORTED, "budget 0");
+    expect(fs_prune_prefix(&good, fx, 0, 0, ix, ix, NULL, 0, NULL), FS_ERR_UNSUPPORTED, "budget 0");
+    expect(fs_prune_prefix(&good, fx, 0, 8, ix, ix, x, 4, NULL), FS_ERR_INVALID,
+           "small prune workspace");
+    expect(fs_prune_workspace_size(&good, NULL), FS_ERR_INVALID, "prune ws NULL");
     expect(fs_sparse_attn(&good, (char*)x + 4, x, x, ix, 8, 1e-6f, NULL, 0, x, NULL),
            FS_ERR_INVALID, "misaligned q");
     expect(fs_sparse_attn(&good, x, x, x, ix, 8, -1.f, NULL, 0, x, NULL), FS_ERR_INVALID, "eps");

@@ -110,9 +110,14 @@ def test_bad_strides_and_pointers_rejected(lib):
 
 def test_call_specific_limits(lib):
     p = _prob()
-    assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 0, FAKE, FAKE, None) == 2
-    assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 5000, FAKE, FAKE, None) == 2
-    assert lib.fs_prune_prefix(C.byref(p), FAKE, -1, 4, FAKE, FAKE, None) == 2
+    assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 0, FAKE, FAKE, None, 0, None) == 2
+    assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 5000, FAKE, FAKE, None, 0, None) == 2
+    assert lib.fs_prune_prefix(C.byref(p), FAKE, -1, 4, FAKE, FAKE, None, 0, None) == 2
+    # an undersized prune workspace is an error; the size is one int32 per (b, h) and cell
+    # below the largest candidate count (4096 tokens, w 512: 111 cells, 2 heads)
+    assert fs.fs_prune_workspace_size(p) == 2 * 111 * 4
+    assert lib.fs_prune_prefix(C.byref(p), FAKE, 0, 8, FAKE, FAKE, FAKE, 16, None) == 1
+    assert b"workspace" in lib.fs_last_error()
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 0, FAKE,
                               None, None, 0, None) == 2
     assert lib.fs_select_topk(C.byref(p), FAKE, FAKE, None, None, None, None, None, 0, 65, FAKE,

@@ -564,6 +564,49 @@ def test_empty_query_range_writes_nothing(dtype):
         assert (t.float().cpu() == 7).all()
 
 
+@pytest.mark.parametrize("n_ctx,heads,budget,n_recent,levels", [
+    (65536, 2, 256, 0, 0), (65536, 1, 256, 5, 7), (20000, 3, 7, 0, 3), (20000, 2, 600, 2, 0),
+    (9000, 2, 1, 0, 2), (4096, 2, 64, 30, 1), (33000, 1, 100, 0, 2)])
+def test_prune_workspace_rows_equal_search_rows(n_ctx, heads, budget, n_recent, levels):
+    """fs_prune_prefix with its workspace (each cell's eviction point, then one
+    compaction per row) writes the same rows and counts, bit for bit, as without
+    it (a bitwise search per row), and both equal the oracle's eq. 8 rows on a
+    sample.  levels > 0 quantises a_c to that many values, so ties at the
+    threshold are common (the larger index wins)."""
+    from long_context_fs_amd import fs as fsb
+    gen = np.random.default_rng(n_ctx + budget)
+    C_ = n_ctx // 32
+    am = (8.0 + 2.0 * gen.random((1, heads, C_))).astype(np.float32)
+    if levels:
+        am = (8.0 + np.floor(gen.random((1, heads, C_)) * levels)).astype(np.float32)
+    p = fsb.problem(1, heads, 64, n_ctx, n_ctx, 0, 512, fsb.FS_BF16)
+    n_lo, n_rows = fsb.fs_prune_rows(p)
+    amax = torch.from_numpy(am).cuda()
+    out = []
+    for use_ws in (False, True):
+        keep = torch.full((1, heads, n_rows, n_recent + budget), -7, dtype=torch.int32,
+                          device="cuda")
+        cnt = torch.full((1, heads, n_rows), -7, dtype=torch.int32, device="cuda")
+        ws = None
+        if use_ws:
+            ws = torch.full((fsb.fs_prune_workspace_size(p) // 4,), -5, dtype=torch.int32,
+                            device="cuda")
+        fsb.fs_prune_prefix(p, amax, n_recent, budget, keep, cnt, workspace=ws)
+        torch.cuda.synchronize()
+        out.append((keep.cpu().numpy(), cnt.cpu().numpy()))
+    np.testing.assert_array_equal(out[0][0], out[1][0])
+    np.testing.assert_array_equal(out[0][1], out[1][1])
+    wl = synth.Workload(name="prune", batch=1, heads=heads, n_ctx=n_ctx, head_dim=64,
+                        dtype="bf16", n_q=n_ctx, q_pos0=0, topk=8, budget=budget,
+                        n_recent=n_recent)
+    pr = oracle.problem_from(wl)
+    for h in range(heads):
+        for r in gen.choice(n_rows, min(n_rows, 40), replace=False):
+            want, _ = orc().prune_row(pr, am[0, h].astype(np.float64), n_lo + int(r))
+            c = out[1][1][0, h, r]
+            assert np.array_equal(out[1][0][0, h, r, :c], np.sort(want)), (h, r)
+
+
 @pytest.mark.parametrize("name", ["bf16_d128_decode_wide", "bf16_d64_decode_noprune",
                                   "bf16_d128_decode_prior"])
 def test_split_selection_equals_unsplit(name):
