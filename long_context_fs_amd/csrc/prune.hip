@@ -324,45 +324,59 @@ __global__ __launch_bounds__(kPruneThreads) void prune_evict_kernel(
     }
 }
 
-// Row n = n_lo + blockIdx.x from E: {c < n : n <= E(c)} U {n - n_recent <= c < n},
-// ascending, by per-wave ballots (cell 256 j + t in slot j of thread t).
+// Rows n = n_lo + r for kRowsPerBlock consecutive r from E: {c < n : n <= E(c)}
+// U {n - n_recent <= c < n}, ascending, by per-wave ballots (cell 256 j + t in
+// slot j of thread t; E read once for the block's rows).
+constexpr int kRowsPerBlock = 8;
+
 template <int KPT>
 __global__ __launch_bounds__(kPruneThreads) void prune_rows_kernel(
     const int32_t* __restrict__ evict, int n_max, int n_lo, int n_rows, int n_recent, int keep_w,
     int32_t* __restrict__ keep, int32_t* __restrict__ keep_count)
 {
     __shared__ int cnt[KPT][kPruneWaves];
-    const int r = blockIdx.x;
     const long bh = blockIdx.y;
-    const int n = n_lo + r;
     const int32_t* E = evict + bh * n_max;
-    int32_t* out = keep + (bh * n_rows + r) * (long)keep_w;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    uint32_t kept_bits = 0u;
+    const int r0 = blockIdx.x * kRowsPerBlock;
+    int ev[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int c = 256 * j + tid;
-        const bool kept = c < n && (n <= E[c] || c >= n - n_recent);
-        kept_bits |= (uint32_t)kept << j;
-        const uint64_t km = __ballot(kept);
-        if (lane == 0) cnt[j][wv] = __popcll(km);
+        ev[j] = c < n_max ? E[c] : 0;
     }
-    __syncthreads();
-    int written = 0;
+    for (int rr = 0; rr < kRowsPerBlock; ++rr) {
+        const int r = r0 + rr;
+        if (r >= n_rows) break;                          // block-uniform
+        const int n = n_lo + r;
+        int32_t* out = keep + (bh * n_rows + r) * (long)keep_w;
+        uint32_t kept_bits = 0u;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const bool kept = (kept_bits >> j) & 1u;
-        const uint64_t km = __ballot(kept);
-        int pos = written + lanes_below(km);
-#pragma unroll
-        for (int i = 0; i < kPruneWaves; ++i) {
-            pos += i < wv ? cnt[j][i] : 0;
-            written += cnt[j][i];
+        for (int j = 0; j < KPT; ++j) {
+            const int c = 256 * j + tid;
+            const bool kept = c < n && (n <= ev[j] || c >= n - n_recent);
+            kept_bits |= (uint32_t)kept << j;
+            const uint64_t km = __ballot(kept);
+            if (lane == 0) cnt[j][wv] = __popcll(km);
         }
-        if (kept) out[pos] = 256 * j + tid;
+        __syncthreads();
+        int written = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool kept = (kept_bits >> j) & 1u;
+            const uint64_t km = __ballot(kept);
+            int pos = written + lanes_below(km);
+#pragma unroll
+            for (int i = 0; i < kPruneWaves; ++i) {
+                pos += i < wv ? cnt[j][i] : 0;
+                written += cnt[j][i];
+            }
+            if (kept) out[pos] = 256 * j + tid;
+        }
+        for (int t = written + tid; t < keep_w; t += kPruneThreads) out[t] = -1;
+        if (tid == 0) keep_count[bh * n_rows + r] = written;
+        __syncthreads();                                 // cnt is rewritten by the next row
     }
-    for (int t = written + tid; t < keep_w; t += kPruneThreads) out[t] = -1;
-    if (tid == 0) keep_count[bh * n_rows + r] = written;
 }
 
 // Workspace of the many-row path: E per cell below the largest candidate count.
@@ -396,8 +410,9 @@ hipError_t launch_prune(const Shape& sh, const float* amax, int n_lo, int n_rows
         dim3 egrid((unsigned)((n_max + per_block - 1) / per_block), (unsigned)(sh.B * sh.H));
         hipLaunchKernelGGL(prune_evict_kernel, egrid, block, 0, st, amax, sh.C, n_max, budget,
                            evict);
+        dim3 rgrid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)(sh.B * sh.H));
 #define FS_PRUNE_ROWS(K)                                                                        \
-        hipLaunchKernelGGL((prune_rows_kernel<K>), grid, block, 0, st, evict, n_max, n_lo,      \
+        hipLaunchKernelGGL((prune_rows_kernel<K>), rgrid, block, 0, st, evict, n_max, n_lo,     \
                            n_rows, n_recent, n_recent + budget, keep, keep_count)
         if (kpt <= 4) FS_PRUNE_ROWS(4);
         else if (kpt <= 8) FS_PRUNE_ROWS(8);
