@@ -166,7 +166,10 @@ struct SpLayout {
     size_t off_vt, off_bitmap, off_rank, off_ulist, off_qbits, bytes;
 };
 
-template <int D>
+// F32: fp32 K and V tiles, row-major with rows padded by kSpF32Pad floats.
+constexpr int kSpF32Pad = 4;
+
+template <int D, bool F32 = false>
 __host__ __device__ inline SpLayout sp_layout(int C, int topk)
 {
     SpLayout L;
@@ -174,9 +177,10 @@ __host__ __device__ inline SpLayout sp_layout(int C, int topk)
     L.u_cap = C < kSpQ * topk ? C : kSpQ * topk;
     L.qpitch = ((L.u_cap + 31) / 32) | 1;
     auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
-    size_t off = (size_t)mf::kTileK * D * 2;          // swizzled K tile
+    const size_t tile = F32 ? (size_t)mf::kTileK * (D + kSpF32Pad) * 4 : (size_t)mf::kTileK * D * 2;
+    size_t off = tile;                                   // K tile (swizzled bf16, or fp32 rows)
     L.off_vt = off;
-    off = up16(off + (size_t)D * mf::kTileK * 2);        // swizzled V^T tile
+    off = up16(off + tile);                              // V^T tile (bf16), or V rows (fp32)
     L.off_bitmap = off;
     off = up16(off + (size_t)L.nwords * 4);
     L.off_rank = off;
@@ -210,6 +214,60 @@ __device__ __forceinline__ int block_excl_scan(int x, int* red, int* total)
     __syncthreads();
     *total = all;
     return before + inc - x;
+}
+
+// The union of the cells the tile's queries selected: bitmap over the cells,
+// per-word ranks, the slot -> cell list, and per query a bitmap over the union
+// slots it selected.  Returns the union's size (block-uniform); ends with a
+// barrier.
+__device__ __forceinline__ int sp_union(const SpLayout& L, uint32_t* bitmap, uint16_t* rank,
+                                        uint16_t* ulist, uint32_t* qbits,
+                                        const int32_t* __restrict__ idx_blk, int n_rows, int topk,
+                                        int C, int* red)
+{
+    const int tid = threadIdx.x;
+    for (int wd = tid; wd < L.nwords; wd += 256) bitmap[wd] = 0u;
+    for (int e = tid; e < kSpQ * L.qpitch; e += 256) qbits[e] = 0u;
+    __syncthreads();
+    for (int e = tid; e < n_rows * topk; e += 256) {
+        const int c = idx_blk[e];
+        if (c >= 0 && c < C) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    int cnt[4], mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int wd = 4 * tid + j;
+        cnt[j] = wd < L.nwords ? __popc(bitmap[wd]) : 0;
+        mine += cnt[j];
+    }
+    int n_union;
+    int run = block_excl_scan(mine, red, &n_union);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int wd = 4 * tid + j;
+        if (wd < L.nwords) rank[wd] = (uint16_t)run;
+        run += cnt[j];
+    }
+    __syncthreads();
+    for (int wd = tid; wd < L.nwords; wd += 256) {
+        uint32_t bits = bitmap[wd];
+        int r = rank[wd];
+        while (bits) {
+            const int bpos = __ffs(bits) - 1;
+            ulist[r++] = (uint16_t)(32 * wd + bpos);
+            bits &= bits - 1;
+        }
+    }
+    for (int e = tid; e < n_rows * topk; e += 256) {
+        const int c = idx_blk[e];
+        if (c >= 0 && c < C) {
+            const int sl = rank[c >> 5] + __popc(bitmap[c >> 5] & ((1u << (c & 31)) - 1u));
+            atomicOr(&qbits[(e / topk) * L.qpitch + (sl >> 5)], 1u << (sl & 31));
+        }
+    }
+    __syncthreads();
+    return n_union;
 }
 
 // Register stage of one 64-key tile (two cells): KC 16-byte chunks of K rows
@@ -417,47 +475,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     const int32_t* idx_blk = idx + (bh * nq + t0) * (long)topk;
 
     // ---- union of the selected cells, and each query's selection over it ----
-    for (int wd = tid; wd < L.nwords; wd += 256) bitmap[wd] = 0u;
-    for (int e = tid; e < kSpQ * L.qpitch; e += 256) qbits[e] = 0u;
-    __syncthreads();
-    for (int e = tid; e < n_rows * topk; e += 256) {
-        const int c = idx_blk[e];
-        if (c >= 0 && c < C) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
-    }
-    __syncthreads();
-    int cnt[4], mine = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int wd = 4 * tid + j;
-        cnt[j] = wd < L.nwords ? __popc(bitmap[wd]) : 0;
-        mine += cnt[j];
-    }
-    int n_union;
-    int run = block_excl_scan(mine, red, &n_union);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int wd = 4 * tid + j;
-        if (wd < L.nwords) rank[wd] = (uint16_t)run;
-        run += cnt[j];
-    }
-    __syncthreads();
-    for (int wd = tid; wd < L.nwords; wd += 256) {
-        uint32_t bits = bitmap[wd];
-        int r = rank[wd];
-        while (bits) {
-            const int bpos = __ffs(bits) - 1;
-            ulist[r++] = (uint16_t)(32 * wd + bpos);
-            bits &= bits - 1;
-        }
-    }
-    for (int e = tid; e < n_rows * topk; e += 256) {
-        const int c = idx_blk[e];
-        if (c >= 0 && c < C) {
-            const int sl = rank[c >> 5] + __popc(bitmap[c >> 5] & ((1u << (c & 31)) - 1u));
-            atomicOr(&qbits[(e / topk) * L.qpitch + (sl >> 5)], 1u << (sl & 31));
-        }
-    }
-    __syncthreads();
+    const int n_union = sp_union(L, bitmap, rank, ulist, qbits, idx_blk, n_rows, topk, C, red);
 
     // ---- queries of this wave as B operands -------------------------------
     const char* kh = reinterpret_cast<const char*>(k + b * kvs0 + h * kvs1);
@@ -571,6 +589,274 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(
     }
 }
 
+// fp32 storage on the matrix core: the bf16 kernel's workgroups, union, masks
+// and splits, with fp32 K / V tiles (rows padded against bank conflicts) and
+// the fp32 product v_mfma_f32_16x16x4f32.  As in the fp32 window, the QK^T
+// contraction gives lane group g dimensions g*D/4 .. g*D/4 + D/4 - 1 (contiguous
+// reads), and PV step j of a 16-key block contracts keys 4g + j, register j of
+// the lane's S^T fragment; V needs no transposition.
+namespace {
+
+template <int D>
+struct SpStageF32 {
+    static constexpr int KC = (mf::kTileK * D / 4) / 256;   // 16-byte chunks per thread
+    mf::f32x4 k[KC];   // native vectors: a float4 struct copy would stay in scratch
+    mf::f32x4 v[KC];
+};
+
+template <int D>
+__device__ __forceinline__ void spf_load(SpStageF32<D>& st, const float* kh, const float* vh,
+                                         int64_t kvs2, const uint16_t* ulist, int n_union, int u)
+{
+    // the tile's two cells; past the end of an odd union the second repeats the
+    // first (its keys are then masked for every query)
+    const int c0 = __builtin_amdgcn_readfirstlane(ulist[2 * u]);
+    const int c1 = __builtin_amdgcn_readfirstlane(2 * u + 1 < n_union ? ulist[2 * u + 1] : c0);
+#pragma unroll
+    for (int it = 0; it < SpStageF32<D>::KC; ++it) {
+        const int f = threadIdx.x + 256 * it;
+        const int kr = f / (D / 4), part = f % (D / 4);
+        const long row = (long)(kr < 32 ? c0 : c1) * 32 + (kr & 31);
+        st.k[it] = *reinterpret_cast<const mf::f32x4*>(kh + row * kvs2 + part * 4);
+        st.v[it] = *reinterpret_cast<const mf::f32x4*>(vh + row * kvs2 + part * 4);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void spf_store(const SpStageF32<D>& st, float* ks, float* vs)
+{
+    constexpr int P = D + kSpF32Pad;
+#pragma unroll
+    for (int it = 0; it < SpStageF32<D>::KC; ++it) {
+        const int f = threadIdx.x + 256 * it;
+        const int kr = f / (D / 4), part = f % (D / 4);
+        *reinterpret_cast<mf::f32x4*>(ks + kr * P + part * 4) = st.k[it];
+        *reinterpret_cast<mf::f32x4*>(vs + kr * P + part * 4) = st.v[it];
+    }
+}
+
+__device__ __forceinline__ mf::f32x4 mfma_f32(float a, float b, mf::f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace
+
+// d128's registers (2 x 32 query floats, 2 x 32 accumulators, a 32 KiB tile
+// stage) fit one wave per SIMD.
+template <int D>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_f32_kernel(
+    const float* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+    const float* __restrict__ k, const float* __restrict__ v, int64_t kvs0, int64_t kvs1,
+    int64_t kvs2, int H, int BH, int nq, int C, const int32_t* __restrict__ idx, int topk,
+    float scale_log2, float rms_eps, float* o, int64_t os0, int64_t os1, int64_t os2,
+    int n_split, float* __restrict__ ws_acc, float2* __restrict__ ws_ml, const float* o_sr,
+    const float* __restrict__ alpha)
+{
+    using namespace mf;
+    constexpr int T = D / 4, DB = D / 16, P = D + kSpF32Pad;
+    extern __shared__ uint4 smem_raw[];
+    const SpLayout L = sp_layout<D, true>(C, topk);
+    char* base = reinterpret_cast<char*>(smem_raw);
+    float* ks = reinterpret_cast<float*>(base);
+    float* vs = reinterpret_cast<float*>(base + L.off_vt);
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.off_bitmap);
+    uint16_t* rank = reinterpret_cast<uint16_t*>(base + L.off_rank);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(base + L.off_ulist);
+    uint32_t* qbits = reinterpret_cast<uint32_t*>(base + L.off_qbits);
+    __shared__ int red[4];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const TileOfBlock tb = xcd_tile(BH);
+    const long bh = tb.bh;
+    const int split = (int)(tb.tile % n_split);
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long t0 = (tb.tile / n_split) * kSpQ;
+    const int n_rows = nq - t0 < kSpQ ? (int)(nq - t0) : kSpQ;
+    const int32_t* idx_blk = idx + (bh * nq + t0) * (long)topk;
+    const int n_union = sp_union(L, bitmap, rank, ulist, qbits, idx_blk, n_rows, topk, C, red);
+
+    const float* kh = k + b * kvs0 + h * kvs1;
+    const float* vh = v + b * kvs0 + h * kvs1;
+    float qf[2][T];                                  // dims g*T .. g*T+T-1 of query 16 qg + n
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const int r = 32 * wv + 16 * qg + n;
+        const bool ok = r < n_rows;
+        const float* qrow = q + b * qs0 + h * qs1 + (t0 + (ok ? r : 0)) * qs2 + g * T;
+#pragma unroll
+        for (int c = 0; c < T / 4; ++c) {
+            const float4 x = ok ? *reinterpret_cast<const float4*>(qrow + 4 * c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            qf[qg][4 * c + 0] = x.x;
+            qf[qg][4 * c + 1] = x.y;
+            qf[qg][4 * c + 2] = x.z;
+            qf[qg][4 * c + 3] = x.w;
+        }
+    }
+
+    f32x4 acc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float l_part[2] = {0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};
+    const int qbit_row = (32 * wv + n) * L.qpitch;
+
+    const int n_all = (n_union + 1) / 2;
+    const int u_begin = (int)((long)n_all * split / n_split);
+    const int u_end = (int)((long)n_all * (split + 1) / n_split);
+    SpStageF32<D> stage;
+    if (u_begin < u_end) {
+        spf_load<D>(stage, kh, vh, kvs2, ulist, n_union, u_begin);
+        spf_store<D>(stage, ks, vs);
+    }
+    __syncthreads();
+    uint32_t qw[2] = {0u, 0u};
+    for (int u = u_begin; u < u_end; ++u) {
+        if (u + 1 < u_end) spf_load<D>(stage, kh, vh, kvs2, ulist, n_union, u + 1);
+        if ((u & 15) == 0 || u == u_begin) {
+            qw[0] = qbits[qbit_row + (u >> 4)];
+            qw[1] = qbits[qbit_row + 16 * L.qpitch + (u >> 4)];
+        }
+        const int sh = (2 * u) & 31;
+        const bool sel[2][2] = {{((qw[0] >> sh) & 1u) != 0, ((qw[0] >> (sh + 1)) & 1u) != 0},
+                                {((qw[1] >> sh) & 1u) != 0, ((qw[1] >> (sh + 1)) & 1u) != 0}};
+        if (__ballot(sel[0][0] || sel[0][1] || sel[1][0] || sel[1][1]) != 0) {
+            f32x4 s[4][2];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const float* krow = ks + (16 * kb + n) * P + g * T;
+#pragma unroll
+                for (int c = 0; c < T / 4; ++c) {
+                    const float4 a = *reinterpret_cast<const float4*>(krow + 4 * c);
+                    s[kb][0] = mfma_f32(a.x, qf[0][4 * c + 0], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.x, qf[1][4 * c + 0], s[kb][1]);
+                    s[kb][0] = mfma_f32(a.y, qf[0][4 * c + 1], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.y, qf[1][4 * c + 1], s[kb][1]);
+                    s[kb][0] = mfma_f32(a.z, qf[0][4 * c + 2], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.z, qf[1][4 * c + 2], s[kb][1]);
+                    s[kb][0] = mfma_f32(a.w, qf[0][4 * c + 3], s[kb][0]);
+                    s[kb][1] = mfma_f32(a.w, qf[1][4 * c + 3], s[kb][1]);
+                }
+            }
+            float corr[2];
+            bool any_rescale = false;
+#pragma unroll
+            for (int qg = 0; qg < 2; ++qg) {
+                float cm[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    float x = -INFINITY;
+#pragma unroll
+                    for (int kb = 2 * c; kb < 2 * c + 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            x = __builtin_elementwise_maximum(x, s[kb][qg][r]);
+                    cm[c] = sel[qg][c] ? x : -INFINITY;
+                }
+                const float tmax =
+                    xrow_max(__builtin_elementwise_maximum(cm[0], cm[1])) * scale_log2;
+                const bool raise = tmax > m_run[qg] + kLazy;
+                const float m_new = raise ? tmax : m_run[qg];
+                corr[qg] = raise ? __builtin_amdgcn_exp2f(m_run[qg] - m_new) : 1.f;
+                any_rescale |= raise;
+                m_run[qg] = m_new;
+                float bias[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) bias[c] = sel[qg][c] ? -m_new : -INFINITY;
+                float ls = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s[kb][qg][r] =
+                            __builtin_amdgcn_exp2f(fmaf(s[kb][qg][r], scale_log2, bias[kb >> 1]));
+                        ls += s[kb][qg][r];
+                    }
+                l_part[qg] = fmaf(l_part[qg], corr[qg], ls);
+            }
+            if (__builtin_expect(__ballot(any_rescale) != 0, 0)) {
+#pragma unroll
+                for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) acc[db][qg] *= corr[qg];
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float a = vs[(16 * kb + 4 * g + j) * P + 16 * db + n];
+                        acc[db][0] = mfma_f32(a, s[kb][0][j], acc[db][0]);
+                        acc[db][1] = mfma_f32(a, s[kb][1][j], acc[db][1]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (u + 1 < u_end) {
+            spf_store<D>(stage, ks, vs);
+            __syncthreads();
+        }
+    }
+
+    float l[2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) l[qg] = xrow_sum(l_part[qg]);
+    if (n_split > 1) {
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+            const int r = 32 * wv + 16 * qg + n;
+            if (r >= n_rows) continue;
+            const long slot = (bh * nq + t0 + r) * n_split + split;
+            if (g == 0) ws_ml[slot] = make_float2(m_run[qg], l[qg]);
+            float* a = ws_acc + slot * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<f32x4*>(a + 16 * db + 4 * g) = acc[db][qg];
+        }
+        return;
+    }
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const int r = 32 * wv + 16 * qg + n;
+        const float inv_l = l[qg] > 0.f ? 1.f / l[qg] : 0.f;
+        float ss = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            acc[db][qg] *= inv_l;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss = fmaf(acc[db][qg][e], acc[db][qg][e], ss);
+        }
+        ss = xrow_sum(ss);
+        const float inv_rms = 1.f / sqrtf(ss / (float)D + rms_eps);
+        if (r >= n_rows) continue;
+        float* orow = o + b * os0 + h * os1 + (t0 + r) * os2;
+        if (o_sr) {                    // eq. 2 in the epilogue: o = o_sr + alpha_h o_lr
+            const float* srow = o_sr + b * os0 + h * os1 + (t0 + r) * os2;
+            const float a = alpha[h];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const float4 x = *reinterpret_cast<const float4*>(srow + 16 * db + 4 * g);
+                *reinterpret_cast<float4*>(orow + 16 * db + 4 * g) =
+                    make_float4(fmaf(a, acc[db][qg][0] * inv_rms, x.x),
+                                fmaf(a, acc[db][qg][1] * inv_rms, x.y),
+                                fmaf(a, acc[db][qg][2] * inv_rms, x.z),
+                                fmaf(a, acc[db][qg][3] * inv_rms, x.w));
+            }
+            continue;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float4*>(orow + 16 * db + 4 * g) =
+                make_float4(acc[db][qg][0] * inv_rms, acc[db][qg][1] * inv_rms,
+                            acc[db][qg][2] * inv_rms, acc[db][qg][3] * inv_rms);
+    }
+}
+
 // Merge of a split attention (the readout, or the window branch): per query, the
 // partial states (m_s, l_s, O_s) (reference maxima in the log2 domain) combine as
 // O = sum_s 2^(m_s - M) O_s over l = sum_s 2^(m_s - M) l_s with M = max_s m_s;
@@ -655,8 +941,12 @@ hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const
         } else {
             if (rms) FS_MERGE(Bf16, 128, true); else FS_MERGE(Bf16, 128, false);
         }
-    } else {   // fp32 storage: only the window splits (the readout runs row-wise)
-        if (sh.d == 64) FS_MERGE(F32, 64, false); else FS_MERGE(F32, 128, false);
+    } else {
+        if (sh.d == 64) {
+            if (rms) FS_MERGE(F32, 64, true); else FS_MERGE(F32, 64, false);
+        } else {
+            if (rms) FS_MERGE(F32, 128, true); else FS_MERGE(F32, 128, false);
+        }
     }
 #undef FS_MERGE
     return hipGetLastError();
@@ -665,7 +955,7 @@ hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const
 // Split count: enough workgroups to give every CU two, at most 32 per query tile.
 int sparse_splits(const Shape& sh)
 {
-    if (!sh.bf16 || sh.C > kSpMaxCells || sh.nq == 0) return 1;
+    if (sh.C > kSpMaxCells || sh.nq == 0) return 1;
     const long base = (sh.nq + kSpQ - 1) / kSpQ * (long)sh.B * sh.H;
     if (base >= 512) return 1;
     const long want = (512 + base - 1) / base;
@@ -686,6 +976,32 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
 {
     if (sh.nq == 0) return hipSuccess;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)sh.d));
+    if (!sh.bf16) {
+        const size_t lds32 = sh.d == 64 ? sp_layout<64, true>(sh.C, topk).bytes
+                                        : sp_layout<128, true>(sh.C, topk).bytes;
+        if (sh.C <= kSpMaxCells && lds32 <= 160 * 1024) {
+            const int S = ws ? sparse_splits(sh) : 1;
+            const long rows_all = (long)sh.B * sh.H * sh.nq;
+            float* ws_acc = S > 1 ? static_cast<float*>(ws) : nullptr;
+            float2* ws_ml =
+                S > 1 ? reinterpret_cast<float2*>(ws_acc + rows_all * S * sh.d) : nullptr;
+            const long n_tiles = (sh.nq + kSpQ - 1) / kSpQ;
+            note_path("readout: fp32 MFMA tiles of 128 queries over their union, %d split(s)", S);
+            dim3 grid((unsigned)(n_tiles * S * sh.B * sh.H)), block(256);
+#define FS_SPARSE_F32(D)                                                                          \
+            hipLaunchKernelGGL((sparse_attn_f32_kernel<D>), grid, block, lds32, st,               \
+                               (const float*)q, sh.qs[0], sh.qs[1], sh.qs[2], (const float*)k,    \
+                               (const float*)v, sh.kvs[0], sh.kvs[1], sh.kvs[2], sh.H,            \
+                               sh.B * sh.H, sh.nq, sh.C, idx, topk, scale_log2, rms_eps,          \
+                               (float*)o_lr, sh.os[0], sh.os[1], sh.os[2], S, ws_acc, ws_ml,      \
+                               (const float*)o_sr, alpha)
+            if (sh.d == 64) FS_SPARSE_F32(64); else FS_SPARSE_F32(128);
+#undef FS_SPARSE_F32
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess || S <= 1) return err;
+            return launch_split_merge(sh, S, ws_acc, ws_ml, true, rms_eps, o_lr, st, o_sr, alpha);
+        }
+    }
     const size_t lds = sh.d == 64 ? sp_layout<64>(sh.C, topk).bytes
                                   : sp_layout<128>(sh.C, topk).bytes;
     if (sh.bf16 && sh.C <= kSpMaxCells && lds <= 160 * 1024) {
@@ -711,8 +1027,7 @@ hipError_t launch_sparse(const Shape& sh, const void* q, const void* k, const vo
         return launch_split_merge(sh, S, ws_acc, ws_ml, true, rms_eps, o_lr, st, o_sr, alpha);
     }
     note_path("readout: row-wise, one wavefront per query (%s)",
-              !sh.bf16 ? "fp32 storage"
-              : sh.C > kSpMaxCells ? "more than 32768 cells"
+              sh.C > kSpMaxCells ? "more than 32768 cells"
               : "the union bookkeeping exceeds 160 KiB of LDS");
     dim3 grid((unsigned)((sh.nq + 3) / 4), (unsigned)(sh.B * sh.H)), block(256);
 #define FS_SPARSE(E, D)                                                                          \

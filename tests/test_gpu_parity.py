@@ -890,11 +890,11 @@ def test_window_extreme_magnitudes(d, scale_k, scale_q):
 
 def test_last_path_reports_fallbacks():
     """fs_last_path names the kernel each call took: MFMA for bf16 shapes, the
-    fp32 matrix-core window for fp32 storage, and the row-wise fallback with its
-    reason for fp32 storage (selection, readout) or a candidate union wider than
-    the MFMA selection's 528 slots."""
+    fp32 matrix-core window and readout for fp32 storage, and the row-wise
+    fallback with its reason for fp32 storage (selection) or a candidate union
+    wider than the MFMA selection's 528 slots."""
     from long_context_fs_amd import fs as fsb
-    cases = [("f32_d64_noprune", "fp32 storage", "fp32 storage"),
+    cases = [("f32_d64_noprune", "fp32 storage", None),
              ("bf16_d64_wide_keep_k64", "wider than 528", None),
              ("bf16_d128_needle", None, None)]
     for name, sel_reason, read_reason in cases:
@@ -920,6 +920,7 @@ def test_last_path_reports_fallbacks():
                            fwd.ws_sparse)
         path = fsb.last_path()
         assert path.startswith("readout: ") and (("row-wise" in path) == (read_reason is not None))
+        assert ("fp32" in path) == (wl.dtype == "f32"), path
         if read_reason:
             assert read_reason in path, path
     torch.cuda.synchronize()
