@@ -48,6 +48,14 @@ __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// fp32 16x16x4 product (exact fp32 products, fp32 sums): lane l holds A row l % 16
+// and B column l % 16 at k = l / 16; C register r of lane l is row 4 (l / 16) + r
+// of column l % 16.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Round-to-nearest-even float -> fp16 bits, two values per dword (low first).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
 {

@@ -717,9 +717,13 @@ __device__ __forceinline__ void sel_topk_emit(const uint32_t (&kv)[NB][4], int t
     }
 }
 
-template <int D, int NB>
-__global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel(   // 256 threads exactly
-    const uint16_t* __restrict__ q, int64_t qs0, int64_t qs1, int64_t qs2,
+// F32: fp32 storage.  q and kbar stay fp32 and the scores come from
+// v_mfma_f32_16x16x4f32 (exact fp32 products, fp32 sums): lane group g supplies
+// dimensions g*D/4 .. g*D/4 + D/4 - 1, so a lane keeps D/4 query floats and reads
+// its cell row's D/4 consecutive floats from a padded fp32 chunk.
+template <int D, int NB, bool F32 = false>
+__global__ __launch_bounds__(256, (NB >= 33 || F32) ? 2 : 4) void select_topk_mfma_kernel(   // 256 threads exactly
+    const void* __restrict__ qv, int64_t qs0, int64_t qs1, int64_t qs2,
     const float* __restrict__ kbar, Prior pr, int H, int BH, int C, int nq, int q_pos0,
     int window, int cell, const int32_t* __restrict__ keep, const int32_t* __restrict__ keep_count,
     int keep_w, int n_lo, int n_rows, int topk, int n_hi_all, int u_cap, float inv_sqrt_d,
@@ -760,9 +764,22 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
     const int qr = 16 * wv + n;                 // this lane's query row in the block
     const bool q_ok = qr < n_rows_blk;
     const int n_q = q_ok ? n_candidates((long)q_pos0 + t0 + qr, window, cell, C) : 0;
-    bf16x8 qf[KS];
-    {
-        const uint16_t* qrow = q + b * qs0 + h * qs1 + (t0 + (q_ok ? qr : 0)) * qs2;
+    constexpr int T32 = D / 4, P32 = D + 4;     // fp32: dims per lane group, chunk row pitch
+    bf16x8 qf[F32 ? 1 : KS];
+    float qf32[F32 ? T32 : 1];
+    if constexpr (F32) {
+        const float* qrow = static_cast<const float*>(qv) + b * qs0 + h * qs1 +
+                            (t0 + (q_ok ? qr : 0)) * qs2 + g * T32;
+#pragma unroll
+        for (int c = 0; c < T32 / 4; ++c) {
+            const f32x4 x = q_ok ? *reinterpret_cast<const f32x4*>(qrow + 4 * c)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qf32[4 * c + e] = x[e];
+        }
+    } else {
+        const uint16_t* qrow = static_cast<const uint16_t*>(qv) + b * qs0 + h * qs1 +
+                               (t0 + (q_ok ? qr : 0)) * qs2;
 #pragma unroll
         for (int t = 0; t < KS; ++t)
             qf[t] = as_bf16x8(q_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * t + 8 * g)
@@ -800,6 +817,11 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
             for (int it = 0; it < kIt; ++it) {
                 const int f = tid + 256 * it;
                 const int cl = f / (D / 4), d4 = (f % (D / 4)) * 4;
+                if constexpr (F32) {         // the fp32 row as it is, in a padded row
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(kbs) + cl * P32 + d4) =
+                        f32x4{pre[it].x, pre[it].y, pre[it].z, pre[it].w};
+                    continue;
+                }
                 const float r[4] = {pre[it].x, pre[it].y, pre[it].z, pre[it].w};
                 // x = hi + mid + lo exactly: each residual has at most 16 (then 8)
                 // significant bits, so the fp32 subtractions are exact.
@@ -831,13 +853,24 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void select_topk_mfma_kernel
                 const int slot0 = s_base + 16 * bb;
                 if (slot0 < n_union) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (F32) {
+                        const float* krow =
+                            reinterpret_cast<const float*>(kbs) + (16 * b2 + n) * P32 + g * T32;
 #pragma unroll
-                    for (int t = 0; t < KS; ++t) {
+                        for (int c = 0; c < T32 / 4; ++c) {
+                            const f32x4 a = *reinterpret_cast<const f32x4*>(krow + 4 * c);
 #pragma unroll
-                        for (int pp = 0; pp < 3; ++pp) {
-                            const bf16x8 a = as_bf16x8(
-                                lds_load16(kbs + sw_off<D>(pp * kSelChunk + 16 * b2 + n, 4 * t + g)));
-                            acc = mfma(a, qf[t], acc);
+                            for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], qf32[4 * c + e], acc);
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < KS; ++t) {
+#pragma unroll
+                            for (int pp = 0; pp < 3; ++pp) {
+                                const bf16x8 a = as_bf16x8(lds_load16(
+                                    kbs + sw_off<D>(pp * kSelChunk + 16 * b2 + n, 4 * t + g)));
+                                acc = mfma(a, qf[t], acc);
+                            }
                         }
                     }
 #pragma unroll
@@ -1373,25 +1406,31 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
         const int kw = keep ? keep_w : 0;
         const size_t lds = sh.d == 64 ? sel_layout<64>(n_hi, uc, kw, rerank).bytes
                                       : sel_layout<128>(n_hi, uc, kw, rerank).bytes;
-        if (sh.bf16 && lds <= 64 * 1024 && sh.C <= kSelMaxCells && uc <= 16 * kSelMaxBlocks &&
-            offs_ok) {
+        if ((sh.bf16 || !rerank) && lds <= 64 * 1024 && sh.C <= kSelMaxCells &&
+            uc <= 16 * kSelMaxBlocks && offs_ok) {
+            const bool f32 = !sh.bf16;
             // short query ranges: the union split over workgroups of 64 slots each,
             // then a merge of their top-K lists (selection with a workspace only)
             const int S = !rerank && ws && ws_bytes >= select_ws_bytes(sh, keep != nullptr, keep_w,
                                                                       topk)
                               ? select_splits(sh, keep != nullptr, keep_w) : 1;
             if (S > 1) {
-                note_path("select: MFMA, union split over %d workgroups, then a merge", S);
+                note_path("select: %sMFMA, union split over %d workgroups, then a merge",
+                          f32 ? "fp32 " : "", S);
                 int32_t* ws_cell = static_cast<int32_t*>(ws);
                 float* ws_val = reinterpret_cast<float*>(ws_cell + (size_t)sh.B * sh.H * sh.nq * S * topk);
                 dim3 grid_s((unsigned)((sh.nq + 63) / 64 * S * sh.B * sh.H));
-#define FS_SELECT_SPLIT(D)                                                                      \
-                hipLaunchKernelGGL((select_topk_mfma_kernel<D, 4>), grid_s, dim3(256), lds, st, \
-                                   (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,   \
-                                   sh.H, sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,  \
+#define FS_SELECT_SPLIT(D, F)                                                                   \
+                hipLaunchKernelGGL((select_topk_mfma_kernel<D, 4, F>), grid_s, dim3(256), lds,  \
+                                   st, q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr, sh.H,          \
+                                   sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,        \
                                    keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, \
                                    idx, score, S, ws_cell, ws_val)
-                if (sh.d == 64) { FS_SELECT_SPLIT(64); } else { FS_SELECT_SPLIT(128); }
+                if (f32) {
+                    if (sh.d == 64) { FS_SELECT_SPLIT(64, true); } else { FS_SELECT_SPLIT(128, true); }
+                } else {
+                    if (sh.d == 64) { FS_SELECT_SPLIT(64, false); } else { FS_SELECT_SPLIT(128, false); }
+                }
 #undef FS_SELECT_SPLIT
                 hipError_t err = hipGetLastError();
                 if (err != hipSuccess) return err;
@@ -1403,9 +1442,16 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
             }
             dim3 grid((unsigned)((sh.nq + 63) / 64 * sh.B * sh.H));
             const int nb_need = uc / 16;
-            note_path("%s: MFMA, 64 queries per workgroup", rerank ? "rerank" : "select");
+            note_path("%s: %sMFMA, 64 queries per workgroup", rerank ? "rerank" : "select",
+                      f32 ? "fp32 " : "");
 #define FS_SELECT_MFMA(D, NB)                                                                   \
-            if (rerank)                                                                         \
+            if (f32)                                                                            \
+                hipLaunchKernelGGL((select_topk_mfma_kernel<D, NB, true>), grid, dim3(256), lds,\
+                                   st, q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr, sh.H,          \
+                                   sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,        \
+                                   keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, \
+                                   idx, score, 1, nullptr, nullptr);                             \
+            else if (rerank)                                                                    \
                 hipLaunchKernelGGL((rerank_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,  \
                                    (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2],             \
                                    (const uint16_t*)k, sh.kvs[0], sh.kvs[1], sh.kvs[2], pr,      \
@@ -1414,7 +1460,7 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
                                    idx, score);                                                  \
             else                                                                                \
                 hipLaunchKernelGGL((select_topk_mfma_kernel<D, NB>), grid, dim3(256), lds, st,  \
-                                   (const uint16_t*)q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,   \
+                                   q, sh.qs[0], sh.qs[1], sh.qs[2], kbar, pr,                    \
                                    sh.H, sh.B * sh.H, sh.C, sh.nq, sh.q_pos0, sh.w, sh.s, keep,  \
                                    keep_count, keep_w, n_lo, n_rows, topk, n_hi, uc, inv_sqrt_d, \
                                    idx, score, 1, nullptr, nullptr)
@@ -1433,7 +1479,7 @@ hipError_t launch_topk(const Shape& sh, const void* q, const float* kbar, const 
     {
         const int u_cap = keep ? (keep_w + 3 < n_hi ? keep_w + 3 : n_hi) : n_hi;
         note_path("%s: row-wise, one wavefront per query (%s)", rerank ? "rerank" : "select",
-                  !sh.bf16 ? "fp32 storage"
+                  !sh.bf16 && rerank ? "fp32 storage"
                   : sh.C > kSelMaxCells ? "more than 32768 cells"
                   : u_cap > 16 * kSelMaxBlocks ? "candidate union wider than 528 cells"
                   : "bookkeeping exceeds 64 KiB of LDS");

@@ -635,11 +635,6 @@ __device__ __forceinline__ void spf_store(const SpStageF32<D>& st, float* ks, fl
     }
 }
 
-__device__ __forceinline__ mf::f32x4 mfma_f32(float a, float b, mf::f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 }  // namespace
 
 // d128's registers (2 x 32 query floats, 2 x 32 accumulators, a 32 KiB tile

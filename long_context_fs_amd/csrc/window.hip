@@ -425,11 +425,6 @@ __device__ __forceinline__ void winf_store(const WinStageF32<D>& st, float* ks, 
     }
 }
 
-__device__ __forceinline__ mf::f32x4 mfma_f32(float a, float b, mf::f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 }  // namespace
 
 // d128 holds 2 x 32 rotated query floats, 2 x 32 accumulators and a 16 KiB-per-tile

@@ -3,8 +3,8 @@ calls; the library makes no allocation, copy or memset, so every call
 captures) replays to the eager result bit for bit: three replays with eager
 work and synchronisations between them, on a prefill with the MFMA kernels, a
 short query range whose selection, window and readout split over workgroups
-(workspaces), and fp32 storage (the fp32 matrix-core window, row-wise selection
-and readout)."""
+(workspaces), and fp32 storage (the fp32 matrix-core selection, window and
+readout)."""
 import numpy as np
 import pytest
 

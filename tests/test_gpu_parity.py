@@ -68,11 +68,16 @@ SMALL = {
     "bf16_d128_decode_prior": W["decode_b1h8_n262144_q256_d128_bf16"].replace(
         heads=2, n_ctx=7000, n_q=70, q_pos0=7000 - 70, budget=100, topk=8, needle_queries=70,
         prior_lambda=0.3, prior_sigma=400.0),
-    # eq. 7's position prior, on the MFMA (bf16, pruned) and row-wise (fp32, unpruned) paths
+    # eq. 7's position prior, on the bf16 (pruned) and fp32 (unpruned) MFMA paths
     "bf16_d128_prior": W["prefill_b1h8_n65536_d128_bf16_prior"].replace(
         heads=2, n_ctx=2900, n_q=2900, budget=16, topk=8, prior_lambda=0.3, prior_sigma=300.0),
     "f32_d64_prior_noprune": W["prefill_b1h1_n2048_d64_f32"].replace(
         heads=2, n_ctx=1500, n_q=1500, prior_lambda=0.5, prior_sigma=200.0),
+    # fp32 keep rows wider than the MFMA selection's 528 slots (row-wise selection),
+    # with the prior
+    "f32_d64_wide_keep_prior": W["prefill_b1h1_n2048_d64_f32"].replace(
+        heads=2, n_ctx=24000, n_q=120, q_pos0=23880, budget=700, topk=64, prior_lambda=0.3,
+        prior_sigma=4000.0),
 }
 FULL = list(synth.WORKLOADS)
 
@@ -861,6 +866,46 @@ def test_readout_with_combine_epilogue(name, split):
     assert row_rel_err(got, want).max() <= TOL[wl.dtype]
 
 
+F32_WIDE = {
+    # 512 query tiles of 128, each streaming a union of ~240 cells: the unsplit kernel
+    "f32_d128_prefill_wide": W["prefill_b1h8_n65536_d128_bf16"].replace(
+        dtype="f32", heads=4, n_ctx=16384, n_q=16384),
+    # a short query range over many cells: the key-range splits and their merge
+    "f32_d64_decode_split": W["decode_b1h8_n262144_q256_d128_bf16"].replace(
+        dtype="f32", head_dim=64, n_ctx=20000, n_q=64, q_pos0=20000 - 64, budget=300,
+        needle_queries=64),
+}
+
+
+@pytest.mark.parametrize("name", list(F32_WIDE))
+def test_f32_readout_full_width_unions(name):
+    """fp32 storage on the matrix-core readout at unions as wide as the 64k
+    prefill's: eq. 9 over the GPU's cells against the oracle on every row of
+    head 0 and sampled rows of the others, and o (eq. 2) against the oracle's
+    own pipeline on the sampled rows, at the fp32 tolerance."""
+    from long_context_fs_amd import fs as fsb
+    wl = F32_WIDE[name]
+    x = synth.generate(wl)
+    print(f"[parity-f32] {name}: GPU forward", flush=True)
+    g = run_gpu(wl, x)
+    q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+    fwd = FsForward.for_workload(wl)
+    fsb.fs_sparse_attn(fwd.prob, q, k, v, torch.from_numpy(g["idx"]).cuda(), wl.topk,
+                       wl.rms_eps, fwd.o_lr, fwd.ws_sparse)
+    path = fsb.last_path()
+    assert "fp32 MFMA" in path, path
+    split = "decode" in name
+    assert ("1 split(s)" in path) != split, path
+    rows = sample_rows(wl) + [(0, 0, t) for t in range(wl.n_q)]
+    rows = sorted(set(rows))
+    ref, _ = oracle_rows(wl, x, g, rows, use_gpu_sets=True)
+    err = check_rows(wl, x, g, rows, ref["o_lr"], "o_lr", TOL[wl.dtype])
+    sampled = sample_rows(wl)
+    e2e, n_near = check_end_to_end(wl, x, g, sampled)
+    print(f"[parity-f32] {name}: {path}; o_lr {err:.3g} on {len(rows)} rows, "
+          f"o {e2e:.3g}, near-tie rows {n_near}", flush=True)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale_k,scale_q", [(1.5e4, 1.0 / 1.5e4), (1e-6, 1e6), (3e4, 1.0 / 3e4)])
 def test_window_extreme_magnitudes(d, scale_k, scale_q):
@@ -890,11 +935,11 @@ def test_window_extreme_magnitudes(d, scale_k, scale_q):
 
 def test_last_path_reports_fallbacks():
     """fs_last_path names the kernel each call took: MFMA for bf16 shapes, the
-    fp32 matrix-core window and readout for fp32 storage, and the row-wise
-    fallback with its reason for fp32 storage (selection) or a candidate union
-    wider than the MFMA selection's 528 slots."""
+    fp32 matrix-core kernels for fp32 storage, and the row-wise fallback with
+    its reason for a candidate union wider than the MFMA selection's 528 slots."""
     from long_context_fs_amd import fs as fsb
-    cases = [("f32_d64_noprune", "fp32 storage", None),
+    cases = [("f32_d64_noprune", None, None),
+             ("f32_d64_wide_keep_prior", "wider than 528", None),
              ("bf16_d64_wide_keep_k64", "wider than 528", None),
              ("bf16_d128_needle", None, None)]
     for name, sel_reason, read_reason in cases:
@@ -912,6 +957,8 @@ def test_last_path_reports_fallbacks():
         assert ("row-wise" in path) == (sel_reason is not None), path
         if sel_reason:
             assert sel_reason in path, path
+        else:
+            assert ("fp32" in path) == (wl.dtype == "f32"), path
         fsb.fs_window_attn(fwd.prob, q, k, v, wl.rope_base, fwd.ws, fwd.o_sr)
         path = fsb.last_path()            # both storage types run the window on the matrix core
         assert path.startswith("window: ") and "MFMA" in path, path
