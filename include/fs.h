@@ -254,11 +254,12 @@ fs_status fs_sparse_attn(const fs_problem* problem, const void* q, const void* k
 /* fs_sparse_attn for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * readout as fs_sparse_attn with a workspace of fs_sparse_workspace_size bytes,
- * with the split states held in a device array the library owns (48 MiB per GPU,
- * kept until the process ends) instead of a caller workspace.  It calls no
- * allocating routine.  A shape whose split states exceed 48 MiB returns
- * FS_ERR_UNSUPPORTED and runs nothing (the 256k decode shape, 8 heads x 256
- * queries x 32 splits x 520 bytes, needs 34 MiB).  Every call on one GPU uses
+ * with the split states held in a device array the library owns (16.25 MiB per
+ * GPU, kept until the process ends) instead of a caller workspace.  It calls no
+ * allocating routine.  The readout splits into at most 256 workgroups of 128
+ * query rows, so no shape's states exceed the array (the 256k decode shape,
+ * 8 heads x 256 queries x 16 splits x 520 bytes, fills it); a shape whose
+ * states did would return FS_ERR_UNSUPPORTED and run nothing.  Every call on one GPU uses
  * that GPU's one array: calls that overlap in time on one GPU (other streams,
  * other threads) race and must not be issued; the array keeps the last call's
  * states, which the next call overwrites before reading. */

@@ -87,8 +87,10 @@ hipError_t launch_rope_table(const Shape& sh, double rope_base, void* table, hip
 int sparse_splits(const Shape& sh);
 size_t sparse_ws_bytes(const Shape& sh);
 // The allocation-free readout's scratch: its size, and this device's address of
-// it (looked up once per device; nullptr and *err set on failure).
-constexpr size_t kSparseNoAllocBytes = (size_t)48 << 20;
+// it (looked up once per device; nullptr and *err set on failure).  The split
+// rule launches at most 256 split workgroups of 128 query rows, each row's state
+// d fp32 plus (m, l): 16.25 MiB at d = 128, the most any shape needs.
+constexpr size_t kSparseNoAllocBytes = (size_t)256 * 128 * (128 * sizeof(float) + 8);
 void* sparse_noalloc_scratch(hipError_t* err);
 
 // o_sr (nullable): eq. 2 in the readout's epilogue, o_lr then receives

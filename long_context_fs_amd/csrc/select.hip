@@ -1516,7 +1516,7 @@ int select_splits(const Shape& sh, bool pruned, int keep_w)
 {
     const long blocks = (long)(sh.nq + 63) / 64 * sh.B * sh.H;
     const int uc = select_slots(sh, pruned, keep_w);
-    if (!sh.bf16 || blocks >= 256 || uc <= 64 || uc > 16 * kSelMaxBlocks) return 1;
+    if (blocks >= 256 || uc <= 64 || uc > 16 * kSelMaxBlocks) return 1;
     return (uc + 63) / 64;            // 64 slots (four 16-slot blocks) per split
 }
 

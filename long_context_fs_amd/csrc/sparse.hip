@@ -947,14 +947,20 @@ hipError_t launch_split_merge(const Shape& sh, int S, const float* ws_acc, const
     return hipGetLastError();
 }
 
-// Split count: enough workgroups to give every CU two, at most 32 per query tile.
+// Split count: about one workgroup per CU in all (256), at most 32 per query tile.
+// A second workgroup per CU does not pay: each split's partial state is written
+// and merged, and the two share the CU's LDS and matrix cores (at 256 decode
+// queries over 8 heads, 16 splits take 0.037 ms, 20-32 splits 0.053 ms).
+constexpr long kSpSplitWorkgroups = 256;
+static_assert(kSparseNoAllocBytes >= (size_t)kSpSplitWorkgroups * kSpQ * (128 * sizeof(float) + 8),
+              "the allocation-free readout's array holds the largest split state");
+
 int sparse_splits(const Shape& sh)
 {
     if (sh.C > kSpMaxCells || sh.nq == 0) return 1;
     const long base = (sh.nq + kSpQ - 1) / kSpQ * (long)sh.B * sh.H;
-    if (base >= 512) return 1;
-    const long want = (512 + base - 1) / base;
-    return (int)(want < 32 ? want : 32);
+    const long want = kSpSplitWorkgroups / base;
+    return (int)(want < 1 ? 1 : want < 32 ? want : 32);
 }
 
 size_t sparse_ws_bytes(const Shape& sh)

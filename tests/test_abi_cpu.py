@@ -79,8 +79,31 @@ def test_prune_rows_and_workspace_host_only(lib):
     assert fs.fs_select_workspace_size(dec, 500, 32) == 2 * 256 * 8 * 32 * 8
     assert fs.fs_select_workspace_size(dec, 40, 32) == 0           # union of 48 slots
     assert fs.fs_select_workspace_size(_prob(batch=8, heads=16), 500, 32) == 0   # 2048 tiles
+    # fp32 storage splits alike
     assert fs.fs_select_workspace_size(_prob(dtype=fs.FS_F32, n_ctx=65536, n_q=256,
-                                             q_pos0=65536 - 256), 500, 32) == 0
+                                             q_pos0=65536 - 256), 500, 32) == 2 * 256 * 8 * 32 * 8
+
+
+def test_readout_split_states_bounded(lib):
+    """The readout splits a short query range into at most 256 workgroups of 128
+    query rows (one per CU), each row's state d fp32 plus (m, l); so no shape's
+    states exceed 256 x 128 x 520 bytes, the allocation-free readout's array,
+    and the 256k decode shape (8 heads x 2 tiles, 16 splits) fills it."""
+    cap = 256 * 128 * (128 * 4 + 8)
+    worst = 0
+    for heads in (1, 2, 3, 5, 8, 16, 17, 40, 100, 255, 256, 300):
+        for n_q in (1, 77, 128, 129, 256, 300, 1000, 4096):
+            for d in (64, 128):
+                p = _prob(heads=heads, head_dim=d, n_ctx=8192, n_q=n_q, q_pos0=8192 - n_q)
+                need = fs.fs_sparse_workspace_size(p)
+                tiles = (n_q + 127) // 128 * heads
+                splits = min(32, 256 // tiles) if tiles <= 256 else 1
+                rows = heads * n_q
+                assert need == (0 if splits <= 1 else rows * splits * (d * 4 + 8)), (heads, n_q, d)
+                worst = max(worst, need)
+    assert worst <= cap
+    dec = _prob(heads=8, head_dim=128, n_ctx=262144, n_q=256, q_pos0=262144 - 256)
+    assert fs.fs_sparse_workspace_size(dec) == cap
 
 
 @pytest.mark.parametrize("bad,status", [

@@ -49,13 +49,3 @@ def test_noalloc_equals_workspace_twice():
                 err = np.abs(got[0, h, t] - want).max() / max(np.abs(want).max(), 1e-30)
                 assert err <= 2e-2, (wl.n_ctx, h, t, err)
 
-
-def test_noalloc_rejects_oversized_states():
-    """A split readout whose states exceed the 48 MiB array is refused."""
-    # 170 heads x 3 query tiles: 510 workgroups, so two splits of 384 rows each
-    prob = fs.problem(1, 170, 128, 4096, 384, 4096 - 384, 512, fs.FS_BF16)
-    need = fs.fs_sparse_workspace_size(prob)
-    assert need > 48 << 20
-    dummy = torch.zeros(16, dtype=torch.int32, device="cuda")
-    with pytest.raises(fs.FsError, match="48|scratch"):
-        fs.fs_sparse_attn_noalloc(prob, dummy, dummy, dummy, dummy, 8, 1e-6, dummy)
