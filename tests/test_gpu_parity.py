@@ -881,8 +881,9 @@ F32_WIDE = {
 def test_f32_readout_full_width_unions(name):
     """fp32 storage on the matrix-core readout at unions as wide as the 64k
     prefill's: eq. 9 over the GPU's cells against the oracle on every row of
-    head 0 and sampled rows of the others, and o (eq. 2) against the oracle's
-    own pipeline on the sampled rows, at the fp32 tolerance."""
+    head 0 and sampled rows of the others; on the sampled rows, the selected
+    cells (eq. 7, exact away from near-ties) and o (eq. 2) against the oracle's
+    own pipeline, at the fp32 tolerance."""
     from long_context_fs_amd import fs as fsb
     wl = F32_WIDE[name]
     x = synth.generate(wl)
@@ -901,6 +902,7 @@ def test_f32_readout_full_width_unions(name):
     ref, _ = oracle_rows(wl, x, g, rows, use_gpu_sets=True)
     err = check_rows(wl, x, g, rows, ref["o_lr"], "o_lr", TOL[wl.dtype])
     sampled = sample_rows(wl)
+    check_select(wl, x, g, sampled)              # fp32 MFMA selection (split at decode)
     e2e, n_near = check_end_to_end(wl, x, g, sampled)
     print(f"[parity-f32] {name}: {path}; o_lr {err:.3g} on {len(rows)} rows, "
           f"o {e2e:.3g}, near-tie rows {n_near}", flush=True)
