@@ -127,6 +127,8 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
     del x
     fwd = fs.FsForward.for_workload(wl, device=dev)
     p = fwd.prob
+    # the window's RoPE table depends only on (w, d, rope_base): built once, like a weight
+    fs.fs_window_table(p, fwd.rope_base, fwd.ws)
 
     def step(ev=None):
         def mark(j):
@@ -142,7 +144,7 @@ def run_workload(name, steps, warmup, torch, fs, rerank=False):
         fs.fs_select_topk(p, q, fwd.kbar, fwd.keep, fwd.keep_count, fwd.keep_w, fwd.topk,
                           fwd.idx, None, None, fwd.prior, fwd.ws_select)
         mark(3)
-        fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)
+        fs.fs_window_attn_tabled(p, q, k, v, fwd.ws, fwd.o_sr)
         mark(4)
         fs.fs_sparse_attn_combine(p, q, k, v, fwd.idx, fwd.topk, fwd.rms_eps, fwd.o_sr, alpha,
                                   fwd.o, fwd.ws_sparse)
@@ -347,11 +349,12 @@ def run_fsb(name, steps, warmup, torch, fs):
     fwd = fs.FsForward.for_workload(wl, device=dev)
     p = fwd.prob
     fs.fs_cell_summaries(p, k, fwd.kbar, fwd.amax)
+    fs.fs_window_table(p, fwd.rope_base, fwd.ws)
     fb = FsbSetup(torch, fs, wl, p, fwd.kbar, fwd.amax)
     calls = [("summaries", lambda: fs.fs_cell_summaries(p, k, fwd.kbar, fwd.amax)),
              ("forest_build", fb.build),
              ("beam_select", lambda: fb.search(q)),
-             ("window", lambda: fs.fs_window_attn(p, q, k, v, fwd.rope_base, fwd.ws, fwd.o_sr)),
+             ("window", lambda: fs.fs_window_attn_tabled(p, q, k, v, fwd.ws, fwd.o_sr)),
              ("sparse", lambda: fs.fs_sparse_attn_combine(p, q, k, v, fb.idx, wl.topk,
                                                           fwd.rms_eps, fwd.o_sr, alpha, fwd.o,
                                                           fwd.ws_sparse))]
@@ -528,7 +531,7 @@ def run_phase(name, phase, reps, torch, fs):
                                             f.topk, f.idx, None, None, f.prior, f.ws_select),
         "rerank": lambda: fs.fs_rerank_topk(p, q, k, f.keep, f.keep_count, f.keep_w, f.topk,
                                             f.idx, None, None, f.prior, rr_ws),
-        "window": lambda: fs.fs_window_attn(p, q, k, v, f.rope_base, f.ws, f.o_sr),
+        "window": lambda: fs.fs_window_attn_tabled(p, q, k, v, f.ws, f.o_sr),
         "sparse": lambda: fs.fs_sparse_attn_combine(p, q, k, v, f.idx, f.topk, f.rms_eps, f.o_sr,
                                                     alpha, f.o, f.ws_sparse),
         "combine": lambda: fs.fs_combine(p, f.o_sr, f.o_lr, alpha, f.o),

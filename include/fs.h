@@ -11,6 +11,7 @@
  *                               (+ fs_prune_workspace_size)
  *   fs_select_topk     eq. 7   score q.kbar/sqrt(d) (+ optional erf prior), top-K cells
  *   fs_window_attn     eqs.3-4 RoPE attention over positions max(0,i-w) .. i
+ *                               (+ fs_window_table / fs_window_attn_tabled)
  *   fs_sparse_attn     eq. 9   NoPE attention over the selected cells' tokens, RMSNorm
  *   fs_rerank_topk     eq. 12  token-level reranking (log-sum-exp of a cell's logits), top-K
  *   fs_stream_*        eqs. 2-9 from a bounded per-head state ("Bounded memory",
@@ -233,6 +234,24 @@ fs_status fs_workspace_size(const fs_problem* problem, size_t* bytes);
 fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k, const void* v,
                          float rope_base, void* workspace, size_t ws_bytes, void* o_sr,
                          void* stream);
+
+/* The RoPE table of fs_window_attn's workspace alone (eq. 3's rotations by the
+ * relative offsets -w-128 .. 127, cos/sin built in fp64, stored fp32).  It depends
+ * only on the problem's window and head_dim and on rope_base, so a caller that
+ * makes many window calls with the same three builds it once and then calls
+ * fs_window_attn_tabled.  workspace: at least the table's bytes (the start of
+ * fs_workspace_size). */
+fs_status fs_window_table(const fs_problem* problem, float rope_base, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* fs_window_attn without rebuilding the table: the workspace must already hold
+ * the table that fs_window_table (or fs_window_attn) built for the same window,
+ * head_dim and rope_base; it is read, not written (the split states after it are
+ * overwritten).  A table built for other values is not detected and gives wrong
+ * outputs. */
+fs_status fs_window_attn_tabled(const fs_problem* problem, const void* q, const void* k,
+                                const void* v, void* workspace, size_t ws_bytes, void* o_sr,
+                                void* stream);
 
 /* Bytes of device workspace with which fs_sparse_attn splits each query's cells
  * over several workgroups (0 when the query range already fills the device). */

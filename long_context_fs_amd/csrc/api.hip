@@ -359,6 +359,35 @@ fs_status fs_window_attn(const fs_problem* problem, const void* q, const void* k
                     "fs_window_attn");
 }
 
+fs_status fs_window_table(const fs_problem* problem, float rope_base, void* workspace,
+                          size_t ws_bytes, void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(workspace);
+    if (!(rope_base > 1.0f)) return fail(FS_ERR_INVALID, "rope_base must be > 1");
+    if (ws_bytes < fs::rope_table_bytes(sh))
+        return fail(FS_ERR_INVALID, "workspace of %zu bytes, need %zu", ws_bytes,
+                    fs::rope_table_bytes(sh));
+    return from_hip(fs::launch_rope_table(sh, (double)rope_base, workspace, (hipStream_t)stream),
+                    "fs_window_table");
+}
+
+fs_status fs_window_attn_tabled(const fs_problem* problem, const void* q, const void* k,
+                                const void* v, void* workspace, size_t ws_bytes, void* o_sr,
+                                void* stream)
+{
+    fs::Shape sh;
+    FS_CHECK(check_problem(problem, &sh));
+    FS_PTR(q); FS_PTR(k); FS_PTR(v); FS_PTR(o_sr); FS_PTR(workspace);
+    if (ws_bytes < fs::rope_table_bytes(sh))
+        return fail(FS_ERR_INVALID, "workspace of %zu bytes, need %zu", ws_bytes,
+                    fs::rope_table_bytes(sh));
+    return from_hip(fs::launch_window(sh, q, k, v, 0.0, workspace, o_sr, (hipStream_t)stream,
+                                      true, ws_bytes),
+                    "fs_window_attn_tabled");
+}
+
 fs_status fs_sparse_workspace_size(const fs_problem* problem, size_t* bytes)
 {
     fs::Shape sh;

@@ -19,7 +19,8 @@ CELL = 32
 
 SYMBOLS = ("fs_cell_summaries", "fs_prune_rows", "fs_prune_prefix", "fs_prune_workspace_size",
            "fs_select_topk",
-           "fs_workspace_size", "fs_window_attn", "fs_sparse_workspace_size", "fs_sparse_attn",
+           "fs_workspace_size", "fs_window_attn", "fs_window_table", "fs_window_attn_tabled",
+           "fs_sparse_workspace_size", "fs_sparse_attn",
            "fs_sparse_attn_noalloc", "fs_sparse_attn_combine", "fs_combine", "fs_rerank_topk", "fs_rerank_workspace_size",
            "fs_select_workspace_size", "fs_stream_state_size", "fs_stream_reset",
            "fs_stream_step", "fs_forest_size", "fs_forest_build", "fs_beam_select",
@@ -75,6 +76,8 @@ def load(path: str | None = None):
         "fs_rerank_workspace_size": [P, i32, C.POINTER(C.c_size_t)],
         "fs_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_window_attn": [P, vp, vp, vp, f32, vp, C.c_size_t, vp, vp],
+        "fs_window_table": [P, f32, vp, C.c_size_t, vp],
+        "fs_window_attn_tabled": [P, vp, vp, vp, vp, C.c_size_t, vp, vp],
         "fs_sparse_workspace_size": [P, C.POINTER(C.c_size_t)],
         "fs_sparse_attn": [P, vp, vp, vp, vp, i32, f32, vp, C.c_size_t, vp, vp],
         "fs_sparse_attn_noalloc": [P, vp, vp, vp, vp, i32, f32, vp, vp],
@@ -252,6 +255,19 @@ def fs_window_attn(prob, q, k, v, rope_base, workspace, o_sr, stream=None):
                                                    _p(o_sr), _s(stream)))
 
 
+def fs_window_table(prob, rope_base, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("fs_window_table", load().fs_window_table(C.byref(prob), float(rope_base),
+                                                     _p(workspace), nbytes, _s(stream)))
+
+
+def fs_window_attn_tabled(prob, q, k, v, workspace, o_sr, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("fs_window_attn_tabled",
+           load().fs_window_attn_tabled(C.byref(prob), _p(q), _p(k), _p(v), _p(workspace),
+                                        nbytes, _p(o_sr), _s(stream)))
+
+
 def fs_sparse_workspace_size(prob) -> int:
     n = C.c_size_t()
     _check("fs_sparse_workspace_size", load().fs_sparse_workspace_size(C.byref(prob), C.byref(n)))
@@ -301,7 +317,9 @@ class FsForward:
     """The FS-L forward of one problem shape: eq. 5, 8, 7, 3-4, 9, then 2.
 
     All intermediates are allocated at construction; a call enqueues the six
-    library calls on the stream and allocates nothing."""
+    library calls on the stream and allocates nothing.  The window's RoPE table
+    depends only on (w, d, rope_base): the first call builds it in the workspace,
+    later calls reuse it (fs_window_attn_tabled)."""
 
     def __init__(self, batch, heads, n_ctx, head_dim, n_q, q_pos0, dtype, topk, budget,
                  n_recent=0, window=512, rope_base=10000.0, rms_eps=1e-6, device="cuda",
@@ -327,6 +345,7 @@ class FsForward:
         self.idx = torch.empty((B, H, n_q, topk), dtype=i32, device=device)
         self.score = torch.empty((B, H, n_q, topk), dtype=f32, device=device)
         self.ws = torch.empty(fs_workspace_size(self.prob), dtype=torch.uint8, device=device)
+        self.table_ready = False
         npr = fs_prune_workspace_size(self.prob) if self.pruned else 0
         self.ws_prune = torch.empty(npr, dtype=torch.uint8, device=device) if npr else None
         nsp = fs_sparse_workspace_size(self.prob)
@@ -355,7 +374,12 @@ class FsForward:
         fs_select_topk(p, q, self.kbar, self.keep, self.keep_count, self.keep_w, self.topk,
                        self.idx, self.score if keep_score else None, stream, self.prior,
                        self.ws_select)
-        fs_window_attn(p, q, k, v, self.rope_base, self.ws, self.o_sr, stream)
+        if self.table_ready:
+            fs_window_attn_tabled(p, q, k, v, self.ws, self.o_sr, stream)
+        else:
+            fs_window_attn(p, q, k, v, self.rope_base, self.ws, self.o_sr, stream)
+            # a build recorded into a graph under capture has not run yet
+            self.table_ready = not torch.cuda.is_current_stream_capturing()
         if fused:
             fs_sparse_attn_combine(p, q, k, v, self.idx, self.topk, self.rms_eps, self.o_sr,
                                    alpha, self.o, self.ws_sparse, stream)

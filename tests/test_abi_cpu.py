@@ -193,6 +193,14 @@ def test_call_specific_limits(lib):
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 10000.0, FAKE, 16, FAKE, None) == 1
     assert b"workspace" in lib.fs_last_error()
     assert lib.fs_window_attn(C.byref(p), FAKE, FAKE, FAKE, 0.5, FAKE, 1 << 30, FAKE, None) == 1
+    # the table alone, and the window with a table already built
+    assert lib.fs_window_table(C.byref(p), 10000.0, FAKE, 16, None) == 1
+    assert b"workspace" in lib.fs_last_error()
+    assert lib.fs_window_table(C.byref(p), 1.0, FAKE, 1 << 30, None) == 1
+    assert lib.fs_window_table(C.byref(p), 10000.0, None, 1 << 30, None) == 1
+    assert lib.fs_window_attn_tabled(C.byref(p), FAKE, FAKE, FAKE, FAKE, 16, FAKE, None) == 1
+    assert b"workspace" in lib.fs_last_error()
+    assert lib.fs_window_attn_tabled(C.byref(p), FAKE, None, FAKE, FAKE, 1 << 30, FAKE, None) == 1
     assert lib.fs_combine(C.byref(p), FAKE, FAKE, None, FAKE, None) == 1
     big = _prob(n_ctx=1 << 20, n_q=1 << 20)              # 32752 candidate cells, no pruning
     assert lib.fs_select_topk(C.byref(big), FAKE, FAKE, None, None, None, None, None, 0, 8, FAKE,

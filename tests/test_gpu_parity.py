@@ -433,6 +433,45 @@ def test_token_major_strided_views_equal_contiguous(name):
         np.testing.assert_array_equal(t.float().cpu().numpy(), g[name_], err_msg=name_)
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_needle", "f32_d128_recent", "bf16_d128_decode"])
+def test_window_table_reuse(name):
+    """fs_window_table once, then fs_window_attn_tabled, equals fs_window_attn
+    (which rebuilds the table every call) bit for bit, also for another query range
+    of the same (w, d, rope_base) served by the same table; FsForward's second call
+    (which reuses its table) equals its first."""
+    from long_context_fs_amd import fs as fsb
+    wl, x, g, _ = small_case(name)
+    q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+    fwd = FsForward.for_workload(wl)
+    p = fwd.prob
+    ws = torch.empty_like(fwd.ws)
+    fsb.fs_window_table(p, wl.rope_base, ws)
+    got = torch.full_like(fwd.o_sr, float("nan"))
+    fsb.fs_window_attn_tabled(p, q, k, v, ws, got)
+    want = torch.full_like(fwd.o_sr, float("nan"))
+    fsb.fs_window_attn(p, q, k, v, wl.rope_base, fwd.ws, want)
+    # a shorter query range at the end of the same context, with the same table
+    nq = min(40, wl.n_q)
+    p2 = fsb.problem(wl.batch, wl.heads, wl.head_dim, wl.n_ctx, nq, wl.q_pos0 + wl.n_q - nq,
+                     wl.window, p.dtype)
+    q2 = q[:, :, wl.n_q - nq:].contiguous()
+    ws2 = torch.empty(max(fsb.fs_workspace_size(p2), ws.numel()), dtype=torch.uint8,
+                      device="cuda")
+    ws2[:ws.numel()].copy_(ws)
+    got2 = torch.empty((wl.batch, wl.heads, nq, wl.head_dim), dtype=got.dtype, device="cuda")
+    fsb.fs_window_attn_tabled(p2, q2, k, v, ws2, got2)
+    want2 = torch.empty_like(got2)
+    fsb.fs_window_attn(p2, q2, k, v, wl.rope_base, torch.empty_like(ws2), want2)
+    alpha = torch.from_numpy(x["alpha"]).cuda()
+    first = fwd(q, k, v, alpha).clone()
+    second = fwd(q, k, v, alpha)
+    torch.cuda.synchronize()
+    assert fwd.table_ready
+    for a, b_ in ((got, want), (got2, want2), (second, first)):
+        assert torch.equal(a, b_)
+    np.testing.assert_array_equal(got.float().cpu().numpy(), g["o_sr"])
+
+
 def test_window_dense_equals_causal():
     """w >= N-1: the local branch is dense causal RoPE attention (oracle pinned to SDPA)."""
     wl, x, g, ref = small_case("f32_d64_dense_window")
