@@ -11,7 +11,7 @@
 // key is found exactly by a bitwise search with ballot counts, ties at the
 // threshold go to the larger cell, and the chosen cells are written ascending.
 //
-// bf16 storage (candidate lists up to 528 cells): MFMA kernel.  A workgroup
+// Candidate lists up to 528 cells: MFMA kernel.  A workgroup
 // owns 64 consecutive queries (4 wavefronts x 16); they span at most three
 // candidate counts, so their candidates are the union of at most three keep
 // rows (or the prefix [0, n) without pruning), built in LDS with a bitmap.
@@ -25,7 +25,8 @@
 // and stopping once exactly K keys reach the candidate; the chosen cells are
 // written in slot order from packed prefix counts over the four lanes.  For
 // short query ranges the union can be split over workgroups of 64 slots, whose
-// top-K lists a merge kernel ranks again.
+// top-K lists a merge kernel ranks again.  f32 storage runs the same kernel with
+// q and kbar kept in fp32 and the scores from the fp32 matrix product.
 //
 // Reranking (eq. 12) scores each candidate cell by the log-sum-exp of its 32
 // token logits: 32x32x16 MFMA over two-cell key tiles for 128 queries per
@@ -1332,8 +1333,9 @@ __global__ __launch_bounds__(256, NB >= 33 ? 2 : 4) void rerank32_kernel(
 namespace {
 
 // Top-K over the candidates of every query: eq. 7 scores from kbar, or (rerank)
-// eq. 12 scores from the keys k.  MFMA kernels for bf16 storage when every
-// query's candidates fit the register blocks; row-wise kernels otherwise.
+// eq. 12 scores from the keys k.  MFMA kernels (selection for both storage
+// types, reranking for bf16) when every query's candidates fit the register
+// blocks; row-wise kernels otherwise.
 // Largest candidate list: the keep width, or every cell below the last query's n.
 int largest_candidate_count(const Shape& sh)
 {

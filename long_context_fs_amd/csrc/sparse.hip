@@ -13,8 +13,11 @@
 // (a per-query bitmap over the union slots).  q and k are the exact bf16
 // inputs (no rotation), so S^T = K Q^T is exact-product bf16 MFMA.  Epilogue:
 // divide by the softmax sum, RMSNorm over d with a 4-lane reduction, store.
-// f32 storage (or when the union bookkeeping would not fit in 64 KiB of LDS):
-// one wavefront per query.
+// f32 storage: the same workgroups, union and masks with fp32 K/V tiles on the
+// fp32 matrix product (sparse_attn_f32_kernel).  Short query ranges split each
+// tile's union over workgroups whose partial states a merge kernel combines.
+// More than 32768 cells, or union bookkeeping beyond 160 KiB of LDS: one
+// wavefront per query (row-wise).
 #include <mutex>
 
 #include "fs_device.hpp"
