@@ -913,6 +913,9 @@ F32_WIDE = {
     "f32_d64_decode_split": W["decode_b1h8_n262144_q256_d128_bf16"].replace(
         dtype="f32", head_dim=64, n_ctx=20000, n_q=64, q_pos0=20000 - 64, budget=300,
         needle_queries=64),
+    "f32_d128_decode_split_prior": W["decode_b1h8_n262144_q256_d128_bf16"].replace(
+        dtype="f32", heads=3, n_ctx=30000, n_q=40, q_pos0=30000 - 40, budget=400,
+        needle_queries=40, prior_lambda=0.2, prior_sigma=3000.0),
 }
 
 
