@@ -125,8 +125,8 @@ fs_status fs_select_topk(const fs_problem* problem, const void* q, const float* 
                          size_t workspace_bytes, void* stream);
 
 /* Bytes of the optional workspace of fs_select_topk (keep_width 0: no pruning):
- * 0 unless the query range is short (bf16, fewer than 256 workgroups of 64
- * queries) and the candidate union wider than 64 cells; then B H n_q S topk
+ * 0 unless the query range is short (fewer than 256 workgroups of 64 queries)
+ * and the candidate union wider than 64 cells; then B H n_q S topk
  * (int32 cell + float32 key), S = ceil(union / 64) splits.  With such a
  * workspace (device memory, 256-byte aligned, owned by the caller) the union is
  * split over S workgroups per query tile, each ranking its 64 cells, and a merge
